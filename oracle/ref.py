@@ -1,0 +1,176 @@
+"""ctypes binding of the ELSAA oracle (TEST INFRASTRUCTURE ONLY).
+
+The oracle is a plain fp64 CPU implementation of the operator of "ELSAA:
+Efficient Low-Rank and Sparse Attention Approximation for Training
+Transformers" (Sections 3, 3.1, 3.2, 3.3; Eq. 4 and Eq. 5). Only the test
+suite, the smoke check and the benchmark's CPU-baseline leg may use it; the
+product path never does.
+
+Inputs are numpy arrays holding G independent heads: Q, K, V, dO as float64
+[G, N, d]; planes_s float32 [G, hash_bits, d]; planes_lr float32
+[G, lr_tables, lr_bits, d]; lam float64 [G]; gates float64 [G, N] or None.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "elsaa_ref.c")
+_LIB = os.path.join(_HERE, "libelsaa_ref.so")
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+                               "-fno-fast-math", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _P(ctypes.Structure):
+    _fields_ = [("G", ctypes.c_int), ("N", ctypes.c_int), ("d", ctypes.c_int),
+                ("causal", ctypes.c_int), ("block", ctypes.c_int), ("hash_bits", ctypes.c_int),
+                ("lr_tables", ctypes.c_int), ("lr_bits", ctypes.c_int), ("chunk", ctypes.c_int),
+                ("tau", ctypes.c_double), ("eps", ctypes.c_double), ("scale", ctypes.c_double)]
+
+
+@dataclass
+class RefParams:
+    N: int
+    d: int
+    causal: bool
+    block: int
+    hash_bits: int
+    lr_tables: int
+    lr_bits: int = 4
+    chunk: int = 128
+    tau: float = 1.0
+    eps: float = 1e-6
+    scale: float | None = None
+
+    @property
+    def r(self) -> int:
+        return self.lr_tables << self.lr_bits
+
+    @property
+    def levels(self) -> int:
+        return int(round(math.log2(self.N // self.block))) if self.causal else 1
+
+    @classmethod
+    def from_workload(cls, w, **kw) -> "RefParams":
+        base = dict(N=w.N, d=w.d, causal=w.causal, block=w.block, hash_bits=w.hash_bits,
+                    lr_tables=w.lr_tables, lr_bits=w.lr_bits, chunk=w.chunk)
+        base.update(kw)
+        return cls(**base)
+
+    def c(self, G: int) -> _P:
+        sc = self.scale if self.scale is not None else 1.0 / math.sqrt(self.d)
+        return _P(G, self.N, self.d, int(self.causal), self.block, self.hash_bits, self.lr_tables,
+                  self.lr_bits, self.chunk, self.tau, self.eps, sc)
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        _lib = ctypes.CDLL(build())
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _f32(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what}: invalid parameters (rc={rc})")
+
+
+def select(p: RefParams, q, k, planes_s):
+    q, k, ps = _f64(q), _f64(k), _f32(planes_s)
+    G, N = q.shape[0], p.N
+    plen = p.levels * (N // 2) if p.causal else N
+    qc = np.zeros((G, N), np.uint16)
+    kc = np.zeros((G, N), np.uint16)
+    qp = np.zeros((G, plen), np.int32)
+    kp = np.zeros((G, plen), np.int32)
+    pc = p.c(G)
+    _check(lib().ref_select(ctypes.byref(pc), _ptr(q), _ptr(k), _ptr(ps), _ptr(qc), _ptr(kc),
+                            _ptr(qp), _ptr(kp)), "select")
+    shape = (G, p.levels, N // 2) if p.causal else (G, 1, N)
+    return qc, kc, qp.reshape(shape), kp.reshape(shape)
+
+
+def lowrank_summary(p: RefParams, k, v, planes_lr):
+    k, v, pl = _f64(k), _f64(v), _f32(planes_lr)
+    G, r, d = k.shape[0], p.r, p.d
+    nA = p.N // p.chunk if p.causal else 1
+    A = np.zeros((G, nA, r, d))
+    z = np.zeros((G, nA, r))
+    pc = p.c(G)
+    _check(lib().ref_lowrank_summary(ctypes.byref(pc), _ptr(k), _ptr(v), _ptr(pl), _ptr(A), _ptr(z)),
+           "lowrank_summary")
+    if not p.causal:
+        A, z = A[:, 0], z[:, 0]
+    return A, z
+
+
+def forward(p: RefParams, q, k, v, planes_s, planes_lr, lam, g_s=None, g_lr=None):
+    q, k, v, ps, pl = _f64(q), _f64(k), _f64(v), _f32(planes_s), _f32(planes_lr)
+    lam, g_s, g_lr = _f64(lam), _f64(g_s), _f64(g_lr)
+    G, N, d = q.shape
+    out = {n: np.zeros((G, N, d)) for n in ("O", "O_s", "O_lr")}
+    out.update({n: np.zeros((G, N)) for n in ("lse", "d_lr")})
+    pc = p.c(G)
+    _check(lib().ref_fwd(ctypes.byref(pc), _ptr(q), _ptr(k), _ptr(v), _ptr(ps), _ptr(pl), _ptr(lam),
+                         _ptr(g_s), _ptr(g_lr), _ptr(out["O"]), _ptr(out["O_s"]), _ptr(out["O_lr"]),
+                         _ptr(out["lse"]), _ptr(out["d_lr"])), "fwd")
+    return out
+
+
+def backward(p: RefParams, q, k, v, do, planes_s, planes_lr, lam, g_s=None, g_lr=None):
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    ps, pl, lam, g_s, g_lr = _f32(planes_s), _f32(planes_lr), _f64(lam), _f64(g_s), _f64(g_lr)
+    G, N, d = q.shape
+    out = {n: np.zeros((G, N, d)) for n in ("dQ", "dK", "dV")}
+    out["dlambda"] = np.zeros(G)
+    out["dg_s"] = np.zeros((G, N))
+    out["dg_lr"] = np.zeros((G, N))
+    pc = p.c(G)
+    _check(lib().ref_bwd(ctypes.byref(pc), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(ps), _ptr(pl),
+                         _ptr(lam), _ptr(g_s), _ptr(g_lr), _ptr(out["dQ"]), _ptr(out["dK"]),
+                         _ptr(out["dV"]), _ptr(out["dlambda"]), _ptr(out["dg_s"]),
+                         _ptr(out["dg_lr"])), "bwd")
+    return out
+
+
+def features(p: RefParams, planes_lr_head, x):
+    """RACE soft bucket assignment phi(x) for rows x [n, d] of one head."""
+    x = _f64(x)
+    pl = _f32(planes_lr_head)
+    out = np.zeros((x.shape[0], p.r))
+    pc = p.c(1)
+    for t in range(x.shape[0]):
+        row = np.ascontiguousarray(x[t])
+        o = np.zeros(p.r)
+        _check(lib().ref_features(ctypes.byref(pc), _ptr(pl), _ptr(row), _ptr(o)), "features")
+        out[t] = o
+    return out

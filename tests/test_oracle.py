@@ -1,0 +1,403 @@
+"""Pins of the oracle against what the ELSAA paper and plain mathematics fix:
+exact-rational hash signs, the sort order the sortLSH description implies, the
+closed-form causal support size, brute-force dense masked softmax, textbook
+attention when the support is full, closed forms of the RACE branch, the
+fusion's special cases, permutation invariance, finite differences and
+autograd of a dense formulation. CPU only."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import dense_check as D
+import workloads as W
+from oracle import ref
+
+
+def small(causal, N=128, d=16, block=16, r=32, lr_bits=4, gen="iid", dtype="f32", chunk=32,
+          H=1, **ga):
+    return W.Workload("t", 1, H, N, d, dtype, causal, block, r, gen, ga, lr_bits=lr_bits,
+                      chunk=chunk)
+
+
+def head(w, seed, h=0):
+    q, k = W.gen_qk(w, seed, 0, h)
+    dt = w.torch_dtype
+    q, k = q.to(dt).double(), k.to(dt).double()
+    v = W.gen_v(w, seed, 0, h).to(dt).double()
+    do = W.gen_do(w, seed, 0, h).to(dt).double()
+    ps, pl = W.gen_planes(w, seed)
+    return q.numpy(), k.numpy(), v.numpy(), do.numpy(), ps[h:h + 1].numpy(), pl[h:h + 1].numpy()
+
+
+def run_select(w, p, q, k, ps):
+    return ref.select(p, q[None], k[None], ps)
+
+
+# ----------------------------------------------------------------------------- selection
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_hash_codes_equal_exact_rational_sign(causal):
+    w = small(causal, N=64, d=24, block=8)
+    p = ref.RefParams.from_workload(w)
+    q, k, *_, ps, _ = head(w, 11)
+    qc, kc, _, _ = run_select(w, p, q, k, ps)
+    np.testing.assert_array_equal(qc[0], D.exact_sign_bits(q, ps[0]))
+    np.testing.assert_array_equal(kc[0], D.exact_sign_bits(k, ps[0]))
+
+
+def _check_sorted(perm, tokens, code, bits):
+    rank = D.gray_rank_table(bits)[code.astype(np.int64)]
+    assert sorted(perm.tolist()) == sorted(tokens)
+    key = [(int(rank[t]), int(t)) for t in perm]
+    assert key == sorted(key), "order must be by Gray rank, ties by ascending token index"
+
+
+def test_noncausal_orders_sorted_by_gray_rank_then_index():
+    w = small(False, N=256, d=16, block=16)
+    p = ref.RefParams.from_workload(w)
+    q, k, *_, ps, _ = head(w, 3)
+    qc, kc, qp, kp = run_select(w, p, q, k, ps)
+    assert qp.shape == (1, 1, 256)
+    _check_sorted(qp[0, 0], range(256), qc[0], w.hash_bits)
+    _check_sorted(kp[0, 0], range(256), kc[0], w.hash_bits)
+
+
+def test_causal_orders_per_level_and_segment():
+    w = small(True, N=256, d=16, block=16)
+    p = ref.RefParams.from_workload(w)
+    q, k, *_, ps, _ = head(w, 5)
+    qc, kc, qp, kp = run_select(w, p, q, k, ps)
+    assert qp.shape == (1, 4, 128)
+    for lev in range(4):
+        n = 256 >> lev
+        for a in range(0, 256, n):
+            off = (a // n) * (n // 2)
+            _check_sorted(qp[0, lev, off:off + n // 2], range(a + n // 2, a + n), qc[0], w.hash_bits)
+            _check_sorted(kp[0, lev, off:off + n // 2], range(a, a + n // 2), kc[0], w.hash_bits)
+
+
+def test_gray_rank_table_is_a_gray_order():
+    t = D.gray_rank_table(6)
+    inv = np.argsort(t)
+    for a, b in zip(inv[:-1], inv[1:]):
+        assert bin(int(a) ^ int(b)).count("1") == 1
+
+
+def test_causal_support_closed_form_and_causality():
+    w = small(True, N=256, d=16, block=16)
+    p = ref.RefParams.from_workload(w)
+    q, k, *_, ps, _ = head(w, 7)
+    _, _, qp, kp = run_select(w, p, q, k, ps)
+    M = D.support_mask(256, 16, True, qp[0], kp[0])
+    i = np.arange(256)
+    expect = (i % 16) + 1 + 16 * np.array([D.popcount(x) for x in i // 16])
+    np.testing.assert_array_equal(M.sum(1), expect)
+    assert not np.triu(M, 1).any(), "no key after its query"
+
+
+def test_noncausal_support_is_block_diagonal_after_permutation():
+    w = small(False, N=128, d=16, block=16)
+    p = ref.RefParams.from_workload(w)
+    q, k, *_, ps, _ = head(w, 9)
+    _, _, qp, kp = run_select(w, p, q, k, ps)
+    M = D.support_mask(128, 16, False, qp[0], kp[0])
+    assert (M.sum(1) == 16).all() and (M.sum(0) == 16).all()
+    Mp = M[np.ix_(qp[0, 0], kp[0, 0])]
+    blk = np.kron(np.eye(8, dtype=bool), np.ones((16, 16), bool))
+    np.testing.assert_array_equal(Mp, blk)
+
+
+# ----------------------------------------------------------------------------- sparse branch
+
+@pytest.mark.parametrize("causal,gen", [(False, "iid"), (True, "iid"), (True, "clusters")])
+def test_sparse_branch_equals_dense_masked_softmax(causal, gen):
+    ga = dict(n_clusters=8, sigma=0.3) if gen == "clusters" else {}
+    w = small(causal, N=256, d=16, block=16, gen=gen, **ga)
+    p = ref.RefParams.from_workload(w)
+    q, k, v, _, ps, pl = head(w, 21)
+    _, _, qp, kp = run_select(w, p, q, k, ps)
+    out = ref.forward(p, q[None], k[None], v[None], ps, pl, np.ones(1))
+    M = D.support_mask(256, 16, causal, qp[0], kp[0])
+    dn = D.dense_forward(*(torch.from_numpy(x) for x in (q, k, v)), M, torch.from_numpy(pl[0]), 1.0,
+                         causal, 1 / math.sqrt(16))
+    np.testing.assert_allclose(out["O_s"][0], dn["O_s"].numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out["lse"][0], dn["lse"].numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_full_support_is_exact_attention(causal):
+    w = small(causal, N=64, d=16, block=64)
+    p = ref.RefParams.from_workload(w)
+    q, k, v, _, ps, pl = head(w, 4)
+    out = ref.forward(p, q[None], k[None], v[None], ps, pl, np.zeros(1), g_lr=np.zeros((1, 64)))
+    S = q @ k.T / 4.0
+    if causal:
+        S = np.where(np.tril(np.ones((64, 64), bool)), S, -np.inf)
+    mx = S.max(1, keepdims=True)
+    e = np.exp(S - mx)
+    Oex = (e @ v) / e.sum(1, keepdims=True)
+    np.testing.assert_allclose(out["O_s"][0], Oex, atol=1e-12)
+    np.testing.assert_allclose(out["lse"][0], (mx[:, 0] + np.log(e.sum(1))), atol=1e-12)
+    # lambda = 0 with the default eps = 1e-6 gives m = d_s / (d_s + eps); with
+    # g_lr = 0 the fused output is that multiple of exact attention.
+    ds = np.exp(mx[:, 0]) * e.sum(1)
+    np.testing.assert_allclose(out["O"][0], (ds / (ds + 1e-6))[:, None] * Oex, atol=1e-12)
+
+
+def test_full_support_eps_zero_is_exactly_attention():
+    w = small(False, N=64, d=16, block=64)
+    p = ref.RefParams.from_workload(w, eps=0.0)
+    q, k, v, _, ps, pl = head(w, 6)
+    out = ref.forward(p, q[None], k[None], v[None], ps, pl, np.zeros(1), g_lr=np.zeros((1, 64)))
+    S = q @ k.T / 4.0
+    e = np.exp(S - S.max(1, keepdims=True))
+    np.testing.assert_allclose(out["O"][0], (e @ v) / e.sum(1, keepdims=True), atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- low-rank branch
+
+def test_features_normalised_and_product_of_sigmoids():
+    w = small(False, d=16, r=48, lr_bits=4)
+    p = ref.RefParams.from_workload(w, tau=0.7)
+    q, *_, pl = head(w, 13)
+    phi = ref.features(p, pl[0], q[:20])
+    L, g = 3, 4
+    np.testing.assert_allclose(phi.reshape(20, L, 16).sum(-1), 1.0, atol=1e-14)
+    u = (1 / 4.0) * np.einsum("ltd,nd->nlt", pl[0].astype(np.float64), q[:20])
+    sig = lambda x: 1 / (1 + np.exp(-x))
+    prod = np.ones((20, L, 16))
+    for b in range(16):
+        for t in range(g):
+            sgn = 1.0 if (b >> t) & 1 else -1.0
+            prod[:, :, b] *= sig(2 * sgn * u[:, :, t] / 0.7)
+    np.testing.assert_allclose(phi.reshape(20, L, 16), prod, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_lowrank_without_hyperplanes_is_uniform_mean(causal):
+    w = small(causal, N=128, d=16, r=3, lr_bits=0)
+    p = ref.RefParams.from_workload(w)
+    q, k, v, _, ps, pl = head(w, 17)
+    out = ref.forward(p, q[None], k[None], v[None], ps, pl, np.ones(1))
+    n = np.arange(1, 129) if causal else np.full(128, 128)
+    mean = np.cumsum(v, 0) / n[:, None] if causal else np.broadcast_to(v.mean(0), v.shape)
+    np.testing.assert_allclose(out["O_lr"][0], mean, atol=1e-12)
+    np.testing.assert_allclose(out["d_lr"][0], 3 * n, atol=1e-9)
+
+
+def test_lowrank_large_tau_is_uniform_over_buckets():
+    w = small(True, N=64, d=16, r=32, lr_bits=4)
+    p = ref.RefParams.from_workload(w, tau=1e12)
+    q, k, v, _, ps, pl = head(w, 19)
+    out = ref.forward(p, q[None], k[None], v[None], ps, pl, np.ones(1))
+    n = np.arange(1, 65)
+    np.testing.assert_allclose(out["O_lr"][0], np.cumsum(v, 0) / n[:, None], atol=1e-9)
+    np.testing.assert_allclose(out["d_lr"][0], 2 * n / 16.0, atol=1e-9)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_lowrank_equals_brute_force_double_sum(causal):
+    w = small(causal, N=128, d=16, r=32)
+    p = ref.RefParams.from_workload(w)
+    q, k, v, _, ps, pl = head(w, 23)
+    out = ref.forward(p, q[None], k[None], v[None], ps, pl, np.ones(1))
+    fq = D.features_torch(torch.from_numpy(q), torch.from_numpy(pl[0]), 0.25, 1.0).numpy()
+    fk = D.features_torch(torch.from_numpy(k), torch.from_numpy(pl[0]), 0.25, 1.0).numpy()
+    num = np.zeros_like(v)
+    den = np.zeros(128)
+    for i in range(128):
+        for j in range(128):
+            if causal and j > i:
+                continue
+            wij = float(fq[i] @ fk[j])
+            num[i] += wij * v[j]
+            den[i] += wij
+    np.testing.assert_allclose(out["d_lr"][0], den, rtol=1e-12)
+    np.testing.assert_allclose(out["O_lr"][0], num / den[:, None], atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_summary_statistics(causal):
+    w = small(causal, N=128, d=16, r=32, chunk=32)
+    p = ref.RefParams.from_workload(w)
+    _, k, v, _, ps, pl = head(w, 29)
+    A, z = ref.lowrank_summary(p, k[None], v[None], pl)
+    fk = D.features_torch(torch.from_numpy(k), torch.from_numpy(pl[0]), 0.25, 1.0).numpy()
+    if not causal:
+        np.testing.assert_allclose(A[0], fk.T @ v, atol=1e-11)
+        np.testing.assert_allclose(z[0].sum(), 2 * 128, rtol=1e-12)  # L = 2 tables
+    else:
+        assert A.shape == (1, 4, 32, 16)
+        for c in range(4):
+            np.testing.assert_allclose(A[0, c], fk[:32 * c].T @ v[:32 * c], atol=1e-11)
+            np.testing.assert_allclose(z[0, c], fk[:32 * c].sum(0), atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- fusion
+
+def test_fusion_with_unit_values():
+    w = small(True, N=128, d=16)
+    p = ref.RefParams.from_workload(w)
+    q, k, _, _, ps, pl = head(w, 31)
+    gs, gl = W.gen_gates(w, 31)
+    v = np.ones((128, 16))
+    out = ref.forward(p, q[None], k[None], v[None], ps, pl, np.array([0.8]), gs[0].numpy(),
+                      gl[0].numpy())
+    np.testing.assert_allclose(out["O_s"][0], 1.0, atol=1e-12)
+    np.testing.assert_allclose(out["O_lr"][0], 1.0, atol=1e-12)
+    m = (out["O"][0, :, 0] - gl[0, 0].numpy()) / gs[0, 0].numpy()
+    assert (m > 0).all() and (m < 1).all()
+    ds = np.exp(out["lse"][0])
+    np.testing.assert_allclose(m, ds / (ds + 0.8 * out["d_lr"][0] + 1e-6), rtol=1e-12)
+
+
+def test_fusion_lambda_eps_zero_is_plain_sum():
+    w = small(False, N=128, d=16)
+    p = ref.RefParams.from_workload(w, eps=0.0)
+    q, k, v, _, ps, pl = head(w, 37)
+    out = ref.forward(p, q[None], k[None], v[None], ps, pl, np.zeros(1))
+    np.testing.assert_allclose(out["O"][0], out["O_s"][0] + out["O_lr"][0], atol=1e-14)
+
+
+def test_fusion_lambda_large_keeps_low_rank_only():
+    w = small(False, N=128, d=16)
+    p = ref.RefParams.from_workload(w)
+    q, k, v, _, ps, pl = head(w, 41)
+    out = ref.forward(p, q[None], k[None], v[None], ps, pl, np.array([1e14]))
+    np.testing.assert_allclose(out["O"][0], out["O_lr"][0], atol=1e-6)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fused_weights_nonnegative_with_gate_row_sums(causal):
+    w = small(causal, N=128, d=16)
+    p = ref.RefParams.from_workload(w)
+    q, k, v, _, ps, pl = head(w, 43)
+    gs, gl = W.gen_gates(w, 43)
+    lam = np.array([1.7])
+    _, _, qp, kp = run_select(w, p, q, k, ps)
+    out = ref.forward(p, q[None], k[None], v[None], ps, pl, lam, gs[0].numpy(), gl[0].numpy())
+    M = D.support_mask(128, 16, causal, qp[0], kp[0])
+    dn = D.dense_forward(*(torch.from_numpy(x) for x in (q, k, v)), M, torch.from_numpy(pl[0]), 1.7,
+                         causal, 0.25, g_s=gs[0, 0].double(), g_lr=gl[0, 0].double())
+    S = torch.from_numpy(q @ k.T * 0.25).masked_fill(~torch.from_numpy(M), float("-inf"))
+    P = torch.softmax(S, 1).numpy()
+    fq = D.features_torch(torch.from_numpy(q), torch.from_numpy(pl[0]), 0.25, 1.0).numpy()
+    fk = D.features_torch(torch.from_numpy(k), torch.from_numpy(pl[0]), 0.25, 1.0).numpy()
+    Kl = fq @ fk.T
+    if causal:
+        Kl = np.tril(Kl)
+    Kl /= Kl.sum(1, keepdims=True)
+    m = dn["m"].numpy()
+    g1, g2 = gs[0, 0].numpy(), gl[0, 0].numpy()
+    Wf = (g1 * m)[:, None] * P + g2[:, None] * Kl
+    assert (Wf >= 0).all()
+    np.testing.assert_allclose(Wf.sum(1), g1 * m + g2, atol=1e-12)
+    np.testing.assert_allclose(out["O"][0], Wf @ v, atol=1e-11)
+
+
+# ----------------------------------------------------------------------------- invariance
+
+def test_noncausal_key_value_permutation():
+    w = small(False, N=128, d=16)
+    p = ref.RefParams.from_workload(w)
+    q, k, v, _, ps, pl = head(w, 47)
+    _, kc, _, _ = run_select(w, p, q, k, ps)
+    base = ref.forward(p, q[None], k[None], v[None], ps, pl, np.ones(1))
+    # Moving keys so that relative order inside each hash-rank class is kept leaves
+    # every block, hence the output, unchanged.
+    rank = D.gray_rank_table(w.hash_bits)[kc[0].astype(np.int64)]
+    pi = np.argsort(-rank, kind="stable")
+    out = ref.forward(p, q[None], k[pi][None], v[pi][None], ps, pl, np.ones(1))
+    np.testing.assert_allclose(out["O"][0], base["O"][0], atol=1e-12)
+    # The low-rank branch is invariant under any key/value permutation.
+    pi = np.random.default_rng(0).permutation(128)
+    out = ref.forward(p, q[None], k[pi][None], v[pi][None], ps, pl, np.ones(1))
+    np.testing.assert_allclose(out["O_lr"][0], base["O_lr"][0], atol=1e-12)
+    np.testing.assert_allclose(out["d_lr"][0], base["d_lr"][0], rtol=1e-12)
+
+
+def test_heads_are_independent():
+    w = small(True, N=128, d=16, H=2)
+    p = ref.RefParams.from_workload(w)
+    h0, h1 = head(w, 53, 0), head(w, 53, 1)
+    both = ref.forward(p, np.stack([h0[0], h1[0]]), np.stack([h0[1], h1[1]]),
+                       np.stack([h0[2], h1[2]]), np.concatenate([h0[4], h1[4]]),
+                       np.concatenate([h0[5], h1[5]]), np.array([1.0, 2.0]))
+    one = ref.forward(p, h1[0][None], h1[1][None], h1[2][None], h1[4], h1[5], np.array([2.0]))
+    np.testing.assert_array_equal(both["O"][1], one["O"][0])
+
+
+# ----------------------------------------------------------------------------- backward
+
+def _loss(p, q, k, v, do, ps, pl, lam, gs, gl):
+    o = ref.forward(p, q[None], k[None], v[None], ps, pl, np.array([lam]), gs[None], gl[None])
+    return float((o["O"][0] * do).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_central_differences(causal):
+    w = small(causal, N=64, d=8, block=8, r=32, chunk=16)
+    p = ref.RefParams.from_workload(w)
+    q, k, v, do, ps, pl = head(w, 59)
+    gs, gl = (x[0, 0].numpy().astype(np.float64) for x in W.gen_gates(w, 59))
+    lam = 0.9
+    g = ref.backward(p, q[None], k[None], v[None], do[None], ps, pl, np.array([lam]), gs[None],
+                     gl[None])
+    qc0, kc0, _, _ = run_select(w, p, q, k, ps)
+    rng = np.random.default_rng(1)
+    h = 1e-6
+    checked = 0
+    for name, arr, grad in (("q", q, g["dQ"][0]), ("k", k, g["dK"][0]), ("v", v, g["dV"][0])):
+        for _ in range(10):
+            i, j = int(rng.integers(64)), int(rng.integers(8))
+            vals = []
+            for sgn in (1, -1):
+                a = {"q": q.copy(), "k": k.copy(), "v": v.copy()}
+                a[name][i, j] += sgn * h
+                qc, kc, _, _ = run_select(w, p, a["q"], a["k"], ps)
+                if not (np.array_equal(qc, qc0) and np.array_equal(kc, kc0)):
+                    vals = None
+                    break
+                vals.append(_loss(p, a["q"], a["k"], a["v"], do, ps, pl, lam, gs, gl))
+            if vals is None:
+                continue
+            fd = (vals[0] - vals[1]) / (2 * h)
+            assert abs(fd - grad[i, j]) <= 1e-6 * max(1.0, abs(fd)), (name, i, j, fd, grad[i, j])
+            checked += 1
+    assert checked >= 25
+    fd = (_loss(p, q, k, v, do, ps, pl, lam + h, gs, gl) - _loss(p, q, k, v, do, ps, pl, lam - h, gs, gl)) / (2 * h)
+    assert abs(fd - g["dlambda"][0]) <= 1e-6 * max(1.0, abs(fd))
+    for name, arr, grad in (("gs", gs, g["dg_s"][0]), ("gl", gl, g["dg_lr"][0])):
+        for i in rng.integers(0, 64, 5):
+            a1, a2 = arr.copy(), arr.copy()
+            a1[i] += h
+            a2[i] -= h
+            lp = _loss(p, q, k, v, do, ps, pl, lam, *(a1 if name == "gs" else gs, gl if name == "gs" else a1))
+            lm = _loss(p, q, k, v, do, ps, pl, lam, *(a2 if name == "gs" else gs, gl if name == "gs" else a2))
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grad[i]) <= 1e-6 * max(1.0, abs(fd))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_dense_autograd(causal):
+    w = small(causal, N=128, d=16, block=16, r=32)
+    p = ref.RefParams.from_workload(w)
+    q, k, v, do, ps, pl = head(w, 61)
+    gs, gl = (x[0, 0].double() for x in W.gen_gates(w, 61))
+    _, _, qp, kp = run_select(w, p, q, k, ps)
+    M = D.support_mask(128, 16, causal, qp[0], kp[0])
+    tq, tk, tv = (torch.from_numpy(x).clone().requires_grad_(True) for x in (q, k, v))
+    lam = torch.tensor(1.3, dtype=torch.float64, requires_grad=True)
+    tgs, tgl = gs.clone().requires_grad_(True), gl.clone().requires_grad_(True)
+    dn = D.dense_forward(tq, tk, tv, M, torch.from_numpy(pl[0]), lam, causal, 0.25, g_s=tgs, g_lr=tgl)
+    (dn["O"] * torch.from_numpy(do)).sum().backward()
+    g = ref.backward(p, q[None], k[None], v[None], do[None], ps, pl, np.array([1.3]),
+                     gs.numpy()[None], gl.numpy()[None])
+    for a, b in ((g["dQ"][0], tq.grad), (g["dK"][0], tk.grad), (g["dV"][0], tv.grad),
+                 (g["dg_s"][0], tgs.grad), (g["dg_lr"][0], tgl.grad)):
+        np.testing.assert_allclose(a, b.numpy(), atol=1e-10, rtol=1e-9)
+    np.testing.assert_allclose(g["dlambda"][0], lam.grad.item(), rtol=1e-9)
