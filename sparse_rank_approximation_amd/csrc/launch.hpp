@@ -1,0 +1,105 @@
+// launch.hpp -- internal interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <type_traits>
+#include <utility>
+
+namespace elsaa {
+
+constexpr int kMaxHashBits = 12;
+constexpr int kMaxDh = 128;
+constexpr int kMaxTables = 16;
+constexpr int kLrBits = 4;
+constexpr size_t kLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
+
+// Validated problem description with derived sizes.
+struct Problem {
+  int B, H, N, d;
+  bool bf16;
+  bool causal;
+  int s;          // sortLSH block size
+  int hash_bits;
+  int L;          // RACE tables
+  int r;          // features = 16 L
+  int chunk;      // causal RACE summary spacing (N when not causal)
+  float tau, eps, scale;
+  int levels;     // off-diagonal recursion levels (causal), 1 otherwise
+  int nA;         // summaries per head
+  int elem;       // bytes per element of Q/K/V/...
+};
+
+// Entries of q_perm / k_perm per head.
+__host__ __device__ inline size_t perm_stride(int N, int levels, bool causal) {
+  return causal ? (size_t)levels * (N / 2) : (size_t)N;
+}
+
+// Slots of the sparse partial results of one head: [0, N) leaf blocks (causal)
+// or the single sorted level (non-causal), then level l at N + l N/2 (causal).
+__host__ __device__ inline size_t partial_slots(int N, int levels, bool causal) {
+  return causal ? (size_t)N + (size_t)levels * (N / 2) : (size_t)N;
+}
+
+// Compile-time dispatch over the element type, head dimension and padded table
+// count (tables are padded to an even power of two; padding tables are zero).
+template <typename F>
+void with_T(bool bf16, F&& f) {
+  if (bf16) f((__bf16*)nullptr);
+  else f((float*)nullptr);
+}
+template <typename F>
+void with_D(int d, F&& f) {
+  switch (d) {
+    case 32: f(std::integral_constant<int, 32>{}); break;
+    case 64: f(std::integral_constant<int, 64>{}); break;
+    default: f(std::integral_constant<int, 128>{}); break;
+  }
+}
+inline int padded_tables(int L) { return L <= 2 ? 2 : L <= 4 ? 4 : L <= 8 ? 8 : 16; }
+template <typename F>
+void with_LP(int L, F&& f) {
+  switch (padded_tables(L)) {
+    case 2: f(std::integral_constant<int, 2>{}); break;
+    case 4: f(std::integral_constant<int, 4>{}); break;
+    case 8: f(std::integral_constant<int, 8>{}); break;
+    default: f(std::integral_constant<int, 16>{}); break;
+  }
+}
+#define ELSAA_T(tp) std::remove_pointer_t<decltype(tp)>
+#define ELSAA_C(c) decltype(c)::value
+
+void launch_select(const Problem& pb, const void* Q, const void* K, const float* planes_s,
+                   uint16_t* qc, uint16_t* kc, int32_t* qperm, int32_t* kperm, hipStream_t st);
+
+// RACE tile sums and their prefix/suffix/total combination (lowrank.hip).
+int lr_tile_tokens(const Problem& pb);
+int lr_tiles(const Problem& pb);
+void run_lr_sums(const Problem& pb, const void* X, const void* Y, const float* alpha,
+                 const float* beta, const float* planes, float* S, float* Z, hipStream_t st);
+void run_lr_scan(const Problem& pb, const float* S, const float* Z, int mode, float* A, float* z,
+                 hipStream_t st);
+
+size_t summary_ws_bytes(const Problem& pb);
+void launch_summary(const Problem& pb, const void* K, const void* V, const float* planes_lr,
+                    float* A, float* z, void* ws, hipStream_t st);
+
+size_t fwd_ws_bytes(const Problem& pb);
+void launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
+                const float* planes_lr, const int32_t* qperm, const int32_t* kperm,
+                const float* A, const float* z, const float* lambda, const float* g_s,
+                const float* g_lr, void* O, void* O_s, void* O_lr, float* lse, float* d_lr,
+                void* ws, hipStream_t st);
+
+size_t bwd_ws_bytes(const Problem& pb);
+size_t bwd_lds_need(const Problem& pb);
+void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, const void* dO,
+                const void* O_s, const void* O_lr, const float* planes_lr, const int32_t* qperm,
+                const int32_t* kperm, const float* A, const float* z, const float* lse,
+                const float* d_lr, const float* lambda, const float* g_s, const float* g_lr,
+                void* dQ, void* dK, void* dV, float* dlambda, float* dg_s, float* dg_lr, void* ws,
+                hipStream_t st);
+
+}  // namespace elsaa

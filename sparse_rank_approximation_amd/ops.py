@@ -1,0 +1,254 @@
+"""Python surface of libelsaa: the four C calls with torch device tensors, and
+an autograd Function over them.
+
+PyTorch provides device memory and the current stream only; argument
+marshalling happens here, every computation in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass, replace
+
+import torch
+
+from . import _lib
+
+
+@dataclass(frozen=True)
+class ElsaaConfig:
+    """Problem sizes and method parameters (see include/elsaa.h, elsaa_params)."""
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: torch.dtype = torch.bfloat16
+    causal: bool = False
+    block: int = 128          # sortLSH block size s
+    hash_bits: int | None = None  # default log2(N / block), at least 1
+    lr_tables: int = 8        # RACE tables L (r = 16 L features)
+    lr_bits: int = 4
+    chunk: int = 512          # causal RACE summary spacing
+    tau: float = 1.0
+    eps: float = 1e-6
+    scale: float | None = None
+
+    @property
+    def bits(self) -> int:
+        if self.hash_bits is not None:
+            return self.hash_bits
+        return max(1, int(round(math.log2(max(1, self.N // self.block)))))
+
+    @property
+    def r(self) -> int:
+        return self.lr_tables << self.lr_bits
+
+    @property
+    def levels(self) -> int:
+        return int(round(math.log2(self.N // self.block))) if self.causal else 1
+
+    @property
+    def perm_len(self) -> int:
+        return self.levels * (self.N // 2) if self.causal else self.N
+
+    @property
+    def n_summaries(self) -> int:
+        return self.N // self.eff_chunk if self.causal else 1
+
+    @property
+    def eff_chunk(self) -> int:
+        return min(self.chunk, self.N)
+
+    def with_(self, **kw) -> "ElsaaConfig":
+        return replace(self, **kw)
+
+    def params(self) -> _lib.Params:
+        if self.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError(f"dtype {self.dtype} is not supported (float32 or bfloat16)")
+        sc = self.scale if self.scale is not None else 1.0 / math.sqrt(self.d)
+        return _lib.Params(self.B, self.H, self.N, self.d,
+                           _lib.BF16 if self.dtype == torch.bfloat16 else _lib.F32,
+                           int(self.causal), self.block, self.bits, self.lr_tables, self.lr_bits,
+                           self.eff_chunk, self.tau, self.eps, sc)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_tensor(name, t, shape, dtype, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _opt(name, t, shape, dtype, device):
+    if t is not None:
+        _check_tensor(name, t, shape, dtype, device)
+    return t
+
+
+def _workspace(cfg: ElsaaConfig, call: int, device) -> tuple[torch.Tensor | None, int]:
+    n = _lib.workspace_size(cfg.params(), call)
+    if n == 0:
+        return None, 0
+    return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+def select(cfg: ElsaaConfig, q, k, planes_s):
+    """elsaa_select: codes [B,H,N] uint16 (as int16 storage) and perms [B,H,P] int32."""
+    dev = q.device
+    x = (cfg.B, cfg.H, cfg.N, cfg.d)
+    _check_tensor("q", q, x, cfg.dtype, dev)
+    _check_tensor("k", k, x, cfg.dtype, dev)
+    _check_tensor("planes_s", planes_s, (cfg.H, cfg.bits, cfg.d), torch.float32, dev)
+    qc = torch.empty(cfg.B, cfg.H, cfg.N, dtype=torch.int16, device=dev)
+    kc = torch.empty_like(qc)
+    qp = torch.empty(cfg.B, cfg.H, cfg.perm_len, dtype=torch.int32, device=dev)
+    kp = torch.empty_like(qp)
+    ws, n = _workspace(cfg, _lib.CALL_SELECT, dev)
+    p = cfg.params()
+    _lib.check(_lib.lib().elsaa_select(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(planes_s),
+                                       _ptr(qc), _ptr(kc), _ptr(qp) if qp.numel() else None,
+                                       _ptr(kp) if kp.numel() else None, _ptr(ws), n,
+                                       _stream(dev)))
+    return qc, kc, qp, kp
+
+
+def lowrank_summary(cfg: ElsaaConfig, k, v, planes_lr):
+    """elsaa_lowrank_summary: A [B,H,nA,d,r], z [B,H,nA,r] fp32."""
+    dev = k.device
+    x = (cfg.B, cfg.H, cfg.N, cfg.d)
+    _check_tensor("k", k, x, cfg.dtype, dev)
+    _check_tensor("v", v, x, cfg.dtype, dev)
+    _check_tensor("planes_lr", planes_lr, (cfg.H, cfg.lr_tables, cfg.lr_bits, cfg.d),
+                  torch.float32, dev)
+    nA = cfg.n_summaries
+    A = torch.empty(cfg.B, cfg.H, nA, cfg.d, cfg.r, dtype=torch.float32, device=dev)
+    z = torch.empty(cfg.B, cfg.H, nA, cfg.r, dtype=torch.float32, device=dev)
+    ws, n = _workspace(cfg, _lib.CALL_SUMMARY, dev)
+    p = cfg.params()
+    _lib.check(_lib.lib().elsaa_lowrank_summary(ctypes.byref(p), _ptr(k), _ptr(v),
+                                                _ptr(planes_lr), _ptr(A), _ptr(z), _ptr(ws), n,
+                                                _stream(dev)))
+    return A, z
+
+
+def forward(cfg: ElsaaConfig, q, k, v, planes_lr, q_perm, k_perm, A, z, lam, g_s=None, g_lr=None):
+    """elsaa_fwd: returns dict(O, O_s, O_lr, lse, d_lr)."""
+    dev = q.device
+    x = (cfg.B, cfg.H, cfg.N, cfg.d)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, x, cfg.dtype, dev)
+    _check_tensor("planes_lr", planes_lr, (cfg.H, cfg.lr_tables, cfg.lr_bits, cfg.d),
+                  torch.float32, dev)
+    _check_tensor("q_perm", q_perm, (cfg.B, cfg.H, cfg.perm_len), torch.int32, dev)
+    _check_tensor("k_perm", k_perm, (cfg.B, cfg.H, cfg.perm_len), torch.int32, dev)
+    _check_tensor("A", A, (cfg.B, cfg.H, cfg.n_summaries, cfg.d, cfg.r), torch.float32, dev)
+    _check_tensor("z", z, (cfg.B, cfg.H, cfg.n_summaries, cfg.r), torch.float32, dev)
+    _check_tensor("lam", lam, (cfg.H,), torch.float32, dev)
+    _opt("g_s", g_s, (cfg.B, cfg.H, cfg.N), torch.float32, dev)
+    _opt("g_lr", g_lr, (cfg.B, cfg.H, cfg.N), torch.float32, dev)
+    out = {n: torch.empty(x, dtype=cfg.dtype, device=dev) for n in ("O", "O_s", "O_lr")}
+    out["lse"] = torch.empty(cfg.B, cfg.H, cfg.N, dtype=torch.float32, device=dev)
+    out["d_lr"] = torch.empty_like(out["lse"])
+    ws, n = _workspace(cfg, _lib.CALL_FWD, dev)
+    p = cfg.params()
+    _lib.check(_lib.lib().elsaa_fwd(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(planes_lr),
+        _ptr(q_perm) if q_perm.numel() else None, _ptr(k_perm) if k_perm.numel() else None,
+        _ptr(A), _ptr(z), _ptr(lam), _ptr(g_s), _ptr(g_lr), _ptr(out["O"]), _ptr(out["O_s"]),
+        _ptr(out["O_lr"]), _ptr(out["lse"]), _ptr(out["d_lr"]), _ptr(ws), n, _stream(dev)))
+    return out
+
+
+def backward(cfg: ElsaaConfig, q, k, v, do, O_s, O_lr, planes_lr, q_perm, k_perm, A, z, lse, d_lr,
+             lam, g_s=None, g_lr=None, want_dlam=True, want_dg=True):
+    """elsaa_bwd: returns dict(dQ, dK, dV, dlambda, dg_s, dg_lr)."""
+    dev = q.device
+    x = (cfg.B, cfg.H, cfg.N, cfg.d)
+    for name, t in (("q", q), ("k", k), ("v", v), ("do", do), ("O_s", O_s), ("O_lr", O_lr)):
+        _check_tensor(name, t, x, cfg.dtype, dev)
+    _check_tensor("q_perm", q_perm, (cfg.B, cfg.H, cfg.perm_len), torch.int32, dev)
+    _check_tensor("k_perm", k_perm, (cfg.B, cfg.H, cfg.perm_len), torch.int32, dev)
+    _check_tensor("lse", lse, (cfg.B, cfg.H, cfg.N), torch.float32, dev)
+    _check_tensor("d_lr", d_lr, (cfg.B, cfg.H, cfg.N), torch.float32, dev)
+    _check_tensor("lam", lam, (cfg.H,), torch.float32, dev)
+    _opt("g_s", g_s, (cfg.B, cfg.H, cfg.N), torch.float32, dev)
+    _opt("g_lr", g_lr, (cfg.B, cfg.H, cfg.N), torch.float32, dev)
+    out = {n: torch.empty(x, dtype=cfg.dtype, device=dev) for n in ("dQ", "dK", "dV")}
+    out["dlambda"] = torch.empty(cfg.H, dtype=torch.float32, device=dev) if want_dlam else None
+    out["dg_s"] = torch.empty(cfg.B, cfg.H, cfg.N, dtype=torch.float32, device=dev) if want_dg else None
+    out["dg_lr"] = torch.empty_like(out["dg_s"]) if want_dg else None
+    ws, n = _workspace(cfg, _lib.CALL_BWD, dev)
+    p = cfg.params()
+    _lib.check(_lib.lib().elsaa_bwd(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(O_s), _ptr(O_lr),
+        _ptr(planes_lr), _ptr(q_perm) if q_perm.numel() else None,
+        _ptr(k_perm) if k_perm.numel() else None, _ptr(A), _ptr(z), _ptr(lse), _ptr(d_lr),
+        _ptr(lam), _ptr(g_s), _ptr(g_lr), _ptr(out["dQ"]), _ptr(out["dK"]), _ptr(out["dV"]),
+        _ptr(out["dlambda"]), _ptr(out["dg_s"]), _ptr(out["dg_lr"]), _ptr(ws), n,
+        _stream(dev)))
+    return out
+
+
+class ElsaaFunction(torch.autograd.Function):
+    """O = ELSAA(Q, K, V; lambda, g_s, g_lr) with gradients for Q, K, V, lambda and
+    the gates; the hyperplanes are fixed inputs (no gradient)."""
+
+    @staticmethod
+    def forward(ctx, cfg, q, k, v, lam, g_s, g_lr, planes_s, planes_lr):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        _, _, qp, kp = select(cfg, q, k, planes_s)
+        A, z = lowrank_summary(cfg, k, v, planes_lr)
+        out = forward(cfg, q, k, v, planes_lr, qp, kp, A, z, lam, g_s, g_lr)
+        ctx.cfg = cfg
+        ctx.save_for_backward(q, k, v, lam, g_s, g_lr, planes_lr, qp, kp, A, z, out["O_s"],
+                              out["O_lr"], out["lse"], out["d_lr"])
+        return out["O"]
+
+    @staticmethod
+    def backward(ctx, dO):
+        (q, k, v, lam, g_s, g_lr, planes_lr, qp, kp, A, z, O_s, O_lr, lse, d_lr) = ctx.saved_tensors
+        g = backward(ctx.cfg, q, k, v, dO.contiguous(), O_s, O_lr, planes_lr, qp, kp, A, z, lse,
+                     d_lr, lam, g_s, g_lr, want_dlam=ctx.needs_input_grad[4],
+                     want_dg=ctx.needs_input_grad[5] or ctx.needs_input_grad[6])
+        return (None, g["dQ"], g["dK"], g["dV"], g["dlambda"],
+                g["dg_s"] if ctx.needs_input_grad[5] else None,
+                g["dg_lr"] if ctx.needs_input_grad[6] else None, None, None)
+
+
+def make_planes(cfg: ElsaaConfig, seed: int = 0, device="cuda"):
+    """iid N(0,1) sortLSH and RACE hyperplanes for every head (fixed, no gradient)."""
+    g = torch.Generator().manual_seed(seed)
+    ps = torch.randn(cfg.H, cfg.bits, cfg.d, generator=g)
+    pl = torch.randn(cfg.H, cfg.lr_tables, cfg.lr_bits, cfg.d, generator=g)
+    return ps.to(device), pl.to(device)
+
+
+def elsaa_attention(q, k, v, *, causal: bool, block: int, lr_tables: int, lam=None, g_s=None,
+                    g_lr=None, planes_s=None, planes_lr=None, seed: int = 0, chunk: int = 512,
+                    hash_bits: int | None = None, tau: float = 1.0, eps: float = 1e-6):
+    """ELSAA attention of q, k, v [B, H, N, d] (fp32 or bf16 device tensors)."""
+    B, H, N, d = q.shape
+    cfg = ElsaaConfig(B, H, N, d, q.dtype, causal, block, hash_bits, lr_tables, 4, chunk, tau, eps)
+    if planes_s is None or planes_lr is None:
+        ps, pl = make_planes(cfg, seed, q.device)
+        planes_s = ps if planes_s is None else planes_s
+        planes_lr = pl if planes_lr is None else planes_lr
+    if lam is None:
+        lam = torch.ones(H, dtype=torch.float32, device=q.device)
+    return ElsaaFunction.apply(cfg, q, k, v, lam, g_s, g_lr, planes_s, planes_lr)
