@@ -225,7 +225,6 @@ elsaa_status elsaa_bwd(const elsaa_params* p, const void* Q, const void* K, cons
                        size_t ws_bytes, void* stream) {
   PROLOGUE(ELSAA_CALL_BWD);
   if (empty) return ELSAA_OK;
-  return fail(ELSAA_ERR_UNSUPPORTED, "backward not built yet");
   NEED(Q); NEED(K); NEED(V); NEED(dO); NEED(O_s); NEED(O_lr); NEED(planes_lr);
   if (elsaa::perm_stride(pb.N, pb.levels, pb.causal) > 0) { NEED(q_perm); NEED(k_perm); }
   NEED(A); NEED(z); NEED(lse_s); NEED(d_lr); NEED(lambda); NEED(dQ); NEED(dK);

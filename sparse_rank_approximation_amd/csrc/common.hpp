@@ -137,6 +137,7 @@ struct Features {
   static constexpr int NPT = (4 * LP + 31) / 32;  // 32-row projection tiles
   static constexpr int NJP = LP / 2;               // table pairs
   float phi[NJP][16];
+  float sp[NJP][4], sq[NJP][4];  // sigmoid(+a_t), sigmoid(-a_t), a_t = 2 u_t / tau
 
   __device__ __forceinline__ void compute(const T* xrow, bool valid, const float* planes,
                                           int L, float scale, float tau, int lane) {
@@ -186,6 +187,8 @@ struct Features {
           const float a = c2 * u[mt][4 * g + t];
           p[t] = sigmoid(a);
           q[t] = sigmoid(-a);
+          sp[jp][t] = p[t];
+          sq[jp][t] = q[t];
         }
         float lo4[4], hi4[4];
 #pragma unroll
@@ -214,11 +217,84 @@ struct Features {
     for (int e = 0; e < M::KPL; ++e) x[e] = phi[jp][b0 + e];
     return M::from_floats(x);
   }
+  // Backward of phi through a_t = (2 scale / tau) <R_t, x>: given dphi in this
+  // lane's layout, da_t = sum_b dphi_b phi_b (bit t of b ? sigmoid(-a_t) : -sigmoid(a_t)).
+  __device__ __forceinline__ void backward(const float (&dphi)[NJP][16], float (&da)[NJP][4]) const {
+#pragma unroll
+    for (int jp = 0; jp < NJP; ++jp)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int b = 0; b < 16; ++b) {
+          const float w = dphi[jp][b] * phi[jp][b];
+          acc += ((b >> t) & 1) ? w * sq[jp][t] : -w * sp[jp][t];
+        }
+        da[jp][t] = acc;
+      }
+  }
+
   // Feature index that K step ks, element e uses for lane half h.
   static __device__ __forceinline__ int frag_feat(int ks, int e, int h) {
     constexpr int SPJ = 16 / MF<T>::KPL;
     return 16 * (2 * (ks / SPJ) + h) + (ks % SPJ) * MF<T>::KPL + e;
   }
 };
+
+// A D tile whose rows are the 32 features of tables (2 jp, 2 jp + 1) and whose
+// columns are tokens (lane % 32) holds, in lane half h, rows 8 g + 4 h + t. One
+// exchange with the other half leaves lane half h with all 16 buckets of table
+// 2 jp + h, the layout of Features::phi[jp].
+__device__ __forceinline__ void tile_to_table(const floatx16& acc, int h, float (&out)[16]) {
+#pragma unroll
+  for (int g2 = 0; g2 < 2; ++g2)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float keep = h ? acc[8 + 4 * g2 + t] : acc[4 * g2 + t];
+      const float send = h ? acc[4 * g2 + t] : acc[8 + 4 * g2 + t];
+      const float recv = swap_half(send);
+      // own rows: b = 8 g2 + 4 h + t; partner rows: b = 8 g2 + 4 (1 - h) + t
+      out[8 * g2 + t] = h ? recv : keep;
+      out[8 * g2 + 4 + t] = h ? keep : recv;
+    }
+}
+
+// dX^T (D x 32 tokens, D/32 tiles, columns = lane % 32) = c2 * R^T dA^T, where lane
+// half h holds da[jp][t] for table 2 jp + h of its token and R = planes [L][4][D].
+// This is the last step of the backward through the RACE features:
+// dx = sum_{l,t} da_lt (2 scale / tau) R_lt.
+template <typename T, int D, int LP>
+__device__ __forceinline__ void features_dx(const float (&da)[LP / 2][4], const float* planes, int L,
+                                            float c2, int lane, floatx16 (&dx)[D / 32]) {
+  typedef MF<T> M;
+  constexpr int NQ = 2 * LP;  // (table, hyperplane) pairs per lane half
+  constexpr int NKS = (NQ + M::KPL - 1) / M::KPL;
+  const int h = lane >> 5, col = lane & 31;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) dx[dt] = zero16();
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    float a[M::KPL], b[M::KPL];
+#pragma unroll
+    for (int e = 0; e < M::KPL; ++e) {
+      const int q = ks * M::KPL + e, jp = q >> 2, t = q & 3;
+      b[e] = (q < NQ) ? da[jp < LP / 2 ? jp : 0][t] : 0.0f;
+    }
+    const typename M::frag bf = M::from_floats(b);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int e = 0; e < M::KPL; ++e) {
+        const int q = ks * M::KPL + e, jp = q >> 2, t = q & 3, table = 2 * jp + h;
+        a[e] = (q < NQ && table < L) ? planes[(size_t)(4 * table + t) * D + 32 * dt + col] : 0.0f;
+      }
+      dx[dt] = M::mma(M::from_floats(a), bf, dx[dt]);
+    }
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dx[dt][v] *= c2;
+}
 
 }  // namespace elsaa

@@ -57,3 +57,32 @@ def gpu_forward(w, inp, lam, gs=None, glr=None, **cfgkw):
 
 def all_heads(w):
     return [(b, h) for b in range(w.B) for h in range(w.H)]
+
+
+def wl(name, B, H, N, d, dtype, causal, block, r, gen="iid", chunk=128, **ga):
+    return W.Workload(name, B, H, N, d, dtype, causal, block, r, gen, ga, chunk=chunk)
+
+CASES = {
+    # the tiny single-head workload, as is
+    "tiny_f32": (W.CONFIGS[1], False, False),
+    # several tiles and summary chunks, causal, fp32
+    "causal_f32_N512_d64_s32": (wl("c", 1, 2, 512, 64, "f32", True, 32, 32, chunk=128), True, True),
+    # bf16 causal with planted clusters, d 128, s 128, r 128, two summaries per head
+    "causal_bf16_N1024_d128_s128": (wl("c", 1, 2, 1024, 128, "bf16", True, 128, 128,
+                                       "clusters", chunk=512, n_clusters=16, sigma=0.5), True, True),
+    # bf16 non-causal vision-like field, d 64, s 32, r 32
+    "vit_bf16_N1024_d64_s32": (wl("v", 2, 2, 1024, 64, "bf16", False, 32, 32, "smooth_field",
+                                  grid=32, blur=2.0, noise=0.3), False, False),
+    # ragged: 96 tokens = one 64-token step plus a 32-token tail; 3 blocks of 32
+    "ragged_noncausal_f32_N96": (wl("r", 1, 1, 96, 32, "f32", False, 32, 16), True, True),
+    # ragged causal: 32-token summary chunks inside 64-token steps; block 16
+    "ragged_causal_f32_N256_s16_chunk32": (wl("r", 1, 1, 256, 32, "f32", True, 16, 48, chunk=32),
+                                           True, False),
+    # degenerate causal: N == block, no off-diagonal level (dense causal softmax)
+    "causal_single_block_f32": (wl("d", 1, 1, 64, 32, "f32", True, 64, 32, chunk=64), False, False),
+    # odd table count (padded to 4 tables on the GPU), bf16, d 32
+    "tables3_bf16_causal": (wl("t", 1, 1, 512, 32, "bf16", True, 64, 48, chunk=256), True, True),
+    # maximum block 256 and r 256 at d 128, causal bf16
+    "block256_bf16": (wl("m", 1, 1, 1024, 128, "bf16", True, 256, 256, "clusters", chunk=512,
+                         n_clusters=8, sigma=0.5), False, False),
+}
