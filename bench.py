@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""ELSAA attention, forward + backward, on one MI355X.
+
+One step is the whole hot path over one batch of resident synthetic inputs:
+elsaa_select (hash + sort), elsaa_lowrank_summary, elsaa_fwd and elsaa_bwd.
+Prints one JSON line: whole-job tokens/s (B * N tokens per fwd+bwd step), the
+roofline fraction of the dominant kernel (timed with HIP events on its launch
+stream through the library's diagnostics), and the oracle timed on this host's
+cores on a bounded sample of heads.
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ELSAA fwd+bwd tokens/sec at N=16k,d_h=128 bf16 on 1 GPU; % of roofline"
+UNIT = "tokens/s"
+# MI355X published peaks.
+PEAK_HBM_GBS = 8000.0
+PEAK_MFMA = {"bf16": 2500.0, "f32": 157.3}  # dense TFLOP/s
+PEAK_FP64_VECTOR = 78.6
+
+
+def selected_pairs(w) -> int:
+    """Query-key pairs of the sparse branch per head (the support sizes summed)."""
+    if not w.causal:
+        return w.N * w.block
+    lv = int(round(math.log2(w.N // w.block)))
+    return lv * (w.N // 2) * w.block + w.N * (w.block + 1) // 2
+
+
+def kernel_work(w) -> dict:
+    """Algorithmic work per launch of each kernel: (bound, amount, unit).
+    Flops count the contractions the method needs (not masked-tile waste or
+    recomputation); bytes count compulsory reads and writes of that kernel."""
+    BH, N, d, r = w.B * w.H, w.N, w.d, w.r
+    e = 2 if w.dtype == "bf16" else 4
+    pairs = selected_pairs(w) * BH
+    tok = BH * N
+    return {
+        "sparse_fwd": ("mfma", 4.0 * d * pairs, "TFLOP/s"),
+        "sparse_bwd": ("mfma", 8.0 * d * pairs, "TFLOP/s"),
+        "fwd_epilogue": ("mfma", 2.0 * r * (d + 1) * tok, "TFLOP/s"),
+        "lr_sums": ("mfma", 2.0 * r * (d + 1) * tok, "TFLOP/s"),
+        "lr_bwd_q": ("mfma", 2.0 * r * (d + 1) * tok, "TFLOP/s"),
+        "lr_bwd_k": ("mfma", 4.0 * r * (d + 1) * tok, "TFLOP/s"),
+        "hash": ("hbm", 2.0 * tok * d * e + 4.0 * tok, "GB/s"),
+        "bwd_rows": ("hbm", 3.0 * tok * d * e + 40.0 * tok, "GB/s"),
+    }
+
+
+def roofline(name, launches, total_ms, w, traffic_file):
+    work = kernel_work(w)
+    if name not in work:
+        return None
+    bound, amount, unit = work[name]
+    avg_s = total_ms / launches / 1e3
+    if bound == "mfma":
+        achieved = amount / avg_s / 1e12
+        peak = PEAK_MFMA[w.dtype]
+    else:
+        achieved = amount / avg_s / 1e9
+        peak = PEAK_HBM_GBS
+    return {"bound": bound, "kernel": name, "achieved": round(achieved, 2), "peak": peak,
+            "unit": unit, "frac": round(achieved / peak, 4), "avg_launch_us": round(avg_s * 1e6, 1),
+            "traffic": traffic_bytes(name, traffic_file)}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_rank_approximation_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_bytes(name, path):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, if it was taken from the current kernel sources; else None."""
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except ValueError:
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(name)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, seed, n_heads, threads):
+    """The oracle (plain fp64 C, OpenMP over heads) on `n_heads` full-size heads:
+    select + forward + backward. Scaled to the whole workload's tokens/s."""
+    import numpy as np
+    import workloads as W
+    from oracle import ref
+    heads = [((i * 7) % w.B, (i * 5) % w.H) for i in range(n_heads)]
+    dt = w.torch_dtype
+
+    def arr(t):
+        return t.to(dt).double().numpy()
+
+    q, k, v, do = [], [], [], []
+    for b, h in heads:
+        qq, kk = W.gen_qk(w, seed, b, h)
+        q.append(arr(qq)); k.append(arr(kk))
+        v.append(arr(W.gen_v(w, seed, b, h))); do.append(arr(W.gen_do(w, seed, b, h)))
+    ps, pl = W.gen_planes(w, seed)
+    ps = np.stack([ps[h].numpy() for _, h in heads])
+    pl = np.stack([pl[h].numpy() for _, h in heads])
+    p = ref.RefParams.from_workload(w)
+    ref.lib()
+    t0 = time.perf_counter()
+    ref.backward(p, np.stack(q), np.stack(k), np.stack(v), np.stack(do), ps, pl, np.ones(n_heads))
+    t = time.perf_counter() - t0
+    tokens_per_s = n_heads * w.N / (w.H * t)
+    return {"value": round(tokens_per_s, 1), "unit": UNIT, "cores": threads, "kind": "oracle",
+            "sample": f"{n_heads} of {w.B * w.H} heads at full N={w.N}, select+fwd+bwd in fp64, "
+                      f"{t:.1f} s wall on {threads} threads; scaled by heads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=16)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the operator is measured per GPU; heads would shard across GPUs with no exchange)",
+              file=sys.stderr)
+        sys.exit(1)
+    threads = min(16, int(os.environ.get("OMP_NUM_THREADS", "16")), os.cpu_count() or 1)
+    os.environ["OMP_NUM_THREADS"] = str(threads)
+
+    import torch
+    import workloads as W
+    import sparse_rank_approximation_amd as S
+    from sparse_rank_approximation_amd import _lib
+
+    w = W.CONFIGS[args.config]
+    seed = W.config_seed(args.config)
+    t0 = time.perf_counter()
+    inp = W.gen_inputs(w, seed)
+    dev = torch.device("cuda:0")
+    d = {k: v.to(dev) for k, v in inp.items()}
+    del inp
+    print(f"[bench] inputs for {w.name} ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr,
+          flush=True)
+    cfg = S.ElsaaConfig(w.B, w.H, w.N, w.d, w.torch_dtype, w.causal, w.block, w.hash_bits,
+                        w.lr_tables, w.lr_bits, w.chunk)
+    lam = torch.ones(w.H, dtype=torch.float32, device=dev)
+
+    def step():
+        _, _, qp, kp = S.select(cfg, d["q"], d["k"], d["planes_s"])
+        A, z = S.lowrank_summary(cfg, d["k"], d["v"], d["planes_lr"])
+        o = S.forward(cfg, d["q"], d["k"], d["v"], d["planes_lr"], qp, kp, A, z, lam)
+        S.backward(cfg, d["q"], d["k"], d["v"], d["do"], o["O_s"], o["O_lr"], d["planes_lr"], qp,
+                   kp, A, z, o["lse"], o["d_lr"], lam)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+    _lib.profile(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    _lib.profile(False)
+    ms = start.elapsed_time(end) / args.steps
+    rep = _lib.profile_report()
+    tokens = w.B * w.N
+    value = tokens / (ms / 1e3)
+    kernels = {k: {"launches": n, "avg_us": round(t / n * 1e3, 1),
+                   "ms_per_step": round(t / args.steps, 3)} for k, (n, t) in sorted(rep.items())}
+    dom = max(rep, key=lambda k: rep[k][1])
+    roof = roofline(dom, rep[dom][0], rep[dom][1], w,
+                    os.path.join(ROOT, "profiles", "traffic.json"))
+    print("[bench] timed; kernels: " + json.dumps(kernels), file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, seed, min(args.cpu_heads, w.B * w.H), threads)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": UNIT, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded generators shaped like the paper's long-context workloads)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d_h": w.d,
+                   "causal": w.causal, "block": w.block, "r": w.r, "hash_bits": w.hash_bits,
+                   "chunk": w.chunk, "global_batch": w.B, "seq_len": w.N, "parallelism": "none"},
+        "roofline": roof,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -178,6 +178,17 @@ elsaa_status elsaa_bwd(const elsaa_params* p, const void* Q, const void* K, cons
                        void* dK, void* dV, float* dlambda, float* dg_s, float* dg_lr, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* Diagnostics, not a step of the operator: per-kernel timing. With profiling on,
+ * every kernel the four calls launch is bracketed by two HIP events recorded on
+ * the stream it is launched on. elsaa_profile(1) discards earlier records and
+ * starts recording, elsaa_profile(0) stops. elsaa_profile_report waits for the
+ * recorded events and writes one line per kernel, "name launches total_ms\n",
+ * into buf (host memory, NUL-terminated, truncated to len bytes); *needed (if not
+ * NULL) receives the untruncated length + 1. Returns ELSAA_ERR_HIP if an event
+ * query fails. */
+elsaa_status elsaa_profile(int32_t enable);
+elsaa_status elsaa_profile_report(char* buf, size_t len, size_t* needed);
+
 /* Message for the last non-OK status returned on this host thread ("" if none). */
 const char* elsaa_last_error(void);
 

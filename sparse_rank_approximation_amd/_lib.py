@@ -15,7 +15,7 @@ F32, BF16 = 0, 1
 CALL_SELECT, CALL_SUMMARY, CALL_FWD, CALL_BWD = range(4)
 
 SYMBOLS = ("elsaa_workspace_size", "elsaa_select", "elsaa_lowrank_summary", "elsaa_fwd",
-           "elsaa_bwd", "elsaa_last_error")
+           "elsaa_bwd", "elsaa_profile", "elsaa_profile_report", "elsaa_last_error")
 
 
 class Params(ctypes.Structure):
@@ -53,6 +53,9 @@ def lib() -> ctypes.CDLL:
     L.elsaa_lowrank_summary.argtypes = [_PP, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.elsaa_fwd.argtypes = [_PP] + [_vp] * 17 + [ctypes.c_size_t, _vp]
     L.elsaa_bwd.argtypes = [_PP] + [_vp] * 23 + [ctypes.c_size_t, _vp]
+    L.elsaa_profile.argtypes = [ctypes.c_int32]
+    L.elsaa_profile_report.argtypes = [ctypes.c_char_p, ctypes.c_size_t,
+                                       ctypes.POINTER(ctypes.c_size_t)]
     L.elsaa_last_error.argtypes = []
     L.elsaa_last_error.restype = ctypes.c_char_p
     for s in SYMBOLS[:-1]:
@@ -70,3 +73,21 @@ def workspace_size(p: Params, call: int) -> int:
     n = ctypes.c_size_t(0)
     check(lib().elsaa_workspace_size(ctypes.byref(p), call, ctypes.byref(n)))
     return int(n.value)
+
+
+def profile(enable: bool) -> None:
+    """Start (discarding earlier records) or stop per-kernel event timing."""
+    check(lib().elsaa_profile(1 if enable else 0))
+
+
+def profile_report() -> dict:
+    """{kernel name: (launches, total milliseconds)} of the recorded launches."""
+    need = ctypes.c_size_t(0)
+    check(lib().elsaa_profile_report(None, 0, ctypes.byref(need)))
+    buf = ctypes.create_string_buffer(int(need.value) + 16)
+    check(lib().elsaa_profile_report(buf, len(buf), ctypes.byref(need)))
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, n, ms = line.split()
+        out[name] = (int(n), float(ms))
+    return out

@@ -815,18 +815,18 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
     using T = ELSAA_T(tp);
     with_D(pb.d, [&](auto dc) {
       constexpr int D = ELSAA_C(dc);
-      hipLaunchKernelGGL((bwd_rows_kernel<T, D>), dim3(lay.nblk, BH), dim3(256), 0, st,
+      ELSAA_LAUNCH("bwd_rows", (bwd_rows_kernel<T, D>), dim3(lay.nblk, BH), dim3(256), 0, st,
                          (const T*)dO, (const T*)O_s, (const T*)O_lr, lse, d_lr, lambda, g_s,
                          g_lr, pb.eps, pb.H, pb.N, rc, rD, re, rdd, dg_s, dg_lr, dlam_part);
       if (dlambda)
-        hipLaunchKernelGGL(dlam_reduce_kernel, dim3((pb.H + 63) / 64), dim3(64), 0, st, dlam_part,
+        ELSAA_LAUNCH("dlam_reduce", dlam_reduce_kernel, dim3((pb.H + 63) / 64), dim3(64), 0, st, dlam_part,
                            pb.B, pb.H, lay.nblk, dlambda);
       run_lr_sums(pb, Q, dO, re, rdd, planes_lr, S, Z, st);
       run_lr_scan(pb, S, Z, pb.causal ? 2 : 0, Gs, gzs, st);
       auto run_sparse = [&](auto sc) {
         constexpr int SB = ELSAA_C(sc);
         if constexpr (sbwd_lds<T, D, SB>() <= kLdsBytes)
-          hipLaunchKernelGGL((sparse_bwd_kernel<T, D, SB>), dim3(items, BH),
+          ELSAA_LAUNCH("sparse_bwd", (sparse_bwd_kernel<T, D, SB>), dim3(items, BH),
                              dim3(64 * (SB < 32 ? 1 : SB / 32)), 0, st, (const T*)Q,
                              (const T*)K, (const T*)V, (const T*)dO, lse, rc, rD, qperm, kperm,
                              pb.N, (int)pb.causal, pb.levels, pb.scale, (T*)dQp, (T*)dKp,
@@ -844,13 +844,13 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
         for (int g = 0; g < groups; ++g) {
           const int first = g == 0, last = g == groups - 1;
           if constexpr (sizeof(LbqSmem<T, D, LPG>) <= kLdsBytes)
-            hipLaunchKernelGGL((lr_bwd_q_kernel<T, D, LPG>),
+            ELSAA_LAUNCH("lr_bwd_q", (lr_bwd_q_kernel<T, D, LPG>),
                                dim3((pb.N + span - 1) / span, BH), dim3(256), 0, st, (const T*)Q,
                                (const T*)K, (const T*)V, (const T*)dO, planes_lr, A, z, re, rdd,
                                (const T*)dQp, scrQ, (T*)dQ, pb.H, pb.N, pb.L, span, pb.levels,
                                (int)pb.causal, pb.scale, pb.tau, g, first, last);
           if constexpr (sizeof(LbkSmem<T, D, LPG>) <= kLdsBytes)
-            hipLaunchKernelGGL((lr_bwd_k_kernel<T, D, LPG>),
+            ELSAA_LAUNCH("lr_bwd_k", (lr_bwd_k_kernel<T, D, LPG>),
                                dim3((pb.N + span_k - 1) / span_k, BH), dim3(256), 0, st,
                                (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, planes_lr, Gs,
                                gzs, re, rdd, (const T*)dKp, (const T*)dVp, scrK, scrV, (T*)dK,

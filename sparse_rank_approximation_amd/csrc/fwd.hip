@@ -421,7 +421,7 @@ void launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
       auto run = [&](auto sc) {
         constexpr int SB = ELSAA_C(sc);
         if constexpr (sparse_fwd_lds<T, D, SB>() <= kLdsBytes)
-        hipLaunchKernelGGL((sparse_fwd_kernel<T, D, SB>), dim3(items, BH),
+        ELSAA_LAUNCH("sparse_fwd", (sparse_fwd_kernel<T, D, SB>), dim3(items, BH),
                            dim3(64 * (SB < 32 ? 1 : SB / 32)), 0, st, (const T*)Q, (const T*)K,
                            (const T*)V, qperm, kperm, pb.N, (int)pb.causal, pb.levels, pb.scale,
                            (T*)Opart, Lpart);
@@ -438,7 +438,7 @@ void launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
         const int span = pb.causal ? pb.chunk : 64;
         const int nspan = (pb.N + span - 1) / span;
         if constexpr (sizeof(EpiSmem<T, D, LP>) <= kLdsBytes)
-        hipLaunchKernelGGL((fwd_epilogue_kernel<T, D, LP>), dim3(nspan, BH), dim3(256), 0, st,
+        ELSAA_LAUNCH("fwd_epilogue", (fwd_epilogue_kernel<T, D, LP>), dim3(nspan, BH), dim3(256), 0, st,
                            (const T*)Q, (const T*)K, (const T*)V, planes_lr, A, z,
                            (const T*)Opart, Lpart, lambda, g_s, g_lr, (T*)O, (T*)O_s, (T*)O_lr,
                            lse, d_lr, pb.H, pb.N, pb.L, span, pb.levels, (int)pb.causal, pb.s,

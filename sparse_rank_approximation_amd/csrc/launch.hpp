@@ -71,6 +71,16 @@ void with_LP(int L, F&& f) {
 #define ELSAA_T(tp) std::remove_pointer_t<decltype(tp)>
 #define ELSAA_C(c) decltype(c)::value
 
+// Per-kernel timing (prof.cpp): every launch goes through ELSAA_LAUNCH.
+void prof_begin(hipStream_t st, const char* name);
+void prof_end(hipStream_t st);
+#define ELSAA_LAUNCH(name, kern, grid, block, lds, st, ...)        \
+  do {                                                             \
+    ::elsaa::prof_begin(st, name);                                 \
+    hipLaunchKernelGGL(kern, grid, block, lds, st, __VA_ARGS__);   \
+    ::elsaa::prof_end(st);                                         \
+  } while (0)
+
 void launch_select(const Problem& pb, const void* Q, const void* K, const float* planes_s,
                    uint16_t* qc, uint16_t* kc, int32_t* qperm, int32_t* kperm, hipStream_t st);
 

@@ -153,7 +153,7 @@ void run_lr_sums(const Problem& pb, const void* X, const void* Y, const float* a
       constexpr int D = ELSAA_C(dc);
       with_LP(pb.L, [&](auto lc) {
         constexpr int LP = ELSAA_C(lc);
-        hipLaunchKernelGGL((lr_sums_kernel<T, D, LP>), dim3(nt, BH), dim3(256), 0, st,
+        ELSAA_LAUNCH("lr_sums", (lr_sums_kernel<T, D, LP>), dim3(nt, BH), dim3(256), 0, st,
                            (const T*)X, (const T*)Y, alpha, beta, planes, pb.H, pb.N, pb.L, TT,
                            pb.scale, pb.tau, S, Z);
       });
@@ -164,7 +164,7 @@ void run_lr_sums(const Problem& pb, const void* X, const void* Y, const float* a
 void run_lr_scan(const Problem& pb, const float* S, const float* Z, int mode, float* A, float* z,
                  hipStream_t st) {
   const int BH = pb.B * pb.H, nt = lr_tiles(pb), per = pb.d * pb.r;
-  hipLaunchKernelGGL(lr_scan_kernel, dim3((per + pb.r + 255) / 256, BH), dim3(256), 0, st, S, Z, A,
+  ELSAA_LAUNCH("lr_scan", lr_scan_kernel, dim3((per + pb.r + 255) / 256, BH), dim3(256), 0, st, S, Z, A,
                      z, nt, per, pb.r, mode);
 }
 

@@ -143,15 +143,15 @@ void launch_select(const Problem& pb, const void* Q, const void* K, const float*
   const int BH = pb.B * pb.H;
   dim3 hg((pb.N + 255) / 256, BH, 2);
   if (pb.bf16)
-    hipLaunchKernelGGL(hash_kernel<__bf16>, hg, dim3(256), 0, st, (const __bf16*)Q,
+    ELSAA_LAUNCH("hash", hash_kernel<__bf16>, hg, dim3(256), 0, st, (const __bf16*)Q,
                        (const __bf16*)K, planes_s, qc, kc, pb.H, pb.N, pb.d, pb.hash_bits);
   else
-    hipLaunchKernelGGL(hash_kernel<float>, hg, dim3(256), 0, st, (const float*)Q,
+    ELSAA_LAUNCH("hash", hash_kernel<float>, hg, dim3(256), 0, st, (const float*)Q,
                        (const float*)K, planes_s, qc, kc, pb.H, pb.N, pb.d, pb.hash_bits);
   const int nseg = pb.causal ? (1 << pb.levels) - 1 : 1;
   const size_t lds = sizeof(int) * ((size_t)kSortWaves * (1 << pb.hash_bits) + 256);
   if (nseg > 0)
-    hipLaunchKernelGGL(sort_kernel, dim3(nseg, BH, 2), dim3(256), lds, st, qc, kc, qperm, kperm,
+    ELSAA_LAUNCH("sort", sort_kernel, dim3(nseg, BH, 2), dim3(256), lds, st, qc, kc, qperm, kperm,
                        pb.N, (int)pb.causal, pb.levels, pb.hash_bits);
 }
 

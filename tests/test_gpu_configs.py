@@ -1,0 +1,86 @@
+"""GPU parity at the full sizes of the five workloads, in the launch configuration
+bench.py times, against the oracle on sampled heads (heads are independent, so
+a sampled head is an exact check of that head). Selections are compared bit for
+bit, outputs and gradients within 1e-4 (fp32) / 2e-2 (bf16) max-relative error.
+The N=65536 workload is checked on its selections (all heads) and forward (one
+head); the oracle's backward there takes about a minute per head, and the same
+kernel shapes (block 256, r 256, d 128) are covered by the backward parity
+cases at N=1024."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import ref
+from parity_util import TOL, cfg_of, rel_err
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU containers
+    pytest.skip("no GPU", allow_module_level=True)
+
+SAMPLES = {
+    2: ([(0, 0), (3, 5), (7, 11)], True),
+    3: ([(0, 0), (1, 31)], True),
+    4: ([(0, 3)], False),
+    5: ([(0, 0), (17, 6), (63, 11)], True),
+}
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_full_size_parity(cid):
+    import sparse_rank_approximation_amd as S
+    w = W.CONFIGS[cid]
+    seed = W.config_seed(cid)
+    heads, with_bwd = SAMPLES.get(cid, ([(0, 0)], True))
+    print(f"[gpu full] config {cid} {w.name}: heads {heads}", flush=True)
+    inp = W.gen_inputs(w, seed)
+    d = {k: v.cuda() for k, v in inp.items()}
+    cfg = cfg_of(w)
+    lam = torch.ones(w.H, device="cuda")
+    qc, kc, qp, kp = S.select(cfg, d["q"], d["k"], d["planes_s"])
+    A, z = S.lowrank_summary(cfg, d["k"], d["v"], d["planes_lr"])
+    o = S.forward(cfg, d["q"], d["k"], d["v"], d["planes_lr"], qp, kp, A, z, lam)
+    g = S.backward(cfg, d["q"], d["k"], d["v"], d["do"], o["O_s"], o["O_lr"], d["planes_lr"], qp,
+                   kp, A, z, o["lse"], o["d_lr"], lam) if with_bwd else None
+    torch.cuda.synchronize()
+    print(f"[gpu full] config {cid}: GPU done", flush=True)
+
+    p = ref.RefParams.from_workload(w)
+    if cid == 4:  # every head's selection
+        allh = [(0, h) for h in range(w.H)]
+        qa = np.stack([inp["q"][b, h].double().numpy() for b, h in allh])
+        ka = np.stack([inp["k"][b, h].double().numpy() for b, h in allh])
+        psa = np.stack([inp["planes_s"][h].numpy() for _, h in allh])
+        _, _, rqp, rkp = ref.select(p, qa, ka, psa)
+        np.testing.assert_array_equal(qp.view(w.H, -1).cpu().numpy(), rqp.reshape(w.H, -1))
+        np.testing.assert_array_equal(kp.view(w.H, -1).cpu().numpy(), rkp.reshape(w.H, -1))
+
+    def take(t):
+        return np.stack([t[b, h].double().numpy() for b, h in heads])
+
+    q, k, v, do = take(inp["q"]), take(inp["k"]), take(inp["v"]), take(inp["do"])
+    ps = np.stack([inp["planes_s"][h].numpy() for _, h in heads])
+    pl = np.stack([inp["planes_lr"][h].numpy() for _, h in heads])
+    rqc, rkc, rqp, rkp = ref.select(p, q, k, ps)
+    for i, (b, h) in enumerate(heads):
+        assert np.array_equal(qc[b, h].cpu().numpy().astype(np.uint16), rqc[i])
+        assert np.array_equal(kc[b, h].cpu().numpy().astype(np.uint16), rkc[i])
+        assert np.array_equal(qp[b, h].cpu().numpy(), rqp[i].reshape(-1))
+        assert np.array_equal(kp[b, h].cpu().numpy(), rkp[i].reshape(-1))
+    ro = ref.forward(p, q, k, v, ps, pl, np.ones(len(heads)))
+
+    def pick(t, shape):
+        return np.stack([t[b, h].float().cpu().numpy() for b, h in heads]).reshape(shape)
+
+    errs = {n: rel_err(pick(o[n], ro[n].shape), ro[n]) for n in ("O", "O_s", "O_lr", "lse", "d_lr")}
+    if with_bwd:
+        rg = ref.backward(p, q, k, v, do, ps, pl, np.ones(len(heads)))
+        errs.update({n: rel_err(pick(g[n], rg[n].shape), rg[n]) for n in ("dQ", "dK", "dV")})
+        errs["dg_s"] = rel_err(pick(g["dg_s"], rg["dg_s"].shape), rg["dg_s"])
+    print(f"[gpu full] config {cid}: errors {errs}", flush=True)
+    tol = TOL[w.dtype]
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, f"config {cid}: errors above {tol}: {bad}"
