@@ -40,7 +40,7 @@ int ilog2(long x) {
 size_t lds_need(const Problem& pb) {
   const size_t e = pb.elem, d = pb.d, kt = pb.s < 32 ? 32 : pb.s;
   const size_t rp = 16 * (size_t)elsaa::padded_tables(pb.L);
-  const size_t sparse = e * (kt * (d + 8) + d * (kt + 8)) + 4 * kt;
+  const size_t sparse = e * 2 * kt * (d + 24) + 4 * kt;
   const size_t epi = e * (d * 72 + 64 * (rp + 8) + d * (rp + 8)) + 4 * rp;
   const size_t sums = e * (rp * 72 + d * 72) + 4 * 64;
   size_t m = sparse > epi ? sparse : epi;

@@ -70,9 +70,12 @@ __device__ __forceinline__ void sum_partials(const T* part, int bh, size_t slots
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < 4; ++g) {
+        float x[4];
+        load4(src + 32 * dt + 8 * g + 4 * h, x);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[dt][g][e] += to_f(src[32 * dt + 8 * g + 4 * h + e]);
+        for (int e = 0; e < 4; ++e) acc[dt][g][e] += x[e];
+      }
   }
 }
 
@@ -89,22 +92,36 @@ __device__ __forceinline__ void finish_row(const T* part, float* scratch, T* out
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+    for (int g = 0; g < 4; ++g) {
+      if (first) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        acc[dt][g][e] = first ? 0.0f : scratch[row + 32 * dt + 8 * g + 4 * h + e];
+        for (int e = 0; e < 4; ++e) acc[dt][g][e] = 0.0f;
+      } else {
+        load4(scratch + row + 32 * dt + 8 * g + 4 * h, acc[dt][g]);
+      }
+    }
   if (first) sum_partials<T, D, QUERY>(part, bh, slots, tok, N, levels, causal, h, acc);
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+    for (int g = 0; g < 4; ++g) {
+      float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v = acc[dt][g][e] + lr[dt][4 * g + e];
-        const size_t o = row + 32 * dt + 8 * g + 4 * h + e;
-        if (last) out[o] = from_f<T>(v);
-        else scratch[o] = v;
-      }
+      for (int e = 0; e < 4; ++e) v[e] = acc[dt][g][e] + lr[dt][4 * g + e];
+      const size_t o = row + 32 * dt + 8 * g + 4 * h;
+      if (last) store4(out + o, v);
+      else store4(scratch + o, v);
+    }
+}
+
+// RT[h][d][p] = R[h][p][d] for p < 4 L, zero up to the row stride pw.
+__global__ void planes_transpose_kernel(const float* __restrict__ R, int L, int D, int pw,
+                                        float* __restrict__ RT) {
+  const int h = blockIdx.x;
+  for (int i = threadIdx.x; i < D * pw; i += blockDim.x) {
+    const int d = i / pw, p = i % pw;
+    RT[(size_t)h * D * pw + i] = p < 4 * L ? R[((size_t)h * 4 * L + p) * D + d] : 0.0f;
+  }
 }
 
 }  // namespace
@@ -168,38 +185,84 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-__global__ void dlam_reduce_kernel(const float* __restrict__ part, int B, int H, int nblk,
-                                   float* __restrict__ dlambda) {
-  const int h = blockIdx.x * blockDim.x + threadIdx.x;
-  if (h >= H) return;
+// dlambda per head: one workgroup per head; thread t sums the entries t, t+256,
+// ... in order, then a fixed pairwise tree in LDS (deterministic).
+__global__ void __launch_bounds__(256) dlam_reduce_kernel(const float* __restrict__ part, int B,
+                                                          int H, int nblk,
+                                                          float* __restrict__ dlambda) {
+  __shared__ float red[256];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int total = B * nblk;
   float s = 0.0f;
-  for (int b = 0; b < B; ++b)
-    for (int k = 0; k < nblk; ++k) s += part[((size_t)b * H + h) * nblk + k];
-  dlambda[h] = s;
+  for (int i = tid; i < total; i += 256) {
+    const int b = i / nblk, k = i % nblk;
+    s += part[((size_t)b * H + h) * nblk + k];
+  }
+  red[tid] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) dlambda[h] = red[0];
 }
 
 // ---------------------------------------------------------------------------
-// Sparse branch, one workgroup per selected block. Wave w owns keys
-// [32 w, 32 w + 32) of the block (their K and V rows stay in registers) and
-// accumulates their dK^T, dV^T over the block's query tiles. Per query tile,
-// S = Q K^T and dP = (c dO) V^T put the wave's keys in lanes, so P and dS are
-// directly the B operands of dV^T += (c dO)^T P and dK^T += Q^T dS; dS goes to LDS
-// and dQ = dS K is formed after a barrier from all keys of the block.
-template <typename T, int D, int SB>
+// Sparse branch, one workgroup per selected block (s queries x s keys).
+// The block's K, V, Q and c dO rows are gathered into LDS row-major (16-byte
+// row-contiguous copies, one barrier); then two kinds of waves work without
+// further synchronisation, reading every operand from LDS (row fragments, or
+// transposed fragments through ds_read_b64_tr_b16):
+//   key waves (32 keys each): S = Q K^T and dP = (c dO) V^T put the keys in lanes,
+//     so P and dS feed dV^T += (c dO)^T P and dK^T += Q^T dS from registers; dV and
+//     dK are accumulated in two passes over the queries to bound register use;
+//   query waves (32 queries each): S^T = K Q^T and dP^T = V (c dO)^T put the
+//     queries in lanes, so dS^T feeds dQ^T += K^T dS^T.
+// ROLE selects key waves (1), query waves (2) or both (3, one launch); with one
+// role per launch only the tiles that role reads are staged.
+template <typename T, int D, int SB, int ROLE>
 struct SbwdSmem {
   static constexpr int KT = SB < 32 ? 32 : SB;
-  T Kt[D][KT + 8];
-  T Qs[32][D + 8];
-  T QsT[D][40];
-  T dOs[32][D + 8];
-  T dOsT[D][40];
-  T dSs[32][KT + 8];
-  float lse[32], Dd[32];
+  static constexpr int LD = tile_ld<T>(D);
+  static constexpr bool HK = (ROLE & 2) != 0;  // all keys staged (query waves)
+  static constexpr bool HQ = (ROLE & 1) != 0;  // all queries staged (key waves)
+  T Ks[HK ? KT : 1][LD];
+  T Vs[HK ? KT : 1][LD];
+  T Qs[HQ ? KT : 1][LD];
+  T Os[HQ ? KT : 1][LD];  // c * dO
+  float lse[KT], Dd[KT], cq[KT];
   int kidx[KT], qidx[KT];
 };
 
-template <typename T, int D, int SB>
-__global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
+template <int SB>
+constexpr int sbwd_threads(int role) {
+  return 64 * (SB < 32 ? 1 : SB / 32) * (role == 3 ? 2 : 1);
+}
+
+// Row fragments of one token row read from global memory, scaled.
+template <typename T, int D>
+__device__ __forceinline__ void row_frags(const T* x, bool valid, float sc,
+                                          typename MF<T>::frag (&f)[D / MF<T>::KSTEP], int h) {
+  typedef MF<T> M;
+#pragma unroll
+  for (int ks = 0; ks < D / M::KSTEP; ++ks) {
+    if (!valid) {
+      f[ks] = M::zero();
+    } else if (sc == 1.0f) {
+      f[ks] = M::load(x + ks * M::KSTEP + M::KPL * h);
+    } else {
+      float v[M::KPL];
+      if constexpr (M::KPL == 8) load8(x + ks * M::KSTEP + M::KPL * h, v);
+      else v[0] = to_f(x[ks * M::KSTEP + M::KPL * h]);
+#pragma unroll
+      for (int e = 0; e < M::KPL; ++e) v[e] *= sc;
+      f[ks] = M::from_floats(v);
+    }
+  }
+}
+
+template <typename T, int D, int SB, int ROLE>
+__global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
     sparse_bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                       const T* __restrict__ dO, const float* __restrict__ lse,
                       const float* __restrict__ rc, const float* __restrict__ rD,
@@ -207,12 +270,15 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
                       int causal, int levels, float scale, T* __restrict__ dQp,
                       T* __restrict__ dKp, T* __restrict__ dVp) {
   typedef MF<T> M;
-  constexpr int KT = SB < 32 ? 32 : SB, NW = KT / 32;
-  __shared__ SbwdSmem<T, D, SB> sm;
+  typedef SbwdSmem<T, D, SB, ROLE> Sm;
+  constexpr int KT = Sm::KT, NW = KT / 32, LD = Sm::LD;
+  constexpr int NT = sbwd_threads<SB>(ROLE);
+  __shared__ Sm sm;
   const int bh = blockIdx.y, item = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const size_t P = perm_stride(N, levels, causal);
   const size_t slots = partial_slots(N, levels, causal);
+  const size_t rowbase = (size_t)bh * N;
 
   const int per_level = causal ? (N / 2) / SB : 0;
   const int nlev_items = causal ? levels * per_level : 0;
@@ -232,124 +298,161 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
     qsrc = qperm + (size_t)bh * P + (size_t)item * SB;
     ksrc = kperm + (size_t)bh * P + (size_t)item * SB;
   }
-  for (int t = tid; t < KT; t += blockDim.x) {
-    sm.kidx[t] = t < SB ? (leaf ? tok0 + t : ksrc[t]) : -1;
-    sm.qidx[t] = t < SB ? (leaf ? tok0 + t : qsrc[t]) : -1;
+  for (int t = tid; t < KT; t += NT) {
+    const int kj = t < SB ? (leaf ? tok0 + t : ksrc[t]) : -1;
+    const int qi = t < SB ? (leaf ? tok0 + t : qsrc[t]) : -1;
+    sm.kidx[t] = kj;
+    sm.qidx[t] = qi;
+    sm.lse[t] = qi >= 0 ? lse[rowbase + qi] : 0.0f;
+    sm.Dd[t] = qi >= 0 ? rD[rowbase + qi] : 0.0f;
+    sm.cq[t] = qi >= 0 ? rc[rowbase + qi] : 0.0f;
   }
   __syncthreads();
-  for (int idx = tid; idx < KT * (D / 8); idx += blockDim.x) {
-    const int t = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-    const int j = sm.kidx[t];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      sm.Kt[c8 + e][t] = j >= 0 ? K[((size_t)bh * N + j) * D + c8 + e] : from_f<T>(0.0f);
+  if constexpr (Sm::HK) {
+    T* const dst[2] = {&sm.Ks[0][0], &sm.Vs[0][0]};
+    const T* const src[2] = {K, V};
+    const float* const sc[2] = {nullptr, nullptr};
+    gather_rows<T, D, KT, NT, 2>(dst, LD, src, sc, sm.kidx, rowbase, tid);
   }
-  const int key = 32 * w + col;
-  const int jk = sm.kidx[key];
-  const bool kvalid = jk >= 0;
-  typename M::frag kf[D / M::KSTEP], vf[D / M::KSTEP];
-#pragma unroll
-  for (int ks = 0; ks < D / M::KSTEP; ++ks) {
-    const size_t o = ((size_t)bh * N + (kvalid ? jk : 0)) * D + ks * M::KSTEP + M::KPL * h;
-    kf[ks] = kvalid ? M::load(K + o) : M::zero();
-    vf[ks] = kvalid ? M::load(V + o) : M::zero();
+  if constexpr (Sm::HQ) {
+    T* const dst[2] = {&sm.Qs[0][0], &sm.Os[0][0]};
+    const T* const src[2] = {Q, dO};
+    const float* const sc[2] = {nullptr, sm.cq};
+    gather_rows<T, D, KT, NT, 2>(dst, LD, src, sc, sm.qidx, rowbase, tid);
   }
-  floatx16 dk[D / 32], dv[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) { dk[dt] = zero16(); dv[dt] = zero16(); }
+  __syncthreads();
 
-  for (int qt = 0; qt < KT / 32; ++qt) {
-    __syncthreads();
-    for (int idx = tid; idx < 32 * (D / 8); idx += blockDim.x) {
-      const int r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-      const int i = sm.qidx[32 * qt + r];
-      float qv[8], ov[8];
-      if (i >= 0) {
-        const size_t o = ((size_t)bh * N + i) * D + c8;
-        const float c = rc[(size_t)bh * N + i];
+  const bool key_wave = (ROLE & 1) && w < NW;
+  if (key_wave) {
+    if constexpr (Sm::HQ) {
+      const int key = 32 * w + col;
+      const int jk = sm.kidx[key];
+      const bool kvalid = jk >= 0;
+      typename M::frag kf[D / M::KSTEP], vf[D / M::KSTEP];
+      if constexpr (Sm::HK) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { qv[e] = to_f(Q[o + e]); ov[e] = c * to_f(dO[o + e]); }
+        for (int ks = 0; ks < D / M::KSTEP; ++ks) kf[ks] = row_frag<T>(&sm.Ks[0][0], LD, 32 * w, 0, ks, lane);
       } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { qv[e] = 0.0f; ov[e] = 0.0f; }
+        row_frags<T, D>(K + (rowbase + (kvalid ? jk : 0)) * D, kvalid, 1.0f, kf, h);
       }
+      const int qt0 = leaf ? w : 0;
+      const size_t ksl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_past(jk, N, lev)
+                                  : (size_t)jk;
+      // Pass 0: dV^T = (c dO)^T P.   Pass 1: dK^T = Q^T dS.
+#pragma unroll 1
+      for (int pass = 0; pass < 2; ++pass) {
+        if (pass == 1) {
+          if constexpr (Sm::HK) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const T a = from_f<T>(qv[e]), b = from_f<T>(ov[e]);
-        sm.Qs[r][c8 + e] = a;
-        sm.QsT[c8 + e][r] = a;
-        sm.dOs[r][c8 + e] = b;
-        sm.dOsT[c8 + e][r] = b;
-      }
-    }
-    if (tid < 32) {
-      const int i = sm.qidx[32 * qt + tid];
-      sm.lse[tid] = i >= 0 ? lse[(size_t)bh * N + i] : 0.0f;
-      sm.Dd[tid] = i >= 0 ? rD[(size_t)bh * N + i] : 0.0f;
-    }
-    __syncthreads();
-    if (!(leaf && qt < w)) {
-      floatx16 s = zero16(), dp = zero16();
-#pragma unroll
-      for (int ks = 0; ks < D / M::KSTEP; ++ks) {
-        const int k0 = ks * M::KSTEP + M::KPL * h;
-        s = M::mma(M::load(&sm.Qs[col][k0]), kf[ks], s);
-        dp = M::mma(M::load(&sm.dOs[col][k0]), vf[ks], dp);
-      }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int qr = acc_row(v, h), qloc = 32 * qt + qr;
-        const bool ok = kvalid && sm.qidx[qloc] >= 0 && !(leaf && key > qloc);
-        const float p = ok ? fast_exp(s[v] * scale - sm.lse[qr]) : 0.0f;
-        s[v] = p;
-        dp[v] = p * (dp[v] - sm.Dd[qr]);
-      }
-#pragma unroll
-      for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
-        const typename M::frag pf = M::from_acc(s, ks2), sf = M::from_acc(dp, ks2);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          dv[dt] = M::mma(M::load_accperm(&sm.dOsT[32 * dt + col][0], ks2, h), pf, dv[dt]);
-          dk[dt] = M::mma(M::load_accperm(&sm.QsT[32 * dt + col][0], ks2, h), sf, dk[dt]);
+            for (int ks = 0; ks < D / M::KSTEP; ++ks) vf[ks] = row_frag<T>(&sm.Vs[0][0], LD, 32 * w, 0, ks, lane);
+          } else {
+            row_frags<T, D>(V + (rowbase + (kvalid ? jk : 0)) * D, kvalid, 1.0f, vf, h);
+          }
         }
-      }
+        floatx16 acc[D / 32];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sm.dSs[acc_row(v, h)][key] = from_f<T>(dp[v]);
-    } else {
+        for (int dt = 0; dt < D / 32; ++dt) acc[dt] = zero16();
+        for (int qt = qt0; qt < KT / 32; ++qt) {
+          floatx16 s = zero16();
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sm.dSs[acc_row(v, h)][key] = from_f<T>(0.0f);
-    }
-    __syncthreads();
-    for (int dt = w; dt < D / 32; dt += NW) {
-      floatx16 acc = zero16();
-      for (int ks = 0; ks < KT / M::KSTEP; ++ks) {
-        const int k0 = ks * M::KSTEP + M::KPL * h;
-        acc = M::mma(M::load(&sm.dSs[col][k0]), M::load(&sm.Kt[32 * dt + col][k0]), acc);
-      }
+          for (int ks = 0; ks < D / M::KSTEP; ++ks)
+            s = M::mma(row_frag<T>(&sm.Qs[0][0], LD, 32 * qt, 0, ks, lane), kf[ks], s);
+          floatx16 dp = zero16();
+          if (pass == 1) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int i = sm.qidx[32 * qt + acc_row(v, h)];
-        if (i >= 0) {
-          const size_t sl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_future_b(i, N, lev)
-                                     : (size_t)i;
-          dQp[((size_t)bh * slots + sl) * D + 32 * dt + col] = from_f<T>(acc[v] * scale);
+            for (int ks = 0; ks < D / M::KSTEP; ++ks)
+              dp = M::mma(row_frag<T>(&sm.Os[0][0], LD, 32 * qt, 0, ks, lane), vf[ks], dp);
+          }
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int qr = 32 * qt + acc_row(v, h);
+            const bool ok = kvalid && sm.qidx[qr] >= 0 && !(leaf && key > qr);
+            const float p = ok ? fast_exp(s[v] * scale - sm.lse[qr]) : 0.0f;
+            s[v] = pass == 0 ? p : p * (dp[v] - sm.Dd[qr]);
+          }
+          const T* X = pass == 0 ? &sm.Os[0][0] : &sm.Qs[0][0];
+#pragma unroll
+          for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
+            const typename M::frag pf = M::from_acc(s, ks2);
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+              acc[dt] = M::mma(tr_frag<T>(X, LD, 32 * qt, 32 * dt, ks2, lane, true), pf, acc[dt]);
+          }
+        }
+        if (kvalid) {
+          T* dst = (pass == 0 ? dVp : dKp) + ((size_t)bh * slots + ksl) * D;
+          const float f = pass == 0 ? 1.0f : scale;
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              float x[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) x[e] = acc[dt][4 * g + e] * f;
+              store4(dst + 32 * dt + 8 * g + 4 * h, x);
+            }
         }
       }
     }
-  }
-  if (kvalid) {
-    const size_t sl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_past(jk, N, lev)
-                               : (size_t)jk;
-    T* kd = dKp + ((size_t)bh * slots + sl) * D;
-    T* vd = dVp + ((size_t)bh * slots + sl) * D;
+  } else {
+    if constexpr (Sm::HK) {
+      const int qw = (ROLE & 1) ? w - NW : w;
+      const int query = 32 * qw + col;
+      const int iq = sm.qidx[query];
+      const bool qvalid = iq >= 0;
+      typename M::frag qf[D / M::KSTEP], of[D / M::KSTEP];
+      if constexpr (Sm::HQ) {
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int d = 32 * dt + acc_row(v, h);
-        kd[d] = from_f<T>(dk[dt][v] * scale);
-        vd[d] = from_f<T>(dv[dt][v]);
+        for (int ks = 0; ks < D / M::KSTEP; ++ks) {
+          qf[ks] = row_frag<T>(&sm.Qs[0][0], LD, 32 * qw, 0, ks, lane);
+          of[ks] = row_frag<T>(&sm.Os[0][0], LD, 32 * qw, 0, ks, lane);
+        }
+      } else {
+        row_frags<T, D>(Q + (rowbase + (qvalid ? iq : 0)) * D, qvalid, 1.0f, qf, h);
+        row_frags<T, D>(dO + (rowbase + (qvalid ? iq : 0)) * D, qvalid, sm.cq[query], of, h);
       }
+      const float lq = sm.lse[query], dq = sm.Dd[query];
+      floatx16 acc[D / 32];
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) acc[dt] = zero16();
+      const int nkt = leaf ? qw + 1 : KT / 32;
+      for (int kt = 0; kt < nkt; ++kt) {
+        floatx16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int ks = 0; ks < D / M::KSTEP; ++ks) {
+          s = M::mma(row_frag<T>(&sm.Ks[0][0], LD, 32 * kt, 0, ks, lane), qf[ks], s);
+          dp = M::mma(row_frag<T>(&sm.Vs[0][0], LD, 32 * kt, 0, ks, lane), of[ks], dp);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int kr = 32 * kt + acc_row(v, h);
+          const bool ok = qvalid && sm.kidx[kr] >= 0 && !(leaf && kr > query);
+          const float p = ok ? fast_exp(s[v] * scale - lq) : 0.0f;
+          s[v] = p * (dp[v] - dq);
+        }
+#pragma unroll
+        for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
+          const typename M::frag sf = M::from_acc(s, ks2);
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+            acc[dt] = M::mma(tr_frag<T>(&sm.Ks[0][0], LD, 32 * kt, 32 * dt, ks2, lane, true), sf, acc[dt]);
+        }
+      }
+      if (qvalid) {
+        const size_t sl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_future_b(iq, N, lev)
+                                   : (size_t)iq;
+        T* dst = dQp + ((size_t)bh * slots + sl) * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = acc[dt][4 * g + e] * scale;
+            store4(dst + 32 * dt + 8 * g + 4 * h, x);
+          }
+      }
+    }
   }
 }
 
@@ -371,8 +474,8 @@ __global__ void __launch_bounds__(256)
                     const float* __restrict__ A, const float* __restrict__ z,
                     const float* __restrict__ re, const float* __restrict__ rdd,
                     const T* __restrict__ dQp, float* __restrict__ scratch, T* __restrict__ dQ,
-                    int H, int N, int L, int span, int levels, int causal, float scale, float tau,
-                    int grp, int first, int last) {
+                    const float* __restrict__ RT, int pw, int H, int N, int L, int span,
+                    int levels, int causal, float scale, float tau, int grp, int first, int last) {
   typedef MF<T> M;
   typedef Features<T, D, LPG> Feat;
   constexpr int RP = 16 * LPG, STEP = 128, NFT = RP / 32;
@@ -405,7 +508,7 @@ __global__ void __launch_bounds__(256)
     }
   }
   for (int idx = tid; idx < RP * D; idx += blockDim.x) {
-    const int f = idx / D, d = idx % D;
+    const int d = idx / RP, f = idx % RP;
     sm.AF[f][d] = from_f<T>(f0 + f < r ? Ac[(size_t)d * r + f0 + f] : 0.0f);
   }
   for (int f = tid; f < RP; f += blockDim.x) sm.zr[f] = f0 + f < r ? zc[f0 + f] : 0.0f;
@@ -424,9 +527,12 @@ __global__ void __launch_bounds__(256)
       for (int idx = tid; idx < STEP * (D / 8); idx += blockDim.x) {
         const int t = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
         const int tk = s0 + t;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          sm.VS[t][c8 + e] = tk < t_end ? V[((size_t)bh * N + tk) * D + c8 + e] : from_f<T>(0.0f);
+        if (tk < t_end) {
+          copy8(&sm.VS[t][c8], V + ((size_t)bh * N + tk) * D + c8);
+        } else {
+          const float zz[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          store8(&sm.VS[t][c8], zz);
+        }
       }
     }
     const int qtok = s0 + 32 * w + col;
@@ -442,8 +548,13 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
       for (int ks = 0; ks < D / M::KSTEP; ++ks) {
         float x[M::KPL];
+        if constexpr (M::KPL == 8) {
+          load8(orow + ks * M::KSTEP + M::KPL * h, x);
+        } else {
+          x[0] = to_f(orow[ks * M::KSTEP + M::KPL * h]);
+        }
 #pragma unroll
-        for (int k = 0; k < M::KPL; ++k) x[k] = e * to_f(orow[ks * M::KSTEP + M::KPL * h + k]);
+        for (int k = 0; k < M::KPL; ++k) x[k] *= e;
         dn[ks] = M::from_floats(x);
       }
     }
@@ -486,7 +597,7 @@ __global__ void __launch_bounds__(256)
       for (int ft = 0; ft < NFT; ++ft) tile_to_table(df[ft], h, dphi[ft]);
       Fq.backward(dphi, da);
       floatx16 dx[D / 32];
-      features_dx<T, D, LPG>(da, pl, Lg, c2, lane, dx);
+      features_dx<T, D, LPG>(da, RT + (size_t)head * D * pw + 32 * grp, pw, c2, lane, dx);
       if (qvalid)
         finish_row<T, D, true>(dQp, scratch, dQ, bh, slots, qtok, N, levels, causal, h, dx,
                                first != 0, last != 0);
@@ -545,9 +656,9 @@ __global__ void __launch_bounds__(256)
                     const float* __restrict__ G, const float* __restrict__ gzs,
                     const float* __restrict__ re, const float* __restrict__ rdd,
                     const T* __restrict__ dKp, const T* __restrict__ dVp, float* __restrict__ scrK,
-                    float* __restrict__ scrV, T* __restrict__ dK, T* __restrict__ dV, int H, int N,
-                    int L, int span, int levels, int causal, float scale, float tau, int grp,
-                    int first, int last) {
+                    float* __restrict__ scrV, T* __restrict__ dK, T* __restrict__ dV,
+                    const float* __restrict__ RT, int pw, int H, int N, int L, int span,
+                    int levels, int causal, float scale, float tau, int grp, int first, int last) {
   typedef MF<T> M;
   typedef Features<T, D, LPG> Feat;
   constexpr int RP = 16 * LPG, STEP = 64, NFT = RP / 32;
@@ -595,25 +706,33 @@ __global__ void __launch_bounds__(256)
       Feat Fq;
       Fq.compute(Q + ((size_t)bh * N + (valid ? tok : t_beg)) * D, valid, pl, Lg, scale, tau, lane);
 #pragma unroll
-      for (int jp = 0; jp < LPG / 2; ++jp)
+      for (int jp = 0; jp < LPG / 2; ++jp) {
+        float x[16];
 #pragma unroll
         for (int b = 0; b < 16; ++b) {
-          const int f = Feat::feat(jp, b, h);
-          const T x = from_f<T>(valid ? Fq.phi[jp][b] : 0.0f);
-          sm.QFT[f][32 * w + col] = x;
-          sm.QF[32 * w + col][f] = x;
+          x[b] = valid ? Fq.phi[jp][b] : 0.0f;
+          sm.QFT[Feat::feat(jp, b, h)][32 * w + col] = from_f<T>(x[b]);
         }
+        store8(&sm.QF[32 * w + col][Feat::feat(jp, 0, h)], *reinterpret_cast<float(*)[8]>(&x[0]));
+        store8(&sm.QF[32 * w + col][Feat::feat(jp, 8, h)], *reinterpret_cast<float(*)[8]>(&x[8]));
+      }
     } else {
       for (int idx = tid - 128; idx < STEP * (D / 8); idx += 128) {
-        const int t = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
+        const int t = idx % STEP, c8 = (idx / STEP) * 8;  // token-fastest transposed stores
         const int tk = s0 + t;
-        const float e = tk < t_end ? re[(size_t)bh * N + tk] : 0.0f;
+        float x[8];
+        if (tk < t_end) {
+          const float e = re[(size_t)bh * N + tk];
+          load8(dO + ((size_t)bh * N + tk) * D + c8, x);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const T x = from_f<T>(tk < t_end ? e * to_f(dO[((size_t)bh * N + tk) * D + c8 + k]) : 0.0f);
-          sm.dnS[t][c8 + k] = x;
-          sm.dnT[c8 + k][t] = x;
+          for (int k = 0; k < 8; ++k) x[k] *= e;
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) x[k] = 0.0f;
         }
+        store8(&sm.dnS[t][c8], x);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sm.dnT[c8 + k][t] = from_f<T>(x[k]);
       }
       for (int t = tid - 128; t < STEP; t += 128)
         sm.dd[t] = s0 + t < t_end ? rdd[(size_t)bh * N + s0 + t] : 0.0f;
@@ -666,7 +785,7 @@ __global__ void __launch_bounds__(256)
       for (int ft = 0; ft < NFT; ++ft) tile_to_table(dkt[ft], h, dphi[ft]);
       Fk.backward(dphi, da);
       floatx16 dx[D / 32];
-      features_dx<T, D, LPG>(da, pl, Lg, c2, lane, dx);
+      features_dx<T, D, LPG>(da, RT + (size_t)head * D * pw + 32 * grp, pw, c2, lane, dx);
       if (kvalid)
         finish_row<T, D, false>(dKp, scrK, dK, bh, slots, ktok, N, levels, causal, h, dx,
                                 first != 0, last != 0);
@@ -736,8 +855,10 @@ __global__ void __launch_bounds__(256)
 
 namespace {
 
+int rt_stride(const Problem& pb);
+
 struct BwdLayout {
-  size_t rows, dlam, parts, gsum, gstate, scratch, total;
+  size_t rows, dlam, parts, gsum, gstate, rt, scratch, total;
   int nblk;
 };
 
@@ -754,14 +875,19 @@ BwdLayout bwd_layout(const Problem& pb) {
   l.parts = off; off += al(3 * BH * slots * D * pb.elem);
   l.gsum = off; off += al(summary_ws_bytes(pb));
   l.gstate = off; off += al(sizeof(float) * BH * pb.nA * (D * pb.r + pb.r));
+  l.rt = off; off += al(sizeof(float) * pb.H * D * rt_stride(pb));
   const int groups = padded_tables(pb.L) > 8 ? 2 : 1;
   l.scratch = off; off += groups > 1 ? al(sizeof(float) * 3 * BH * N * D) : 0;
   l.total = off;
   return l;
 }
 
-template <typename T, int D, int SB>
-constexpr size_t sbwd_lds() { return sizeof(SbwdSmem<T, D, SB>); }
+
+// Row stride of the transposed hyperplanes (covers the reads of every group).
+int rt_stride(const Problem& pb) {
+  const int w = 4 * padded_tables(pb.L);
+  return w < 32 ? 32 : w;
+}
 
 }  // namespace
 
@@ -770,7 +896,7 @@ size_t bwd_ws_bytes(const Problem& pb) { return bwd_layout(pb).total; }
 size_t bwd_lds_need(const Problem& pb) {
   const size_t e = pb.elem, d = pb.d, kt = pb.s < 32 ? 32 : pb.s;
   const size_t rpg = 16 * (size_t)(padded_tables(pb.L) > 8 ? 8 : padded_tables(pb.L));
-  const size_t sb = e * (d * (kt + 8) + 2 * 32 * (d + 8) + 2 * d * 40 + 32 * (kt + 8)) + 8 * 32 + 8 * kt;
+  const size_t sb = e * (2 * kt * (d + 24)) + 20 * kt;  // one-role launch (two tiles)
   const size_t lq = e * (rpg * (d + 8) + rpg * 136 + 128 * (d + 8)) + 4 * rpg;
   const size_t lk = e * (2 * rpg * (d + 8) + rpg * 72 + 64 * (rpg + 8) + 64 * (d + 8) + d * 72) +
                     4 * rpg + 4 * 64;
@@ -803,6 +929,8 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
   float* Gs = (float*)(base + lay.gstate);
   float* gzs = Gs + BH * pb.nA * pb.d * pb.r;
   float* scr = (float*)(base + lay.scratch);
+  float* RT = (float*)(base + lay.rt);
+  const int pw = rt_stride(pb);
   const int groups = padded_tables(pb.L) > 8 ? 2 : 1;
   float* scrQ = scr;
   float* scrK = scr + BH * N * pb.d;
@@ -815,22 +943,34 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
     using T = ELSAA_T(tp);
     with_D(pb.d, [&](auto dc) {
       constexpr int D = ELSAA_C(dc);
+      ELSAA_LAUNCH("planes_t", planes_transpose_kernel, dim3(pb.H), dim3(256), 0, st, planes_lr,
+                   pb.L, pb.d, pw, RT);
       ELSAA_LAUNCH("bwd_rows", (bwd_rows_kernel<T, D>), dim3(lay.nblk, BH), dim3(256), 0, st,
                          (const T*)dO, (const T*)O_s, (const T*)O_lr, lse, d_lr, lambda, g_s,
                          g_lr, pb.eps, pb.H, pb.N, rc, rD, re, rdd, dg_s, dg_lr, dlam_part);
       if (dlambda)
-        ELSAA_LAUNCH("dlam_reduce", dlam_reduce_kernel, dim3((pb.H + 63) / 64), dim3(64), 0, st, dlam_part,
+        ELSAA_LAUNCH("dlam_reduce", dlam_reduce_kernel, dim3(pb.H), dim3(256), 0, st, dlam_part,
                            pb.B, pb.H, lay.nblk, dlambda);
       run_lr_sums(pb, Q, dO, re, rdd, planes_lr, S, Z, st);
       run_lr_scan(pb, S, Z, pb.causal ? 2 : 0, Gs, gzs, st);
       auto run_sparse = [&](auto sc) {
         constexpr int SB = ELSAA_C(sc);
-        if constexpr (sbwd_lds<T, D, SB>() <= kLdsBytes)
-          ELSAA_LAUNCH("sparse_bwd", (sparse_bwd_kernel<T, D, SB>), dim3(items, BH),
-                             dim3(64 * (SB < 32 ? 1 : SB / 32)), 0, st, (const T*)Q,
-                             (const T*)K, (const T*)V, (const T*)dO, lse, rc, rD, qperm, kperm,
-                             pb.N, (int)pb.causal, pb.levels, pb.scale, (T*)dQp, (T*)dKp,
-                             (T*)dVp);
+        const dim3 grid(items, BH);
+        if constexpr (sizeof(SbwdSmem<T, D, SB, 3>) <= kLdsBytes && SB <= 128) {
+          ELSAA_LAUNCH("sparse_bwd", (sparse_bwd_kernel<T, D, SB, 3>), grid,
+                       dim3(sbwd_threads<SB>(3)), 0, st, (const T*)Q, (const T*)K, (const T*)V,
+                       (const T*)dO, lse, rc, rD, qperm, kperm, pb.N, (int)pb.causal, pb.levels,
+                       pb.scale, (T*)dQp, (T*)dKp, (T*)dVp);
+        } else if constexpr (sizeof(SbwdSmem<T, D, SB, 1>) <= kLdsBytes) {
+          ELSAA_LAUNCH("sparse_bwd", (sparse_bwd_kernel<T, D, SB, 1>), grid,
+                       dim3(sbwd_threads<SB>(1)), 0, st, (const T*)Q, (const T*)K, (const T*)V,
+                       (const T*)dO, lse, rc, rD, qperm, kperm, pb.N, (int)pb.causal, pb.levels,
+                       pb.scale, (T*)dQp, (T*)dKp, (T*)dVp);
+          ELSAA_LAUNCH("sparse_bwd_q", (sparse_bwd_kernel<T, D, SB, 2>), grid,
+                       dim3(sbwd_threads<SB>(2)), 0, st, (const T*)Q, (const T*)K, (const T*)V,
+                       (const T*)dO, lse, rc, rD, qperm, kperm, pb.N, (int)pb.causal, pb.levels,
+                       pb.scale, (T*)dQp, (T*)dKp, (T*)dVp);
+        }
       };
       switch (pb.s) {
         case 16: run_sparse(std::integral_constant<int, 16>{}); break;
@@ -847,14 +987,14 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
             ELSAA_LAUNCH("lr_bwd_q", (lr_bwd_q_kernel<T, D, LPG>),
                                dim3((pb.N + span - 1) / span, BH), dim3(256), 0, st, (const T*)Q,
                                (const T*)K, (const T*)V, (const T*)dO, planes_lr, A, z, re, rdd,
-                               (const T*)dQp, scrQ, (T*)dQ, pb.H, pb.N, pb.L, span, pb.levels,
+                               (const T*)dQp, scrQ, (T*)dQ, RT, pw, pb.H, pb.N, pb.L, span, pb.levels,
                                (int)pb.causal, pb.scale, pb.tau, g, first, last);
           if constexpr (sizeof(LbkSmem<T, D, LPG>) <= kLdsBytes)
             ELSAA_LAUNCH("lr_bwd_k", (lr_bwd_k_kernel<T, D, LPG>),
                                dim3((pb.N + span_k - 1) / span_k, BH), dim3(256), 0, st,
                                (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, planes_lr, Gs,
                                gzs, re, rdd, (const T*)dKp, (const T*)dVp, scrK, scrV, (T*)dK,
-                               (T*)dV, pb.H, pb.N, pb.L, span_k, pb.levels, (int)pb.causal,
+                               (T*)dV, RT, pw, pb.H, pb.N, pb.L, span_k, pb.levels, (int)pb.causal,
                                pb.scale, pb.tau, g, first, last);
         }
       };

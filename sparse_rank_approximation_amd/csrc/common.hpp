@@ -91,6 +91,64 @@ struct MF<float> {
   static __device__ __forceinline__ frag from_floats(const float* x) { return x[0]; }
 };
 
+typedef __bf16 bf16x4_tr __attribute__((ext_vector_type(4)));
+
+// Leading dimension (elements) of row-major LDS tiles with D columns. For bf16 a
+// row stride of 12 (mod 64) dwords makes both 16-lane row-fragment reads (lane ->
+// row, 16 bytes each) and transposed reads (4 rows x 32 bytes per 16 lanes) free
+// of bank conflicts, for D = 32, 64 and 128.
+template <typename T>
+__host__ __device__ constexpr int tile_ld(int D) { return sizeof(T) == 2 ? D + 24 : D + 8; }
+
+// Fragment whose lanes run over the COLUMNS of a row-major LDS matrix X (leading
+// dimension ld, in elements) and whose K elements run over its ROWS: lane
+// (n = n0 + lane % 32, half h) receives X[k0 + kofs(e)][n] for e < KPL, with the
+// K order of the accumulator rows (accperm: kofs = acc_row(ks * KPL + e, h)) or the
+// plain order (kofs = ks * KSTEP + KPL h + e). This is the operand of a product
+// that contracts over the rows of X, read without a transposed copy.
+//
+// bf16 uses ds_read_b64_tr_b16: within each 16-lane group, lane s supplies the
+// address of 4 consecutive elements and output lane i, element e receives element
+// i % 4 of lane 4 e + (i % 16) / 4's address; pointing lane s at
+// X[kb + s / 4][nb + 4 (s % 4)] therefore returns X[kb + e][nb + i % 16] in lane i.
+// Two such reads (rows kb .. kb+3 and kb2 .. kb2+3) make the 8 elements.
+template <typename T>
+__device__ __forceinline__ typename MF<T>::frag tr_frag(const T* X, int ld, int k0, int n0, int ks,
+                                                        int lane, bool accperm);
+
+template <>
+__device__ __forceinline__ bf16x8 tr_frag<__bf16>(const __bf16* X, int ld, int k0, int n0, int ks,
+                                                  int lane, bool accperm) {
+  const int s = lane & 15, g = lane >> 4, h = lane >> 5;
+  const int nb = n0 + 16 * (g & 1) + 4 * (s & 3);
+  const int kb1 = k0 + (accperm ? 16 * ks + 4 * h : 16 * ks + 8 * h);
+  const int kb2 = kb1 + (accperm ? 8 : 4);
+  typedef __attribute__((address_space(3))) bf16x4_tr* lds_ptr;
+  const bf16x4_tr a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_ptr)(X + (size_t)(kb1 + (s >> 2)) * ld + nb));
+  const bf16x4_tr b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_ptr)(X + (size_t)(kb2 + (s >> 2)) * ld + nb));
+  bf16x8 f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { f[e] = a[e]; f[4 + e] = b[e]; }
+  return f;
+}
+
+template <>
+__device__ __forceinline__ float tr_frag<float>(const float* X, int ld, int k0, int n0, int ks,
+                                                int lane, bool accperm) {
+  const int h = lane >> 5;
+  const int k = k0 + (accperm ? acc_row(ks, h) : 2 * ks + h);
+  return X[(size_t)k * ld + n0 + (lane & 31)];
+}
+
+// Row fragment from LDS: lane (row r0 + lane % 32, half h) receives
+// X[r0 + lane % 32][k0 + ks * KSTEP + KPL h + e], e < KPL.
+template <typename T>
+__device__ __forceinline__ typename MF<T>::frag row_frag(const T* X, int ld, int r0, int k0, int ks,
+                                                         int lane) {
+  typedef MF<T> M;
+  return M::load(X + (size_t)(r0 + (lane & 31)) * ld + k0 + ks * M::KSTEP + M::KPL * (lane >> 5));
+}
+
 __device__ __forceinline__ floatx16 zero16() {
   floatx16 z;
 #pragma unroll
@@ -103,6 +161,139 @@ __device__ __forceinline__ float to_f(T x) { return (float)x; }
 
 template <typename T>
 __device__ __forceinline__ T from_f(float x) { return (T)x; }
+
+// Vector loads / stores of 4 and 8 consecutive elements (8/16 B for bf16,
+// 16/32 B for fp32), converted to / from fp32. Pointers must be aligned to the
+// access size.
+__device__ __forceinline__ void load4(const __bf16* p, float (&x)[4]) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = (float)v[e];
+}
+__device__ __forceinline__ void load4(const float* p, float (&x)[4]) {
+  const floatx4 v = *reinterpret_cast<const floatx4*>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = v[e];
+}
+__device__ __forceinline__ void store4(__bf16* p, const float (&x)[4]) {
+  bf16x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = (__bf16)x[e];
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ void store4(float* p, const float (&x)[4]) {
+  floatx4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = x[e];
+  *reinterpret_cast<floatx4*>(p) = v;
+}
+__device__ __forceinline__ void load8(const __bf16* p, float (&x)[8]) {
+  const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+}
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const floatx4 a = *reinterpret_cast<const floatx4*>(p);
+  const floatx4 b = *reinterpret_cast<const floatx4*>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+}
+__device__ __forceinline__ void store8(__bf16* p, const float (&x)[8]) {
+  bf16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (__bf16)x[e];
+  *reinterpret_cast<bf16x8*>(p) = v;
+}
+__device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
+  floatx4 a, b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { a[e] = x[e]; b[e] = x[4 + e]; }
+  *reinterpret_cast<floatx4*>(p) = a;
+  *reinterpret_cast<floatx4*>(p + 4) = b;
+}
+// Copy of 8 consecutive elements.
+__device__ __forceinline__ void copy8(__bf16* d, const __bf16* s) {
+  *reinterpret_cast<bf16x8*>(d) = *reinterpret_cast<const bf16x8*>(s);
+}
+__device__ __forceinline__ void copy8(float* d, const float* s) {
+  *reinterpret_cast<floatx4*>(d) = *reinterpret_cast<const floatx4*>(s);
+  *reinterpret_cast<floatx4*>(d + 4) = *reinterpret_cast<const floatx4*>(s + 4);
+}
+
+// 8 consecutive elements held in registers (16 B for bf16, 32 B for fp32).
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<__bf16> {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const __bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
+  }
+  __device__ __forceinline__ void scale(float c) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (__bf16)((float)v[e] * c);
+  }
+  __device__ __forceinline__ void store(__bf16* p) const { *reinterpret_cast<bf16x8*>(p) = v; }
+};
+template <>
+struct Vec8<float> {
+  floatx4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const floatx4*>(p);
+    b = *reinterpret_cast<const floatx4*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { a[e] = 0.0f; b[e] = 0.0f; }
+  }
+  __device__ __forceinline__ void scale(float c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { a[e] *= c; b[e] *= c; }
+  }
+  __device__ __forceinline__ void store(float* p) const {
+    *reinterpret_cast<floatx4*>(p) = a;
+    *reinterpret_cast<floatx4*>(p + 4) = b;
+  }
+};
+
+// Gathers ROWS rows of D elements (row r of tensor t taken from
+// X[t] + (base + idx[r]) * D, zero when idx[r] < 0, optionally multiplied by
+// scale[t][r]) into row-major LDS tiles dst[t] (leading dimension ld) with NT
+// threads. Consecutive threads copy consecutive 16-byte pieces of a row, and
+// every load of a thread is issued before its first store so that the gather
+// costs one memory latency rather than one per row.
+template <typename T, int D, int ROWS, int NT, int NX>
+__device__ __forceinline__ void gather_rows(T* const (&dst)[NX], int ld, const T* const (&X)[NX],
+                                            const float* const (&scale)[NX], const int* idx,
+                                            size_t base, int tid) {
+  constexpr int CH = D / 8, TOT = ROWS * CH, IT = (TOT + NT - 1) / NT;
+  Vec8<T> buf[NX][IT];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int it = tid + i * NT;
+    const int r = it / CH, c8 = (it % CH) * 8;
+    const int j = (it < TOT) ? idx[r] : -1;
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+      if (j >= 0) buf[x][i].load(X[x] + (base + j) * D + c8);
+      else buf[x][i].zero();
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int it = tid + i * NT;
+    if (it < TOT) {
+      const int r = it / CH, c8 = (it % CH) * 8;
+#pragma unroll
+      for (int x = 0; x < NX; ++x) {
+        if (scale[x]) buf[x][i].scale(scale[x][r]);
+        buf[x][i].store(dst[x] + (size_t)r * ld + c8);
+      }
+    }
+  }
+}
 
 // Value of the other lane half (lane ^ 32).
 __device__ __forceinline__ float swap_half(float x) { return __shfl_xor(x, 32, 64); }
@@ -155,8 +346,12 @@ struct Features {
         const int prow = 32 * mt + col;  // projection index of this lane's A row
         float r[M::KPL];
         if (prow < 4 * L) {
+          if constexpr (M::KPL == 8) {
+            load8(planes + (size_t)prow * D + k0, r);
+          } else {
 #pragma unroll
-          for (int e = 0; e < M::KPL; ++e) r[e] = planes[(size_t)prow * D + k0 + e];
+            for (int e = 0; e < M::KPL; ++e) r[e] = planes[(size_t)prow * D + k0 + e];
+          }
         } else {
 #pragma unroll
           for (int e = 0; e < M::KPL; ++e) r[e] = 0.0f;
@@ -260,11 +455,14 @@ __device__ __forceinline__ void tile_to_table(const floatx16& acc, int h, float 
 }
 
 // dX^T (D x 32 tokens, D/32 tiles, columns = lane % 32) = c2 * R^T dA^T, where lane
-// half h holds da[jp][t] for table 2 jp + h of its token and R = planes [L][4][D].
-// This is the last step of the backward through the RACE features:
-// dx = sum_{l,t} da_lt (2 scale / tau) R_lt.
+// half h holds da[jp][t] for table 2 jp + h of its token. This is the last step of
+// the backward through the RACE features: dx = sum_{l,t} da_lt (2 scale / tau) R_lt.
+// The K order of the product (projection p = 4 (2 jp + h) + t for element q of
+// the lane half, jp = q / 4, t = q % 4) is the accumulator-row order, so the
+// hyperplanes are read from RT = R^T ([D][row stride pw] fp32, zero past 4 L) with
+// the same two-run pattern as load_accperm.
 template <typename T, int D, int LP>
-__device__ __forceinline__ void features_dx(const float (&da)[LP / 2][4], const float* planes, int L,
+__device__ __forceinline__ void features_dx(const float (&da)[LP / 2][4], const float* RT, int pw,
                                             float c2, int lane, floatx16 (&dx)[D / 32]) {
   typedef MF<T> M;
   constexpr int NQ = 2 * LP;  // (table, hyperplane) pairs per lane half
@@ -274,7 +472,7 @@ __device__ __forceinline__ void features_dx(const float (&da)[LP / 2][4], const 
   for (int dt = 0; dt < D / 32; ++dt) dx[dt] = zero16();
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    float a[M::KPL], b[M::KPL];
+    float b[M::KPL];
 #pragma unroll
     for (int e = 0; e < M::KPL; ++e) {
       const int q = ks * M::KPL + e, jp = q >> 2, t = q & 3;
@@ -283,10 +481,16 @@ __device__ __forceinline__ void features_dx(const float (&da)[LP / 2][4], const 
     const typename M::frag bf = M::from_floats(b);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
+      const float* row = RT + (size_t)(32 * dt + col) * pw;
+      float a[M::KPL];
+      if constexpr (M::KPL == 8) {
+        float lo[4], hi[4];
+        load4(row + 16 * ks + 4 * h, lo);
+        load4(row + 16 * ks + 8 + 4 * h, hi);
 #pragma unroll
-      for (int e = 0; e < M::KPL; ++e) {
-        const int q = ks * M::KPL + e, jp = q >> 2, t = q & 3, table = 2 * jp + h;
-        a[e] = (q < NQ && table < L) ? planes[(size_t)(4 * table + t) * D + 32 * dt + col] : 0.0f;
+        for (int e = 0; e < 4; ++e) { a[e] = lo[e]; a[4 + e] = hi[e]; }
+      } else {
+        a[0] = row[acc_row(ks, h)];
       }
       dx[dt] = M::mma(M::from_floats(a), bf, dx[dt]);
     }

@@ -34,7 +34,7 @@ __device__ __forceinline__ int compact_future(int i, int N, int l) {
 template <typename T, int D, int SB>
 constexpr size_t sparse_fwd_lds() {
   constexpr int KT = SB < 32 ? 32 : SB;
-  return sizeof(T) * ((size_t)KT * (D + 8) + (size_t)D * (KT + 8)) + sizeof(int) * KT;
+  return sizeof(T) * 2 * (size_t)KT * tile_ld<T>(D) + sizeof(int) * KT;
 }
 
 template <typename T, int D, int SB>
@@ -45,9 +45,9 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
                       float* __restrict__ Lpart) {
   typedef MF<T> M;
   constexpr int KT = SB < 32 ? 32 : SB;  // key rows held in LDS
-  constexpr int PADK = 8, PADV = 8;
-  __shared__ T Ks[KT][D + PADK];
-  __shared__ T Vt[D][KT + PADV];
+  constexpr int LD = tile_ld<T>(D);        // row stride (elements) of the LDS tiles
+  __shared__ T Ks[KT][LD];
+  __shared__ T Vs[KT][LD];
   __shared__ int kidx[KT];
 
   const int bh = blockIdx.y, item = blockIdx.x;
@@ -78,25 +78,13 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
   for (int t = tid; t < KT; t += blockDim.x)
     kidx[t] = t < SB ? (leaf ? tok0 + t : ksrc[t]) : -1;
   __syncthreads();
-  // Gather K rows and V (transposed) into LDS; rows past the block are zero.
-  for (int idx = tid; idx < KT * (D / 8); idx += blockDim.x) {
-    const int t = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-    const int j = kidx[t];
-    float kv[8], vv[8];
-    if (j >= 0) {
-      const T* kr = K + ((size_t)bh * N + j) * D + c8;
-      const T* vr = V + ((size_t)bh * N + j) * D + c8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { kv[e] = to_f(kr[e]); vv[e] = to_f(vr[e]); }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { kv[e] = 0.0f; vv[e] = 0.0f; }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      Ks[t][c8 + e] = from_f<T>(kv[e]);
-      Vt[c8 + e][t] = from_f<T>(vv[e]);
-    }
+  // Gather the block's K and V rows into LDS (row-major, 16-byte row-contiguous
+  // copies, all loads in flight together); rows past the block are zero.
+  {
+    T* const dst[2] = {&Ks[0][0], &Vs[0][0]};
+    const T* const src[2] = {K, V};
+    const float* const sc[2] = {nullptr, nullptr};
+    gather_rows<T, D, KT, 64 * (SB < 32 ? 1 : SB / 32), 2>(dst, LD, src, sc, kidx, (size_t)bh * N, tid);
   }
 
   // This wave's queries (one per lane column).
@@ -121,7 +109,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
     floatx16 sacc = zero16();
 #pragma unroll
     for (int ks = 0; ks < D / M::KSTEP; ++ks)
-      sacc = M::mma(M::load(&Ks[32 * kt + col][ks * M::KSTEP + M::KPL * h]), qf[ks], sacc);
+      sacc = M::mma(row_frag<T>(&Ks[0][0], LD, 32 * kt, 0, ks, lane), qf[ks], sacc);
     float mx = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -152,7 +140,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
       const typename M::frag pf = M::from_acc(sacc, ks2);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
-        o[dt] = M::mma(M::load_accperm(&Vt[32 * dt + col][32 * kt], ks2, h), pf, o[dt]);
+        o[dt] = M::mma(tr_frag<T>(&Vs[0][0], LD, 32 * kt, 32 * dt, ks2, lane, true), pf, o[dt]);
     }
   }
 
@@ -165,9 +153,10 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * dt + 8 * g + 4 * h;
+        float x[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[d0 + e] = from_f<T>(o[dt][4 * g + e] * inv);
+        for (int e = 0; e < 4; ++e) x[e] = o[dt][4 * g + e] * inv;
+        store4(dst + 32 * dt + 8 * g + 4 * h, x);
       }
     if (h == 0) Lpart[(size_t)bh * slots + slot] = mrun + __logf(lrun);
   }
@@ -253,11 +242,17 @@ __global__ void __launch_bounds__(256)
             sm.KF[32 * qt + col][Feat::feat(jp, b, h)] = from_f<T>(valid ? Fk.phi[jp][b] : 0.0f);
       } else {
         for (int idx = lane + 64 * qt; idx < STEP * (D / 8); idx += 128) {
-          const int tk = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
+          const int tk = idx % STEP, c8 = (idx / STEP) * 8;  // token-fastest V^T stores
           const int tok = s0 + tk;
+          float x[8];
+          if (tok < t_end) {
+            load8(V + ((size_t)bh * N + tok) * D + c8, x);
+          } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            sm.VT[c8 + e][tk] = tok < t_end ? V[((size_t)bh * N + tok) * D + c8 + e] : from_f<T>(0.0f);
+            for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sm.VT[c8 + e][tk] = from_f<T>(x[e]);
         }
       }
     }
@@ -366,10 +361,12 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
+          for (int g = 0; g < 4; ++g) {
+            float x[4];
+            load4(src + dbase + 32 * dt + 8 * g + 4 * h, x);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              os[dt][g][e] += wk * to_f(src[dbase + 32 * dt + 8 * g + 4 * h + e]);
+            for (int e = 0; e < 4; ++e) os[dt][g][e] += wk * x[e];
+          }
       }
       const float m = 1.0f / (1.0f + fast_exp(__logf(lam * den + eps) - lse));
       const float g1 = gs ? gs[(size_t)bh * N + i] : 1.0f;
@@ -380,15 +377,18 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
+          for (int g = 0; g < 4; ++g) {
+            const int dd = dbase + 32 * dt + 8 * g + 4 * h;
+            float xo[4], xl[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int dd = dbase + 32 * dt + 8 * g + 4 * h + e;
-              const float olr = num[dt][4 * g + e] * dinv;
-              O[row + dd] = from_f<T>(g1 * m * os[dt][g][e] + g2 * olr);
-              Os[row + dd] = from_f<T>(os[dt][g][e]);
-              Olr[row + dd] = from_f<T>(olr);
+              xl[e] = num[dt][4 * g + e] * dinv;
+              xo[e] = g1 * m * os[dt][g][e] + g2 * xl[e];
             }
+            store4(O + row + dd, xo);
+            store4(Os + row + dd, os[dt][g]);
+            store4(Olr + row + dd, xl);
+          }
         if (h == 0 && dh == 0) {
           lse_out[(size_t)bh * N + i] = lse;
           dlr_out[(size_t)bh * N + i] = den;

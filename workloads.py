@@ -36,7 +36,7 @@ class Workload:
     gen: str            # Q/K generator kind
     gen_args: dict = field(default_factory=dict)
     lr_bits: int = 4
-    chunk: int = 128    # causal RACE summary spacing
+    chunk: int = 512    # causal RACE summary spacing
 
     @property
     def hash_bits(self) -> int:
