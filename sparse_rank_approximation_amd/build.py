@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libelsaa.so")
-SOURCES = ["select.hip", "lowrank.hip", "fwd.hip", "bwd.hip", "api.cpp", "prof.cpp"]
+SOURCES = ["select.hip", "lowrank.hip", "fwd.hip", "bwd.hip", "merge.hip", "api.cpp", "prof.cpp"]
 HEADERS = ["common.hpp", "launch.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -38,12 +38,10 @@ int ilog2(long x) {
 
 // LDS each kernel family would need for these parameters (bytes).
 size_t lds_need(const Problem& pb) {
-  const size_t e = pb.elem, d = pb.d, kt = pb.s < 32 ? 32 : pb.s;
+  const size_t e = pb.elem, d = pb.d;
   const size_t rp = 16 * (size_t)elsaa::padded_tables(pb.L);
-  const size_t sparse = e * 2 * kt * (d + 24) + 4 * kt;
-  const size_t epi = e * (d * 72 + 64 * (rp + 8) + d * (rp + 8)) + 4 * rp;
   const size_t sums = e * (rp * 72 + d * 72) + 4 * 64;
-  size_t m = sparse > epi ? sparse : epi;
+  size_t m = elsaa::fwd_lds_need(pb);
   if (sums > m) m = sums;
   const size_t bwd = elsaa::bwd_lds_need(pb);
   return bwd > m ? bwd : m;

@@ -46,72 +46,88 @@ __device__ __forceinline__ int compact_past(int j, int N, int l) {
   return (j / n) * (n >> 1) + (j % n);
 }
 
-// Accumulates, for this lane's token and the D-layout rows of every 32-row tile
-// (d = 32 dt + 8 g + 4 h + e), the sum of the token's sparse partial slots:
-// leaf/own slot, then each level where the token is a query of a future half
-// (QUERY) or a key of a past half (!QUERY).
-template <typename T, int D, bool QUERY>
-__device__ __forceinline__ void sum_partials(const T* part, int bh, size_t slots, int tok, int N,
-                                             int levels, bool causal, int h,
-                                             float (&acc)[D / 32][4][4]) {
-  const int logN = 31 - __clz(N);
-  for (int l = -1; l < levels; ++l) {
-    size_t sl;
-    if (l < 0) {
-      sl = (size_t)tok;
-    } else {
-      if (!causal) break;
-      const bool fut = (tok >> (logN - 1 - l)) & 1;
-      if (QUERY != fut) continue;
-      sl = (size_t)N + (size_t)l * (N / 2) +
-           (QUERY ? compact_future_b(tok, N, l) : compact_past(tok, N, l));
-    }
-    const T* src = part + ((size_t)bh * slots + sl) * D;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float x[4];
-        load4(src + 32 * dt + 8 * g + 4 * h, x);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[dt][g][e] += x[e];
-      }
-  }
-}
-
-// Final write of one gradient row held in D layout (lane = token, rows = d):
-// value = (first ? sparse partial sum : fp32 running sum) + lr, stored as T
-// (last) or kept as the fp32 running sum for the next feature group.
-template <typename T, int D, bool QUERY>
-__device__ __forceinline__ void finish_row(const T* part, float* scratch, T* out, int bh,
-                                           size_t slots, int tok, int N, int levels, bool causal,
-                                           int h, const floatx16 (&lr)[D / 32], bool first,
-                                           bool last) {
-  float acc[D / 32][4][4];
-  const size_t row = ((size_t)bh * N + tok) * D;
+// Writes the low-rank part of one gradient row held in the accumulator layout
+// (lane = token): lr + the fp32 running sum of earlier feature groups (unless
+// first), stored as T (last group) or as the fp32 running sum. The sparse partial
+// rows are added afterwards (combine_kernel).
+template <typename T, int D>
+__device__ __forceinline__ void write_grad_row(const floatx16 (&lr)[D / 32], float* scratch, T* out,
+                                               size_t row, int h, bool first, bool last) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      if (first) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[dt][g][e] = 0.0f;
-      } else {
-        load4(scratch + row + 32 * dt + 8 * g + 4 * h, acc[dt][g]);
-      }
-    }
-  if (first) sum_partials<T, D, QUERY>(part, bh, slots, tok, N, levels, causal, h, acc);
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      float v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = acc[dt][g][e] + lr[dt][4 * g + e];
       const size_t o = row + 32 * dt + 8 * g + 4 * h;
+      float v[4];
+      if (!first) load4(scratch + o, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (first ? 0.0f : v[e]) + lr[dt][4 * g + e];
       if (last) store4(out + o, v);
       else store4(scratch + o, v);
     }
+}
+
+// Loads the running RACE statistics of a walk (fp32 [channel][feature] rows of
+// length r, features f0 .. f0 + RP) into fp32 D tiles st (rows = channels, lanes =
+// features; tile w + 4 i of this wave) and their operand copy SF[feature][channel].
+template <typename T, int D, int LP, int SPW>
+__device__ __forceinline__ void load_stats(const float* Ac, int r, int f0, int w, int lane,
+                                           floatx16 (&st)[SPW], T* SF, int ldd) {
+  constexpr int NFT = LP / 2, NST = (D / 32) * NFT;
+  const int h = lane >> 5, col = lane & 31;
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    const int tix = w + 4 * i;
+    st[i] = zero16();
+    if (tix < NST) {
+      const int mt = tix / NFT, f = f0 + 32 * (tix % NFT) + col;
+      if (f < r)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) st[i][v] = Ac[(size_t)(32 * mt + acc_row(v, h)) * r + f];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    const int tix = w + 4 * i;
+    if (tix < NST) {
+      const int mt = tix / NFT, fl = 32 * (tix % NFT) + col;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = st[i][4 * g + e];
+        store4(SF + (size_t)fl * ldd + 32 * mt + 8 * g + 4 * h, x);
+      }
+    }
+  }
+}
+
+// st += X^T F over the STEP rows of the step (X: [token][channel], F:
+// [token][feature], both row-major in LDS), then the operand copy SF.
+template <typename T, int D, int LP, int SPW, int STEP>
+__device__ __forceinline__ void advance_stats(const T* X, int ldd, const T* F, int ldr, int w,
+                                              int lane, floatx16 (&st)[SPW], T* SF) {
+  typedef MF<T> M;
+  constexpr int NFT = LP / 2, NST = (D / 32) * NFT;
+  const int h = lane >> 5, col = lane & 31;
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    const int tix = w + 4 * i;
+    if (tix < NST) {
+      const int mt = tix / NFT, nt = tix % NFT;
+#pragma unroll
+      for (int ks = 0; ks < STEP / M::KSTEP; ++ks)
+        st[i] = M::mma(tr_frag<T>(X, ldd, 0, 32 * mt, ks, lane, false),
+                       tr_frag<T>(F, ldr, 0, 32 * nt, ks, lane, false), st[i]);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = st[i][4 * g + e];
+        store4(SF + (size_t)(32 * nt + col) * ldd + 32 * mt + 8 * g + 4 * h, x);
+      }
+    }
+  }
 }
 
 // RT[h][d][p] = R[h][p][d] for p < 4 L, zero up to the row stride pw.
@@ -457,17 +473,11 @@ __global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
 }
 
 // ---------------------------------------------------------------------------
-// Low-rank branch, query side. 128 tokens per step, wave w owns query tile w.
-template <typename T, int D, int LPG>
-struct LbqSmem {
-  static constexpr int RP = 16 * LPG, STEP = 128;
-  T AF[RP][D + 8];      // running key statistics A = sum phi(K) V^T, [feature][channel]
-  T KFT[RP][STEP + 8];  // phi(K) of the step's keys, [feature][key]
-  T VS[STEP][D + 8];    // V of the step's keys
-  float zr[RP];         // running sum of phi(K)
-};
-
-template <typename T, int D, int LPG>
+// Low-rank branch, query side: one head and span per workgroup, walked forwards in
+// steps of STEP tokens by 4 waves; wave w < STEP / 32 owns the step's query tile w.
+// LDS (WalkSmem): V (XS) and phi(K) (FS) of the step's keys, the running key
+// statistics S = sum_j phi(K_j) V_j^T (SF) and z (zr).
+template <typename T, int D, int LPG, int STEP>
 __global__ void __launch_bounds__(256)
     lr_bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                     const T* __restrict__ dO, const float* __restrict__ planes,
@@ -478,178 +488,164 @@ __global__ void __launch_bounds__(256)
                     int levels, int causal, float scale, float tau, int grp, int first, int last) {
   typedef MF<T> M;
   typedef Features<T, D, LPG> Feat;
-  constexpr int RP = 16 * LPG, STEP = 128, NFT = RP / 32;
-  constexpr int NST = NFT * (D / 32), SPW = (NST + 3) / 4;
-  __shared__ LbqSmem<T, D, LPG> sm;
+  typedef WalkSmem<T, D, LPG, STEP> Sm;
+  constexpr int RP = 16 * LPG, NFT = RP / 32, LDD = Sm::LDD, LDR = Sm::LDR;
+  constexpr int QT = STEP / 32, NST = NFT * (D / 32), SPW = (NST + 3) / 4;
+  constexpr int VCH = D / 8, VIT = (STEP * VCH + 255) / 256;
+  __shared__ Sm sm;
   const int bh = blockIdx.y, c = blockIdx.x, head = bh % H;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int r = 16 * L, f0 = 128 * grp, Lg = min(8, L - 8 * grp);
   const float* pl = planes + ((size_t)head * L + 8 * grp) * 4 * D;
   const int t_beg = c * span, t_end = min(N, t_beg + span);
-  const size_t slots = partial_slots(N, levels, causal);
   const float c2 = 2.0f * scale / tau;
   const size_t sidx = causal ? (size_t)bh * (N / span) + c : (size_t)bh;
-  const float* Ac = A + sidx * D * r;
-  const float* zc = z + sidx * r;
+  const T* Qh = Q + (size_t)bh * N * D;
+  const T* Kh = K + (size_t)bh * N * D;
+  const T* Vh = V + (size_t)bh * N * D;
+  const T* dOh = dO + (size_t)bh * N * D;
+  const bool qwave = w < QT;
 
-  // State tiles (ft, dt): D layout with lanes = channels, rows = features.
   floatx16 st[SPW];
+  load_stats<T, D, LPG, SPW>(A + sidx * D * r, r, f0, w, lane, st, &sm.SF[0][0], LDD);
+  for (int f = tid; f < RP; f += 256) sm.zr[f] = f0 + f < r ? z[sidx * r + f0 + f] : 0.0f;
+
+  typename M::frag qx[D / M::KSTEP], ox[D / M::KSTEP], kx[D / M::KSTEP];
+  Vec8<T> vb[VIT];
+  float eq = 0.0f, ddq = 0.0f;
+  auto load_rows = [&](int s0) __attribute__((always_inline)) {
+    const int tok = s0 + 32 * w + col;
+    const bool valid = qwave && tok < t_end;
+    const size_t rrow = (size_t)min(tok, N - 1) * D;
+    load_row_frags<T, D>(Qh + rrow, valid, qx, h);
+    load_row_frags<T, D>(dOh + rrow, valid, ox, h);
+    eq = re[(size_t)bh * N + min(tok, N - 1)];
+    ddq = rdd[(size_t)bh * N + min(tok, N - 1)];
+    if (!valid) eq = ddq = 0.0f;
+    if (causal) {
+      load_row_frags<T, D>(Kh + rrow, valid, kx, h);
 #pragma unroll
-  for (int i = 0; i < SPW; ++i) {
-    st[i] = zero16();
-    const int tix = w + 4 * i;
-    if (causal && tix < NST) {
-      const int dt = tix % (D / 32), ft = tix / (D / 32), d = 32 * dt + col;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int f = f0 + 32 * ft + acc_row(v, h);
-        st[i][v] = f < r ? Ac[(size_t)d * r + f] : 0.0f;
+      for (int i = 0; i < VIT; ++i) {
+        const int it = tid + 256 * i, t = it / VCH, tk = s0 + t;
+        vb[i].load_if(Vh + (size_t)min(tk, N - 1) * D + (it % VCH) * 8,
+                      it < STEP * VCH && tk < t_end);
       }
     }
-  }
-  for (int idx = tid; idx < RP * D; idx += blockDim.x) {
-    const int d = idx / RP, f = idx % RP;
-    sm.AF[f][d] = from_f<T>(f0 + f < r ? Ac[(size_t)d * r + f0 + f] : 0.0f);
-  }
-  for (int f = tid; f < RP; f += blockDim.x) sm.zr[f] = f0 + f < r ? zc[f0 + f] : 0.0f;
+  };
+  load_rows(t_beg);
 
   for (int s0 = t_beg; s0 < t_end; s0 += STEP) {
+    const int qtok = s0 + 32 * w + col;
+    const bool qvalid = qwave && qtok < t_end;
     if (causal) {
-      const int tok = s0 + 32 * w + col;
-      const bool valid = tok < t_end;
-      Feat Fk;
-      Fk.compute(K + ((size_t)bh * N + (valid ? tok : t_beg)) * D, valid, pl, Lg, scale, tau, lane);
+      if (qwave) {
+        Feat Fk;
+        Fk.compute(kx, pl, Lg, scale, tau, lane);
 #pragma unroll
-      for (int jp = 0; jp < LPG / 2; ++jp)
+        for (int jp = 0; jp < LPG / 2; ++jp) {
+          float x0[8], x1[8];
 #pragma unroll
-        for (int b = 0; b < 16; ++b)
-          sm.KFT[Feat::feat(jp, b, h)][32 * w + col] = from_f<T>(valid ? Fk.phi[jp][b] : 0.0f);
-      for (int idx = tid; idx < STEP * (D / 8); idx += blockDim.x) {
-        const int t = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-        const int tk = s0 + t;
-        if (tk < t_end) {
-          copy8(&sm.VS[t][c8], V + ((size_t)bh * N + tk) * D + c8);
-        } else {
-          const float zz[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-          store8(&sm.VS[t][c8], zz);
+          for (int b = 0; b < 8; ++b) {
+            x0[b] = qvalid ? Fk.phi[jp][b] : 0.0f;
+            x1[b] = qvalid ? Fk.phi[jp][8 + b] : 0.0f;
+          }
+          store8(&sm.FS[32 * w + col][Feat::feat(jp, 0, h)], x0);
+          store8(&sm.FS[32 * w + col][Feat::feat(jp, 8, h)], x1);
         }
       }
+#pragma unroll
+      for (int i = 0; i < VIT; ++i) {
+        const int it = tid + 256 * i;
+        if (it < STEP * VCH) vb[i].store(&sm.XS[it / VCH][(it % VCH) * 8]);
+      }
     }
-    const int qtok = s0 + 32 * w + col;
-    const bool qvalid = qtok < t_end;
     Feat Fq;
-    Fq.compute(Q + ((size_t)bh * N + (qvalid ? qtok : t_beg)) * D, qvalid, pl, Lg, scale, tau, lane);
     typename M::frag dn[D / M::KSTEP];
-    float ddq = 0.0f;
-    {
-      const float e = qvalid ? re[(size_t)bh * N + qtok] : 0.0f;
-      ddq = qvalid ? rdd[(size_t)bh * N + qtok] : 0.0f;
-      const T* orow = dO + ((size_t)bh * N + (qvalid ? qtok : t_beg)) * D;
+    if (qwave) {
+      Fq.compute(qx, pl, Lg, scale, tau, lane);
 #pragma unroll
       for (int ks = 0; ks < D / M::KSTEP; ++ks) {
         float x[M::KPL];
         if constexpr (M::KPL == 8) {
-          load8(orow + ks * M::KSTEP + M::KPL * h, x);
-        } else {
-          x[0] = to_f(orow[ks * M::KSTEP + M::KPL * h]);
-        }
 #pragma unroll
-        for (int k = 0; k < M::KPL; ++k) x[k] *= e;
+          for (int e = 0; e < 8; ++e) x[e] = (float)ox[ks][e] * eq;
+        } else {
+          x[0] = ox[ks] * eq;
+        }
         dn[ks] = M::from_floats(x);
       }
     }
     __syncthreads();
 
-    // dphi(Q)^T tiles: rows = features of tables (2 ft, 2 ft + 1), columns = queries.
-    floatx16 df[NFT];
+    if (qwave) {
+      // Sparse dQ partials of this query (first group only), loads in flight
+      // during the products below.
+      // dphi(Q)^T (rows = features, columns = queries) = S dnum^T + z dd^T + the
+      // causally masked part of the step.
+      floatx16 df[NFT];
 #pragma unroll
-    for (int ft = 0; ft < NFT; ++ft) {
-      df[ft] = zero16();
-#pragma unroll
-      for (int ks = 0; ks < D / M::KSTEP; ++ks)
-        df[ft] = M::mma(M::load(&sm.AF[32 * ft + col][ks * M::KSTEP + M::KPL * h]), dn[ks], df[ft]);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) df[ft][v] += sm.zr[32 * ft + acc_row(v, h)] * ddq;
-    }
-    if (causal) {
-      for (int kt = 0; kt <= w; ++kt) {
-        floatx16 gt = zero16();
+      for (int ft = 0; ft < NFT; ++ft) {
+        df[ft] = zero16();
 #pragma unroll
         for (int ks = 0; ks < D / M::KSTEP; ++ks)
-          gt = M::mma(M::load(&sm.VS[32 * kt + col][ks * M::KSTEP + M::KPL * h]), dn[ks], gt);
+          df[ft] = M::mma(row_frag<T>(&sm.SF[0][0], LDD, 32 * ft, 0, ks, lane), dn[ks], df[ft]);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          gt[v] += ddq;
-          if (kt == w && acc_row(v, h) > col) gt[v] = 0.0f;
-        }
+        for (int v = 0; v < 16; ++v) df[ft][v] += sm.zr[32 * ft + acc_row(v, h)] * ddq;
+      }
+      if (causal) {
+        for (int kt = 0; kt <= w; ++kt) {
+          floatx16 gt = zero16();
 #pragma unroll
-        for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
-          const typename M::frag gf = M::from_acc(gt, ks2);
+          for (int ks = 0; ks < D / M::KSTEP; ++ks)
+            gt = M::mma(row_frag<T>(&sm.XS[0][0], LDD, 32 * kt, 0, ks, lane), dn[ks], gt);
 #pragma unroll
-          for (int ft = 0; ft < NFT; ++ft)
-            df[ft] = M::mma(M::load_accperm(&sm.KFT[32 * ft + col][32 * kt], ks2, h), gf, df[ft]);
+          for (int v = 0; v < 16; ++v) {
+            gt[v] += ddq;
+            if (kt == w && acc_row(v, h) > col) gt[v] = 0.0f;
+          }
+#pragma unroll
+          for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
+            const typename M::frag gf = M::from_acc(gt, ks2);
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft)
+              df[ft] = M::mma(tr_frag<T>(&sm.FS[0][0], LDR, 32 * kt, 32 * ft, ks2, lane, true), gf, df[ft]);
+          }
         }
       }
-    }
-    {
-      float dphi[LPG / 2][16], da[LPG / 2][4];
+      float da[LPG / 2][4];
 #pragma unroll
-      for (int ft = 0; ft < NFT; ++ft) tile_to_table(df[ft], h, dphi[ft]);
-      Fq.backward(dphi, da);
+      for (int ft = 0; ft < NFT; ++ft) {
+        float dphi[16];
+        tile_to_table(df[ft], h, dphi);
+        Fq.backward_table(ft, dphi, da[ft]);
+      }
       floatx16 dx[D / 32];
       features_dx<T, D, LPG>(da, RT + (size_t)head * D * pw + 32 * grp, pw, c2, lane, dx);
       if (qvalid)
-        finish_row<T, D, true>(dQp, scratch, dQ, bh, slots, qtok, N, levels, causal, h, dx,
-                               first != 0, last != 0);
+        write_grad_row<T, D>(dx, scratch, dQ, ((size_t)bh * N + qtok) * D, h, first != 0,
+                             last != 0);
     }
+    load_rows(s0 + STEP);  // past the span: loads nothing
+    if (!causal) break;
     __syncthreads();
-
-    if (causal) {
-#pragma unroll
-      for (int i = 0; i < SPW; ++i) {
-        const int tix = w + 4 * i;
-        if (tix < NST) {
-          const int dt = tix % (D / 32), ft = tix / (D / 32);
-#pragma unroll
-          for (int ks = 0; ks < STEP / M::KSTEP; ++ks) {
-            const int k0 = ks * M::KSTEP + M::KPL * h;
-            float vb[M::KPL];
-#pragma unroll
-            for (int k = 0; k < M::KPL; ++k) vb[k] = to_f(sm.VS[k0 + k][32 * dt + col]);
-            st[i] = M::mma(M::load(&sm.KFT[32 * ft + col][k0]), M::from_floats(vb), st[i]);
-          }
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            sm.AF[32 * ft + acc_row(v, h)][32 * dt + col] = from_f<T>(st[i][v]);
-        }
-      }
-      for (int f = tid; f < RP; f += blockDim.x) {
-        float zs = 0.0f;
-        for (int t = 0; t < STEP; ++t) zs += to_f(sm.KFT[f][t]);
-        sm.zr[f] += zs;
-      }
+    advance_stats<T, D, LPG, SPW, STEP>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, w, lane, st, &sm.SF[0][0]);
+    for (int f = tid; f < RP; f += 256) {
+      float zs = 0.0f;
+#pragma unroll 8
+      for (int t = 0; t < STEP; ++t) zs += to_f(sm.FS[t][f]);
+      sm.zr[f] += zs;
     }
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
-// Low-rank branch, key side. 64 tokens per step walked from the end of the chunk;
-// wave w owns key tile kt = w / 2 and computes dK (w even) or dV (w odd).
-template <typename T, int D, int LPG>
-struct LbkSmem {
-  static constexpr int RP = 16 * LPG, STEP = 64;
-  T GF[RP][D + 8];      // running query statistics G = sum phi(Q) dnum^T, [feature][channel]
-  T GT[D][RP + 8];      // the same, [channel][feature]
-  T QFT[RP][STEP + 8];  // phi(Q) of the step's queries, [feature][query]
-  T QF[STEP][RP + 8];   // [query][feature]
-  T dnS[STEP][D + 8];   // dnum of the step's queries
-  T dnT[D][STEP + 8];
-  float gz[RP];         // running sum of phi(Q) dd_lr
-  float dd[STEP];
-};
-
-template <typename T, int D, int LPG>
+// Low-rank branch, key side: one head and span per workgroup, walked backwards in
+// steps of STEP tokens by 4 waves: wave w handles key tile kt = w % (STEP / 32) for
+// dK (w < STEP / 32) or dV (the next STEP / 32 waves). LDS (WalkSmem): dnum (XS) and
+// phi(Q) (FS) of the step's queries, dd_lr of the step (dd), the running query
+// statistics G = sum_i phi(Q_i) dnum_i^T (SF) and g = sum_i phi(Q_i) dd_lr,i (zr).
+template <typename T, int D, int LPG, int STEP>
 __global__ void __launch_bounds__(256)
     lr_bwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                     const T* __restrict__ dO, const float* __restrict__ planes,
@@ -661,111 +657,120 @@ __global__ void __launch_bounds__(256)
                     int levels, int causal, float scale, float tau, int grp, int first, int last) {
   typedef MF<T> M;
   typedef Features<T, D, LPG> Feat;
-  constexpr int RP = 16 * LPG, STEP = 64, NFT = RP / 32;
-  constexpr int NST = NFT * (D / 32), SPW = (NST + 3) / 4;
-  __shared__ LbkSmem<T, D, LPG> sm;
+  typedef WalkSmem<T, D, LPG, STEP> Sm;
+  constexpr int RP = 16 * LPG, NFT = RP / 32, LDD = Sm::LDD, LDR = Sm::LDR;
+  constexpr int QT = STEP / 32, NST = NFT * (D / 32), SPW = (NST + 3) / 4;
+  constexpr int VCH = D / 8, NDW = QT < 2 ? 1 : QT;  // dO staging waves
+  constexpr int OIT = (STEP * VCH + 64 * NDW - 1) / (64 * NDW);
+  __shared__ Sm sm;
   const int bh = blockIdx.y, c = blockIdx.x, head = bh % H;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, col = lane & 31;
-  const int kt = w >> 1, part = w & 1;
+  const int kt = w % QT, role = w / QT;  // role 0: dK, 1: dV, 2+: staging only
   const int r = 16 * L, f0 = 128 * grp, Lg = min(8, L - 8 * grp);
   const float* pl = planes + ((size_t)head * L + 8 * grp) * 4 * D;
   const int t_beg = c * span, t_end = min(N, t_beg + span);
-  const size_t slots = partial_slots(N, levels, causal);
   const float c2 = 2.0f * scale / tau;
   const size_t sidx = causal ? (size_t)bh * (N / span) + c : (size_t)bh;
-  const float* Gc = G + sidx * D * r;
-  const float* gc = gzs + sidx * r;
+  const T* Qh = Q + (size_t)bh * N * D;
+  const T* Kh = K + (size_t)bh * N * D;
+  const T* Vh = V + (size_t)bh * N * D;
+  const T* dOh = dO + (size_t)bh * N * D;
+  const bool kwave = role < 2;
+  // dO staging: waves QT .. QT + NDW - 1 (waves 1 .. 2 when QT == 1).
+  const int ow = QT < 2 ? w - 1 : w - QT;
+  const bool owave = ow >= 0 && ow < NDW;
 
-  // State tiles (mt, nt): G^T with lanes = features, rows = channels.
   floatx16 st[SPW];
-#pragma unroll
-  for (int i = 0; i < SPW; ++i) {
-    st[i] = zero16();
-    const int tix = w + 4 * i;
-    if (causal && tix < NST) {
-      const int mt = tix / NFT, nt = tix % NFT, f = f0 + 32 * nt + col;
-      if (f < r)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) st[i][v] = Gc[(size_t)(32 * mt + acc_row(v, h)) * r + f];
-    }
-  }
-  for (int idx = tid; idx < RP * D; idx += blockDim.x) {
-    const int d = idx / RP, f = idx % RP;
-    const T x = from_f<T>(f0 + f < r ? Gc[(size_t)d * r + f0 + f] : 0.0f);
-    sm.GT[d][f] = x;
-    sm.GF[f][d] = x;
-  }
-  for (int f = tid; f < RP; f += blockDim.x) sm.gz[f] = f0 + f < r ? gc[f0 + f] : 0.0f;
+  load_stats<T, D, LPG, SPW>(G + sidx * D * r, r, f0, w, lane, st, &sm.SF[0][0], LDD);
+  for (int f = tid; f < RP; f += 256) sm.zr[f] = f0 + f < r ? gzs[sidx * r + f0 + f] : 0.0f;
 
+  typename M::frag qx[D / M::KSTEP], kx[D / M::KSTEP], vx[D / M::KSTEP];
+  Vec8<T> ob[OIT];
+  float oe[OIT];
+  float ddv = 0.0f;
+  auto load_rows = [&](int s0) __attribute__((always_inline)) {
+    const bool live = s0 >= t_beg;
+    const int qtok = s0 + 32 * w + col;  // query tile w (waves < QT) for phi(Q)
+    load_row_frags<T, D>(Qh + (size_t)min(max(qtok, 0), N - 1) * D, live && w < QT && qtok < t_end,
+                         qx, h);
+    const int ktok = s0 + 32 * kt + col;
+    const size_t krow = (size_t)min(max(ktok, 0), N - 1) * D;
+    load_row_frags<T, D>(Kh + krow, live && kwave && ktok < t_end, kx, h);
+    load_row_frags<T, D>(Vh + krow, live && role == 0 && ktok < t_end, vx, h);
+    if (owave) {
+#pragma unroll
+      for (int i = 0; i < OIT; ++i) {
+        const int it = 64 * ow + lane + 64 * NDW * i, t = it / VCH, tk = s0 + t;
+        const bool ok = live && it < STEP * VCH && tk < t_end;
+        const int tc = min(max(tk, 0), N - 1);
+        ob[i].load_if(dOh + (size_t)tc * D + (it % VCH) * 8, ok);
+        oe[i] = re[(size_t)bh * N + tc];
+        if (!ok) oe[i] = 0.0f;
+      }
+      if (ow == 0) {
+        const int tk = s0 + lane;
+        ddv = rdd[(size_t)bh * N + min(max(tk, 0), N - 1)];
+        if (!(live && lane < STEP && tk < t_end)) ddv = 0.0f;
+      }
+    }
+  };
   const int nstep = (t_end - t_beg + STEP - 1) / STEP;
+  load_rows(t_beg + (nstep - 1) * STEP);
+
   for (int si = nstep - 1; si >= 0; --si) {
     const int s0 = t_beg + si * STEP;
-    if (w < 2) {
-      const int tok = s0 + 32 * w + col;
-      const bool valid = tok < t_end;
+    if (w < QT) {
+      const bool valid = s0 + 32 * w + col < t_end;
       Feat Fq;
-      Fq.compute(Q + ((size_t)bh * N + (valid ? tok : t_beg)) * D, valid, pl, Lg, scale, tau, lane);
+      Fq.compute(qx, pl, Lg, scale, tau, lane);
 #pragma unroll
       for (int jp = 0; jp < LPG / 2; ++jp) {
-        float x[16];
+        float x0[8], x1[8];
 #pragma unroll
-        for (int b = 0; b < 16; ++b) {
-          x[b] = valid ? Fq.phi[jp][b] : 0.0f;
-          sm.QFT[Feat::feat(jp, b, h)][32 * w + col] = from_f<T>(x[b]);
+        for (int b = 0; b < 8; ++b) {
+          x0[b] = valid ? Fq.phi[jp][b] : 0.0f;
+          x1[b] = valid ? Fq.phi[jp][8 + b] : 0.0f;
         }
-        store8(&sm.QF[32 * w + col][Feat::feat(jp, 0, h)], *reinterpret_cast<float(*)[8]>(&x[0]));
-        store8(&sm.QF[32 * w + col][Feat::feat(jp, 8, h)], *reinterpret_cast<float(*)[8]>(&x[8]));
+        store8(&sm.FS[32 * w + col][Feat::feat(jp, 0, h)], x0);
+        store8(&sm.FS[32 * w + col][Feat::feat(jp, 8, h)], x1);
       }
-    } else {
-      for (int idx = tid - 128; idx < STEP * (D / 8); idx += 128) {
-        const int t = idx % STEP, c8 = (idx / STEP) * 8;  // token-fastest transposed stores
-        const int tk = s0 + t;
-        float x[8];
-        if (tk < t_end) {
-          const float e = re[(size_t)bh * N + tk];
-          load8(dO + ((size_t)bh * N + tk) * D + c8, x);
+    }
+    if (owave) {
 #pragma unroll
-          for (int k = 0; k < 8; ++k) x[k] *= e;
-        } else {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) x[k] = 0.0f;
+      for (int i = 0; i < OIT; ++i) {
+        const int it = 64 * ow + lane + 64 * NDW * i;
+        if (it < STEP * VCH) {
+          ob[i].scale(oe[i]);
+          ob[i].store(&sm.XS[it / VCH][(it % VCH) * 8]);
         }
-        store8(&sm.dnS[t][c8], x);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) sm.dnT[c8 + k][t] = from_f<T>(x[k]);
       }
-      for (int t = tid - 128; t < STEP; t += 128)
-        sm.dd[t] = s0 + t < t_end ? rdd[(size_t)bh * N + s0 + t] : 0.0f;
+      if (ow == 0 && lane < STEP) sm.dd[lane] = ddv;
     }
     const int ktok = s0 + 32 * kt + col;
-    const bool kvalid = ktok < t_end;
+    const bool kvalid = kwave && ktok < t_end;
     Feat Fk;
-    Fk.compute(K + ((size_t)bh * N + (kvalid ? ktok : t_beg)) * D, kvalid, pl, Lg, scale, tau, lane);
+    if (kwave) Fk.compute(kx, pl, Lg, scale, tau, lane);
     __syncthreads();
 
-    if (part == 0) {
-      // dphi(K)^T tiles: rows = features, columns = keys.
-      typename M::frag vf[D / M::KSTEP];
-      const T* vrow = V + ((size_t)bh * N + (kvalid ? ktok : t_beg)) * D;
-#pragma unroll
-      for (int ks = 0; ks < D / M::KSTEP; ++ks)
-        vf[ks] = kvalid ? M::load(vrow + ks * M::KSTEP + M::KPL * h) : M::zero();
+    if (role == 0) {
+      // dphi(K)^T (rows = features, columns = keys) = G V^T + g 1^T + the part of
+      // the step's queries at or after each key.
       floatx16 dkt[NFT];
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft) {
         dkt[ft] = zero16();
 #pragma unroll
         for (int ks = 0; ks < D / M::KSTEP; ++ks)
-          dkt[ft] = M::mma(M::load(&sm.GF[32 * ft + col][ks * M::KSTEP + M::KPL * h]), vf[ks], dkt[ft]);
+          dkt[ft] = M::mma(row_frag<T>(&sm.SF[0][0], LDD, 32 * ft, 0, ks, lane), vx[ks], dkt[ft]);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) dkt[ft][v] += sm.gz[32 * ft + acc_row(v, h)];
+        for (int v = 0; v < 16; ++v) dkt[ft][v] += sm.zr[32 * ft + acc_row(v, h)];
       }
       if (causal) {
-        for (int qt = kt; qt < STEP / 32; ++qt) {
+        for (int qt = kt; qt < QT; ++qt) {
           floatx16 gm = zero16();
 #pragma unroll
           for (int ks = 0; ks < D / M::KSTEP; ++ks)
-            gm = M::mma(M::load(&sm.dnS[32 * qt + col][ks * M::KSTEP + M::KPL * h]), vf[ks], gm);
+            gm = M::mma(row_frag<T>(&sm.XS[0][0], LDD, 32 * qt, 0, ks, lane), vx[ks], gm);
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             gm[v] += sm.dd[32 * qt + acc_row(v, h)];
@@ -776,34 +781,40 @@ __global__ void __launch_bounds__(256)
             const typename M::frag gf = M::from_acc(gm, ks2);
 #pragma unroll
             for (int ft = 0; ft < NFT; ++ft)
-              dkt[ft] = M::mma(M::load_accperm(&sm.QFT[32 * ft + col][32 * qt], ks2, h), gf, dkt[ft]);
+              dkt[ft] = M::mma(tr_frag<T>(&sm.FS[0][0], LDR, 32 * qt, 32 * ft, ks2, lane, true), gf, dkt[ft]);
           }
         }
       }
-      float dphi[LPG / 2][16], da[LPG / 2][4];
+      float da[LPG / 2][4];
 #pragma unroll
-      for (int ft = 0; ft < NFT; ++ft) tile_to_table(dkt[ft], h, dphi[ft]);
-      Fk.backward(dphi, da);
+      for (int ft = 0; ft < NFT; ++ft) {
+        float dphi[16];
+        tile_to_table(dkt[ft], h, dphi);
+        Fk.backward_table(ft, dphi, da[ft]);
+      }
       floatx16 dx[D / 32];
       features_dx<T, D, LPG>(da, RT + (size_t)head * D * pw + 32 * grp, pw, c2, lane, dx);
       if (kvalid)
-        finish_row<T, D, false>(dKp, scrK, dK, bh, slots, ktok, N, levels, causal, h, dx,
-                                first != 0, last != 0);
-    } else {
+        write_grad_row<T, D>(dx, scrK, dK, ((size_t)bh * N + ktok) * D, h, first != 0,
+                             last != 0);
+    } else if (role == 1) {
+      // dV^T (rows = channels, columns = keys) = G^T phi(K)^T + the step's part.
       floatx16 dvt[D / 32];
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         dvt[dt] = zero16();
 #pragma unroll
-        for (int ks = 0; ks < RP / M::KSTEP; ++ks)
-          dvt[dt] = M::mma(M::load(&sm.GT[32 * dt + col][Feat::frag_feat(ks, 0, h)]), Fk.frag(ks), dvt[dt]);
+        for (int ks = 0; ks < RP / M::KSTEP; ++ks) {
+          const int fk = Feat::frag_feat(ks, 0, h);
+          dvt[dt] = M::mma(tr_rows(&sm.SF[0][0], LDD, fk, fk + 4, 32 * dt, lane), Fk.frag(ks), dvt[dt]);
+        }
       }
       if (causal) {
-        for (int qt = kt; qt < STEP / 32; ++qt) {
+        for (int qt = kt; qt < QT; ++qt) {
           floatx16 wq = zero16();
 #pragma unroll
           for (int ks = 0; ks < RP / M::KSTEP; ++ks)
-            wq = M::mma(M::load(&sm.QF[32 * qt + col][Feat::frag_feat(ks, 0, h)]), Fk.frag(ks), wq);
+            wq = M::mma(M::load(&sm.FS[32 * qt + col][Feat::frag_feat(ks, 0, h)]), Fk.frag(ks), wq);
 #pragma unroll
           for (int v = 0; v < 16; ++v)
             if (qt == kt && acc_row(v, h) < col) wq[v] = 0.0f;
@@ -812,40 +823,23 @@ __global__ void __launch_bounds__(256)
             const typename M::frag wf = M::from_acc(wq, ks2);
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
-              dvt[dt] = M::mma(M::load_accperm(&sm.dnT[32 * dt + col][32 * qt], ks2, h), wf, dvt[dt]);
+              dvt[dt] = M::mma(tr_frag<T>(&sm.XS[0][0], LDD, 32 * qt, 32 * dt, ks2, lane, true), wf, dvt[dt]);
           }
         }
       }
       if (kvalid)
-        finish_row<T, D, false>(dVp, scrV, dV, bh, slots, ktok, N, levels, causal, h, dvt,
-                                first != 0, last != 0);
+        write_grad_row<T, D>(dvt, scrV, dV, ((size_t)bh * N + ktok) * D, h, first != 0,
+                             last != 0);
     }
+    load_rows(s0 - STEP);  // before the span: loads nothing
+    if (!causal) break;
     __syncthreads();
-
-    if (causal) {
-#pragma unroll
-      for (int i = 0; i < SPW; ++i) {
-        const int tix = w + 4 * i;
-        if (tix < NST) {
-          const int mt = tix / NFT, nt = tix % NFT;
-#pragma unroll
-          for (int ks = 0; ks < STEP / M::KSTEP; ++ks) {
-            const int k0 = ks * M::KSTEP + M::KPL * h;
-            st[i] = M::mma(M::load(&sm.dnT[32 * mt + col][k0]), M::load(&sm.QFT[32 * nt + col][k0]), st[i]);
-          }
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const T x = from_f<T>(st[i][v]);
-            sm.GT[32 * mt + acc_row(v, h)][32 * nt + col] = x;
-            sm.GF[32 * nt + col][32 * mt + acc_row(v, h)] = x;
-          }
-        }
-      }
-      for (int f = tid; f < RP; f += blockDim.x) {
-        float s = 0.0f;
-        for (int t = 0; t < STEP; ++t) s += to_f(sm.QFT[f][t]) * sm.dd[t];
-        sm.gz[f] += s;
-      }
+    advance_stats<T, D, LPG, SPW, STEP>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, w, lane, st, &sm.SF[0][0]);
+    for (int f = tid; f < RP; f += 256) {
+      float s = 0.0f;
+#pragma unroll 8
+      for (int t = 0; t < STEP; ++t) s += to_f(sm.FS[t][f]) * sm.dd[t];
+      sm.zr[f] += s;
     }
     __syncthreads();
   }
@@ -895,13 +889,27 @@ size_t bwd_ws_bytes(const Problem& pb) { return bwd_layout(pb).total; }
 
 size_t bwd_lds_need(const Problem& pb) {
   const size_t e = pb.elem, d = pb.d, kt = pb.s < 32 ? 32 : pb.s;
-  const size_t rpg = 16 * (size_t)(padded_tables(pb.L) > 8 ? 8 : padded_tables(pb.L));
-  const size_t sb = e * (2 * kt * (d + 24)) + 20 * kt;  // one-role launch (two tiles)
-  const size_t lq = e * (rpg * (d + 8) + rpg * 136 + 128 * (d + 8)) + 4 * rpg;
-  const size_t lk = e * (2 * rpg * (d + 8) + rpg * 72 + 64 * (rpg + 8) + 64 * (d + 8) + d * 72) +
-                    4 * rpg + 4 * 64;
-  size_t m = sb > lq ? sb : lq;
-  return lk > m ? lk : m;
+  const size_t sb = e * (2 * kt * (d + (pb.bf16 ? 24 : 8))) + 20 * kt;  // one-role launch
+  size_t lr = 0;
+  with_T(pb.bf16, [&](auto tp) {
+    using T = ELSAA_T(tp);
+    with_D(pb.d, [&](auto dc) {
+      constexpr int D = ELSAA_C(dc);
+      auto need = [&](auto lc) {
+        constexpr int LPG = ELSAA_C(lc);
+        constexpr int SQ = walk_step<T, D, LPG, 128>(), SK = walk_step<T, D, LPG, 64>();
+        const size_t a = SQ > 0 ? sizeof(WalkSmem<T, D, LPG, SQ>) : sizeof(WalkSmem<T, D, LPG, 32>);
+        const size_t b = SK > 0 ? sizeof(WalkSmem<T, D, LPG, SK>) : sizeof(WalkSmem<T, D, LPG, 32>);
+        lr = a > b ? a : b;
+      };
+      switch (padded_tables(pb.L)) {
+        case 2: need(std::integral_constant<int, 2>{}); break;
+        case 4: need(std::integral_constant<int, 4>{}); break;
+        default: need(std::integral_constant<int, 8>{}); break;
+      }
+    });
+  });
+  return sb > lr ? sb : lr;
 }
 
 void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, const void* dO,
@@ -936,8 +944,6 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
   float* scrK = scr + BH * N * pb.d;
   float* scrV = scr + 2 * BH * N * pb.d;
   const int items = pb.causal ? pb.levels * (pb.N / 2) / pb.s + pb.N / pb.s : pb.N / pb.s;
-  const int span = pb.causal ? pb.chunk : 128;
-  const int span_k = pb.causal ? pb.chunk : 64;
 
   with_T(pb.bf16, [&](auto tp) {
     using T = ELSAA_T(tp);
@@ -981,21 +987,24 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
       }
       auto run_lr = [&](auto lc) {
         constexpr int LPG = ELSAA_C(lc);
-        for (int g = 0; g < groups; ++g) {
-          const int first = g == 0, last = g == groups - 1;
-          if constexpr (sizeof(LbqSmem<T, D, LPG>) <= kLdsBytes)
-            ELSAA_LAUNCH("lr_bwd_q", (lr_bwd_q_kernel<T, D, LPG>),
-                               dim3((pb.N + span - 1) / span, BH), dim3(256), 0, st, (const T*)Q,
-                               (const T*)K, (const T*)V, (const T*)dO, planes_lr, A, z, re, rdd,
-                               (const T*)dQp, scrQ, (T*)dQ, RT, pw, pb.H, pb.N, pb.L, span, pb.levels,
-                               (int)pb.causal, pb.scale, pb.tau, g, first, last);
-          if constexpr (sizeof(LbkSmem<T, D, LPG>) <= kLdsBytes)
-            ELSAA_LAUNCH("lr_bwd_k", (lr_bwd_k_kernel<T, D, LPG>),
-                               dim3((pb.N + span_k - 1) / span_k, BH), dim3(256), 0, st,
-                               (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, planes_lr, Gs,
-                               gzs, re, rdd, (const T*)dKp, (const T*)dVp, scrK, scrV, (T*)dK,
-                               (T*)dV, RT, pw, pb.H, pb.N, pb.L, span_k, pb.levels, (int)pb.causal,
-                               pb.scale, pb.tau, g, first, last);
+        constexpr int SQ = walk_step<T, D, LPG, 128>(), SK = walk_step<T, D, LPG, 64>();
+        if constexpr (SQ > 0 && SK > 0) {
+          const int span_q = pb.causal ? pb.chunk : SQ;
+          const int span_k = pb.causal ? pb.chunk : SK;
+          for (int g = 0; g < groups; ++g) {
+            const int first = g == 0, last = g == groups - 1;
+            ELSAA_LAUNCH("lr_bwd_q", (lr_bwd_q_kernel<T, D, LPG, SQ>),
+                         dim3((pb.N + span_q - 1) / span_q, BH), dim3(256), 0, st, (const T*)Q,
+                         (const T*)K, (const T*)V, (const T*)dO, planes_lr, A, z, re, rdd,
+                         (const T*)dQp, scrQ, (T*)dQ, RT, pw, pb.H, pb.N, pb.L, span_q,
+                         pb.levels, (int)pb.causal, pb.scale, pb.tau, g, first, last);
+            ELSAA_LAUNCH("lr_bwd_k", (lr_bwd_k_kernel<T, D, LPG, SK>),
+                         dim3((pb.N + span_k - 1) / span_k, BH), dim3(256), 0, st, (const T*)Q,
+                         (const T*)K, (const T*)V, (const T*)dO, planes_lr, Gs, gzs, re, rdd,
+                         (const T*)dKp, (const T*)dVp, scrK, scrV, (T*)dK, (T*)dV, RT, pw, pb.H,
+                         pb.N, pb.L, span_k, pb.levels, (int)pb.causal, pb.scale, pb.tau, g,
+                         first, last);
+          }
         }
       };
       switch (padded_tables(pb.L)) {
@@ -1003,6 +1012,7 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
         case 4: run_lr(std::integral_constant<int, 4>{}); break;
         default: run_lr(std::integral_constant<int, 8>{}); break;
       }
+      launch_combine(pb, dQp, dKp, dVp, dQ, dK, dV, st);
     });
   });
 }

@@ -116,13 +116,12 @@ template <typename T>
 __device__ __forceinline__ typename MF<T>::frag tr_frag(const T* X, int ld, int k0, int n0, int ks,
                                                         int lane, bool accperm);
 
-template <>
-__device__ __forceinline__ bf16x8 tr_frag<__bf16>(const __bf16* X, int ld, int k0, int n0, int ks,
-                                                  int lane, bool accperm) {
-  const int s = lane & 15, g = lane >> 4, h = lane >> 5;
+// The bf16 primitive: elements 0..3 from rows kb1 .. kb1 + 3, elements 4..7 from
+// rows kb2 .. kb2 + 3 (kb1, kb2 may differ between lane halves).
+__device__ __forceinline__ bf16x8 tr_rows(const __bf16* X, int ld, int kb1, int kb2, int n0,
+                                          int lane) {
+  const int s = lane & 15, g = lane >> 4;
   const int nb = n0 + 16 * (g & 1) + 4 * (s & 3);
-  const int kb1 = k0 + (accperm ? 16 * ks + 4 * h : 16 * ks + 8 * h);
-  const int kb2 = kb1 + (accperm ? 8 : 4);
   typedef __attribute__((address_space(3))) bf16x4_tr* lds_ptr;
   const bf16x4_tr a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_ptr)(X + (size_t)(kb1 + (s >> 2)) * ld + nb));
   const bf16x4_tr b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_ptr)(X + (size_t)(kb2 + (s >> 2)) * ld + nb));
@@ -130,6 +129,17 @@ __device__ __forceinline__ bf16x8 tr_frag<__bf16>(const __bf16* X, int ld, int k
 #pragma unroll
   for (int e = 0; e < 4; ++e) { f[e] = a[e]; f[4 + e] = b[e]; }
   return f;
+}
+__device__ __forceinline__ float tr_rows(const float* X, int ld, int kb1, int, int n0, int lane) {
+  return X[(size_t)kb1 * ld + n0 + (lane & 31)];
+}
+
+template <>
+__device__ __forceinline__ bf16x8 tr_frag<__bf16>(const __bf16* X, int ld, int k0, int n0, int ks,
+                                                  int lane, bool accperm) {
+  const int h = lane >> 5;
+  const int kb1 = k0 + (accperm ? 16 * ks + 4 * h : 16 * ks + 8 * h);
+  return tr_rows(X, ld, kb1, kb1 + (accperm ? 8 : 4), n0, lane);
 }
 
 template <>
@@ -236,6 +246,12 @@ struct Vec8<__bf16> {
     for (int e = 0; e < 8; ++e) v[e] = (__bf16)((float)v[e] * c);
   }
   __device__ __forceinline__ void store(__bf16* p) const { *reinterpret_cast<bf16x8*>(p) = v; }
+  // Reads p (which must be readable) and keeps the value only if ok.
+  __device__ __forceinline__ void load_if(const __bf16* p, bool ok) {
+    load(p);
+    if (!ok) zero();
+  }
+  __device__ __forceinline__ float get(int e) const { return (float)v[e]; }
 };
 template <>
 struct Vec8<float> {
@@ -256,6 +272,11 @@ struct Vec8<float> {
     *reinterpret_cast<floatx4*>(p) = a;
     *reinterpret_cast<floatx4*>(p + 4) = b;
   }
+  __device__ __forceinline__ void load_if(const float* p, bool ok) {
+    load(p);
+    if (!ok) zero();
+  }
+  __device__ __forceinline__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
 };
 
 // Gathers ROWS rows of D elements (row r of tensor t taken from
@@ -311,6 +332,99 @@ __device__ __forceinline__ unsigned gray_rank(unsigned c) {
   return c;
 }
 
+// Row fragments of one token row in global memory (B operand of a product over
+// the row's D elements; lane half h holds elements ks * KSTEP + KPL h + e).
+// The row is always read (x must point to a valid row); invalid rows give zeros.
+template <typename T, int D>
+__device__ __forceinline__ void load_row_frags(const T* x, bool valid,
+                                               typename MF<T>::frag (&f)[D / MF<T>::KSTEP], int h) {
+  typedef MF<T> M;
+#pragma unroll
+  for (int ks = 0; ks < D / M::KSTEP; ++ks) f[ks] = M::load(x + ks * M::KSTEP + M::KPL * h);
+  if (!valid)
+#pragma unroll
+    for (int ks = 0; ks < D / M::KSTEP; ++ks) f[ks] = M::zero();
+}
+
+// 4 consecutive elements in registers.
+template <typename T>
+struct Raw4;
+template <>
+struct Raw4<__bf16> {
+  bf16x4 v;
+  __device__ __forceinline__ void load(const __bf16* p) { v = *reinterpret_cast<const bf16x4*>(p); }
+  __device__ __forceinline__ float operator[](int e) const { return (float)v[e]; }
+};
+template <>
+struct Raw4<float> {
+  floatx4 v;
+  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const floatx4*>(p); }
+  __device__ __forceinline__ float operator[](int e) const { return v[e]; }
+};
+
+// The part of one token row that a lane holds in the accumulator layout of
+// D x 32 tiles whose columns are tokens: channels 32 dt + 8 g + 4 h + e for the
+// NDT tiles dt0 .. dt0 + NDT - 1 (dt0 = 0 unless given).
+template <typename T, int NDT>
+struct DRow {
+  Raw4<T> x[NDT][4];
+  __device__ __forceinline__ void load(const T* row, int h, int dt0 = 0) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) x[dt][g].load(row + 32 * (dt0 + dt) + 8 * g + 4 * h);
+  }
+  __device__ __forceinline__ void add_to(float (&acc)[NDT][4][4], float w) const {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[dt][g][e] += w * x[dt][g][e];
+  }
+};
+
+// Partial-result slots of one token (see partial_slots): its own slot (the causal
+// leaf block, or the single non-causal block) and, causal, the slot of level l for
+// every level at which the token lies in a future half of a segment (QUERY) or in
+// a past half (!QUERY). next() hands them out in batches so that a batch of row
+// loads can be in flight together.
+template <bool QUERY>
+struct SlotWalk {
+  int tok, N, levels, logN, l;
+  bool own;
+  __device__ __forceinline__ SlotWalk(int tok_, int N_, int levels_, bool causal)
+      : tok(tok_), N(N_), levels(causal ? levels_ : 0), logN(31 - __clz(N_)), l(0), own(true) {}
+  __device__ __forceinline__ bool member(int lv) const {
+    return (((tok >> (logN - 1 - lv)) & 1) != 0) == QUERY;
+  }
+  __device__ __forceinline__ size_t slot(int lv) const {
+    const int n = N >> lv, half = n >> 1;
+    const int c = QUERY ? (tok / n) * half + (tok % n) - half : (tok / n) * half + (tok % n);
+    return (size_t)N + (size_t)lv * (N / 2) + c;
+  }
+  // Fills sl[0 .. n) with the next n <= KB slots; returns n (0 when done).
+  template <int KB>
+  __device__ __forceinline__ int next(size_t (&sl)[KB]) {
+    int n = 0;
+    if (own) {
+      sl[0] = (size_t)tok;
+      n = 1;
+      own = false;
+    }
+    for (; l < levels && n < KB; ++l) {
+      if (member(l)) {
+        const size_t x = slot(l);
+#pragma unroll
+        for (int j = 0; j < KB; ++j)
+          if (j == n) sl[j] = x;
+        ++n;
+      }
+    }
+    return n;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // RACE features of the 32 tokens of one wave (lane % 32 = token, h = lane / 32).
 //
@@ -328,10 +442,18 @@ struct Features {
   static constexpr int NPT = (4 * LP + 31) / 32;  // 32-row projection tiles
   static constexpr int NJP = LP / 2;               // table pairs
   float phi[NJP][16];
-  float sp[NJP][4], sq[NJP][4];  // sigmoid(+a_t), sigmoid(-a_t), a_t = 2 u_t / tau
+  float sp[NJP][4];  // sigmoid(a_t), a_t = 2 u_t / tau
 
   __device__ __forceinline__ void compute(const T* xrow, bool valid, const float* planes,
                                           int L, float scale, float tau, int lane) {
+    typename MF<T>::frag xb[D / MF<T>::KSTEP];
+    load_row_frags<T, D>(xrow, valid, xb, lane >> 5);
+    compute(xb, planes, L, scale, tau, lane);
+  }
+  // Same, from the token's row fragments (zero fragments give zero projections).
+  __device__ __forceinline__ void compute(const typename MF<T>::frag (&xf)[D / MF<T>::KSTEP],
+                                          const float* planes, int L, float scale, float tau,
+                                          int lane) {
     typedef MF<T> M;
     const int h = lane >> 5, col = lane & 31;
     floatx16 u[NPT];
@@ -340,7 +462,7 @@ struct Features {
 #pragma unroll
     for (int ks = 0; ks < D / M::KSTEP; ++ks) {
       const int k0 = ks * M::KSTEP + M::KPL * h;
-      typename M::frag xb = valid ? M::load(xrow + k0) : M::zero();
+      const typename M::frag xb = xf[ks];
 #pragma unroll
       for (int mt = 0; mt < NPT; ++mt) {
         const int prow = 32 * mt + col;  // projection index of this lane's A row
@@ -383,7 +505,6 @@ struct Features {
           p[t] = sigmoid(a);
           q[t] = sigmoid(-a);
           sp[jp][t] = p[t];
-          sq[jp][t] = q[t];
         }
         float lo4[4], hi4[4];
 #pragma unroll
@@ -412,21 +533,26 @@ struct Features {
     for (int e = 0; e < M::KPL; ++e) x[e] = phi[jp][b0 + e];
     return M::from_floats(x);
   }
-  // Backward of phi through a_t = (2 scale / tau) <R_t, x>: given dphi in this
-  // lane's layout, da_t = sum_b dphi_b phi_b (bit t of b ? sigmoid(-a_t) : -sigmoid(a_t)).
+  // Backward of phi through a_t = (2 scale / tau) <R_t, x> for table pair jp:
+  // with w_b = dphi_b phi_b, d phi_b / d a_t = phi_b ([bit t of b] - sigmoid(a_t)),
+  // so da_t = sum_{b with bit t} w_b - sigmoid(a_t) sum_b w_b.
+  __device__ __forceinline__ void backward_table(int jp, const float (&dphi)[16],
+                                                 float (&da)[4]) const {
+    float wsum = 0.0f, s1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      const float w = dphi[b] * phi[jp][b];
+      wsum += w;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if ((b >> t) & 1) s1[t] += w;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) da[t] = s1[t] - sp[jp][t] * wsum;
+  }
   __device__ __forceinline__ void backward(const float (&dphi)[NJP][16], float (&da)[NJP][4]) const {
 #pragma unroll
-    for (int jp = 0; jp < NJP; ++jp)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int b = 0; b < 16; ++b) {
-          const float w = dphi[jp][b] * phi[jp][b];
-          acc += ((b >> t) & 1) ? w * sq[jp][t] : -w * sp[jp][t];
-        }
-        da[jp][t] = acc;
-      }
+    for (int jp = 0; jp < NJP; ++jp) backward_table(jp, dphi[jp], da[jp]);
   }
 
   // Feature index that K step ks, element e uses for lane half h.

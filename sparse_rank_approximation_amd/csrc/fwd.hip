@@ -164,236 +164,233 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
 
 // ---------------------------------------------------------------------------
 
-template <typename T, int D, int LP>
-struct EpiSmem {
-  static constexpr int RP = 16 * LP, STEP = 64;
-  T VT[D][STEP + 8];     // V^T of the step's keys
-  T KF[STEP][RP + 8];    // phi(K) of the step's keys, [key][feature]
-  T AT[D][RP + 8];       // running statistics (value channel x feature) as MFMA operand
-  float zr[RP];          // running sum of phi(K)
-};
-
-template <typename T, int D, int LP>
+// Epilogue workgroup: one head and one span of tokens (a summary chunk when
+// causal), walked in steps of STEP tokens by 4 waves. LDS (WalkSmem) holds the
+// step's keys (V in XS, phi(K) in FS, row-major) and the running RACE statistics
+// S = sum_j phi(K_j) V_j^T as an MFMA operand (SF, [feature][channel]).
+template <typename T, int D, int LP, int STEP>
 __global__ void __launch_bounds__(256)
     fwd_epilogue_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                         const float* __restrict__ planes, const float* __restrict__ A,
-                        const float* __restrict__ z, const T* __restrict__ Opart,
-                        const float* __restrict__ Lpart, const float* __restrict__ lambda,
+                        const float* __restrict__ z, const T* __restrict__ Os,
+                        const float* __restrict__ lse_s, const float* __restrict__ lambda,
                         const float* __restrict__ gs, const float* __restrict__ glr,
-                        T* __restrict__ O, T* __restrict__ Os, T* __restrict__ Olr,
-                        float* __restrict__ lse_out, float* __restrict__ dlr_out, int H, int N,
-                        int L, int span, int levels, int causal, int s, float scale, float tau,
+                        T* __restrict__ O, T* __restrict__ Olr, float* __restrict__ dlr_out,
+                        int H, int N, int L, int span, int causal, float scale, float tau,
                         float eps) {
   typedef MF<T> M;
   typedef Features<T, D, LP> Feat;
-  constexpr int RP = 16 * LP, STEP = 64;
-  constexpr int NT_N = RP / 32, NST = (D / 32) * NT_N, SPW = (NST + 3) / 4;
-  constexpr int DH = D / 2;                     // output rows per wave
-  constexpr int NDT = DH >= 32 ? DH / 32 : 1;   // 32-row output tiles per wave
-  __shared__ EpiSmem<T, D, LP> sm;
+  typedef WalkSmem<T, D, LP, STEP> Sm;
+  constexpr int RP = 16 * LP, LDD = Sm::LDD, LDR = Sm::LDR;
+  constexpr int QT = STEP / 32;                         // query (and key) tiles per step
+  constexpr int WPT = 4 / QT;                           // waves per query tile
+  constexpr int NDA = D / 32;                           // channel tiles
+  constexpr int NDT = NDA / WPT > 0 ? NDA / WPT : 1;    // channel tiles per wave
+  constexpr int NFT = RP / 32, NST = NDA * NFT, SPW = (NST + 3) / 4;
+  constexpr int VCH = D / 8, VIT = (STEP * VCH + 255) / 256;
+  __shared__ Sm sm;
 
   const int bh = blockIdx.y, c = blockIdx.x, head = bh % H;
   const int r = 16 * L;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, col = lane & 31;
-  const int qt = w >> 1, dh = w & 1;
-  // D = 32: one 32-row tile; both waves of a query tile compute it, only dh == 0 writes.
-  const int dbase = D >= 64 ? dh * DH : 0;
-  const bool writer = D >= 64 || dh == 0;
+  const int qt = w % QT, dt0 = (w / QT) * NDT;
+  const bool owner = dt0 < NDA;  // waves past the channel tiles only stage
   const float* pl = planes + (size_t)head * L * 4 * D;
   const int t_beg = c * span, t_end = min(N, t_beg + span);
-  const size_t slots = partial_slots(N, levels, causal);
   const float lam = lambda[head];
-  const int logN = 31 - __clz(N);
+  const T* Qh = Q + (size_t)bh * N * D;
+  const T* Kh = K + (size_t)bh * N * D;
+  const T* Vh = V + (size_t)bh * N * D;
 
-  // Load the statistics at the start of this span.
-  const float* Ac = A + (size_t)(causal ? (size_t)bh * (N / span) + c : bh) * D * r;
-  const float* zc = z + (size_t)(causal ? (size_t)bh * (N / span) + c : bh) * r;
+  // Statistics at the start of the span: fp32 tiles in registers (D layout, rows =
+  // channels, lanes = features) and their operand copy in SF.
+  const size_t sidx = causal ? (size_t)bh * (N / span) + c : (size_t)bh;
+  const float* Ac = A + sidx * D * r;
+  const float* zc = z + sidx * r;
   floatx16 st[SPW];
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
-    st[i] = zero16();
     const int tix = w + 4 * i;
-    if (causal && tix < NST) {
-      const int mt = tix / NT_N, nt = tix % NT_N, f = 32 * nt + col;
+    st[i] = zero16();
+    if (tix < NST) {
+      const int mt = tix / NFT, f = 32 * (tix % NFT) + col;
       if (f < r)
 #pragma unroll
         for (int v = 0; v < 16; ++v) st[i][v] = Ac[(size_t)(32 * mt + acc_row(v, h)) * r + f];
     }
   }
-  for (int idx = tid; idx < D * RP; idx += blockDim.x) {
-    const int e = idx / RP, f = idx % RP;
-    sm.AT[e][f] = from_f<T>(f < r ? Ac[(size_t)e * r + f] : 0.0f);
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    const int tix = w + 4 * i;
+    if (tix < NST) {
+      const int mt = tix / NFT, f = 32 * (tix % NFT) + col;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = st[i][4 * g + e];
+        store4(&sm.SF[f][32 * mt + 8 * g + 4 * h], x);
+      }
+    }
   }
-  for (int f = tid; f < RP; f += blockDim.x) sm.zr[f] = f < r ? zc[f] : 0.0f;
+  for (int f = tid; f < RP; f += 256) sm.zr[f] = f < r ? zc[f] : 0.0f;
+
+  // Global rows of one step, loaded one step ahead: this wave's query tile, the
+  // key tile it featurizes (waves < QT) and its share of the V rows.
+  typename M::frag qx[D / M::KSTEP], kx[D / M::KSTEP];
+  Vec8<T> vb[VIT];
+  auto load_rows = [&](int s0) __attribute__((always_inline)) {
+    const int qtok = s0 + 32 * qt + col;
+    load_row_frags<T, D>(Qh + (size_t)min(qtok, N - 1) * D, qtok < t_end, qx, h);
+    if (causal) {
+      const int ktok = s0 + 32 * w + col;
+      if (w < QT) load_row_frags<T, D>(Kh + (size_t)min(ktok, N - 1) * D, ktok < t_end, kx, h);
+#pragma unroll
+      for (int i = 0; i < VIT; ++i) {
+        const int it = tid + 256 * i, t = it / VCH, tok = s0 + t;
+        vb[i].load_if(Vh + (size_t)min(tok, N - 1) * D + (it % VCH) * 8,
+                      it < STEP * VCH && tok < t_end);
+      }
+    }
+  };
+  load_rows(t_beg);
 
   for (int s0 = t_beg; s0 < t_end; s0 += STEP) {
-    // phase A: phi(K) of the step's keys and V^T into LDS (causal only); phi(Q) in
-    // registers for this wave's query tile.
+    // Stage the step's keys: phi(K) and V into LDS (causal only).
     if (causal) {
-      if (dh == 0) {
-        const int tok = s0 + 32 * qt + col;
-        const bool valid = tok < t_end;
+      if (w < QT) {
         Feat Fk;
-        Fk.compute(K + ((size_t)bh * N + (valid ? tok : t_beg)) * D, valid, pl, L, scale, tau, lane);
+        Fk.compute(kx, pl, L, scale, tau, lane);
+        const bool kv = s0 + 32 * w + col < t_end;
 #pragma unroll
-        for (int jp = 0; jp < LP / 2; ++jp)
+        for (int jp = 0; jp < LP / 2; ++jp) {
+          float x0[8], x1[8];
 #pragma unroll
-          for (int b = 0; b < 16; ++b)
-            sm.KF[32 * qt + col][Feat::feat(jp, b, h)] = from_f<T>(valid ? Fk.phi[jp][b] : 0.0f);
-      } else {
-        for (int idx = lane + 64 * qt; idx < STEP * (D / 8); idx += 128) {
-          const int tk = idx % STEP, c8 = (idx / STEP) * 8;  // token-fastest V^T stores
-          const int tok = s0 + tk;
-          float x[8];
-          if (tok < t_end) {
-            load8(V + ((size_t)bh * N + tok) * D + c8, x);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+          for (int b = 0; b < 8; ++b) {
+            x0[b] = kv ? Fk.phi[jp][b] : 0.0f;
+            x1[b] = kv ? Fk.phi[jp][8 + b] : 0.0f;
           }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sm.VT[c8 + e][tk] = from_f<T>(x[e]);
+          store8(&sm.FS[32 * w + col][Feat::feat(jp, 0, h)], x0);
+          store8(&sm.FS[32 * w + col][Feat::feat(jp, 8, h)], x1);
         }
+      }
+#pragma unroll
+      for (int i = 0; i < VIT; ++i) {
+        const int it = tid + 256 * i;
+        if (it < STEP * VCH) vb[i].store(&sm.XS[it / VCH][(it % VCH) * 8]);
       }
     }
     const int qtok = s0 + 32 * qt + col;
     const bool qvalid = qtok < t_end;
     Feat Fq;
-    Fq.compute(Q + ((size_t)bh * N + (qvalid ? qtok : t_beg)) * D, qvalid, pl, L, scale, tau, lane);
+    Fq.compute(qx, pl, L, scale, tau, lane);
     __syncthreads();
 
-    // phase B: readout. num^T rows [dbase, dbase + 32 NDT) x this wave's 32 queries.
-    floatx16 num[NDT];
+    if (owner) {
+      // The query's merged sparse output and log-sum-exp (loads in flight during
+      // the readout).
+      const size_t k = (size_t)bh * N + min(qtok, N - 1);
+      DRow<T, NDT> osr;
+      osr.load(Os + k * D, h, dt0);
+      const float lse = lse_s[k];
+
+      // Low-rank branch readout: num^T = S^T phi(Q)^T over the channel tiles of
+      // this wave, den = phi(Q) . z; then the causally masked part of the step.
+      floatx16 num[NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) num[dt] = zero16();
-    float den = 0.0f;
+      for (int dt = 0; dt < NDT; ++dt) num[dt] = zero16();
+      float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int jp = 0; jp < LP / 2; ++jp)
+      for (int jp = 0; jp < LP / 2; ++jp)
 #pragma unroll
-      for (int b = 0; b < 16; ++b) den += Fq.phi[jp][b] * sm.zr[Feat::feat(jp, b, h)];
-    den += swap_half(den);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const floatx4 zz = *reinterpret_cast<const floatx4*>(&sm.zr[Feat::feat(jp, 4 * q4, h)]);
 #pragma unroll
-    for (int ks = 0; ks < RP / M::KSTEP; ++ks) {
-      const typename M::frag fb = Fq.frag(ks);
-      const int f0 = Feat::frag_feat(ks, 0, h);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        num[dt] = M::mma(M::load(&sm.AT[dbase + 32 * dt + col][f0]), fb, num[dt]);
-    }
-    if (causal) {
-      float dintra = 0.0f;
-      for (int kt = 0; kt <= qt; ++kt) {
-        floatx16 wt = zero16();
-#pragma unroll
-        for (int ks = 0; ks < RP / M::KSTEP; ++ks)
-          wt = M::mma(M::load(&sm.KF[32 * kt + col][Feat::frag_feat(ks, 0, h)]), Fq.frag(ks), wt);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          if (kt == qt && acc_row(v, h) > col) wt[v] = 0.0f;
-          dintra += wt[v];
+          for (int e = 0; e < 4; ++e) d4[e] += Fq.phi[jp][4 * q4 + e] * zz[e];
         }
+      float den = (d4[0] + d4[1]) + (d4[2] + d4[3]);
+      den += swap_half(den);
 #pragma unroll
-        for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
-          const typename M::frag wf = M::from_acc(wt, ks2);
+      for (int ks = 0; ks < RP / M::KSTEP; ++ks) {
+        const typename M::frag fb = Fq.frag(ks);
+        const int f0 = Feat::frag_feat(ks, 0, h);
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-            num[dt] = M::mma(M::load_accperm(&sm.VT[dbase + 32 * dt + col][32 * kt], ks2, h), wf, num[dt]);
-        }
+        for (int dt = 0; dt < NDT; ++dt)
+          num[dt] = M::mma(tr_rows(&sm.SF[0][0], LDD, f0, f0 + 4, 32 * (dt0 + dt), lane), fb, num[dt]);
       }
-      den += dintra + swap_half(dintra);
-    }
-    __syncthreads();
-
-    // phase C: advance the running statistics by the step's keys.
-    if (causal) {
+      if (causal) {
+        float dintra = 0.0f;
+        for (int kt = 0; kt <= qt; ++kt) {
+          floatx16 wt = zero16();
 #pragma unroll
-      for (int i = 0; i < SPW; ++i) {
-        const int tix = w + 4 * i;
-        if (tix < NST) {
-          const int mt = tix / NT_N, nt = tix % NT_N;
+          for (int ks = 0; ks < RP / M::KSTEP; ++ks)
+            wt = M::mma(M::load(&sm.FS[32 * kt + col][Feat::frag_feat(ks, 0, h)]), Fq.frag(ks), wt);
 #pragma unroll
-          for (int ks = 0; ks < STEP / M::KSTEP; ++ks) {
-            const int k0 = ks * M::KSTEP + M::KPL * h;
-            float kb[M::KPL];
-#pragma unroll
-            for (int e = 0; e < M::KPL; ++e) kb[e] = to_f(sm.KF[k0 + e][32 * nt + col]);
-            st[i] = M::mma(M::load(&sm.VT[32 * mt + col][k0]), M::from_floats(kb), st[i]);
+          for (int v = 0; v < 16; ++v) {
+            if (kt == qt && acc_row(v, h) > col) wt[v] = 0.0f;
+            dintra += wt[v];
           }
 #pragma unroll
-          for (int v = 0; v < 16; ++v) sm.AT[32 * mt + acc_row(v, h)][32 * nt + col] = from_f<T>(st[i][v]);
+          for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
+            const typename M::frag wf = M::from_acc(wt, ks2);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+              num[dt] = M::mma(tr_frag<T>(&sm.XS[0][0], LDD, 32 * kt, 32 * (dt0 + dt), ks2, lane, true), wf, num[dt]);
+          }
         }
+        den += dintra + swap_half(dintra);
       }
-      for (int f = tid; f < RP; f += blockDim.x) {
-        float zs = 0.0f;
-        for (int t = 0; t < STEP; ++t) zs += to_f(sm.KF[t][f]);
-        sm.zr[f] += zs;
-      }
-    }
 
-    // phase D: sparse merge, fusion, outputs for this wave's queries and rows.
-    if (qvalid) {
-      const int i = qtok;
-      const float* lp = Lpart + (size_t)bh * slots;
-      auto slot_of = [&](int l) -> size_t {
-        return (size_t)N + (size_t)l * (N / 2) + compact_future(i, N, l);
-      };
-      auto in_level = [&](int l) -> bool { return causal && ((i >> (logN - 1 - l)) & 1); };
-      float lmax = lp[i];
-      for (int l = 0; l < levels; ++l)
-        if (in_level(l)) lmax = fmaxf(lmax, lp[slot_of(l)]);
-      float wsum = fast_exp(lp[i] - lmax);
-      for (int l = 0; l < levels; ++l)
-        if (in_level(l)) wsum += fast_exp(lp[slot_of(l)] - lmax);
-      const float lse = lmax + __logf(wsum);
-      const float winv = 1.0f / wsum;
-      float os[NDT][4][4];
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) os[dt][g][e] = 0.0f;
-      for (int l = -1; l < levels; ++l) {
-        if (l >= 0 && !in_level(l)) continue;
-        const size_t sl = l < 0 ? (size_t)i : slot_of(l);
-        const float wk = fast_exp(lp[sl] - lmax) * winv;
-        const T* src = Opart + ((size_t)bh * slots + sl) * D;
+      if (qvalid) {
+        const float m = 1.0f / (1.0f + fast_exp(__logf(lam * den + eps) - lse));
+        const float g1 = gs ? gs[k] : 1.0f;
+        const float g2 = glr ? glr[k] : 1.0f;
+        const float dinv = 1.0f / den;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            float x[4];
-            load4(src + dbase + 32 * dt + 8 * g + 4 * h, x);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) os[dt][g][e] += wk * x[e];
-          }
-      }
-      const float m = 1.0f / (1.0f + fast_exp(__logf(lam * den + eps) - lse));
-      const float g1 = gs ? gs[(size_t)bh * N + i] : 1.0f;
-      const float g2 = glr ? glr[(size_t)bh * N + i] : 1.0f;
-      const float dinv = 1.0f / den;
-      const size_t row = ((size_t)bh * N + i) * D;
-      if (writer) {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int dd = dbase + 32 * dt + 8 * g + 4 * h;
+            const size_t o = k * D + 32 * (dt0 + dt) + 8 * g + 4 * h;
             float xo[4], xl[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               xl[e] = num[dt][4 * g + e] * dinv;
-              xo[e] = g1 * m * os[dt][g][e] + g2 * xl[e];
+              xo[e] = g1 * m * osr.x[dt][g][e] + g2 * xl[e];
             }
-            store4(O + row + dd, xo);
-            store4(Os + row + dd, os[dt][g]);
-            store4(Olr + row + dd, xl);
+            store4(O + o, xo);
+            store4(Olr + o, xl);
           }
-        if (h == 0 && dh == 0) {
-          lse_out[(size_t)bh * N + i] = lse;
-          dlr_out[(size_t)bh * N + i] = den;
+        if (h == 0 && dt0 == 0) dlr_out[k] = den;
+      }
+    }
+    load_rows(s0 + STEP);  // past the span: loads nothing
+    if (!causal) break;
+    __syncthreads();
+
+    // Advance the statistics by the step's keys: S^T += V^T phi(K), z += sum phi(K).
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      const int tix = w + 4 * i;
+      if (tix < NST) {
+        const int mt = tix / NFT, nt = tix % NFT;
+#pragma unroll
+        for (int ks = 0; ks < STEP / M::KSTEP; ++ks)
+          st[i] = M::mma(tr_frag<T>(&sm.XS[0][0], LDD, 0, 32 * mt, ks, lane, false),
+                         tr_frag<T>(&sm.FS[0][0], LDR, 0, 32 * nt, ks, lane, false), st[i]);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = st[i][4 * g + e];
+          store4(&sm.SF[32 * nt + col][32 * mt + 8 * g + 4 * h], x);
         }
       }
+    }
+    for (int f = tid; f < RP; f += 256) {
+      float zs = 0.0f;
+#pragma unroll 8
+      for (int t = 0; t < STEP; ++t) zs += to_f(sm.FS[t][f]);
+      sm.zr[f] += zs;
     }
     __syncthreads();
   }
@@ -402,6 +399,24 @@ __global__ void __launch_bounds__(256)
 size_t fwd_ws_bytes(const Problem& pb) {
   const size_t slots = partial_slots(pb.N, pb.levels, pb.causal);
   return (size_t)pb.B * pb.H * slots * ((size_t)pb.d * pb.elem + sizeof(float)) + 256;
+}
+
+size_t fwd_lds_need(const Problem& pb) {
+  size_t need = 0;
+  with_T(pb.bf16, [&](auto tp) {
+    using T = ELSAA_T(tp);
+    with_D(pb.d, [&](auto dc) {
+      constexpr int D = ELSAA_C(dc);
+      with_LP(pb.L, [&](auto lc) {
+        constexpr int LP = ELSAA_C(lc);
+        constexpr int STEP = walk_step<T, D, LP, 128>();
+        need = STEP > 0 ? sizeof(WalkSmem<T, D, LP, STEP>) : sizeof(WalkSmem<T, D, LP, 32>);
+      });
+    });
+  });
+  const size_t kt = pb.s < 32 ? 32 : pb.s;
+  const size_t sparse = (size_t)pb.elem * 2 * kt * (pb.d + (pb.bf16 ? 24 : 8)) + 4 * kt;
+  return need > sparse ? need : sparse;
 }
 
 void launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
@@ -433,16 +448,18 @@ void launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
         case 128: run(std::integral_constant<int, 128>{}); break;
         default: run(std::integral_constant<int, 256>{}); break;
       }
+      launch_merge(pb, Opart, Lpart, O_s, lse, st);
       with_LP(pb.L, [&](auto lc) {
         constexpr int LP = ELSAA_C(lc);
-        const int span = pb.causal ? pb.chunk : 64;
-        const int nspan = (pb.N + span - 1) / span;
-        if constexpr (sizeof(EpiSmem<T, D, LP>) <= kLdsBytes)
-        ELSAA_LAUNCH("fwd_epilogue", (fwd_epilogue_kernel<T, D, LP>), dim3(nspan, BH), dim3(256), 0, st,
-                           (const T*)Q, (const T*)K, (const T*)V, planes_lr, A, z,
-                           (const T*)Opart, Lpart, lambda, g_s, g_lr, (T*)O, (T*)O_s, (T*)O_lr,
-                           lse, d_lr, pb.H, pb.N, pb.L, span, pb.levels, (int)pb.causal, pb.s,
-                           pb.scale, pb.tau, pb.eps);
+        constexpr int STEP = walk_step<T, D, LP, 128>();
+        if constexpr (STEP > 0) {
+          const int span = pb.causal ? pb.chunk : STEP;
+          const int nspan = (pb.N + span - 1) / span;
+          ELSAA_LAUNCH("fwd_epilogue", (fwd_epilogue_kernel<T, D, LP, STEP>), dim3(nspan, BH),
+                       dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V, planes_lr, A, z,
+                       (const T*)O_s, lse, lambda, g_s, g_lr, (T*)O, (T*)O_lr, d_lr, pb.H, pb.N,
+                       pb.L, span, (int)pb.causal, pb.scale, pb.tau, pb.eps);
+        }
       });
     });
   });

@@ -8,6 +8,8 @@
 #include <type_traits>
 #include <utility>
 
+#include "common.hpp"
+
 namespace elsaa {
 
 constexpr int kMaxHashBits = 12;
@@ -15,6 +17,32 @@ constexpr int kMaxDh = 128;
 constexpr int kMaxTables = 16;
 constexpr int kLrBits = 4;
 constexpr size_t kLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
+
+constexpr int kMaxLevels = 20;           // log2(N / s) for N <= 2^24, s >= 16
+
+// LDS of the kernels that walk a span of tokens in steps of STEP tokens: one
+// step's row-major channel tile (V, or the low-rank output gradient dnum), its
+// feature tile (phi of the keys or of the queries), the running RACE statistics
+// as an MFMA operand ([feature][channel]), their feature sums and one scalar per
+// token of the step.
+template <typename T, int D, int LP, int STEP>
+struct WalkSmem {
+  static constexpr int RP = 16 * LP, LDD = tile_ld<T>(D), LDR = tile_ld<T>(RP);
+  T XS[STEP][LDD];
+  T FS[STEP][LDR];
+  T SF[RP][LDD];
+  alignas(16) float zr[RP];
+  float dd[STEP];
+};
+
+// Largest step (MAXSTEP, halved down to 32) whose LDS fits; 0 if none does.
+template <typename T, int D, int LP, int MAXSTEP>
+constexpr int walk_step() {
+  return (MAXSTEP >= 128 && sizeof(WalkSmem<T, D, LP, 128>) <= kLdsBytes) ? 128
+         : (MAXSTEP >= 64 && sizeof(WalkSmem<T, D, LP, 64>) <= kLdsBytes) ? 64
+         : sizeof(WalkSmem<T, D, LP, 32>) <= kLdsBytes                    ? 32
+                                                                          : 0;
+}
 
 // Validated problem description with derived sizes.
 struct Problem {
@@ -97,11 +125,18 @@ void launch_summary(const Problem& pb, const void* K, const void* V, const float
                     float* A, float* z, void* ws, hipStream_t st);
 
 size_t fwd_ws_bytes(const Problem& pb);
+size_t fwd_lds_need(const Problem& pb);
 void launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
                 const float* planes_lr, const int32_t* qperm, const int32_t* kperm,
                 const float* A, const float* z, const float* lambda, const float* g_s,
                 const float* g_lr, void* O, void* O_s, void* O_lr, float* lse, float* d_lr,
                 void* ws, hipStream_t st);
+
+// Per-token reductions over the sparse partial slots (merge.hip).
+void launch_merge(const Problem& pb, const void* Opart, const float* Lpart, void* O_s, float* lse,
+                  hipStream_t st);
+void launch_combine(const Problem& pb, const void* dQp, const void* dKp, const void* dVp, void* dQ,
+                    void* dK, void* dV, hipStream_t st);
 
 size_t bwd_ws_bytes(const Problem& pb);
 size_t bwd_lds_need(const Problem& pb);
