@@ -67,69 +67,6 @@ __device__ __forceinline__ void write_grad_row(const floatx16 (&lr)[D / 32], flo
     }
 }
 
-// Loads the running RACE statistics of a walk (fp32 [channel][feature] rows of
-// length r, features f0 .. f0 + RP) into fp32 D tiles st (rows = channels, lanes =
-// features; tile w + 4 i of this wave) and their operand copy SF[feature][channel].
-template <typename T, int D, int LP, int SPW>
-__device__ __forceinline__ void load_stats(const float* Ac, int r, int f0, int w, int lane,
-                                           floatx16 (&st)[SPW], T* SF, int ldd) {
-  constexpr int NFT = LP / 2, NST = (D / 32) * NFT;
-  const int h = lane >> 5, col = lane & 31;
-#pragma unroll
-  for (int i = 0; i < SPW; ++i) {
-    const int tix = w + 4 * i;
-    st[i] = zero16();
-    if (tix < NST) {
-      const int mt = tix / NFT, f = f0 + 32 * (tix % NFT) + col;
-      if (f < r)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) st[i][v] = Ac[(size_t)(32 * mt + acc_row(v, h)) * r + f];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < SPW; ++i) {
-    const int tix = w + 4 * i;
-    if (tix < NST) {
-      const int mt = tix / NFT, fl = 32 * (tix % NFT) + col;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float x[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = st[i][4 * g + e];
-        store4(SF + (size_t)fl * ldd + 32 * mt + 8 * g + 4 * h, x);
-      }
-    }
-  }
-}
-
-// st += X^T F over the STEP rows of the step (X: [token][channel], F:
-// [token][feature], both row-major in LDS), then the operand copy SF.
-template <typename T, int D, int LP, int SPW, int STEP>
-__device__ __forceinline__ void advance_stats(const T* X, int ldd, const T* F, int ldr, int w,
-                                              int lane, floatx16 (&st)[SPW], T* SF) {
-  typedef MF<T> M;
-  constexpr int NFT = LP / 2, NST = (D / 32) * NFT;
-  const int h = lane >> 5, col = lane & 31;
-#pragma unroll
-  for (int i = 0; i < SPW; ++i) {
-    const int tix = w + 4 * i;
-    if (tix < NST) {
-      const int mt = tix / NFT, nt = tix % NFT;
-#pragma unroll
-      for (int ks = 0; ks < STEP / M::KSTEP; ++ks)
-        st[i] = M::mma(tr_frag<T>(X, ldd, 0, 32 * mt, ks, lane, false),
-                       tr_frag<T>(F, ldr, 0, 32 * nt, ks, lane, false), st[i]);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float x[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = st[i][4 * g + e];
-        store4(SF + (size_t)(32 * nt + col) * ldd + 32 * mt + 8 * g + 4 * h, x);
-      }
-    }
-  }
-}
-
 // RT[h][d][p] = R[h][p][d] for p < 4 L, zero up to the row stride pw.
 __global__ void planes_transpose_kernel(const float* __restrict__ R, int L, int D, int pw,
                                         float* __restrict__ RT) {
@@ -473,6 +410,245 @@ __global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
 }
 
 // ---------------------------------------------------------------------------
+// Sparse branch, single pass (bf16, blocks of at most 128 tokens). Persistent
+// workgroups take the selected blocks g, g + G, g + 2G, ... (G = grid size; the
+// blocks of one head are adjacent in g, so concurrent workgroups share a head's
+// rows in the last-level cache). While block g computes, the next block's Q, dO
+// and K rows (and each key wave's V rows) are loaded into registers, and the block
+// after that's row indices.
+//
+// Key wave w owns keys 32 w .. 32 w + 31 (K from LDS, V in registers) and walks
+// the query tiles: S = Q K^T and dP_raw = dO V^T with the keys in lanes, then
+// P = exp(scale S - lse), dS = P (c dP_raw - D) (c = g_s m per query row),
+// dV^T += dO^T (c P) and dK^T += Q^T dS from registers, and dS^T goes to LDS.
+// After a barrier, wave w forms dQ^T = K^T dS^T for query tile w.
+template <int D, int SB>
+struct Sb2Smem {
+  static constexpr int KT = SB < 32 ? 32 : SB;
+  static constexpr int LD = tile_ld<__bf16>(D), LDK = tile_ld<__bf16>(KT);
+  __bf16 Qs[KT][LD];
+  __bf16 Os[KT][LD];    // dO (the row factor c is applied in registers)
+  __bf16 Ks[KT][LD];
+  __bf16 dST[KT][LDK];  // dS^T, [key][query]
+  alignas(16) float lse[KT];  // +inf for rows past the block (P = 0)
+  alignas(16) float Dd[KT];
+  alignas(16) float cq[KT];
+  int qidx[KT], kidx[KT];    // token of each row of this block, -1 past the block
+  int qnext[KT], knext[KT];  // the same for the next block
+};
+
+template <int D, int SB>
+__global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
+    sparse_bwd2_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                       const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                       const float* __restrict__ lse, const float* __restrict__ rc,
+                       const float* __restrict__ rD, const int32_t* __restrict__ qperm,
+                       const int32_t* __restrict__ kperm, int N, int causal, int levels,
+                       float scale, int items, int total, __bf16* __restrict__ dQp,
+                       __bf16* __restrict__ dKp, __bf16* __restrict__ dVp) {
+  typedef __bf16 T;
+  typedef MF<T> M;
+  typedef Sb2Smem<D, SB> Sm;
+  constexpr int KT = Sm::KT, NW = KT / 32, NT = 64 * NW, LD = Sm::LD, LDK = Sm::LDK;
+  constexpr int CH = D / 8, GIT = KT * CH / NT, KS = D / M::KSTEP;
+  __shared__ Sm sm;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int G = gridDim.x;
+  const size_t P = perm_stride(N, levels, causal);
+  const size_t slots = partial_slots(N, levels, causal);
+  const int per_level = causal ? (N / 2) / SB : 0;
+  const int nlev = causal ? levels * per_level : 0;
+
+  // Block g: head, level (-1 for a causal leaf or the non-causal level), rows.
+  auto head_of = [&](int g) __attribute__((always_inline)) { return g / items; };
+  auto lev_of = [&](int g) __attribute__((always_inline)) {
+    const int it = g % items;
+    return causal ? (it < nlev ? it / per_level : -1) : -1;
+  };
+  auto leaf_of = [&](int g) __attribute__((always_inline)) { return causal && (g % items) >= nlev; };
+  // Token of row t (< KT) of block g, -1 past the block.
+  auto rows_of = [&](int g, int t, int& qi, int& kj) __attribute__((always_inline)) {
+    const int bh = g / items, it = g % items;
+    if (t >= SB) {
+      qi = kj = -1;
+    } else if (causal && it >= nlev) {
+      qi = kj = (it - nlev) * SB + t;
+    } else {
+      const size_t off = (size_t)bh * P + (causal ? (size_t)(it / per_level) * (N / 2) +
+                                                        (size_t)(it % per_level) * SB
+                                                  : (size_t)it * SB) + t;
+      qi = qperm[off];
+      kj = kperm[off];
+    }
+  };
+
+  // Registers holding the next block.
+  Vec8<T> pq[GIT], po[GIT], pk[GIT];
+  typename M::frag pv[KS];
+  float plse = 0.0f, pD = 0.0f, pc = 0.0f;
+  bool pvalid = false;
+  int pqi = -1, pki = -1;
+  auto gather = [&](int g) __attribute__((always_inline)) {
+    const size_t rb = (size_t)head_of(g) * N;
+#pragma unroll
+    for (int i = 0; i < GIT; ++i) {
+      const int piece = tid + NT * i, r = piece / CH, c8 = (piece % CH) * 8;
+      const int qi = sm.qnext[r], kj = sm.knext[r];
+      // Rows past the block (s < 32 only) read row 0: their lse (+inf) and key
+      // masks make them contribute nothing.
+      pq[i].load(Q + (rb + max(qi, 0)) * D + c8);
+      po[i].load(dO + (rb + max(qi, 0)) * D + c8);
+      pk[i].load(K + (rb + max(kj, 0)) * D + c8);
+    }
+    const int kv = sm.knext[32 * w + col];
+    prefetch_row_frags<T, D>(V + (rb + max(kv, 0)) * D, pv, h);
+    if (tid < KT) {
+      const int qi = sm.qnext[tid];
+      const size_t k = rb + max(qi, 0);
+      pvalid = qi >= 0;
+      plse = lse[k];
+      pD = rD[k];
+      pc = rc[k];
+    }
+  };
+
+  int g = blockIdx.x;
+  if (g >= total) return;
+  if (tid < KT) rows_of(g, tid, sm.qnext[tid], sm.knext[tid]);
+  __syncthreads();
+  gather(g);
+  if (g + G < total && tid < KT) rows_of(g + G, tid, pqi, pki);
+
+  for (; g < total; g += G) {
+    __syncthreads();  // the previous block is done with LDS
+    // Stage block g from registers.
+#pragma unroll
+    for (int i = 0; i < GIT; ++i) {
+      const int piece = tid + NT * i, r = piece / CH, c8 = (piece % CH) * 8;
+      pq[i].store(&sm.Qs[r][c8]);
+      po[i].store(&sm.Os[r][c8]);
+      pk[i].store(&sm.Ks[r][c8]);
+    }
+    if (tid < KT) {
+      sm.qidx[tid] = sm.qnext[tid];
+      sm.kidx[tid] = sm.knext[tid];
+      sm.qnext[tid] = pqi;
+      sm.knext[tid] = pki;
+      sm.lse[tid] = pvalid ? plse : INFINITY;
+      sm.Dd[tid] = pvalid ? pD : 0.0f;
+      sm.cq[tid] = pvalid ? pc : 0.0f;
+    }
+    typename M::frag vf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) vf[ks] = pv[ks];
+    __syncthreads();
+    // Loads for the next block (rows) and the one after (indices).
+    if (g + G < total) gather(g + G);
+    if (g + 2 * G < total && tid < KT) rows_of(g + 2 * G, tid, pqi, pki);
+
+    const int bh = head_of(g), lev = lev_of(g);
+    const bool leaf = leaf_of(g);
+    // Phase 1: key wave w.
+    {
+      const int key = 32 * w + col;
+      const int jk = sm.kidx[key];
+      const bool kvalid = jk >= 0;
+      typename M::frag kf[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[ks] = row_frag<T>(&sm.Ks[0][0], LD, 32 * w, 0, ks, lane);
+      floatx16 dv[D / 32], dk[D / 32];
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) dv[dt] = dk[dt] = zero16();
+      for (int qt = leaf ? w : 0; qt < NW; ++qt) {
+        floatx16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          s = M::mma(row_frag<T>(&sm.Qs[0][0], LD, 32 * qt, 0, ks, lane), kf[ks], s);
+          dp = M::mma(row_frag<T>(&sm.Os[0][0], LD, 32 * qt, 0, ks, lane), vf[ks], dp);
+        }
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int r0 = 32 * qt + 8 * gg + 4 * h;
+          const floatx4 L4 = *reinterpret_cast<const floatx4*>(&sm.lse[r0]);
+          const floatx4 D4 = *reinterpret_cast<const floatx4*>(&sm.Dd[r0]);
+          const floatx4 C4 = *reinterpret_cast<const floatx4*>(&sm.cq[r0]);
+          float dsv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * gg + e;
+            const bool ok = kvalid && !(leaf && key > r0 + e);
+            const float p = ok ? fast_exp(s[v] * scale - L4[e]) : 0.0f;
+            dsv[e] = p * (C4[e] * dp[v] - D4[e]);
+            s[v] = C4[e] * p;
+            dp[v] = dsv[e];
+          }
+          store4(&sm.dST[key][r0], dsv);
+        }
+#pragma unroll
+        for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
+          const typename M::frag pf = M::from_acc(s, ks2);
+          const typename M::frag sf = M::from_acc(dp, ks2);
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+            dv[dt] = M::mma(tr_frag<T>(&sm.Os[0][0], LD, 32 * qt, 32 * dt, ks2, lane, true), pf, dv[dt]);
+            dk[dt] = M::mma(tr_frag<T>(&sm.Qs[0][0], LD, 32 * qt, 32 * dt, ks2, lane, true), sf, dk[dt]);
+          }
+        }
+      }
+      if (kvalid) {
+        const size_t ksl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_past(jk, N, lev)
+                                    : (size_t)jk;
+        T* dvp = dVp + ((size_t)bh * slots + ksl) * D;
+        T* dkp = dKp + ((size_t)bh * slots + ksl) * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            float xv[4], xk[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              xv[e] = dv[dt][4 * gg + e];
+              xk[e] = dk[dt][4 * gg + e] * scale;
+            }
+            store4(dvp + 32 * dt + 8 * gg + 4 * h, xv);
+            store4(dkp + 32 * dt + 8 * gg + 4 * h, xk);
+          }
+      }
+    }
+    __syncthreads();  // dS^T complete
+    // Phase 2: dQ^T = K^T dS^T for query tile w (leaf blocks: keys up to the tile).
+    {
+      const int query = 32 * w + col;
+      const int iq = sm.qidx[query];
+      floatx16 dq[D / 32];
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) dq[dt] = zero16();
+      const int nks = leaf ? 2 * (w + 1) : KT / M::KSTEP;
+      for (int ks = 0; ks < nks; ++ks) {
+        const typename M::frag bq = tr_frag<T>(&sm.dST[0][0], LDK, 0, 32 * w, ks, lane, false);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          dq[dt] = M::mma(tr_frag<T>(&sm.Ks[0][0], LD, 0, 32 * dt, ks, lane, false), bq, dq[dt]);
+      }
+      if (iq >= 0) {
+        const size_t sl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_future_b(iq, N, lev)
+                                   : (size_t)iq;
+        T* dst = dQp + ((size_t)bh * slots + sl) * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = dq[dt][4 * gg + e] * scale;
+            store4(dst + 32 * dt + 8 * gg + 4 * h, x);
+          }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Low-rank branch, query side: one head and span per workgroup, walked forwards in
 // steps of STEP tokens by 4 waves; wave w < STEP / 32 owns the step's query tile w.
 // LDS (WalkSmem): V (XS) and phi(K) (FS) of the step's keys, the running key
@@ -493,6 +669,7 @@ __global__ void __launch_bounds__(256)
   constexpr int QT = STEP / 32, NST = NFT * (D / 32), SPW = (NST + 3) / 4;
   constexpr int VCH = D / 8, VIT = (STEP * VCH + 255) / 256;
   __shared__ Sm sm;
+  __shared__ T RTs[D * rt_lds_width<LPG>()];
   const int bh = blockIdx.y, c = blockIdx.x, head = bh % H;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int r = 16 * L, f0 = 128 * grp, Lg = min(8, L - 8 * grp);
@@ -508,27 +685,27 @@ __global__ void __launch_bounds__(256)
 
   floatx16 st[SPW];
   load_stats<T, D, LPG, SPW>(A + sidx * D * r, r, f0, w, lane, st, &sm.SF[0][0], LDD);
+  stage_rt<T, D, LPG, 256>(RT + (size_t)head * D * pw + 32 * grp, pw, RTs, tid);
   for (int f = tid; f < RP; f += 256) sm.zr[f] = f0 + f < r ? z[sidx * r + f0 + f] : 0.0f;
 
   typename M::frag qx[D / M::KSTEP], ox[D / M::KSTEP], kx[D / M::KSTEP];
   Vec8<T> vb[VIT];
   float eq = 0.0f, ddq = 0.0f;
   auto load_rows = [&](int s0) __attribute__((always_inline)) {
+    // Tokens past the span read a stand-in row; their dnum and dd_lr are zeroed
+    // where used and their phi(K) rows are stored as zero.
     const int tok = s0 + 32 * w + col;
-    const bool valid = qwave && tok < t_end;
     const size_t rrow = (size_t)min(tok, N - 1) * D;
-    load_row_frags<T, D>(Qh + rrow, valid, qx, h);
-    load_row_frags<T, D>(dOh + rrow, valid, ox, h);
+    prefetch_row_frags<T, D>(Qh + rrow, qx, h);
+    prefetch_row_frags<T, D>(dOh + rrow, ox, h);
     eq = re[(size_t)bh * N + min(tok, N - 1)];
     ddq = rdd[(size_t)bh * N + min(tok, N - 1)];
-    if (!valid) eq = ddq = 0.0f;
     if (causal) {
-      load_row_frags<T, D>(Kh + rrow, valid, kx, h);
+      prefetch_row_frags<T, D>(Kh + rrow, kx, h);
 #pragma unroll
       for (int i = 0; i < VIT; ++i) {
         const int it = tid + 256 * i, t = it / VCH, tk = s0 + t;
-        vb[i].load_if(Vh + (size_t)min(tk, N - 1) * D + (it % VCH) * 8,
-                      it < STEP * VCH && tk < t_end);
+        if (it < STEP * VCH) vb[i].load(Vh + (size_t)min(tk, N - 1) * D + (it % VCH) * 8);
       }
     }
   };
@@ -561,6 +738,7 @@ __global__ void __launch_bounds__(256)
     }
     Feat Fq;
     typename M::frag dn[D / M::KSTEP];
+    const float e_q = qvalid ? eq : 0.0f, dd_q = qvalid ? ddq : 0.0f;
     if (qwave) {
       Fq.compute(qx, pl, Lg, scale, tau, lane);
 #pragma unroll
@@ -568,9 +746,9 @@ __global__ void __launch_bounds__(256)
         float x[M::KPL];
         if constexpr (M::KPL == 8) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = (float)ox[ks][e] * eq;
+          for (int e = 0; e < 8; ++e) x[e] = (float)ox[ks][e] * e_q;
         } else {
-          x[0] = ox[ks] * eq;
+          x[0] = ox[ks] * e_q;
         }
         dn[ks] = M::from_floats(x);
       }
@@ -590,7 +768,7 @@ __global__ void __launch_bounds__(256)
         for (int ks = 0; ks < D / M::KSTEP; ++ks)
           df[ft] = M::mma(row_frag<T>(&sm.SF[0][0], LDD, 32 * ft, 0, ks, lane), dn[ks], df[ft]);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) df[ft][v] += sm.zr[32 * ft + acc_row(v, h)] * ddq;
+        for (int v = 0; v < 16; ++v) df[ft][v] += sm.zr[32 * ft + acc_row(v, h)] * dd_q;
       }
       if (causal) {
         for (int kt = 0; kt <= w; ++kt) {
@@ -600,7 +778,7 @@ __global__ void __launch_bounds__(256)
             gt = M::mma(row_frag<T>(&sm.XS[0][0], LDD, 32 * kt, 0, ks, lane), dn[ks], gt);
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            gt[v] += ddq;
+            gt[v] += dd_q;
             if (kt == w && acc_row(v, h) > col) gt[v] = 0.0f;
           }
 #pragma unroll
@@ -620,7 +798,7 @@ __global__ void __launch_bounds__(256)
         Fq.backward_table(ft, dphi, da[ft]);
       }
       floatx16 dx[D / 32];
-      features_dx<T, D, LPG>(da, RT + (size_t)head * D * pw + 32 * grp, pw, c2, lane, dx);
+      features_dx<T, D, LPG>(da, RTs, rt_lds_width<LPG>(), c2, lane, dx);
       if (qvalid)
         write_grad_row<T, D>(dx, scratch, dQ, ((size_t)bh * N + qtok) * D, h, first != 0,
                              last != 0);
@@ -628,13 +806,8 @@ __global__ void __launch_bounds__(256)
     load_rows(s0 + STEP);  // past the span: loads nothing
     if (!causal) break;
     __syncthreads();
-    advance_stats<T, D, LPG, SPW, STEP>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, w, lane, st, &sm.SF[0][0]);
-    for (int f = tid; f < RP; f += 256) {
-      float zs = 0.0f;
-#pragma unroll 8
-      for (int t = 0; t < STEP; ++t) zs += to_f(sm.FS[t][f]);
-      sm.zr[f] += zs;
-    }
+    advance_stats<T, D, LPG, SPW, STEP>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, nullptr, w, lane, st,
+                                        &sm.SF[0][0], sm.zr);
     __syncthreads();
   }
 }
@@ -663,6 +836,7 @@ __global__ void __launch_bounds__(256)
   constexpr int VCH = D / 8, NDW = QT < 2 ? 1 : QT;  // dO staging waves
   constexpr int OIT = (STEP * VCH + 64 * NDW - 1) / (64 * NDW);
   __shared__ Sm sm;
+  __shared__ T RTs[D * rt_lds_width<LPG>()];
   const int bh = blockIdx.y, c = blockIdx.x, head = bh % H;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int kt = w % QT, role = w / QT;  // role 0: dK, 1: dV, 2+: staging only
@@ -682,6 +856,7 @@ __global__ void __launch_bounds__(256)
 
   floatx16 st[SPW];
   load_stats<T, D, LPG, SPW>(G + sidx * D * r, r, f0, w, lane, st, &sm.SF[0][0], LDD);
+  stage_rt<T, D, LPG, 256>(RT + (size_t)head * D * pw + 32 * grp, pw, RTs, tid);
   for (int f = tid; f < RP; f += 256) sm.zr[f] = f0 + f < r ? gzs[sidx * r + f0 + f] : 0.0f;
 
   typename M::frag qx[D / M::KSTEP], kx[D / M::KSTEP], vx[D / M::KSTEP];
@@ -689,29 +864,25 @@ __global__ void __launch_bounds__(256)
   float oe[OIT];
   float ddv = 0.0f;
   auto load_rows = [&](int s0) __attribute__((always_inline)) {
-    const bool live = s0 >= t_beg;
+    // Tokens outside the span read a stand-in row: their phi(Q) rows are stored
+    // as zero, their dnum rows and dd_lr are zeroed when staged, and no key
+    // result of theirs is written. Nothing is loaded before the span.
+    if (s0 < t_beg) return;
     const int qtok = s0 + 32 * w + col;  // query tile w (waves < QT) for phi(Q)
-    load_row_frags<T, D>(Qh + (size_t)min(max(qtok, 0), N - 1) * D, live && w < QT && qtok < t_end,
-                         qx, h);
+    if (w < QT) prefetch_row_frags<T, D>(Qh + (size_t)min(qtok, N - 1) * D, qx, h);
     const int ktok = s0 + 32 * kt + col;
-    const size_t krow = (size_t)min(max(ktok, 0), N - 1) * D;
-    load_row_frags<T, D>(Kh + krow, live && kwave && ktok < t_end, kx, h);
-    load_row_frags<T, D>(Vh + krow, live && role == 0 && ktok < t_end, vx, h);
+    const size_t krow = (size_t)min(ktok, N - 1) * D;
+    if (kwave) prefetch_row_frags<T, D>(Kh + krow, kx, h);
+    if (role == 0) prefetch_row_frags<T, D>(Vh + krow, vx, h);
     if (owave) {
 #pragma unroll
       for (int i = 0; i < OIT; ++i) {
-        const int it = 64 * ow + lane + 64 * NDW * i, t = it / VCH, tk = s0 + t;
-        const bool ok = live && it < STEP * VCH && tk < t_end;
-        const int tc = min(max(tk, 0), N - 1);
-        ob[i].load_if(dOh + (size_t)tc * D + (it % VCH) * 8, ok);
+        const int it = 64 * ow + lane + 64 * NDW * i, t = it / VCH;
+        const int tc = min(s0 + t, N - 1);
+        if (it < STEP * VCH) ob[i].load(dOh + (size_t)tc * D + (it % VCH) * 8);
         oe[i] = re[(size_t)bh * N + tc];
-        if (!ok) oe[i] = 0.0f;
       }
-      if (ow == 0) {
-        const int tk = s0 + lane;
-        ddv = rdd[(size_t)bh * N + min(max(tk, 0), N - 1)];
-        if (!(live && lane < STEP && tk < t_end)) ddv = 0.0f;
-      }
+      if (ow == 0) ddv = rdd[(size_t)bh * N + min(s0 + lane, N - 1)];
     }
   };
   const int nstep = (t_end - t_beg + STEP - 1) / STEP;
@@ -740,11 +911,11 @@ __global__ void __launch_bounds__(256)
       for (int i = 0; i < OIT; ++i) {
         const int it = 64 * ow + lane + 64 * NDW * i;
         if (it < STEP * VCH) {
-          ob[i].scale(oe[i]);
+          ob[i].scale(s0 + it / VCH < t_end ? oe[i] : 0.0f);
           ob[i].store(&sm.XS[it / VCH][(it % VCH) * 8]);
         }
       }
-      if (ow == 0 && lane < STEP) sm.dd[lane] = ddv;
+      if (ow == 0 && lane < STEP) sm.dd[lane] = s0 + lane < t_end ? ddv : 0.0f;
     }
     const int ktok = s0 + 32 * kt + col;
     const bool kvalid = kwave && ktok < t_end;
@@ -793,7 +964,7 @@ __global__ void __launch_bounds__(256)
         Fk.backward_table(ft, dphi, da[ft]);
       }
       floatx16 dx[D / 32];
-      features_dx<T, D, LPG>(da, RT + (size_t)head * D * pw + 32 * grp, pw, c2, lane, dx);
+      features_dx<T, D, LPG>(da, RTs, rt_lds_width<LPG>(), c2, lane, dx);
       if (kvalid)
         write_grad_row<T, D>(dx, scrK, dK, ((size_t)bh * N + ktok) * D, h, first != 0,
                              last != 0);
@@ -834,13 +1005,8 @@ __global__ void __launch_bounds__(256)
     load_rows(s0 - STEP);  // before the span: loads nothing
     if (!causal) break;
     __syncthreads();
-    advance_stats<T, D, LPG, SPW, STEP>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, w, lane, st, &sm.SF[0][0]);
-    for (int f = tid; f < RP; f += 256) {
-      float s = 0.0f;
-#pragma unroll 8
-      for (int t = 0; t < STEP; ++t) s += to_f(sm.FS[t][f]) * sm.dd[t];
-      sm.zr[f] += s;
-    }
+    advance_stats<T, D, LPG, SPW, STEP>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, sm.dd, w, lane, st,
+                                        &sm.SF[0][0], sm.zr);
     __syncthreads();
   }
 }
@@ -850,6 +1016,21 @@ __global__ void __launch_bounds__(256)
 namespace {
 
 int rt_stride(const Problem& pb);
+
+// Workgroups of a persistent launch: as many as fit on the device at once.
+int persistent_grid(const void* kern, int threads, int total) {
+  static int cus[64] = {0};
+  int dev = 0;
+  hipGetDevice(&dev);
+  int& n = cus[dev & 63];
+  if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    n = 256;
+  int per = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, threads, 0) != hipSuccess || per < 1)
+    per = 1;
+  const long g = (long)n * per;
+  return (int)(g < total ? g : total);
+}
 
 struct BwdLayout {
   size_t rows, dlam, parts, gsum, gstate, rt, scratch, total;
@@ -897,9 +1078,10 @@ size_t bwd_lds_need(const Problem& pb) {
       constexpr int D = ELSAA_C(dc);
       auto need = [&](auto lc) {
         constexpr int LPG = ELSAA_C(lc);
-        constexpr int SQ = walk_step<T, D, LPG, 128>(), SK = walk_step<T, D, LPG, 64>();
-        const size_t a = SQ > 0 ? sizeof(WalkSmem<T, D, LPG, SQ>) : sizeof(WalkSmem<T, D, LPG, 32>);
-        const size_t b = SK > 0 ? sizeof(WalkSmem<T, D, LPG, SK>) : sizeof(WalkSmem<T, D, LPG, 32>);
+        constexpr size_t RTB = sizeof(T) * D * rt_lds_width<LPG>();
+        constexpr int SQ = walk_step<T, D, LPG, 128, RTB>(), SK = walk_step<T, D, LPG, 64, RTB>();
+        const size_t a = RTB + (SQ > 0 ? sizeof(WalkSmem<T, D, LPG, SQ>) : sizeof(WalkSmem<T, D, LPG, 32>));
+        const size_t b = RTB + (SK > 0 ? sizeof(WalkSmem<T, D, LPG, SK>) : sizeof(WalkSmem<T, D, LPG, 32>));
         lr = a > b ? a : b;
       };
       switch (padded_tables(pb.L)) {
@@ -962,7 +1144,16 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
       auto run_sparse = [&](auto sc) {
         constexpr int SB = ELSAA_C(sc);
         const dim3 grid(items, BH);
-        if constexpr (sizeof(SbwdSmem<T, D, SB, 3>) <= kLdsBytes && SB <= 128) {
+        if constexpr (std::is_same_v<T, __bf16> && SB <= 128 &&
+                      sizeof(Sb2Smem<D, SB>) <= kLdsBytes) {
+          constexpr int NT = 64 * (SB < 32 ? 1 : SB / 32);
+          const int total = items * (int)BH;
+          const int G = persistent_grid((const void*)sparse_bwd2_kernel<D, SB>, NT, total);
+          ELSAA_LAUNCH("sparse_bwd", (sparse_bwd2_kernel<D, SB>), dim3(G), dim3(NT), 0, st,
+                       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, lse, rc, rD, qperm,
+                       kperm, pb.N, (int)pb.causal, pb.levels, pb.scale, items, total, (T*)dQp,
+                       (T*)dKp, (T*)dVp);
+        } else if constexpr (sizeof(SbwdSmem<T, D, SB, 3>) <= kLdsBytes && SB <= 128) {
           ELSAA_LAUNCH("sparse_bwd", (sparse_bwd_kernel<T, D, SB, 3>), grid,
                        dim3(sbwd_threads<SB>(3)), 0, st, (const T*)Q, (const T*)K, (const T*)V,
                        (const T*)dO, lse, rc, rD, qperm, kperm, pb.N, (int)pb.causal, pb.levels,
@@ -987,7 +1178,8 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
       }
       auto run_lr = [&](auto lc) {
         constexpr int LPG = ELSAA_C(lc);
-        constexpr int SQ = walk_step<T, D, LPG, 128>(), SK = walk_step<T, D, LPG, 64>();
+        constexpr size_t RTB = sizeof(T) * D * rt_lds_width<LPG>();
+        constexpr int SQ = walk_step<T, D, LPG, 128, RTB>(), SK = walk_step<T, D, LPG, 64, RTB>();
         if constexpr (SQ > 0 && SK > 0) {
           const int span_q = pb.causal ? pb.chunk : SQ;
           const int span_k = pb.causal ? pb.chunk : SK;

@@ -246,11 +246,6 @@ struct Vec8<__bf16> {
     for (int e = 0; e < 8; ++e) v[e] = (__bf16)((float)v[e] * c);
   }
   __device__ __forceinline__ void store(__bf16* p) const { *reinterpret_cast<bf16x8*>(p) = v; }
-  // Reads p (which must be readable) and keeps the value only if ok.
-  __device__ __forceinline__ void load_if(const __bf16* p, bool ok) {
-    load(p);
-    if (!ok) zero();
-  }
   __device__ __forceinline__ float get(int e) const { return (float)v[e]; }
 };
 template <>
@@ -271,10 +266,6 @@ struct Vec8<float> {
   __device__ __forceinline__ void store(float* p) const {
     *reinterpret_cast<floatx4*>(p) = a;
     *reinterpret_cast<floatx4*>(p + 4) = b;
-  }
-  __device__ __forceinline__ void load_if(const float* p, bool ok) {
-    load(p);
-    if (!ok) zero();
   }
   __device__ __forceinline__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
 };
@@ -316,8 +307,30 @@ __device__ __forceinline__ void gather_rows(T* const (&dst)[NX], int ld, const T
   }
 }
 
+// x of lane l % 32 (lo) and of lane l % 32 + 32 (hi), for every lane l, with one
+// v_permlane32_swap (a VALU operation: no LDS round trip).
+struct HalfPair {
+  float lo, hi;
+};
+__device__ __forceinline__ HalfPair half_pair(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
 // Value of the other lane half (lane ^ 32).
-__device__ __forceinline__ float swap_half(float x) { return __shfl_xor(x, 32, 64); }
+__device__ __forceinline__ float swap_half(float x) {
+  const HalfPair p = half_pair(x);
+  return (threadIdx.x & 32) ? p.lo : p.hi;
+}
+// x + swap_half(x) and max(x, swap_half(x)), the same in both halves.
+__device__ __forceinline__ float sum_halves(float x) {
+  const HalfPair p = half_pair(x);
+  return p.lo + p.hi;
+}
+__device__ __forceinline__ float max_halves(float x) {
+  const HalfPair p = half_pair(x);
+  return fmaxf(p.lo, p.hi);
+}
 
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
@@ -334,16 +347,27 @@ __device__ __forceinline__ unsigned gray_rank(unsigned c) {
 
 // Row fragments of one token row in global memory (B operand of a product over
 // the row's D elements; lane half h holds elements ks * KSTEP + KPL h + e).
-// The row is always read (x must point to a valid row); invalid rows give zeros.
+// Invalid rows give zero fragments (x is not read for them).
 template <typename T, int D>
 __device__ __forceinline__ void load_row_frags(const T* x, bool valid,
                                                typename MF<T>::frag (&f)[D / MF<T>::KSTEP], int h) {
   typedef MF<T> M;
 #pragma unroll
-  for (int ks = 0; ks < D / M::KSTEP; ++ks) f[ks] = M::load(x + ks * M::KSTEP + M::KPL * h);
-  if (!valid)
+  for (int ks = 0; ks < D / M::KSTEP; ++ks)
+    f[ks] = valid ? M::load(x + ks * M::KSTEP + M::KPL * h) : M::zero();
+}
+
+// The same row fragments, always read (x must point to a readable row). Nothing
+// here depends on the loaded values, so the loads stay in flight until the
+// fragments are used; a caller that loads a stand-in row for a token that does not
+// exist must keep it from mattering where it is used.
+template <typename T, int D>
+__device__ __forceinline__ void prefetch_row_frags(const T* x,
+                                                   typename MF<T>::frag (&f)[D / MF<T>::KSTEP],
+                                                   int h) {
+  typedef MF<T> M;
 #pragma unroll
-    for (int ks = 0; ks < D / M::KSTEP; ++ks) f[ks] = M::zero();
+  for (int ks = 0; ks < D / M::KSTEP; ++ks) f[ks] = M::load(x + ks * M::KSTEP + M::KPL * h);
 }
 
 // 4 consecutive elements in registers.
@@ -587,8 +611,8 @@ __device__ __forceinline__ void tile_to_table(const floatx16& acc, int h, float 
 // the lane half, jp = q / 4, t = q % 4) is the accumulator-row order, so the
 // hyperplanes are read from RT = R^T ([D][row stride pw] fp32, zero past 4 L) with
 // the same two-run pattern as load_accperm.
-template <typename T, int D, int LP>
-__device__ __forceinline__ void features_dx(const float (&da)[LP / 2][4], const float* RT, int pw,
+template <typename T, int D, int LP, typename R>
+__device__ __forceinline__ void features_dx(const float (&da)[LP / 2][4], const R* RT, int pw,
                                             float c2, int lane, floatx16 (&dx)[D / 32]) {
   typedef MF<T> M;
   constexpr int NQ = 2 * LP;  // (table, hyperplane) pairs per lane half
@@ -607,7 +631,7 @@ __device__ __forceinline__ void features_dx(const float (&da)[LP / 2][4], const 
     const typename M::frag bf = M::from_floats(b);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      const float* row = RT + (size_t)(32 * dt + col) * pw;
+      const R* row = RT + (size_t)(32 * dt + col) * pw;
       float a[M::KPL];
       if constexpr (M::KPL == 8) {
         float lo[4], hi[4];
@@ -616,7 +640,7 @@ __device__ __forceinline__ void features_dx(const float (&da)[LP / 2][4], const 
 #pragma unroll
         for (int e = 0; e < 4; ++e) { a[e] = lo[e]; a[4 + e] = hi[e]; }
       } else {
-        a[0] = row[acc_row(ks, h)];
+        a[0] = (float)row[acc_row(ks, h)];
       }
       dx[dt] = M::mma(M::from_floats(a), bf, dx[dt]);
     }
@@ -625,6 +649,106 @@ __device__ __forceinline__ void features_dx(const float (&da)[LP / 2][4], const 
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) dx[dt][v] *= c2;
+}
+
+// Row stride of the transposed hyperplanes staged in LDS for features_dx (which
+// reads columns up to max(16, 4 LP)); 2 (mod 4) dwords keeps its row reads apart.
+template <int LP>
+constexpr int rt_lds_width() { return (4 * LP > 16 ? 4 * LP : 16) + 4; }
+
+// RTs[d][p] = RT[d * pw + p] for p < 4 LP, zero beyond (NT threads).
+template <typename T, int D, int LP, int NT>
+__device__ __forceinline__ void stage_rt(const float* RT, int pw, T* RTs, int tid) {
+  constexpr int W = rt_lds_width<LP>();
+  for (int i = tid; i < D * W; i += NT) {
+    const int d = i / W, p = i % W;
+    RTs[i] = from_f<T>(p < 4 * LP ? RT[(size_t)d * pw + p] : 0.0f);
+  }
+}
+
+// Loads the running RACE statistics of a walk (fp32 [channel][feature] rows of
+// length r, features f0 .. f0 + RP) into fp32 D tiles st (rows = channels, lanes =
+// features; tile w + 4 i of this wave) and their operand copy SF[feature][channel].
+template <typename T, int D, int LP, int SPW>
+__device__ __forceinline__ void load_stats(const float* Ac, int r, int f0, int w, int lane,
+                                           floatx16 (&st)[SPW], T* SF, int ldd) {
+  constexpr int NFT = LP / 2, NST = (D / 32) * NFT;
+  const int h = lane >> 5, col = lane & 31;
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    const int tix = w + 4 * i;
+    st[i] = zero16();
+    if (tix < NST) {
+      const int mt = tix / NFT, f = f0 + 32 * (tix % NFT) + col;
+      if (f < r)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) st[i][v] = Ac[(size_t)(32 * mt + acc_row(v, h)) * r + f];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    const int tix = w + 4 * i;
+    if (tix < NST) {
+      const int mt = tix / NFT, fl = 32 * (tix % NFT) + col;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = st[i][4 * g + e];
+        store4(SF + (size_t)fl * ldd + 32 * mt + 8 * g + 4 * h, x);
+      }
+    }
+  }
+}
+
+// Advances the statistics by one step of STEP tokens: st += X^T F (X: [token]
+// [channel], F: [token][feature], both row-major in LDS), rewrites the operand
+// copy SF, and adds sum_t wt[t] F[t][f] (wt == nullptr: weights 1) to zr[f]. The
+// feature sums are products with a constant-row A operand, formed by the wave that
+// owns channel tile 0 of each feature tile; bf16 weights are split into hi + lo
+// parts (two products).
+template <typename T, int D, int LP, int SPW, int STEP>
+__device__ __forceinline__ void advance_stats(const T* X, int ldd, const T* F, int ldr,
+                                              const float* wt, int w, int lane,
+                                              floatx16 (&st)[SPW], T* SF, float* zr) {
+  typedef MF<T> M;
+  constexpr int NFT = LP / 2, NST = (D / 32) * NFT;
+  const int h = lane >> 5, col = lane & 31;
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    const int tix = w + 4 * i;
+    if (tix < NST) {
+      const int mt = tix / NFT, nt = tix % NFT;
+      floatx16 zs = zero16();
+#pragma unroll
+      for (int ks = 0; ks < STEP / M::KSTEP; ++ks) {
+        const typename M::frag fb = tr_frag<T>(F, ldr, 0, 32 * nt, ks, lane, false);
+        st[i] = M::mma(tr_frag<T>(X, ldd, 0, 32 * mt, ks, lane, false), fb, st[i]);
+        if (mt == 0) {
+          float a[M::KPL];
+#pragma unroll
+          for (int e = 0; e < M::KPL; ++e) a[e] = wt ? wt[ks * M::KSTEP + M::KPL * h + e] : 1.0f;
+          const typename M::frag ahi = M::from_floats(a);
+          zs = M::mma(ahi, fb, zs);
+          if constexpr (M::KPL > 1) {
+            if (wt) {
+#pragma unroll
+              for (int e = 0; e < M::KPL; ++e) a[e] -= (float)ahi[e];
+              zs = M::mma(M::from_floats(a), fb, zs);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = st[i][4 * g + e];
+        store4(SF + (size_t)(32 * nt + col) * ldd + 32 * mt + 8 * g + 4 * h, x);
+      }
+      if (mt == 0 && h == 0) zr[32 * nt + col] += zs[0];
+    }
+  }
 }
 
 }  // namespace elsaa

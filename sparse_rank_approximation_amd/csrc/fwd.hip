@@ -118,7 +118,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
       sacc[v] = masked ? -INFINITY : sacc[v] * scale;
       mx = fmaxf(mx, sacc[v]);
     }
-    mx = fmaxf(mx, swap_half(mx));
+    mx = max_halves(mx);
     const float mnew = fmaxf(mrun, mx);
     const float msub = mnew == -INFINITY ? 0.0f : mnew;
     const float alpha = fast_exp(mrun - msub);
@@ -128,7 +128,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
       sacc[v] = fast_exp(sacc[v] - msub);
       ps += sacc[v];
     }
-    ps += swap_half(ps);
+    ps = sum_halves(ps);
     lrun = lrun * alpha + ps;
     mrun = mnew;
 #pragma unroll
@@ -208,31 +208,7 @@ __global__ void __launch_bounds__(256)
   const float* Ac = A + sidx * D * r;
   const float* zc = z + sidx * r;
   floatx16 st[SPW];
-#pragma unroll
-  for (int i = 0; i < SPW; ++i) {
-    const int tix = w + 4 * i;
-    st[i] = zero16();
-    if (tix < NST) {
-      const int mt = tix / NFT, f = 32 * (tix % NFT) + col;
-      if (f < r)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) st[i][v] = Ac[(size_t)(32 * mt + acc_row(v, h)) * r + f];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < SPW; ++i) {
-    const int tix = w + 4 * i;
-    if (tix < NST) {
-      const int mt = tix / NFT, f = 32 * (tix % NFT) + col;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float x[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = st[i][4 * g + e];
-        store4(&sm.SF[f][32 * mt + 8 * g + 4 * h], x);
-      }
-    }
-  }
+  load_stats<T, D, LP, SPW>(Ac, r, 0, w, lane, st, &sm.SF[0][0], LDD);
   for (int f = tid; f < RP; f += 256) sm.zr[f] = f < r ? zc[f] : 0.0f;
 
   // Global rows of one step, loaded one step ahead: this wave's query tile, the
@@ -241,15 +217,17 @@ __global__ void __launch_bounds__(256)
   Vec8<T> vb[VIT];
   auto load_rows = [&](int s0) __attribute__((always_inline)) {
     const int qtok = s0 + 32 * qt + col;
-    load_row_frags<T, D>(Qh + (size_t)min(qtok, N - 1) * D, qtok < t_end, qx, h);
+    // Tokens past the span read a stand-in row: their phi(Q) rows are not
+    // written out and their phi(K) rows are stored as zero, which also cancels
+    // their V rows in every product.
+    prefetch_row_frags<T, D>(Qh + (size_t)min(qtok, N - 1) * D, qx, h);
     if (causal) {
       const int ktok = s0 + 32 * w + col;
-      if (w < QT) load_row_frags<T, D>(Kh + (size_t)min(ktok, N - 1) * D, ktok < t_end, kx, h);
+      if (w < QT) prefetch_row_frags<T, D>(Kh + (size_t)min(ktok, N - 1) * D, kx, h);
 #pragma unroll
       for (int i = 0; i < VIT; ++i) {
         const int it = tid + 256 * i, t = it / VCH, tok = s0 + t;
-        vb[i].load_if(Vh + (size_t)min(tok, N - 1) * D + (it % VCH) * 8,
-                      it < STEP * VCH && tok < t_end);
+        if (it < STEP * VCH) vb[i].load(Vh + (size_t)min(tok, N - 1) * D + (it % VCH) * 8);
       }
     }
   };
@@ -309,7 +287,7 @@ __global__ void __launch_bounds__(256)
           for (int e = 0; e < 4; ++e) d4[e] += Fq.phi[jp][4 * q4 + e] * zz[e];
         }
       float den = (d4[0] + d4[1]) + (d4[2] + d4[3]);
-      den += swap_half(den);
+      den = sum_halves(den);
 #pragma unroll
       for (int ks = 0; ks < RP / M::KSTEP; ++ks) {
         const typename M::frag fb = Fq.frag(ks);
@@ -338,7 +316,7 @@ __global__ void __launch_bounds__(256)
               num[dt] = M::mma(tr_frag<T>(&sm.XS[0][0], LDD, 32 * kt, 32 * (dt0 + dt), ks2, lane, true), wf, num[dt]);
           }
         }
-        den += dintra + swap_half(dintra);
+        den += sum_halves(dintra);
       }
 
       if (qvalid) {
@@ -368,30 +346,8 @@ __global__ void __launch_bounds__(256)
     __syncthreads();
 
     // Advance the statistics by the step's keys: S^T += V^T phi(K), z += sum phi(K).
-#pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-      const int tix = w + 4 * i;
-      if (tix < NST) {
-        const int mt = tix / NFT, nt = tix % NFT;
-#pragma unroll
-        for (int ks = 0; ks < STEP / M::KSTEP; ++ks)
-          st[i] = M::mma(tr_frag<T>(&sm.XS[0][0], LDD, 0, 32 * mt, ks, lane, false),
-                         tr_frag<T>(&sm.FS[0][0], LDR, 0, 32 * nt, ks, lane, false), st[i]);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float x[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = st[i][4 * g + e];
-          store4(&sm.SF[32 * nt + col][32 * mt + 8 * g + 4 * h], x);
-        }
-      }
-    }
-    for (int f = tid; f < RP; f += 256) {
-      float zs = 0.0f;
-#pragma unroll 8
-      for (int t = 0; t < STEP; ++t) zs += to_f(sm.FS[t][f]);
-      sm.zr[f] += zs;
-    }
+    advance_stats<T, D, LP, SPW, STEP>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, nullptr, w, lane, st,
+                                       &sm.SF[0][0], sm.zr);
     __syncthreads();
   }
 }

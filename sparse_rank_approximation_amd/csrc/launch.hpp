@@ -35,13 +35,14 @@ struct WalkSmem {
   float dd[STEP];
 };
 
-// Largest step (MAXSTEP, halved down to 32) whose LDS fits; 0 if none does.
-template <typename T, int D, int LP, int MAXSTEP>
+// Largest step (MAXSTEP, halved down to 32) whose LDS, plus EXTRA bytes of the
+// kernel's own, fits; 0 if none does.
+template <typename T, int D, int LP, int MAXSTEP, size_t EXTRA = 0>
 constexpr int walk_step() {
-  return (MAXSTEP >= 128 && sizeof(WalkSmem<T, D, LP, 128>) <= kLdsBytes) ? 128
-         : (MAXSTEP >= 64 && sizeof(WalkSmem<T, D, LP, 64>) <= kLdsBytes) ? 64
-         : sizeof(WalkSmem<T, D, LP, 32>) <= kLdsBytes                    ? 32
-                                                                          : 0;
+  return (MAXSTEP >= 128 && sizeof(WalkSmem<T, D, LP, 128>) + EXTRA <= kLdsBytes) ? 128
+         : (MAXSTEP >= 64 && sizeof(WalkSmem<T, D, LP, 64>) + EXTRA <= kLdsBytes) ? 64
+         : sizeof(WalkSmem<T, D, LP, 32>) + EXTRA <= kLdsBytes                    ? 32
+                                                                                  : 0;
 }
 
 // Validated problem description with derived sizes.
