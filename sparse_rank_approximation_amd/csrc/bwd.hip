@@ -670,6 +670,7 @@ __global__ void __launch_bounds__(256)
   constexpr int VCH = D / 8, VIT = (STEP * VCH + 255) / 256;
   __shared__ Sm sm;
   __shared__ T RTs[D * rt_lds_width<LPG>()];
+  __shared__ PlanesLds<T, D, LPG> PLs;
   const int bh = blockIdx.y, c = blockIdx.x, head = bh % H;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int r = 16 * L, f0 = 128 * grp, Lg = min(8, L - 8 * grp);
@@ -686,6 +687,11 @@ __global__ void __launch_bounds__(256)
   floatx16 st[SPW];
   load_stats<T, D, LPG, SPW>(A + sidx * D * r, r, f0, w, lane, st, &sm.SF[0][0], LDD);
   stage_rt<T, D, LPG, 256>(RT + (size_t)head * D * pw + 32 * grp, pw, RTs, tid);
+  stage_planes<T, D, LPG, 256>(pl, Lg, PLs, tid);
+  const T* PH = &PLs.p[0][0][0];
+  const T* PLo = &PLs.p[PlanesLds<T, D, LPG>::NPART - 1][0][0];
+  constexpr int LDP = PlanesLds<T, D, LPG>::LDP;
+  __syncthreads();  // hyperplanes staged before the first feature computation
   for (int f = tid; f < RP; f += 256) sm.zr[f] = f0 + f < r ? z[sidx * r + f0 + f] : 0.0f;
 
   typename M::frag qx[D / M::KSTEP], ox[D / M::KSTEP], kx[D / M::KSTEP];
@@ -717,7 +723,7 @@ __global__ void __launch_bounds__(256)
     if (causal) {
       if (qwave) {
         Feat Fk;
-        Fk.compute(kx, pl, Lg, scale, tau, lane);
+        Fk.compute(kx, PH, PLo, LDP, Lg, scale, tau, lane);
 #pragma unroll
         for (int jp = 0; jp < LPG / 2; ++jp) {
           float x0[8], x1[8];
@@ -740,7 +746,7 @@ __global__ void __launch_bounds__(256)
     typename M::frag dn[D / M::KSTEP];
     const float e_q = qvalid ? eq : 0.0f, dd_q = qvalid ? ddq : 0.0f;
     if (qwave) {
-      Fq.compute(qx, pl, Lg, scale, tau, lane);
+      Fq.compute(qx, PH, PLo, LDP, Lg, scale, tau, lane);
 #pragma unroll
       for (int ks = 0; ks < D / M::KSTEP; ++ks) {
         float x[M::KPL];
@@ -836,10 +842,14 @@ __global__ void __launch_bounds__(256)
   constexpr int VCH = D / 8, NDW = QT < 2 ? 1 : QT;  // dO staging waves
   constexpr int OIT = (STEP * VCH + 64 * NDW - 1) / (64 * NDW);
   __shared__ Sm sm;
+  __shared__ T KFs[STEP][LDR];  // phi(K) of the step's keys, [key][feature]
   __shared__ T RTs[D * rt_lds_width<LPG>()];
+  __shared__ PlanesLds<T, D, LPG> PLs;
   const int bh = blockIdx.y, c = blockIdx.x, head = bh % H;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, col = lane & 31;
-  const int kt = w % QT, role = w / QT;  // role 0: dK, 1: dV, 2+: staging only
+  // role 0: dK of key tile kt (and phi(K) of it); role 1: dV of key tile kt, phi(Q)
+  // of query tile kt and the dnum staging; 2+: staging only.
+  const int kt = w % QT, role = w / QT;
   const int r = 16 * L, f0 = 128 * grp, Lg = min(8, L - 8 * grp);
   const float* pl = planes + ((size_t)head * L + 8 * grp) * 4 * D;
   const int t_beg = c * span, t_end = min(N, t_beg + span);
@@ -849,7 +859,6 @@ __global__ void __launch_bounds__(256)
   const T* Kh = K + (size_t)bh * N * D;
   const T* Vh = V + (size_t)bh * N * D;
   const T* dOh = dO + (size_t)bh * N * D;
-  const bool kwave = role < 2;
   // dO staging: waves QT .. QT + NDW - 1 (waves 1 .. 2 when QT == 1).
   const int ow = QT < 2 ? w - 1 : w - QT;
   const bool owave = ow >= 0 && ow < NDW;
@@ -857,9 +866,17 @@ __global__ void __launch_bounds__(256)
   floatx16 st[SPW];
   load_stats<T, D, LPG, SPW>(G + sidx * D * r, r, f0, w, lane, st, &sm.SF[0][0], LDD);
   stage_rt<T, D, LPG, 256>(RT + (size_t)head * D * pw + 32 * grp, pw, RTs, tid);
+  stage_planes<T, D, LPG, 256>(pl, Lg, PLs, tid);
+  const T* PH = &PLs.p[0][0][0];
+  const T* PLo = &PLs.p[PlanesLds<T, D, LPG>::NPART - 1][0][0];
+  constexpr int LDP = PlanesLds<T, D, LPG>::LDP;
+  __syncthreads();  // hyperplanes staged before the first feature computation
   for (int f = tid; f < RP; f += 256) sm.zr[f] = f0 + f < r ? gzs[sidx * r + f0 + f] : 0.0f;
 
-  typename M::frag qx[D / M::KSTEP], kx[D / M::KSTEP], vx[D / M::KSTEP];
+  // xr: the row this wave featurizes (K for role 0, Q for role 1); vx: V (role 0).
+  // One array for both roles keeps the two load paths from being merged into
+  // stores through a selected pointer (which would put the arrays in scratch).
+  typename M::frag xr[D / M::KSTEP], vx[D / M::KSTEP];
   Vec8<T> ob[OIT];
   float oe[OIT];
   float ddv = 0.0f;
@@ -868,12 +885,9 @@ __global__ void __launch_bounds__(256)
     // as zero, their dnum rows and dd_lr are zeroed when staged, and no key
     // result of theirs is written. Nothing is loaded before the span.
     if (s0 < t_beg) return;
-    const int qtok = s0 + 32 * w + col;  // query tile w (waves < QT) for phi(Q)
-    if (w < QT) prefetch_row_frags<T, D>(Qh + (size_t)min(qtok, N - 1) * D, qx, h);
-    const int ktok = s0 + 32 * kt + col;
-    const size_t krow = (size_t)min(ktok, N - 1) * D;
-    if (kwave) prefetch_row_frags<T, D>(Kh + krow, kx, h);
-    if (role == 0) prefetch_row_frags<T, D>(Vh + krow, vx, h);
+    const size_t trow = (size_t)min(s0 + 32 * kt + col, N - 1) * D;
+    if (role < 2) prefetch_row_frags<T, D>((role == 0 ? Kh : Qh) + trow, xr, h);
+    if (role == 0) prefetch_row_frags<T, D>(Vh + trow, vx, h);
     if (owave) {
 #pragma unroll
       for (int i = 0; i < OIT; ++i) {
@@ -890,20 +904,21 @@ __global__ void __launch_bounds__(256)
 
   for (int si = nstep - 1; si >= 0; --si) {
     const int s0 = t_beg + si * STEP;
-    if (w < QT) {
-      const bool valid = s0 + 32 * w + col < t_end;
+    const int ktok = s0 + 32 * kt + col;
+    const bool kvalid = ktok < t_end;
+    if (role == 1) {
       Feat Fq;
-      Fq.compute(qx, pl, Lg, scale, tau, lane);
+      Fq.compute(xr, PH, PLo, LDP, Lg, scale, tau, lane);
 #pragma unroll
       for (int jp = 0; jp < LPG / 2; ++jp) {
         float x0[8], x1[8];
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
-          x0[b] = valid ? Fq.phi[jp][b] : 0.0f;
-          x1[b] = valid ? Fq.phi[jp][8 + b] : 0.0f;
+          x0[b] = kvalid ? Fq.phi[jp][b] : 0.0f;
+          x1[b] = kvalid ? Fq.phi[jp][8 + b] : 0.0f;
         }
-        store8(&sm.FS[32 * w + col][Feat::feat(jp, 0, h)], x0);
-        store8(&sm.FS[32 * w + col][Feat::feat(jp, 8, h)], x1);
+        store8(&sm.FS[32 * kt + col][Feat::feat(jp, 0, h)], x0);
+        store8(&sm.FS[32 * kt + col][Feat::feat(jp, 8, h)], x1);
       }
     }
     if (owave) {
@@ -917,10 +932,21 @@ __global__ void __launch_bounds__(256)
       }
       if (ow == 0 && lane < STEP) sm.dd[lane] = s0 + lane < t_end ? ddv : 0.0f;
     }
-    const int ktok = s0 + 32 * kt + col;
-    const bool kvalid = kwave && ktok < t_end;
     Feat Fk;
-    if (kwave) Fk.compute(kx, pl, Lg, scale, tau, lane);
+    if (role == 0) {
+      Fk.compute(xr, PH, PLo, LDP, Lg, scale, tau, lane);
+#pragma unroll
+      for (int jp = 0; jp < LPG / 2; ++jp) {
+        float x0[8], x1[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          x0[b] = kvalid ? Fk.phi[jp][b] : 0.0f;
+          x1[b] = kvalid ? Fk.phi[jp][8 + b] : 0.0f;
+        }
+        store8(&KFs[32 * kt + col][Feat::feat(jp, 0, h)], x0);
+        store8(&KFs[32 * kt + col][Feat::feat(jp, 8, h)], x1);
+      }
+    }
     __syncthreads();
 
     if (role == 0) {
@@ -977,7 +1003,8 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
         for (int ks = 0; ks < RP / M::KSTEP; ++ks) {
           const int fk = Feat::frag_feat(ks, 0, h);
-          dvt[dt] = M::mma(tr_rows(&sm.SF[0][0], LDD, fk, fk + 4, 32 * dt, lane), Fk.frag(ks), dvt[dt]);
+          dvt[dt] = M::mma(tr_rows(&sm.SF[0][0], LDD, fk, fk + 4, 32 * dt, lane),
+                           M::load(&KFs[32 * kt + col][fk]), dvt[dt]);
         }
       }
       if (causal) {
@@ -985,7 +1012,8 @@ __global__ void __launch_bounds__(256)
           floatx16 wq = zero16();
 #pragma unroll
           for (int ks = 0; ks < RP / M::KSTEP; ++ks)
-            wq = M::mma(M::load(&sm.FS[32 * qt + col][Feat::frag_feat(ks, 0, h)]), Fk.frag(ks), wq);
+            wq = M::mma(M::load(&sm.FS[32 * qt + col][Feat::frag_feat(ks, 0, h)]),
+                        M::load(&KFs[32 * kt + col][Feat::frag_feat(ks, 0, h)]), wq);
 #pragma unroll
           for (int v = 0; v < 16; ++v)
             if (qt == kt && acc_row(v, h) < col) wq[v] = 0.0f;
@@ -1078,10 +1106,12 @@ size_t bwd_lds_need(const Problem& pb) {
       constexpr int D = ELSAA_C(dc);
       auto need = [&](auto lc) {
         constexpr int LPG = ELSAA_C(lc);
-        constexpr size_t RTB = sizeof(T) * D * rt_lds_width<LPG>();
-        constexpr int SQ = walk_step<T, D, LPG, 128, RTB>(), SK = walk_step<T, D, LPG, 64, RTB>();
+        constexpr size_t RTB = sizeof(T) * D * rt_lds_width<LPG>() + sizeof(PlanesLds<T, D, LPG>);
+        constexpr int SQ = walk_step<T, D, LPG, 128, RTB>();
+        constexpr int SK = walk_step<T, D, LPG, 64, RTB + sizeof(T) * 64 * tile_ld<T>(16 * LPG)>();
         const size_t a = RTB + (SQ > 0 ? sizeof(WalkSmem<T, D, LPG, SQ>) : sizeof(WalkSmem<T, D, LPG, 32>));
-        const size_t b = RTB + (SK > 0 ? sizeof(WalkSmem<T, D, LPG, SK>) : sizeof(WalkSmem<T, D, LPG, 32>));
+        const size_t b = RTB + (SK > 0 ? sizeof(WalkSmem<T, D, LPG, SK>) : sizeof(WalkSmem<T, D, LPG, 32>)) +
+                         sizeof(T) * (SK > 0 ? SK : 32) * tile_ld<T>(16 * LPG);
         lr = a > b ? a : b;
       };
       switch (padded_tables(pb.L)) {
@@ -1178,8 +1208,9 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
       }
       auto run_lr = [&](auto lc) {
         constexpr int LPG = ELSAA_C(lc);
-        constexpr size_t RTB = sizeof(T) * D * rt_lds_width<LPG>();
-        constexpr int SQ = walk_step<T, D, LPG, 128, RTB>(), SK = walk_step<T, D, LPG, 64, RTB>();
+        constexpr size_t RTB = sizeof(T) * D * rt_lds_width<LPG>() + sizeof(PlanesLds<T, D, LPG>);
+        constexpr int SQ = walk_step<T, D, LPG, 128, RTB>();
+        constexpr int SK = walk_step<T, D, LPG, 64, RTB + sizeof(T) * 64 * tile_ld<T>(16 * LPG)>();
         if constexpr (SQ > 0 && SK > 0) {
           const int span_q = pb.causal ? pb.chunk : SQ;
           const int span_k = pb.causal ? pb.chunk : SK;

@@ -514,6 +514,29 @@ struct Features {
         }
       }
     }
+    activate(u, L, scale, tau, lane);
+  }
+  // Same, with the hyperplanes staged in LDS by stage_planes (PL unused for fp32).
+  __device__ __forceinline__ void compute(const typename MF<T>::frag (&xf)[D / MF<T>::KSTEP],
+                                          const T* PH, const T* PL, int ldp, int L, float scale,
+                                          float tau, int lane) {
+    typedef MF<T> M;
+    floatx16 u[NPT];
+#pragma unroll
+    for (int mt = 0; mt < NPT; ++mt) u[mt] = zero16();
+#pragma unroll
+    for (int ks = 0; ks < D / M::KSTEP; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < NPT; ++mt) {
+        u[mt] = M::mma(row_frag<T>(PH, ldp, 32 * mt, 0, ks, lane), xf[ks], u[mt]);
+        if constexpr (M::KPL > 1) u[mt] = M::mma(row_frag<T>(PL, ldp, 32 * mt, 0, ks, lane), xf[ks], u[mt]);
+      }
+    activate(u, L, scale, tau, lane);
+  }
+  // phi from the projection tiles u (rows = projections, columns = tokens).
+  __device__ __forceinline__ void activate(const floatx16 (&u)[NPT], int L, float scale, float tau,
+                                           int lane) {
+    const int h = lane >> 5;
     const float c2 = 2.0f * scale / tau;
 #pragma unroll
     for (int mt = 0; mt < NPT; ++mt) {
@@ -663,6 +686,28 @@ __device__ __forceinline__ void stage_rt(const float* RT, int pw, T* RTs, int ti
   for (int i = tid; i < D * W; i += NT) {
     const int d = i / W, p = i % W;
     RTs[i] = from_f<T>(p < 4 * LP ? RT[(size_t)d * pw + p] : 0.0f);
+  }
+}
+
+// The hyperplanes of LP tables as MFMA A operands in LDS: [projection][channel]
+// (row stride tile_ld), bf16 hi and lo parts (hi + lo carries about 16 bits of the
+// fp32 value), or fp32 once. Projections past 4 L are zero.
+template <typename T, int D, int LP>
+struct PlanesLds {
+  static constexpr int NP = 32 * ((4 * LP + 31) / 32), LDP = tile_ld<T>(D);
+  static constexpr int NPART = sizeof(T) == 2 ? 2 : 1;
+  T p[NPART][NP][LDP];
+};
+template <typename T, int D, int LP, int NT>
+__device__ __forceinline__ void stage_planes(const float* planes, int L, PlanesLds<T, D, LP>& P,
+                                             int tid) {
+  typedef PlanesLds<T, D, LP> PL;
+  for (int i = tid; i < PL::NP * D; i += NT) {
+    const int p = i / D, d = i % D;
+    const float x = p < 4 * L ? planes[(size_t)p * D + d] : 0.0f;
+    const T hi = from_f<T>(x);
+    P.p[0][p][d] = hi;
+    if constexpr (PL::NPART > 1) P.p[1][p][d] = from_f<T>(x - to_f(hi));
   }
 }
 

@@ -189,6 +189,7 @@ __global__ void __launch_bounds__(256)
   constexpr int NFT = RP / 32, NST = NDA * NFT, SPW = (NST + 3) / 4;
   constexpr int VCH = D / 8, VIT = (STEP * VCH + 255) / 256;
   __shared__ Sm sm;
+  __shared__ PlanesLds<T, D, LP> PLs;
 
   const int bh = blockIdx.y, c = blockIdx.x, head = bh % H;
   const int r = 16 * L;
@@ -209,6 +210,11 @@ __global__ void __launch_bounds__(256)
   const float* zc = z + sidx * r;
   floatx16 st[SPW];
   load_stats<T, D, LP, SPW>(Ac, r, 0, w, lane, st, &sm.SF[0][0], LDD);
+  stage_planes<T, D, LP, 256>(pl, L, PLs, tid);
+  const T* PH = &PLs.p[0][0][0];
+  const T* PLo = &PLs.p[PlanesLds<T, D, LP>::NPART - 1][0][0];
+  constexpr int LDP = PlanesLds<T, D, LP>::LDP;
+  __syncthreads();  // hyperplanes staged before the first feature computation
   for (int f = tid; f < RP; f += 256) sm.zr[f] = f < r ? zc[f] : 0.0f;
 
   // Global rows of one step, loaded one step ahead: this wave's query tile, the
@@ -238,7 +244,7 @@ __global__ void __launch_bounds__(256)
     if (causal) {
       if (w < QT) {
         Feat Fk;
-        Fk.compute(kx, pl, L, scale, tau, lane);
+        Fk.compute(kx, PH, PLo, LDP, L, scale, tau, lane);
         const bool kv = s0 + 32 * w + col < t_end;
 #pragma unroll
         for (int jp = 0; jp < LP / 2; ++jp) {
@@ -261,7 +267,7 @@ __global__ void __launch_bounds__(256)
     const int qtok = s0 + 32 * qt + col;
     const bool qvalid = qtok < t_end;
     Feat Fq;
-    Fq.compute(qx, pl, L, scale, tau, lane);
+    Fq.compute(qx, PH, PLo, LDP, L, scale, tau, lane);
     __syncthreads();
 
     if (owner) {
@@ -365,8 +371,9 @@ size_t fwd_lds_need(const Problem& pb) {
       constexpr int D = ELSAA_C(dc);
       with_LP(pb.L, [&](auto lc) {
         constexpr int LP = ELSAA_C(lc);
-        constexpr int STEP = walk_step<T, D, LP, 128>();
-        need = STEP > 0 ? sizeof(WalkSmem<T, D, LP, STEP>) : sizeof(WalkSmem<T, D, LP, 32>);
+        constexpr int STEP = walk_step<T, D, LP, 128, sizeof(PlanesLds<T, D, LP>)>();
+        need = sizeof(PlanesLds<T, D, LP>) +
+               (STEP > 0 ? sizeof(WalkSmem<T, D, LP, STEP>) : sizeof(WalkSmem<T, D, LP, 32>));
       });
     });
   });
@@ -407,7 +414,7 @@ void launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
       launch_merge(pb, Opart, Lpart, O_s, lse, st);
       with_LP(pb.L, [&](auto lc) {
         constexpr int LP = ELSAA_C(lc);
-        constexpr int STEP = walk_step<T, D, LP, 128>();
+        constexpr int STEP = walk_step<T, D, LP, 128, sizeof(PlanesLds<T, D, LP>)>();
         if constexpr (STEP > 0) {
           const int span = pb.causal ? pb.chunk : STEP;
           const int nspan = (pb.N + span - 1) / span;
