@@ -121,6 +121,8 @@ elsaa_status elsaa_workspace_size(const elsaa_params* p, int32_t call, size_t* b
  *               a = g n, entries [l N/2 + g n/2, l N/2 + (g+1) n/2) hold the sorted
  *               future half [a + n/2, a + n) (q_perm) and past half [a, a + n/2)
  *               (k_perm).
+ *   ws        : device workspace of elsaa_workspace_size(p, ELSAA_CALL_SELECT) bytes
+ *               (the hyperplanes widened to fp64).
  */
 elsaa_status elsaa_select(const elsaa_params* p, const void* Q, const void* K,
                           const float* planes_s, uint16_t* q_code, uint16_t* k_code,

@@ -122,6 +122,7 @@ elsaa_status need(const void* ptr, const char* name) {
 
 size_t ws_bytes_for(const Problem& pb, int call) {
   switch (call) {
+    case ELSAA_CALL_SELECT: return elsaa::select_ws_bytes(pb);
     case ELSAA_CALL_SUMMARY: return elsaa::summary_ws_bytes(pb);
     case ELSAA_CALL_FWD: return elsaa::fwd_ws_bytes(pb);
     case ELSAA_CALL_BWD: return elsaa::bwd_ws_bytes(pb);
@@ -177,7 +178,8 @@ elsaa_status elsaa_select(const elsaa_params* p, const void* Q, const void* K,
     elsaa_status s_ = check_ws(pb, ELSAA_CALL_SELECT, ws, ws_bytes);
     if (s_ != ELSAA_OK) return s_;
   }
-  elsaa::launch_select(pb, Q, K, planes_s, q_code, k_code, q_perm, k_perm, (hipStream_t)stream);
+  elsaa::launch_select(pb, Q, K, planes_s, q_code, k_code, q_perm, k_perm, ws,
+                       (hipStream_t)stream);
   return launched();
 }
 

@@ -110,8 +110,10 @@ void prof_end(hipStream_t st);
     ::elsaa::prof_end(st);                                         \
   } while (0)
 
+size_t select_ws_bytes(const Problem& pb);
 void launch_select(const Problem& pb, const void* Q, const void* K, const float* planes_s,
-                   uint16_t* qc, uint16_t* kc, int32_t* qperm, int32_t* kperm, hipStream_t st);
+                   uint16_t* qc, uint16_t* kc, int32_t* qperm, int32_t* kperm, void* ws,
+                   hipStream_t st);
 
 // RACE tile sums and their prefix/suffix/total combination (lowrank.hip).
 int lr_tile_tokens(const Problem& pb);

@@ -6,43 +6,87 @@
 
 namespace elsaa {
 
+// The sortLSH hyperplanes widened to fp64 once per call, [H][bits][D].
+__global__ void __launch_bounds__(256) planes_f64_kernel(const float* __restrict__ planes, int n,
+                                                         double* __restrict__ out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) out[i] = (double)planes[i];
+}
+
 // One thread per (token, tensor): bit b of the code is the sign of the fp64
 // fused-multiply-add chain over the row against hyperplane b, in index order
 // from +0.0. Correctly rounded FMA in a fixed order makes every bit
-// reproducible by any other correctly rounded implementation.
-template <typename T>
-__global__ void __launch_bounds__(256) hash_kernel(const T* __restrict__ Q, const T* __restrict__ K,
-                                                   const float* __restrict__ planes,
+// reproducible by any other correctly rounded implementation. The workgroup's
+// 128 rows are first copied into LDS with 16-byte row-contiguous loads (row
+// stride padded by 16 bytes so that each thread's 16-byte reads of its own row
+// are free of bank conflicts); the fp64 hyperplanes are the same for every lane
+// and are read with scalar loads (operands in scalar registers).
+template <typename T, int D, int BITS>
+__global__ void __launch_bounds__(128) hash_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                   const double* __restrict__ planes,
                                                    uint16_t* __restrict__ qc,
-                                                   uint16_t* __restrict__ kc, int H, int N, int d,
-                                                   int bits) {
-  __shared__ double pl[kMaxHashBits * kMaxDh];
-  const int bh = blockIdx.y, h = bh % H;
-  for (int i = threadIdx.x; i < bits * d; i += blockDim.x)
-    pl[i] = (double)planes[(size_t)h * bits * d + i];
-  __syncthreads();
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= N) return;
-  const T* x = (blockIdx.z ? K : Q) + ((size_t)bh * N + t) * d;
-  double acc[kMaxHashBits];
+                                                   uint16_t* __restrict__ kc, int H, int N) {
+  constexpr int ROWS = 128, CH = D * (int)sizeof(T) / 16, EPP = 16 / (int)sizeof(T);
+  constexpr int RW = D * (int)sizeof(T) / 4 + 4;  // row stride in dwords
+  constexpr int IT = ROWS * CH / 128;
+  __shared__ uint4 xs[ROWS * RW / 4];
+  const int bh = blockIdx.y, h = bh % H, tid = threadIdx.x;
+  const int tok0 = blockIdx.x * ROWS;
+  const T* X = (blockIdx.z ? K : Q) + (size_t)bh * N * D;
+  const double* pl = planes + (size_t)h * BITS * D;
+  {
+    uint4 buf[IT];
 #pragma unroll
-  for (int b = 0; b < kMaxHashBits; ++b) acc[b] = 0.0;
-  for (int j0 = 0; j0 < d; j0 += 8) {
-    float xv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) xv[e] = to_f(x[j0 + e]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const double xd = (double)xv[e];
-#pragma unroll
-      for (int b = 0; b < kMaxHashBits; ++b)
-        if (b < bits) acc[b] = __builtin_fma(xd, pl[b * d + j0 + e], acc[b]);
+    for (int i = 0; i < IT; ++i) {
+      const int p = tid + ROWS * i, r = p / CH, c = p % CH;
+      const int tok = min(tok0 + r, N - 1);
+      buf[i] = reinterpret_cast<const uint4*>(X + (size_t)tok * D)[c];
     }
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int p = tid + ROWS * i, r = p / CH, c = p % CH;
+      xs[r * (RW / 4) + c] = buf[i];
+    }
+  }
+  __syncthreads();
+  const int t = tok0 + tid;
+  if (t >= N) return;
+  double acc[BITS];
+#pragma unroll
+  for (int b = 0; b < BITS; ++b) acc[b] = 0.0;
+  for (int c = 0; c < CH; ++c) {
+    const uint4 v = xs[tid * (RW / 4) + c];
+    float xv[EPP];
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xv[2 * e] = __uint_as_float(w4[e] << 16);
+        xv[2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+      }
+    } else {
+      xv[0] = __uint_as_float(v.x);
+      xv[1] = __uint_as_float(v.y);
+      xv[2] = __uint_as_float(v.z);
+      xv[3] = __uint_as_float(v.w);
+    }
+    double xd[EPP];
+#pragma unroll
+    for (int e = 0; e < EPP; ++e) xd[e] = (double)xv[e];
+    double pv[BITS][EPP];
+#pragma unroll
+    for (int b = 0; b < BITS; ++b)
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) pv[b][e] = pl[b * D + c * EPP + e];
+#pragma unroll
+    for (int e = 0; e < EPP; ++e)
+#pragma unroll
+      for (int b = 0; b < BITS; ++b) acc[b] = __builtin_fma(xd[e], pv[b][e], acc[b]);
   }
   unsigned code = 0;
 #pragma unroll
-  for (int b = 0; b < kMaxHashBits; ++b)
-    if (b < bits && acc[b] > 0.0) code |= 1u << b;
+  for (int b = 0; b < BITS; ++b)
+    if (acc[b] > 0.0) code |= 1u << b;
   (blockIdx.z ? kc : qc)[(size_t)bh * N + t] = (uint16_t)code;
 }
 
@@ -137,17 +181,44 @@ __global__ void __launch_bounds__(256) sort_kernel(const uint16_t* __restrict__ 
   }
 }
 
+size_t select_ws_bytes(const Problem& pb) {
+  return (sizeof(double) * pb.H * pb.hash_bits * pb.d + 255) & ~(size_t)255;
+}
+
 void launch_select(const Problem& pb, const void* Q, const void* K, const float* planes_s,
-                   uint16_t* qc, uint16_t* kc, int32_t* qperm, int32_t* kperm,
+                   uint16_t* qc, uint16_t* kc, int32_t* qperm, int32_t* kperm, void* ws,
                    hipStream_t st) {
   const int BH = pb.B * pb.H;
-  dim3 hg((pb.N + 255) / 256, BH, 2);
-  if (pb.bf16)
-    ELSAA_LAUNCH("hash", hash_kernel<__bf16>, hg, dim3(256), 0, st, (const __bf16*)Q,
-                       (const __bf16*)K, planes_s, qc, kc, pb.H, pb.N, pb.d, pb.hash_bits);
-  else
-    ELSAA_LAUNCH("hash", hash_kernel<float>, hg, dim3(256), 0, st, (const float*)Q,
-                       (const float*)K, planes_s, qc, kc, pb.H, pb.N, pb.d, pb.hash_bits);
+  double* pld = (double*)ws;
+  const int np = pb.H * pb.hash_bits * pb.d;
+  ELSAA_LAUNCH("planes_f64", planes_f64_kernel, dim3((np + 255) / 256), dim3(256), 0, st, planes_s,
+               np, pld);
+  const dim3 hg((pb.N + 127) / 128, BH, 2);
+  with_T(pb.bf16, [&](auto tp) {
+    using T = ELSAA_T(tp);
+    with_D(pb.d, [&](auto dc) {
+      constexpr int D = ELSAA_C(dc);
+      auto run = [&](auto bc) {
+        constexpr int BITS = ELSAA_C(bc);
+        ELSAA_LAUNCH("hash", (hash_kernel<T, D, BITS>), hg, dim3(128), 0, st, (const T*)Q,
+                     (const T*)K, (const double*)pld, qc, kc, pb.H, pb.N);
+      };
+      switch (pb.hash_bits) {
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 3: run(std::integral_constant<int, 3>{}); break;
+        case 4: run(std::integral_constant<int, 4>{}); break;
+        case 5: run(std::integral_constant<int, 5>{}); break;
+        case 6: run(std::integral_constant<int, 6>{}); break;
+        case 7: run(std::integral_constant<int, 7>{}); break;
+        case 8: run(std::integral_constant<int, 8>{}); break;
+        case 9: run(std::integral_constant<int, 9>{}); break;
+        case 10: run(std::integral_constant<int, 10>{}); break;
+        case 11: run(std::integral_constant<int, 11>{}); break;
+        default: run(std::integral_constant<int, kMaxHashBits>{}); break;
+      }
+    });
+  });
   const int nseg = pb.causal ? (1 << pb.levels) - 1 : 1;
   const size_t lds = sizeof(int) * ((size_t)kSortWaves * (1 << pb.hash_bits) + 256);
   if (nseg > 0)

@@ -64,7 +64,9 @@ def test_valid_params_and_workspace_sizes():
     for call in range(4):
         s, msg, n = status_of(base(), call)
         assert s == _lib.OK, msg
-    assert status_of(base(), _lib.CALL_SELECT)[2] == 0
+    # select: the hyperplanes widened to fp64, [H, hash_bits, d_h], 256-byte rounded
+    p = base().params()
+    assert status_of(base(), _lib.CALL_SELECT)[2] == (8 * p.H * p.hash_bits * p.d_h + 255) // 256 * 256
     assert status_of(base(), _lib.CALL_FWD)[2] > 0
     # An empty batch is valid and needs no workspace.
     assert status_of(base(B=0), _lib.CALL_FWD)[:1] == (_lib.OK,)
