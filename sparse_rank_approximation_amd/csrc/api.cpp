@@ -38,9 +38,7 @@ int ilog2(long x) {
 
 // LDS each kernel family would need for these parameters (bytes).
 size_t lds_need(const Problem& pb) {
-  const size_t e = pb.elem, d = pb.d;
-  const size_t rp = 16 * (size_t)elsaa::padded_tables(pb.L);
-  const size_t sums = e * (rp * 72 + d * 72) + 4 * 64;
+  const size_t sums = elsaa::summary_lds_need(pb);
   size_t m = elsaa::fwd_lds_need(pb);
   if (sums > m) m = sums;
   const size_t bwd = elsaa::bwd_lds_need(pb);

@@ -714,14 +714,14 @@ __device__ __forceinline__ void stage_planes(const float* planes, int L, PlanesL
 // Loads the running RACE statistics of a walk (fp32 [channel][feature] rows of
 // length r, features f0 .. f0 + RP) into fp32 D tiles st (rows = channels, lanes =
 // features; tile w + 4 i of this wave) and their operand copy SF[feature][channel].
-template <typename T, int D, int LP, int SPW>
+template <typename T, int D, int LP, int SPW, int NW = 4>
 __device__ __forceinline__ void load_stats(const float* Ac, int r, int f0, int w, int lane,
                                            floatx16 (&st)[SPW], T* SF, int ldd) {
   constexpr int NFT = LP / 2, NST = (D / 32) * NFT;
   const int h = lane >> 5, col = lane & 31;
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
-    const int tix = w + 4 * i;
+    const int tix = w + NW * i;
     st[i] = zero16();
     if (tix < NST) {
       const int mt = tix / NFT, f = f0 + 32 * (tix % NFT) + col;
@@ -732,7 +732,7 @@ __device__ __forceinline__ void load_stats(const float* Ac, int r, int f0, int w
   }
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
-    const int tix = w + 4 * i;
+    const int tix = w + NW * i;
     if (tix < NST) {
       const int mt = tix / NFT, fl = 32 * (tix % NFT) + col;
 #pragma unroll
@@ -752,7 +752,7 @@ __device__ __forceinline__ void load_stats(const float* Ac, int r, int f0, int w
 // feature sums are products with a constant-row A operand, formed by the wave that
 // owns channel tile 0 of each feature tile; bf16 weights are split into hi + lo
 // parts (two products).
-template <typename T, int D, int LP, int SPW, int STEP>
+template <typename T, int D, int LP, int SPW, int STEP, bool WRITE_SF = true, int NW = 4>
 __device__ __forceinline__ void advance_stats(const T* X, int ldd, const T* F, int ldr,
                                               const float* wt, int w, int lane,
                                               floatx16 (&st)[SPW], T* SF, float* zr) {
@@ -761,7 +761,7 @@ __device__ __forceinline__ void advance_stats(const T* X, int ldd, const T* F, i
   const int h = lane >> 5, col = lane & 31;
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
-    const int tix = w + 4 * i;
+    const int tix = w + NW * i;
     if (tix < NST) {
       const int mt = tix / NFT, nt = tix % NFT;
       floatx16 zs = zero16();
@@ -784,12 +784,14 @@ __device__ __forceinline__ void advance_stats(const T* X, int ldd, const T* F, i
           }
         }
       }
+      if constexpr (WRITE_SF) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float x[4];
+        for (int g = 0; g < 4; ++g) {
+          float x[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = st[i][4 * g + e];
-        store4(SF + (size_t)(32 * nt + col) * ldd + 32 * mt + 8 * g + 4 * h, x);
+          for (int e = 0; e < 4; ++e) x[e] = st[i][4 * g + e];
+          store4(SF + (size_t)(32 * nt + col) * ldd + 32 * mt + 8 * g + 4 * h, x);
+        }
       }
       if (mt == 0 && h == 0) zr[32 * nt + col] += zs[0];
     }

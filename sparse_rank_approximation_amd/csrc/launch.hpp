@@ -124,6 +124,7 @@ void run_lr_scan(const Problem& pb, const float* S, const float* Z, int mode, fl
                  hipStream_t st);
 
 size_t summary_ws_bytes(const Problem& pb);
+size_t summary_lds_need(const Problem& pb);
 void launch_summary(const Problem& pb, const void* K, const void* V, const float* planes_lr,
                     float* A, float* z, void* ws, hipStream_t st);
 

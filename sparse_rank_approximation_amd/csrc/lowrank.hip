@@ -6,7 +6,7 @@
 // lr_sums_kernel: per (head, tile of TT tokens) the sums
 //     S^T[e][f] = sum_t phi_f(X_t) alpha_t Y_t[e],   z[f] = sum_t phi_f(X_t) beta_t
 // (forward: X = K, Y = V, alpha = beta = 1), as a bf16/fp32 MFMA contraction over
-// the tokens with fp32 accumulation, 64 tokens per step.
+// the tokens with fp32 accumulation.
 // lr_scan_kernel: combines the tile sums into the summaries: the total
 // (non-causal), the exclusive prefix (causal forward) or the exclusive suffix
 // (causal backward) over tiles.
@@ -15,94 +15,129 @@
 
 namespace elsaa {
 
+template <typename T, int D, int LP, int SUB>
+struct SumsSmem {
+  static constexpr int LDD = tile_ld<T>(D), LDR = tile_ld<T>(16 * LP);
+  T YS[SUB][LDD];        // alpha_t Y_t of the step, [token][channel]
+  T FS[SUB][LDR];        // phi(X_t) of the step, [token][feature]
+  alignas(16) float zr[16 * LP];
+  alignas(16) float bet[SUB];
+};
+
+// Largest step (128, 64 or 32 tokens) whose LDS (with the staged hyperplanes) fits.
 template <typename T, int D, int LP>
-__global__ void __launch_bounds__(256) lr_sums_kernel(const T* __restrict__ X, const T* __restrict__ Y,
+constexpr int sums_step() {
+  constexpr size_t P = sizeof(PlanesLds<T, D, LP>);
+  return sizeof(SumsSmem<T, D, LP, 128>) + P <= kLdsBytes  ? 128
+         : sizeof(SumsSmem<T, D, LP, 64>) + P <= kLdsBytes ? 64
+                                                            : 32;
+}
+
+// One workgroup per (head, tile of TT tokens), 8 waves, SUB tokens per step: wave
+// w < SUB / 32 featurizes token tile w of the step (hyperplanes in LDS), waves
+// 4..7 stage the step's alpha-scaled Y rows; then st += Y^T phi(X) and
+// z += phi(X)^T beta on MFMA (advance_stats, tiles spread over the 8 waves) with
+// the next step's rows already in flight. Eight waves keep each wave's registers
+// within half the file, so two waves share each SIMD.
+template <typename T, int D, int LP, int SUB>
+__global__ void __launch_bounds__(512) lr_sums_kernel(const T* __restrict__ X, const T* __restrict__ Y,
                                                       const float* __restrict__ alpha,
                                                       const float* __restrict__ beta,
                                                       const float* __restrict__ planes, int H, int N,
                                                       int L, int TT, float scale, float tau,
                                                       float* __restrict__ S, float* __restrict__ Z) {
   typedef MF<T> M;
-  constexpr int RP = 16 * LP, SUB = 64, PAD = 8;
-  constexpr int NT_N = RP / 32, NTILES = (D / 32) * NT_N, TPW = (NTILES + 3) / 4;
-  __shared__ T KfT[RP][SUB + PAD];
-  __shared__ T YT[D][SUB + PAD];
-  __shared__ float bet[SUB];
+  typedef Features<T, D, LP> Feat;
+  typedef SumsSmem<T, D, LP, SUB> Sm;
+  constexpr int NW = 8, RP = 16 * LP, NFT = RP / 32, NST = (D / 32) * NFT;
+  constexpr int SPW = (NST + NW - 1) / NW;
+  constexpr int QT = SUB / 32, LDD = Sm::LDD, LDR = Sm::LDR;
+  constexpr int VCH = D / 8, VIT = (SUB * VCH + 255) / 256;  // per staging thread (waves 4..7)
+  __shared__ Sm sm;
+  __shared__ PlanesLds<T, D, LP> PLs;
   const int bh = blockIdx.y, tile = blockIdx.x, ntile = gridDim.x;
   const int r = 16 * L;
   const int t0 = tile * TT, t1 = min(N, t0 + TT);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, col = lane & 31;
-  const float* pl = planes + (size_t)(bh % H) * L * 4 * D;
+  const T* Xh = X + (size_t)bh * N * D;
+  const T* Yh = Y + (size_t)bh * N * D;
+  stage_planes<T, D, LP, 512>(planes + (size_t)(bh % H) * L * 4 * D, L, PLs, tid);
+  const T* PH = &PLs.p[0][0][0];
+  const T* PLo = &PLs.p[PlanesLds<T, D, LP>::NPART - 1][0][0];
+  constexpr int LDP = PlanesLds<T, D, LP>::LDP;
+  for (int f = tid; f < RP; f += 512) sm.zr[f] = 0.0f;
+  const int ts = tid - 256;  // staging thread index (waves 4..7)
 
-  floatx16 acc[TPW];
+  floatx16 st[SPW];
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) acc[i] = zero16();
-  float zacc = 0.0f;
+  for (int i = 0; i < SPW; ++i) st[i] = zero16();
 
-  for (int s0 = t0; s0 < t1; s0 += SUB) {
-    if (w < 2) {
-      const int tok = s0 + 32 * w + col;
-      const bool valid = tok < t1;
-      Features<T, D, LP> F;
-      F.compute(X + ((size_t)bh * N + (valid ? tok : t0)) * D, valid, pl, L, scale, tau, lane);
+  // Rows of one step (tokens past the tile read a stand-in row and get zero
+  // weight: their phi rows are stored as zero).
+  typename M::frag xr[D / M::KSTEP];
+  Vec8<T> yb[VIT];
+  float ya[VIT], bt = 0.0f;
+  auto load_rows = [&](int s0) __attribute__((always_inline)) {
+    if (w < QT) prefetch_row_frags<T, D>(Xh + (size_t)min(s0 + 32 * w + col, N - 1) * D, xr, h);
+    if (ts >= 0) {
 #pragma unroll
-      for (int jp = 0; jp < LP / 2; ++jp)
-#pragma unroll
-        for (int b = 0; b < 16; ++b)
-          KfT[Features<T, D, LP>::feat(jp, b, h)][32 * w + col] = from_f<T>(valid ? F.phi[jp][b] : 0.0f);
-      if (h == 0) bet[32 * w + col] = valid ? (beta ? beta[(size_t)bh * N + tok] : 1.0f) : 0.0f;
-    } else {
-      for (int idx = tid - 128; idx < SUB * (D / 8); idx += 128) {
-        const int tk = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-        const int tok = s0 + tk;
-        float y[8];
-        if (tok < t1) {
-          const float a = alpha ? alpha[(size_t)bh * N + tok] : 1.0f;
-          const T* yr = Y + ((size_t)bh * N + tok) * D + c8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] = to_f(yr[e]) * a;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] = 0.0f;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) YT[c8 + e][tk] = from_f<T>(y[e]);
+      for (int i = 0; i < VIT; ++i) {
+        const int it = ts + 256 * i, tc = min(s0 + it / VCH, N - 1);
+        if (it < SUB * VCH) yb[i].load(Yh + (size_t)tc * D + (it % VCH) * 8);
+        ya[i] = alpha ? alpha[(size_t)bh * N + tc] : 1.0f;
       }
+      if (ts < SUB) bt = beta ? beta[(size_t)bh * N + min(s0 + ts, N - 1)] : 1.0f;
+    }
+  };
+  __syncthreads();  // hyperplanes staged
+  load_rows(t0);
+  for (int s0 = t0; s0 < t1; s0 += SUB) {
+    if (w < QT) {
+      const bool valid = s0 + 32 * w + col < t1;
+      Feat F;
+      F.compute(xr, PH, PLo, LDP, L, scale, tau, lane);
+#pragma unroll
+      for (int jp = 0; jp < LP / 2; ++jp) {
+        float x0[8], x1[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          x0[b] = valid ? F.phi[jp][b] : 0.0f;
+          x1[b] = valid ? F.phi[jp][8 + b] : 0.0f;
+        }
+        store8(&sm.FS[32 * w + col][Feat::feat(jp, 0, h)], x0);
+        store8(&sm.FS[32 * w + col][Feat::feat(jp, 8, h)], x1);
+      }
+    }
+    if (ts >= 0) {
+#pragma unroll
+      for (int i = 0; i < VIT; ++i) {
+        const int it = ts + 256 * i;
+        if (it < SUB * VCH) {
+          yb[i].scale(s0 + it / VCH < t1 ? ya[i] : 0.0f);
+          yb[i].store(&sm.YS[it / VCH][(it % VCH) * 8]);
+        }
+      }
+      if (ts < SUB) sm.bet[ts] = s0 + ts < t1 ? bt : 0.0f;
     }
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int tix = w + 4 * i;
-      if (tix < NTILES) {
-        const int mt = tix / NT_N, nt = tix % NT_N;
-#pragma unroll
-        for (int ks = 0; ks < SUB / M::KSTEP; ++ks) {
-          const int k0 = ks * M::KSTEP + M::KPL * h;
-          acc[i] = M::mma(M::load(&YT[32 * mt + col][k0]), M::load(&KfT[32 * nt + col][k0]), acc[i]);
-        }
-      }
-    }
-    if (tid < RP) {
-#pragma unroll 8
-      for (int t = 0; t < SUB; ++t) zacc += to_f(KfT[tid][t]) * bet[t];
-    }
+    load_rows(s0 + SUB);
+    advance_stats<T, D, LP, SPW, SUB, false, NW>(&sm.YS[0][0], LDD, &sm.FS[0][0], LDR, sm.bet, w,
+                                                 lane, st, nullptr, sm.zr);
     __syncthreads();
   }
 
   const size_t base = (size_t)bh * ntile + tile;
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int tix = w + 4 * i;
-    if (tix < NTILES) {
-      const int mt = tix / NT_N, nt = tix % NT_N;
-      const int f = 32 * nt + col;
-      if (f < r) {
+  for (int i = 0; i < SPW; ++i) {
+    const int tix = w + NW * i;
+    if (tix < NST) {
+      const int mt = tix / NFT, f = 32 * (tix % NFT) + col;
+      if (f < r)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) S[(base * D + 32 * mt + acc_row(v, h)) * r + f] = acc[i][v];
-      }
+        for (int v = 0; v < 16; ++v) S[(base * D + 32 * mt + acc_row(v, h)) * r + f] = st[i][v];
     }
   }
-  if (tid < r) Z[base * r + tid] = zacc;
+  for (int f = tid; f < r; f += 512) Z[base * r + f] = sm.zr[f];
 }
 
 // mode 0: total over tiles (one output); 1: exclusive prefix; 2: exclusive suffix.
@@ -153,9 +188,10 @@ void run_lr_sums(const Problem& pb, const void* X, const void* Y, const float* a
       constexpr int D = ELSAA_C(dc);
       with_LP(pb.L, [&](auto lc) {
         constexpr int LP = ELSAA_C(lc);
-        ELSAA_LAUNCH("lr_sums", (lr_sums_kernel<T, D, LP>), dim3(nt, BH), dim3(256), 0, st,
-                           (const T*)X, (const T*)Y, alpha, beta, planes, pb.H, pb.N, pb.L, TT,
-                           pb.scale, pb.tau, S, Z);
+        constexpr int SUB = sums_step<T, D, LP>();
+        ELSAA_LAUNCH("lr_sums", (lr_sums_kernel<T, D, LP, SUB>), dim3(nt, BH), dim3(512), 0, st,
+                     (const T*)X, (const T*)Y, alpha, beta, planes, pb.H, pb.N, pb.L, TT,
+                     pb.scale, pb.tau, S, Z);
       });
     });
   });
@@ -166,6 +202,21 @@ void run_lr_scan(const Problem& pb, const float* S, const float* Z, int mode, fl
   const int BH = pb.B * pb.H, nt = lr_tiles(pb), per = pb.d * pb.r;
   ELSAA_LAUNCH("lr_scan", lr_scan_kernel, dim3((per + pb.r + 255) / 256, BH), dim3(256), 0, st, S, Z, A,
                      z, nt, per, pb.r, mode);
+}
+
+size_t summary_lds_need(const Problem& pb) {
+  size_t need = 0;
+  with_T(pb.bf16, [&](auto tp) {
+    using T = ELSAA_T(tp);
+    with_D(pb.d, [&](auto dc) {
+      constexpr int D = ELSAA_C(dc);
+      with_LP(pb.L, [&](auto lc) {
+        constexpr int LP = ELSAA_C(lc);
+        need = sizeof(SumsSmem<T, D, LP, sums_step<T, D, LP>()>) + sizeof(PlanesLds<T, D, LP>);
+      });
+    });
+  });
+  return need;
 }
 
 size_t summary_ws_bytes(const Problem& pb) {
