@@ -139,6 +139,8 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="causal RACE summary spacing (numerics-neutral); 0 keeps the workload's")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -154,6 +156,8 @@ def main():
     from sparse_rank_approximation_amd import _lib
 
     w = W.CONFIGS[args.config]
+    if args.chunk:
+        w = w.with_(chunk=args.chunk)
     seed = W.config_seed(args.config)
     t0 = time.perf_counter()
     inp = W.gen_inputs(w, seed)

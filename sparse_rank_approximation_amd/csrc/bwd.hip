@@ -50,14 +50,15 @@ __device__ __forceinline__ int compact_past(int j, int N, int l) {
 // (lane = token): lr + the fp32 running sum of earlier feature groups (unless
 // first), stored as T (last group) or as the fp32 running sum. The sparse partial
 // rows are added afterwards (combine_kernel).
-template <typename T, int D>
-__device__ __forceinline__ void write_grad_row(const floatx16 (&lr)[D / 32], float* scratch, T* out,
-                                               size_t row, int h, bool first, bool last) {
+template <typename T, int D, int NDT = D / 32>
+__device__ __forceinline__ void write_grad_row(const floatx16 (&lr)[NDT], float* scratch, T* out,
+                                               size_t row, int h, bool first, bool last,
+                                               int dt0 = 0) {
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const size_t o = row + 32 * dt + 8 * g + 4 * h;
+      const size_t o = row + 32 * (dt0 + dt) + 8 * g + 4 * h;
       float v[4];
       if (!first) load4(scratch + o, v);
 #pragma unroll
@@ -228,7 +229,8 @@ __global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
   constexpr int NT = sbwd_threads<SB>(ROLE);
   __shared__ Sm sm;
   const int bh = blockIdx.y, item = blockIdx.x;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int w = wave_id();  // wave index, uniform (scalar) so that role branches stay uniform
   const size_t P = perm_stride(N, levels, causal);
   const size_t slots = partial_slots(N, levels, causal);
   const size_t rowbase = (size_t)bh * N;
@@ -452,7 +454,8 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
   constexpr int KT = Sm::KT, NW = KT / 32, NT = 64 * NW, LD = Sm::LD, LDK = Sm::LDK;
   constexpr int CH = D / 8, GIT = KT * CH / NT, KS = D / M::KSTEP;
   __shared__ Sm sm;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int w = wave_id();  // wave index, uniform (scalar) so that role branches stay uniform
   const int G = gridDim.x;
   const size_t P = perm_stride(N, levels, causal);
   const size_t slots = partial_slots(N, levels, causal);
@@ -650,11 +653,19 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
 
 // ---------------------------------------------------------------------------
 // Low-rank branch, query side: one head and span per workgroup, walked forwards in
-// steps of STEP tokens by 4 waves; wave w < STEP / 32 owns the step's query tile w.
-// LDS (WalkSmem): V (XS) and phi(K) (FS) of the step's keys, the running key
-// statistics S = sum_j phi(K_j) V_j^T (SF) and z (zr).
+// steps of STEP tokens by 8 waves. Query tile qt = w % 4 of the step is shared by
+// waves qt (half 0) and qt + 4 (half 1): each forms dphi(Q) for half of the feature
+// tiles and takes it back through its half of the tables; the hyperplane
+// gradients da go through LDS so that each wave then forms dQ for half of the
+// channels. LDS (WalkSmem): V (XS) and phi(K) (FS) of the step's keys, the
+// running key statistics S = sum_j phi(K_j) V_j^T (SF) and z (zr).
+template <int LPG>
+struct QdaLds {
+  float da[4][2][32][2 * LPG];  // [query tile][lane half][token][table pair * 4 + t]
+};
+
 template <typename T, int D, int LPG, int STEP>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
     lr_bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                     const T* __restrict__ dO, const float* __restrict__ planes,
                     const float* __restrict__ A, const float* __restrict__ z,
@@ -665,14 +676,20 @@ __global__ void __launch_bounds__(256)
   typedef MF<T> M;
   typedef Features<T, D, LPG> Feat;
   typedef WalkSmem<T, D, LPG, STEP> Sm;
-  constexpr int RP = 16 * LPG, NFT = RP / 32, LDD = Sm::LDD, LDR = Sm::LDR;
-  constexpr int QT = STEP / 32, NST = NFT * (D / 32), SPW = (NST + 3) / 4;
+  constexpr int NW = 8, RP = 16 * LPG, NFT = RP / 32, LDD = Sm::LDD, LDR = Sm::LDR;
+  constexpr int QT = STEP / 32, NST = NFT * (D / 32), SPW = (NST + NW - 1) / NW;
+  constexpr int NFH = NFT > 1 ? NFT / 2 : 1;            // feature tiles per half
+  constexpr int NDA = D / 32, NDH = NDA > 1 ? NDA / 2 : 1;  // channel tiles per half
   constexpr int VCH = D / 8, VIT = (STEP * VCH + 255) / 256;
   __shared__ Sm sm;
   __shared__ T RTs[D * rt_lds_width<LPG>()];
   __shared__ PlanesLds<T, D, LPG> PLs;
+  __shared__ QdaLds<LPG> DA;
   const int bh = blockIdx.y, c = blockIdx.x, head = bh % H;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int w = tid >> 6;
+  const int qt = w & 3, half = w >> 2;
+  const bool qwave = qt < QT;
   const int r = 16 * L, f0 = 128 * grp, Lg = min(8, L - 8 * grp);
   const float* pl = planes + ((size_t)head * L + 8 * grp) * 4 * D;
   const int t_beg = c * span, t_end = min(N, t_beg + span);
@@ -682,138 +699,157 @@ __global__ void __launch_bounds__(256)
   const T* Kh = K + (size_t)bh * N * D;
   const T* Vh = V + (size_t)bh * N * D;
   const T* dOh = dO + (size_t)bh * N * D;
-  const bool qwave = w < QT;
 
   floatx16 st[SPW];
-  load_stats<T, D, LPG, SPW>(A + sidx * D * r, r, f0, w, lane, st, &sm.SF[0][0], LDD);
-  stage_rt<T, D, LPG, 256>(RT + (size_t)head * D * pw + 32 * grp, pw, RTs, tid);
-  stage_planes<T, D, LPG, 256>(pl, Lg, PLs, tid);
+  load_stats<T, D, LPG, SPW, NW>(A + sidx * D * r, r, f0, w, lane, st, &sm.SF[0][0], LDD);
+  stage_rt<T, D, LPG, 512>(RT + (size_t)head * D * pw + 32 * grp, pw, RTs, tid);
+  stage_planes<T, D, LPG, 512>(pl, Lg, PLs, tid);
   const T* PH = &PLs.p[0][0][0];
   const T* PLo = &PLs.p[PlanesLds<T, D, LPG>::NPART - 1][0][0];
   constexpr int LDP = PlanesLds<T, D, LPG>::LDP;
-  __syncthreads();  // hyperplanes staged before the first feature computation
-  for (int f = tid; f < RP; f += 256) sm.zr[f] = f0 + f < r ? z[sidx * r + f0 + f] : 0.0f;
+  for (int f = tid; f < RP; f += 512) sm.zr[f] = f0 + f < r ? z[sidx * r + f0 + f] : 0.0f;
+  __syncthreads();  // hyperplanes and statistics staged
 
+  // Rows of one step: the wave's query tile (Q, dO, dd_lr, scale of dnum; both
+  // halves), its key tile (K; half 0) and a share of the V rows (half 1). Tokens
+  // past the span read a stand-in row; their dnum and dd_lr are zeroed where used
+  // and their phi(K) rows are stored as zero.
   typename M::frag qx[D / M::KSTEP], ox[D / M::KSTEP], kx[D / M::KSTEP];
   Vec8<T> vb[VIT];
   float eq = 0.0f, ddq = 0.0f;
+  const int ts = tid - 256;  // V staging thread (half 1)
   auto load_rows = [&](int s0) __attribute__((always_inline)) {
-    // Tokens past the span read a stand-in row; their dnum and dd_lr are zeroed
-    // where used and their phi(K) rows are stored as zero.
-    const int tok = s0 + 32 * w + col;
-    const size_t rrow = (size_t)min(tok, N - 1) * D;
+    const int tok = min(s0 + 32 * qt + col, N - 1);
+    const size_t rrow = (size_t)tok * D;
     prefetch_row_frags<T, D>(Qh + rrow, qx, h);
     prefetch_row_frags<T, D>(dOh + rrow, ox, h);
-    eq = re[(size_t)bh * N + min(tok, N - 1)];
-    ddq = rdd[(size_t)bh * N + min(tok, N - 1)];
+    eq = re[(size_t)bh * N + tok];
+    ddq = rdd[(size_t)bh * N + tok];
     if (causal) {
-      prefetch_row_frags<T, D>(Kh + rrow, kx, h);
+      if (half == 0) prefetch_row_frags<T, D>(Kh + rrow, kx, h);
+      if (ts >= 0) {
 #pragma unroll
-      for (int i = 0; i < VIT; ++i) {
-        const int it = tid + 256 * i, t = it / VCH, tk = s0 + t;
-        if (it < STEP * VCH) vb[i].load(Vh + (size_t)min(tk, N - 1) * D + (it % VCH) * 8);
+        for (int i = 0; i < VIT; ++i) {
+          const int it = ts + 256 * i;
+          if (it < STEP * VCH) vb[i].load(Vh + (size_t)min(s0 + it / VCH, N - 1) * D + (it % VCH) * 8);
+        }
       }
     }
   };
   load_rows(t_beg);
 
   for (int s0 = t_beg; s0 < t_end; s0 += STEP) {
-    const int qtok = s0 + 32 * w + col;
+    const int qtok = s0 + 32 * qt + col;
     const bool qvalid = qwave && qtok < t_end;
-    if (causal) {
-      if (qwave) {
-        Feat Fk;
-        Fk.compute(kx, PH, PLo, LDP, Lg, scale, tau, lane);
-#pragma unroll
-        for (int jp = 0; jp < LPG / 2; ++jp) {
-          float x0[8], x1[8];
-#pragma unroll
-          for (int b = 0; b < 8; ++b) {
-            x0[b] = qvalid ? Fk.phi[jp][b] : 0.0f;
-            x1[b] = qvalid ? Fk.phi[jp][8 + b] : 0.0f;
-          }
-          store8(&sm.FS[32 * w + col][Feat::feat(jp, 0, h)], x0);
-          store8(&sm.FS[32 * w + col][Feat::feat(jp, 8, h)], x1);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < VIT; ++i) {
-        const int it = tid + 256 * i;
-        if (it < STEP * VCH) vb[i].store(&sm.XS[it / VCH][(it % VCH) * 8]);
-      }
-    }
-    Feat Fq;
-    typename M::frag dn[D / M::KSTEP];
     const float e_q = qvalid ? eq : 0.0f, dd_q = qvalid ? ddq : 0.0f;
-    if (qwave) {
-      Fq.compute(qx, PH, PLo, LDP, Lg, scale, tau, lane);
-#pragma unroll
-      for (int ks = 0; ks < D / M::KSTEP; ++ks) {
-        float x[M::KPL];
-        if constexpr (M::KPL == 8) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = (float)ox[ks][e] * e_q;
-        } else {
-          x[0] = ox[ks] * e_q;
-        }
-        dn[ks] = M::from_floats(x);
-      }
-    }
-    __syncthreads();
-
-    if (qwave) {
-      // Sparse dQ partials of this query (first group only), loads in flight
-      // during the products below.
-      // dphi(Q)^T (rows = features, columns = queries) = S dnum^T + z dd^T + the
-      // causally masked part of the step.
-      floatx16 df[NFT];
-#pragma unroll
-      for (int ft = 0; ft < NFT; ++ft) {
-        df[ft] = zero16();
-#pragma unroll
-        for (int ks = 0; ks < D / M::KSTEP; ++ks)
-          df[ft] = M::mma(row_frag<T>(&sm.SF[0][0], LDD, 32 * ft, 0, ks, lane), dn[ks], df[ft]);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) df[ft][v] += sm.zr[32 * ft + acc_row(v, h)] * dd_q;
-      }
+    // One step for one half, compiled per half so that only that half's tables
+    // are kept. Both halves pass the same two barriers.
+    auto step = [&](auto hc) __attribute__((always_inline)) {
+      constexpr int HALF = decltype(hc)::value;
+      constexpr bool ACTIVE_A = HALF == 0 || NFT >= 2;
+      // Staging: phi(K) of key tile qt (half 0) or a share of the V rows (half 1).
       if (causal) {
-        for (int kt = 0; kt <= w; ++kt) {
-          floatx16 gt = zero16();
+        if constexpr (HALF == 0) {
+          if (qwave)
+            Feat::compute_to_row(kx, PH, PLo, LDP, Lg, scale, tau, lane, qvalid, &sm.FS[32 * qt + col][0]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < VIT; ++i) {
+            const int it = ts + 256 * i;
+            if (it < STEP * VCH) vb[i].store(&sm.XS[it / VCH][(it % VCH) * 8]);
+          }
+        }
+      }
+      // phi(Q) and dnum of the query tile, from registers.
+      Feat Fq;
+      typename M::frag dn[D / M::KSTEP];
+      if (qwave && ACTIVE_A) {
+        Fq.compute(qx, PH, PLo, LDP, Lg, scale, tau, lane);
+#pragma unroll
+        for (int ks = 0; ks < D / M::KSTEP; ++ks) {
+          float x[M::KPL];
+          if constexpr (M::KPL == 8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = (float)ox[ks][e] * e_q;
+          } else {
+            x[0] = ox[ks] * e_q;
+          }
+          dn[ks] = M::from_floats(x);
+        }
+      }
+      __syncthreads();
+
+      // dphi(Q)^T for this half's feature tiles (rows = features, columns =
+      // queries) = S dnum^T + z dd^T + the causally masked part of the step, then
+      // back through this half's tables; da to LDS.
+      if (qwave && ACTIVE_A) {
+        floatx16 df[NFH];
+#pragma unroll
+        for (int i = 0; i < NFH; ++i) {
+          const int ft = HALF * NFH + i;
+          df[i] = zero16();
 #pragma unroll
           for (int ks = 0; ks < D / M::KSTEP; ++ks)
-            gt = M::mma(row_frag<T>(&sm.XS[0][0], LDD, 32 * kt, 0, ks, lane), dn[ks], gt);
+            df[i] = M::mma(row_frag<T>(&sm.SF[0][0], LDD, 32 * ft, 0, ks, lane), dn[ks], df[i]);
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            gt[v] += dd_q;
-            if (kt == w && acc_row(v, h) > col) gt[v] = 0.0f;
-          }
+          for (int v = 0; v < 16; ++v) df[i][v] += sm.zr[32 * ft + acc_row(v, h)] * dd_q;
+        }
+        if (causal) {
+          for (int kt = 0; kt <= qt; ++kt) {
+            floatx16 gt = zero16();
 #pragma unroll
-          for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
-            const typename M::frag gf = M::from_acc(gt, ks2);
+            for (int ks = 0; ks < D / M::KSTEP; ++ks)
+              gt = M::mma(row_frag<T>(&sm.XS[0][0], LDD, 32 * kt, 0, ks, lane), dn[ks], gt);
 #pragma unroll
-            for (int ft = 0; ft < NFT; ++ft)
-              df[ft] = M::mma(tr_frag<T>(&sm.FS[0][0], LDR, 32 * kt, 32 * ft, ks2, lane, true), gf, df[ft]);
+            for (int v = 0; v < 16; ++v) {
+              gt[v] += dd_q;
+              if (kt == qt && acc_row(v, h) > col) gt[v] = 0.0f;
+            }
+#pragma unroll
+            for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
+              const typename M::frag gf = M::from_acc(gt, ks2);
+#pragma unroll
+              for (int i = 0; i < NFH; ++i)
+                df[i] = M::mma(tr_frag<T>(&sm.FS[0][0], LDR, 32 * kt, 32 * (HALF * NFH + i), ks2, lane,
+                                          true),
+                               gf, df[i]);
+            }
           }
         }
-      }
-      float da[LPG / 2][4];
 #pragma unroll
-      for (int ft = 0; ft < NFT; ++ft) {
-        float dphi[16];
-        tile_to_table(df[ft], h, dphi);
-        Fq.backward_table(ft, dphi, da[ft]);
+        for (int i = 0; i < NFH; ++i) {
+          const int ft = HALF * NFH + i;
+          float dphi[16], da4[4];
+          tile_to_table(df[i], h, dphi);
+          Fq.backward_table(ft, dphi, da4);
+          *reinterpret_cast<floatx4*>(&DA.da[qt][h][col][4 * ft]) =
+              floatx4{da4[0], da4[1], da4[2], da4[3]};
+        }
       }
-      floatx16 dx[D / 32];
-      features_dx<T, D, LPG>(da, RTs, rt_lds_width<LPG>(), c2, lane, dx);
-      if (qvalid)
-        write_grad_row<T, D>(dx, scratch, dQ, ((size_t)bh * N + qtok) * D, h, first != 0,
-                             last != 0);
-    }
-    load_rows(s0 + STEP);  // past the span: loads nothing
+      __syncthreads();  // da of every table in LDS
+
+      // dQ for this half's channel tiles from every table's da.
+      if (qwave && (NDA > 1 || HALF == 0)) {
+        float da[LPG / 2][4];
+#pragma unroll
+        for (int jp = 0; jp < LPG / 2; ++jp) {
+          const floatx4 x = *reinterpret_cast<const floatx4*>(&DA.da[qt][h][col][4 * jp]);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) da[jp][t] = x[t];
+        }
+        floatx16 dx[NDH];
+        features_dx<T, D, LPG, T, NDH>(da, RTs, rt_lds_width<LPG>(), c2, lane, dx, HALF * NDH);
+        if (qvalid)
+          write_grad_row<T, D, NDH>(dx, scratch, dQ, ((size_t)bh * N + qtok) * D, h, first != 0,
+                                    last != 0, HALF * NDH);
+      }
+    };
+    if (half == 0) step(std::integral_constant<int, 0>{});
+    else step(std::integral_constant<int, 1>{});
     if (!causal) break;
-    __syncthreads();
-    advance_stats<T, D, LPG, SPW, STEP>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, nullptr, w, lane, st,
-                                        &sm.SF[0][0], sm.zr);
+    advance_stats<T, D, LPG, SPW, STEP, true, NW>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, nullptr, w,
+                                                  lane, st, &sm.SF[0][0], sm.zr);
+    load_rows(s0 + STEP);  // past the span: loads nothing that matters
     __syncthreads();
   }
 }
@@ -846,7 +882,8 @@ __global__ void __launch_bounds__(256)
   __shared__ T RTs[D * rt_lds_width<LPG>()];
   __shared__ PlanesLds<T, D, LPG> PLs;
   const int bh = blockIdx.y, c = blockIdx.x, head = bh % H;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int w = tid >> 6;
   // role 0: dK of key tile kt (and phi(K) of it); role 1: dV of key tile kt, phi(Q)
   // of query tile kt and the dnum staging; 2+: staging only.
   const int kt = w % QT, role = w / QT;
@@ -906,21 +943,8 @@ __global__ void __launch_bounds__(256)
     const int s0 = t_beg + si * STEP;
     const int ktok = s0 + 32 * kt + col;
     const bool kvalid = ktok < t_end;
-    if (role == 1) {
-      Feat Fq;
-      Fq.compute(xr, PH, PLo, LDP, Lg, scale, tau, lane);
-#pragma unroll
-      for (int jp = 0; jp < LPG / 2; ++jp) {
-        float x0[8], x1[8];
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          x0[b] = kvalid ? Fq.phi[jp][b] : 0.0f;
-          x1[b] = kvalid ? Fq.phi[jp][8 + b] : 0.0f;
-        }
-        store8(&sm.FS[32 * kt + col][Feat::feat(jp, 0, h)], x0);
-        store8(&sm.FS[32 * kt + col][Feat::feat(jp, 8, h)], x1);
-      }
-    }
+    if (role == 1)
+      Feat::compute_to_row(xr, PH, PLo, LDP, Lg, scale, tau, lane, kvalid, &sm.FS[32 * kt + col][0]);
     if (owave) {
 #pragma unroll
       for (int i = 0; i < OIT; ++i) {
@@ -1107,9 +1131,10 @@ size_t bwd_lds_need(const Problem& pb) {
       auto need = [&](auto lc) {
         constexpr int LPG = ELSAA_C(lc);
         constexpr size_t RTB = sizeof(T) * D * rt_lds_width<LPG>() + sizeof(PlanesLds<T, D, LPG>);
-        constexpr int SQ = walk_step<T, D, LPG, 128, RTB>();
+        constexpr int SQ = walk_step<T, D, LPG, 128, RTB + sizeof(QdaLds<LPG>)>();
         constexpr int SK = walk_step<T, D, LPG, 64, RTB + sizeof(T) * 64 * tile_ld<T>(16 * LPG)>();
-        const size_t a = RTB + (SQ > 0 ? sizeof(WalkSmem<T, D, LPG, SQ>) : sizeof(WalkSmem<T, D, LPG, 32>));
+        const size_t a = RTB + sizeof(QdaLds<LPG>) +
+                         (SQ > 0 ? sizeof(WalkSmem<T, D, LPG, SQ>) : sizeof(WalkSmem<T, D, LPG, 32>));
         const size_t b = RTB + (SK > 0 ? sizeof(WalkSmem<T, D, LPG, SK>) : sizeof(WalkSmem<T, D, LPG, 32>)) +
                          sizeof(T) * (SK > 0 ? SK : 32) * tile_ld<T>(16 * LPG);
         lr = a > b ? a : b;
@@ -1209,7 +1234,7 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
       auto run_lr = [&](auto lc) {
         constexpr int LPG = ELSAA_C(lc);
         constexpr size_t RTB = sizeof(T) * D * rt_lds_width<LPG>() + sizeof(PlanesLds<T, D, LPG>);
-        constexpr int SQ = walk_step<T, D, LPG, 128, RTB>();
+        constexpr int SQ = walk_step<T, D, LPG, 128, RTB + sizeof(QdaLds<LPG>)>();
         constexpr int SK = walk_step<T, D, LPG, 64, RTB + sizeof(T) * 64 * tile_ld<T>(16 * LPG)>();
         if constexpr (SQ > 0 && SK > 0) {
           const int span_q = pb.causal ? pb.chunk : SQ;
@@ -1217,7 +1242,7 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
           for (int g = 0; g < groups; ++g) {
             const int first = g == 0, last = g == groups - 1;
             ELSAA_LAUNCH("lr_bwd_q", (lr_bwd_q_kernel<T, D, LPG, SQ>),
-                         dim3((pb.N + span_q - 1) / span_q, BH), dim3(256), 0, st, (const T*)Q,
+                         dim3((pb.N + span_q - 1) / span_q, BH), dim3(512), 0, st, (const T*)Q,
                          (const T*)K, (const T*)V, (const T*)dO, planes_lr, A, z, re, rdd,
                          (const T*)dQp, scrQ, (T*)dQ, RT, pw, pb.H, pb.N, pb.L, span_q,
                          pb.levels, (int)pb.causal, pb.scale, pb.tau, g, first, last);

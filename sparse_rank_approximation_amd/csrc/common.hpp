@@ -28,6 +28,12 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ int acc_row(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
 
+// Index of this wave in its workgroup, as a wave-uniform (scalar register) value:
+// branches and loop bounds that depend only on it are then known to be uniform.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+}
+
 template <typename T>
 struct MF;
 
@@ -533,6 +539,56 @@ struct Features {
       }
     activate(u, L, scale, tau, lane);
   }
+  // phi of every table for this lane's token (zero when !valid) stored straight
+  // into the LDS row dst (features 16 table + b), one table pair at a time so that
+  // only 16 feature values are live at once.
+  static __device__ __forceinline__ void compute_to_row(
+      const typename MF<T>::frag (&xf)[D / MF<T>::KSTEP], const T* PH, const T* PL, int ldp, int L,
+      float scale, float tau, int lane, bool valid, T* dst) {
+    typedef MF<T> M;
+    const int h = lane >> 5;
+    floatx16 u[NPT];
+#pragma unroll
+    for (int mt = 0; mt < NPT; ++mt) u[mt] = zero16();
+#pragma unroll
+    for (int ks = 0; ks < D / M::KSTEP; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < NPT; ++mt) {
+        u[mt] = M::mma(row_frag<T>(PH, ldp, 32 * mt, 0, ks, lane), xf[ks], u[mt]);
+        if constexpr (M::KPL > 1) u[mt] = M::mma(row_frag<T>(PL, ldp, 32 * mt, 0, ks, lane), xf[ks], u[mt]);
+      }
+    const float c2 = 2.0f * scale / tau;
+#pragma unroll
+    for (int mt = 0; mt < NPT; ++mt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int jp = 4 * mt + g;
+        if (jp >= NJP) continue;
+        const bool live = valid && 2 * jp + h < L;
+        float p[4], q[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float a = c2 * u[mt][4 * g + t];
+          p[t] = sigmoid(a);
+          q[t] = sigmoid(-a);
+        }
+        float lo4[4], hi4[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          lo4[b] = ((b & 1) ? p[0] : q[0]) * ((b & 2) ? p[1] : q[1]);
+          hi4[b] = ((b & 1) ? p[2] : q[2]) * ((b & 2) ? p[3] : q[3]);
+        }
+        float x0[8], x1[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          x0[b] = live ? lo4[b & 3] * hi4[b >> 2] : 0.0f;
+          x1[b] = live ? lo4[(8 + b) & 3] * hi4[(8 + b) >> 2] : 0.0f;
+        }
+        store8(dst + feat(jp, 0, h), x0);
+        store8(dst + feat(jp, 8, h), x1);
+      }
+  }
+
   // phi from the projection tiles u (rows = projections, columns = tokens).
   __device__ __forceinline__ void activate(const floatx16 (&u)[NPT], int L, float scale, float tau,
                                            int lane) {
@@ -634,15 +690,15 @@ __device__ __forceinline__ void tile_to_table(const floatx16& acc, int h, float 
 // the lane half, jp = q / 4, t = q % 4) is the accumulator-row order, so the
 // hyperplanes are read from RT = R^T ([D][row stride pw] fp32, zero past 4 L) with
 // the same two-run pattern as load_accperm.
-template <typename T, int D, int LP, typename R>
+template <typename T, int D, int LP, typename R, int NDT = D / 32>
 __device__ __forceinline__ void features_dx(const float (&da)[LP / 2][4], const R* RT, int pw,
-                                            float c2, int lane, floatx16 (&dx)[D / 32]) {
+                                            float c2, int lane, floatx16 (&dx)[NDT], int dt0 = 0) {
   typedef MF<T> M;
   constexpr int NQ = 2 * LP;  // (table, hyperplane) pairs per lane half
   constexpr int NKS = (NQ + M::KPL - 1) / M::KPL;
   const int h = lane >> 5, col = lane & 31;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) dx[dt] = zero16();
+  for (int dt = 0; dt < NDT; ++dt) dx[dt] = zero16();
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     float b[M::KPL];
@@ -653,8 +709,8 @@ __device__ __forceinline__ void features_dx(const float (&da)[LP / 2][4], const 
     }
     const typename M::frag bf = M::from_floats(b);
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const R* row = RT + (size_t)(32 * dt + col) * pw;
+    for (int dt = 0; dt < NDT; ++dt) {
+      const R* row = RT + (size_t)(32 * (dt0 + dt) + col) * pw;
       float a[M::KPL];
       if constexpr (M::KPL == 8) {
         float lo[4], hi[4];
@@ -669,7 +725,7 @@ __device__ __forceinline__ void features_dx(const float (&da)[LP / 2][4], const 
     }
   }
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) dx[dt][v] *= c2;
 }
@@ -759,14 +815,18 @@ __device__ __forceinline__ void advance_stats(const T* X, int ldd, const T* F, i
   typedef MF<T> M;
   constexpr int NFT = LP / 2, NST = (D / 32) * NFT;
   const int h = lane >> 5, col = lane & 31;
+  floatx16 zs[SPW];
 #pragma unroll
-  for (int i = 0; i < SPW; ++i) {
-    const int tix = w + NW * i;
-    if (tix < NST) {
-      const int mt = tix / NFT, nt = tix % NFT;
-      floatx16 zs = zero16();
+  for (int i = 0; i < SPW; ++i) zs[i] = zero16();
+  // K steps outermost (two at a time) with this wave's tiles inside, so that the
+  // operand fragments in flight stay few.
+#pragma unroll 2
+  for (int ks = 0; ks < STEP / M::KSTEP; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < STEP / M::KSTEP; ++ks) {
+    for (int i = 0; i < SPW; ++i) {
+      const int tix = w + NW * i;
+      if (tix < NST) {
+        const int mt = tix / NFT, nt = tix % NFT;
         const typename M::frag fb = tr_frag<T>(F, ldr, 0, 32 * nt, ks, lane, false);
         st[i] = M::mma(tr_frag<T>(X, ldd, 0, 32 * mt, ks, lane, false), fb, st[i]);
         if (mt == 0) {
@@ -774,16 +834,23 @@ __device__ __forceinline__ void advance_stats(const T* X, int ldd, const T* F, i
 #pragma unroll
           for (int e = 0; e < M::KPL; ++e) a[e] = wt ? wt[ks * M::KSTEP + M::KPL * h + e] : 1.0f;
           const typename M::frag ahi = M::from_floats(a);
-          zs = M::mma(ahi, fb, zs);
+          zs[i] = M::mma(ahi, fb, zs[i]);
           if constexpr (M::KPL > 1) {
             if (wt) {
 #pragma unroll
               for (int e = 0; e < M::KPL; ++e) a[e] -= (float)ahi[e];
-              zs = M::mma(M::from_floats(a), fb, zs);
+              zs[i] = M::mma(M::from_floats(a), fb, zs[i]);
             }
           }
         }
       }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    const int tix = w + NW * i;
+    if (tix < NST) {
+      const int mt = tix / NFT, nt = tix % NFT;
       if constexpr (WRITE_SF) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -793,7 +860,7 @@ __device__ __forceinline__ void advance_stats(const T* X, int ldd, const T* F, i
           store4(SF + (size_t)(32 * nt + col) * ldd + 32 * mt + 8 * g + 4 * h, x);
         }
       }
-      if (mt == 0 && h == 0) zr[32 * nt + col] += zs[0];
+      if (mt == 0 && h == 0) zr[32 * nt + col] += zs[i][0];
     }
   }
 }

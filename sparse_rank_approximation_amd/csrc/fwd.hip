@@ -51,7 +51,8 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
   __shared__ int kidx[KT];
 
   const int bh = blockIdx.y, item = blockIdx.x;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int w = wave_id();  // wave index, uniform (scalar) so that role branches stay uniform
   const size_t P = perm_stride(N, levels, causal);
   const size_t slots = partial_slots(N, levels, causal);
 
@@ -193,7 +194,8 @@ __global__ void __launch_bounds__(256)
 
   const int bh = blockIdx.y, c = blockIdx.x, head = bh % H;
   const int r = 16 * L;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int w = wave_id();  // wave index, uniform (scalar) so that role branches stay uniform
   const int qt = w % QT, dt0 = (w / QT) * NDT;
   const bool owner = dt0 < NDA;  // waves past the channel tiles only stage
   const float* pl = planes + (size_t)head * L * 4 * D;
@@ -242,22 +244,9 @@ __global__ void __launch_bounds__(256)
   for (int s0 = t_beg; s0 < t_end; s0 += STEP) {
     // Stage the step's keys: phi(K) and V into LDS (causal only).
     if (causal) {
-      if (w < QT) {
-        Feat Fk;
-        Fk.compute(kx, PH, PLo, LDP, L, scale, tau, lane);
-        const bool kv = s0 + 32 * w + col < t_end;
-#pragma unroll
-        for (int jp = 0; jp < LP / 2; ++jp) {
-          float x0[8], x1[8];
-#pragma unroll
-          for (int b = 0; b < 8; ++b) {
-            x0[b] = kv ? Fk.phi[jp][b] : 0.0f;
-            x1[b] = kv ? Fk.phi[jp][8 + b] : 0.0f;
-          }
-          store8(&sm.FS[32 * w + col][Feat::feat(jp, 0, h)], x0);
-          store8(&sm.FS[32 * w + col][Feat::feat(jp, 8, h)], x1);
-        }
-      }
+      if (w < QT)
+        Feat::compute_to_row(kx, PH, PLo, LDP, L, scale, tau, lane, s0 + 32 * w + col < t_end,
+                             &sm.FS[32 * w + col][0]);
 #pragma unroll
       for (int i = 0; i < VIT; ++i) {
         const int it = tid + 256 * i;

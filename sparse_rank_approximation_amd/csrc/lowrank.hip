@@ -58,7 +58,8 @@ __global__ void __launch_bounds__(512) lr_sums_kernel(const T* __restrict__ X, c
   const int bh = blockIdx.y, tile = blockIdx.x, ntile = gridDim.x;
   const int r = 16 * L;
   const int t0 = tile * TT, t1 = min(N, t0 + TT);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int w = wave_id();  // wave index, uniform (scalar) so that role branches stay uniform
   const T* Xh = X + (size_t)bh * N * D;
   const T* Yh = Y + (size_t)bh * N * D;
   stage_planes<T, D, LP, 512>(planes + (size_t)(bh % H) * L * 4 * D, L, PLs, tid);
@@ -92,22 +93,9 @@ __global__ void __launch_bounds__(512) lr_sums_kernel(const T* __restrict__ X, c
   __syncthreads();  // hyperplanes staged
   load_rows(t0);
   for (int s0 = t0; s0 < t1; s0 += SUB) {
-    if (w < QT) {
-      const bool valid = s0 + 32 * w + col < t1;
-      Feat F;
-      F.compute(xr, PH, PLo, LDP, L, scale, tau, lane);
-#pragma unroll
-      for (int jp = 0; jp < LP / 2; ++jp) {
-        float x0[8], x1[8];
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          x0[b] = valid ? F.phi[jp][b] : 0.0f;
-          x1[b] = valid ? F.phi[jp][8 + b] : 0.0f;
-        }
-        store8(&sm.FS[32 * w + col][Feat::feat(jp, 0, h)], x0);
-        store8(&sm.FS[32 * w + col][Feat::feat(jp, 8, h)], x1);
-      }
-    }
+    if (w < QT)
+      Feat::compute_to_row(xr, PH, PLo, LDP, L, scale, tau, lane, s0 + 32 * w + col < t1,
+                           &sm.FS[32 * w + col][0]);
     if (ts >= 0) {
 #pragma unroll
       for (int i = 0; i < VIT; ++i) {

@@ -36,7 +36,7 @@ class Workload:
     gen: str            # Q/K generator kind
     gen_args: dict = field(default_factory=dict)
     lr_bits: int = 4
-    chunk: int = 512    # causal RACE summary spacing
+    chunk: int = 2048   # causal RACE summary spacing (numerics-neutral; larger is faster)
 
     @property
     def hash_bits(self) -> int:
