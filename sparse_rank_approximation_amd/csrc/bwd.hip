@@ -552,14 +552,14 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
     const int bh = head_of(g), lev = lev_of(g);
     const bool leaf = leaf_of(g);
     // Phase 1: key wave w.
+    const int key = 32 * w + col;
+    floatx16 dv[D / 32], dk[D / 32];
     {
-      const int key = 32 * w + col;
       const int jk = sm.kidx[key];
       const bool kvalid = jk >= 0;
       typename M::frag kf[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kf[ks] = row_frag<T>(&sm.Ks[0][0], LD, 32 * w, 0, ks, lane);
-      floatx16 dv[D / 32], dk[D / 32];
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) dv[dt] = dk[dt] = zero16();
       for (int qt = leaf ? w : 0; qt < NW; ++qt) {
@@ -598,32 +598,26 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
           }
         }
       }
-      if (kvalid) {
-        const size_t ksl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_past(jk, N, lev)
-                                    : (size_t)jk;
-        T* dvp = dVp + ((size_t)bh * slots + ksl) * D;
-        T* dkp = dKp + ((size_t)bh * slots + ksl) * D;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int gg = 0; gg < 4; ++gg) {
-            float xv[4], xk[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              xv[e] = dv[dt][4 * gg + e];
-              xk[e] = dk[dt][4 * gg + e] * scale;
-            }
-            store4(dvp + 32 * dt + 8 * gg + 4 * h, xv);
-            store4(dkp + 32 * dt + 8 * gg + 4 * h, xk);
-          }
-      }
     }
-    __syncthreads();  // dS^T complete
+    __syncthreads();  // dS^T complete; Qs and Os no longer read
+    // dV and dK tiles to LDS (rows = keys of the block) for row-contiguous stores.
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        float xv[4], xk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xv[e] = dv[dt][4 * gg + e];
+          xk[e] = dk[dt][4 * gg + e] * scale;
+        }
+        const int c = 32 * dt + 8 * gg + 4 * h;
+        store4(&sm.Qs[key][c], xv);
+        store4(&sm.Os[key][c], xk);
+      }
     // Phase 2: dQ^T = K^T dS^T for query tile w (leaf blocks: keys up to the tile).
+    floatx16 dq[D / 32];
     {
-      const int query = 32 * w + col;
-      const int iq = sm.qidx[query];
-      floatx16 dq[D / 32];
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) dq[dt] = zero16();
       const int nks = leaf ? 2 * (w + 1) : KT / M::KSTEP;
@@ -633,19 +627,42 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
         for (int dt = 0; dt < D / 32; ++dt)
           dq[dt] = M::mma(tr_frag<T>(&sm.Ks[0][0], LD, 0, 32 * dt, ks, lane, false), bq, dq[dt]);
       }
-      if (iq >= 0) {
-        const size_t sl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_future_b(iq, N, lev)
-                                   : (size_t)iq;
-        T* dst = dQp + ((size_t)bh * slots + sl) * D;
+    }
+    __syncthreads();  // Ks no longer read; dV, dK tiles complete
+    // dQ tile to LDS (rows = queries of the block); the three gradient tiles then
+    // go out to their slots with row-contiguous 16-byte stores.
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-          for (int gg = 0; gg < 4; ++gg) {
-            float x[4];
+      for (int gg = 0; gg < 4; ++gg) {
+        float xq[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = dq[dt][4 * gg + e] * scale;
-            store4(dst + 32 * dt + 8 * gg + 4 * h, x);
-          }
+        for (int e = 0; e < 4; ++e) xq[e] = dq[dt][4 * gg + e] * scale;
+        store4(&sm.Ks[key][32 * dt + 8 * gg + 4 * h], xq);
+      }
+    __syncthreads();
+    {
+      const size_t hb = (size_t)bh * slots;
+#pragma unroll
+      for (int i = 0; i < GIT; ++i) {
+        const int piece = tid + NT * i, rr = piece / CH, c8 = (piece % CH) * 8;
+        const int jk = sm.kidx[rr], iq = sm.qidx[rr];
+        if (jk >= 0) {
+          const size_t sl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_past(jk, N, lev)
+                                     : (size_t)jk;
+          Vec8<T> a, b2;
+          a.load(&sm.Qs[rr][c8]);
+          b2.load(&sm.Os[rr][c8]);
+          a.store(dVp + (hb + sl) * D + c8);
+          b2.store(dKp + (hb + sl) * D + c8);
+        }
+        if (iq >= 0) {
+          const size_t sl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_future_b(iq, N, lev)
+                                     : (size_t)iq;
+          Vec8<T> a;
+          a.load(&sm.Ks[rr][c8]);
+          a.store(dQp + (hb + sl) * D + c8);
+        }
       }
     }
   }
