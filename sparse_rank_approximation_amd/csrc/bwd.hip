@@ -727,158 +727,170 @@ __global__ void __launch_bounds__(512)
   for (int f = tid; f < RP; f += 512) sm.zr[f] = f0 + f < r ? z[sidx * r + f0 + f] : 0.0f;
   __syncthreads();  // hyperplanes and statistics staged
 
-  // Rows of one step: the wave's query tile (Q, dO, dd_lr, scale of dnum; both
-  // halves), its key tile (K; half 0) and a share of the V rows (half 1). Tokens
-  // past the span read a stand-in row; their dnum and dd_lr are zeroed where used
-  // and their phi(K) rows are stored as zero.
-  typename M::frag qx[D / M::KSTEP], ox[D / M::KSTEP], kx[D / M::KSTEP];
-  Vec8<T> vb[VIT];
-  float eq = 0.0f, ddq = 0.0f;
-  const int ts = tid - 256;  // V staging thread (half 1)
-  auto load_rows = [&](int s0) __attribute__((always_inline)) {
-    const int tok = min(s0 + 32 * qt + col, N - 1);
-    const size_t rrow = (size_t)tok * D;
-    prefetch_row_frags<T, D>(Qh + rrow, qx, h);
-    prefetch_row_frags<T, D>(dOh + rrow, ox, h);
-    eq = re[(size_t)bh * N + tok];
-    ddq = rdd[(size_t)bh * N + tok];
-    if (causal) {
-      if (half == 0) prefetch_row_frags<T, D>(Kh + rrow, kx, h);
-      if (ts >= 0) {
-#pragma unroll
-        for (int i = 0; i < VIT; ++i) {
-          const int it = ts + 256 * i;
-          if (it < STEP * VCH) vb[i].load(Vh + (size_t)min(s0 + it / VCH, N - 1) * D + (it % VCH) * 8);
-        }
-      }
-    }
-  };
-  load_rows(t_beg);
-
-  for (int s0 = t_beg; s0 < t_end; s0 += STEP) {
-    const int qtok = s0 + 32 * qt + col;
-    const bool qvalid = qwave && qtok < t_end;
-    const float e_q = qvalid ? eq : 0.0f, dd_q = qvalid ? ddq : 0.0f;
-    // One step for one half, compiled per half so that only that half's tables
-    // are kept. Both halves pass the same two barriers.
-    auto step = [&](auto hc) __attribute__((always_inline)) {
-      constexpr int HALF = decltype(hc)::value;
-      constexpr bool ACTIVE_A = HALF == 0 || NFT >= 2;
-      // Staging: phi(K) of key tile qt (half 0) or a share of the V rows (half 1).
+  // The walk, compiled per half so that each wave keeps only its half's
+  // registers; both halves pass the same barriers.
+  auto walk = [&](auto hc) __attribute__((always_inline)) {
+    constexpr int HALF = decltype(hc)::value;
+    // Rows of one step: the wave's query tile (Q, dO, dd_lr, scale of dnum; both
+    // halves), its key tile (K; half 0) and a share of the V rows (half 1). Tokens
+    // past the span read a stand-in row; their dnum and dd_lr are zeroed where used
+    // and their phi(K) rows are stored as zero.
+    typename M::frag qx[D / M::KSTEP], ox[D / M::KSTEP], kx[D / M::KSTEP];
+    Vec8<T> vb[VIT];
+    float eq = 0.0f, ddq = 0.0f;
+    const int ts = tid - 256;  // V staging thread (half 1)
+    auto load_rows = [&](int s0) __attribute__((always_inline)) {
+      const int tok = min(s0 + 32 * qt + col, N - 1);
+      const size_t rrow = (size_t)tok * D;
+      prefetch_row_frags<T, D>(Qh + rrow, qx, h);
+      prefetch_row_frags<T, D>(dOh + rrow, ox, h);
+      eq = re[(size_t)bh * N + tok];
+      ddq = rdd[(size_t)bh * N + tok];
       if (causal) {
-        if constexpr (HALF == 0) {
-          if (qwave)
-            Feat::compute_to_row(kx, PH, PLo, LDP, Lg, scale, tau, lane, qvalid, &sm.FS[32 * qt + col][0]);
-        } else {
-#pragma unroll
+        if constexpr (HALF == 0) prefetch_row_frags<T, D>(Kh + rrow, kx, h);
+        if constexpr (HALF == 1) {
+  #pragma unroll
           for (int i = 0; i < VIT; ++i) {
             const int it = ts + 256 * i;
-            if (it < STEP * VCH) vb[i].store(&sm.XS[it / VCH][(it % VCH) * 8]);
+            if (it < STEP * VCH) vb[i].load(Vh + (size_t)min(s0 + it / VCH, N - 1) * D + (it % VCH) * 8);
           }
         }
-      }
-      // phi(Q) and dnum of the query tile, from registers.
-      Feat Fq;
-      typename M::frag dn[D / M::KSTEP];
-      if (qwave && ACTIVE_A) {
-        Fq.compute(qx, PH, PLo, LDP, Lg, scale, tau, lane);
-#pragma unroll
-        for (int ks = 0; ks < D / M::KSTEP; ++ks) {
-          float x[M::KPL];
-          if constexpr (M::KPL == 8) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = (float)ox[ks][e] * e_q;
-          } else {
-            x[0] = ox[ks] * e_q;
-          }
-          dn[ks] = M::from_floats(x);
-        }
-      }
-      __syncthreads();
-
-      // dphi(Q)^T for this half's feature tiles (rows = features, columns =
-      // queries) = S dnum^T + z dd^T + the causally masked part of the step, then
-      // back through this half's tables; da to LDS.
-      if (qwave && ACTIVE_A) {
-        floatx16 df[NFH];
-#pragma unroll
-        for (int i = 0; i < NFH; ++i) {
-          const int ft = HALF * NFH + i;
-          df[i] = zero16();
-#pragma unroll
-          for (int ks = 0; ks < D / M::KSTEP; ++ks)
-            df[i] = M::mma(row_frag<T>(&sm.SF[0][0], LDD, 32 * ft, 0, ks, lane), dn[ks], df[i]);
-#pragma unroll
-          for (int v = 0; v < 16; ++v) df[i][v] += sm.zr[32 * ft + acc_row(v, h)] * dd_q;
-        }
-        if (causal) {
-          for (int kt = 0; kt <= qt; ++kt) {
-            floatx16 gt = zero16();
-#pragma unroll
-            for (int ks = 0; ks < D / M::KSTEP; ++ks)
-              gt = M::mma(row_frag<T>(&sm.XS[0][0], LDD, 32 * kt, 0, ks, lane), dn[ks], gt);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              gt[v] += dd_q;
-              if (kt == qt && acc_row(v, h) > col) gt[v] = 0.0f;
-            }
-#pragma unroll
-            for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
-              const typename M::frag gf = M::from_acc(gt, ks2);
-#pragma unroll
-              for (int i = 0; i < NFH; ++i)
-                df[i] = M::mma(tr_frag<T>(&sm.FS[0][0], LDR, 32 * kt, 32 * (HALF * NFH + i), ks2, lane,
-                                          true),
-                               gf, df[i]);
-            }
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < NFH; ++i) {
-          const int ft = HALF * NFH + i;
-          float dphi[16], da4[4];
-          tile_to_table(df[i], h, dphi);
-          Fq.backward_table(ft, dphi, da4);
-          *reinterpret_cast<floatx4*>(&DA.da[qt][h][col][4 * ft]) =
-              floatx4{da4[0], da4[1], da4[2], da4[3]};
-        }
-      }
-      __syncthreads();  // da of every table in LDS
-
-      // dQ for this half's channel tiles from every table's da.
-      if (qwave && (NDA > 1 || HALF == 0)) {
-        float da[LPG / 2][4];
-#pragma unroll
-        for (int jp = 0; jp < LPG / 2; ++jp) {
-          const floatx4 x = *reinterpret_cast<const floatx4*>(&DA.da[qt][h][col][4 * jp]);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) da[jp][t] = x[t];
-        }
-        floatx16 dx[NDH];
-        features_dx<T, D, LPG, T, NDH>(da, RTs, rt_lds_width<LPG>(), c2, lane, dx, HALF * NDH);
-        if (qvalid)
-          write_grad_row<T, D, NDH>(dx, scratch, dQ, ((size_t)bh * N + qtok) * D, h, first != 0,
-                                    last != 0, HALF * NDH);
       }
     };
-    if (half == 0) step(std::integral_constant<int, 0>{});
-    else step(std::integral_constant<int, 1>{});
-    if (!causal) break;
-    advance_stats<T, D, LPG, SPW, STEP, true, NW>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, nullptr, w,
-                                                  lane, st, &sm.SF[0][0], sm.zr);
-    load_rows(s0 + STEP);  // past the span: loads nothing that matters
-    __syncthreads();
-  }
+    load_rows(t_beg);
+
+    for (int s0 = t_beg; s0 < t_end; s0 += STEP) {
+      const int qtok = s0 + 32 * qt + col;
+      const bool qvalid = qwave && qtok < t_end;
+      const float e_q = qvalid ? eq : 0.0f, dd_q = qvalid ? ddq : 0.0f;
+      // One step for one half, compiled per half so that only that half's tables
+      // are kept. Both halves pass the same two barriers.
+      {
+        constexpr bool ACTIVE_A = HALF == 0 || NFT >= 2;
+        // Staging: phi(K) of key tile qt (half 0) or a share of the V rows (half 1).
+        if (causal) {
+          if constexpr (HALF == 0) {
+            if (qwave)
+              Feat::compute_to_row(kx, PH, PLo, LDP, Lg, scale, tau, lane, qvalid, &sm.FS[32 * qt + col][0]);
+          } else {
+  #pragma unroll
+            for (int i = 0; i < VIT; ++i) {
+              const int it = ts + 256 * i;
+              if (it < STEP * VCH) vb[i].store(&sm.XS[it / VCH][(it % VCH) * 8]);
+            }
+          }
+        }
+        // phi(Q) and dnum of the query tile, from registers.
+        Feat Fq;
+        typename M::frag dn[D / M::KSTEP];
+        if (qwave && ACTIVE_A) {
+          Fq.compute(qx, PH, PLo, LDP, Lg, scale, tau, lane);
+  #pragma unroll
+          for (int ks = 0; ks < D / M::KSTEP; ++ks) {
+            float x[M::KPL];
+            if constexpr (M::KPL == 8) {
+  #pragma unroll
+              for (int e = 0; e < 8; ++e) x[e] = (float)ox[ks][e] * e_q;
+            } else {
+              x[0] = ox[ks] * e_q;
+            }
+            dn[ks] = M::from_floats(x);
+          }
+        }
+        __syncthreads();
+
+        // dphi(Q)^T for this half's feature tiles (rows = features, columns =
+        // queries) = S dnum^T + z dd^T + the causally masked part of the step, then
+        // back through this half's tables; da to LDS.
+        if (qwave && ACTIVE_A) {
+          floatx16 df[NFH];
+  #pragma unroll
+          for (int i = 0; i < NFH; ++i) {
+            const int ft = HALF * NFH + i;
+            df[i] = zero16();
+  #pragma unroll
+            for (int ks = 0; ks < D / M::KSTEP; ++ks)
+              df[i] = M::mma(row_frag<T>(&sm.SF[0][0], LDD, 32 * ft, 0, ks, lane), dn[ks], df[i]);
+  #pragma unroll
+            for (int v = 0; v < 16; ++v) df[i][v] += sm.zr[32 * ft + acc_row(v, h)] * dd_q;
+          }
+          if (causal) {
+            for (int kt = 0; kt <= qt; ++kt) {
+              floatx16 gt = zero16();
+  #pragma unroll
+              for (int ks = 0; ks < D / M::KSTEP; ++ks)
+                gt = M::mma(row_frag<T>(&sm.XS[0][0], LDD, 32 * kt, 0, ks, lane), dn[ks], gt);
+  #pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                gt[v] += dd_q;
+                if (kt == qt && acc_row(v, h) > col) gt[v] = 0.0f;
+              }
+  #pragma unroll
+              for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
+                const typename M::frag gf = M::from_acc(gt, ks2);
+  #pragma unroll
+                for (int i = 0; i < NFH; ++i)
+                  df[i] = M::mma(tr_frag<T>(&sm.FS[0][0], LDR, 32 * kt, 32 * (HALF * NFH + i), ks2, lane,
+                                            true),
+                                 gf, df[i]);
+              }
+            }
+          }
+  #pragma unroll
+          for (int i = 0; i < NFH; ++i) {
+            const int ft = HALF * NFH + i;
+            float dphi[16], da4[4];
+            tile_to_table(df[i], h, dphi);
+            Fq.backward_table(ft, dphi, da4);
+            *reinterpret_cast<floatx4*>(&DA.da[qt][h][col][4 * ft]) =
+                floatx4{da4[0], da4[1], da4[2], da4[3]};
+          }
+        }
+        __syncthreads();  // da of every table in LDS
+
+        // dQ for this half's channel tiles from every table's da.
+        if (qwave && (NDA > 1 || HALF == 0)) {
+          float da[LPG / 2][4];
+  #pragma unroll
+          for (int jp = 0; jp < LPG / 2; ++jp) {
+            const floatx4 x = *reinterpret_cast<const floatx4*>(&DA.da[qt][h][col][4 * jp]);
+  #pragma unroll
+            for (int t = 0; t < 4; ++t) da[jp][t] = x[t];
+          }
+          floatx16 dx[NDH];
+          features_dx<T, D, LPG, T, NDH>(da, RTs, rt_lds_width<LPG>(), c2, lane, dx, HALF * NDH);
+          if (qvalid)
+            write_grad_row<T, D, NDH>(dx, scratch, dQ, ((size_t)bh * N + qtok) * D, h, first != 0,
+                                      last != 0, HALF * NDH);
+        }
+      }
+      if (!causal) break;
+      advance_stats<T, D, LPG, SPW, STEP, true, NW>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, nullptr, w,
+                                                    lane, st, &sm.SF[0][0], sm.zr);
+      load_rows(s0 + STEP);  // past the span: loads nothing that matters
+      __syncthreads();
+    }
+  };
+  if (half == 0) walk(std::integral_constant<int, 0>{});
+  else walk(std::integral_constant<int, 1>{});
 }
 
 // ---------------------------------------------------------------------------
 // Low-rank branch, key side: one head and span per workgroup, walked backwards in
-// steps of STEP tokens by 4 waves: wave w handles key tile kt = w % (STEP / 32) for
-// dK (w < STEP / 32) or dV (the next STEP / 32 waves). LDS (WalkSmem): dnum (XS) and
-// phi(Q) (FS) of the step's queries, dd_lr of the step (dd), the running query
-// statistics G = sum_i phi(Q_i) dnum_i^T (SF) and g = sum_i phi(Q_i) dd_lr,i (zr).
+// steps of STEP tokens by 8 waves. Key tile kt = (w / 2) % QT, half = w % 2:
+// waves 0 .. 3 form dK (each half takes half of the feature tiles of dphi(K) and
+// its tables; the hyperplane gradients da meet in LDS and each half then forms
+// half of the channels of dK), waves 4 .. 7 form dV (each half takes half of the
+// channels). LDS (WalkSmem): dnum (XS) and phi(Q) (FS) of the step's queries,
+// dd_lr of the step (dd), the running query statistics G = sum_i phi(Q_i) dnum_i^T
+// (SF) and g = sum_i phi(Q_i) dd_lr,i (zr); phi(K) of the step's keys (KFs).
+template <int LPG>
+struct KdaLds {
+  float da[2][2][32][2 * LPG];  // [key tile][lane half][token][table pair * 4 + t]
+};
+
 template <typename T, int D, int LPG, int STEP>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
     lr_bwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                     const T* __restrict__ dO, const float* __restrict__ planes,
                     const float* __restrict__ G, const float* __restrict__ gzs,
@@ -890,20 +902,22 @@ __global__ void __launch_bounds__(256)
   typedef MF<T> M;
   typedef Features<T, D, LPG> Feat;
   typedef WalkSmem<T, D, LPG, STEP> Sm;
-  constexpr int RP = 16 * LPG, NFT = RP / 32, LDD = Sm::LDD, LDR = Sm::LDR;
-  constexpr int QT = STEP / 32, NST = NFT * (D / 32), SPW = (NST + 3) / 4;
-  constexpr int VCH = D / 8, NDW = QT < 2 ? 1 : QT;  // dO staging waves
-  constexpr int OIT = (STEP * VCH + 64 * NDW - 1) / (64 * NDW);
+  constexpr int NW = 8, RP = 16 * LPG, NFT = RP / 32, LDD = Sm::LDD, LDR = Sm::LDR;
+  constexpr int QT = STEP / 32, NST = NFT * (D / 32), SPW = (NST + NW - 1) / NW;
+  constexpr int NFH = NFT > 1 ? NFT / 2 : 1;
+  constexpr int NJH = LPG / 2 > 1 ? LPG / 4 : 1;  // table pairs per half
+  constexpr int NDA = D / 32, NDH = NDA > 1 ? NDA / 2 : 1;
+  constexpr int VCH = D / 8, OIT = (STEP * VCH + 255) / 256;  // dnum pieces per dV thread
   __shared__ Sm sm;
   __shared__ T KFs[STEP][LDR];  // phi(K) of the step's keys, [key][feature]
   __shared__ T RTs[D * rt_lds_width<LPG>()];
   __shared__ PlanesLds<T, D, LPG> PLs;
+  __shared__ KdaLds<LPG> DA;
   const int bh = blockIdx.y, c = blockIdx.x, head = bh % H;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int w = tid >> 6;
-  // role 0: dK of key tile kt (and phi(K) of it); role 1: dV of key tile kt, phi(Q)
-  // of query tile kt and the dnum staging; 2+: staging only.
-  const int kt = w % QT, role = w / QT;
+  const int role = w >> 2, kt = (w >> 1) & 1, half = w & 1;  // role 0: dK, 1: dV
+  const bool kwave = kt < QT;
   const int r = 16 * L, f0 = 128 * grp, Lg = min(8, L - 8 * grp);
   const float* pl = planes + ((size_t)head * L + 8 * grp) * 4 * D;
   const int t_beg = c * span, t_end = min(N, t_beg + span);
@@ -913,170 +927,212 @@ __global__ void __launch_bounds__(256)
   const T* Kh = K + (size_t)bh * N * D;
   const T* Vh = V + (size_t)bh * N * D;
   const T* dOh = dO + (size_t)bh * N * D;
-  // dO staging: waves QT .. QT + NDW - 1 (waves 1 .. 2 when QT == 1).
-  const int ow = QT < 2 ? w - 1 : w - QT;
-  const bool owave = ow >= 0 && ow < NDW;
+  const int ts = tid - 256;  // dnum staging thread (dV waves)
 
   floatx16 st[SPW];
-  load_stats<T, D, LPG, SPW>(G + sidx * D * r, r, f0, w, lane, st, &sm.SF[0][0], LDD);
-  stage_rt<T, D, LPG, 256>(RT + (size_t)head * D * pw + 32 * grp, pw, RTs, tid);
-  stage_planes<T, D, LPG, 256>(pl, Lg, PLs, tid);
+  load_stats<T, D, LPG, SPW, NW>(G + sidx * D * r, r, f0, w, lane, st, &sm.SF[0][0], LDD);
+  stage_rt<T, D, LPG, 512>(RT + (size_t)head * D * pw + 32 * grp, pw, RTs, tid);
+  stage_planes<T, D, LPG, 512>(pl, Lg, PLs, tid);
   const T* PH = &PLs.p[0][0][0];
   const T* PLo = &PLs.p[PlanesLds<T, D, LPG>::NPART - 1][0][0];
   constexpr int LDP = PlanesLds<T, D, LPG>::LDP;
-  __syncthreads();  // hyperplanes staged before the first feature computation
-  for (int f = tid; f < RP; f += 256) sm.zr[f] = f0 + f < r ? gzs[sidx * r + f0 + f] : 0.0f;
+  for (int f = tid; f < RP; f += 512) sm.zr[f] = f0 + f < r ? gzs[sidx * r + f0 + f] : 0.0f;
+  __syncthreads();  // hyperplanes and statistics staged
 
-  // xr: the row this wave featurizes (K for role 0, Q for role 1); vx: V (role 0).
-  // One array for both roles keeps the two load paths from being merged into
-  // stores through a selected pointer (which would put the arrays in scratch).
-  typename M::frag xr[D / M::KSTEP], vx[D / M::KSTEP];
-  Vec8<T> ob[OIT];
-  float oe[OIT];
-  float ddv = 0.0f;
-  auto load_rows = [&](int s0) __attribute__((always_inline)) {
-    // Tokens outside the span read a stand-in row: their phi(Q) rows are stored
-    // as zero, their dnum rows and dd_lr are zeroed when staged, and no key
-    // result of theirs is written. Nothing is loaded before the span.
-    if (s0 < t_beg) return;
-    const size_t trow = (size_t)min(s0 + 32 * kt + col, N - 1) * D;
-    if (role < 2) prefetch_row_frags<T, D>((role == 0 ? Kh : Qh) + trow, xr, h);
-    if (role == 0) prefetch_row_frags<T, D>(Vh + trow, vx, h);
-    if (owave) {
+  // The walk, compiled per (role, half) so that each wave keeps only its own
+  // role's registers; every instantiation passes the same barriers.
+  auto walk = [&](auto rc, auto hc) __attribute__((always_inline)) {
+    constexpr int ROLE = decltype(rc)::value, HALF = decltype(hc)::value;
+    constexpr int JP0 = HALF * NJH;
+    constexpr bool FEAT_HALF = HALF == 0 || LPG / 2 > 1;  // this half owns tables
+    // Rows of one step. dK waves: K and V of their key tile. dV waves: Q of query
+    // tile kt (for phi(Q)) and a share of the dO rows with their dnum scale and
+    // dd_lr. Tokens outside the span read a stand-in row: their phi rows are
+    // stored as zero, their dnum rows and dd_lr are zeroed when staged, and no key
+    // result of theirs is written.
+    typename M::frag xr[D / M::KSTEP], vx[D / M::KSTEP];
+    Vec8<T> ob[ROLE == 1 ? OIT : 1];
+    float oe[ROLE == 1 ? OIT : 1];
+    float ddv = 0.0f;
+    auto load_rows = [&](int s0) __attribute__((always_inline)) {
+      if (s0 < t_beg) return;
+      const size_t trow = (size_t)min(s0 + 32 * kt + col, N - 1) * D;
+      prefetch_row_frags<T, D>((ROLE == 0 ? Kh : Qh) + trow, xr, h);
+      if constexpr (ROLE == 0) {
+        prefetch_row_frags<T, D>(Vh + trow, vx, h);
+      } else {
 #pragma unroll
-      for (int i = 0; i < OIT; ++i) {
-        const int it = 64 * ow + lane + 64 * NDW * i, t = it / VCH;
-        const int tc = min(s0 + t, N - 1);
-        if (it < STEP * VCH) ob[i].load(dOh + (size_t)tc * D + (it % VCH) * 8);
-        oe[i] = re[(size_t)bh * N + tc];
+        for (int i = 0; i < OIT; ++i) {
+          const int it = ts + 256 * i;
+          const int tc = min(s0 + it / VCH, N - 1);
+          if (it < STEP * VCH) ob[i].load(dOh + (size_t)tc * D + (it % VCH) * 8);
+          oe[i] = re[(size_t)bh * N + tc];
+        }
+        if (ts < STEP) ddv = rdd[(size_t)bh * N + min(s0 + ts, N - 1)];
       }
-      if (ow == 0) ddv = rdd[(size_t)bh * N + min(s0 + lane, N - 1)];
+    };
+    const int nstep = (t_end - t_beg + STEP - 1) / STEP;
+    load_rows(t_beg + (nstep - 1) * STEP);
+
+    for (int si = nstep - 1; si >= 0; --si) {
+      const int s0 = t_beg + si * STEP;
+      const int ktok = s0 + 32 * kt + col;
+      const bool kvalid = kwave && ktok < t_end;
+      // Staging. dK waves: phi(K) of this half's tables (kept for the backward and
+      // stored to KFs). dV waves: phi(Q) of this half's tables to FS, dnum rows to
+      // XS, dd_lr.
+      Feat Fk;
+      if constexpr (ROLE == 0) {
+        if (kwave && FEAT_HALF) {
+          Fk.compute(xr, PH, PLo, LDP, Lg, scale, tau, lane);
+#pragma unroll
+          for (int jp = JP0; jp < JP0 + NJH; ++jp) {
+            float x0[8], x1[8];
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+              x0[b] = kvalid ? Fk.phi[jp][b] : 0.0f;
+              x1[b] = kvalid ? Fk.phi[jp][8 + b] : 0.0f;
+            }
+            store8(&KFs[32 * kt + col][Feat::feat(jp, 0, h)], x0);
+            store8(&KFs[32 * kt + col][Feat::feat(jp, 8, h)], x1);
+          }
+        }
+      } else {
+        if (kwave && FEAT_HALF)
+          Feat::template compute_to_row<JP0, NJH>(xr, PH, PLo, LDP, Lg, scale, tau, lane, kvalid,
+                                                  &sm.FS[32 * kt + col][0]);
+#pragma unroll
+        for (int i = 0; i < OIT; ++i) {
+          const int it = ts + 256 * i;
+          if (it < STEP * VCH) {
+            ob[i].scale(s0 + it / VCH < t_end ? oe[i] : 0.0f);
+            ob[i].store(&sm.XS[it / VCH][(it % VCH) * 8]);
+          }
+        }
+        if (ts < STEP) sm.dd[ts] = s0 + ts < t_end ? ddv : 0.0f;
+      }
+      __syncthreads();
+
+      if constexpr (ROLE == 0) {
+        // dphi(K)^T for this half's feature tiles (rows = features, columns =
+        // keys) = G V^T + g 1^T + the part of the step's queries at or after each
+        // key; back through this half's tables; da to LDS.
+        if (kwave && NFH * HALF < NFT) {
+          floatx16 dkt[NFH];
+#pragma unroll
+          for (int i = 0; i < NFH; ++i) {
+            const int ft = HALF * NFH + i;
+            dkt[i] = zero16();
+#pragma unroll
+            for (int ks = 0; ks < D / M::KSTEP; ++ks)
+              dkt[i] = M::mma(row_frag<T>(&sm.SF[0][0], LDD, 32 * ft, 0, ks, lane), vx[ks], dkt[i]);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) dkt[i][v] += sm.zr[32 * ft + acc_row(v, h)];
+          }
+          if (causal) {
+            for (int qt = kt; qt < QT; ++qt) {
+              floatx16 gm = zero16();
+#pragma unroll
+              for (int ks = 0; ks < D / M::KSTEP; ++ks)
+                gm = M::mma(row_frag<T>(&sm.XS[0][0], LDD, 32 * qt, 0, ks, lane), vx[ks], gm);
+#pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                gm[v] += sm.dd[32 * qt + acc_row(v, h)];
+                if (qt == kt && acc_row(v, h) < col) gm[v] = 0.0f;
+              }
+#pragma unroll
+              for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
+                const typename M::frag gf = M::from_acc(gm, ks2);
+#pragma unroll
+                for (int i = 0; i < NFH; ++i)
+                  dkt[i] = M::mma(tr_frag<T>(&sm.FS[0][0], LDR, 32 * qt, 32 * (HALF * NFH + i), ks2,
+                                             lane, true),
+                                  gf, dkt[i]);
+              }
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < NFH; ++i) {
+            const int ft = HALF * NFH + i;
+            float dphi[16], da4[4];
+            tile_to_table(dkt[i], h, dphi);
+            Fk.backward_table(ft, dphi, da4);
+            *reinterpret_cast<floatx4*>(&DA.da[kt][h][col][4 * ft]) =
+                floatx4{da4[0], da4[1], da4[2], da4[3]};
+          }
+        }
+      } else if (kwave && (NDA > 1 || HALF == 0)) {
+        // dV^T for this half's channel tiles (rows = channels, columns = keys) =
+        // G^T phi(K)^T + the step's part.
+        floatx16 dvt[NDH];
+#pragma unroll
+        for (int i = 0; i < NDH; ++i) {
+          const int dt = HALF * NDH + i;
+          dvt[i] = zero16();
+#pragma unroll
+          for (int ks = 0; ks < RP / M::KSTEP; ++ks) {
+            const int fk = Feat::frag_feat(ks, 0, h);
+            dvt[i] = M::mma(tr_rows(&sm.SF[0][0], LDD, fk, fk + 4, 32 * dt, lane),
+                            M::load(&KFs[32 * kt + col][fk]), dvt[i]);
+          }
+        }
+        if (causal) {
+          for (int qt = kt; qt < QT; ++qt) {
+            floatx16 wq = zero16();
+#pragma unroll
+            for (int ks = 0; ks < RP / M::KSTEP; ++ks)
+              wq = M::mma(M::load(&sm.FS[32 * qt + col][Feat::frag_feat(ks, 0, h)]),
+                          M::load(&KFs[32 * kt + col][Feat::frag_feat(ks, 0, h)]), wq);
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              if (qt == kt && acc_row(v, h) < col) wq[v] = 0.0f;
+#pragma unroll
+            for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
+              const typename M::frag wf = M::from_acc(wq, ks2);
+#pragma unroll
+              for (int i = 0; i < NDH; ++i)
+                dvt[i] = M::mma(tr_frag<T>(&sm.XS[0][0], LDD, 32 * qt, 32 * (HALF * NDH + i), ks2,
+                                           lane, true),
+                                wf, dvt[i]);
+            }
+          }
+        }
+        if (kvalid)
+          write_grad_row<T, D, NDH>(dvt, scrV, dV, ((size_t)bh * N + ktok) * D, h, first != 0,
+                                    last != 0, HALF * NDH);
+      }
+      __syncthreads();  // da of every table in LDS
+
+      // dK for this half's channel tiles from every table's da.
+      if constexpr (ROLE == 0) {
+        if (kwave && (NDA > 1 || HALF == 0)) {
+          float da[LPG / 2][4];
+#pragma unroll
+          for (int jp = 0; jp < LPG / 2; ++jp) {
+            const floatx4 x = *reinterpret_cast<const floatx4*>(&DA.da[kt][h][col][4 * jp]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) da[jp][t] = x[t];
+          }
+          floatx16 dx[NDH];
+          features_dx<T, D, LPG, T, NDH>(da, RTs, rt_lds_width<LPG>(), c2, lane, dx, HALF * NDH);
+          if (kvalid)
+            write_grad_row<T, D, NDH>(dx, scrK, dK, ((size_t)bh * N + ktok) * D, h, first != 0,
+                                      last != 0, HALF * NDH);
+        }
+      }
+      if (!causal) break;
+      advance_stats<T, D, LPG, SPW, STEP, true, NW>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, sm.dd, w,
+                                                    lane, st, &sm.SF[0][0], sm.zr);
+      load_rows(s0 - STEP);  // before the span: loads nothing
+      __syncthreads();
     }
   };
-  const int nstep = (t_end - t_beg + STEP - 1) / STEP;
-  load_rows(t_beg + (nstep - 1) * STEP);
-
-  for (int si = nstep - 1; si >= 0; --si) {
-    const int s0 = t_beg + si * STEP;
-    const int ktok = s0 + 32 * kt + col;
-    const bool kvalid = ktok < t_end;
-    if (role == 1)
-      Feat::compute_to_row(xr, PH, PLo, LDP, Lg, scale, tau, lane, kvalid, &sm.FS[32 * kt + col][0]);
-    if (owave) {
-#pragma unroll
-      for (int i = 0; i < OIT; ++i) {
-        const int it = 64 * ow + lane + 64 * NDW * i;
-        if (it < STEP * VCH) {
-          ob[i].scale(s0 + it / VCH < t_end ? oe[i] : 0.0f);
-          ob[i].store(&sm.XS[it / VCH][(it % VCH) * 8]);
-        }
-      }
-      if (ow == 0 && lane < STEP) sm.dd[lane] = s0 + lane < t_end ? ddv : 0.0f;
-    }
-    Feat Fk;
-    if (role == 0) {
-      Fk.compute(xr, PH, PLo, LDP, Lg, scale, tau, lane);
-#pragma unroll
-      for (int jp = 0; jp < LPG / 2; ++jp) {
-        float x0[8], x1[8];
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          x0[b] = kvalid ? Fk.phi[jp][b] : 0.0f;
-          x1[b] = kvalid ? Fk.phi[jp][8 + b] : 0.0f;
-        }
-        store8(&KFs[32 * kt + col][Feat::feat(jp, 0, h)], x0);
-        store8(&KFs[32 * kt + col][Feat::feat(jp, 8, h)], x1);
-      }
-    }
-    __syncthreads();
-
-    if (role == 0) {
-      // dphi(K)^T (rows = features, columns = keys) = G V^T + g 1^T + the part of
-      // the step's queries at or after each key.
-      floatx16 dkt[NFT];
-#pragma unroll
-      for (int ft = 0; ft < NFT; ++ft) {
-        dkt[ft] = zero16();
-#pragma unroll
-        for (int ks = 0; ks < D / M::KSTEP; ++ks)
-          dkt[ft] = M::mma(row_frag<T>(&sm.SF[0][0], LDD, 32 * ft, 0, ks, lane), vx[ks], dkt[ft]);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) dkt[ft][v] += sm.zr[32 * ft + acc_row(v, h)];
-      }
-      if (causal) {
-        for (int qt = kt; qt < QT; ++qt) {
-          floatx16 gm = zero16();
-#pragma unroll
-          for (int ks = 0; ks < D / M::KSTEP; ++ks)
-            gm = M::mma(row_frag<T>(&sm.XS[0][0], LDD, 32 * qt, 0, ks, lane), vx[ks], gm);
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            gm[v] += sm.dd[32 * qt + acc_row(v, h)];
-            if (qt == kt && acc_row(v, h) < col) gm[v] = 0.0f;
-          }
-#pragma unroll
-          for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
-            const typename M::frag gf = M::from_acc(gm, ks2);
-#pragma unroll
-            for (int ft = 0; ft < NFT; ++ft)
-              dkt[ft] = M::mma(tr_frag<T>(&sm.FS[0][0], LDR, 32 * qt, 32 * ft, ks2, lane, true), gf, dkt[ft]);
-          }
-        }
-      }
-      float da[LPG / 2][4];
-#pragma unroll
-      for (int ft = 0; ft < NFT; ++ft) {
-        float dphi[16];
-        tile_to_table(dkt[ft], h, dphi);
-        Fk.backward_table(ft, dphi, da[ft]);
-      }
-      floatx16 dx[D / 32];
-      features_dx<T, D, LPG>(da, RTs, rt_lds_width<LPG>(), c2, lane, dx);
-      if (kvalid)
-        write_grad_row<T, D>(dx, scrK, dK, ((size_t)bh * N + ktok) * D, h, first != 0,
-                             last != 0);
-    } else if (role == 1) {
-      // dV^T (rows = channels, columns = keys) = G^T phi(K)^T + the step's part.
-      floatx16 dvt[D / 32];
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        dvt[dt] = zero16();
-#pragma unroll
-        for (int ks = 0; ks < RP / M::KSTEP; ++ks) {
-          const int fk = Feat::frag_feat(ks, 0, h);
-          dvt[dt] = M::mma(tr_rows(&sm.SF[0][0], LDD, fk, fk + 4, 32 * dt, lane),
-                           M::load(&KFs[32 * kt + col][fk]), dvt[dt]);
-        }
-      }
-      if (causal) {
-        for (int qt = kt; qt < QT; ++qt) {
-          floatx16 wq = zero16();
-#pragma unroll
-          for (int ks = 0; ks < RP / M::KSTEP; ++ks)
-            wq = M::mma(M::load(&sm.FS[32 * qt + col][Feat::frag_feat(ks, 0, h)]),
-                        M::load(&KFs[32 * kt + col][Feat::frag_feat(ks, 0, h)]), wq);
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (qt == kt && acc_row(v, h) < col) wq[v] = 0.0f;
-#pragma unroll
-          for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
-            const typename M::frag wf = M::from_acc(wq, ks2);
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-              dvt[dt] = M::mma(tr_frag<T>(&sm.XS[0][0], LDD, 32 * qt, 32 * dt, ks2, lane, true), wf, dvt[dt]);
-          }
-        }
-      }
-      if (kvalid)
-        write_grad_row<T, D>(dvt, scrV, dV, ((size_t)bh * N + ktok) * D, h, first != 0,
-                             last != 0);
-    }
-    load_rows(s0 - STEP);  // before the span: loads nothing
-    if (!causal) break;
-    __syncthreads();
-    advance_stats<T, D, LPG, SPW, STEP>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, sm.dd, w, lane, st,
-                                        &sm.SF[0][0], sm.zr);
-    __syncthreads();
+  if (role == 0) {
+    if (half == 0) walk(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    else walk(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+  } else {
+    if (half == 0) walk(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+    else walk(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
   }
 }
 
@@ -1149,10 +1205,12 @@ size_t bwd_lds_need(const Problem& pb) {
         constexpr int LPG = ELSAA_C(lc);
         constexpr size_t RTB = sizeof(T) * D * rt_lds_width<LPG>() + sizeof(PlanesLds<T, D, LPG>);
         constexpr int SQ = walk_step<T, D, LPG, 128, RTB + sizeof(QdaLds<LPG>)>();
-        constexpr int SK = walk_step<T, D, LPG, 64, RTB + sizeof(T) * 64 * tile_ld<T>(16 * LPG)>();
+        constexpr int SK = walk_step<T, D, LPG, 64,
+                                     RTB + sizeof(KdaLds<LPG>) + sizeof(T) * 64 * tile_ld<T>(16 * LPG)>();
         const size_t a = RTB + sizeof(QdaLds<LPG>) +
                          (SQ > 0 ? sizeof(WalkSmem<T, D, LPG, SQ>) : sizeof(WalkSmem<T, D, LPG, 32>));
-        const size_t b = RTB + (SK > 0 ? sizeof(WalkSmem<T, D, LPG, SK>) : sizeof(WalkSmem<T, D, LPG, 32>)) +
+        const size_t b = RTB + sizeof(KdaLds<LPG>) +
+                         (SK > 0 ? sizeof(WalkSmem<T, D, LPG, SK>) : sizeof(WalkSmem<T, D, LPG, 32>)) +
                          sizeof(T) * (SK > 0 ? SK : 32) * tile_ld<T>(16 * LPG);
         lr = a > b ? a : b;
       };
@@ -1252,7 +1310,8 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
         constexpr int LPG = ELSAA_C(lc);
         constexpr size_t RTB = sizeof(T) * D * rt_lds_width<LPG>() + sizeof(PlanesLds<T, D, LPG>);
         constexpr int SQ = walk_step<T, D, LPG, 128, RTB + sizeof(QdaLds<LPG>)>();
-        constexpr int SK = walk_step<T, D, LPG, 64, RTB + sizeof(T) * 64 * tile_ld<T>(16 * LPG)>();
+        constexpr int SK = walk_step<T, D, LPG, 64,
+                                     RTB + sizeof(KdaLds<LPG>) + sizeof(T) * 64 * tile_ld<T>(16 * LPG)>();
         if constexpr (SQ > 0 && SK > 0) {
           const int span_q = pb.causal ? pb.chunk : SQ;
           const int span_k = pb.causal ? pb.chunk : SK;
@@ -1264,7 +1323,7 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
                          (const T*)dQp, scrQ, (T*)dQ, RT, pw, pb.H, pb.N, pb.L, span_q,
                          pb.levels, (int)pb.causal, pb.scale, pb.tau, g, first, last);
             ELSAA_LAUNCH("lr_bwd_k", (lr_bwd_k_kernel<T, D, LPG, SK>),
-                         dim3((pb.N + span_k - 1) / span_k, BH), dim3(256), 0, st, (const T*)Q,
+                         dim3((pb.N + span_k - 1) / span_k, BH), dim3(512), 0, st, (const T*)Q,
                          (const T*)K, (const T*)V, (const T*)dO, planes_lr, Gs, gzs, re, rdd,
                          (const T*)dKp, (const T*)dVp, scrK, scrV, (T*)dK, (T*)dV, RT, pw, pb.H,
                          pb.N, pb.L, span_k, pb.levels, (int)pb.causal, pb.scale, pb.tau, g,

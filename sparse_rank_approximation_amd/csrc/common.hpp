@@ -542,6 +542,7 @@ struct Features {
   // phi of every table for this lane's token (zero when !valid) stored straight
   // into the LDS row dst (features 16 table + b), one table pair at a time so that
   // only 16 feature values are live at once.
+  template <int JP0 = 0, int NJ = NJP>
   static __device__ __forceinline__ void compute_to_row(
       const typename MF<T>::frag (&xf)[D / MF<T>::KSTEP], const T* PH, const T* PL, int ldp, int L,
       float scale, float tau, int lane, bool valid, T* dst) {
@@ -563,7 +564,7 @@ struct Features {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int jp = 4 * mt + g;
-        if (jp >= NJP) continue;
+        if (jp >= NJP || jp < JP0 || jp >= JP0 + NJ) continue;
         const bool live = valid && 2 * jp + h < L;
         float p[4], q[4];
 #pragma unroll
