@@ -170,7 +170,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
 // step's keys (V in XS, phi(K) in FS, row-major) and the running RACE statistics
 // S = sum_j phi(K_j) V_j^T as an MFMA operand (SF, [feature][channel]).
 template <typename T, int D, int LP, int STEP>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
     fwd_epilogue_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                         const float* __restrict__ planes, const float* __restrict__ A,
                         const float* __restrict__ z, const T* __restrict__ Os,
@@ -182,22 +182,21 @@ __global__ void __launch_bounds__(256)
   typedef MF<T> M;
   typedef Features<T, D, LP> Feat;
   typedef WalkSmem<T, D, LP, STEP> Sm;
-  constexpr int RP = 16 * LP, LDD = Sm::LDD, LDR = Sm::LDR;
+  constexpr int NW = 8, RP = 16 * LP, LDD = Sm::LDD, LDR = Sm::LDR;
   constexpr int QT = STEP / 32;                         // query (and key) tiles per step
-  constexpr int WPT = 4 / QT;                           // waves per query tile
-  constexpr int NDA = D / 32;                           // channel tiles
-  constexpr int NDT = NDA / WPT > 0 ? NDA / WPT : 1;    // channel tiles per wave
-  constexpr int NFT = RP / 32, NST = NDA * NFT, SPW = (NST + 3) / 4;
-  constexpr int VCH = D / 8, VIT = (STEP * VCH + 255) / 256;
+  constexpr int NDA = D / 32, NDH = NDA > 1 ? NDA / 2 : 1;  // channel tiles per half
+  constexpr int NJP = LP / 2, NJH = NJP > 1 ? NJP / 2 : 1;   // table pairs per half
+  constexpr int NFT = RP / 32, NST = NDA * NFT, SPW = (NST + NW - 1) / NW;
+  constexpr int VCH = D / 8, VIT = (STEP * VCH + 511) / 512;
   __shared__ Sm sm;
   __shared__ PlanesLds<T, D, LP> PLs;
 
   const int bh = blockIdx.y, c = blockIdx.x, head = bh % H;
   const int r = 16 * L;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
-  const int w = wave_id();  // wave index, uniform (scalar) so that role branches stay uniform
-  const int qt = w % QT, dt0 = (w / QT) * NDT;
-  const bool owner = dt0 < NDA;  // waves past the channel tiles only stage
+  const int w = tid >> 6;
+  const int qt = w & 3, half = w >> 2;
+  const bool qwave = qt < QT;
   const float* pl = planes + (size_t)head * L * 4 * D;
   const int t_beg = c * span, t_end = min(N, t_beg + span);
   const float lam = lambda[head];
@@ -211,140 +210,149 @@ __global__ void __launch_bounds__(256)
   const float* Ac = A + sidx * D * r;
   const float* zc = z + sidx * r;
   floatx16 st[SPW];
-  load_stats<T, D, LP, SPW>(Ac, r, 0, w, lane, st, &sm.SF[0][0], LDD);
-  stage_planes<T, D, LP, 256>(pl, L, PLs, tid);
+  load_stats<T, D, LP, SPW, NW>(Ac, r, 0, w, lane, st, &sm.SF[0][0], LDD);
+  stage_planes<T, D, LP, 512>(pl, L, PLs, tid);
   const T* PH = &PLs.p[0][0][0];
   const T* PLo = &PLs.p[PlanesLds<T, D, LP>::NPART - 1][0][0];
   constexpr int LDP = PlanesLds<T, D, LP>::LDP;
-  __syncthreads();  // hyperplanes staged before the first feature computation
-  for (int f = tid; f < RP; f += 256) sm.zr[f] = f < r ? zc[f] : 0.0f;
+  for (int f = tid; f < RP; f += 512) sm.zr[f] = f < r ? zc[f] : 0.0f;
+  __syncthreads();  // hyperplanes and statistics staged
 
-  // Global rows of one step, loaded one step ahead: this wave's query tile, the
-  // key tile it featurizes (waves < QT) and its share of the V rows.
-  typename M::frag qx[D / M::KSTEP], kx[D / M::KSTEP];
-  Vec8<T> vb[VIT];
-  auto load_rows = [&](int s0) __attribute__((always_inline)) {
-    const int qtok = s0 + 32 * qt + col;
-    // Tokens past the span read a stand-in row: their phi(Q) rows are not
-    // written out and their phi(K) rows are stored as zero, which also cancels
-    // their V rows in every product.
-    prefetch_row_frags<T, D>(Qh + (size_t)min(qtok, N - 1) * D, qx, h);
-    if (causal) {
-      const int ktok = s0 + 32 * w + col;
-      if (w < QT) prefetch_row_frags<T, D>(Kh + (size_t)min(ktok, N - 1) * D, kx, h);
+  // The walk, compiled per half (half 0: channel tiles 0 .. NDH-1 and the first
+  // half of the tables of phi(K); half 1: the rest), so that each wave keeps only
+  // its own registers; both halves pass the same barriers.
+  auto walk = [&](auto hc) __attribute__((always_inline)) {
+    constexpr int HALF = decltype(hc)::value;
+    constexpr int JP0 = HALF * NJH, DT0 = HALF * NDH;
+    constexpr bool FEAT_HALF = HALF == 0 || NJP > 1;
+    constexpr bool OWNER = HALF == 0 || NDA > 1;
+    // Rows of one step, loaded one step ahead: the wave's query tile, its key
+    // tile (for its half of phi(K)) and a share of the V rows. Tokens past the
+    // span read a stand-in row: their outputs are not written and their phi(K)
+    // rows are stored as zero, which also cancels their V rows in every product.
+    typename M::frag qx[D / M::KSTEP], kx[D / M::KSTEP];
+    Vec8<T> vb[VIT];
+    auto load_rows = [&](int s0) __attribute__((always_inline)) {
+      const size_t trow = (size_t)min(s0 + 32 * qt + col, N - 1) * D;
+      prefetch_row_frags<T, D>(Qh + trow, qx, h);
+      if (causal) {
+        if (FEAT_HALF) prefetch_row_frags<T, D>(Kh + trow, kx, h);
 #pragma unroll
-      for (int i = 0; i < VIT; ++i) {
-        const int it = tid + 256 * i, t = it / VCH, tok = s0 + t;
-        if (it < STEP * VCH) vb[i].load(Vh + (size_t)min(tok, N - 1) * D + (it % VCH) * 8);
+        for (int i = 0; i < VIT; ++i) {
+          const int it = tid + 512 * i, tok = s0 + it / VCH;
+          if (it < STEP * VCH) vb[i].load(Vh + (size_t)min(tok, N - 1) * D + (it % VCH) * 8);
+        }
       }
+    };
+    load_rows(t_beg);
+
+    for (int s0 = t_beg; s0 < t_end; s0 += STEP) {
+      const int qtok = s0 + 32 * qt + col;
+      const bool qvalid = qwave && qtok < t_end;
+      // Stage the step's keys: this half's phi(K) tables and V into LDS (causal).
+      if (causal) {
+        if (qwave && FEAT_HALF)
+          Feat::template compute_to_row<JP0, NJH>(kx, PH, PLo, LDP, L, scale, tau, lane, qvalid,
+                                                  &sm.FS[32 * qt + col][0]);
+#pragma unroll
+        for (int i = 0; i < VIT; ++i) {
+          const int it = tid + 512 * i;
+          if (it < STEP * VCH) vb[i].store(&sm.XS[it / VCH][(it % VCH) * 8]);
+        }
+      }
+      Feat Fq;
+      if (qwave && OWNER) Fq.compute(qx, PH, PLo, LDP, L, scale, tau, lane);
+      __syncthreads();
+
+      if (qwave && OWNER) {
+        // The query's merged sparse output and log-sum-exp (loads in flight during
+        // the readout).
+        const size_t k = (size_t)bh * N + min(qtok, N - 1);
+        DRow<T, NDH> osr;
+        osr.load(Os + k * D, h, DT0);
+        const float lse = lse_s[k];
+
+        // Low-rank readout: num^T = S^T phi(Q)^T over this half's channel tiles,
+        // den = phi(Q) . z; then the causally masked part of the step.
+        floatx16 num[NDH];
+#pragma unroll
+        for (int i = 0; i < NDH; ++i) num[i] = zero16();
+        float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int jp = 0; jp < NJP; ++jp)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const floatx4 zz = *reinterpret_cast<const floatx4*>(&sm.zr[Feat::feat(jp, 4 * q4, h)]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d4[e] += Fq.phi[jp][4 * q4 + e] * zz[e];
+          }
+        float den = (d4[0] + d4[1]) + (d4[2] + d4[3]);
+        den = sum_halves(den);
+#pragma unroll
+        for (int ks = 0; ks < RP / M::KSTEP; ++ks) {
+          const typename M::frag fb = Fq.frag(ks);
+          const int f0 = Feat::frag_feat(ks, 0, h);
+#pragma unroll
+          for (int i = 0; i < NDH; ++i)
+            num[i] = M::mma(tr_rows(&sm.SF[0][0], LDD, f0, f0 + 4, 32 * (DT0 + i), lane), fb, num[i]);
+        }
+        if (causal) {
+          float dintra = 0.0f;
+          for (int kt = 0; kt <= qt; ++kt) {
+            floatx16 wt = zero16();
+#pragma unroll
+            for (int ks = 0; ks < RP / M::KSTEP; ++ks)
+              wt = M::mma(M::load(&sm.FS[32 * kt + col][Feat::frag_feat(ks, 0, h)]), Fq.frag(ks), wt);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              if (kt == qt && acc_row(v, h) > col) wt[v] = 0.0f;
+              dintra += wt[v];
+            }
+#pragma unroll
+            for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
+              const typename M::frag wf = M::from_acc(wt, ks2);
+#pragma unroll
+              for (int i = 0; i < NDH; ++i)
+                num[i] = M::mma(tr_frag<T>(&sm.XS[0][0], LDD, 32 * kt, 32 * (DT0 + i), ks2, lane, true), wf,
+                                num[i]);
+            }
+          }
+          den += sum_halves(dintra);
+        }
+
+        if (qvalid) {
+          const float m = 1.0f / (1.0f + fast_exp(__logf(lam * den + eps) - lse));
+          const float g1 = gs ? gs[k] : 1.0f;
+          const float g2 = glr ? glr[k] : 1.0f;
+          const float dinv = 1.0f / den;
+#pragma unroll
+          for (int i = 0; i < NDH; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const size_t o = k * D + 32 * (DT0 + i) + 8 * g + 4 * h;
+              float xo[4], xl[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                xl[e] = num[i][4 * g + e] * dinv;
+                xo[e] = g1 * m * osr.x[i][g][e] + g2 * xl[e];
+              }
+              store4(O + o, xo);
+              store4(Olr + o, xl);
+            }
+          if (HALF == 0 && h == 0) dlr_out[k] = den;
+        }
+      }
+      if (!causal) break;
+      __syncthreads();
+      // Advance the statistics by the step's keys: S^T += V^T phi(K), z += sum phi(K).
+      advance_stats<T, D, LP, SPW, STEP, true, NW>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, nullptr, w,
+                                                   lane, st, &sm.SF[0][0], sm.zr);
+      load_rows(s0 + STEP);  // past the span: loads nothing that matters
+      __syncthreads();
     }
   };
-  load_rows(t_beg);
-
-  for (int s0 = t_beg; s0 < t_end; s0 += STEP) {
-    // Stage the step's keys: phi(K) and V into LDS (causal only).
-    if (causal) {
-      if (w < QT)
-        Feat::compute_to_row(kx, PH, PLo, LDP, L, scale, tau, lane, s0 + 32 * w + col < t_end,
-                             &sm.FS[32 * w + col][0]);
-#pragma unroll
-      for (int i = 0; i < VIT; ++i) {
-        const int it = tid + 256 * i;
-        if (it < STEP * VCH) vb[i].store(&sm.XS[it / VCH][(it % VCH) * 8]);
-      }
-    }
-    const int qtok = s0 + 32 * qt + col;
-    const bool qvalid = qtok < t_end;
-    Feat Fq;
-    Fq.compute(qx, PH, PLo, LDP, L, scale, tau, lane);
-    __syncthreads();
-
-    if (owner) {
-      // The query's merged sparse output and log-sum-exp (loads in flight during
-      // the readout).
-      const size_t k = (size_t)bh * N + min(qtok, N - 1);
-      DRow<T, NDT> osr;
-      osr.load(Os + k * D, h, dt0);
-      const float lse = lse_s[k];
-
-      // Low-rank branch readout: num^T = S^T phi(Q)^T over the channel tiles of
-      // this wave, den = phi(Q) . z; then the causally masked part of the step.
-      floatx16 num[NDT];
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) num[dt] = zero16();
-      float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int jp = 0; jp < LP / 2; ++jp)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const floatx4 zz = *reinterpret_cast<const floatx4*>(&sm.zr[Feat::feat(jp, 4 * q4, h)]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) d4[e] += Fq.phi[jp][4 * q4 + e] * zz[e];
-        }
-      float den = (d4[0] + d4[1]) + (d4[2] + d4[3]);
-      den = sum_halves(den);
-#pragma unroll
-      for (int ks = 0; ks < RP / M::KSTEP; ++ks) {
-        const typename M::frag fb = Fq.frag(ks);
-        const int f0 = Feat::frag_feat(ks, 0, h);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          num[dt] = M::mma(tr_rows(&sm.SF[0][0], LDD, f0, f0 + 4, 32 * (dt0 + dt), lane), fb, num[dt]);
-      }
-      if (causal) {
-        float dintra = 0.0f;
-        for (int kt = 0; kt <= qt; ++kt) {
-          floatx16 wt = zero16();
-#pragma unroll
-          for (int ks = 0; ks < RP / M::KSTEP; ++ks)
-            wt = M::mma(M::load(&sm.FS[32 * kt + col][Feat::frag_feat(ks, 0, h)]), Fq.frag(ks), wt);
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            if (kt == qt && acc_row(v, h) > col) wt[v] = 0.0f;
-            dintra += wt[v];
-          }
-#pragma unroll
-          for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
-            const typename M::frag wf = M::from_acc(wt, ks2);
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-              num[dt] = M::mma(tr_frag<T>(&sm.XS[0][0], LDD, 32 * kt, 32 * (dt0 + dt), ks2, lane, true), wf, num[dt]);
-          }
-        }
-        den += sum_halves(dintra);
-      }
-
-      if (qvalid) {
-        const float m = 1.0f / (1.0f + fast_exp(__logf(lam * den + eps) - lse));
-        const float g1 = gs ? gs[k] : 1.0f;
-        const float g2 = glr ? glr[k] : 1.0f;
-        const float dinv = 1.0f / den;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const size_t o = k * D + 32 * (dt0 + dt) + 8 * g + 4 * h;
-            float xo[4], xl[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              xl[e] = num[dt][4 * g + e] * dinv;
-              xo[e] = g1 * m * osr.x[dt][g][e] + g2 * xl[e];
-            }
-            store4(O + o, xo);
-            store4(Olr + o, xl);
-          }
-        if (h == 0 && dt0 == 0) dlr_out[k] = den;
-      }
-    }
-    load_rows(s0 + STEP);  // past the span: loads nothing
-    if (!causal) break;
-    __syncthreads();
-
-    // Advance the statistics by the step's keys: S^T += V^T phi(K), z += sum phi(K).
-    advance_stats<T, D, LP, SPW, STEP>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, nullptr, w, lane, st,
-                                       &sm.SF[0][0], sm.zr);
-    __syncthreads();
-  }
+  if (half == 0) walk(std::integral_constant<int, 0>{});
+  else walk(std::integral_constant<int, 1>{});
 }
 
 size_t fwd_ws_bytes(const Problem& pb) {
@@ -408,7 +416,7 @@ void launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
           const int span = pb.causal ? pb.chunk : STEP;
           const int nspan = (pb.N + span - 1) / span;
           ELSAA_LAUNCH("fwd_epilogue", (fwd_epilogue_kernel<T, D, LP, STEP>), dim3(nspan, BH),
-                       dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V, planes_lr, A, z,
+                       dim3(512), 0, st, (const T*)Q, (const T*)K, (const T*)V, planes_lr, A, z,
                        (const T*)O_s, lse, lambda, g_s, g_lr, (T*)O, (T*)O_lr, d_lr, pb.H, pb.N,
                        pb.L, span, (int)pb.causal, pb.scale, pb.tau, pb.eps);
         }
