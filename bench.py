@@ -13,7 +13,6 @@ cores on a bounded sample of heads.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -77,12 +76,8 @@ def roofline(name, launches, total_ms, w, traffic_file):
 
 
 def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "sparse_rank_approximation_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
-    return h.hexdigest()[:16]
+    from sparse_rank_approximation_amd.traffic import source_hash
+    return source_hash()
 
 
 def traffic_bytes(name, path):

@@ -1,0 +1,114 @@
+"""Memory traffic per kernel from rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE).
+
+Two roles, one per step of the measurement:
+
+    python -m sparse_rank_approximation_amd.traffic copy
+        A plain device copy of COPY_BYTES (torch's copy kernel), the calibration
+        workload: run it under `rocprofv3 --pmc FETCH_SIZE` and again under
+        `--pmc WRITE_SIZE`. It reads and writes exactly COPY_BYTES, so the ratio
+        COPY_BYTES / counter converts the counters to bytes.
+
+    python -m sparse_rank_approximation_amd.traffic summarize OUT.json \\
+        FETCH_BENCH.csv WRITE_BENCH.csv FETCH_COPY.csv WRITE_COPY.csv
+        Reads the counter_collection CSVs of the four runs (the bench.py runs and
+        the copy runs) and writes OUT.json: per kernel, the average FETCH_SIZE and
+        WRITE_SIZE per dispatch, the calibration factors and the calibrated bytes
+        per launch, tagged with the hash of the kernel sources they were taken
+        from (bench.py uses the figures only while the sources are unchanged).
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import hashlib
+import json
+import os
+import sys
+
+COPY_BYTES = 1 << 30  # 1 GiB read + 1 GiB written: well past the last-level cache
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(PKG, "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str):
+    """The library's launch name of a kernel symbol; None for kernels of other libraries."""
+    if "elsaa" not in name:
+        return None
+    if "combine_kernel" in name:
+        return "combine_q" if "ELb1" in name else "combine_kv"
+    for k in ("sparse_bwd", "sparse_fwd", "lr_bwd_k", "lr_bwd_q", "fwd_epilogue", "lr_sums",
+              "lr_scan", "hash_kernel", "sort_kernel", "merge_kernel", "bwd_rows", "dlam_reduce",
+              "planes_transpose", "planes_f64"):
+        if k in name:
+            return k.replace("_kernel", "").replace("planes_transpose", "planes_t")
+    return name.split("(")[0][-48:]
+
+
+def per_dispatch(path: str) -> dict:
+    """{kernel: (dispatches, mean counter value per dispatch in KiB)}."""
+    tot = collections.defaultdict(float)
+    disp = collections.defaultdict(set)
+    for r in csv.DictReader(open(path)):
+        k = short_name(r["Kernel_Name"])
+        if k is None:
+            continue
+        tot[k] += float(r["Counter_Value"])
+        disp[k].add(r["Dispatch_Id"])
+    return {k: (len(disp[k]), tot[k] / len(disp[k])) for k in tot}
+
+
+def copy_kib(path: str) -> float:
+    """Counter value (KiB) of the largest dispatch of the calibration run."""
+    best = 0.0
+    vals = collections.defaultdict(float)
+    for r in csv.DictReader(open(path)):
+        vals[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    for v in vals.values():
+        best = max(best, v)
+    return best
+
+
+def run_copy() -> None:
+    import torch
+    n = COPY_BYTES // 2
+    src = torch.randn(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {COPY_BYTES} bytes", flush=True)
+
+
+def summarize(out, fb, wb, fc, wc) -> None:
+    f_bench, w_bench = per_dispatch(fb), per_dispatch(wb)
+    kf = COPY_BYTES / (copy_kib(fc) * 1024.0)
+    kw = COPY_BYTES / (copy_kib(wc) * 1024.0)
+    kernels = {}
+    for k in sorted(set(f_bench) | set(w_bench)):
+        fk = f_bench.get(k, (0, 0.0))[1]
+        wk = w_bench.get(k, (0, 0.0))[1]
+        kernels[k] = {"fetch_kib_per_launch": round(fk, 1), "write_kib_per_launch": round(wk, 1),
+                      "hbm_bytes_per_launch": round(fk * 1024.0 * kf + wk * 1024.0 * kw)}
+    rec = {"source_hash": source_hash(), "copy_bytes": COPY_BYTES,
+           "fetch_factor": round(kf, 4), "write_factor": round(kw, 4), "kernels": kernels}
+    json.dump(rec, open(out, "w"), indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+if __name__ == "__main__":
+    if len(sys.argv) >= 2 and sys.argv[1] == "copy":
+        run_copy()
+    elif len(sys.argv) == 7 and sys.argv[1] == "summarize":
+        summarize(*sys.argv[2:])
+    else:
+        print(__doc__)
+        sys.exit(2)
