@@ -28,7 +28,7 @@ class ElsaaConfig:
     hash_bits: int | None = None  # default log2(N / block), at least 1
     lr_tables: int = 8        # RACE tables L (r = 16 L features)
     lr_bits: int = 4
-    chunk: int = 512          # causal RACE summary spacing
+    chunk: int = 2048         # causal RACE summary spacing (rounding only; larger is faster)
     tau: float = 1.0
     eps: float = 1e-6
     scale: float | None = None
@@ -240,7 +240,7 @@ def make_planes(cfg: ElsaaConfig, seed: int = 0, device="cuda"):
 
 
 def elsaa_attention(q, k, v, *, causal: bool, block: int, lr_tables: int, lam=None, g_s=None,
-                    g_lr=None, planes_s=None, planes_lr=None, seed: int = 0, chunk: int = 512,
+                    g_lr=None, planes_s=None, planes_lr=None, seed: int = 0, chunk: int = 2048,
                     hash_bits: int | None = None, tau: float = 1.0, eps: float = 1e-6):
     """ELSAA attention of q, k, v [B, H, N, d] (fp32 or bf16 device tensors)."""
     B, H, N, d = q.shape
