@@ -469,20 +469,23 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
     return causal ? (it < nlev ? it / per_level : -1) : -1;
   };
   auto leaf_of = [&](int g) __attribute__((always_inline)) { return causal && (g % items) >= nlev; };
-  // Token of row t (< KT) of block g, -1 past the block.
-  auto rows_of = [&](int g, int t, int& qi, int& kj) __attribute__((always_inline)) {
+  // Rows of block g: row t's query and key tokens are (a, b) when alt < -1, else
+  // both are alt (a causal leaf: the token itself; -1 past the block). The order
+  // entries are read on every path (a leaf or a row past the block reads the
+  // head's first entry and discards it), so that the prefetches are issued in the
+  // same number on every path and the waits for them are exact; the choice is
+  // made only where the rows are used, so that nothing waits for the loads early.
+  struct Rows {
+    int a, b, alt;
+  };
+  auto rows_of = [&](int g, int t) __attribute__((always_inline)) {
     const int bh = g / items, it = g % items;
-    if (t >= SB) {
-      qi = kj = -1;
-    } else if (causal && it >= nlev) {
-      qi = kj = (it - nlev) * SB + t;
-    } else {
-      const size_t off = (size_t)bh * P + (causal ? (size_t)(it / per_level) * (N / 2) +
-                                                        (size_t)(it % per_level) * SB
-                                                  : (size_t)it * SB) + t;
-      qi = qperm[off];
-      kj = kperm[off];
-    }
+    const bool lf = causal && it >= nlev, past = t >= SB;
+    const size_t off = (size_t)bh * P + (lf || past ? (size_t)0
+                                         : causal ? (size_t)(it / per_level) * (N / 2) +
+                                                        (size_t)(it % per_level) * SB + t
+                                                  : (size_t)it * SB + t);
+    return Rows{qperm[off], kperm[off], past ? -1 : lf ? (it - nlev) * SB + t : -2};
   };
 
   // Registers holding the next block.
@@ -490,7 +493,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
   typename M::frag pv[KS];
   float plse = 0.0f, pD = 0.0f, pc = 0.0f;
   bool pvalid = false;
-  int pqi = -1, pki = -1;
+  Rows prow{-1, -1, -1};
   auto gather = [&](int g) __attribute__((always_inline)) {
     const size_t rb = (size_t)head_of(g) * N;
 #pragma unroll
@@ -503,10 +506,8 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
       po[i].load(dO + (rb + max(qi, 0)) * D + c8);
       pk[i].load(K + (rb + max(kj, 0)) * D + c8);
     }
-    const int kv = sm.knext[32 * w + col];
-    prefetch_row_frags<T, D>(V + (rb + max(kv, 0)) * D, pv, h);
-    if (tid < KT) {
-      const int qi = sm.qnext[tid];
+    {  // row terms of query row tid % KT (used by threads tid < KT)
+      const int qi = sm.qnext[tid % KT];
       const size_t k = rb + max(qi, 0);
       pvalid = qi >= 0;
       plse = lse[k];
@@ -515,12 +516,25 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
     }
   };
 
+  // V rows of the next block's keys of this wave, as MFMA operands (issued once
+  // the current block no longer needs the registers).
+  auto gather_v = [&](int g) __attribute__((always_inline)) {
+    const int kv = sm.knext[32 * w + col];
+    prefetch_row_frags<T, D>(V + ((size_t)head_of(g) * N + max(kv, 0)) * D, pv, h);
+  };
+
   int g = blockIdx.x;
   if (g >= total) return;
-  if (tid < KT) rows_of(g, tid, sm.qnext[tid], sm.knext[tid]);
+  if (tid < KT) {
+    const Rows r0 = rows_of(g, tid);
+    sm.qnext[tid] = r0.alt < -1 ? r0.a : r0.alt;
+    sm.knext[tid] = r0.alt < -1 ? r0.b : r0.alt;
+  }
   __syncthreads();
   gather(g);
-  if (g + G < total && tid < KT) rows_of(g + G, tid, pqi, pki);
+  // Past the last block, the prefetches repeat the last block (never used).
+  prow = rows_of(min(g + G, total - 1), tid);
+  gather_v(g);
 
   for (; g < total; g += G) {
     __syncthreads();  // the previous block is done with LDS
@@ -535,19 +549,16 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
     if (tid < KT) {
       sm.qidx[tid] = sm.qnext[tid];
       sm.kidx[tid] = sm.knext[tid];
-      sm.qnext[tid] = pqi;
-      sm.knext[tid] = pki;
+      sm.qnext[tid] = prow.alt < -1 ? prow.a : prow.alt;
+      sm.knext[tid] = prow.alt < -1 ? prow.b : prow.alt;
       sm.lse[tid] = pvalid ? plse : INFINITY;
       sm.Dd[tid] = pvalid ? pD : 0.0f;
       sm.cq[tid] = pvalid ? pc : 0.0f;
     }
-    typename M::frag vf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) vf[ks] = pv[ks];
     __syncthreads();
     // Loads for the next block (rows) and the one after (indices).
-    if (g + G < total) gather(g + G);
-    if (g + 2 * G < total && tid < KT) rows_of(g + 2 * G, tid, pqi, pki);
+    gather(min(g + G, total - 1));
+    prow = rows_of(min(g + 2 * G, total - 1), tid);
 
     const int bh = head_of(g), lev = lev_of(g);
     const bool leaf = leaf_of(g);
@@ -564,10 +575,21 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
       for (int dt = 0; dt < D / 32; ++dt) dv[dt] = dk[dt] = zero16();
       for (int qt = leaf ? w : 0; qt < NW; ++qt) {
         floatx16 s = zero16(), dp = zero16();
+        // Fragments read KB k-steps at a time so that their LDS reads overlap.
+        constexpr int KB = KS < 4 ? KS : 4;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          s = M::mma(row_frag<T>(&sm.Qs[0][0], LD, 32 * qt, 0, ks, lane), kf[ks], s);
-          dp = M::mma(row_frag<T>(&sm.Os[0][0], LD, 32 * qt, 0, ks, lane), vf[ks], dp);
+        for (int k4 = 0; k4 < KS; k4 += KB) {
+          typename M::frag qa[KB], oa[KB];
+#pragma unroll
+          for (int j = 0; j < KB; ++j) {
+            qa[j] = row_frag<T>(&sm.Qs[0][0], LD, 32 * qt, 0, k4 + j, lane);
+            oa[j] = row_frag<T>(&sm.Os[0][0], LD, 32 * qt, 0, k4 + j, lane);
+          }
+#pragma unroll
+          for (int j = 0; j < KB; ++j) {
+            s = M::mma(qa[j], kf[k4 + j], s);
+            dp = M::mma(oa[j], pv[k4 + j], dp);
+          }
         }
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
@@ -579,8 +601,9 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int v = 4 * gg + e;
-            const bool ok = kvalid && !(leaf && key > r0 + e);
-            const float p = ok ? fast_exp(s[v] * scale - L4[e]) : 0.0f;
+            // Masked pairs get exp(-inf) = 0 (no branch around the exponential).
+            const bool ok = kvalid & !(leaf & (key > r0 + e));
+            const float p = fast_exp(ok ? s[v] * scale - L4[e] : -INFINITY);
             dsv[e] = p * (C4[e] * dp[v] - D4[e]);
             s[v] = C4[e] * p;
             dp[v] = dsv[e];
@@ -599,6 +622,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
         }
       }
     }
+    gather_v(min(g + G, total - 1));
     __syncthreads();  // dS^T complete; Qs and Os no longer read
     // dV and dK tiles to LDS (rows = keys of the block) for row-contiguous stores.
 #pragma unroll
@@ -620,12 +644,22 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
     {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) dq[dt] = zero16();
+      // Leaf blocks: keys up to the tile (an even number of k-steps: 32 keys each
+      // two); the k-steps go two at a time so that their LDS reads overlap.
       const int nks = leaf ? 2 * (w + 1) : KT / M::KSTEP;
-      for (int ks = 0; ks < nks; ++ks) {
-        const typename M::frag bq = tr_frag<T>(&sm.dST[0][0], LDK, 0, 32 * w, ks, lane, false);
+      for (int ks = 0; ks < nks; ks += 2) {
+        typename M::frag bq[2], ka[2][D / 32];
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-          dq[dt] = M::mma(tr_frag<T>(&sm.Ks[0][0], LD, 0, 32 * dt, ks, lane, false), bq, dq[dt]);
+        for (int j = 0; j < 2; ++j) {
+          bq[j] = tr_frag<T>(&sm.dST[0][0], LDK, 0, 32 * w, ks + j, lane, false);
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+            ka[j][dt] = tr_frag<T>(&sm.Ks[0][0], LD, 0, 32 * dt, ks + j, lane, false);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) dq[dt] = M::mma(ka[j][dt], bq[j], dq[dt]);
       }
     }
     __syncthreads();  // Ks no longer read; dV, dK tiles complete
@@ -647,7 +681,9 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
       for (int i = 0; i < GIT; ++i) {
         const int piece = tid + NT * i, rr = piece / CH, c8 = (piece % CH) * 8;
         const int jk = sm.kidx[rr], iq = sm.qidx[rr];
-        if (jk >= 0) {
+        // Every row of a block of 32 or more is valid: the stores are then issued
+        // on every path, which keeps the waits for the prefetches exact.
+        if (SB >= 32 || jk >= 0) {
           const size_t sl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_past(jk, N, lev)
                                      : (size_t)jk;
           Vec8<T> a, b2;
@@ -656,7 +692,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
           a.store(dVp + (hb + sl) * D + c8);
           b2.store(dKp + (hb + sl) * D + c8);
         }
-        if (iq >= 0) {
+        if (SB >= 32 || iq >= 0) {
           const size_t sl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_future_b(iq, N, lev)
                                      : (size_t)iq;
           Vec8<T> a;
