@@ -288,16 +288,18 @@ __device__ __forceinline__ void gather_rows(T* const (&dst)[NX], int ld, const T
                                             size_t base, int tid) {
   constexpr int CH = D / 8, TOT = ROWS * CH, IT = (TOT + NT - 1) / NT;
   Vec8<T> buf[NX][IT];
+  bool ok[IT];
+  // Every load is issued unconditionally (a missing row reads row 0 of the
+  // block's tensor in its place and is zeroed when stored), so that no load has
+  // to complete before the next one is issued.
 #pragma unroll
   for (int i = 0; i < IT; ++i) {
     const int it = tid + i * NT;
     const int r = it / CH, c8 = (it % CH) * 8;
-    const int j = (it < TOT) ? idx[r] : -1;
+    const int j = idx[r < ROWS ? r : ROWS - 1];
+    ok[i] = it < TOT && j >= 0;
 #pragma unroll
-    for (int x = 0; x < NX; ++x) {
-      if (j >= 0) buf[x][i].load(X[x] + (base + j) * D + c8);
-      else buf[x][i].zero();
-    }
+    for (int x = 0; x < NX; ++x) buf[x][i].load(X[x] + (base + (j > 0 ? j : 0)) * D + c8);
   }
 #pragma unroll
   for (int i = 0; i < IT; ++i) {
@@ -306,6 +308,7 @@ __device__ __forceinline__ void gather_rows(T* const (&dst)[NX], int ld, const T
       const int r = it / CH, c8 = (it % CH) * 8;
 #pragma unroll
       for (int x = 0; x < NX; ++x) {
+        if (!ok[i]) buf[x][i].zero();
         if (scale[x]) buf[x][i].scale(scale[x][r]);
         buf[x][i].store(dst[x] + (size_t)r * ld + c8);
       }

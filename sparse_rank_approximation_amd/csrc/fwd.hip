@@ -78,26 +78,23 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
 
   for (int t = tid; t < KT; t += blockDim.x)
     kidx[t] = t < SB ? (leaf ? tok0 + t : ksrc[t]) : -1;
+  // This wave's queries (one per lane column); the order entries of the keys and
+  // queries are read together.
+  const int qloc = 32 * w + col;
+  const bool qvalid = qloc < SB;
+  const int qi = qvalid ? (leaf ? tok0 + qloc : qsrc[qloc]) : 0;
   __syncthreads();
-  // Gather the block's K and V rows into LDS (row-major, 16-byte row-contiguous
-  // copies, all loads in flight together); rows past the block are zero.
+  // The query rows as MFMA operands (queries past the block read row 0, unused),
+  // then the block's K and V rows gathered into LDS (row-major, 16-byte
+  // row-contiguous copies; rows past the block are zero), all loads in flight
+  // together.
+  typename M::frag qf[D / M::KSTEP];
+  prefetch_row_frags<T, D>(Q + ((size_t)bh * N + qi) * D, qf, h);
   {
     T* const dst[2] = {&Ks[0][0], &Vs[0][0]};
     const T* const src[2] = {K, V};
     const float* const sc[2] = {nullptr, nullptr};
     gather_rows<T, D, KT, 64 * (SB < 32 ? 1 : SB / 32), 2>(dst, LD, src, sc, kidx, (size_t)bh * N, tid);
-  }
-
-  // This wave's queries (one per lane column).
-  const int qloc = 32 * w + col;
-  const bool qvalid = qloc < SB;
-  const int qi = qvalid ? (leaf ? tok0 + qloc : qsrc[qloc]) : 0;
-  typename M::frag qf[D / M::KSTEP];
-  {
-    const T* qr = Q + ((size_t)bh * N + qi) * D;
-#pragma unroll
-    for (int ks = 0; ks < D / M::KSTEP; ++ks)
-      qf[ks] = qvalid ? M::load(qr + ks * M::KSTEP + M::KPL * h) : M::zero();
   }
   __syncthreads();
 
@@ -145,11 +142,14 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
     }
   }
 
-  if (qvalid) {
+  // The normalized output tile goes to LDS as rows (one per query, over the key
+  // tile once every wave is done with it) and leaves with row-contiguous 16-byte
+  // stores to the queries' slots.
+  const size_t slot = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_future(qi, N, lev)
+                               : (size_t)qi;
+  __syncthreads();
+  {
     const float inv = 1.0f / lrun;
-    const size_t slot = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_future(qi, N, lev)
-                                 : (size_t)qi;
-    T* dst = Opart + ((size_t)bh * slots + slot) * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -157,9 +157,23 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
         float x[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = o[dt][4 * g + e] * inv;
-        store4(dst + 32 * dt + 8 * g + 4 * h, x);
+        store4(&Ks[qloc][32 * dt + 8 * g + 4 * h], x);
       }
-    if (h == 0) Lpart[(size_t)bh * slots + slot] = mrun + __logf(lrun);
+    if (h == 0) kidx[qloc] = qvalid ? (int)slot : -1;
+  }
+  if (qvalid && h == 0) Lpart[(size_t)bh * slots + slot] = mrun + __logf(lrun);
+  __syncthreads();
+  {
+    constexpr int CH = D / 8, NT = 64 * (SB < 32 ? 1 : SB / 32);
+#pragma unroll
+    for (int i = 0; i < (KT * CH + NT - 1) / NT; ++i) {
+      const int piece = tid + NT * i, r = piece / CH, c8 = (piece % CH) * 8;
+      if (piece < KT * CH && kidx[r] >= 0) {
+        Vec8<T> x;
+        x.load(&Ks[r][c8]);
+        x.store(Opart + ((size_t)bh * slots + kidx[r]) * D + c8);
+      }
+    }
   }
 }
 
