@@ -428,15 +428,17 @@ template <int D, int SB>
 struct Sb2Smem {
   static constexpr int KT = SB < 32 ? 32 : SB;
   static constexpr int LD = tile_ld<__bf16>(D), LDK = tile_ld<__bf16>(KT);
-  __bf16 Qs[KT][LD];
-  __bf16 Os[KT][LD];    // dO (the row factor c is applied in registers)
-  __bf16 Ks[KT][LD];
-  __bf16 dST[KT][LDK];  // dS^T, [key][query]
+  // The per-row arrays come first: their addresses are then small constants
+  // from one per-thread base (instruction offsets), not separate registers.
   alignas(16) float lse[KT];  // +inf for rows past the block (P = 0)
   alignas(16) float Dd[KT];
   alignas(16) float cq[KT];
   int qidx[KT], kidx[KT];    // token of each row of this block, -1 past the block
   int qnext[KT], knext[KT];  // the same for the next block
+  alignas(16) __bf16 Qs[KT][LD];
+  __bf16 Os[KT][LD];    // dO (the row factor c is applied in registers)
+  __bf16 Ks[KT][LD];
+  __bf16 dST[KT][LDK];  // dS^T, [key][query]
 };
 
 template <int D, int SB>
@@ -462,13 +464,13 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
   const int per_level = causal ? (N / 2) / SB : 0;
   const int nlev = causal ? levels * per_level : 0;
 
-  // Block g: head, level (-1 for a causal leaf or the non-causal level), rows.
-  auto head_of = [&](int g) __attribute__((always_inline)) { return g / items; };
-  auto lev_of = [&](int g) __attribute__((always_inline)) {
-    const int it = g % items;
-    return causal ? (it < nlev ? it / per_level : -1) : -1;
+  // Block g (in the XCD-aware order): head, level (-1 for a causal leaf or the
+  // non-causal level), rows. G is a multiple of 8, so a workgroup's blocks are
+  // all of its own XCD's share.
+  auto head_of = [&](int g) __attribute__((always_inline)) {
+    int it;
+    return xcd_item(g, items, per_level, levels, it);
   };
-  auto leaf_of = [&](int g) __attribute__((always_inline)) { return causal && (g % items) >= nlev; };
   // Rows of block g: row t's query and key tokens are (a, b) when alt < -1, else
   // both are alt (a causal leaf: the token itself; -1 past the block). The order
   // entries are read on every path (a leaf or a row past the block reads the
@@ -479,7 +481,8 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
     int a, b, alt;
   };
   auto rows_of = [&](int g, int t) __attribute__((always_inline)) {
-    const int bh = g / items, it = g % items;
+    int it;
+    const int bh = xcd_item(g, items, per_level, levels, it);
     const bool lf = causal && it >= nlev, past = t >= SB;
     const size_t off = (size_t)bh * P + (lf || past ? (size_t)0
                                          : causal ? (size_t)(it / per_level) * (N / 2) +
@@ -494,8 +497,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
   float plse = 0.0f, pD = 0.0f, pc = 0.0f;
   bool pvalid = false;
   Rows prow{-1, -1, -1};
-  auto gather = [&](int g) __attribute__((always_inline)) {
-    const size_t rb = (size_t)head_of(g) * N;
+  auto gather = [&](size_t rb) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < GIT; ++i) {
       const int piece = tid + NT * i, r = piece / CH, c8 = (piece % CH) * 8;
@@ -518,9 +520,9 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
 
   // V rows of the next block's keys of this wave, as MFMA operands (issued once
   // the current block no longer needs the registers).
-  auto gather_v = [&](int g) __attribute__((always_inline)) {
+  auto gather_v = [&](size_t rb) __attribute__((always_inline)) {
     const int kv = sm.knext[32 * w + col];
-    prefetch_row_frags<T, D>(V + ((size_t)head_of(g) * N + max(kv, 0)) * D, pv, h);
+    prefetch_row_frags<T, D>(V + (rb + max(kv, 0)) * D, pv, h);
   };
 
   int g = blockIdx.x;
@@ -531,10 +533,10 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
     sm.knext[tid] = r0.alt < -1 ? r0.b : r0.alt;
   }
   __syncthreads();
-  gather(g);
+  gather((size_t)head_of(g) * N);
   // Past the last block, the prefetches repeat the last block (never used).
   prow = rows_of(min(g + G, total - 1), tid);
-  gather_v(g);
+  gather_v((size_t)head_of(g) * N);
 
   for (; g < total; g += G) {
     __syncthreads();  // the previous block is done with LDS
@@ -556,12 +558,11 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
       sm.cq[tid] = pvalid ? pc : 0.0f;
     }
     __syncthreads();
-    // Loads for the next block (rows) and the one after (indices).
-    gather(min(g + G, total - 1));
-    prow = rows_of(min(g + 2 * G, total - 1), tid);
 
-    const int bh = head_of(g), lev = lev_of(g);
-    const bool leaf = leaf_of(g);
+    int it;
+    const int bh = xcd_item(g, items, per_level, levels, it);
+    const int lev = causal ? (it < nlev ? it / per_level : -1) : -1;
+    const bool leaf = causal && it >= nlev;
     // Phase 1: key wave w.
     const int key = 32 * w + col;
     floatx16 dv[D / 32], dk[D / 32];
@@ -573,7 +574,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
       for (int ks = 0; ks < KS; ++ks) kf[ks] = row_frag<T>(&sm.Ks[0][0], LD, 32 * w, 0, ks, lane);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) dv[dt] = dk[dt] = zero16();
-      for (int qt = leaf ? w : 0; qt < NW; ++qt) {
+      auto qtile = [&](int qt) __attribute__((always_inline)) {
         floatx16 s = zero16(), dp = zero16();
         // Fragments read KB k-steps at a time so that their LDS reads overlap.
         constexpr int KB = KS < 4 ? KS : 4;
@@ -620,9 +621,23 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
             dk[dt] = M::mma(tr_frag<T>(&sm.Qs[0][0], LD, 32 * qt, 32 * dt, ks2, lane, true), sf, dk[dt]);
           }
         }
+      };
+      // Leaf blocks: query tiles from the diagonal on; otherwise all of them, the
+      // loop unrolled so that one tile's products overlap the next tile's reads.
+      if (leaf) {
+        for (int qt = w; qt < NW; ++qt) qtile(qt);
+      } else {
+#pragma unroll
+        for (int qt = 0; qt < NW; ++qt) qtile(qt);
       }
     }
-    gather_v(min(g + G, total - 1));
+    // Loads for the next block (rows, issued now that phase 1 no longer needs the
+    // registers; phase 2 and the stores cover their latency) and the one after
+    // (indices).
+    const size_t nrb = (size_t)head_of(min(g + G, total - 1)) * N;
+    gather(nrb);
+    prow = rows_of(min(g + 2 * G, total - 1), tid);
+    gather_v(nrb);
     __syncthreads();  // dS^T complete; Qs and Os no longer read
     // dV and dK tiles to LDS (rows = keys of the block) for row-contiguous stores.
 #pragma unroll
@@ -1189,8 +1204,9 @@ int persistent_grid(const void* kern, int threads, int total) {
   int per = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, threads, 0) != hipSuccess || per < 1)
     per = 1;
-  const long g = (long)n * per;
-  return (int)(g < total ? g : total);
+  long g = (long)n * per;
+  if (g >= total) return total;
+  return (int)(g >= 8 ? g & ~7L : g);  // a multiple of 8: each workgroup stays on one XCD's share
 }
 
 struct BwdLayout {

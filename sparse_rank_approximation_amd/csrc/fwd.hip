@@ -50,15 +50,18 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
   __shared__ T Vs[KT][LD];
   __shared__ int kidx[KT];
 
-  const int bh = blockIdx.y, item = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int w = wave_id();  // wave index, uniform (scalar) so that role branches stay uniform
   const size_t P = perm_stride(N, levels, causal);
   const size_t slots = partial_slots(N, levels, causal);
 
-  // Decode the work item.
+  // Decode the work item (workgroup blockIdx.y * gridDim.x + blockIdx.x of the
+  // launch, which runs on XCD blockIdx.x % 8 as gridDim.x is a multiple of 8
+  // whenever the XCD-aware order applies).
   const int per_level = causal ? (N / 2) / SB : 0;
   const int nlev_items = causal ? levels * per_level : 0;
+  int item;
+  const int bh = xcd_item(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, per_level, levels, item);
   const int32_t* qsrc = nullptr;
   const int32_t* ksrc = nullptr;
   int lev = -1, tok0 = 0;

@@ -72,6 +72,29 @@ __host__ __device__ inline size_t partial_slots(int N, int levels, bool causal) 
   return causal ? (size_t)N + (size_t)levels * (N / 2) : (size_t)N;
 }
 
+// Sparse work items of one head: causal, `levels` off-diagonal levels of
+// `per_level` blocks each (level-major), then the N / s leaf blocks; non-causal,
+// the N / s blocks of the single sorted order.
+//
+// Workgroup g of a launch runs on XCD g % 8 (workgroups go round-robin to the
+// eight XCDs, each with its own L2). Where every level's block count is a
+// multiple of 8, item g is picked so that XCD x takes the x-th eighth of every
+// level's blocks and of the leaf blocks: blocks of the levels whose segments are
+// at most N / 8 long, and the leaf blocks, then read rows of only the x-th eighth
+// of the tokens, which stay in that XCD's L2 from one level to the next.
+// Otherwise the order is plain (head-major). Returns the head; `it` is the item.
+__host__ __device__ inline int xcd_item(int g, int items, int per_level, int levels, int& it) {
+  if (per_level == 0 || (per_level & 7) != 0) {
+    it = g % items;
+    return g / items;
+  }
+  const int x = g & 7, k = g >> 3, ipx = items >> 3, lpx = per_level >> 3;
+  const int j = k % ipx, nl = levels * lpx;
+  it = j < nl ? (j / lpx) * per_level + x * lpx + j % lpx
+              : levels * per_level + x * (ipx - nl) + (j - nl);
+  return k / ipx;
+}
+
 // Compile-time dispatch over the element type, head dimension and padded table
 // count (tables are padded to an even power of two; padding tables are zero).
 template <typename F>
