@@ -790,15 +790,18 @@ __global__ void __launch_bounds__(512)
     Vec8<T> vb[VIT];
     float eq = 0.0f, ddq = 0.0f;
     const int ts = tid - 256;  // V staging thread (half 1)
-    auto load_rows = [&](int s0) __attribute__((always_inline)) {
+    auto load_q = [&](int s0) __attribute__((always_inline)) {
       const int tok = min(s0 + 32 * qt + col, N - 1);
       const size_t rrow = (size_t)tok * D;
       prefetch_row_frags<T, D>(Qh + rrow, qx, h);
       prefetch_row_frags<T, D>(dOh + rrow, ox, h);
       eq = re[(size_t)bh * N + tok];
       ddq = rdd[(size_t)bh * N + tok];
+    };
+    auto load_keys = [&](int s0) __attribute__((always_inline)) {
       if (causal) {
-        if constexpr (HALF == 0) prefetch_row_frags<T, D>(Kh + rrow, kx, h);
+        if constexpr (HALF == 0)
+          prefetch_row_frags<T, D>(Kh + (size_t)min(s0 + 32 * qt + col, N - 1) * D, kx, h);
         if constexpr (HALF == 1) {
   #pragma unroll
           for (int i = 0; i < VIT; ++i) {
@@ -808,7 +811,8 @@ __global__ void __launch_bounds__(512)
         }
       }
     };
-    load_rows(t_beg);
+    load_q(t_beg);
+    load_keys(t_beg);
 
     for (int s0 = t_beg; s0 < t_end; s0 += STEP) {
       const int qtok = s0 + 32 * qt + col;
@@ -848,6 +852,10 @@ __global__ void __launch_bounds__(512)
             dn[ks] = M::from_floats(x);
           }
         }
+        // The next step's keys, issued as soon as this step's are staged so that
+        // their latency hides behind the rest of the step (past the span: loads
+        // nothing that matters); its queries follow before the statistics update.
+        load_keys(s0 + STEP);
         __syncthreads();
 
         // dphi(Q)^T for this half's feature tiles (rows = features, columns =
@@ -916,9 +924,9 @@ __global__ void __launch_bounds__(512)
         }
       }
       if (!causal) break;
+      load_q(s0 + STEP);
       advance_stats<T, D, LPG, SPW, STEP, true, NW>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, nullptr, w,
                                                     lane, st, &sm.SF[0][0], sm.zr);
-      load_rows(s0 + STEP);  // past the span: loads nothing that matters
       __syncthreads();
     }
   };
@@ -1005,13 +1013,20 @@ __global__ void __launch_bounds__(512)
     Vec8<T> ob[ROLE == 1 ? OIT : 1];
     float oe[ROLE == 1 ? OIT : 1];
     float ddv = 0.0f;
+    // Two parts, each issued as soon as the registers it fills are free: the rows
+    // staged at the start of a step (K for dK waves; Q, dO, dd_lr for dV waves) and
+    // the V rows of the dK waves, used until the da exchange.
+    auto load_v = [&](int s0) __attribute__((always_inline)) {
+      if constexpr (ROLE == 0) {
+        if (s0 < t_beg) return;
+        prefetch_row_frags<T, D>(Vh + (size_t)min(s0 + 32 * kt + col, N - 1) * D, vx, h);
+      }
+    };
     auto load_rows = [&](int s0) __attribute__((always_inline)) {
       if (s0 < t_beg) return;
       const size_t trow = (size_t)min(s0 + 32 * kt + col, N - 1) * D;
       prefetch_row_frags<T, D>((ROLE == 0 ? Kh : Qh) + trow, xr, h);
-      if constexpr (ROLE == 0) {
-        prefetch_row_frags<T, D>(Vh + trow, vx, h);
-      } else {
+      if constexpr (ROLE == 1) {
 #pragma unroll
         for (int i = 0; i < OIT; ++i) {
           const int it = ts + 256 * i;
@@ -1024,6 +1039,7 @@ __global__ void __launch_bounds__(512)
     };
     const int nstep = (t_end - t_beg + STEP - 1) / STEP;
     load_rows(t_beg + (nstep - 1) * STEP);
+    load_v(t_beg + (nstep - 1) * STEP);
 
     for (int si = nstep - 1; si >= 0; --si) {
       const int s0 = t_beg + si * STEP;
@@ -1062,6 +1078,10 @@ __global__ void __launch_bounds__(512)
         }
         if (ts < STEP) sm.dd[ts] = s0 + ts < t_end ? ddv : 0.0f;
       }
+      // The next step's staged rows, issued now that this step's are consumed, so
+      // that their latency hides behind the rest of the step (before the span:
+      // loads nothing).
+      load_rows(s0 - STEP);
       __syncthreads();
 
       if constexpr (ROLE == 0) {
@@ -1112,6 +1132,7 @@ __global__ void __launch_bounds__(512)
                 floatx4{da4[0], da4[1], da4[2], da4[3]};
           }
         }
+        load_v(s0 - STEP);  // this step's V rows are no longer needed
       } else if (kwave && (NDA > 1 || HALF == 0)) {
         // dV^T for this half's channel tiles (rows = channels, columns = keys) =
         // G^T phi(K)^T + the step's part.
@@ -1174,7 +1195,6 @@ __global__ void __launch_bounds__(512)
       if (!causal) break;
       advance_stats<T, D, LPG, SPW, STEP, true, NW>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, sm.dd, w,
                                                     lane, st, &sm.SF[0][0], sm.zr);
-      load_rows(s0 - STEP);  // before the span: loads nothing
       __syncthreads();
     }
   };

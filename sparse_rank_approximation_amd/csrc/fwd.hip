@@ -243,17 +243,19 @@ __global__ void __launch_bounds__(512)
     constexpr int JP0 = HALF * NJH, DT0 = HALF * NDH;
     constexpr bool FEAT_HALF = HALF == 0 || NJP > 1;
     constexpr bool OWNER = HALF == 0 || NDA > 1;
+    constexpr bool EARLY = LP <= 8;  // next step's rows issued early (register room)
     // Rows of one step, loaded one step ahead: the wave's query tile, its key
     // tile (for its half of phi(K)) and a share of the V rows. Tokens past the
     // span read a stand-in row: their outputs are not written and their phi(K)
     // rows are stored as zero, which also cancels their V rows in every product.
     typename M::frag qx[D / M::KSTEP], kx[D / M::KSTEP];
     Vec8<T> vb[VIT];
-    auto load_rows = [&](int s0) __attribute__((always_inline)) {
-      const size_t trow = (size_t)min(s0 + 32 * qt + col, N - 1) * D;
-      prefetch_row_frags<T, D>(Qh + trow, qx, h);
+    auto load_q = [&](int s0) __attribute__((always_inline)) {
+      prefetch_row_frags<T, D>(Qh + (size_t)min(s0 + 32 * qt + col, N - 1) * D, qx, h);
+    };
+    auto load_keys = [&](int s0) __attribute__((always_inline)) {
       if (causal) {
-        if (FEAT_HALF) prefetch_row_frags<T, D>(Kh + trow, kx, h);
+        if (FEAT_HALF) prefetch_row_frags<T, D>(Kh + (size_t)min(s0 + 32 * qt + col, N - 1) * D, kx, h);
 #pragma unroll
         for (int i = 0; i < VIT; ++i) {
           const int it = tid + 512 * i, tok = s0 + it / VCH;
@@ -261,7 +263,8 @@ __global__ void __launch_bounds__(512)
         }
       }
     };
-    load_rows(t_beg);
+    load_q(t_beg);
+    load_keys(t_beg);
 
     for (int s0 = t_beg; s0 < t_end; s0 += STEP) {
       const int qtok = s0 + 32 * qt + col;
@@ -279,6 +282,11 @@ __global__ void __launch_bounds__(512)
       }
       Feat Fq;
       if (qwave && OWNER) Fq.compute(qx, PH, PLo, LDP, L, scale, tau, lane);
+      // The next step's keys: issued as soon as this step's are consumed, so that
+      // their latency hides behind the readout and the statistics update (past the
+      // span: loads nothing that matters). With 16 tables the registers do not
+      // allow it: they are issued with the queries.
+      if constexpr (EARLY) load_keys(s0 + STEP);
       __syncthreads();
 
       if (qwave && OWNER) {
@@ -362,9 +370,13 @@ __global__ void __launch_bounds__(512)
       if (!causal) break;
       __syncthreads();
       // Advance the statistics by the step's keys: S^T += V^T phi(K), z += sum phi(K).
+      if constexpr (EARLY) load_q(s0 + STEP);
       advance_stats<T, D, LP, SPW, STEP, true, NW>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, nullptr, w,
                                                    lane, st, &sm.SF[0][0], sm.zr);
-      load_rows(s0 + STEP);  // past the span: loads nothing that matters
+      if constexpr (!EARLY) {
+        load_q(s0 + STEP);
+        load_keys(s0 + STEP);
+      }
       __syncthreads();
     }
   };
