@@ -107,7 +107,7 @@ __global__ void __launch_bounds__(256) sort_kernel(const uint16_t* __restrict__ 
   extern __shared__ int smem[];
   const int nbins = 1 << bits;
   int* cnt = smem;                               // [kSortWaves][nbins]
-  int* part = smem + kSortWaves * nbins;         // [256]
+  int* part = smem + kSortWaves * nbins;         // [kSortWaves] wave totals
   const int bh = blockIdx.y, isk = blockIdx.z;
   int base, count;
   size_t out_off;
@@ -141,18 +141,18 @@ __global__ void __launch_bounds__(256) sort_kernel(const uint16_t* __restrict__ 
   auto at = [&](int e) -> int& { return cnt[(e % kSortWaves) * nbins + e / kSortWaves]; };
   int s = 0;
   for (int e = tid * chunk; e < min(E, (tid + 1) * chunk); ++e) s += at(e);
-  part[tid] = s;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < (int)blockDim.x; ++i) {
-      const int v = part[i];
-      part[i] = run;
-      run += v;
-    }
+  // Exclusive prefix of the per-thread sums: inclusive scan inside each wave
+  // (shuffles), then the totals of the earlier waves.
+  int incl = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
   }
+  if (lane == 63) part[w] = incl;
   __syncthreads();
-  s = part[tid];
+  for (int i = 0; i < w; ++i) incl += part[i];
+  s = incl - s;
   for (int e = tid * chunk; e < min(E, (tid + 1) * chunk); ++e) {
     const int v = at(e);
     at(e) = s;
