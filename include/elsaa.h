@@ -68,7 +68,10 @@ typedef enum {
 
 /* Problem description.
  *   B, H, N, d_h : batch, heads, tokens, head dimension; d_h in {32, 64, 128};
- *                  N a multiple of 32; B * H == 0 is a valid empty problem.
+ *                  N a multiple of 32 up to 2^24; B * H == 0 is a valid empty
+ *                  problem; B * H <= 65535, and B * H times the number of sparse
+ *                  blocks per head (causal: log2(N/s) * N/(2s) + N/s; otherwise
+ *                  N/s) below 2^31 (larger batches are split over calls).
  *   dtype        : element type of Q, K, V, O, dO, dQ, dK, dV (elsaa_dtype).
  *   causal       : 0 = every query may see every key; 1 = key j only for j <= i.
  *   block        : sortLSH block size s in {16, 32, 64, 128, 256}; N % s == 0; when

@@ -85,8 +85,18 @@ elsaa_status make_problem(const elsaa_params* p, Problem* pb, bool* empty) {
     return fail(ELSAA_ERR_INVALID_ARG, "eps must be finite and >= 0");
   if (!(p->scale > 0.0f) || !std::isfinite(p->scale))
     return fail(ELSAA_ERR_INVALID_ARG, "scale must be finite and > 0");
-  if ((long)p->B * p->H > (1L << 24))
-    return fail(ELSAA_ERR_INVALID_ARG, "B * H too large");
+  // Heads index the second launch dimension (at most 65535); the sparse work
+  // items of all heads are counted in 32-bit integers.
+  if ((long)p->B * p->H > 65535)
+    return fail(ELSAA_ERR_INVALID_ARG, "B * H = %ld: at most 65535 heads per call",
+                (long)p->B * p->H);
+  {
+    const long nb = p->N / p->block;
+    const long items = p->causal ? (long)ilog2((int)nb) * (nb / 2) + nb : nb;
+    if (items * p->B * p->H > 0x7fffffffL)
+      return fail(ELSAA_ERR_INVALID_ARG,
+                  "B * H * %ld sparse blocks exceeds 2^31 - 1: split the heads over calls", items);
+  }
 
   pb->B = p->B; pb->H = p->H; pb->N = p->N; pb->d = p->d_h;
   pb->bf16 = p->dtype == ELSAA_BF16;

@@ -89,6 +89,8 @@ def test_valid_params_and_workspace_sizes():
     (dict(eps=-1.0), _lib.ERR_INVALID_ARG, "eps"),
     (dict(scale=float("nan")), _lib.ERR_INVALID_ARG, "scale"),
     (dict(dtype=torch.float32, d=128, block=256, N=1024), _lib.ERR_UNSUPPORTED, "LDS"),
+    (dict(B=300, H=300), _lib.ERR_INVALID_ARG, "65535"),
+    (dict(B=1, H=200, N=1 << 24, block=16, hash_bits=12), _lib.ERR_INVALID_ARG, "2^31"),
 ])
 def test_invalid_parameters(kw, status, needle):
     s, msg, _ = status_of(base(**kw))
