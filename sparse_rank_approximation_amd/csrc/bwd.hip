@@ -923,8 +923,8 @@ __global__ void __launch_bounds__(512)
                                       last != 0, HALF * NDH);
         }
       }
-      if (!causal) break;
       load_q(s0 + STEP);
+      if (!causal) continue;  // fixed statistics
       advance_stats<T, D, LPG, SPW, STEP, true, NW>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, nullptr, w,
                                                     lane, st, &sm.SF[0][0], sm.zr);
       __syncthreads();
@@ -1192,7 +1192,7 @@ __global__ void __launch_bounds__(512)
                                       last != 0, HALF * NDH);
         }
       }
-      if (!causal) break;
+      if (!causal) continue;  // fixed statistics
       advance_stats<T, D, LPG, SPW, STEP, true, NW>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, sm.dd, w,
                                                     lane, st, &sm.SF[0][0], sm.zr);
       __syncthreads();
@@ -1385,8 +1385,8 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
         constexpr int SK = walk_step<T, D, LPG, 64,
                                      RTB + sizeof(KdaLds<LPG>) + sizeof(T) * 64 * tile_ld<T>(16 * LPG)>();
         if constexpr (SQ > 0 && SK > 0) {
-          const int span_q = pb.causal ? pb.chunk : SQ;
-          const int span_k = pb.causal ? pb.chunk : SK;
+          const int span_q = pb.causal ? pb.chunk : noncausal_span(pb.N, (int)BH, SQ);
+          const int span_k = pb.causal ? pb.chunk : noncausal_span(pb.N, (int)BH, SK);
           for (int g = 0; g < groups; ++g) {
             const int first = g == 0, last = g == groups - 1;
             ELSAA_LAUNCH("lr_bwd_q", (lr_bwd_q_kernel<T, D, LPG, SQ>),

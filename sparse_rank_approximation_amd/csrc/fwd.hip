@@ -367,7 +367,10 @@ __global__ void __launch_bounds__(512)
           if (HALF == 0 && h == 0) dlr_out[k] = den;
         }
       }
-      if (!causal) break;
+      if (!causal) {  // fixed statistics: on to the next step's queries
+        load_q(s0 + STEP);
+        continue;
+      }
       __syncthreads();
       // Advance the statistics by the step's keys: S^T += V^T phi(K), z += sum phi(K).
       if constexpr (EARLY) load_q(s0 + STEP);
@@ -442,7 +445,7 @@ void launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
         constexpr int LP = ELSAA_C(lc);
         constexpr int STEP = walk_step<T, D, LP, 128, sizeof(PlanesLds<T, D, LP>)>();
         if constexpr (STEP > 0) {
-          const int span = pb.causal ? pb.chunk : STEP;
+          const int span = pb.causal ? pb.chunk : noncausal_span(pb.N, BH, STEP);
           const int nspan = (pb.N + span - 1) / span;
           ELSAA_LAUNCH("fwd_epilogue", (fwd_epilogue_kernel<T, D, LP, STEP>), dim3(nspan, BH),
                        dim3(512), 0, st, (const T*)Q, (const T*)K, (const T*)V, planes_lr, A, z,

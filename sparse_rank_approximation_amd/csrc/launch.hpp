@@ -95,6 +95,16 @@ __host__ __device__ inline int xcd_item(int g, int items, int per_level, int lev
   return k / ipx;
 }
 
+// Tokens per workgroup of the low-rank walks when not causal: the statistics are
+// the whole sequence's and stay fixed, so a workgroup walks several steps after
+// loading them once; as many steps as keep at least 512 workgroups in the launch.
+inline int noncausal_span(int N, int BH, int step) {
+  const int steps = (N + step - 1) / step;
+  int per = steps * BH / 512;
+  per = per < 1 ? 1 : per > steps ? steps : per;
+  return per * step;
+}
+
 // Compile-time dispatch over the element type, head dimension and padded table
 // count (tables are padded to an even power of two; padding tables are zero).
 template <typename F>
