@@ -36,7 +36,7 @@ class Workload:
     gen: str            # Q/K generator kind
     gen_args: dict = field(default_factory=dict)
     lr_bits: int = 4
-    chunk: int = 2048   # causal RACE summary spacing (numerics-neutral; larger is faster)
+    chunk: int = 2048   # causal RACE summary spacing (rounding only); sets the walks' parallelism
 
     @property
     def hash_bits(self) -> int:
@@ -62,7 +62,7 @@ CONFIGS = {
     1: Workload("tiny_single_head_B1_H1_N256_d32_f32", 1, 1, 256, 32, "f32", False, 16, 16,
                 "iid", chunk=64),
     2: Workload("gpt2_small_layer_B8_H12_N4096_d64_bf16_causal", 8, 12, 4096, 64, "bf16", True,
-                64, 64, "clusters", dict(n_clusters=64, sigma=0.3)),
+                64, 64, "clusters", dict(n_clusters=64, sigma=0.3), chunk=512),
     3: Workload("llama_long_context_B2_H32_N16384_d128_bf16_causal", 2, 32, 16384, 128, "bf16",
                 True, 128, 128, "clusters_diffuse",
                 dict(n_clusters=256, sigma=0.5, diffuse=0.2)),
