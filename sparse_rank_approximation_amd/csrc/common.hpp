@@ -483,13 +483,13 @@ struct Features {
     load_row_frags<T, D>(xrow, valid, xb, lane >> 5);
     compute(xb, planes, L, scale, tau, lane);
   }
-  // Same, from the token's row fragments (zero fragments give zero projections).
-  __device__ __forceinline__ void compute(const typename MF<T>::frag (&xf)[D / MF<T>::KSTEP],
-                                          const float* planes, int L, float scale, float tau,
-                                          int lane) {
+  // Projection tiles U^T = R X^T of this lane's token, from fp32 hyperplanes in
+  // memory (bf16: split into hi + lo parts on the fly).
+  static __device__ __forceinline__ void project(const typename MF<T>::frag (&xf)[D / MF<T>::KSTEP],
+                                                 const float* planes, int L, int lane,
+                                                 floatx16 (&u)[NPT]) {
     typedef MF<T> M;
     const int h = lane >> 5, col = lane & 31;
-    floatx16 u[NPT];
 #pragma unroll
     for (int mt = 0; mt < NPT; ++mt) u[mt] = zero16();
 #pragma unroll
@@ -523,14 +523,12 @@ struct Features {
         }
       }
     }
-    activate(u, L, scale, tau, lane);
   }
-  // Same, with the hyperplanes staged in LDS by stage_planes (PL unused for fp32).
-  __device__ __forceinline__ void compute(const typename MF<T>::frag (&xf)[D / MF<T>::KSTEP],
-                                          const T* PH, const T* PL, int ldp, int L, float scale,
-                                          float tau, int lane) {
+  // The same from the hyperplanes staged in LDS by stage_planes (PL unused for fp32).
+  static __device__ __forceinline__ void project(const typename MF<T>::frag (&xf)[D / MF<T>::KSTEP],
+                                                 const T* PH, const T* PL, int ldp, int lane,
+                                                 floatx16 (&u)[NPT]) {
     typedef MF<T> M;
-    floatx16 u[NPT];
 #pragma unroll
     for (int mt = 0; mt < NPT; ++mt) u[mt] = zero16();
 #pragma unroll
@@ -540,6 +538,22 @@ struct Features {
         u[mt] = M::mma(row_frag<T>(PH, ldp, 32 * mt, 0, ks, lane), xf[ks], u[mt]);
         if constexpr (M::KPL > 1) u[mt] = M::mma(row_frag<T>(PL, ldp, 32 * mt, 0, ks, lane), xf[ks], u[mt]);
       }
+  }
+
+  // Same, from the token's row fragments (zero fragments give zero projections).
+  __device__ __forceinline__ void compute(const typename MF<T>::frag (&xf)[D / MF<T>::KSTEP],
+                                          const float* planes, int L, float scale, float tau,
+                                          int lane) {
+    floatx16 u[NPT];
+    project(xf, planes, L, lane, u);
+    activate(u, L, scale, tau, lane);
+  }
+  // Same, with the hyperplanes staged in LDS by stage_planes (PL unused for fp32).
+  __device__ __forceinline__ void compute(const typename MF<T>::frag (&xf)[D / MF<T>::KSTEP],
+                                          const T* PH, const T* PL, int ldp, int L, float scale,
+                                          float tau, int lane) {
+    floatx16 u[NPT];
+    project(xf, PH, PL, ldp, lane, u);
     activate(u, L, scale, tau, lane);
   }
   // phi of every table for this lane's token (zero when !valid) stored straight
@@ -549,18 +563,23 @@ struct Features {
   static __device__ __forceinline__ void compute_to_row(
       const typename MF<T>::frag (&xf)[D / MF<T>::KSTEP], const T* PH, const T* PL, int ldp, int L,
       float scale, float tau, int lane, bool valid, T* dst) {
-    typedef MF<T> M;
-    const int h = lane >> 5;
     floatx16 u[NPT];
-#pragma unroll
-    for (int mt = 0; mt < NPT; ++mt) u[mt] = zero16();
-#pragma unroll
-    for (int ks = 0; ks < D / M::KSTEP; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < NPT; ++mt) {
-        u[mt] = M::mma(row_frag<T>(PH, ldp, 32 * mt, 0, ks, lane), xf[ks], u[mt]);
-        if constexpr (M::KPL > 1) u[mt] = M::mma(row_frag<T>(PL, ldp, 32 * mt, 0, ks, lane), xf[ks], u[mt]);
-      }
+    project(xf, PH, PL, ldp, lane, u);
+    store_row<JP0, NJ>(u, L, scale, tau, lane, valid, dst);
+  }
+  // The same with the hyperplanes read from memory.
+  template <int JP0 = 0, int NJ = NJP>
+  static __device__ __forceinline__ void compute_to_row(
+      const typename MF<T>::frag (&xf)[D / MF<T>::KSTEP], const float* planes, int L, float scale,
+      float tau, int lane, bool valid, T* dst) {
+    floatx16 u[NPT];
+    project(xf, planes, L, lane, u);
+    store_row<JP0, NJ>(u, L, scale, tau, lane, valid, dst);
+  }
+  template <int JP0, int NJ>
+  static __device__ __forceinline__ void store_row(const floatx16 (&u)[NPT], int L, float scale,
+                                                   float tau, int lane, bool valid, T* dst) {
+    const int h = lane >> 5;
     const float c2 = 2.0f * scale / tau;
 #pragma unroll
     for (int mt = 0; mt < NPT; ++mt)

@@ -183,10 +183,12 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
 // ---------------------------------------------------------------------------
 
 // Epilogue workgroup: one head and one span of tokens (a summary chunk when
-// causal), walked in steps of STEP tokens by 4 waves. LDS (WalkSmem) holds the
+// causal), walked in steps of STEP tokens by 8 waves. LDS (WalkSmem) holds the
 // step's keys (V in XS, phi(K) in FS, row-major) and the running RACE statistics
-// S = sum_j phi(K_j) V_j^T as an MFMA operand (SF, [feature][channel]).
-template <typename T, int D, int LP, int STEP>
+// S = sum_j phi(K_j) V_j^T as an MFMA operand (SF, [feature][channel]); the RACE
+// hyperplanes too when PLDS (else they are read from memory, which leaves room
+// for a longer step).
+template <typename T, int D, int LP, int STEP, bool PLDS>
 __global__ void __launch_bounds__(512)
     fwd_epilogue_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                         const float* __restrict__ planes, const float* __restrict__ A,
@@ -206,7 +208,7 @@ __global__ void __launch_bounds__(512)
   constexpr int NFT = RP / 32, NST = NDA * NFT, SPW = (NST + NW - 1) / NW;
   constexpr int VCH = D / 8, VIT = (STEP * VCH + 511) / 512;
   __shared__ Sm sm;
-  __shared__ PlanesLds<T, D, LP> PLs;
+  __shared__ PlanesLds<T, D, PLDS ? LP : 2> PLs;
 
   const int bh = blockIdx.y, c = blockIdx.x, head = bh % H;
   const int r = 16 * L;
@@ -228,10 +230,10 @@ __global__ void __launch_bounds__(512)
   const float* zc = z + sidx * r;
   floatx16 st[SPW];
   load_stats<T, D, LP, SPW, NW>(Ac, r, 0, w, lane, st, &sm.SF[0][0], LDD);
-  stage_planes<T, D, LP, 512>(pl, L, PLs, tid);
+  if constexpr (PLDS) stage_planes<T, D, LP, 512>(pl, L, PLs, tid);
   const T* PH = &PLs.p[0][0][0];
-  const T* PLo = &PLs.p[PlanesLds<T, D, LP>::NPART - 1][0][0];
-  constexpr int LDP = PlanesLds<T, D, LP>::LDP;
+  const T* PLo = &PLs.p[PlanesLds<T, D, PLDS ? LP : 2>::NPART - 1][0][0];
+  constexpr int LDP = PlanesLds<T, D, PLDS ? LP : 2>::LDP;
   for (int f = tid; f < RP; f += 512) sm.zr[f] = f < r ? zc[f] : 0.0f;
   __syncthreads();  // hyperplanes and statistics staged
 
@@ -272,6 +274,10 @@ __global__ void __launch_bounds__(512)
       // Stage the step's keys: this half's phi(K) tables and V into LDS (causal).
       if (causal) {
         if (qwave && FEAT_HALF)
+          if constexpr (!PLDS)
+            Feat::template compute_to_row<JP0, NJH>(kx, pl, L, scale, tau, lane, qvalid,
+                                                    &sm.FS[32 * qt + col][0]);
+          else
           Feat::template compute_to_row<JP0, NJH>(kx, PH, PLo, LDP, L, scale, tau, lane, qvalid,
                                                   &sm.FS[32 * qt + col][0]);
 #pragma unroll
@@ -281,7 +287,10 @@ __global__ void __launch_bounds__(512)
         }
       }
       Feat Fq;
-      if (qwave && OWNER) Fq.compute(qx, PH, PLo, LDP, L, scale, tau, lane);
+      if (qwave && OWNER) {
+        if constexpr (PLDS) Fq.compute(qx, PH, PLo, LDP, L, scale, tau, lane);
+        else Fq.compute(qx, pl, L, scale, tau, lane);
+      }
       // The next step's keys: issued as soon as this step's are consumed, so that
       // their latency hides behind the readout and the statistics update (past the
       // span: loads nothing that matters). With 16 tables the registers do not
@@ -392,6 +401,20 @@ size_t fwd_ws_bytes(const Problem& pb) {
   return (size_t)pb.B * pb.H * slots * ((size_t)pb.d * pb.elem + sizeof(float)) + 256;
 }
 
+// The epilogue keeps the RACE hyperplanes in LDS unless that would cut its step
+// to 32 tokens where reading them from memory allows a longer one.
+template <typename T, int D, int LP>
+constexpr bool epilogue_planes_in_lds() {
+  constexpr int with = walk_step<T, D, LP, 128, sizeof(PlanesLds<T, D, LP>)>();
+  constexpr int without = walk_step<T, D, LP, 128, 0>();
+  return with >= 64 || without <= with;
+}
+template <typename T, int D, int LP>
+constexpr int epilogue_step() {
+  return epilogue_planes_in_lds<T, D, LP>() ? walk_step<T, D, LP, 128, sizeof(PlanesLds<T, D, LP>)>()
+                                            : walk_step<T, D, LP, 128, 0>();
+}
+
 size_t fwd_lds_need(const Problem& pb) {
   size_t need = 0;
   with_T(pb.bf16, [&](auto tp) {
@@ -400,8 +423,9 @@ size_t fwd_lds_need(const Problem& pb) {
       constexpr int D = ELSAA_C(dc);
       with_LP(pb.L, [&](auto lc) {
         constexpr int LP = ELSAA_C(lc);
-        constexpr int STEP = walk_step<T, D, LP, 128, sizeof(PlanesLds<T, D, LP>)>();
-        need = sizeof(PlanesLds<T, D, LP>) +
+        constexpr bool PLDS = epilogue_planes_in_lds<T, D, LP>();
+        constexpr int STEP = epilogue_step<T, D, LP>();
+        need = (PLDS ? sizeof(PlanesLds<T, D, LP>) : 0) +
                (STEP > 0 ? sizeof(WalkSmem<T, D, LP, STEP>) : sizeof(WalkSmem<T, D, LP, 32>));
       });
     });
@@ -443,11 +467,12 @@ void launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
       launch_merge(pb, Opart, Lpart, O_s, lse, st);
       with_LP(pb.L, [&](auto lc) {
         constexpr int LP = ELSAA_C(lc);
-        constexpr int STEP = walk_step<T, D, LP, 128, sizeof(PlanesLds<T, D, LP>)>();
+        constexpr bool PLDS = epilogue_planes_in_lds<T, D, LP>();
+        constexpr int STEP = epilogue_step<T, D, LP>();
         if constexpr (STEP > 0) {
           const int span = pb.causal ? pb.chunk : noncausal_span(pb.N, BH, STEP);
           const int nspan = (pb.N + span - 1) / span;
-          ELSAA_LAUNCH("fwd_epilogue", (fwd_epilogue_kernel<T, D, LP, STEP>), dim3(nspan, BH),
+          ELSAA_LAUNCH("fwd_epilogue", (fwd_epilogue_kernel<T, D, LP, STEP, PLDS>), dim3(nspan, BH),
                        dim3(512), 0, st, (const T*)Q, (const T*)K, (const T*)V, planes_lr, A, z,
                        (const T*)O_s, lse, lambda, g_s, g_lr, (T*)O, (T*)O_lr, d_lr, pb.H, pb.N,
                        pb.L, span, (int)pb.causal, pb.scale, pb.tau, pb.eps);
