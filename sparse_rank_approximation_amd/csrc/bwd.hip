@@ -309,20 +309,34 @@ __global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
         for (int dt = 0; dt < D / 32; ++dt) acc[dt] = zero16();
         for (int qt = qt0; qt < KT / 32; ++qt) {
           floatx16 s = zero16();
+          // Fragments read four k-steps at a time so that their LDS reads overlap.
+          constexpr int KB = D / M::KSTEP < 4 ? D / M::KSTEP : 4;
 #pragma unroll
-          for (int ks = 0; ks < D / M::KSTEP; ++ks)
-            s = M::mma(row_frag<T>(&sm.Qs[0][0], LD, 32 * qt, 0, ks, lane), kf[ks], s);
+          for (int k4 = 0; k4 < D / M::KSTEP; k4 += KB) {
+            typename M::frag qa[KB];
+#pragma unroll
+            for (int j = 0; j < KB; ++j) qa[j] = row_frag<T>(&sm.Qs[0][0], LD, 32 * qt, 0, k4 + j, lane);
+#pragma unroll
+            for (int j = 0; j < KB; ++j) s = M::mma(qa[j], kf[k4 + j], s);
+          }
           floatx16 dp = zero16();
           if (pass == 1) {
 #pragma unroll
-            for (int ks = 0; ks < D / M::KSTEP; ++ks)
-              dp = M::mma(row_frag<T>(&sm.Os[0][0], LD, 32 * qt, 0, ks, lane), vf[ks], dp);
+            for (int k4 = 0; k4 < D / M::KSTEP; k4 += KB) {
+              typename M::frag oa[KB];
+#pragma unroll
+              for (int j = 0; j < KB; ++j) oa[j] = row_frag<T>(&sm.Os[0][0], LD, 32 * qt, 0, k4 + j, lane);
+#pragma unroll
+              for (int j = 0; j < KB; ++j) dp = M::mma(oa[j], vf[k4 + j], dp);
+            }
           }
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int qr = 32 * qt + acc_row(v, h);
-            const bool ok = kvalid && sm.qidx[qr] >= 0 && !(leaf && key > qr);
-            const float p = ok ? fast_exp(s[v] * scale - sm.lse[qr]) : 0.0f;
+            // Masked pairs get exp(-inf) = 0 (no branch around the exponential);
+            // every row of a block of 32 or more is valid.
+            const bool ok = kvalid & (SB >= 32 || sm.qidx[qr] >= 0) & !(leaf & (key > qr));
+            const float p = fast_exp(ok ? s[v] * scale - sm.lse[qr] : -INFINITY);
             s[v] = pass == 0 ? p : p * (dp[v] - sm.Dd[qr]);
           }
           const T* X = pass == 0 ? &sm.Os[0][0] : &sm.Qs[0][0];
@@ -373,16 +387,26 @@ __global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
       const int nkt = leaf ? qw + 1 : KT / 32;
       for (int kt = 0; kt < nkt; ++kt) {
         floatx16 s = zero16(), dp = zero16();
+        constexpr int KB = D / M::KSTEP < 4 ? D / M::KSTEP : 4;
 #pragma unroll
-        for (int ks = 0; ks < D / M::KSTEP; ++ks) {
-          s = M::mma(row_frag<T>(&sm.Ks[0][0], LD, 32 * kt, 0, ks, lane), qf[ks], s);
-          dp = M::mma(row_frag<T>(&sm.Vs[0][0], LD, 32 * kt, 0, ks, lane), of[ks], dp);
+        for (int k4 = 0; k4 < D / M::KSTEP; k4 += KB) {
+          typename M::frag ka[KB], va[KB];
+#pragma unroll
+          for (int j = 0; j < KB; ++j) {
+            ka[j] = row_frag<T>(&sm.Ks[0][0], LD, 32 * kt, 0, k4 + j, lane);
+            va[j] = row_frag<T>(&sm.Vs[0][0], LD, 32 * kt, 0, k4 + j, lane);
+          }
+#pragma unroll
+          for (int j = 0; j < KB; ++j) {
+            s = M::mma(ka[j], qf[k4 + j], s);
+            dp = M::mma(va[j], of[k4 + j], dp);
+          }
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int kr = 32 * kt + acc_row(v, h);
-          const bool ok = qvalid && sm.kidx[kr] >= 0 && !(leaf && kr > query);
-          const float p = ok ? fast_exp(s[v] * scale - lq) : 0.0f;
+          const bool ok = qvalid & (SB >= 32 || sm.kidx[kr] >= 0) & !(leaf & (kr > query));
+          const float p = fast_exp(ok ? s[v] * scale - lq : -INFINITY);
           s[v] = p * (dp[v] - dq);
         }
 #pragma unroll
