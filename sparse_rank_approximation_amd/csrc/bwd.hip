@@ -193,24 +193,29 @@ constexpr int sbwd_threads(int role) {
   return 64 * (SB < 32 ? 1 : SB / 32) * (role == 3 ? 2 : 1);
 }
 
-// Row fragments of one token row read from global memory, scaled.
-template <typename T, int D>
+// Row fragments of one token row read from global memory (x must point to a
+// readable row), scaled by sc when SCALED, zero when !valid. Every load is issued
+// before any value is used, so that they are in flight together.
+template <typename T, int D, bool SCALED = false>
 __device__ __forceinline__ void row_frags(const T* x, bool valid, float sc,
                                           typename MF<T>::frag (&f)[D / MF<T>::KSTEP], int h) {
   typedef MF<T> M;
+  typename M::frag raw[D / M::KSTEP];
+  prefetch_row_frags<T, D>(x, raw, h);
 #pragma unroll
   for (int ks = 0; ks < D / M::KSTEP; ++ks) {
-    if (!valid) {
-      f[ks] = M::zero();
-    } else if (sc == 1.0f) {
-      f[ks] = M::load(x + ks * M::KSTEP + M::KPL * h);
-    } else {
+    if constexpr (SCALED) {
+      const float c = valid ? sc : 0.0f;
       float v[M::KPL];
-      if constexpr (M::KPL == 8) load8(x + ks * M::KSTEP + M::KPL * h, v);
-      else v[0] = to_f(x[ks * M::KSTEP + M::KPL * h]);
+      if constexpr (M::KPL == 8) {
 #pragma unroll
-      for (int e = 0; e < M::KPL; ++e) v[e] *= sc;
+        for (int e = 0; e < 8; ++e) v[e] = (float)raw[ks][e] * c;
+      } else {
+        v[0] = raw[ks] * c;
+      }
       f[ks] = M::from_floats(v);
+    } else {
+      f[ks] = valid ? raw[ks] : M::zero();
     }
   }
 }
@@ -378,7 +383,7 @@ __global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
         }
       } else {
         row_frags<T, D>(Q + (rowbase + (qvalid ? iq : 0)) * D, qvalid, 1.0f, qf, h);
-        row_frags<T, D>(dO + (rowbase + (qvalid ? iq : 0)) * D, qvalid, sm.cq[query], of, h);
+        row_frags<T, D, true>(dO + (rowbase + (qvalid ? iq : 0)) * D, qvalid, sm.cq[query], of, h);
       }
       const float lq = sm.lse[query], dq = sm.Dd[query];
       floatx16 acc[D / 32];
