@@ -49,11 +49,15 @@ __device__ __forceinline__ int compact_past(int j, int N, int l) {
 // Writes the low-rank part of one gradient row held in the accumulator layout
 // (lane = token): lr + the fp32 running sum of earlier feature groups (unless
 // first), stored as T (last group) or as the fp32 running sum. The sparse partial
-// rows are added afterwards (combine_kernel).
-template <typename T, int D, int NDT = D / 32>
+// rows are added afterwards (combine_kernel). SINGLE: one feature group, stored
+// straight to out (no running-sum load, so nothing here waits for memory).
+template <typename T, int D, int NDT = D / 32, bool SINGLE = false>
 __device__ __forceinline__ void write_grad_row(const floatx16 (&lr)[NDT], float* scratch, T* out,
                                                size_t row, int h, bool first, bool last,
                                                int dt0 = 0) {
+  if constexpr (SINGLE) {
+    first = last = true;
+  }
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -761,7 +765,7 @@ struct QdaLds {
   float da[4][2][32][2 * LPG];  // [query tile][lane half][token][table pair * 4 + t]
 };
 
-template <typename T, int D, int LPG, int STEP>
+template <typename T, int D, int LPG, int STEP, bool SINGLE>
 __global__ void __launch_bounds__(512)
     lr_bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                     const T* __restrict__ dO, const float* __restrict__ planes,
@@ -819,29 +823,33 @@ __global__ void __launch_bounds__(512)
     Vec8<T> vb[VIT];
     float eq = 0.0f, ddq = 0.0f;
     const int ts = tid - 256;  // V staging thread (half 1)
+    // (The row terms first: they are used first, so waiting for them leaves the
+    // row loads in flight.)
     auto load_q = [&](int s0) __attribute__((always_inline)) {
       const int tok = min(s0 + 32 * qt + col, N - 1);
       const size_t rrow = (size_t)tok * D;
-      prefetch_row_frags<T, D>(Qh + rrow, qx, h);
-      prefetch_row_frags<T, D>(dOh + rrow, ox, h);
       eq = re[(size_t)bh * N + tok];
       ddq = rdd[(size_t)bh * N + tok];
+      prefetch_row_frags<T, D>(Qh + rrow, qx, h);
+      prefetch_row_frags<T, D>(dOh + rrow, ox, h);
     };
+    // (Also issued when not causal, where they are unused: the loads are then the
+    // same on every path, which keeps the waits for them exact.)
     auto load_keys = [&](int s0) __attribute__((always_inline)) {
-      if (causal) {
-        if constexpr (HALF == 0)
-          prefetch_row_frags<T, D>(Kh + (size_t)min(s0 + 32 * qt + col, N - 1) * D, kx, h);
-        if constexpr (HALF == 1) {
+      if constexpr (HALF == 0)
+        prefetch_row_frags<T, D>(Kh + (size_t)min(s0 + 32 * qt + col, N - 1) * D, kx, h);
+      if constexpr (HALF == 1) {
   #pragma unroll
-          for (int i = 0; i < VIT; ++i) {
-            const int it = ts + 256 * i;
-            if (it < STEP * VCH) vb[i].load(Vh + (size_t)min(s0 + it / VCH, N - 1) * D + (it % VCH) * 8);
-          }
+        for (int i = 0; i < VIT; ++i) {
+          const int it = ts + 256 * i;
+          if (it < STEP * VCH) vb[i].load(Vh + (size_t)min(s0 + it / VCH, N - 1) * D + (it % VCH) * 8);
         }
       }
     };
-    load_q(t_beg);
+    // The same order as in the walk (keys, then queries), so that the waits for
+    // them are the same on the first step as on every other.
     load_keys(t_beg);
+    load_q(t_beg);
 
     for (int s0 = t_beg; s0 < t_end; s0 += STEP) {
       const int qtok = s0 + 32 * qt + col;
@@ -948,7 +956,7 @@ __global__ void __launch_bounds__(512)
           floatx16 dx[NDH];
           features_dx<T, D, LPG, T, NDH>(da, RTs, rt_lds_width<LPG>(), c2, lane, dx, HALF * NDH);
           if (qvalid)
-            write_grad_row<T, D, NDH>(dx, scratch, dQ, ((size_t)bh * N + qtok) * D, h, first != 0,
+            write_grad_row<T, D, NDH, SINGLE>(dx, scratch, dQ, ((size_t)bh * N + qtok) * D, h, first != 0,
                                       last != 0, HALF * NDH);
         }
       }
@@ -977,7 +985,7 @@ struct KdaLds {
   float da[2][2][32][2 * LPG];  // [key tile][lane half][token][table pair * 4 + t]
 };
 
-template <typename T, int D, int LPG, int STEP>
+template <typename T, int D, int LPG, int STEP, bool SINGLE>
 __global__ void __launch_bounds__(512)
     lr_bwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                     const T* __restrict__ dO, const float* __restrict__ planes,
@@ -1199,7 +1207,7 @@ __global__ void __launch_bounds__(512)
           }
         }
         if (kvalid)
-          write_grad_row<T, D, NDH>(dvt, scrV, dV, ((size_t)bh * N + ktok) * D, h, first != 0,
+          write_grad_row<T, D, NDH, SINGLE>(dvt, scrV, dV, ((size_t)bh * N + ktok) * D, h, first != 0,
                                     last != 0, HALF * NDH);
       }
       __syncthreads();  // da of every table in LDS
@@ -1217,7 +1225,7 @@ __global__ void __launch_bounds__(512)
           floatx16 dx[NDH];
           features_dx<T, D, LPG, T, NDH>(da, RTs, rt_lds_width<LPG>(), c2, lane, dx, HALF * NDH);
           if (kvalid)
-            write_grad_row<T, D, NDH>(dx, scrK, dK, ((size_t)bh * N + ktok) * D, h, first != 0,
+            write_grad_row<T, D, NDH, SINGLE>(dx, scrK, dK, ((size_t)bh * N + ktok) * D, h, first != 0,
                                       last != 0, HALF * NDH);
         }
       }
@@ -1416,19 +1424,27 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
         if constexpr (SQ > 0 && SK > 0) {
           const int span_q = pb.causal ? pb.chunk : noncausal_span(pb.N, (int)BH, SQ);
           const int span_k = pb.causal ? pb.chunk : noncausal_span(pb.N, (int)BH, SK);
-          for (int g = 0; g < groups; ++g) {
+          // One feature group: the gradients go straight out (SINGLE); two: the
+          // first group's part is kept in fp32 scratch and added by the second.
+          auto launch_group = [&](auto sc, int g) {
+            constexpr bool SINGLE = decltype(sc)::value;
             const int first = g == 0, last = g == groups - 1;
-            ELSAA_LAUNCH("lr_bwd_q", (lr_bwd_q_kernel<T, D, LPG, SQ>),
+            ELSAA_LAUNCH("lr_bwd_q", (lr_bwd_q_kernel<T, D, LPG, SQ, SINGLE>),
                          dim3((pb.N + span_q - 1) / span_q, BH), dim3(512), 0, st, (const T*)Q,
                          (const T*)K, (const T*)V, (const T*)dO, planes_lr, A, z, re, rdd,
                          (const T*)dQp, scrQ, (T*)dQ, RT, pw, pb.H, pb.N, pb.L, span_q,
                          pb.levels, (int)pb.causal, pb.scale, pb.tau, g, first, last);
-            ELSAA_LAUNCH("lr_bwd_k", (lr_bwd_k_kernel<T, D, LPG, SK>),
+            ELSAA_LAUNCH("lr_bwd_k", (lr_bwd_k_kernel<T, D, LPG, SK, SINGLE>),
                          dim3((pb.N + span_k - 1) / span_k, BH), dim3(512), 0, st, (const T*)Q,
                          (const T*)K, (const T*)V, (const T*)dO, planes_lr, Gs, gzs, re, rdd,
                          (const T*)dKp, (const T*)dVp, scrK, scrV, (T*)dK, (T*)dV, RT, pw, pb.H,
                          pb.N, pb.L, span_k, pb.levels, (int)pb.causal, pb.scale, pb.tau, g,
                          first, last);
+          };
+          if (groups == 1) {
+            launch_group(std::true_type{}, 0);
+          } else {
+            for (int g = 0; g < groups; ++g) launch_group(std::false_type{}, g);
           }
         }
       };
