@@ -291,6 +291,17 @@ __global__ void __launch_bounds__(512)
         if constexpr (PLDS) Fq.compute(qx, PH, PLo, LDP, L, scale, tau, lane);
         else Fq.compute(qx, pl, L, scale, tau, lane);
       }
+      // The query's merged sparse output and log-sum-exp, in flight during the
+      // readout. Without the early key loads they are issued here, ahead of the
+      // key loads of the step (so that waiting for them does not wait for those);
+      // with them, after the barrier, where the registers are free.
+      const size_t k = (size_t)bh * N + min(qtok, N - 1);
+      DRow<T, NDH> osr;
+      float lse = 0.0f;
+      if constexpr (!EARLY) {
+        osr.load(Os + k * D, h, DT0);
+        lse = lse_s[k];
+      }
       // The next step's keys: issued as soon as this step's are consumed, so that
       // their latency hides behind the readout and the statistics update (past the
       // span: loads nothing that matters). With 16 tables the registers do not
@@ -299,13 +310,10 @@ __global__ void __launch_bounds__(512)
       __syncthreads();
 
       if (qwave && OWNER) {
-        // The query's merged sparse output and log-sum-exp (loads in flight during
-        // the readout).
-        const size_t k = (size_t)bh * N + min(qtok, N - 1);
-        DRow<T, NDH> osr;
-        osr.load(Os + k * D, h, DT0);
-        const float lse = lse_s[k];
-
+        if constexpr (EARLY) {
+          osr.load(Os + k * D, h, DT0);
+          lse = lse_s[k];
+        }
         // Low-rank readout: num^T = S^T phi(Q)^T over this half's channel tiles,
         // den = phi(Q) . z; then the causally masked part of the step.
         floatx16 num[NDH];
