@@ -39,7 +39,9 @@ constexpr int sums_step() {
 // z += phi(X)^T beta on MFMA (advance_stats, tiles spread over the 8 waves) with
 // the next step's rows already in flight. Eight waves keep each wave's registers
 // within half the file, so two waves share each SIMD.
-template <typename T, int D, int LP, int SUB>
+// WEIGHTED: alpha and beta are given (else both are 1), a compile-time choice so
+// that the weight loads are unconditional and never make the row loads wait.
+template <typename T, int D, int LP, int SUB, bool WEIGHTED>
 __global__ void __launch_bounds__(512) lr_sums_kernel(const T* __restrict__ X, const T* __restrict__ Y,
                                                       const float* __restrict__ alpha,
                                                       const float* __restrict__ beta,
@@ -77,17 +79,19 @@ __global__ void __launch_bounds__(512) lr_sums_kernel(const T* __restrict__ X, c
   // weight: their phi rows are stored as zero).
   typename M::frag xr[D / M::KSTEP];
   Vec8<T> yb[VIT];
-  float ya[VIT], bt = 0.0f;
+  float ya[VIT], bt = 1.0f;
+#pragma unroll
+  for (int i = 0; i < VIT; ++i) ya[i] = 1.0f;
   auto load_rows = [&](int s0) __attribute__((always_inline)) {
     if (w < QT) prefetch_row_frags<T, D>(Xh + (size_t)min(s0 + 32 * w + col, N - 1) * D, xr, h);
     if (ts >= 0) {
 #pragma unroll
       for (int i = 0; i < VIT; ++i) {
         const int it = ts + 256 * i, tc = min(s0 + it / VCH, N - 1);
-        if (it < SUB * VCH) yb[i].load(Yh + (size_t)tc * D + (it % VCH) * 8);
-        ya[i] = alpha ? alpha[(size_t)bh * N + tc] : 1.0f;
+        if ((SUB * VCH) % 256 == 0 || it < SUB * VCH) yb[i].load(Yh + (size_t)tc * D + (it % VCH) * 8);
+        if constexpr (WEIGHTED) ya[i] = alpha[(size_t)bh * N + tc];
       }
-      if (ts < SUB) bt = beta ? beta[(size_t)bh * N + min(s0 + ts, N - 1)] : 1.0f;
+      if constexpr (WEIGHTED) bt = beta[(size_t)bh * N + min(s0 + ts % SUB, N - 1)];
     }
   };
   __syncthreads();  // hyperplanes staged
@@ -177,9 +181,14 @@ void run_lr_sums(const Problem& pb, const void* X, const void* Y, const float* a
       with_LP(pb.L, [&](auto lc) {
         constexpr int LP = ELSAA_C(lc);
         constexpr int SUB = sums_step<T, D, LP>();
-        ELSAA_LAUNCH("lr_sums", (lr_sums_kernel<T, D, LP, SUB>), dim3(nt, BH), dim3(512), 0, st,
-                     (const T*)X, (const T*)Y, alpha, beta, planes, pb.H, pb.N, pb.L, TT,
-                     pb.scale, pb.tau, S, Z);
+        auto go = [&](auto wc) {
+          constexpr bool W = decltype(wc)::value;
+          ELSAA_LAUNCH("lr_sums", (lr_sums_kernel<T, D, LP, SUB, W>), dim3(nt, BH), dim3(512), 0, st,
+                       (const T*)X, (const T*)Y, alpha, beta, planes, pb.H, pb.N, pb.L, TT,
+                       pb.scale, pb.tau, S, Z);
+        };
+        if (alpha) go(std::true_type{});
+        else go(std::false_type{});
       });
     });
   });
