@@ -37,8 +37,10 @@ constexpr size_t sparse_fwd_lds() {
   return sizeof(T) * 2 * (size_t)KT * tile_ld<T>(D) + sizeof(int) * KT;
 }
 
+// bf16: two workgroups per CU (two waves per SIMD) is what the LDS allows; the
+// register budget is held to it.
 template <typename T, int D, int SB>
-__global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
+__global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 ? 2 : 1)
     sparse_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                       const int32_t* __restrict__ qperm, const int32_t* __restrict__ kperm, int N,
                       int causal, int levels, float scale, T* __restrict__ Opart,
@@ -105,8 +107,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = zero16();
   float mrun = -INFINITY, lrun = 0.0f;
-  const int nkt = leaf ? (w + 1) : KT / 32;  // causal leaf: key tiles up to the diagonal
-  for (int kt = 0; kt < nkt; ++kt) {
+  auto ktile = [&](int kt) __attribute__((always_inline)) {
     floatx16 sacc = zero16();
 #pragma unroll
     for (int ks = 0; ks < D / M::KSTEP; ++ks)
@@ -143,6 +144,14 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
       for (int dt = 0; dt < D / 32; ++dt)
         o[dt] = M::mma(tr_frag<T>(&Vs[0][0], LD, 32 * kt, 32 * dt, ks2, lane, true), pf, o[dt]);
     }
+  };
+  // Causal leaf: key tiles up to the diagonal; otherwise all of them, unrolled so
+  // that one tile's scores can be formed while the previous tile's softmax runs.
+  if (leaf) {
+    for (int kt = 0; kt <= w; ++kt) ktile(kt);
+  } else {
+#pragma unroll
+    for (int kt = 0; kt < KT / 32; ++kt) ktile(kt);
   }
 
   // The normalized output tile goes to LDS as rows (one per query, over the key
