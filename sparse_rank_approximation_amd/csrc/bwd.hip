@@ -1251,21 +1251,6 @@ namespace {
 int rt_stride(const Problem& pb);
 
 // Workgroups of a persistent launch: as many as fit on the device at once.
-int persistent_grid(const void* kern, int threads, int total) {
-  static int cus[64] = {0};
-  int dev = 0;
-  hipGetDevice(&dev);
-  int& n = cus[dev & 63];
-  if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    n = 256;
-  int per = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, threads, 0) != hipSuccess || per < 1)
-    per = 1;
-  long g = (long)n * per;
-  if (g >= total) return total;
-  return (int)(g >= 8 ? g & ~7L : g);  // a multiple of 8: each workgroup stays on one XCD's share
-}
-
 struct BwdLayout {
   size_t rows, dlam, parts, gsum, gstate, rt, scratch, total;
   int nblk;
@@ -1388,9 +1373,14 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
           constexpr int NT = 64 * (SB < 32 ? 1 : SB / 32);
           const int total = items * (int)BH;
           const int G = persistent_grid((const void*)sparse_bwd2_kernel<D, SB>, NT, total);
+          // The kernel reads an order entry for every row, leaves included; with no
+          // level (causal, N = s) the orders are empty and may be null, and the
+          // entry it reads (and discards) is then the first row term.
+          const int32_t* qp = qperm ? qperm : (const int32_t*)rc;
+          const int32_t* kp = kperm ? kperm : (const int32_t*)rc;
           ELSAA_LAUNCH("sparse_bwd", (sparse_bwd2_kernel<D, SB>), dim3(G), dim3(NT), 0, st,
-                       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, lse, rc, rD, qperm,
-                       kperm, pb.N, (int)pb.causal, pb.levels, pb.scale, items, total, (T*)dQp,
+                       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, lse, rc, rD, qp, kp,
+                       pb.N, (int)pb.causal, pb.levels, pb.scale, items, total, (T*)dQp,
                        (T*)dKp, (T*)dVp);
         } else if constexpr (sizeof(SbwdSmem<T, D, SB, 3>) <= kLdsBytes && SB <= 128) {
           ELSAA_LAUNCH("sparse_bwd", (sparse_bwd_kernel<T, D, SB, 3>), grid,

@@ -34,158 +34,174 @@ __device__ __forceinline__ int compact_future(int i, int N, int l) {
 template <typename T, int D, int SB>
 constexpr size_t sparse_fwd_lds() {
   constexpr int KT = SB < 32 ? 32 : SB;
-  return sizeof(T) * 2 * (size_t)KT * tile_ld<T>(D) + sizeof(int) * KT;
+  return sizeof(T) * 2 * (size_t)KT * tile_ld<T>(D) + sizeof(int) * 5 * KT;
 }
 
+// Persistent workgroups take the selected blocks g, g + G, g + 2G, ... (G = grid
+// size, a multiple of 8, so that all of a workgroup's blocks are its XCD's share
+// in the XCD-aware order). The order entries of the next block are loaded with
+// this block's rows and kept in LDS, so that a block's row gathers start at once.
 // bf16: two workgroups per CU (two waves per SIMD) is what the LDS allows; the
 // register budget is held to it.
 template <typename T, int D, int SB>
 __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 ? 2 : 1)
     sparse_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                       const int32_t* __restrict__ qperm, const int32_t* __restrict__ kperm, int N,
-                      int causal, int levels, float scale, T* __restrict__ Opart,
-                      float* __restrict__ Lpart) {
+                      int causal, int levels, float scale, int items, int total,
+                      T* __restrict__ Opart, float* __restrict__ Lpart) {
   typedef MF<T> M;
   constexpr int KT = SB < 32 ? 32 : SB;  // key rows held in LDS
   constexpr int LD = tile_ld<T>(D);        // row stride (elements) of the LDS tiles
+  constexpr int NT = 64 * (SB < 32 ? 1 : SB / 32);
   __shared__ T Ks[KT][LD];
   __shared__ T Vs[KT][LD];
-  __shared__ int kidx[KT];
+  __shared__ int kix[2][KT], qix[2][KT];  // key / query token of each row, by block parity
+  __shared__ int oslot[KT];               // output slot of each query row
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int w = wave_id();  // wave index, uniform (scalar) so that role branches stay uniform
   const size_t P = perm_stride(N, levels, causal);
   const size_t slots = partial_slots(N, levels, causal);
-
-  // Decode the work item (workgroup blockIdx.y * gridDim.x + blockIdx.x of the
-  // launch, which runs on XCD blockIdx.x % 8 as gridDim.x is a multiple of 8
-  // whenever the XCD-aware order applies).
   const int per_level = causal ? (N / 2) / SB : 0;
   const int nlev_items = causal ? levels * per_level : 0;
-  int item;
-  const int bh = xcd_item(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, per_level, levels, item);
-  const int32_t* qsrc = nullptr;
-  const int32_t* ksrc = nullptr;
-  int lev = -1, tok0 = 0;
-  bool leaf = false;
-  if (causal && item < nlev_items) {
-    lev = item / per_level;
-    const int b = item % per_level;
-    qsrc = qperm + (size_t)bh * P + (size_t)lev * (N / 2) + (size_t)b * SB;
-    ksrc = kperm + (size_t)bh * P + (size_t)lev * (N / 2) + (size_t)b * SB;
-  } else if (causal) {
-    leaf = true;
-    tok0 = (item - nlev_items) * SB;
-  } else {
-    qsrc = qperm + (size_t)bh * P + (size_t)item * SB;
-    ksrc = kperm + (size_t)bh * P + (size_t)item * SB;
-  }
+  const int G = gridDim.x;
 
-  for (int t = tid; t < KT; t += blockDim.x)
-    kidx[t] = t < SB ? (leaf ? tok0 + t : ksrc[t]) : -1;
-  // This wave's queries (one per lane column); the order entries of the keys and
-  // queries are read together.
-  const int qloc = 32 * w + col;
-  const bool qvalid = qloc < SB;
-  const int qi = qvalid ? (leaf ? tok0 + qloc : qsrc[qloc]) : 0;
-  __syncthreads();
-  // The query rows as MFMA operands (queries past the block read row 0, unused),
-  // then the block's K and V rows gathered into LDS (row-major, 16-byte
-  // row-contiguous copies; rows past the block are zero), all loads in flight
-  // together.
-  typename M::frag qf[D / M::KSTEP];
-  prefetch_row_frags<T, D>(Q + ((size_t)bh * N + qi) * D, qf, h);
-  {
-    T* const dst[2] = {&Ks[0][0], &Vs[0][0]};
-    const T* const src[2] = {K, V};
-    const float* const sc[2] = {nullptr, nullptr};
-    gather_rows<T, D, KT, 64 * (SB < 32 ? 1 : SB / 32), 2>(dst, LD, src, sc, kidx, (size_t)bh * N, tid);
-  }
-  __syncthreads();
-
-  floatx16 o[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) o[dt] = zero16();
-  float mrun = -INFINITY, lrun = 0.0f;
-  auto ktile = [&](int kt) __attribute__((always_inline)) {
-    floatx16 sacc = zero16();
-#pragma unroll
-    for (int ks = 0; ks < D / M::KSTEP; ++ks)
-      sacc = M::mma(row_frag<T>(&Ks[0][0], LD, 32 * kt, 0, ks, lane), qf[ks], sacc);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int kr = 32 * kt + acc_row(v, h);
-      const bool masked = kr >= SB || (leaf && kr > qloc);
-      sacc[v] = masked ? -INFINITY : sacc[v] * scale;
-      mx = fmaxf(mx, sacc[v]);
-    }
-    mx = max_halves(mx);
-    const float mnew = fmaxf(mrun, mx);
-    const float msub = mnew == -INFINITY ? 0.0f : mnew;
-    const float alpha = fast_exp(mrun - msub);
-    float ps = 0.0f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      sacc[v] = fast_exp(sacc[v] - msub);
-      ps += sacc[v];
-    }
-    ps = sum_halves(ps);
-    lrun = lrun * alpha + ps;
-    mrun = mnew;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
-#pragma unroll
-    for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
-      const typename M::frag pf = M::from_acc(sacc, ks2);
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        o[dt] = M::mma(tr_frag<T>(&Vs[0][0], LD, 32 * kt, 32 * dt, ks2, lane, true), pf, o[dt]);
+  // Order entries of row t of block g: both are read on every path (a leaf or a
+  // row past the block reads the head's first entry and discards it); the choice
+  // is made when they are stored, so that nothing waits for them early.
+  struct RowIdx {
+    int q, k, alt;  // alt: the token itself (causal leaf), -1 past the block, else -2
+  };
+  auto row_idx = [&](int g, int t) __attribute__((always_inline)) {
+    int it;
+    const int bh = xcd_item(g, items, per_level, levels, it);
+    const bool lf = causal && it >= nlev_items, past = t >= SB;
+    const size_t off = (size_t)bh * P + (lf || past ? (size_t)0
+                                         : causal ? (size_t)(it / per_level) * (N / 2) +
+                                                        (size_t)(it % per_level) * SB + t
+                                                  : (size_t)it * SB + t);
+    return RowIdx{qperm[off], kperm[off], past ? -1 : lf ? (it - nlev_items) * SB + t : -2};
+  };
+  auto put_idx = [&](int par, const RowIdx& r) __attribute__((always_inline)) {
+    if (tid < KT) {
+      qix[par][tid] = r.alt < -1 ? r.q : r.alt;
+      kix[par][tid] = r.alt < -1 ? r.k : r.alt;
     }
   };
-  // Causal leaf: key tiles up to the diagonal; otherwise all of them, unrolled so
-  // that one tile's scores can be formed while the previous tile's softmax runs.
-  if (leaf) {
-    for (int kt = 0; kt <= w; ++kt) ktile(kt);
-  } else {
-#pragma unroll
-    for (int kt = 0; kt < KT / 32; ++kt) ktile(kt);
-  }
 
-  // The normalized output tile goes to LDS as rows (one per query, over the key
-  // tile once every wave is done with it) and leaves with row-contiguous 16-byte
-  // stores to the queries' slots.
-  const size_t slot = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_future(qi, N, lev)
-                               : (size_t)qi;
+  int g = blockIdx.x;
+  if (g >= total) return;
+  put_idx(0, row_idx(g, tid % KT));
   __syncthreads();
-  {
-    const float inv = 1.0f / lrun;
+  const int qloc = 32 * w + col;  // this lane's query row
+  const bool qvalid = qloc < SB;
+  for (int par = 0; g < total; g += G, par ^= 1) {
+    int item;
+    const int bh = xcd_item(g, items, per_level, levels, item);
+    const bool leaf = causal && item >= nlev_items;
+    const int lev = causal && !leaf ? item / per_level : -1;
+    // The next block's order entries, then this block's query rows as MFMA
+    // operands (queries past the block read row 0, unused) and its K and V rows
+    // gathered into LDS (row-major, 16-byte row-contiguous copies; rows past the
+    // block are zero), all loads in flight together.
+    const RowIdx nx = row_idx(min(g + G, total - 1), tid % KT);
+    const int qi = qvalid ? qix[par][qloc] : 0;
+    typename M::frag qf[D / M::KSTEP];
+    prefetch_row_frags<T, D>(Q + ((size_t)bh * N + qi) * D, qf, h);
+    {
+      T* const dst[2] = {&Ks[0][0], &Vs[0][0]};
+      const T* const src[2] = {K, V};
+      const float* const sc[2] = {nullptr, nullptr};
+      gather_rows<T, D, KT, NT, 2>(dst, LD, src, sc, kix[par], (size_t)bh * N, tid);
+    }
+    __syncthreads();
+    put_idx(par ^ 1, nx);
+
+    floatx16 o[D / 32];
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < D / 32; ++dt) o[dt] = zero16();
+    float mrun = -INFINITY, lrun = 0.0f;
+    auto ktile = [&](int kt) __attribute__((always_inline)) {
+      floatx16 sacc = zero16();
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float x[4];
+      for (int ks = 0; ks < D / M::KSTEP; ++ks)
+        sacc = M::mma(row_frag<T>(&Ks[0][0], LD, 32 * kt, 0, ks, lane), qf[ks], sacc);
+      float mx = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = o[dt][4 * g + e] * inv;
-        store4(&Ks[qloc][32 * dt + 8 * g + 4 * h], x);
+      for (int v = 0; v < 16; ++v) {
+        const int kr = 32 * kt + acc_row(v, h);
+        const bool masked = kr >= SB || (leaf && kr > qloc);
+        sacc[v] = masked ? -INFINITY : sacc[v] * scale;
+        mx = fmaxf(mx, sacc[v]);
       }
-    if (h == 0) kidx[qloc] = qvalid ? (int)slot : -1;
-  }
-  if (qvalid && h == 0) Lpart[(size_t)bh * slots + slot] = mrun + __logf(lrun);
-  __syncthreads();
-  {
-    constexpr int CH = D / 8, NT = 64 * (SB < 32 ? 1 : SB / 32);
+      mx = max_halves(mx);
+      const float mnew = fmaxf(mrun, mx);
+      const float msub = mnew == -INFINITY ? 0.0f : mnew;
+      const float alpha = fast_exp(mrun - msub);
+      float ps = 0.0f;
 #pragma unroll
-    for (int i = 0; i < (KT * CH + NT - 1) / NT; ++i) {
-      const int piece = tid + NT * i, r = piece / CH, c8 = (piece % CH) * 8;
-      if (piece < KT * CH && kidx[r] >= 0) {
-        Vec8<T> x;
-        x.load(&Ks[r][c8]);
-        x.store(Opart + ((size_t)bh * slots + kidx[r]) * D + c8);
+      for (int v = 0; v < 16; ++v) {
+        sacc[v] = fast_exp(sacc[v] - msub);
+        ps += sacc[v];
+      }
+      ps = sum_halves(ps);
+      lrun = lrun * alpha + ps;
+      mrun = mnew;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+#pragma unroll
+      for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
+        const typename M::frag pf = M::from_acc(sacc, ks2);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          o[dt] = M::mma(tr_frag<T>(&Vs[0][0], LD, 32 * kt, 32 * dt, ks2, lane, true), pf, o[dt]);
+      }
+    };
+    // Causal leaf: key tiles up to the diagonal; otherwise all of them, unrolled so
+    // that one tile's scores can be formed while the previous tile's softmax runs.
+    if (leaf) {
+      for (int kt = 0; kt <= w; ++kt) ktile(kt);
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < KT / 32; ++kt) ktile(kt);
+    }
+
+    // The normalized output tile goes to LDS as rows (one per query, over the key
+    // tile once every wave is done with it) and leaves with row-contiguous 16-byte
+    // stores to the queries' slots.
+    const size_t slot = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_future(qi, N, lev)
+                                 : (size_t)qi;
+    __syncthreads();
+    {
+      const float inv = 1.0f / lrun;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = o[dt][4 * gg + e] * inv;
+          store4(&Ks[qloc][32 * dt + 8 * gg + 4 * h], x);
+        }
+      if (h == 0) oslot[qloc] = qvalid ? (int)slot : -1;
+    }
+    if (qvalid && h == 0) Lpart[(size_t)bh * slots + slot] = mrun + __logf(lrun);
+    __syncthreads();
+    {
+      constexpr int CH = D / 8;
+#pragma unroll
+      for (int i = 0; i < (KT * CH + NT - 1) / NT; ++i) {
+        const int piece = tid + NT * i, r = piece / CH, c8 = (piece % CH) * 8;
+        if (piece < KT * CH && oslot[r] >= 0) {
+          Vec8<T> x;
+          x.load(&Ks[r][c8]);
+          x.store(Opart + ((size_t)bh * slots + oslot[r]) * D + c8);
+        }
       }
     }
+    __syncthreads();  // Ks and oslot free for the next block
   }
 }
 
@@ -448,7 +464,7 @@ size_t fwd_lds_need(const Problem& pb) {
     });
   });
   const size_t kt = pb.s < 32 ? 32 : pb.s;
-  const size_t sparse = (size_t)pb.elem * 2 * kt * (pb.d + (pb.bf16 ? 24 : 8)) + 4 * kt;
+  const size_t sparse = (size_t)pb.elem * 2 * kt * (pb.d + (pb.bf16 ? 24 : 8)) + 4 * 5 * kt;
   return need > sparse ? need : sparse;
 }
 
@@ -469,10 +485,19 @@ void launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
       auto run = [&](auto sc) {
         constexpr int SB = ELSAA_C(sc);
         if constexpr (sparse_fwd_lds<T, D, SB>() <= kLdsBytes)
-        ELSAA_LAUNCH("sparse_fwd", (sparse_fwd_kernel<T, D, SB>), dim3(items, BH),
-                           dim3(64 * (SB < 32 ? 1 : SB / 32)), 0, st, (const T*)Q, (const T*)K,
-                           (const T*)V, qperm, kperm, pb.N, (int)pb.causal, pb.levels, pb.scale,
-                           (T*)Opart, Lpart);
+        {
+          constexpr int NT = 64 * (SB < 32 ? 1 : SB / 32);
+          const int total = items * BH;
+          const int G = persistent_grid((const void*)sparse_fwd_kernel<T, D, SB>, NT, total);
+          // The kernel reads an order entry for every row, leaves included; with no
+          // level (causal, N = s) the orders are empty and may be null, and the
+          // entry it reads (and discards) is then the first word of the workspace.
+          const int32_t* qp = qperm ? qperm : (const int32_t*)Lpart;
+          const int32_t* kp = kperm ? kperm : (const int32_t*)Lpart;
+          ELSAA_LAUNCH("sparse_fwd", (sparse_fwd_kernel<T, D, SB>), dim3(G), dim3(NT), 0, st,
+                       (const T*)Q, (const T*)K, (const T*)V, qp, kp, pb.N, (int)pb.causal,
+                       pb.levels, pb.scale, items, total, (T*)Opart, Lpart);
+        }
       };
       switch (pb.s) {
         case 16: run(std::integral_constant<int, 16>{}); break;

@@ -98,6 +98,24 @@ __host__ __device__ inline int xcd_item(int g, int items, int per_level, int lev
 // Tokens per workgroup of the low-rank walks when not causal: the statistics are
 // the whole sequence's and stay fixed, so a workgroup walks several steps after
 // loading them once; as many steps as keep at least 512 workgroups in the launch.
+// Grid of a persistent launch: the workgroups that fit on the device at once
+// (at most total), a multiple of 8 when below total so that workgroup g and its
+// later items g + G, g + 2G, ... all run on XCD g mod 8.
+inline int persistent_grid(const void* kern, int threads, int total) {
+  static int cus[64] = {0};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  int& n = cus[dev & 63];
+  if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    n = 256;
+  int per = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, threads, 0) != hipSuccess || per < 1)
+    per = 1;
+  long g = (long)n * per;
+  if (g >= total) return total;
+  return (int)(g >= 8 ? g & ~7L : g);
+}
+
 inline int noncausal_span(int N, int BH, int step) {
   const int steps = (N + step - 1) / step;
   int per = steps * BH / 512;

@@ -80,6 +80,9 @@ CASES = {
                                            True, False),
     # degenerate causal: N == block, no off-diagonal level (dense causal softmax)
     "causal_single_block_f32": (wl("d", 1, 1, 64, 32, "f32", True, 64, 32, chunk=64), False, False),
+    # the same in bf16 (empty orders, passed as null pointers), two heads
+    "causal_single_block_bf16": (wl("e", 1, 2, 128, 64, "bf16", True, 128, 32, chunk=128),
+                                 True, True),
     # odd table count (padded to 4 tables on the GPU), bf16, d 32
     "tables3_bf16_causal": (wl("t", 1, 1, 512, 32, "bf16", True, 64, 48, chunk=256), True, True),
     # maximum block 256 and r 256 at d 128, causal bf16
