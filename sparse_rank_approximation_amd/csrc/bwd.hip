@@ -37,13 +37,16 @@ namespace elsaa {
 
 namespace {
 
+// Compact index of query i within level l's future halves, and of key j within its
+// past halves. N is a power of two whenever there are levels, so the segment
+// length n is one and masks and shifts replace divisions.
 __device__ __forceinline__ int compact_future_b(int i, int N, int l) {
-  const int n = N >> l, half = n >> 1;
-  return (i / n) * half + (i % n) - half;
+  const int n = N >> l;
+  return ((i & -n) >> 1) + (i & (n - 1)) - (n >> 1);
 }
 __device__ __forceinline__ int compact_past(int j, int N, int l) {
   const int n = N >> l;
-  return (j / n) * (n >> 1) + (j % n);
+  return ((j & -n) >> 1) + (j & (n - 1));
 }
 
 // Writes the low-rank part of one gradient row held in the accumulator layout
@@ -725,27 +728,41 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
     __syncthreads();
     {
       const size_t hb = (size_t)bh * slots;
+      // Two row pieces at a time: their six LDS reads are issued before any of
+      // their stores, so that one wait covers them.
+      constexpr int PB = GIT % 2 == 0 ? 2 : 1;
 #pragma unroll
-      for (int i = 0; i < GIT; ++i) {
-        const int piece = tid + NT * i, rr = piece / CH, c8 = (piece % CH) * 8;
-        const int jk = sm.kidx[rr], iq = sm.qidx[rr];
-        // Every row of a block of 32 or more is valid: the stores are then issued
-        // on every path, which keeps the waits for the prefetches exact.
-        if (SB >= 32 || jk >= 0) {
-          const size_t sl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_past(jk, N, lev)
-                                     : (size_t)jk;
-          Vec8<T> a, b2;
-          a.load(&sm.Qs[rr][c8]);
-          b2.load(&sm.Os[rr][c8]);
-          a.store(dVp + (hb + sl) * D + c8);
-          b2.store(dKp + (hb + sl) * D + c8);
+      for (int i0 = 0; i0 < GIT; i0 += PB) {
+        Vec8<T> a[PB], b2[PB], c[PB];
+        int jk[PB], iq[PB], rr[PB], c8[PB];
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+          const int piece = tid + NT * (i0 + j);
+          rr[j] = piece / CH;
+          c8[j] = (piece % CH) * 8;
+          jk[j] = sm.kidx[rr[j]];
+          iq[j] = sm.qidx[rr[j]];
+          a[j].load(&sm.Qs[rr[j]][c8[j]]);
+          b2[j].load(&sm.Os[rr[j]][c8[j]]);
+          c[j].load(&sm.Ks[rr[j]][c8[j]]);
         }
-        if (SB >= 32 || iq >= 0) {
-          const size_t sl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_future_b(iq, N, lev)
-                                     : (size_t)iq;
-          Vec8<T> a;
-          a.load(&sm.Ks[rr][c8]);
-          a.store(dQp + (hb + sl) * D + c8);
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+          // Every row of a block of 32 or more is valid: the stores are then
+          // issued on every path, which keeps the waits for the prefetches exact.
+          if (SB >= 32 || jk[j] >= 0) {
+            const size_t sl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) +
+                                             compact_past(jk[j], N, lev)
+                                       : (size_t)jk[j];
+            a[j].store(dVp + (hb + sl) * D + c8[j]);
+            b2[j].store(dKp + (hb + sl) * D + c8[j]);
+          }
+          if (SB >= 32 || iq[j] >= 0) {
+            const size_t sl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) +
+                                             compact_future_b(iq[j], N, lev)
+                                       : (size_t)iq[j];
+            c[j].store(dQp + (hb + sl) * D + c8[j]);
+          }
         }
       }
     }

@@ -25,10 +25,12 @@
 
 namespace elsaa {
 
-// Compact index of query i within level l's future halves (i must be in one).
+// Compact index of query i within level l's future halves (i must be in one). N is
+// a power of two whenever there are levels, so the segment length n is one and
+// masks and shifts replace divisions.
 __device__ __forceinline__ int compact_future(int i, int N, int l) {
-  const int n = N >> l, half = n >> 1;
-  return (i / n) * half + (i % n) - half;
+  const int n = N >> l;
+  return ((i & -n) >> 1) + (i & (n - 1)) - (n >> 1);
 }
 
 template <typename T, int D, int SB>
