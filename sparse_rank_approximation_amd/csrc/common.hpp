@@ -431,9 +431,10 @@ struct SlotWalk {
   __device__ __forceinline__ bool member(int lv) const {
     return (((tok >> (logN - 1 - lv)) & 1) != 0) == QUERY;
   }
+  // (N is a power of two whenever there are levels: masks instead of divisions.)
   __device__ __forceinline__ size_t slot(int lv) const {
-    const int n = N >> lv, half = n >> 1;
-    const int c = QUERY ? (tok / n) * half + (tok % n) - half : (tok / n) * half + (tok % n);
+    const int n = N >> lv;
+    const int c = ((tok & -n) >> 1) + (tok & (n - 1)) - (QUERY ? n >> 1 : 0);
     return (size_t)N + (size_t)lv * (N / 2) + c;
   }
   // Fills sl[0 .. n) with the next n <= KB slots; returns n (0 when done).

@@ -192,15 +192,23 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 ?
     if (qvalid && h == 0) Lpart[(size_t)bh * slots + slot] = mrun + __logf(lrun);
     __syncthreads();
     {
-      constexpr int CH = D / 8;
+      // All of the thread's LDS reads are issued before its stores (one wait);
+      // rows of a block of 32 or more are all valid, so their stores are
+      // unconditional.
+      constexpr int CH = D / 8, PIT = (KT * CH + NT - 1) / NT;
+      Vec8<T> x[PIT];
+      int os[PIT];
 #pragma unroll
-      for (int i = 0; i < (KT * CH + NT - 1) / NT; ++i) {
-        const int piece = tid + NT * i, r = piece / CH, c8 = (piece % CH) * 8;
-        if (piece < KT * CH && oslot[r] >= 0) {
-          Vec8<T> x;
-          x.load(&Ks[r][c8]);
-          x.store(Opart + ((size_t)bh * slots + oslot[r]) * D + c8);
-        }
+      for (int i = 0; i < PIT; ++i) {
+        const int piece = tid + NT * i, r = min(piece / CH, KT - 1), c8 = (piece % CH) * 8;
+        x[i].load(&Ks[r][c8]);
+        os[i] = piece < KT * CH ? oslot[r] : -1;
+      }
+#pragma unroll
+      for (int i = 0; i < PIT; ++i) {
+        const int piece = tid + NT * i, c8 = (piece % CH) * 8;
+        if ((SB >= 32 && (KT * CH) % NT == 0) || os[i] >= 0)
+          x[i].store(Opart + ((size_t)bh * slots + os[i]) * D + c8);
       }
     }
     __syncthreads();  // Ks and oslot free for the next block
