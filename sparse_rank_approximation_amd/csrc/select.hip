@@ -13,23 +13,73 @@ __global__ void __launch_bounds__(256) planes_f64_kernel(const float* __restrict
   if (i < n) out[i] = (double)planes[i];
 }
 
-// One thread per (token, tensor): bit b of the code is the sign of the fp64
-// fused-multiply-add chain over the row against hyperplane b, in index order
-// from +0.0. Correctly rounded FMA in a fixed order makes every bit
-// reproducible by any other correctly rounded implementation. The workgroup's
+// Bits P0 .. P0 + NB - 1 of the code of the row at xr (LDS, CH pieces of 16 bytes):
+// bit b is the sign of the fp64 fused-multiply-add chain over the row against
+// hyperplane b, in index order from +0.0. The hyperplanes are the same for every
+// lane and are read with scalar loads (operands in scalar registers).
+template <typename T, int D, int P0, int NB>
+__device__ __forceinline__ unsigned hash_bits(const uint4* xr, const double* pl) {
+  constexpr int CH = D * (int)sizeof(T) / 16, EPP = 16 / (int)sizeof(T);
+  if constexpr (NB == 0) {
+    return 0u;
+  } else {
+    double acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = 0.0;
+    for (int c = 0; c < CH; ++c) {
+      const uint4 v = xr[c];
+      float xv[EPP];
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xv[2 * e] = __uint_as_float(w4[e] << 16);
+          xv[2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+        }
+      } else {
+        xv[0] = __uint_as_float(v.x);
+        xv[1] = __uint_as_float(v.y);
+        xv[2] = __uint_as_float(v.z);
+        xv[3] = __uint_as_float(v.w);
+      }
+      double xd[EPP];
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) xd[e] = (double)xv[e];
+      double pv[NB][EPP];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int e = 0; e < EPP; ++e) pv[b][e] = pl[(P0 + b) * D + c * EPP + e];
+#pragma unroll
+      for (int e = 0; e < EPP; ++e)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b] = __builtin_fma(xd[e], pv[b][e], acc[b]);
+    }
+    unsigned code = 0;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (acc[b] > 0.0) code |= 1u << (P0 + b);
+    return code;
+  }
+}
+
+// One row per (token, tensor) and two threads per row: waves 0-1 form the first
+// half of the code's bits and waves 2-3 the rest, each bit its own chain in the
+// order above (correctly rounded FMA in a fixed order makes every bit
+// reproducible by any other correctly rounded implementation). The workgroup's
 // 128 rows are first copied into LDS with 16-byte row-contiguous loads (row
 // stride padded by 16 bytes so that each thread's 16-byte reads of its own row
-// are free of bank conflicts); the fp64 hyperplanes are the same for every lane
-// and are read with scalar loads (operands in scalar registers).
+// are free of bank conflicts).
 template <typename T, int D, int BITS>
-__global__ void __launch_bounds__(128) hash_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ void __launch_bounds__(256) hash_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                    const double* __restrict__ planes,
                                                    uint16_t* __restrict__ qc,
                                                    uint16_t* __restrict__ kc, int H, int N) {
-  constexpr int ROWS = 128, CH = D * (int)sizeof(T) / 16, EPP = 16 / (int)sizeof(T);
+  constexpr int ROWS = 128, CH = D * (int)sizeof(T) / 16;
   constexpr int RW = D * (int)sizeof(T) / 4 + 4;  // row stride in dwords
-  constexpr int IT = ROWS * CH / 128;
+  constexpr int IT = ROWS * CH / 256, B0 = (BITS + 1) / 2;
   __shared__ uint4 xs[ROWS * RW / 4];
+  __shared__ unsigned hib[ROWS];
   const int bh = blockIdx.y, h = bh % H, tid = threadIdx.x;
   const int tok0 = blockIdx.x * ROWS;
   const T* X = (blockIdx.z ? K : Q) + (size_t)bh * N * D;
@@ -38,56 +88,24 @@ __global__ void __launch_bounds__(128) hash_kernel(const T* __restrict__ Q, cons
     uint4 buf[IT];
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
-      const int p = tid + ROWS * i, r = p / CH, c = p % CH;
+      const int p = tid + 256 * i, r = p / CH, c = p % CH;
       const int tok = min(tok0 + r, N - 1);
       buf[i] = reinterpret_cast<const uint4*>(X + (size_t)tok * D)[c];
     }
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
-      const int p = tid + ROWS * i, r = p / CH, c = p % CH;
+      const int p = tid + 256 * i, r = p / CH, c = p % CH;
       xs[r * (RW / 4) + c] = buf[i];
     }
   }
   __syncthreads();
-  const int t = tok0 + tid;
-  if (t >= N) return;
-  double acc[BITS];
-#pragma unroll
-  for (int b = 0; b < BITS; ++b) acc[b] = 0.0;
-  for (int c = 0; c < CH; ++c) {
-    const uint4 v = xs[tid * (RW / 4) + c];
-    float xv[EPP];
-    if constexpr (sizeof(T) == 2) {
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        xv[2 * e] = __uint_as_float(w4[e] << 16);
-        xv[2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
-      }
-    } else {
-      xv[0] = __uint_as_float(v.x);
-      xv[1] = __uint_as_float(v.y);
-      xv[2] = __uint_as_float(v.z);
-      xv[3] = __uint_as_float(v.w);
-    }
-    double xd[EPP];
-#pragma unroll
-    for (int e = 0; e < EPP; ++e) xd[e] = (double)xv[e];
-    double pv[BITS][EPP];
-#pragma unroll
-    for (int b = 0; b < BITS; ++b)
-#pragma unroll
-      for (int e = 0; e < EPP; ++e) pv[b][e] = pl[b * D + c * EPP + e];
-#pragma unroll
-    for (int e = 0; e < EPP; ++e)
-#pragma unroll
-      for (int b = 0; b < BITS; ++b) acc[b] = __builtin_fma(xd[e], pv[b][e], acc[b]);
-  }
-  unsigned code = 0;
-#pragma unroll
-  for (int b = 0; b < BITS; ++b)
-    if (acc[b] > 0.0) code |= 1u << b;
-  (blockIdx.z ? kc : qc)[(size_t)bh * N + t] = (uint16_t)code;
+  const int row = tid & (ROWS - 1);
+  const uint4* xr = &xs[row * (RW / 4)];
+  if (tid >= ROWS) hib[row] = hash_bits<T, D, B0, BITS - B0>(xr, pl);  // waves 2-3
+  const unsigned lo = tid < ROWS ? hash_bits<T, D, 0, B0>(xr, pl) : 0u;
+  __syncthreads();
+  const int t = tok0 + row;
+  if (tid < ROWS && t < N) (blockIdx.z ? kc : qc)[(size_t)bh * N + t] = (uint16_t)(lo | hib[row]);
 }
 
 // Stable counting sort of one segment half by Gray rank (ties by token index).
@@ -200,7 +218,7 @@ void launch_select(const Problem& pb, const void* Q, const void* K, const float*
       constexpr int D = ELSAA_C(dc);
       auto run = [&](auto bc) {
         constexpr int BITS = ELSAA_C(bc);
-        ELSAA_LAUNCH("hash", (hash_kernel<T, D, BITS>), hg, dim3(128), 0, st, (const T*)Q,
+        ELSAA_LAUNCH("hash", (hash_kernel<T, D, BITS>), hg, dim3(256), 0, st, (const T*)Q,
                      (const T*)K, (const double*)pld, qc, kc, pb.H, pb.N);
       };
       switch (pb.hash_bits) {
