@@ -53,13 +53,17 @@ __device__ __forceinline__ int compact_past(int j, int N, int l) {
 // (lane = token): lr + the fp32 running sum of earlier feature groups (unless
 // first), stored as T (last group) or as the fp32 running sum. The sparse partial
 // rows are added afterwards (combine_kernel). SINGLE: one feature group, stored
-// straight to out (no running-sum load, so nothing here waits for memory).
+// straight to out (no running-sum load, so nothing here waits for memory; the
+// two lanes of a token must be active together).
 template <typename T, int D, int NDT = D / 32, bool SINGLE = false>
 __device__ __forceinline__ void write_grad_row(const floatx16 (&lr)[NDT], float* scratch, T* out,
                                                size_t row, int h, bool first, bool last,
                                                int dt0 = 0) {
   if constexpr (SINGLE) {
-    first = last = true;
+    // One feature group: straight to out, 16 bytes per lane.
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) store_tile_row(out + row + 32 * (dt0 + dt), lr[dt], h);
+    return;
   }
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)

@@ -203,6 +203,36 @@ __device__ __forceinline__ void store4(float* p, const float (&x)[4]) {
   for (int e = 0; e < 4; ++e) v[e] = x[e];
   *reinterpret_cast<floatx4*>(p) = v;
 }
+// Stores one 32-channel tile of a row held in the MFMA accumulator layout (lane
+// half h holds channels 8 g + 4 h .. 8 g + 4 h + 3 of group g = 0..3 as x[4 g ..
+// 4 g + 3]) to dst (the tile's first channel). bf16: the lane halves trade 8-byte
+// pieces (one v_permlane32_swap per dword) so that each lane stores 16 contiguous
+// bytes, half 0 the channels 16 m .. 16 m + 7 and half 1 the next eight (m = 0, 1);
+// the two lanes of a pair must be active together. fp32: four 16-byte stores.
+template <typename X>
+__device__ __forceinline__ void store_tile_row(__bf16* dst, const X& x, int h) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    bf16x4 a, b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = (__bf16)x[8 * m + e];
+      b[e] = (__bf16)x[8 * m + 4 + e];
+    }
+    const uint2 au = *reinterpret_cast<const uint2*>(&a);
+    const uint2 bu = *reinterpret_cast<const uint2*>(&b);
+    const auto s0 = __builtin_amdgcn_permlane32_swap(au.x, bu.x, false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(au.y, bu.y, false, false);
+    *reinterpret_cast<uint4*>(dst + 16 * m + 8 * h) = uint4{s0[0], s1[0], s0[1], s1[1]};
+  }
+}
+template <typename X>
+__device__ __forceinline__ void store_tile_row(float* dst, const X& x, int h) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    *reinterpret_cast<floatx4*>(dst + 8 * g + 4 * h) =
+        floatx4{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
+}
 __device__ __forceinline__ void load8(const __bf16* p, float (&x)[8]) {
   const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
 #pragma unroll

@@ -403,19 +403,19 @@ __global__ void __launch_bounds__(512)
           const float g2 = glr ? glr[k] : 1.0f;
           const float dinv = 1.0f / den;
 #pragma unroll
-          for (int i = 0; i < NDH; ++i)
+          for (int i = 0; i < NDH; ++i) {
+            float xo[16], xl[16];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const size_t o = k * D + 32 * (DT0 + i) + 8 * g + 4 * h;
-              float xo[4], xl[4];
+            for (int g = 0; g < 4; ++g)
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                xl[e] = num[i][4 * g + e] * dinv;
-                xo[e] = g1 * m * osr.x[i][g][e] + g2 * xl[e];
+                xl[4 * g + e] = num[i][4 * g + e] * dinv;
+                xo[4 * g + e] = g1 * m * osr.x[i][g][e] + g2 * xl[4 * g + e];
               }
-              store4(O + o, xo);
-              store4(Olr + o, xl);
-            }
+            // (qvalid is the same for the two lanes of a token)
+            store_tile_row(O + k * D + 32 * (DT0 + i), xo, h);
+            store_tile_row(Olr + k * D + 32 * (DT0 + i), xl, h);
+          }
           if (HALF == 0 && h == 0) dlr_out[k] = den;
         }
       }
