@@ -117,6 +117,7 @@ __global__ void __launch_bounds__(256) hash_kernel(const T* __restrict__ Q, cons
 // ordered by lane), which keeps the order stable without atomics on positions.
 constexpr int kSortWaves = 4;
 
+template <bool STAGED>
 __global__ void __launch_bounds__(256) sort_kernel(const uint16_t* __restrict__ qc,
                                                    const uint16_t* __restrict__ kc,
                                                    int32_t* __restrict__ qperm,
@@ -126,6 +127,10 @@ __global__ void __launch_bounds__(256) sort_kernel(const uint16_t* __restrict__ 
   const int nbins = 1 << bits;
   int* cnt = smem;                               // [kSortWaves][nbins]
   int* part = smem + kSortWaves * nbins;         // [kSortWaves] wave totals
+  // STAGED: the segment's codes are first copied into LDS (after 256 words for
+  // the wave totals) with 16-byte loads all in flight, and both passes read them
+  // there.
+  uint16_t* cs = reinterpret_cast<uint16_t*>(part + 256);
   const int bh = blockIdx.y, isk = blockIdx.z;
   int base, count;
   size_t out_off;
@@ -147,10 +152,17 @@ __global__ void __launch_bounds__(256) sort_kernel(const uint16_t* __restrict__ 
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   for (int i = tid; i < kSortWaves * nbins; i += blockDim.x) cnt[i] = 0;
+  if constexpr (STAGED)  // count and base are multiples of 8
+    for (int i = tid; i < count / 8; i += blockDim.x)
+      reinterpret_cast<uint4*>(cs)[i] = reinterpret_cast<const uint4*>(code + base)[i];
   __syncthreads();
+  auto code_at = [&](int t) -> unsigned {
+    if constexpr (STAGED) return cs[t];
+    else return code[base + t];
+  };
   const int per = (count + kSortWaves - 1) / kSortWaves;
   const int beg = min(count, w * per), end = min(count, beg + per);
-  for (int t = beg + lane; t < end; t += 64) atomicAdd(&cnt[w * nbins + gray_rank(code[base + t])], 1);
+  for (int t = beg + lane; t < end; t += 64) atomicAdd(&cnt[w * nbins + gray_rank(code_at(t))], 1);
   __syncthreads();
 
   // Exclusive scan of cnt in (bin, wave) order, written back as start offsets.
@@ -182,7 +194,7 @@ __global__ void __launch_bounds__(256) sort_kernel(const uint16_t* __restrict__ 
   for (int t0 = beg; t0 < end; t0 += 64) {
     const int t = t0 + lane;
     const bool valid = t < end;
-    const unsigned key = valid ? gray_rank(code[base + t]) : 0u;
+    const unsigned key = valid ? gray_rank(code_at(t)) : 0u;
     unsigned long long eq = __ballot(valid);
     for (int b = 0; b < bits; ++b) {
       const unsigned long long m = __ballot(valid && ((key >> b) & 1u));
@@ -239,9 +251,15 @@ void launch_select(const Problem& pb, const void* Q, const void* K, const float*
   });
   const int nseg = pb.causal ? (1 << pb.levels) - 1 : 1;
   const size_t lds = sizeof(int) * ((size_t)kSortWaves * (1 << pb.hash_bits) + 256);
-  if (nseg > 0)
-    ELSAA_LAUNCH("sort", sort_kernel, dim3(nseg, BH, 2), dim3(256), lds, st, qc, kc, qperm, kperm,
-                       pb.N, (int)pb.causal, pb.levels, pb.hash_bits);
+  const size_t seg_codes = sizeof(uint16_t) * (size_t)(pb.causal ? pb.N / 2 : pb.N);
+  if (nseg > 0) {
+    if (lds + seg_codes <= 64 * 1024)
+      ELSAA_LAUNCH("sort", sort_kernel<true>, dim3(nseg, BH, 2), dim3(256), lds + seg_codes, st, qc,
+                   kc, qperm, kperm, pb.N, (int)pb.causal, pb.levels, pb.hash_bits);
+    else
+      ELSAA_LAUNCH("sort", sort_kernel<false>, dim3(nseg, BH, 2), dim3(256), lds, st, qc, kc, qperm,
+                   kperm, pb.N, (int)pb.causal, pb.levels, pb.hash_bits);
+  }
 }
 
 }  // namespace elsaa
