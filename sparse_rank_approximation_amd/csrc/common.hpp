@@ -409,41 +409,63 @@ __device__ __forceinline__ void prefetch_row_frags(const T* x,
   for (int ks = 0; ks < D / M::KSTEP; ++ks) f[ks] = M::load(x + ks * M::KSTEP + M::KPL * h);
 }
 
-// 4 consecutive elements in registers.
-template <typename T>
-struct Raw4;
-template <>
-struct Raw4<__bf16> {
-  bf16x4 v;
-  __device__ __forceinline__ void load(const __bf16* p) { v = *reinterpret_cast<const bf16x4*>(p); }
-  __device__ __forceinline__ float operator[](int e) const { return (float)v[e]; }
-};
-template <>
-struct Raw4<float> {
-  floatx4 v;
-  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const floatx4*>(p); }
-  __device__ __forceinline__ float operator[](int e) const { return v[e]; }
-};
-
 // The part of one token row that a lane holds in the accumulator layout of
 // D x 32 tiles whose columns are tokens: channels 32 dt + 8 g + 4 h + e for the
-// NDT tiles dt0 .. dt0 + NDT - 1 (dt0 = 0 unless given).
+// NDT tiles dt0 .. dt0 + NDT - 1 (dt0 = 0 unless given). load() issues the loads;
+// unpack() (once they are needed) gives the values as x[dt][g][e]. bf16: each lane
+// loads 16 contiguous bytes (half 0 the channels 16 m .. 16 m + 7 of a tile, half
+// 1 the next eight, m = 0, 1) and unpack() trades 8-byte pieces between the lane
+// halves (v_permlane32_swap), so the two lanes of a token must unpack together.
 template <typename T, int NDT>
-struct DRow {
-  Raw4<T> x[NDT][4];
-  __device__ __forceinline__ void load(const T* row, int h, int dt0 = 0) {
+struct DRow;
+template <int NDT>
+struct DRow<__bf16, NDT> {
+  uint4 raw[NDT][2];
+  __device__ __forceinline__ void load(const __bf16* row, int h, int dt0 = 0) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) x[dt][g].load(row + 32 * (dt0 + dt) + 8 * g + 4 * h);
+      for (int m = 0; m < 2; ++m)
+        raw[dt][m] = *reinterpret_cast<const uint4*>(row + 32 * (dt0 + dt) + 16 * m + 8 * h);
   }
-  __device__ __forceinline__ void add_to(float (&acc)[NDT][4][4], float w) const {
+  __device__ __forceinline__ void unpack(float (&x)[NDT][4][4]) const {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        // half 0 holds (A0, A1), half 1 (B0, B1); groups 2 m and 2 m + 1 want
+        // (A0 | A1) and (B0 | B1) split by half.
+        const uint4 u = raw[dt][m];
+        const auto s0 = __builtin_amdgcn_permlane32_swap(u.x, u.z, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(u.y, u.w, false, false);
+        const uint32_t g0[2] = {s0[0], s1[0]}, g1[2] = {s0[1], s1[1]};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          x[dt][2 * m][2 * e] = __uint_as_float(g0[e] << 16);
+          x[dt][2 * m][2 * e + 1] = __uint_as_float(g0[e] & 0xffff0000u);
+          x[dt][2 * m + 1][2 * e] = __uint_as_float(g1[e] << 16);
+          x[dt][2 * m + 1][2 * e + 1] = __uint_as_float(g1[e] & 0xffff0000u);
+        }
+      }
+  }
+};
+template <int NDT>
+struct DRow<float, NDT> {
+  floatx4 raw[NDT][4];
+  __device__ __forceinline__ void load(const float* row, int h, int dt0 = 0) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        raw[dt][g] = *reinterpret_cast<const floatx4*>(row + 32 * (dt0 + dt) + 8 * g + 4 * h);
+  }
+  __device__ __forceinline__ void unpack(float (&x)[NDT][4][4]) const {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[dt][g][e] += w * x[dt][g][e];
+        for (int e = 0; e < 4; ++e) x[dt][g][e] = raw[dt][g][e];
   }
 };
 

@@ -402,6 +402,8 @@ __global__ void __launch_bounds__(512)
           const float g1 = gs ? gs[k] : 1.0f;
           const float g2 = glr ? glr[k] : 1.0f;
           const float dinv = 1.0f / den;
+          float os[NDH][4][4];
+          osr.unpack(os);
 #pragma unroll
           for (int i = 0; i < NDH; ++i) {
             float xo[16], xl[16];
@@ -410,7 +412,7 @@ __global__ void __launch_bounds__(512)
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 xl[4 * g + e] = num[i][4 * g + e] * dinv;
-                xo[4 * g + e] = g1 * m * osr.x[i][g][e] + g2 * xl[4 * g + e];
+                xo[4 * g + e] = g1 * m * os[i][g][e] + g2 * xl[4 * g + e];
               }
             // (qvalid is the same for the two lanes of a token)
             store_tile_row(O + k * D + 32 * (DT0 + i), xo, h);
