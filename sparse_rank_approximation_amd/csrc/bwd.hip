@@ -364,18 +364,16 @@ __global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
               acc[dt] = M::mma(tr_frag<T>(X, LD, 32 * qt, 32 * dt, ks2, lane, true), pf, acc[dt]);
           }
         }
-        if (kvalid) {
+        if (kvalid) {  // (the same for the two lanes of a key)
           T* dst = (pass == 0 ? dVp : dKp) + ((size_t)bh * slots + ksl) * D;
           const float f = pass == 0 ? 1.0f : scale;
 #pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt)
+          for (int dt = 0; dt < D / 32; ++dt) {
+            float x[16];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              float x[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) x[e] = acc[dt][4 * g + e] * f;
-              store4(dst + 32 * dt + 8 * g + 4 * h, x);
-            }
+            for (int v = 0; v < 16; ++v) x[v] = acc[dt][v] * f;
+            store_tile_row(dst + 32 * dt, x, h);
+          }
         }
       }
     }
@@ -436,16 +434,14 @@ __global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
       if (qvalid) {
         const size_t sl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_future_b(iq, N, lev)
                                    : (size_t)iq;
-        T* dst = dQp + ((size_t)bh * slots + sl) * D;
+        T* dst = dQp + ((size_t)bh * slots + sl) * D;  // (qvalid: the same for a query's two lanes)
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt) {
+          float x[16];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            float x[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = acc[dt][4 * g + e] * scale;
-            store4(dst + 32 * dt + 8 * g + 4 * h, x);
-          }
+          for (int v = 0; v < 16; ++v) x[v] = acc[dt][v] * scale;
+          store_tile_row(dst + 32 * dt, x, h);
+        }
       }
     }
   }
