@@ -1023,6 +1023,7 @@ __global__ void __launch_bounds__(512)
   constexpr int VCH = D / 8, OIT = (STEP * VCH + 255) / 256;  // dnum pieces per dV thread
   __shared__ Sm sm;
   __shared__ T KFs[STEP][LDR];  // phi(K) of the step's keys, [key][feature]
+  __shared__ T FSn[STEP][LDR];  // phi(Q): steps of odd index here, even in sm.FS
   __shared__ T RTs[D * rt_lds_width<LPG>()];
   __shared__ PlanesLds<T, D, LPG> PLs;
   __shared__ KdaLds<LPG> DA;
@@ -1076,10 +1077,26 @@ __global__ void __launch_bounds__(512)
         prefetch_row_frags<T, D>(Vh + (size_t)min(s0 + 32 * kt + col, N - 1) * D, vx, h);
       }
     };
+    // dV waves: the Q rows of a step, which they featurize during the step before
+    // (in the wait for the dK waves' da) into that step's phi(Q) buffer.
+    auto load_q = [&](int s0) __attribute__((always_inline)) {
+      if constexpr (ROLE == 1) {
+        if (s0 < t_beg) return;
+        prefetch_row_frags<T, D>(Qh + (size_t)min(s0 + 32 * kt + col, N - 1) * D, xr, h);
+      }
+    };
+    auto feat_q = [&](int s0, T* fs) __attribute__((always_inline)) {
+      if constexpr (ROLE == 1) {
+        if (s0 >= t_beg && kwave && FEAT_HALF)
+          Feat::template compute_to_row<JP0, NJH>(xr, PH, PLo, LDP, Lg, scale, tau, lane,
+                                                  s0 + 32 * kt + col < t_end,
+                                                  fs + (size_t)(32 * kt + col) * LDR);
+      }
+    };
     auto load_rows = [&](int s0) __attribute__((always_inline)) {
       if (s0 < t_beg) return;
       const size_t trow = (size_t)min(s0 + 32 * kt + col, N - 1) * D;
-      prefetch_row_frags<T, D>((ROLE == 0 ? Kh : Qh) + trow, xr, h);
+      if constexpr (ROLE == 0) prefetch_row_frags<T, D>(Kh + trow, xr, h);
       if constexpr (ROLE == 1) {
 #pragma unroll
         for (int i = 0; i < OIT; ++i) {
@@ -1092,6 +1109,12 @@ __global__ void __launch_bounds__(512)
       }
     };
     const int nstep = (t_end - t_beg + STEP - 1) / STEP;
+    auto fs_of = [&](int si) __attribute__((always_inline)) {
+      return (si & 1) ? &FSn[0][0] : &sm.FS[0][0];
+    };
+    load_q(t_beg + (nstep - 1) * STEP);
+    feat_q(t_beg + (nstep - 1) * STEP, fs_of(nstep - 1));
+    load_q(t_beg + (nstep - 2) * STEP);
     load_rows(t_beg + (nstep - 1) * STEP);
     load_v(t_beg + (nstep - 1) * STEP);
 
@@ -1099,6 +1122,7 @@ __global__ void __launch_bounds__(512)
       const int s0 = t_beg + si * STEP;
       const int ktok = s0 + 32 * kt + col;
       const bool kvalid = kwave && ktok < t_end;
+      const T* fsc = fs_of(si);  // phi(Q) of this step's queries
       // Staging. dK waves: phi(K) of this half's tables (kept for the backward and
       // stored to KFs). dV waves: phi(Q) of this half's tables to FS, dnum rows to
       // XS, dd_lr.
@@ -1119,9 +1143,6 @@ __global__ void __launch_bounds__(512)
           }
         }
       } else {
-        if (kwave && FEAT_HALF)
-          Feat::template compute_to_row<JP0, NJH>(xr, PH, PLo, LDP, Lg, scale, tau, lane, kvalid,
-                                                  &sm.FS[32 * kt + col][0]);
 #pragma unroll
         for (int i = 0; i < OIT; ++i) {
           const int it = ts + 256 * i;
@@ -1170,7 +1191,7 @@ __global__ void __launch_bounds__(512)
                 const typename M::frag gf = M::from_acc(gm, ks2);
 #pragma unroll
                 for (int i = 0; i < NFH; ++i)
-                  dkt[i] = M::mma(tr_frag<T>(&sm.FS[0][0], LDR, 32 * qt, 32 * (HALF * NFH + i), ks2,
+                  dkt[i] = M::mma(tr_frag<T>(fsc, LDR, 32 * qt, 32 * (HALF * NFH + i), ks2,
                                              lane, true),
                                   gf, dkt[i]);
               }
@@ -1207,7 +1228,7 @@ __global__ void __launch_bounds__(512)
             floatx16 wq = zero16();
 #pragma unroll
             for (int ks = 0; ks < RP / M::KSTEP; ++ks)
-              wq = M::mma(M::load(&sm.FS[32 * qt + col][Feat::frag_feat(ks, 0, h)]),
+              wq = M::mma(M::load(fsc + (size_t)(32 * qt + col) * LDR + Feat::frag_feat(ks, 0, h)),
                           M::load(&KFs[32 * kt + col][Feat::frag_feat(ks, 0, h)]), wq);
 #pragma unroll
             for (int v = 0; v < 16; ++v)
@@ -1226,6 +1247,14 @@ __global__ void __launch_bounds__(512)
         if (kvalid)
           write_grad_row<T, D, NDH, SINGLE>(dvt, scrV, dV, ((size_t)bh * N + ktok) * D, h, first != 0,
                                     last != 0, HALF * NDH);
+      }
+      if constexpr (ROLE == 1) {
+        // While the dK waves finish their da: phi(Q) of the next step (walking
+        // backwards) into its buffer, then the Q rows of the step after it.
+        if (si > 0) {
+          feat_q(s0 - STEP, fs_of(si - 1));
+          load_q(s0 - 2 * STEP);
+        }
       }
       __syncthreads();  // da of every table in LDS
 
@@ -1247,7 +1276,7 @@ __global__ void __launch_bounds__(512)
         }
       }
       if (!causal) continue;  // fixed statistics
-      advance_stats<T, D, LPG, SPW, STEP, true, NW>(&sm.XS[0][0], LDD, &sm.FS[0][0], LDR, sm.dd, w,
+      advance_stats<T, D, LPG, SPW, STEP, true, NW>(&sm.XS[0][0], LDD, fsc, LDR, sm.dd, w,
                                                     lane, st, &sm.SF[0][0], sm.zr);
       __syncthreads();
     }
@@ -1317,12 +1346,12 @@ size_t bwd_lds_need(const Problem& pb) {
         constexpr size_t RTB = sizeof(T) * D * rt_lds_width<LPG>() + sizeof(PlanesLds<T, D, LPG>);
         constexpr int SQ = walk_step<T, D, LPG, 128, RTB + sizeof(QdaLds<LPG>)>();
         constexpr int SK = walk_step<T, D, LPG, 64,
-                                     RTB + sizeof(KdaLds<LPG>) + sizeof(T) * 64 * tile_ld<T>(16 * LPG)>();
+                                     RTB + sizeof(KdaLds<LPG>) + 2 * sizeof(T) * 64 * tile_ld<T>(16 * LPG)>();
         const size_t a = RTB + sizeof(QdaLds<LPG>) +
                          (SQ > 0 ? sizeof(WalkSmem<T, D, LPG, SQ>) : sizeof(WalkSmem<T, D, LPG, 32>));
         const size_t b = RTB + sizeof(KdaLds<LPG>) +
                          (SK > 0 ? sizeof(WalkSmem<T, D, LPG, SK>) : sizeof(WalkSmem<T, D, LPG, 32>)) +
-                         sizeof(T) * (SK > 0 ? SK : 32) * tile_ld<T>(16 * LPG);
+                         2 * sizeof(T) * (SK > 0 ? SK : 32) * tile_ld<T>(16 * LPG);
         lr = a > b ? a : b;
       };
       switch (padded_tables(pb.L)) {
@@ -1427,7 +1456,7 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
         constexpr size_t RTB = sizeof(T) * D * rt_lds_width<LPG>() + sizeof(PlanesLds<T, D, LPG>);
         constexpr int SQ = walk_step<T, D, LPG, 128, RTB + sizeof(QdaLds<LPG>)>();
         constexpr int SK = walk_step<T, D, LPG, 64,
-                                     RTB + sizeof(KdaLds<LPG>) + sizeof(T) * 64 * tile_ld<T>(16 * LPG)>();
+                                     RTB + sizeof(KdaLds<LPG>) + 2 * sizeof(T) * 64 * tile_ld<T>(16 * LPG)>();
         if constexpr (SQ > 0 && SK > 0) {
           const int span_q = pb.causal ? pb.chunk : noncausal_span(pb.N, (int)BH, SQ);
           const int span_k = pb.causal ? pb.chunk : noncausal_span(pb.N, (int)BH, SK);
