@@ -771,8 +771,9 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
 
 // ---------------------------------------------------------------------------
 // Low-rank branch, query side: one head and span per workgroup, walked forwards in
-// steps of STEP tokens by 8 waves. Query tile qt = w % 4 of the step is shared by
-// waves qt (half 0) and qt + 4 (half 1): each forms dphi(Q) for half of the feature
+// steps of STEP tokens by 8 waves. Each query tile of the step is shared by a
+// wave of half 0 (waves 0..3, tiles in order) and one of half 1 (waves 4..7, tiles
+// in reverse order): each forms dphi(Q) for half of the feature
 // tiles and takes it back through its half of the tables; the hyperplane
 // gradients da go through LDS so that each wave then forms dQ for half of the
 // channels. LDS (WalkSmem): V (XS) and phi(K) (FS) of the step's keys, the
@@ -806,7 +807,10 @@ __global__ void __launch_bounds__(512)
   const int bh = blockIdx.y, c = blockIdx.x, head = bh % H;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int w = tid >> 6;
-  const int qt = w & 3, half = w >> 2;
+  // Waves w and w + 4 share a SIMD; the causal part of a query tile grows with
+  // its index, so the second half takes the tiles in reverse order and every SIMD
+  // gets the same work.
+  const int half = w >> 2, qt = half ? 3 - (w & 3) : (w & 3);
   const bool qwave = qt < QT;
   const int r = 16 * L, f0 = 128 * grp, Lg = min(8, L - 8 * grp);
   const float* pl = planes + ((size_t)head * L + 8 * grp) * 4 * D;
@@ -990,8 +994,8 @@ __global__ void __launch_bounds__(512)
 
 // ---------------------------------------------------------------------------
 // Low-rank branch, key side: one head and span per workgroup, walked backwards in
-// steps of STEP tokens by 8 waves. Key tile kt = (w / 2) % QT, half = w % 2:
-// waves 0 .. 3 form dK (each half takes half of the feature tiles of dphi(K) and
+// steps of STEP tokens by 8 waves. half = w % 2, key tile kt = (w / 2) % 2 for
+// waves 0 .. 3 and the reverse for waves 4 .. 7 (see below): waves 0 .. 3 form dK (each half takes half of the feature tiles of dphi(K) and
 // its tables; the hyperplane gradients da meet in LDS and each half then forms
 // half of the channels of dK), waves 4 .. 7 form dV (each half takes half of the
 // channels). LDS (WalkSmem): dnum (XS) and phi(Q) (FS) of the step's queries,
@@ -1030,7 +1034,10 @@ __global__ void __launch_bounds__(512)
   const int bh = blockIdx.y, c = blockIdx.x, head = bh % H;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int w = tid >> 6;
-  const int role = w >> 2, kt = (w >> 1) & 1, half = w & 1;  // role 0: dK, 1: dV
+  // role 0: dK, 1: dV. Waves w and w + 4 share a SIMD; the causal part of a key
+  // tile shrinks with its index, so the dV waves take the key tiles in reverse
+  // order and every SIMD gets the same work.
+  const int role = w >> 2, half = w & 1, kt = role ? 1 - ((w >> 1) & 1) : (w >> 1) & 1;
   const bool kwave = kt < QT;
   const int r = 16 * L, f0 = 128 * grp, Lg = min(8, L - 8 * grp);
   const float* pl = planes + ((size_t)head * L + 8 * grp) * 4 * D;

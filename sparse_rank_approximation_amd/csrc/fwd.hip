@@ -249,7 +249,10 @@ __global__ void __launch_bounds__(512)
   const int r = 16 * L;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int w = tid >> 6;
-  const int qt = w & 3, half = w >> 2;
+  // Waves w and w + 4 share a SIMD; the causal part of a query tile grows with
+  // its index, so the second half takes the tiles in reverse order and every SIMD
+  // gets the same work (and with two tiles per step, one of each half).
+  const int half = w >> 2, qt = half ? 3 - (w & 3) : (w & 3);
   const bool qwave = qt < QT;
   const float* pl = planes + (size_t)head * L * 4 * D;
   const int t_beg = c * span, t_end = min(N, t_beg + span);
