@@ -897,7 +897,8 @@ __global__ void __launch_bounds__(512)
         Feat Fq;
         typename M::frag dn[D / M::KSTEP];
         if (qwave && ACTIVE_A) {
-          Fq.compute(qx, PH, PLo, LDP, Lg, scale, tau, lane);
+          // (only this half's tables: the backward below takes only those)
+          Fq.template compute<HALF * NFH, NFH>(qx, PH, PLo, LDP, Lg, scale, tau, lane);
   #pragma unroll
           for (int ks = 0; ks < D / M::KSTEP; ++ks) {
             float x[M::KPL];
@@ -1136,7 +1137,8 @@ __global__ void __launch_bounds__(512)
       Feat Fk;
       if constexpr (ROLE == 0) {
         if (kwave && FEAT_HALF) {
-          Fk.compute(xr, PH, PLo, LDP, Lg, scale, tau, lane);
+          // (only this half's tables: they are all that is stored and taken back)
+          Fk.template compute<JP0, NJH>(xr, PH, PLo, LDP, Lg, scale, tau, lane);
 #pragma unroll
           for (int jp = JP0; jp < JP0 + NJH; ++jp) {
             float x0[8], x1[8];

@@ -601,13 +601,16 @@ struct Features {
     project(xf, planes, L, lane, u);
     activate(u, L, scale, tau, lane);
   }
-  // Same, with the hyperplanes staged in LDS by stage_planes (PL unused for fp32).
+  // Same, with the hyperplanes staged in LDS by stage_planes (PL unused for fp32);
+  // phi and sp of the table pairs JP0 .. JP0 + NJ - 1 only (the rest are left
+  // unset).
+  template <int JP0 = 0, int NJ = NJP>
   __device__ __forceinline__ void compute(const typename MF<T>::frag (&xf)[D / MF<T>::KSTEP],
                                           const T* PH, const T* PL, int ldp, int L, float scale,
                                           float tau, int lane) {
     floatx16 u[NPT];
     project(xf, PH, PL, ldp, lane, u);
-    activate(u, L, scale, tau, lane);
+    activate<JP0, NJ>(u, L, scale, tau, lane);
   }
   // phi of every table for this lane's token (zero when !valid) stored straight
   // into the LDS row dst (features 16 table + b), one table pair at a time so that
@@ -665,7 +668,9 @@ struct Features {
       }
   }
 
-  // phi from the projection tiles u (rows = projections, columns = tokens).
+  // phi from the projection tiles u (rows = projections, columns = tokens), for
+  // the table pairs JP0 .. JP0 + NJ - 1.
+  template <int JP0 = 0, int NJ = NJP>
   __device__ __forceinline__ void activate(const floatx16 (&u)[NPT], int L, float scale, float tau,
                                            int lane) {
     const int h = lane >> 5;
@@ -675,7 +680,7 @@ struct Features {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int jp = 4 * mt + g;
-        if (jp >= NJP) continue;
+        if (jp >= NJP || jp < JP0 || jp >= JP0 + NJ) continue;
         const int table = 2 * jp + h;
         float p[4], q[4];
 #pragma unroll
