@@ -17,17 +17,19 @@
 //   lr_sums + lr_scan    (lowrank.hip) G = sum_i phi(Q_i) dnum_i^T, g = sum_i
 //                        phi(Q_i) dd_lr,i per chunk, combined as the exclusive suffix
 //                        over chunks (causal) or the total;
-//   sparse_bwd_kernel    per selected block: dQ, dK, dV partials per level slot;
+//   sparse_bwd2_kernel   per selected block (bf16, blocks of at most 128; else
+//   / sparse_bwd_kernel  sparse_bwd_kernel, in one launch or a key launch and a
+//                        query launch): dQ, dK, dV partials per level slot;
 //   lr_bwd_q_kernel      query side of the low-rank branch, walking each chunk
 //                        forwards with the running key statistics A, z:
 //                        dphi(Q_i) = sum_{j<=i} (<dnum_i, V_j> + dd_lr,i) phi(K_j),
-//                        then through the features to dQ, plus the sparse dQ
-//                        partials -> dQ;
+//                        then through the features to the low-rank part of dQ;
 //   lr_bwd_k_kernel      key side, walking each chunk backwards with the running
 //                        query statistics G, g:
 //                        dphi(K_j) = sum_{i>=j} (<dnum_i, V_j> + dd_lr,i) phi(Q_i),
-//                        dV_j += sum_{i>=j} (phi(Q_i).phi(K_j)) dnum_i, plus the sparse
-//                        partials -> dK, dV.
+//                        dV_j += sum_{i>=j} (phi(Q_i).phi(K_j)) dnum_i: the low-rank
+//                        parts of dK, dV;
+//   combine_kernel       (merge.hip) adds the sparse partial rows: dQ, then dK, dV.
 // Features are processed in groups of at most 8 tables (128 features); with two
 // groups the first launch leaves an fp32 running sum that the second completes.
 #include "common.hpp"

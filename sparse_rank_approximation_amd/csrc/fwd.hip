@@ -1,9 +1,9 @@
 // fwd.hip -- forward of the ELSAA operator on gfx950.
 //
-// sparse_fwd_kernel (ELSAA paper, Section 3.2): one workgroup per selected block.
-// The block's s keys are gathered by the sorted order into LDS (K row-major, V
-// transposed); each wave owns 32 of the block's queries and streams the keys in
-// tiles of 32 with an online softmax. Scores are formed as S^T = K Q^T so that a
+// sparse_fwd_kernel (ELSAA paper, Section 3.2): persistent workgroups walk the
+// selected blocks. A block's s keys are gathered by the sorted order into LDS (K
+// and V row-major, V read transposed); each wave owns 32 of the block's queries
+// and streams the keys in tiles of 32 with an online softmax. Scores are formed as S^T = K Q^T so that a
 // lane owns one query (column statistics stay in-lane) and the probabilities P^T
 // are directly the B operand of O^T += V^T P^T. The normalized block output and
 // its log-sum-exp go to a partial slot of the query:
@@ -11,7 +11,7 @@
 //           level l block   -> slot N + l N/2 + compact_l(i);
 //   non-causal: the single block of query i -> slot i.
 //
-// fwd_epilogue_kernel: per head and chunk of tokens, 64 tokens per step:
+// fwd_epilogue_kernel: per head and chunk of tokens, in steps of 64 or 128 tokens:
 //   - sparse branch: log-sum-exp merge of the query's partials (Section 3.2's
 //     merge that keeps exact softmax normalization over the union support);
 //   - low-rank branch (Section 3.1): normalized ratio readout of the running
