@@ -75,21 +75,18 @@ def roofline(name, launches, total_ms, w, traffic_file):
             "traffic": traffic_bytes(name, traffic_file)}
 
 
-def kernel_source_hash() -> str:
-    from sparse_rank_approximation_amd.traffic import source_hash
-    return source_hash()
-
-
 def traffic_bytes(name, path):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary, if it was taken from the current kernel sources; else None."""
+    summary, if it was taken with the library this run loads; else None."""
+    from sparse_rank_approximation_amd.traffic import library_hash
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
     except ValueError:
         return None
-    if rec.get("source_hash") != kernel_source_hash():
+    lib = library_hash()
+    if lib is None or rec.get("library_hash") != lib:
         return None
     k = rec.get("kernels", {}).get(name)
     return None if k is None else k.get("hbm_bytes_per_launch")

@@ -13,8 +13,9 @@ Two roles, one per step of the measurement:
         Reads the counter_collection CSVs of the four runs (the bench.py runs and
         the copy runs) and writes OUT.json: per kernel, the average FETCH_SIZE and
         WRITE_SIZE per dispatch, the calibration factors and the calibrated bytes
-        per launch, tagged with the hash of the kernel sources they were taken
-        from (bench.py uses the figures only while the sources are unchanged).
+        per launch, tagged with the hash of the built library they were taken
+        with (bench.py uses the figures only while that library is the one it
+        loads: a change to a kernel or to a launch changes it, a comment does not).
 """
 from __future__ import annotations
 
@@ -30,13 +31,12 @@ COPY_BYTES = 1 << 30  # 1 GiB read + 1 GiB written: well past the last-level cac
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 
-def source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(PKG, "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
-    return h.hexdigest()[:16]
+def library_hash():
+    """First 16 hex digits of the SHA-256 of the built library; None if not built."""
+    from sparse_rank_approximation_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        return None
+    return hashlib.sha256(open(_lib.LIB_PATH, "rb").read()).hexdigest()[:16]
 
 
 def short_name(name: str):
@@ -98,7 +98,7 @@ def summarize(out, fb, wb, fc, wc) -> None:
         wk = w_bench.get(k, (0, 0.0))[1]
         kernels[k] = {"fetch_kib_per_launch": round(fk, 1), "write_kib_per_launch": round(wk, 1),
                       "hbm_bytes_per_launch": round(fk * 1024.0 * kf + wk * 1024.0 * kw)}
-    rec = {"source_hash": source_hash(), "copy_bytes": COPY_BYTES,
+    rec = {"library_hash": library_hash(), "copy_bytes": COPY_BYTES,
            "fetch_factor": round(kf, 4), "write_factor": round(kw, 4), "kernels": kernels}
     json.dump(rec, open(out, "w"), indent=1)
     print(json.dumps(rec, indent=1))

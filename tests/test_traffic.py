@@ -65,4 +65,4 @@ def test_summarize_calibrates_and_averages(tmp_path):
     assert k["fetch_kib_per_launch"] == 100.0  # (120 + 80) / 2 dispatches
     assert k["write_kib_per_launch"] == 5.0
     assert k["hbm_bytes_per_launch"] == round(100.0 * 1024 * 2 + 5.0 * 1024)
-    assert len(rec["source_hash"]) == 16 and rec["source_hash"] == traffic.source_hash()
+    assert rec["library_hash"] == traffic.library_hash()
