@@ -9,7 +9,7 @@ import torch
 
 import workloads as W
 from oracle import ref
-from parity_util import CASES, TOL, all_heads, gpu_forward, head_arrays, rel_err
+from parity_util import CASES, TOL, all_heads, gpu_forward, head_arrays, rel_err, wl
 
 pytestmark = pytest.mark.gpu
 
@@ -53,6 +53,36 @@ def test_forward_parity(case):
     print(f"[gpu fwd] {case} errors {errs}", flush=True)
     bad = {k: e for k, e in errs.items() if not e <= tol}
     assert not bad, f"{case}: errors above {tol}: {bad}"
+
+
+# Wider codes than the workloads use (9 to 12 hyperplanes: the hash kernel's
+# two-threads-per-row split and the counting sort with up to 4096 bins, staged in
+# LDS or not), causal and non-causal: codes and orders bit-exact.
+SELECT_CASES = {
+    "bits12_causal_f32_N65536_s16": wl("s", 1, 1, 65536, 32, "f32", True, 16, 16),
+    "bits9_causal_bf16_N32768_s64": wl("s", 1, 2, 32768, 128, "bf16", True, 64, 16),
+    "bits11_noncausal_bf16_N32768_s16": wl("s", 1, 1, 32768, 64, "bf16", False, 16, 16),
+}
+
+
+@pytest.mark.parametrize("case", list(SELECT_CASES))
+def test_select_wide_codes(case):
+    import sparse_rank_approximation_amd as S
+    from parity_util import cfg_of, to_dev
+    w = SELECT_CASES[case]
+    print(f"[gpu select] {case} {w} bits {w.hash_bits}", flush=True)
+    inp = W.gen_inputs(w, 4242)
+    d = to_dev({k: inp[k] for k in ("q", "k", "planes_s")})
+    qc, kc, qp, kp = S.select(cfg_of(w), d["q"], d["k"], d["planes_s"])
+    torch.cuda.synchronize()
+    heads = all_heads(w)
+    q, k, _, _, ps, _ = head_arrays(w, inp, heads)
+    rqc, rkc, rqp, rkp = ref.select(ref.RefParams.from_workload(w), q, k, ps)
+    G = len(heads)
+    np.testing.assert_array_equal(qc.view(G, -1).cpu().numpy().astype(np.uint16), rqc)
+    np.testing.assert_array_equal(kc.view(G, -1).cpu().numpy().astype(np.uint16), rkc)
+    np.testing.assert_array_equal(qp.view(G, -1).cpu().numpy(), rqp.reshape(G, -1))
+    np.testing.assert_array_equal(kp.view(G, -1).cpu().numpy(), rkp.reshape(G, -1))
 
 
 def test_forward_deterministic():
