@@ -480,7 +480,7 @@ struct Sb2Smem {
 };
 
 template <int D, int SB>
-__global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32))
+__global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
     sparse_bwd2_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                        const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                        const float* __restrict__ lse, const float* __restrict__ rc,
