@@ -147,10 +147,10 @@ def main():
     import sparse_rank_approximation_amd as S
     from sparse_rank_approximation_amd import _lib
 
-    w = W.CONFIGS[args.config]
+    w = W.WORKLOADS[args.config]
     if args.chunk:
         w = w.with_(chunk=args.chunk)
-    seed = W.config_seed(args.config)
+    seed = W.workload_seed(args.config)
     t0 = time.perf_counter()
     inp = W.gen_inputs(w, seed)
     dev = torch.device("cuda:0")

@@ -64,7 +64,7 @@ def wl(name, B, H, N, d, dtype, causal, block, r, gen="iid", chunk=128, **ga):
 
 CASES = {
     # the tiny single-head workload, as is
-    "tiny_f32": (W.CONFIGS[1], False, False),
+    "tiny_f32": (W.WORKLOADS[1], False, False),
     # several tiles and summary chunks, causal, fp32
     "causal_f32_N512_d64_s32": (wl("c", 1, 2, 512, 64, "f32", True, 32, 32, chunk=128), True, True),
     # bf16 causal with planted clusters, d 128, s 128, r 128, two summaries per head

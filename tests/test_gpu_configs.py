@@ -32,8 +32,8 @@ SAMPLES = {
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
 def test_full_size_parity(cid):
     import sparse_rank_approximation_amd as S
-    w = W.CONFIGS[cid]
-    seed = W.config_seed(cid)
+    w = W.WORKLOADS[cid]
+    seed = W.workload_seed(cid)
     heads, with_bwd = SAMPLES.get(cid, ([(0, 0)], True))
     print(f"[gpu full] config {cid} {w.name}: heads {heads}", flush=True)
     inp = W.gen_inputs(w, seed)

@@ -58,7 +58,7 @@ class Workload:
         return replace(self, **kw)
 
 
-CONFIGS = {
+WORKLOADS = {
     1: Workload("tiny_single_head_B1_H1_N256_d32_f32", 1, 1, 256, 32, "f32", False, 16, 16,
                 "iid", chunk=64),
     2: Workload("gpt2_small_layer_B8_H12_N4096_d64_bf16_causal", 8, 12, 4096, 64, "bf16", True,
@@ -73,7 +73,7 @@ CONFIGS = {
 }
 
 
-def config_seed(idx: int) -> int:
+def workload_seed(idx: int) -> int:
     return BASE_SEED + idx
 
 
