@@ -373,7 +373,17 @@ __device__ __forceinline__ float max_halves(float x) {
 
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
-__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// sigmoid(a) and sigmoid(-a) from one exponential and one reciprocal: with
+// t = exp(-|a|) in (0, 1], sigmoid(|a|) = 1 / (1 + t) and sigmoid(-|a|) =
+// t / (1 + t) (no cancellation for either, no overflow); v_rcp_f32 is within
+// 1 ulp of 1 / (1 + t) on (1, 2].
+__device__ __forceinline__ void sigmoid_pair(float a, float& p, float& q) {
+  const float t = __expf(-fabsf(a));
+  const float s = __builtin_amdgcn_rcpf(1.0f + t);
+  const float r = t * s;
+  p = a >= 0.0f ? s : r;
+  q = a >= 0.0f ? r : s;
+}
 
 // Inverse of the reflected binary Gray code (position along the Gray sequence).
 __device__ __forceinline__ unsigned gray_rank(unsigned c) {
@@ -648,8 +658,7 @@ struct Features {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const float a = c2 * u[mt][4 * g + t];
-          p[t] = sigmoid(a);
-          q[t] = sigmoid(-a);
+          sigmoid_pair(a, p[t], q[t]);
         }
         float lo4[4], hi4[4];
 #pragma unroll
@@ -686,8 +695,7 @@ struct Features {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const float a = c2 * u[mt][4 * g + t];
-          p[t] = sigmoid(a);
-          q[t] = sigmoid(-a);
+          sigmoid_pair(a, p[t], q[t]);
           sp[jp][t] = p[t];
         }
         float lo4[4], hi4[4];
