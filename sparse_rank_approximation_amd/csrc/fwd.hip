@@ -401,7 +401,8 @@ __global__ void __launch_bounds__(512)
         }
 
         if (qvalid) {
-          const float m = 1.0f / (1.0f + fast_exp(__logf(lam * den + eps) - lse));
+          // (the hardware reciprocal is within 1 ulp here: its argument is at least 1)
+          const float m = __builtin_amdgcn_rcpf(1.0f + fast_exp(__logf(lam * den + eps) - lse));
           const float g1 = gs ? gs[k] : 1.0f;
           const float g2 = glr ? glr[k] : 1.0f;
           const float dinv = 1.0f / den;
