@@ -660,6 +660,9 @@ struct Features {
           const float a = c2 * u[mt][4 * g + t];
           sigmoid_pair(a, p[t], q[t]);
         }
+        // (every product takes p[0] or q[0]: zeroing those zeroes a dead row)
+        p[0] = live ? p[0] : 0.0f;
+        q[0] = live ? q[0] : 0.0f;
         float lo4[4], hi4[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -669,8 +672,8 @@ struct Features {
         float x0[8], x1[8];
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
-          x0[b] = live ? lo4[b & 3] * hi4[b >> 2] : 0.0f;
-          x1[b] = live ? lo4[(8 + b) & 3] * hi4[(8 + b) >> 2] : 0.0f;
+          x0[b] = lo4[b & 3] * hi4[b >> 2];
+          x1[b] = lo4[(8 + b) & 3] * hi4[(8 + b) >> 2];
         }
         store8(dst + feat(jp, 0, h), x0);
         store8(dst + feat(jp, 8, h), x1);
@@ -698,15 +701,18 @@ struct Features {
           sigmoid_pair(a, p[t], q[t]);
           sp[jp][t] = p[t];
         }
+        // (every product takes p[0] or q[0]: zeroing those zeroes a dead table)
+        const bool live = table < L;
+        p[0] = live ? p[0] : 0.0f;
+        q[0] = live ? q[0] : 0.0f;
         float lo4[4], hi4[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           lo4[b] = ((b & 1) ? p[0] : q[0]) * ((b & 2) ? p[1] : q[1]);
           hi4[b] = ((b & 1) ? p[2] : q[2]) * ((b & 2) ? p[3] : q[3]);
         }
-        const bool live = table < L;
 #pragma unroll
-        for (int b = 0; b < 16; ++b) phi[jp][b] = live ? lo4[b & 3] * hi4[b >> 2] : 0.0f;
+        for (int b = 0; b < 16; ++b) phi[jp][b] = lo4[b & 3] * hi4[b >> 2];
       }
     }
   }
@@ -759,16 +765,22 @@ struct Features {
 // exchange with the other half leaves lane half h with all 16 buckets of table
 // 2 jp + h, the layout of Features::phi[jp].
 __device__ __forceinline__ void tile_to_table(const floatx16& acc, int h, float (&out)[16]) {
+  (void)h;
+  // v_permlane32_swap(x = acc[i], y = acc[8 + i]) trades the upper lanes of x for
+  // the lower lanes of y. Lane half 0 then holds its own acc[i] (bucket 8 g2 + t of
+  // table 2 jp) and the partner's acc[i] (bucket 8 g2 + 4 + t); lane half 1 holds
+  // the partner's acc[8 + i] (bucket 8 g2 + t of table 2 jp + 1) and its own
+  // acc[8 + i] (bucket 8 g2 + 4 + t). The same two outputs for both halves, no
+  // selects.
 #pragma unroll
   for (int g2 = 0; g2 < 2; ++g2)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const float keep = h ? acc[8 + 4 * g2 + t] : acc[4 * g2 + t];
-      const float send = h ? acc[4 * g2 + t] : acc[8 + 4 * g2 + t];
-      const float recv = swap_half(send);
-      // own rows: b = 8 g2 + 4 h + t; partner rows: b = 8 g2 + 4 (1 - h) + t
-      out[8 * g2 + t] = h ? recv : keep;
-      out[8 * g2 + 4 + t] = h ? keep : recv;
+      const int i = 4 * g2 + t;
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i]),
+                                                      __float_as_uint(acc[8 + i]), false, false);
+      out[8 * g2 + t] = __uint_as_float(r[0]);
+      out[8 * g2 + 4 + t] = __uint_as_float(r[1]);
     }
 }
 
