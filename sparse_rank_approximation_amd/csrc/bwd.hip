@@ -895,23 +895,13 @@ __global__ void __launch_bounds__(512)
             }
           }
         }
-        // phi(Q) and dnum of the query tile, from registers.
+        // phi(Q) of the query tile, from registers. (dnum = e_q dO: the products
+        // below take the dO rows as they are and scale their columns, one per
+        // query, by e_q afterwards.)
         Feat Fq;
-        typename M::frag dn[D / M::KSTEP];
         if (qwave && ACTIVE_A) {
           // (only this half's tables: the backward below takes only those)
           Fq.template compute<HALF * NFH, NFH>(qx, PH, PLo, LDP, Lg, scale, tau, lane);
-  #pragma unroll
-          for (int ks = 0; ks < D / M::KSTEP; ++ks) {
-            float x[M::KPL];
-            if constexpr (M::KPL == 8) {
-  #pragma unroll
-              for (int e = 0; e < 8; ++e) x[e] = (float)ox[ks][e] * e_q;
-            } else {
-              x[0] = ox[ks] * e_q;
-            }
-            dn[ks] = M::from_floats(x);
-          }
         }
         // The next step's keys, issued as soon as this step's are staged so that
         // their latency hides behind the rest of the step (past the span: loads
@@ -930,19 +920,19 @@ __global__ void __launch_bounds__(512)
             df[i] = zero16();
   #pragma unroll
             for (int ks = 0; ks < D / M::KSTEP; ++ks)
-              df[i] = M::mma(row_frag<T>(&sm.SF[0][0], LDD, 32 * ft, 0, ks, lane), dn[ks], df[i]);
+              df[i] = M::mma(row_frag<T>(&sm.SF[0][0], LDD, 32 * ft, 0, ks, lane), ox[ks], df[i]);
   #pragma unroll
-            for (int v = 0; v < 16; ++v) df[i][v] += sm.zr[32 * ft + acc_row(v, h)] * dd_q;
+            for (int v = 0; v < 16; ++v) df[i][v] = df[i][v] * e_q + sm.zr[32 * ft + acc_row(v, h)] * dd_q;
           }
           if (causal) {
             for (int kt = 0; kt <= qt; ++kt) {
               floatx16 gt = zero16();
   #pragma unroll
               for (int ks = 0; ks < D / M::KSTEP; ++ks)
-                gt = M::mma(row_frag<T>(&sm.XS[0][0], LDD, 32 * kt, 0, ks, lane), dn[ks], gt);
+                gt = M::mma(row_frag<T>(&sm.XS[0][0], LDD, 32 * kt, 0, ks, lane), ox[ks], gt);
   #pragma unroll
               for (int v = 0; v < 16; ++v) {
-                gt[v] += dd_q;
+                gt[v] = gt[v] * e_q + dd_q;
                 if (kt == qt && acc_row(v, h) > col) gt[v] = 0.0f;
               }
   #pragma unroll
