@@ -122,7 +122,13 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 ?
     floatx16 o[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) o[dt] = zero16();
+    // Online softmax in base 2 (scores times scale log2 e). The running maximum
+    // moves only when a score exceeds it by more than 8, so the probabilities
+    // against it stay below 2^8, and the output tiles are rescaled only when a
+    // lane of the wave moved it (the result is the same; most tiles after the
+    // first move no maximum).
     float mrun = -INFINITY, lrun = 0.0f;
+    const float c2 = scale * kLog2e;
     auto ktile = [&](int kt) __attribute__((always_inline)) {
       floatx16 sacc = zero16();
 #pragma unroll
@@ -133,26 +139,31 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 ?
       for (int v = 0; v < 16; ++v) {
         const int kr = 32 * kt + acc_row(v, h);
         const bool masked = kr >= SB || (leaf && kr > qloc);
-        sacc[v] = masked ? -INFINITY : sacc[v] * scale;
+        sacc[v] = masked ? -INFINITY : sacc[v] * c2;
         mx = fmaxf(mx, sacc[v]);
       }
       mx = max_halves(mx);
-      const float mnew = fmaxf(mrun, mx);
+      const float mnew = mx > mrun + 8.0f ? mx : mrun;
       const float msub = mnew == -INFINITY ? 0.0f : mnew;
-      const float alpha = fast_exp(mrun - msub);
+      const float alpha = __builtin_amdgcn_exp2f(mrun - msub);
       float ps = 0.0f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        sacc[v] = fast_exp(sacc[v] - msub);
+        sacc[v] = __builtin_amdgcn_exp2f(sacc[v] - msub);
         ps += sacc[v];
       }
       ps = sum_halves(ps);
       lrun = lrun * alpha + ps;
+      const bool moved = mnew != mrun;
       mrun = mnew;
+      // (before the first tile the output tiles are zero; lanes that kept their
+      // maximum have alpha = 1 exactly)
+      if (kt > 0 && __any(moved)) {
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+          for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+      }
 #pragma unroll
       for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
         const typename M::frag pf = M::from_acc(sacc, ks2);
@@ -189,7 +200,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 ?
         }
       if (h == 0) oslot[qloc] = qvalid ? (int)slot : -1;
     }
-    if (qvalid && h == 0) Lpart[(size_t)bh * slots + slot] = mrun + __logf(lrun);
+    if (qvalid && h == 0) Lpart[(size_t)bh * slots + slot] = (mrun + __log2f(lrun)) * kLn2;
     __syncthreads();
     {
       // All of the thread's LDS reads are issued before its stores (one wait);
