@@ -468,7 +468,7 @@ struct Sb2Smem {
   static constexpr int LD = tile_ld<__bf16>(D), LDK = tile_ld<__bf16>(KT);
   // The per-row arrays come first: their addresses are then small constants
   // from one per-thread base (instruction offsets), not separate registers.
-  alignas(16) float lse[KT];  // +inf for rows past the block (P = 0)
+  alignas(16) float lse[KT];  // lse log2 e; +inf for rows past the block (P = 0)
   alignas(16) float Dd[KT];
   alignas(16) float cq[KT];
   int qidx[KT], kidx[KT];    // token of each row of this block, -1 past the block
@@ -591,7 +591,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
       sm.kidx[tid] = sm.knext[tid];
       sm.qnext[tid] = prow.alt < -1 ? prow.a : prow.alt;
       sm.knext[tid] = prow.alt < -1 ? prow.b : prow.alt;
-      sm.lse[tid] = pvalid ? plse : INFINITY;
+      sm.lse[tid] = pvalid ? plse * kLog2e : INFINITY;  // (base 2)
       sm.Dd[tid] = pvalid ? pD : 0.0f;
       sm.cq[tid] = pvalid ? pc : 0.0f;
     }
@@ -607,6 +607,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
     {
       const int jk = sm.kidx[key];
       const bool kvalid = jk >= 0;
+      const float c2 = scale * kLog2e;  // P = 2^(c2 S - lse log2 e)
       typename M::frag kf[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kf[ks] = row_frag<T>(&sm.Ks[0][0], LD, 32 * w, 0, ks, lane);
@@ -642,7 +643,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
             const int v = 4 * gg + e;
             // Masked pairs get exp(-inf) = 0 (no branch around the exponential).
             const bool ok = kvalid & !(leaf & (key > r0 + e));
-            const float p = fast_exp(ok ? s[v] * scale - L4[e] : -INFINITY);
+            const float p = __builtin_amdgcn_exp2f(ok ? fmaf(s[v], c2, -L4[e]) : -INFINITY);
             dsv[e] = p * (C4[e] * dp[v] - D4[e]);
             s[v] = C4[e] * p;
             dp[v] = dsv[e];
