@@ -13,6 +13,15 @@ from oracle import ref
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 
+# Per-case bounds above TOL, each with the effect that sets it.
+# peaked_clusters_bf16_causal, dQ: with near one-hot probability rows, the row term
+# D = rowsum(dO * O_s) nearly cancels dP in dS = P (dP - D), and D is formed from
+# the stored bf16 O_s, whose rounding (2^-9 relative) the cancellation amplifies.
+# In an fp64 model of this input (dense causal softmax, D from bf16-rounded O, all
+# else exact) that rounding alone gives 0.044 relative error in dQ; the bound is
+# set at 0.05.
+BWD_TOL = {"peaked_clusters_bf16_causal": {"dQ": 5e-2}}
+
 
 def rel_err(x, r) -> float:
     x = np.asarray(x, dtype=np.float64)
@@ -83,6 +92,11 @@ CASES = {
     # the same in bf16 (empty orders, passed as null pointers), two heads
     "causal_single_block_bf16": (wl("e", 1, 2, 128, 64, "bf16", True, 128, 32, chunk=128),
                                  True, True),
+    # peaked softmax: 128 tight clusters of 4 tokens at d 128, so a query's few
+    # same-cluster keys (scores near 11, the rest near 0) often sit in a later key
+    # tile than the first and the sparse forward's running maximum has to move
+    "peaked_clusters_bf16_causal": (wl("k", 1, 2, 512, 128, "bf16", True, 128, 32, "clusters",
+                                       chunk=128, n_clusters=128, sigma=0.1), True, True),
     # odd table count (padded to 4 tables on the GPU), bf16, d 32
     "tables3_bf16_causal": (wl("t", 1, 1, 512, 32, "bf16", True, 64, 48, chunk=256), True, True),
     # maximum block 256 and r 256 at d 128, causal bf16
