@@ -406,6 +406,22 @@ static void head_fwd_free(head_fwd* f) {
   free(f->O_lr); free(f->m); free(f->qperm); free(f->kperm); free(f->qc); free(f->kc);
 }
 
+/* Eq. 5, m = d_sparse / (d_sparse + c) with d_sparse = exp(lse) and
+ * c = lambda d_lr + eps, together with w = d_sparse / (d_sparse + c)^2 (so that
+ * dm/dc = -w and dm/dlse = c w). For lse >= 0 numerator and denominator are
+ * divided by d_sparse, so exp(lse) is never formed where it could overflow. */
+static void mass_ratio(double lse, double c, double* m, double* w) {
+  if (lse >= 0.0) {
+    const double t = exp(-lse), den = 1.0 + c * t;
+    *m = 1.0 / den;
+    *w = t / (den * den);
+  } else {
+    const double u = exp(lse), T = u + c;
+    *m = u / T;
+    *w = u / (T * T);
+  }
+}
+
 /* One head forward. gs/glr may be NULL (gate 1). */
 static void forward_head(const ref_params* p, const double* Q, const double* K,
                          const double* V, const float* Rs, const float* Rlr, double lam,
@@ -420,8 +436,8 @@ static void forward_head(const ref_params* p, const double* Q, const double* K,
   for (int i = 0; i < N; ++i) {
     for (int c = 0; c < d; ++c) f->O_lr[(size_t)i * d + c] = f->num[(size_t)i * d + c] / f->den[i];
     /* Eq. 5 with d_sparse,i = sum over the support of exp(score) = exp(lse_i). */
-    const double ds = exp(f->lse[i]);
-    f->m[i] = ds / (ds + lam * f->den[i] + p->eps);
+    double w;
+    mass_ratio(f->lse[i], lam * f->den[i] + p->eps, &f->m[i], &w);
     const double a = (gs ? gs[i] : 1.0) * f->m[i], b = glr ? glr[i] : 1.0;
     for (int c = 0; c < d; ++c)
       O[(size_t)i * d + c] = a * f->O_s[(size_t)i * d + c] + b * f->O_lr[(size_t)i * d + c];
@@ -561,13 +577,14 @@ static void backward_head(const ref_params* p, const double* Q, const double* K,
     }
     /* O_lr = num / den */
     dden[i] = -dOnum / (f.den[i] * f.den[i]);
-    /* m = ds / T with ds = exp(lse), T = ds + lam den + eps */
-    const double ds = exp(f.lse[i]);
-    const double T = ds + lam * f.den[i] + p->eps;
-    const double dds = dm * (lam * f.den[i] + p->eps) / (T * T);
-    dlse[i] = dds * ds;
-    dden[i] += -dm * lam * ds / (T * T);
-    lam_grad += -dm * f.den[i] * ds / (T * T);
+    /* m = ds / (ds + c) with ds = exp(lse), c = lam den + eps:
+     * dm/dlse = c w, dm/dc = -w, w = ds / (ds + c)^2 */
+    const double c = lam * f.den[i] + p->eps;
+    double mm, w;
+    mass_ratio(f.lse[i], c, &mm, &w);
+    dlse[i] = dm * c * w;
+    dden[i] += -dm * lam * w;
+    lam_grad += -dm * f.den[i] * w;
   }
   *dlam = lam_grad;
 

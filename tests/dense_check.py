@@ -84,8 +84,10 @@ def features_torch(x: torch.Tensor, planes: torch.Tensor, scale: float, tau: flo
 
 
 def dense_forward(q, k, v, mask, planes_lr, lam, causal, scale, tau=1.0, eps=1e-6,
-                  g_s=None, g_lr=None):
-    """Dense fp64 ELSAA forward of one head. q,k,v torch float64 [N, d]."""
+                  g_s=None, g_lr=None, logistic=False):
+    """Dense fp64 ELSAA forward of one head. q,k,v torch float64 [N, d].
+    logistic: evaluate Eq. 5 as the logistic function of lse - log(lam d_lr + eps)
+    (the same value; needed where exp(lse) or its square would overflow)."""
     N = q.shape[0]
     Mt = torch.as_tensor(mask)
     S = (q @ k.t()) * scale
@@ -100,8 +102,11 @@ def dense_forward(q, k, v, mask, planes_lr, lam, causal, scale, tau=1.0, eps=1e-
         Wl = torch.tril(Wl)
     d_lr = Wl.sum(dim=1)
     O_lr = (Wl @ v) / d_lr[:, None]
-    ds = torch.exp(lse)
-    m = ds / (ds + lam * d_lr + eps)
+    if logistic:
+        m = torch.sigmoid(lse - torch.log(lam * d_lr + eps))
+    else:
+        ds = torch.exp(lse)
+        m = ds / (ds + lam * d_lr + eps)
     gs = torch.ones(N, dtype=torch.float64) if g_s is None else g_s
     gl = torch.ones(N, dtype=torch.float64) if g_lr is None else g_lr
     O = (gs * m)[:, None] * O_s + gl[:, None] * O_lr

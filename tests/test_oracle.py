@@ -401,3 +401,31 @@ def test_backward_matches_dense_autograd(causal):
                  (g["dg_s"][0], tgs.grad), (g["dg_lr"][0], tgl.grad)):
         np.testing.assert_allclose(a, b.numpy(), atol=1e-10, rtol=1e-9)
     np.testing.assert_allclose(g["dlambda"][0], lam.grad.item(), rtol=1e-9)
+
+
+def test_backward_with_large_scores_matches_dense_autograd():
+    """Scores in the hundreds (lse up to about 450), where d_sparse = exp(lse)
+    squared exceeds the fp64 range, with lambda large enough that Eq. 5's ratio m
+    takes every value in (0, 1) across the rows: the oracle stays finite and agrees
+    with autograd of the dense formulation (Eq. 5 as a logistic function there)."""
+    w = small(True, N=128, d=16, block=16, r=32)
+    sc = 45.0
+    p = ref.RefParams.from_workload(w, scale=sc)
+    q, k, v, do, ps, pl = head(w, 67)
+    lam_v = 1e150
+    _, _, qp, kp = run_select(w, p, q, k, ps)
+    M = D.support_mask(128, 16, True, qp[0], kp[0])
+    tq, tk, tv = (torch.from_numpy(x).clone().requires_grad_(True) for x in (q, k, v))
+    lam = torch.tensor(lam_v, dtype=torch.float64, requires_grad=True)
+    dn = D.dense_forward(tq, tk, tv, M, torch.from_numpy(pl[0]), lam, True, sc, logistic=True)
+    m = dn["m"].detach().numpy()
+    assert dn["lse"].max().item() > 354.0 and m.min() < 0.05 and m.max() > 0.95
+    (dn["O"] * torch.from_numpy(do)).sum().backward()
+    o = ref.forward(p, q[None], k[None], v[None], ps, pl, np.array([lam_v]))
+    g = ref.backward(p, q[None], k[None], v[None], do[None], ps, pl, np.array([lam_v]))
+    for x in (o["O"], g["dQ"], g["dK"], g["dV"], g["dg_s"], g["dlambda"]):
+        assert np.isfinite(x).all()
+    np.testing.assert_allclose(o["O"][0], dn["O"].detach().numpy(), atol=1e-10, rtol=1e-9)
+    for a, b in ((g["dQ"][0], tq.grad), (g["dK"][0], tk.grad), (g["dV"][0], tv.grad)):
+        np.testing.assert_allclose(a, b.numpy(), atol=1e-8 * np.abs(b.numpy()).max(), rtol=1e-7)
+    np.testing.assert_allclose(g["dlambda"][0], lam.grad.item(), rtol=1e-7)
