@@ -3,10 +3,11 @@
 
 One step is the whole hot path over one batch of resident synthetic inputs:
 elsaa_select (hash + sort), elsaa_lowrank_summary, elsaa_fwd and elsaa_bwd.
-Prints one JSON line: whole-job tokens/s (B * N tokens per fwd+bwd step), the
-roofline fraction of the dominant kernel (timed with HIP events on its launch
-stream through the library's diagnostics), and the oracle timed on this host's
-cores on a bounded sample of heads.
+Prints one JSON line: whole-job tokens/s (B * N tokens per fwd+bwd step, timed
+with no instrumentation), the roofline fraction of the dominant kernel (timed
+with HIP events on its launch stream through the library's diagnostics, in a
+second pass), the whole step's fraction of its own roofline, and the oracle
+timed on this host's cores on a bounded sample of heads.
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
 """
@@ -56,6 +57,24 @@ def kernel_work(w) -> dict:
         "hash": ("hbm", 2.0 * tok * d * e + 4.0 * tok, "GB/s"),
         "bwd_rows": ("hbm", 3.0 * tok * d * e + 40.0 * tok, "GB/s"),
     }
+
+
+def step_work(w) -> tuple[float, float]:
+    """Algorithmic flops and bytes of one fwd+bwd step over the whole batch.
+    Flops: 4 d per selected pair in the forward and 8 d in the backward; per token
+    4 r (d + 1) + 4 d L gamma for the low-rank branch in the forward, twice that in
+    the backward. Bytes: each token-head reads Q, K, V and writes O, lse, d_lr
+    (forward), reads Q, K, V, O, dO and its row statistics and writes dQ, dK, dV
+    (backward): 12 d e + 16; plus its two codes (4) and its share of the two
+    orders, written once and read twice (3 x 8 P / N)."""
+    BH, N, d, r = w.B * w.H, w.N, w.d, w.r
+    e = 2 if w.dtype == "bf16" else 4
+    tok = BH * N
+    perm_len = w.levels * (N // 2) if w.causal else N
+    flops = 12.0 * d * selected_pairs(w) * BH
+    flops += 3.0 * tok * (4.0 * r * (d + 1) + 4.0 * d * w.lr_tables * w.lr_bits)
+    nbytes = tok * (12.0 * d * e + 16.0 + 4.0 + 3.0 * 8.0 * perm_len / N)
+    return flops, nbytes
 
 
 def roofline(name, launches, total_ms, w, traffic_file):
@@ -118,9 +137,11 @@ def cpu_baseline(w, seed, n_heads, threads):
     ref.backward(p, np.stack(q), np.stack(k), np.stack(v), np.stack(do), ps, pl, np.ones(n_heads))
     t = time.perf_counter() - t0
     tokens_per_s = n_heads * w.N / (w.H * t)
-    return {"value": round(tokens_per_s, 1), "unit": UNIT, "cores": threads, "kind": "oracle",
+    return {"value": round(tokens_per_s, 1), "unit": UNIT, "cores": threads,
+            "host_cpus": os.cpu_count(), "kind": "oracle",
             "sample": f"{n_heads} of {w.B * w.H} heads at full N={w.N}, select+fwd+bwd in fp64, "
-                      f"{t:.1f} s wall on {threads} threads; scaled by heads"}
+                      f"{t:.1f} s wall on {threads} threads (OpenMP over heads; the host shows "
+                      f"{os.cpu_count()} CPUs); scaled by heads"}
 
 
 def main():
@@ -173,7 +194,8 @@ def main():
         step()
     torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
-    _lib.profile(True)
+    # The headline: K steps with no instrumentation, between two events on the
+    # stream every call enqueues on.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -181,17 +203,32 @@ def main():
         step()
     end.record()
     torch.cuda.synchronize()
-    _lib.profile(False)
     ms = start.elapsed_time(end) / args.steps
-    rep = _lib.profile_report()
     tokens = w.B * w.N
     value = tokens / (ms / 1e3)
+    print(f"[bench] timed: {ms:.4f} ms per step", file=sys.stderr, flush=True)
+    # Per-kernel times from a second pass with the library's launch events on.
+    psteps = max(1, min(args.steps, 10))
+    _lib.profile(True)
+    for _ in range(psteps):
+        step()
+    torch.cuda.synchronize()
+    _lib.profile(False)
+    rep = _lib.profile_report()
     kernels = {k: {"launches": n, "avg_us": round(t / n * 1e3, 1),
-                   "ms_per_step": round(t / args.steps, 3)} for k, (n, t) in sorted(rep.items())}
+                   "ms_per_step": round(t / psteps, 3)} for k, (n, t) in sorted(rep.items())}
     dom = max(rep, key=lambda k: rep[k][1])
     roof = roofline(dom, rep[dom][0], rep[dom][1], w,
                     os.path.join(ROOT, "profiles", "traffic.json"))
-    print("[bench] timed; kernels: " + json.dumps(kernels), file=sys.stderr, flush=True)
+    if roof is None:
+        roof = {"kernel": dom, "avg_launch_us": round(rep[dom][1] / rep[dom][0] * 1e3, 1)}
+    f_alg, b_alg = step_work(w)
+    t_roof = max(f_alg / (PEAK_MFMA[w.dtype] * 1e12), b_alg / (PEAK_HBM_GBS * 1e9))
+    roof["step_frac"] = round(t_roof / (ms / 1e3), 4)
+    roof["step"] = {"flops": f_alg, "bytes": b_alg, "t_roof_us": round(t_roof * 1e6, 1),
+                    "bound": "mfma" if f_alg / (PEAK_MFMA[w.dtype] * 1e12) >=
+                             b_alg / (PEAK_HBM_GBS * 1e9) else "hbm"}
+    print("[bench] profiled; kernels: " + json.dumps(kernels), file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -38,6 +38,23 @@
  *   - Results are bitwise reproducible run to run (no floating-point atomics).
  *   - Selections (codes and permutations) are exact: they reproduce, bit for bit,
  *     the fp64 fused-multiply-add sign tests described at elsaa_select.
+ *   - Any pointer that is not 16-byte aligned is rejected with
+ *     ELSAA_ERR_INVALID_ARG (the kernels read rows with 16-byte vector loads).
+ *   - Sizes that are valid for the method but for which no kernel variant is
+ *     built (LDS or register limits) return ELSAA_ERR_UNSUPPORTED; a call never
+ *     returns ELSAA_OK without having enqueued all of its work.
+ *
+ * Deliberate differences from a minimal statement of the four calls:
+ *   - elsaa_fwd returns the two normalized branch outputs O_s and O_lr next to the
+ *     fused O, and elsaa_bwd takes them in place of O: the backward needs
+ *     <dO, O_s> and <dO, O_lr> separately (Eq. 4 weighs them with different row
+ *     factors), and recovering them from O alone would divide by a gate.
+ *   - elsaa_workspace_size takes the call it sizes (the four calls need different
+ *     scratch), instead of one size for all.
+ *   - The low-rank statistics A are laid out [.., d_h, r] (value channel major):
+ *     the kernels read a channel's statistics of all features as one row.
+ *   - The RACE tables have 4 hyperplanes each (16 buckets, lr_bits = 4) and the
+ *     sortLSH codes at most 12 bits: the sizes the kernels are built for.
  */
 #ifndef ELSAA_H
 #define ELSAA_H
@@ -154,29 +171,33 @@ elsaa_status elsaa_lowrank_summary(const elsaa_params* p, const void* K, const v
  *   lambda           : fp32 [H] (>= 0), the lambda of Eq. 5 per head.
  *   g_s, g_lr        : fp32 [B, H, N] gates g_sparse, g_lr of Eq. 4, or NULL for 1.
  *   O (out)          : [B, H, N, d_h] dtype, the fused output.
- *   O_s, O_lr (out)  : [B, H, N, d_h] dtype, the normalized branch outputs (saved
- *                      for elsaa_bwd).
+ *   O_s (out)        : fp32 [B, H, N, d_h], the normalized sparse output (Section
+ *                      3.2), saved for elsaa_bwd. It is kept in fp32 because the
+ *                      backward forms D_i = g_s m_i^2 <dO_i, O_s,i>, which nearly
+ *                      cancels <dO_i, V_j> in dS_ij when a query's softmax is peaked.
+ *   O_lr (out)       : [B, H, N, d_h] dtype, the normalized low-rank output (Section
+ *                      3.1), saved for elsaa_bwd.
  *   lse_s (out)      : fp32 [B, H, N], log d_sparse (log-sum-exp over the support).
  *   d_lr (out)       : fp32 [B, H, N], the low-rank denominator phi(Q_i)^T z.
  */
 elsaa_status elsaa_fwd(const elsaa_params* p, const void* Q, const void* K, const void* V,
                        const float* planes_lr, const int32_t* q_perm, const int32_t* k_perm,
                        const float* A, const float* z, const float* lambda, const float* g_s,
-                       const float* g_lr, void* O, void* O_s, void* O_lr, float* lse_s,
+                       const float* g_lr, void* O, float* O_s, void* O_lr, float* lse_s,
                        float* d_lr, void* ws, size_t ws_bytes, void* stream);
 
 /* Backward of elsaa_fwd for training: the chain rule through Eq. 4, Eq. 5, the
  * exact block softmaxes and the RACE readout, with the selection held fixed (it is
  * piecewise constant in Q and K).
  *   dO                      : [B, H, N, d_h] dtype, gradient of the loss w.r.t. O.
- *   O_s, O_lr, lse_s, d_lr  : as saved by elsaa_fwd for the same inputs.
+ *   O_s (fp32), O_lr, lse_s, d_lr : as saved by elsaa_fwd for the same inputs.
  *   dQ, dK, dV (out)        : [B, H, N, d_h] dtype (overwritten).
  *   dlambda (out)           : fp32 [H] or NULL (overwritten; summed over the batch).
  *   dg_s, dg_lr (out)       : fp32 [B, H, N] or NULL (gradients w.r.t. the gates,
  *                             also when g_s / g_lr are NULL, i.e. at gate 1).
  */
 elsaa_status elsaa_bwd(const elsaa_params* p, const void* Q, const void* K, const void* V,
-                       const void* dO, const void* O_s, const void* O_lr,
+                       const void* dO, const float* O_s, const void* O_lr,
                        const float* planes_lr, const int32_t* q_perm, const int32_t* k_perm,
                        const float* A, const float* z, const float* lse_s, const float* d_lr,
                        const float* lambda, const float* g_s, const float* g_lr, void* dQ,

@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <string>
 
@@ -118,14 +119,25 @@ elsaa_status make_problem(const elsaa_params* p, Problem* pb, bool* empty) {
   return ELSAA_OK;
 }
 
-elsaa_status need(const void* ptr, const char* name) {
-  return ptr ? ELSAA_OK : fail(ELSAA_ERR_INVALID_ARG, "%s is NULL", name);
+// A pointer the kernels read or write with 16-byte vector accesses: NULL is an
+// error for a required one (optional ones may be NULL), and any that is given
+// must be 16-byte aligned.
+elsaa_status need(const void* ptr, const char* name, bool required) {
+  if (!ptr) return required ? fail(ELSAA_ERR_INVALID_ARG, "%s is NULL", name) : ELSAA_OK;
+  if (reinterpret_cast<uintptr_t>(ptr) & 15u)
+    return fail(ELSAA_ERR_INVALID_ARG, "%s = %p is not 16-byte aligned", name, ptr);
+  return ELSAA_OK;
 }
 
-#define NEED(x)                                          \
-  do {                                                   \
-    elsaa_status s_ = need((const void*)(x), #x);        \
-    if (s_ != ELSAA_OK) return s_;                       \
+#define NEED(x)                                                \
+  do {                                                         \
+    elsaa_status s_ = need((const void*)(x), #x, true);        \
+    if (s_ != ELSAA_OK) return s_;                             \
+  } while (0)
+#define OPTIONAL(x)                                            \
+  do {                                                         \
+    elsaa_status s_ = need((const void*)(x), #x, false);       \
+    if (s_ != ELSAA_OK) return s_;                             \
   } while (0)
 
 size_t ws_bytes_for(const Problem& pb, int call) {
@@ -143,7 +155,7 @@ elsaa_status check_ws(const Problem& pb, int call, const void* ws, size_t ws_byt
   if (ws_bytes < n)
     return fail(ELSAA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, n);
   if (n > 0 && !ws) return fail(ELSAA_ERR_INVALID_ARG, "ws is NULL but %zu bytes are needed", n);
-  return ELSAA_OK;
+  return need(ws, "ws", false);
 }
 
 elsaa_status launched() {
@@ -182,6 +194,7 @@ elsaa_status elsaa_select(const elsaa_params* p, const void* Q, const void* K,
   if (empty) return ELSAA_OK;
   NEED(Q); NEED(K); NEED(planes_s); NEED(q_code); NEED(k_code);
   if (elsaa::perm_stride(pb.N, pb.levels, pb.causal) > 0) { NEED(q_perm); NEED(k_perm); }
+  OPTIONAL(q_perm); OPTIONAL(k_perm);
   {
     elsaa_status s_ = check_ws(pb, ELSAA_CALL_SELECT, ws, ws_bytes);
     if (s_ != ELSAA_OK) return s_;
@@ -208,24 +221,29 @@ elsaa_status elsaa_lowrank_summary(const elsaa_params* p, const void* K, const v
 elsaa_status elsaa_fwd(const elsaa_params* p, const void* Q, const void* K, const void* V,
                        const float* planes_lr, const int32_t* q_perm, const int32_t* k_perm,
                        const float* A, const float* z, const float* lambda, const float* g_s,
-                       const float* g_lr, void* O, void* O_s, void* O_lr, float* lse_s,
+                       const float* g_lr, void* O, float* O_s, void* O_lr, float* lse_s,
                        float* d_lr, void* ws, size_t ws_bytes, void* stream) {
   PROLOGUE(ELSAA_CALL_FWD);
   if (empty) return ELSAA_OK;
   NEED(Q); NEED(K); NEED(V); NEED(planes_lr); NEED(A); NEED(z);
   if (elsaa::perm_stride(pb.N, pb.levels, pb.causal) > 0) { NEED(q_perm); NEED(k_perm); }
-  NEED(lambda); NEED(O); NEED(O_s); NEED(O_lr); NEED(lse_s); NEED(d_lr);
+  OPTIONAL(q_perm); OPTIONAL(k_perm);
+  NEED(lambda); OPTIONAL(g_s); OPTIONAL(g_lr);
+  NEED(O); NEED(O_s); NEED(O_lr); NEED(lse_s); NEED(d_lr);
   {
     elsaa_status s_ = check_ws(pb, ELSAA_CALL_FWD, ws, ws_bytes);
     if (s_ != ELSAA_OK) return s_;
   }
+  if (!elsaa::launch_fwd(pb, Q, K, V, planes_lr, q_perm, k_perm, A, z, lambda, g_s, g_lr, O, O_s,
+                         O_lr, lse_s, d_lr, ws, (hipStream_t)stream, true))
+    return fail(ELSAA_ERR_UNSUPPORTED, "no forward kernel variant is built for these sizes");
   elsaa::launch_fwd(pb, Q, K, V, planes_lr, q_perm, k_perm, A, z, lambda, g_s, g_lr, O, O_s, O_lr,
-                    lse_s, d_lr, ws, (hipStream_t)stream);
+                    lse_s, d_lr, ws, (hipStream_t)stream, false);
   return launched();
 }
 
 elsaa_status elsaa_bwd(const elsaa_params* p, const void* Q, const void* K, const void* V,
-                       const void* dO, const void* O_s, const void* O_lr,
+                       const void* dO, const float* O_s, const void* O_lr,
                        const float* planes_lr, const int32_t* q_perm, const int32_t* k_perm,
                        const float* A, const float* z, const float* lse_s, const float* d_lr,
                        const float* lambda, const float* g_s, const float* g_lr, void* dQ,
@@ -235,14 +253,20 @@ elsaa_status elsaa_bwd(const elsaa_params* p, const void* Q, const void* K, cons
   if (empty) return ELSAA_OK;
   NEED(Q); NEED(K); NEED(V); NEED(dO); NEED(O_s); NEED(O_lr); NEED(planes_lr);
   if (elsaa::perm_stride(pb.N, pb.levels, pb.causal) > 0) { NEED(q_perm); NEED(k_perm); }
-  NEED(A); NEED(z); NEED(lse_s); NEED(d_lr); NEED(lambda); NEED(dQ); NEED(dK);
-  NEED(dV);
+  OPTIONAL(q_perm); OPTIONAL(k_perm);
+  NEED(A); NEED(z); NEED(lse_s); NEED(d_lr); NEED(lambda); OPTIONAL(g_s); OPTIONAL(g_lr);
+  NEED(dQ); NEED(dK); NEED(dV); OPTIONAL(dlambda); OPTIONAL(dg_s); OPTIONAL(dg_lr);
   {
     elsaa_status s_ = check_ws(pb, ELSAA_CALL_BWD, ws, ws_bytes);
     if (s_ != ELSAA_OK) return s_;
   }
+  if (!elsaa::launch_bwd(pb, Q, K, V, dO, O_s, O_lr, planes_lr, q_perm, k_perm, A, z, lse_s, d_lr,
+                         lambda, g_s, g_lr, dQ, dK, dV, dlambda, dg_s, dg_lr, ws,
+                         (hipStream_t)stream, true))
+    return fail(ELSAA_ERR_UNSUPPORTED, "no backward kernel variant is built for these sizes");
   elsaa::launch_bwd(pb, Q, K, V, dO, O_s, O_lr, planes_lr, q_perm, k_perm, A, z, lse_s, d_lr,
-                    lambda, g_s, g_lr, dQ, dK, dV, dlambda, dg_s, dg_lr, ws, (hipStream_t)stream);
+                    lambda, g_s, g_lr, dQ, dK, dV, dlambda, dg_s, dg_lr, ws, (hipStream_t)stream,
+                    false);
   return launched();
 }
 

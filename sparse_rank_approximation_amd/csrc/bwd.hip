@@ -11,6 +11,16 @@
 //   dlambda = -sum_i dm_i d_lr,i m_i^2 / d_s; dg_s,i = m_i a_i; dg_lr,i = b_i.
 // m_i^2 / d_s is evaluated as exp(lse - 2 log(d_s + lambda d_lr + eps)).
 //
+// dQ_i = scale sum_j dS_ij K_j is formed relative to the query: since p_i sums
+// to 1 over the support, sum_j dS_ij = c_i a_i - D_i = g_s a_i m_i (1 - m_i)
+// =: sigma_i exactly, so dQ_i = scale (sum_j dS_ij (K_j - Q_i) + sigma_i Q_i).
+// Each block stores its part of the first sum (its own block, the causal leaf
+// or the only non-causal one, adds sigma_i Q_i). When a query's selected keys
+// lie near it, as sortLSH makes them, these parts are small and cancel little
+// across levels, so storing them per level in the element type loses little;
+// the plain parts sum_j dS_ij K_j share a large component along the keys' mean
+// that cancels between levels.
+//
 // Kernels, in launch order:
 //   bwd_rows_kernel      per-row terms above, dg_s, dg_lr, per-block dlambda sums;
 //   dlam_reduce_kernel   dlambda per head (fixed order: deterministic);
@@ -97,11 +107,12 @@ __global__ void planes_transpose_kernel(const float* __restrict__ R, int L, int 
 // Row terms.
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
-    bwd_rows_kernel(const T* __restrict__ dO, const T* __restrict__ Os, const T* __restrict__ Olr,
+    bwd_rows_kernel(const T* __restrict__ dO, const float* __restrict__ Os, const T* __restrict__ Olr,
                     const float* __restrict__ lse, const float* __restrict__ dlr,
                     const float* __restrict__ lambda, const float* __restrict__ gs,
                     const float* __restrict__ glr, float eps, int H, int N, float* __restrict__ rc,
-                    float* __restrict__ rD, float* __restrict__ re, float* __restrict__ rdd,
+                    float* __restrict__ rD, float* __restrict__ rsig, float* __restrict__ re,
+                    float* __restrict__ rdd,
                     float* __restrict__ dgs, float* __restrict__ dglr, float* __restrict__ dlam_part) {
   constexpr int TPR = D / 8, RPB = 256 / TPR;
   __shared__ float red[RPB];
@@ -115,7 +126,7 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float x = to_f(dO[row + e]);
-      a += x * to_f(Os[row + e]);
+      a += x * Os[row + e];
       b += x * to_f(Olr[row + e]);
     }
   }
@@ -137,6 +148,9 @@ __global__ void __launch_bounds__(256)
     const float dm = g1 * a;
     rc[k] = g1 * m;
     rD[k] = g1 * a * m * m;
+    // sum over the support of dS_ij = c a - D (p_i sums to 1), with 1 - m formed
+    // as (lambda d_lr + eps) / (d_s + lambda d_lr + eps)
+    rsig[k] = g1 * a * m * fast_exp(lo - lt);
     re[k] = g2 / den;
     rdd[k] = -g2 * b / den - dm * lam * w2;
     dl = -dm * den * w2;
@@ -197,7 +211,7 @@ struct SbwdSmem {
   T Vs[HK ? KT : 1][LD];
   T Qs[HQ ? KT : 1][LD];
   T Os[HQ ? KT : 1][LD];  // c * dO
-  float lse[KT], Dd[KT], cq[KT];
+  float lse[KT], Dd[KT], cq[KT], sig[KT];
   int kidx[KT], qidx[KT];
 };
 
@@ -238,7 +252,8 @@ __global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
     sparse_bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                       const T* __restrict__ dO, const float* __restrict__ lse,
                       const float* __restrict__ rc, const float* __restrict__ rD,
-                      const int32_t* __restrict__ qperm, const int32_t* __restrict__ kperm, int N,
+                      const float* __restrict__ rsig, const int32_t* __restrict__ qperm,
+                      const int32_t* __restrict__ kperm, int N,
                       int causal, int levels, float scale, T* __restrict__ dQp,
                       T* __restrict__ dKp, T* __restrict__ dVp) {
   typedef MF<T> M;
@@ -279,6 +294,7 @@ __global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
     sm.lse[t] = qi >= 0 ? lse[rowbase + qi] : 0.0f;
     sm.Dd[t] = qi >= 0 ? rD[rowbase + qi] : 0.0f;
     sm.cq[t] = qi >= 0 ? rc[rowbase + qi] : 0.0f;
+    sm.sig[t] = qi >= 0 ? rsig[rowbase + qi] : 0.0f;
   }
   __syncthreads();
   if constexpr (Sm::HK) {
@@ -400,6 +416,11 @@ __global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
       floatx16 acc[D / 32];
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) acc[dt] = zero16();
+      // The query's row in the accumulator layout (for the shift below), in
+      // flight during the products.
+      DRow<T, D / 32> qrow;
+      qrow.load(Q + (rowbase + (qvalid ? iq : 0)) * D, h);
+      float sig = 0.0f;  // sum over the block's keys of dS (as rounded for the product)
       const int nkt = leaf ? qw + 1 : KT / 32;
       for (int kt = 0; kt < nkt; ++kt) {
         floatx16 s = zero16(), dp = zero16();
@@ -428,20 +449,27 @@ __global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
 #pragma unroll
         for (int ks2 = 0; ks2 < 32 / M::KSTEP; ++ks2) {
           const typename M::frag sf = M::from_acc(s, ks2);
+          sig = frag_sum<T>(sf, sig);
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt)
             acc[dt] = M::mma(tr_frag<T>(&sm.Ks[0][0], LD, 32 * kt, 32 * dt, ks2, lane, true), sf, acc[dt]);
         }
       }
+      // (the query's own block, its leaf or its only block, adds the support-wide
+      // sum back)
+      sig = sum_halves(sig) - (lev < 0 ? sm.sig[query] : 0.0f);
+      float qv[D / 32][4][4];
+      qrow.unpack(qv);
       if (qvalid) {
         const size_t sl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_future_b(iq, N, lev)
                                    : (size_t)iq;
         T* dst = dQp + ((size_t)bh * slots + sl) * D;  // (qvalid: the same for a query's two lanes)
+        // The block's dQ part relative to the query: sum_j dS_ij (K_j - Q_i).
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           float x[16];
 #pragma unroll
-          for (int v = 0; v < 16; ++v) x[v] = acc[dt][v] * scale;
+          for (int v = 0; v < 16; ++v) x[v] = (acc[dt][v] - sig * qv[dt][v >> 2][v & 3]) * scale;
           store_tile_row(dst + 32 * dt, x, h);
         }
       }
@@ -471,6 +499,7 @@ struct Sb2Smem {
   alignas(16) float lse[KT];  // lse log2 e; +inf for rows past the block (P = 0)
   alignas(16) float Dd[KT];
   alignas(16) float cq[KT];
+  float sig[KT];              // sum over the query's whole support of dS_ij
   int qidx[KT], kidx[KT];    // token of each row of this block, -1 past the block
   int qnext[KT], knext[KT];  // the same for the next block
   alignas(16) __bf16 Qs[KT][LD];
@@ -484,7 +513,8 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
     sparse_bwd2_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                        const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                        const float* __restrict__ lse, const float* __restrict__ rc,
-                       const float* __restrict__ rD, const int32_t* __restrict__ qperm,
+                       const float* __restrict__ rD, const float* __restrict__ rsig,
+                       const int32_t* __restrict__ qperm,
                        const int32_t* __restrict__ kperm, int N, int causal, int levels,
                        float scale, int items, int total, __bf16* __restrict__ dQp,
                        __bf16* __restrict__ dKp, __bf16* __restrict__ dVp) {
@@ -532,7 +562,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
   // Registers holding the next block.
   Vec8<T> pq[GIT], po[GIT], pk[GIT];
   typename M::frag pv[KS];
-  float plse = 0.0f, pD = 0.0f, pc = 0.0f;
+  float plse = 0.0f, pD = 0.0f, pc = 0.0f, psig = 0.0f;
   bool pvalid = false;
   Rows prow{-1, -1, -1};
   auto gather = [&](size_t rb) __attribute__((always_inline)) {
@@ -553,6 +583,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
       plse = lse[k];
       pD = rD[k];
       pc = rc[k];
+      psig = rsig[k];
     }
   };
 
@@ -594,6 +625,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
       sm.lse[tid] = pvalid ? plse * kLog2e : INFINITY;  // (base 2)
       sm.Dd[tid] = pvalid ? pD : 0.0f;
       sm.cq[tid] = pvalid ? pc : 0.0f;
+      sm.sig[tid] = pvalid ? psig : 0.0f;
     }
     __syncthreads();
 
@@ -677,6 +709,10 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
     gather(nrb);
     prow = rows_of(min(g + 2 * G, total - 1), tid);
     gather_v(nrb);
+    // The rows of phase 2's query tile (for the dQ parts relative to the query),
+    // read before the barrier after which Qs holds dV.
+    DRow<T, D / 32> qrow;
+    qrow.load(&sm.Qs[key][0], h);
     __syncthreads();  // dS^T complete; Qs and Os no longer read
     // dV and dK tiles to LDS (rows = keys of the block) for row-contiguous stores.
 #pragma unroll
@@ -693,8 +729,11 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
         store4(&sm.Qs[key][c], xv);
         store4(&sm.Os[key][c], xk);
       }
-    // Phase 2: dQ^T = K^T dS^T for query tile w (leaf blocks: keys up to the tile).
+    // Phase 2: dQ^T = K^T dS^T for query tile w (leaf blocks: keys up to the tile),
+    // with sig = the sum of the tile's dS^T over the keys as rounded for the
+    // product.
     floatx16 dq[D / 32];
+    float sig = 0.0f;
     {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) dq[dt] = zero16();
@@ -711,21 +750,29 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
             ka[j][dt] = tr_frag<T>(&sm.Ks[0][0], LD, 0, 32 * dt, ks + j, lane, false);
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j) {
+          sig = frag_sum<T>(bq[j], sig);
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt) dq[dt] = M::mma(ka[j][dt], bq[j], dq[dt]);
+        }
       }
     }
+    // (the query's own block, its leaf or its only block, adds the support-wide
+    // sum back)
+    sig = sum_halves(sig) - (lev < 0 ? sm.sig[key] : 0.0f);
+    float qv[D / 32][4][4];
+    qrow.unpack(qv);
     __syncthreads();  // Ks no longer read; dV, dK tiles complete
-    // dQ tile to LDS (rows = queries of the block); the three gradient tiles then
-    // go out to their slots with row-contiguous 16-byte stores.
+    // dQ tile to LDS (rows = queries of the block), relative to the query; the
+    // three gradient tiles then go out to their slots with row-contiguous 16-byte
+    // stores.
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) {
         float xq[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) xq[e] = dq[dt][4 * gg + e] * scale;
+        for (int e = 0; e < 4; ++e) xq[e] = (dq[dt][4 * gg + e] - sig * qv[dt][gg][e]) * scale;
         store4(&sm.Ks[key][32 * dt + 8 * gg + 4 * h], xq);
       }
     __syncthreads();
@@ -1312,7 +1359,7 @@ BwdLayout bwd_layout(const Problem& pb) {
   l.nblk = (pb.N + rpb - 1) / rpb;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t off = 0;
-  l.rows = off; off += al(sizeof(float) * 4 * BH * N);
+  l.rows = off; off += al(sizeof(float) * 5 * BH * N);
   l.dlam = off; off += al(sizeof(float) * BH * l.nblk);
   l.parts = off; off += al(3 * BH * slots * D * pb.elem);
   l.gsum = off; off += al(summary_ws_bytes(pb));
@@ -1337,7 +1384,7 @@ size_t bwd_ws_bytes(const Problem& pb) { return bwd_layout(pb).total; }
 
 size_t bwd_lds_need(const Problem& pb) {
   const size_t e = pb.elem, d = pb.d, kt = pb.s < 32 ? 32 : pb.s;
-  const size_t sb = e * (2 * kt * (d + (pb.bf16 ? 24 : 8))) + 20 * kt;  // one-role launch
+  const size_t sb = e * (2 * kt * (d + (pb.bf16 ? 24 : 8))) + 24 * kt;  // one-role launch
   size_t lr = 0;
   with_T(pb.bf16, [&](auto tp) {
     using T = ELSAA_T(tp);
@@ -1366,12 +1413,13 @@ size_t bwd_lds_need(const Problem& pb) {
   return sb > lr ? sb : lr;
 }
 
-void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, const void* dO,
-                const void* O_s, const void* O_lr, const float* planes_lr, const int32_t* qperm,
+bool launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, const void* dO,
+                const float* O_s, const void* O_lr, const float* planes_lr, const int32_t* qperm,
                 const int32_t* kperm, const float* A, const float* z, const float* lse,
                 const float* d_lr, const float* lambda, const float* g_s, const float* g_lr,
                 void* dQ, void* dK, void* dV, float* dlambda, float* dg_s, float* dg_lr, void* ws,
-                hipStream_t st) {
+                hipStream_t st, bool dry) {
+  bool ok = true;
   const BwdLayout lay = bwd_layout(pb);
   char* base = (char*)ws;
   const size_t BH = (size_t)pb.B * pb.H, N = pb.N;
@@ -1379,6 +1427,7 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
   float* rD = rc + BH * N;
   float* re = rD + BH * N;
   float* rdd = re + BH * N;
+  float* rsig = rdd + BH * N;
   float* dlam_part = (float*)(base + lay.dlam);
   const size_t slots = partial_slots(pb.N, pb.levels, pb.causal);
   char* parts = base + lay.parts;
@@ -1403,21 +1452,30 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
     using T = ELSAA_T(tp);
     with_D(pb.d, [&](auto dc) {
       constexpr int D = ELSAA_C(dc);
-      ELSAA_LAUNCH("planes_t", planes_transpose_kernel, dim3(pb.H), dim3(256), 0, st, planes_lr,
-                   pb.L, pb.d, pw, RT);
-      ELSAA_LAUNCH("bwd_rows", (bwd_rows_kernel<T, D>), dim3(lay.nblk, BH), dim3(256), 0, st,
-                         (const T*)dO, (const T*)O_s, (const T*)O_lr, lse, d_lr, lambda, g_s,
-                         g_lr, pb.eps, pb.H, pb.N, rc, rD, re, rdd, dg_s, dg_lr, dlam_part);
-      if (dlambda)
-        ELSAA_LAUNCH("dlam_reduce", dlam_reduce_kernel, dim3(pb.H), dim3(256), 0, st, dlam_part,
-                           pb.B, pb.H, lay.nblk, dlambda);
-      run_lr_sums(pb, Q, dO, re, rdd, planes_lr, S, Z, st);
-      run_lr_scan(pb, S, Z, pb.causal ? 2 : 0, Gs, gzs, st);
+      if (!dry) {
+        ELSAA_LAUNCH("planes_t", planes_transpose_kernel, dim3(pb.H), dim3(256), 0, st, planes_lr,
+                     pb.L, pb.d, pw, RT);
+        ELSAA_LAUNCH("bwd_rows", (bwd_rows_kernel<T, D>), dim3(lay.nblk, BH), dim3(256), 0, st,
+                           (const T*)dO, O_s, (const T*)O_lr, lse, d_lr, lambda, g_s,
+                           g_lr, pb.eps, pb.H, pb.N, rc, rD, rsig, re, rdd, dg_s, dg_lr,
+                           dlam_part);
+        if (dlambda)
+          ELSAA_LAUNCH("dlam_reduce", dlam_reduce_kernel, dim3(pb.H), dim3(256), 0, st, dlam_part,
+                             pb.B, pb.H, lay.nblk, dlambda);
+        run_lr_sums(pb, Q, dO, re, rdd, planes_lr, S, Z, st);
+        run_lr_scan(pb, S, Z, pb.causal ? 2 : 0, Gs, gzs, st);
+      }
       auto run_sparse = [&](auto sc) {
         constexpr int SB = ELSAA_C(sc);
         const dim3 grid(items, BH);
-        if constexpr (std::is_same_v<T, __bf16> && SB <= 128 &&
-                      sizeof(Sb2Smem<D, SB>) <= kLdsBytes) {
+        if constexpr (!(std::is_same_v<T, __bf16> && SB <= 128 &&
+                        sizeof(Sb2Smem<D, SB>) <= kLdsBytes) &&
+                      !(sizeof(SbwdSmem<T, D, SB, 3>) <= kLdsBytes && SB <= 128) &&
+                      !(sizeof(SbwdSmem<T, D, SB, 1>) <= kLdsBytes)) {
+          ok = false;
+        } else if (dry) {
+        } else if constexpr (std::is_same_v<T, __bf16> && SB <= 128 &&
+                             sizeof(Sb2Smem<D, SB>) <= kLdsBytes) {
           constexpr int NT = 64 * (SB < 32 ? 1 : SB / 32);
           const int total = items * (int)BH;
           const int G = persistent_grid((const void*)sparse_bwd2_kernel<D, SB>, NT, total);
@@ -1427,22 +1485,22 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
           const int32_t* qp = qperm ? qperm : (const int32_t*)rc;
           const int32_t* kp = kperm ? kperm : (const int32_t*)rc;
           ELSAA_LAUNCH("sparse_bwd", (sparse_bwd2_kernel<D, SB>), dim3(G), dim3(NT), 0, st,
-                       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, lse, rc, rD, qp, kp,
+                       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, lse, rc, rD, rsig, qp, kp,
                        pb.N, (int)pb.causal, pb.levels, pb.scale, items, total, (T*)dQp,
                        (T*)dKp, (T*)dVp);
         } else if constexpr (sizeof(SbwdSmem<T, D, SB, 3>) <= kLdsBytes && SB <= 128) {
           ELSAA_LAUNCH("sparse_bwd", (sparse_bwd_kernel<T, D, SB, 3>), grid,
                        dim3(sbwd_threads<SB>(3)), 0, st, (const T*)Q, (const T*)K, (const T*)V,
-                       (const T*)dO, lse, rc, rD, qperm, kperm, pb.N, (int)pb.causal, pb.levels,
+                       (const T*)dO, lse, rc, rD, rsig, qperm, kperm, pb.N, (int)pb.causal, pb.levels,
                        pb.scale, (T*)dQp, (T*)dKp, (T*)dVp);
         } else if constexpr (sizeof(SbwdSmem<T, D, SB, 1>) <= kLdsBytes) {
           ELSAA_LAUNCH("sparse_bwd", (sparse_bwd_kernel<T, D, SB, 1>), grid,
                        dim3(sbwd_threads<SB>(1)), 0, st, (const T*)Q, (const T*)K, (const T*)V,
-                       (const T*)dO, lse, rc, rD, qperm, kperm, pb.N, (int)pb.causal, pb.levels,
+                       (const T*)dO, lse, rc, rD, rsig, qperm, kperm, pb.N, (int)pb.causal, pb.levels,
                        pb.scale, (T*)dQp, (T*)dKp, (T*)dVp);
           ELSAA_LAUNCH("sparse_bwd_q", (sparse_bwd_kernel<T, D, SB, 2>), grid,
                        dim3(sbwd_threads<SB>(2)), 0, st, (const T*)Q, (const T*)K, (const T*)V,
-                       (const T*)dO, lse, rc, rD, qperm, kperm, pb.N, (int)pb.causal, pb.levels,
+                       (const T*)dO, lse, rc, rD, rsig, qperm, kperm, pb.N, (int)pb.causal, pb.levels,
                        pb.scale, (T*)dQp, (T*)dKp, (T*)dVp);
         }
       };
@@ -1459,7 +1517,9 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
         constexpr int SQ = walk_step<T, D, LPG, 128, RTB + sizeof(QdaLds<LPG>)>();
         constexpr int SK = walk_step<T, D, LPG, 64,
                                      RTB + sizeof(KdaLds<LPG>) + 2 * sizeof(T) * 64 * tile_ld<T>(16 * LPG)>();
-        if constexpr (SQ > 0 && SK > 0) {
+        if constexpr (SQ == 0 || SK == 0) {
+          ok = false;
+        } else if (!dry) {
           const int span_q = pb.causal ? pb.chunk : noncausal_span(pb.N, (int)BH, SQ);
           const int span_k = pb.causal ? pb.chunk : noncausal_span(pb.N, (int)BH, SK);
           // One feature group: the gradients go straight out (SINGLE); two: the
@@ -1491,9 +1551,10 @@ void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
         case 4: run_lr(std::integral_constant<int, 4>{}); break;
         default: run_lr(std::integral_constant<int, 8>{}); break;
       }
-      launch_combine(pb, dQp, dKp, dVp, dQ, dK, dV, st);
+      if (!dry) launch_combine(pb, dQp, dKp, dVp, dQ, dK, dV, st);
     });
   });
+  return ok;
 }
 
 }  // namespace elsaa

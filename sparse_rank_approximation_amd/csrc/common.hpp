@@ -165,6 +165,21 @@ __device__ __forceinline__ typename MF<T>::frag row_frag(const T* X, int ld, int
   return M::load(X + (size_t)(r0 + (lane & 31)) * ld + k0 + ks * M::KSTEP + M::KPL * (lane >> 5));
 }
 
+// acc + the sum of a fragment's elements, as the product sees them (bf16: four
+// v_dot2_f32_bf16 against ones).
+template <typename T>
+__device__ __forceinline__ float frag_sum(const typename MF<T>::frag& f, float acc);
+template <>
+__device__ __forceinline__ float frag_sum<__bf16>(const bf16x8& f, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{f[2 * e], f[2 * e + 1]}, one, acc, false);
+  return acc;
+}
+template <>
+__device__ __forceinline__ float frag_sum<float>(const float& f, float acc) { return acc + f; }
+
 __device__ __forceinline__ floatx16 zero16() {
   floatx16 z;
 #pragma unroll

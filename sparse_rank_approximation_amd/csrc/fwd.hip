@@ -238,7 +238,7 @@ template <typename T, int D, int LP, int STEP, bool PLDS>
 __global__ void __launch_bounds__(512)
     fwd_epilogue_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                         const float* __restrict__ planes, const float* __restrict__ A,
-                        const float* __restrict__ z, const T* __restrict__ Os,
+                        const float* __restrict__ z, const float* __restrict__ Os,
                         const float* __restrict__ lse_s, const float* __restrict__ lambda,
                         const float* __restrict__ gs, const float* __restrict__ glr,
                         T* __restrict__ O, T* __restrict__ Olr, float* __restrict__ dlr_out,
@@ -345,7 +345,7 @@ __global__ void __launch_bounds__(512)
       // key loads of the step (so that waiting for them does not wait for those);
       // with them, after the barrier, where the registers are free.
       const size_t k = (size_t)bh * N + min(qtok, N - 1);
-      DRow<T, NDH> osr;
+      DRow<float, NDH> osr;
       float lse = 0.0f;
       if constexpr (!EARLY) {
         osr.load(Os + k * D, h, DT0);
@@ -495,11 +495,12 @@ size_t fwd_lds_need(const Problem& pb) {
   return need > sparse ? need : sparse;
 }
 
-void launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
+bool launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
                 const float* planes_lr, const int32_t* qperm, const int32_t* kperm,
                 const float* A, const float* z, const float* lambda, const float* g_s,
-                const float* g_lr, void* O, void* O_s, void* O_lr, float* lse, float* d_lr,
-                void* ws, hipStream_t st) {
+                const float* g_lr, void* O, float* O_s, void* O_lr, float* lse, float* d_lr,
+                void* ws, hipStream_t st, bool dry) {
+  bool ok = true;
   const int BH = pb.B * pb.H;
   const size_t slots = partial_slots(pb.N, pb.levels, pb.causal);
   float* Lpart = (float*)ws;
@@ -511,8 +512,9 @@ void launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
       constexpr int D = ELSAA_C(dc);
       auto run = [&](auto sc) {
         constexpr int SB = ELSAA_C(sc);
-        if constexpr (sparse_fwd_lds<T, D, SB>() <= kLdsBytes)
-        {
+        if constexpr (sparse_fwd_lds<T, D, SB>() > kLdsBytes) {
+          ok = false;
+        } else if (!dry) {
           constexpr int NT = 64 * (SB < 32 ? 1 : SB / 32);
           const int total = items * BH;
           const int G = persistent_grid((const void*)sparse_fwd_kernel<T, D, SB>, NT, total);
@@ -533,22 +535,25 @@ void launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
         case 128: run(std::integral_constant<int, 128>{}); break;
         default: run(std::integral_constant<int, 256>{}); break;
       }
-      launch_merge(pb, Opart, Lpart, O_s, lse, st);
+      if (!dry) launch_merge(pb, Opart, Lpart, O_s, lse, st);
       with_LP(pb.L, [&](auto lc) {
         constexpr int LP = ELSAA_C(lc);
         constexpr bool PLDS = epilogue_planes_in_lds<T, D, LP>();
         constexpr int STEP = epilogue_step<T, D, LP>();
-        if constexpr (STEP > 0) {
+        if constexpr (STEP == 0) {
+          ok = false;
+        } else if (!dry) {
           const int span = pb.causal ? pb.chunk : noncausal_span(pb.N, BH, STEP);
           const int nspan = (pb.N + span - 1) / span;
           ELSAA_LAUNCH("fwd_epilogue", (fwd_epilogue_kernel<T, D, LP, STEP, PLDS>), dim3(nspan, BH),
                        dim3(512), 0, st, (const T*)Q, (const T*)K, (const T*)V, planes_lr, A, z,
-                       (const T*)O_s, lse, lambda, g_s, g_lr, (T*)O, (T*)O_lr, d_lr, pb.H, pb.N,
+                       O_s, lse, lambda, g_s, g_lr, (T*)O, (T*)O_lr, d_lr, pb.H, pb.N,
                        pb.L, span, (int)pb.causal, pb.scale, pb.tau, pb.eps);
         }
       });
     });
   });
+  return ok;
 }
 
 }  // namespace elsaa

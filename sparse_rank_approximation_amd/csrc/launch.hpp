@@ -181,25 +181,29 @@ void launch_summary(const Problem& pb, const void* K, const void* V, const float
 
 size_t fwd_ws_bytes(const Problem& pb);
 size_t fwd_lds_need(const Problem& pb);
-void launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
+// The forward and backward launch sequences. With dry set they launch nothing
+// and only report whether every kernel of the sequence has a variant built for
+// these sizes (the same compile-time choices as the real launch); they return
+// false when one has not.
+bool launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
                 const float* planes_lr, const int32_t* qperm, const int32_t* kperm,
                 const float* A, const float* z, const float* lambda, const float* g_s,
-                const float* g_lr, void* O, void* O_s, void* O_lr, float* lse, float* d_lr,
-                void* ws, hipStream_t st);
+                const float* g_lr, void* O, float* O_s, void* O_lr, float* lse, float* d_lr,
+                void* ws, hipStream_t st, bool dry);
 
 // Per-token reductions over the sparse partial slots (merge.hip).
-void launch_merge(const Problem& pb, const void* Opart, const float* Lpart, void* O_s, float* lse,
+void launch_merge(const Problem& pb, const void* Opart, const float* Lpart, float* O_s, float* lse,
                   hipStream_t st);
 void launch_combine(const Problem& pb, const void* dQp, const void* dKp, const void* dVp, void* dQ,
                     void* dK, void* dV, hipStream_t st);
 
 size_t bwd_ws_bytes(const Problem& pb);
 size_t bwd_lds_need(const Problem& pb);
-void launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, const void* dO,
-                const void* O_s, const void* O_lr, const float* planes_lr, const int32_t* qperm,
+bool launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, const void* dO,
+                const float* O_s, const void* O_lr, const float* planes_lr, const int32_t* qperm,
                 const int32_t* kperm, const float* A, const float* z, const float* lse,
                 const float* d_lr, const float* lambda, const float* g_s, const float* g_lr,
                 void* dQ, void* dK, void* dV, float* dlambda, float* dg_s, float* dg_lr, void* ws,
-                hipStream_t st);
+                hipStream_t st, bool dry);
 
 }  // namespace elsaa

@@ -18,7 +18,7 @@ constexpr int kMergeBatch = 8;  // slots in flight per lane
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
     merge_kernel(const T* __restrict__ Opart, const float* __restrict__ Lpart, int N, int levels,
-                 int causal, T* __restrict__ Os, float* __restrict__ lse) {
+                 int causal, float* __restrict__ Os, float* __restrict__ lse) {
   constexpr int LPR = D / 8, RPB = 256 / LPR, MB = kMergeBatch;
   const int bh = blockIdx.y, tid = threadIdx.x;
   const int tok = blockIdx.x * RPB + tid / LPR, c8 = (tid % LPR) * 8;
@@ -112,7 +112,7 @@ __global__ void __launch_bounds__(256)
 
 }  // namespace
 
-void launch_merge(const Problem& pb, const void* Opart, const float* Lpart, void* O_s, float* lse,
+void launch_merge(const Problem& pb, const void* Opart, const float* Lpart, float* O_s, float* lse,
                   hipStream_t st) {
   const int BH = pb.B * pb.H;
   with_T(pb.bf16, [&](auto tp) {
@@ -121,7 +121,7 @@ void launch_merge(const Problem& pb, const void* Opart, const float* Lpart, void
       constexpr int D = ELSAA_C(dc);
       constexpr int RPB = 256 / (D / 8);
       ELSAA_LAUNCH("merge", (merge_kernel<T, D>), dim3((pb.N + RPB - 1) / RPB, BH), dim3(256), 0,
-                   st, (const T*)Opart, Lpart, pb.N, pb.levels, (int)pb.causal, (T*)O_s, lse);
+                   st, (const T*)Opart, Lpart, pb.N, pb.levels, (int)pb.causal, O_s, lse);
     });
   });
 }

@@ -148,7 +148,7 @@ def lowrank_summary(cfg: ElsaaConfig, k, v, planes_lr):
 
 
 def forward(cfg: ElsaaConfig, q, k, v, planes_lr, q_perm, k_perm, A, z, lam, g_s=None, g_lr=None):
-    """elsaa_fwd: returns dict(O, O_s, O_lr, lse, d_lr)."""
+    """elsaa_fwd: returns dict(O, O_s (fp32), O_lr, lse, d_lr)."""
     dev = q.device
     x = (cfg.B, cfg.H, cfg.N, cfg.d)
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -162,7 +162,8 @@ def forward(cfg: ElsaaConfig, q, k, v, planes_lr, q_perm, k_perm, A, z, lam, g_s
     _check_tensor("lam", lam, (cfg.H,), torch.float32, dev)
     _opt("g_s", g_s, (cfg.B, cfg.H, cfg.N), torch.float32, dev)
     _opt("g_lr", g_lr, (cfg.B, cfg.H, cfg.N), torch.float32, dev)
-    out = {n: torch.empty(x, dtype=cfg.dtype, device=dev) for n in ("O", "O_s", "O_lr")}
+    out = {n: torch.empty(x, dtype=cfg.dtype, device=dev) for n in ("O", "O_lr")}
+    out["O_s"] = torch.empty(x, dtype=torch.float32, device=dev)
     out["lse"] = torch.empty(cfg.B, cfg.H, cfg.N, dtype=torch.float32, device=dev)
     out["d_lr"] = torch.empty_like(out["lse"])
     ws, n = _workspace(cfg, _lib.CALL_FWD, dev)
@@ -180,8 +181,9 @@ def backward(cfg: ElsaaConfig, q, k, v, do, O_s, O_lr, planes_lr, q_perm, k_perm
     """elsaa_bwd: returns dict(dQ, dK, dV, dlambda, dg_s, dg_lr)."""
     dev = q.device
     x = (cfg.B, cfg.H, cfg.N, cfg.d)
-    for name, t in (("q", q), ("k", k), ("v", v), ("do", do), ("O_s", O_s), ("O_lr", O_lr)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("do", do), ("O_lr", O_lr)):
         _check_tensor(name, t, x, cfg.dtype, dev)
+    _check_tensor("O_s", O_s, x, torch.float32, dev)
     _check_tensor("q_perm", q_perm, (cfg.B, cfg.H, cfg.perm_len), torch.int32, dev)
     _check_tensor("k_perm", k_perm, (cfg.B, cfg.H, cfg.perm_len), torch.int32, dev)
     _check_tensor("lse", lse, (cfg.B, cfg.H, cfg.N), torch.float32, dev)

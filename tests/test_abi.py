@@ -130,3 +130,33 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _lib.lib()
+
+
+def test_misaligned_pointers_are_rejected_before_launching():
+    """Every pointer must be 16-byte aligned (the kernels use 16-byte vector
+    loads): a misaligned one, required or optional, is INVALID_ARG, and nothing
+    is launched (the fake addresses are never dereferenced)."""
+    L = _lib.lib()
+    p = base().params()
+    ok = ctypes.c_void_p(0x1000)
+    bad = ctypes.c_void_p(0x1008)
+    # elsaa_fwd: Q misaligned
+    args = [bad] + [ok] * 15 + [ok, 1 << 40, None]
+    s = L.elsaa_fwd(ctypes.byref(p), *args)
+    assert s == _lib.ERR_INVALID_ARG and "aligned" in L.elsaa_last_error().decode()
+    # elsaa_fwd: optional gate g_s misaligned (argument 10)
+    args = [ok] * 16 + [ok, 1 << 40, None]
+    args[9] = bad
+    s = L.elsaa_fwd(ctypes.byref(p), *args)
+    assert s == _lib.ERR_INVALID_ARG and "g_s" in L.elsaa_last_error().decode()
+    # elsaa_bwd: optional dg_lr misaligned (argument 22)
+    args = [ok] * 22 + [ok, 1 << 40, None]
+    args[21] = bad
+    s = L.elsaa_bwd(ctypes.byref(p), *args)
+    assert s == _lib.ERR_INVALID_ARG and "dg_lr" in L.elsaa_last_error().decode()
+    # the workspace too
+    args = [ok] * 16 + [bad, 1 << 40, None]
+    s = L.elsaa_fwd(ctypes.byref(p), *args)
+    assert s == _lib.ERR_INVALID_ARG and "ws" in L.elsaa_last_error().decode()
+    s = L.elsaa_select(ctypes.byref(p), ok, ok, ok, ok, bad, ok, ok, ok, 1 << 40, None)
+    assert s == _lib.ERR_INVALID_ARG and "k_code" in L.elsaa_last_error().decode()

@@ -10,7 +10,7 @@ import torch
 
 import workloads as W
 from oracle import ref
-from parity_util import BWD_TOL, CASES, TOL, all_heads, gpu_forward, head_arrays, rel_err
+from parity_util import CASES, TOL, all_heads, gpu_forward, head_arrays, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -60,8 +60,8 @@ def test_backward_parity(case):
     errs["dg_lr"] = rel_err(g["dg_lr"].view(G, w.N).cpu().numpy(), o["dg_lr"])
     errs["dlambda"] = rel_err(g["dlambda"].cpu().numpy(), o["dlambda_h"])
     print(f"[gpu bwd] {case} errors {errs}", flush=True)
-    tol = {k: BWD_TOL.get(case, {}).get(k, TOL[w.dtype]) for k in errs}
-    bad = {k: e for k, e in errs.items() if not e <= tol[k]}
+    tol = TOL[w.dtype]
+    bad = {k: e for k, e in errs.items() if not e <= tol}
     assert not bad, f"{case}: errors above {tol}: {bad}"
 
 

@@ -2,10 +2,9 @@
 bench.py times, against the oracle on sampled heads (heads are independent, so
 a sampled head is an exact check of that head). Selections are compared bit for
 bit, outputs and gradients within 1e-4 (fp32) / 2e-2 (bf16) max-relative error.
-The N=65536 workload is checked on its selections (all heads) and forward (one
-head); the oracle's backward there takes about a minute per head, and the same
-kernel shapes (block 256, r 256, d 128) are covered by the backward parity
-cases at N=1024."""
+The N=65536 workload is checked on its selections (all heads) and forward and
+backward on one head (the oracle's backward there takes over a minute on one
+thread, hence the longer time limit of that case)."""
 from __future__ import annotations
 
 import numpy as np
@@ -24,12 +23,12 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU containers
 SAMPLES = {
     2: ([(0, 0), (3, 5), (7, 11)], True),
     3: ([(0, 0), (1, 31)], True),
-    4: ([(0, 3)], False),
+    4: ([(0, 3)], True),
     5: ([(0, 0), (17, 6), (63, 11)], True),
 }
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cid", [1, 2, 3, pytest.param(4, marks=pytest.mark.timeout(900)), 5])
 def test_full_size_parity(cid):
     import sparse_rank_approximation_amd as S
     w = W.WORKLOADS[cid]

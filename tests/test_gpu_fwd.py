@@ -9,7 +9,8 @@ import torch
 
 import workloads as W
 from oracle import ref
-from parity_util import CASES, TOL, all_heads, gpu_forward, head_arrays, rel_err, wl
+from parity_util import (CASES, TOL, all_heads, elem_rel_err, gpu_forward, head_arrays,
+                         lse_abs_err, rel_err, wl)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +51,8 @@ def test_forward_parity(case):
     for name, key in (("O", "O"), ("O_s", "O_s"), ("O_lr", "O_lr"), ("lse", "lse"),
                       ("d_lr", "d_lr")):
         errs[name] = rel_err(g[key].float().view(o[key].shape).cpu().numpy(), o[key])
+    errs["lse_elem_abs"] = lse_abs_err(g["lse"].view(o["lse"].shape).cpu().numpy(), o["lse"])
+    errs["d_lr_elem_rel"] = elem_rel_err(g["d_lr"].view(o["d_lr"].shape).cpu().numpy(), o["d_lr"])
     print(f"[gpu fwd] {case} errors {errs}", flush=True)
     bad = {k: e for k, e in errs.items() if not e <= tol}
     assert not bad, f"{case}: errors above {tol}: {bad}"
