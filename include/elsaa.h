@@ -149,6 +149,19 @@ elsaa_status elsaa_select(const elsaa_params* p, const void* Q, const void* K,
                           int32_t* q_perm, int32_t* k_perm, void* ws, size_t ws_bytes,
                           void* stream);
 
+/* elsaa_select for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same selection, bit for bit, with no workspace argument. Its scratch (the
+ * hyperplanes widened to fp64, 8 * H * hash_bits * d_h bytes) lives in a fixed
+ * device array of at most 1 MiB that the library holds on every GPU it runs on
+ * until the process ends; larger sizes return ELSAA_ERR_UNSUPPORTED. It calls no
+ * allocation routine (the diagnostics of elsaa_profile skip its launches).
+ * Calls on one GPU share that array: calls that overlap on one GPU (e.g. on two
+ * streams) race on it and must be ordered by the caller. */
+elsaa_status elsaa_select_noalloc(const elsaa_params* p, const void* Q, const void* K,
+                                  const float* planes_s, uint16_t* q_code, uint16_t* k_code,
+                                  int32_t* q_perm, int32_t* k_perm, void* stream);
+
 /* RACE bucket statistics (Section 3.1: each table softly assigns keys to hypercube
  * buckets and accumulates key/value statistics in them). With
  * u_lt(x) = scale <R_lt, x> and phi_{l,b}(x) = prod_t sigmoid(2 s_bt u_lt(x) / tau),

@@ -14,8 +14,9 @@ STATUS_NAMES = {0: "ELSAA_OK", 1: "ELSAA_ERR_INVALID_ARG", 2: "ELSAA_ERR_UNSUPPO
 F32, BF16 = 0, 1
 CALL_SELECT, CALL_SUMMARY, CALL_FWD, CALL_BWD = range(4)
 
-SYMBOLS = ("elsaa_workspace_size", "elsaa_select", "elsaa_lowrank_summary", "elsaa_fwd",
-           "elsaa_bwd", "elsaa_profile", "elsaa_profile_report", "elsaa_last_error")
+SYMBOLS = ("elsaa_workspace_size", "elsaa_select", "elsaa_select_noalloc",
+           "elsaa_lowrank_summary", "elsaa_fwd", "elsaa_bwd", "elsaa_profile",
+           "elsaa_profile_report", "elsaa_last_error")
 
 
 class Params(ctypes.Structure):
@@ -50,6 +51,7 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     L.elsaa_workspace_size.argtypes = [_PP, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     L.elsaa_select.argtypes = [_PP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.elsaa_select_noalloc.argtypes = [_PP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.elsaa_lowrank_summary.argtypes = [_PP, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.elsaa_fwd.argtypes = [_PP] + [_vp] * 17 + [ctypes.c_size_t, _vp]
     L.elsaa_bwd.argtypes = [_PP] + [_vp] * 23 + [ctypes.c_size_t, _vp]

@@ -204,6 +204,31 @@ elsaa_status elsaa_select(const elsaa_params* p, const void* Q, const void* K,
   return launched();
 }
 
+elsaa_status elsaa_select_noalloc(const elsaa_params* p, const void* Q, const void* K,
+                                  const float* planes_s, uint16_t* q_code, uint16_t* k_code,
+                                  int32_t* q_perm, int32_t* k_perm, void* stream) {
+  PROLOGUE(ELSAA_CALL_SELECT);
+  if (empty) return ELSAA_OK;
+  NEED(Q); NEED(K); NEED(planes_s); NEED(q_code); NEED(k_code);
+  if (elsaa::perm_stride(pb.N, pb.levels, pb.causal) > 0) { NEED(q_perm); NEED(k_perm); }
+  OPTIONAL(q_perm); OPTIONAL(k_perm);
+  const size_t n = elsaa::select_ws_bytes(pb), cap = elsaa::noalloc_scratch_bytes();
+  if (n > cap)
+    return fail(ELSAA_ERR_UNSUPPORTED,
+                "the allocation-free selection holds at most %zu bytes of scratch; these sizes "
+                "need %zu (8 * H * hash_bits * d_h): use elsaa_select with a workspace",
+                cap, n);
+  void* scr = nullptr;
+  const hipError_t e = elsaa::noalloc_scratch(&scr);
+  if (e != hipSuccess)
+    return fail(ELSAA_ERR_HIP, "device address of the fixed scratch: %s", hipGetErrorString(e));
+  elsaa::prof_suspend(true);  // (the diagnostics would create events)
+  elsaa::launch_select(pb, Q, K, planes_s, q_code, k_code, q_perm, k_perm, scr,
+                       (hipStream_t)stream);
+  elsaa::prof_suspend(false);
+  return launched();
+}
+
 elsaa_status elsaa_lowrank_summary(const elsaa_params* p, const void* K, const void* V,
                                    const float* planes_lr, float* A, float* z, void* ws,
                                    size_t ws_bytes, void* stream) {

@@ -152,8 +152,11 @@ void with_LP(int L, F&& f) {
 #define ELSAA_C(c) decltype(c)::value
 
 // Per-kernel timing (prof.cpp): every launch goes through ELSAA_LAUNCH.
+// prof_suspend(true) makes this host thread's launches skip it (no events are
+// created) until prof_suspend(false).
 void prof_begin(hipStream_t st, const char* name);
 void prof_end(hipStream_t st);
+void prof_suspend(bool on);
 #define ELSAA_LAUNCH(name, kern, grid, block, lds, st, ...)        \
   do {                                                             \
     ::elsaa::prof_begin(st, name);                                 \
@@ -162,6 +165,10 @@ void prof_end(hipStream_t st);
   } while (0)
 
 size_t select_ws_bytes(const Problem& pb);
+// The allocation-free selection's fixed scratch (select.hip): its size, and its
+// device address on the current device (looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** out);
 void launch_select(const Problem& pb, const void* Q, const void* K, const float* planes_s,
                    uint16_t* qc, uint16_t* kc, int32_t* qperm, int32_t* kperm, void* ws,
                    hipStream_t st);

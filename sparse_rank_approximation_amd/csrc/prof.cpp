@@ -36,19 +36,34 @@ void clear_locked() {
 
 }  // namespace
 
+// This thread's launches are not recorded while suspended; the record a
+// prof_begin opened on this thread (-1: none) is the one its prof_end closes.
+thread_local bool t_suspended = false;
+thread_local long t_open = -1;
+
+void prof_suspend(bool on) { t_suspended = on; }
+
 void prof_begin(hipStream_t st, const char* name) {
+  t_open = -1;
+  if (t_suspended) return;
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_on) return;
   Rec r{name, nullptr, nullptr};
-  if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) return;
+  if (hipEventCreate(&r.a) != hipSuccess) return;
+  if (hipEventCreate(&r.b) != hipSuccess) {
+    (void)hipEventDestroy(r.a);
+    return;
+  }
   (void)hipEventRecord(r.a, st);
   g_recs.push_back(r);
+  t_open = (long)g_recs.size() - 1;
 }
 
 void prof_end(hipStream_t st) {
+  if (t_open < 0) return;
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_on || g_recs.empty()) return;
-  (void)hipEventRecord(g_recs.back().b, st);
+  if (g_on && t_open < (long)g_recs.size()) (void)hipEventRecord(g_recs[t_open].b, st);
+  t_open = -1;
 }
 
 }  // namespace elsaa

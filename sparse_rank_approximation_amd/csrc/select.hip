@@ -1,6 +1,8 @@
 // select.hip -- sortLSH selection: hash codes and sorted orders (ELSAA paper,
 // Section 3.2: queries and keys are hashed, sorted by hash and cut into
 // equal-size blocks; causally, per level of the past/future divide-and-conquer).
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -209,6 +211,37 @@ __global__ void __launch_bounds__(256) sort_kernel(const uint16_t* __restrict__ 
     if (valid && (eq >> lane) == 1ull) off[key] += __popcll(eq);
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+// Scratch of the allocation-free selection (elsaa_select_noalloc): the fp64
+// hyperplanes go to this fixed array instead of a caller's workspace. Every GPU
+// the library runs on holds its own copy until the process ends; calls on one
+// GPU share it, so such calls must not overlap (they would race on it). Nothing
+// in it has to start at zero: each call writes all of what it then reads.
+constexpr size_t kNoallocScratchBytes = (size_t)1 << 20;
+static __device__ __align__(256) double scratch[kNoallocScratchBytes / sizeof(double)];
+
+size_t noalloc_scratch_bytes() { return kNoallocScratchBytes; }
+
+hipError_t noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptrs[dev]) {
+    // The device address of this device's copy (in host code `scratch` names a
+    // host-side stand-in, not device memory).
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
 }
 
 size_t select_ws_bytes(const Problem& pb) {

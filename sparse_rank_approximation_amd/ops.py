@@ -128,6 +128,33 @@ def select(cfg: ElsaaConfig, q, k, planes_s):
     return qc, kc, qp, kp
 
 
+def select_noalloc(cfg: ElsaaConfig, q, k, planes_s, out=None):
+    """elsaa_select_noalloc: the same selection with no workspace. `out` =
+    (q_code, k_code, q_perm, k_perm) preallocated by the caller, or None to have
+    them allocated here (the call itself allocates nothing)."""
+    dev = q.device
+    x = (cfg.B, cfg.H, cfg.N, cfg.d)
+    _check_tensor("q", q, x, cfg.dtype, dev)
+    _check_tensor("k", k, x, cfg.dtype, dev)
+    _check_tensor("planes_s", planes_s, (cfg.H, cfg.bits, cfg.d), torch.float32, dev)
+    if out is None:
+        qc = torch.empty(cfg.B, cfg.H, cfg.N, dtype=torch.int16, device=dev)
+        qp = torch.empty(cfg.B, cfg.H, cfg.perm_len, dtype=torch.int32, device=dev)
+        out = (qc, torch.empty_like(qc), qp, torch.empty_like(qp))
+    qc, kc, qp, kp = out
+    for name, t, shp, dt in (("q_code", qc, (cfg.B, cfg.H, cfg.N), torch.int16),
+                             ("k_code", kc, (cfg.B, cfg.H, cfg.N), torch.int16),
+                             ("q_perm", qp, (cfg.B, cfg.H, cfg.perm_len), torch.int32),
+                             ("k_perm", kp, (cfg.B, cfg.H, cfg.perm_len), torch.int32)):
+        _check_tensor(name, t, shp, dt, dev)
+    p = cfg.params()
+    _lib.check(_lib.lib().elsaa_select_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(planes_s),
+                                               _ptr(qc), _ptr(kc),
+                                               _ptr(qp) if qp.numel() else None,
+                                               _ptr(kp) if kp.numel() else None, _stream(dev)))
+    return qc, kc, qp, kp
+
+
 def lowrank_summary(cfg: ElsaaConfig, k, v, planes_lr):
     """elsaa_lowrank_summary: A [B,H,nA,d,r], z [B,H,nA,r] fp32."""
     dev = k.device

@@ -160,3 +160,17 @@ def test_misaligned_pointers_are_rejected_before_launching():
     assert s == _lib.ERR_INVALID_ARG and "ws" in L.elsaa_last_error().decode()
     s = L.elsaa_select(ctypes.byref(p), ok, ok, ok, ok, bad, ok, ok, ok, 1 << 40, None)
     assert s == _lib.ERR_INVALID_ARG and "k_code" in L.elsaa_last_error().decode()
+
+
+def test_noalloc_select_rejects_sizes_beyond_its_scratch():
+    """elsaa_select_noalloc holds at most 1 MiB of scratch (8 * H * hash_bits * d_h
+    bytes): larger sizes are ELSAA_ERR_UNSUPPORTED, checked before any GPU call."""
+    L = _lib.lib()
+    ok = ctypes.c_void_p(0x1000)
+    p = base(H=128, d=128, hash_bits=12, N=1 << 16, block=16).params()  # 1.5 MiB
+    s = L.elsaa_select_noalloc(ctypes.byref(p), ok, ok, ok, ok, ok, ok, ok, None)
+    assert s == _lib.ERR_UNSUPPORTED, L.elsaa_last_error().decode()
+    assert "at most 1048576 bytes" in L.elsaa_last_error().decode()
+    p = base().params()
+    s = L.elsaa_select_noalloc(ctypes.byref(p), None, ok, ok, ok, ok, ok, ok, None)
+    assert s == _lib.ERR_INVALID_ARG and "NULL" in L.elsaa_last_error().decode()
