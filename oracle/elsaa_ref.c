@@ -681,3 +681,59 @@ int ref_bwd(const ref_params* p, const double* Q, const double* K, const double*
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Learnable gates of Eq. 4: g_k,i = sigmoid(<W_k, Q_i> + b_k) per head.        */
+/* ------------------------------------------------------------------------- */
+
+static double gate_logit(const double* w, double b, const double* q, int d) {
+  double t = b;
+  for (int c = 0; c < d; ++c) t += w[c] * q[c];
+  return t;
+}
+
+static double logistic(double t) { return 1.0 / (1.0 + exp(-t)); }
+
+int ref_gates_fwd(const ref_params* p, const double* Q, const double* W, const double* b,
+                  double* g_s, double* g_lr) {
+  if (!p || p->G <= 0 || p->N <= 0 || p->d <= 0 || !Q || !W || !b || !g_s || !g_lr)
+    return RET_BAD;
+  const int N = p->N, d = p->d;
+  for (int g = 0; g < p->G; ++g)
+    for (int i = 0; i < N; ++i) {
+      const double* q = Q + ((size_t)g * N + i) * d;
+      g_s[(size_t)g * N + i] = logistic(gate_logit(W + (size_t)g * 2 * d, b[2 * g], q, d));
+      g_lr[(size_t)g * N + i] = logistic(gate_logit(W + ((size_t)g * 2 + 1) * d, b[2 * g + 1], q, d));
+    }
+  return 0;
+}
+
+/* dL/dt = dL/dg g (1 - g) for t the gate's logit; t is linear in W, b and Q. */
+int ref_gates_bwd(const ref_params* p, const double* Q, const double* W, const double* b,
+                  const double* dg_s, const double* dg_lr, double* dQ, double* dW, double* db) {
+  if (!p || p->G <= 0 || p->N <= 0 || p->d <= 0 || !Q || !W || !b || !dg_s || !dg_lr || !dQ ||
+      !dW || !db)
+    return RET_BAD;
+  const int N = p->N, d = p->d;
+  for (int g = 0; g < p->G; ++g) {
+    for (int k = 0; k < 2; ++k) {
+      db[2 * g + k] = 0.0;
+      for (int c = 0; c < d; ++c) dW[((size_t)g * 2 + k) * d + c] = 0.0;
+    }
+    for (int i = 0; i < N; ++i) {
+      const double* q = Q + ((size_t)g * N + i) * d;
+      double* dq = dQ + ((size_t)g * N + i) * d;
+      for (int k = 0; k < 2; ++k) {
+        const double* w = W + ((size_t)g * 2 + k) * d;
+        const double gv = logistic(gate_logit(w, b[2 * g + k], q, d));
+        const double dt = (k == 0 ? dg_s : dg_lr)[(size_t)g * N + i] * gv * (1.0 - gv);
+        db[2 * g + k] += dt;
+        for (int c = 0; c < d; ++c) {
+          dW[((size_t)g * 2 + k) * d + c] += dt * q[c];
+          dq[c] += dt * w[c];
+        }
+      }
+    }
+  }
+  return 0;
+}

@@ -55,6 +55,21 @@ int ref_bwd(const ref_params* p, const double* Q, const double* K, const double*
             double* dQ, double* dK, double* dV, double* dlambda,
             double* dg_s, double* dg_lr);
 
+/* Learnable gates of Eq. 4. The paper names g_sparse,i and g_lr,i, has them
+ * learned with the model (Section 7: the branches' gates are shared with the
+ * Sort_Lsh_RACE ablation, and on NIAH the gate learns to up-weight the low-rank
+ * branch; Section 8: gate schedules per depth and head) but prints no formula.
+ * Reading taken here: the logistic function of a per-head affine projection of
+ * the query,
+ *   g_k,i = 1 / (1 + exp(-(<W[k], Q_i> + b[k]))),  k = 0: g_sparse, 1: g_lr,
+ * with W double [G][2][d] and b double [G][2]. ref_gates_bwd takes dL/dg_s and
+ * dL/dg_lr (as ref_bwd returns them), ADDS the gate path's dL/dQ to dQ, and
+ * writes dL/dW and dL/db. */
+int ref_gates_fwd(const ref_params* p, const double* Q, const double* W, const double* b,
+                  double* g_s, double* g_lr);
+int ref_gates_bwd(const ref_params* p, const double* Q, const double* W, const double* b,
+                  const double* dg_s, const double* dg_lr, double* dQ, double* dW, double* db);
+
 /* Exposed for the pins: the RACE soft bucket assignment of one row x[d]. */
 int ref_features(const ref_params* p, const float* planes_lr_head, const double* x,
                  double* phi);

@@ -162,6 +162,30 @@ def backward(p: RefParams, q, k, v, do, planes_s, planes_lr, lam, g_s=None, g_lr
     return out
 
 
+def gates_fwd(p: RefParams, q, W, b):
+    """Learnable gates g_s, g_lr [G, N] = sigmoid(<W[:, k], Q_i> + b[:, k]), W [G, 2, d],
+    b [G, 2]."""
+    q, W, b = _f64(q), _f64(W), _f64(b)
+    G, N, _ = q.shape
+    gs = np.zeros((G, N))
+    gl = np.zeros((G, N))
+    _check(lib().ref_gates_fwd(ctypes.byref(p.c(G)), _ptr(q), _ptr(W), _ptr(b), _ptr(gs),
+                               _ptr(gl)), "gates_fwd")
+    return gs, gl
+
+
+def gates_bwd(p: RefParams, q, W, b, dg_s, dg_lr):
+    """The gate path's (dQ, dW, db) from dL/dg_s, dL/dg_lr."""
+    q, W, b, dg_s, dg_lr = _f64(q), _f64(W), _f64(b), _f64(dg_s), _f64(dg_lr)
+    G, N, d = q.shape
+    dq = np.zeros((G, N, d))
+    dW = np.zeros((G, 2, d))
+    db = np.zeros((G, 2))
+    _check(lib().ref_gates_bwd(ctypes.byref(p.c(G)), _ptr(q), _ptr(W), _ptr(b), _ptr(dg_s),
+                               _ptr(dg_lr), _ptr(dq), _ptr(dW), _ptr(db)), "gates_bwd")
+    return dq, dW, db
+
+
 def features(p: RefParams, planes_lr_head, x):
     """RACE soft bucket assignment phi(x) for rows x [n, d] of one head."""
     x = _f64(x)

@@ -429,3 +429,86 @@ def test_backward_with_large_scores_matches_dense_autograd():
     for a, b in ((g["dQ"][0], tq.grad), (g["dK"][0], tk.grad), (g["dV"][0], tv.grad)):
         np.testing.assert_allclose(a, b.numpy(), atol=1e-8 * np.abs(b.numpy()).max(), rtol=1e-7)
     np.testing.assert_allclose(g["dlambda"][0], lam.grad.item(), rtol=1e-7)
+
+
+# ----------------------------------------------------------------------------- learnable gates
+
+def _gate_params(d, seed):
+    rng = np.random.default_rng(seed)
+    return rng.normal(0, 0.3, (1, 2, d)), rng.normal(0, 0.5, (1, 2))
+
+
+def test_gates_closed_forms():
+    """W = 0, b = 0 gives 1/2; the logistic symmetry g(Q, W, b) + g(-Q, W, -b) = 1;
+    a zero query row gives sigmoid(b)."""
+    w = small(True, N=64, d=16, block=16)
+    p = ref.RefParams.from_workload(w)
+    q, *_ = head(w, 71)
+    W, b = _gate_params(16, 71)
+    gs, gl = ref.gates_fwd(p, q[None], np.zeros_like(W), np.zeros_like(b))
+    assert np.all(gs == 0.5) and np.all(gl == 0.5)
+    g1 = ref.gates_fwd(p, q[None], W, b)
+    g2 = ref.gates_fwd(p, -q[None], W, -b)
+    for a, c in zip(g1, g2):
+        np.testing.assert_allclose(a + c, 1.0, rtol=0, atol=1e-15)
+    q0 = q.copy()
+    q0[5] = 0.0
+    gs, gl = ref.gates_fwd(p, q0[None], W, b)
+    assert gs[0, 5] == 1 / (1 + math.exp(-b[0, 0])) and gl[0, 5] == 1 / (1 + math.exp(-b[0, 1]))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gated_operator_matches_dense_autograd(causal):
+    """Gates from the query's projection composed with the operator: ref_bwd's
+    dg_s, dg_lr taken through ref_gates_bwd give the same dQ, dW, db as autograd
+    of the dense fp64 formulation with the gates computed there."""
+    w = small(causal, N=128, d=16, block=16, r=32)
+    p = ref.RefParams.from_workload(w)
+    q, k, v, do, ps, pl = head(w, 73)
+    W, b = _gate_params(16, 73)
+    _, _, qp, kp = run_select(w, p, q, k, ps)
+    M = D.support_mask(128, 16, causal, qp[0], kp[0])
+    tq, tk, tv = (torch.from_numpy(x).clone().requires_grad_(True) for x in (q, k, v))
+    tW = torch.from_numpy(W[0]).clone().requires_grad_(True)
+    tb = torch.from_numpy(b[0]).clone().requires_grad_(True)
+    tg = torch.sigmoid(tq @ tW.t() + tb)
+    dn = D.dense_forward(tq, tk, tv, M, torch.from_numpy(pl[0]), 1.1, causal, 0.25,
+                         g_s=tg[:, 0], g_lr=tg[:, 1])
+    (dn["O"] * torch.from_numpy(do)).sum().backward()
+    gs, gl = ref.gates_fwd(p, q[None], W, b)
+    g = ref.backward(p, q[None], k[None], v[None], do[None], ps, pl, np.array([1.1]), gs, gl)
+    dq_gate, dW, db = ref.gates_bwd(p, q[None], W, b, g["dg_s"], g["dg_lr"])
+    np.testing.assert_allclose(g["dQ"][0] + dq_gate[0], tq.grad.numpy(), atol=1e-10, rtol=1e-9)
+    np.testing.assert_allclose(g["dK"][0], tk.grad.numpy(), atol=1e-10, rtol=1e-9)
+    np.testing.assert_allclose(dW[0], tW.grad.numpy(), atol=1e-10, rtol=1e-9)
+    np.testing.assert_allclose(db[0], tb.grad.numpy(), atol=1e-10, rtol=1e-9)
+
+
+def test_gate_gradients_match_central_differences():
+    """dW and db of the gate path against central differences of the composed loss
+    (the selection does not depend on W, b)."""
+    w = small(True, N=64, d=8, block=8, r=32, chunk=16)
+    p = ref.RefParams.from_workload(w)
+    q, k, v, do, ps, pl = head(w, 79)
+    W, b = _gate_params(8, 79)
+
+    def loss(W_, b_):
+        gs, gl = ref.gates_fwd(p, q[None], W_, b_)
+        return _loss(p, q, k, v, do, ps, pl, 0.8, gs[0], gl[0])
+
+    gs, gl = ref.gates_fwd(p, q[None], W, b)
+    g = ref.backward(p, q[None], k[None], v[None], do[None], ps, pl, np.array([0.8]), gs, gl)
+    _, dW, db = ref.gates_bwd(p, q[None], W, b, g["dg_s"], g["dg_lr"])
+    h = 1e-6
+    for kk in range(2):
+        for c in range(8):
+            a1, a2 = W.copy(), W.copy()
+            a1[0, kk, c] += h
+            a2[0, kk, c] -= h
+            fd = (loss(a1, b) - loss(a2, b)) / (2 * h)
+            assert abs(fd - dW[0, kk, c]) <= 1e-6 * max(1.0, abs(fd))
+        b1, b2 = b.copy(), b.copy()
+        b1[0, kk] += h
+        b2[0, kk] -= h
+        fd = (loss(W, b1) - loss(W, b2)) / (2 * h)
+        assert abs(fd - db[0, kk]) <= 1e-6 * max(1.0, abs(fd))
