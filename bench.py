@@ -56,6 +56,8 @@ def kernel_work(w) -> dict:
         "lr_bwd_k": ("mfma", 4.0 * r * (d + 1) * tok, "TFLOP/s"),
         "hash": ("hbm", 2.0 * tok * d * e + 4.0 * tok, "GB/s"),
         "bwd_rows": ("hbm", 3.0 * tok * d * e + 40.0 * tok, "GB/s"),
+        "gates_fwd": ("hbm", tok * d * e + 8.0 * tok, "GB/s"),
+        "gates_bwd": ("hbm", 3.0 * tok * d * e + 16.0 * tok, "GB/s"),
     }
 
 
@@ -152,6 +154,9 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--learned-gates", action="store_true",
+                    help="gates of Eq. 4 from a learned projection of the query (elsaa_gates_fwd/"
+                         "_bwd in every step) instead of unit gates")
     ap.add_argument("--chunk", type=int, default=0,
                     help="causal RACE summary spacing (numerics-neutral); 0 keeps the workload's")
     args = ap.parse_args()
@@ -182,13 +187,21 @@ def main():
     cfg = S.ElsaaConfig(w.B, w.H, w.N, w.d, w.torch_dtype, w.causal, w.block, w.hash_bits,
                         w.lr_tables, w.lr_bits, w.chunk)
     lam = torch.ones(w.H, dtype=torch.float32, device=dev)
+    gen = torch.Generator().manual_seed(seed + 5)
+    gate_w = (0.2 * torch.randn(w.H, 2, w.d, generator=gen)).to(dev)
+    gate_b = (0.5 * torch.randn(w.H, 2, generator=gen)).to(dev)
 
     def step():
+        gs = gl = None
+        if args.learned_gates:
+            gs, gl = S.gates(cfg, d["q"], gate_w, gate_b)
         _, _, qp, kp = S.select(cfg, d["q"], d["k"], d["planes_s"])
         A, z = S.lowrank_summary(cfg, d["k"], d["v"], d["planes_lr"])
-        o = S.forward(cfg, d["q"], d["k"], d["v"], d["planes_lr"], qp, kp, A, z, lam)
-        S.backward(cfg, d["q"], d["k"], d["v"], d["do"], o["O_s"], o["O_lr"], d["planes_lr"], qp,
-                   kp, A, z, o["lse"], o["d_lr"], lam)
+        o = S.forward(cfg, d["q"], d["k"], d["v"], d["planes_lr"], qp, kp, A, z, lam, gs, gl)
+        g = S.backward(cfg, d["q"], d["k"], d["v"], d["do"], o["O_s"], o["O_lr"], d["planes_lr"],
+                       qp, kp, A, z, o["lse"], o["d_lr"], lam, gs, gl)
+        if args.learned_gates:
+            S.gates_backward(cfg, d["q"], gate_w, gs, gl, g["dg_s"], g["dg_lr"], g["dQ"])
 
     for _ in range(args.warmup):
         step()
@@ -241,7 +254,8 @@ def main():
         "data": "synthetic (seeded generators shaped like the paper's long-context workloads)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d_h": w.d,
                    "causal": w.causal, "block": w.block, "r": w.r, "hash_bits": w.hash_bits,
-                   "chunk": w.chunk, "global_batch": w.B, "seq_len": w.N, "parallelism": "none"},
+                   "chunk": w.chunk, "gates": "learned" if args.learned_gates else "unit",
+                   "global_batch": w.B, "seq_len": w.N, "parallelism": "none"},
         "roofline": roof,
         "kernels": kernels,
         "cpu_baseline": cpu,

@@ -80,7 +80,8 @@ typedef enum {
   ELSAA_CALL_SELECT = 0,
   ELSAA_CALL_SUMMARY = 1,
   ELSAA_CALL_FWD = 2,
-  ELSAA_CALL_BWD = 3
+  ELSAA_CALL_BWD = 3,
+  ELSAA_CALL_GATES_BWD = 4
 } elsaa_call;
 
 /* Problem description.
@@ -216,6 +217,27 @@ elsaa_status elsaa_bwd(const elsaa_params* p, const void* Q, const void* K, cons
                        const float* lambda, const float* g_s, const float* g_lr, void* dQ,
                        void* dK, void* dV, float* dlambda, float* dg_s, float* dg_lr, void* ws,
                        size_t ws_bytes, void* stream);
+
+/* Learnable gates of Eq. 4. The paper has g_sparse,i and g_lr,i learned with the
+ * model (Section 7: shared by ELSAA and its Sort_Lsh_RACE ablation, and on NIAH
+ * the gate learns to up-weight the low-rank branch; Section 8: gate schedules per
+ * depth and head) but prints no formula; here they are the logistic function of
+ * a per-head affine projection of the query:
+ *   g_k,i = 1 / (1 + exp(-(<W[h][k], Q_i> + b[h][k]))),  k = 0: g_sparse, 1: g_lr.
+ * elsaa_gates_fwd writes them for elsaa_fwd / elsaa_bwd (as their g_s, g_lr).
+ *   W : fp32 [H, 2, d_h];  b : fp32 [H, 2];  g_s, g_lr (out): fp32 [B, H, N]. */
+elsaa_status elsaa_gates_fwd(const elsaa_params* p, const void* Q, const float* W,
+                             const float* b, float* g_s, float* g_lr, void* stream);
+
+/* Backward of elsaa_gates_fwd: from dg_s, dg_lr (as elsaa_bwd returns them) it
+ * ADDS the gate path's gradient to dQ ([B, H, N, d_h] dtype, in place: pass the
+ * dQ of elsaa_bwd) and writes dW (fp32 [H, 2, d_h]) and db (fp32 [H, 2]), summed
+ * over the batch in a fixed order. g_s, g_lr: the gates elsaa_gates_fwd returned.
+ * ws: elsaa_workspace_size(p, ELSAA_CALL_GATES_BWD) bytes. */
+elsaa_status elsaa_gates_bwd(const elsaa_params* p, const void* Q, const float* W,
+                             const float* g_s, const float* g_lr, const float* dg_s,
+                             const float* dg_lr, void* dQ, float* dW, float* db, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /* Diagnostics, not a step of the operator: per-kernel timing. With profiling on,
  * every kernel the four calls launch is bracketed by two HIP events recorded on

@@ -1,8 +1,8 @@
 """ELSAA attention (sparse sortLSH branch + RACE low-rank branch + denominator-aware
 fusion) on AMD MI355X (gfx950): hand-written HIP kernels behind a C ABI
 (include/elsaa.h), with a thin torch binding."""
-from .ops import (ElsaaConfig, ElsaaFunction, backward, elsaa_attention, forward,
-                  lowrank_summary, make_planes, select, select_noalloc)
+from .ops import (ElsaaConfig, ElsaaFunction, backward, elsaa_attention, forward, gates,
+                  gates_backward, lowrank_summary, make_planes, select, select_noalloc)
 
-__all__ = ["ElsaaConfig", "ElsaaFunction", "backward", "elsaa_attention", "forward",
-           "lowrank_summary", "make_planes", "select", "select_noalloc"]
+__all__ = ["ElsaaConfig", "ElsaaFunction", "backward", "elsaa_attention", "forward", "gates",
+           "gates_backward", "lowrank_summary", "make_planes", "select", "select_noalloc"]

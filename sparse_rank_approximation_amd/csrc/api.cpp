@@ -146,6 +146,7 @@ size_t ws_bytes_for(const Problem& pb, int call) {
     case ELSAA_CALL_SUMMARY: return elsaa::summary_ws_bytes(pb);
     case ELSAA_CALL_FWD: return elsaa::fwd_ws_bytes(pb);
     case ELSAA_CALL_BWD: return elsaa::bwd_ws_bytes(pb);
+    case ELSAA_CALL_GATES_BWD: return elsaa::gates_bwd_ws_bytes(pb);
     default: return 0;
   }
 }
@@ -179,7 +180,7 @@ extern "C" {
 
 elsaa_status elsaa_workspace_size(const elsaa_params* p, int32_t call, size_t* bytes) {
   if (!bytes) return fail(ELSAA_ERR_INVALID_ARG, "bytes is NULL");
-  if (call < ELSAA_CALL_SELECT || call > ELSAA_CALL_BWD)
+  if (call < ELSAA_CALL_SELECT || call > ELSAA_CALL_GATES_BWD)
     return fail(ELSAA_ERR_INVALID_ARG, "unknown call %d", call);
   PROLOGUE(call);
   *bytes = empty ? 0 : ws_bytes_for(pb, call);
@@ -292,6 +293,30 @@ elsaa_status elsaa_bwd(const elsaa_params* p, const void* Q, const void* K, cons
   elsaa::launch_bwd(pb, Q, K, V, dO, O_s, O_lr, planes_lr, q_perm, k_perm, A, z, lse_s, d_lr,
                     lambda, g_s, g_lr, dQ, dK, dV, dlambda, dg_s, dg_lr, ws, (hipStream_t)stream,
                     false);
+  return launched();
+}
+
+elsaa_status elsaa_gates_fwd(const elsaa_params* p, const void* Q, const float* W,
+                             const float* b, float* g_s, float* g_lr, void* stream) {
+  PROLOGUE(ELSAA_CALL_GATES_BWD);
+  if (empty) return ELSAA_OK;
+  NEED(Q); NEED(W); NEED(b); NEED(g_s); NEED(g_lr);
+  elsaa::launch_gates_fwd(pb, Q, W, b, g_s, g_lr, (hipStream_t)stream);
+  return launched();
+}
+
+elsaa_status elsaa_gates_bwd(const elsaa_params* p, const void* Q, const float* W,
+                             const float* g_s, const float* g_lr, const float* dg_s,
+                             const float* dg_lr, void* dQ, float* dW, float* db, void* ws,
+                             size_t ws_bytes, void* stream) {
+  PROLOGUE(ELSAA_CALL_GATES_BWD);
+  if (empty) return ELSAA_OK;
+  NEED(Q); NEED(W); NEED(g_s); NEED(g_lr); NEED(dg_s); NEED(dg_lr); NEED(dQ); NEED(dW); NEED(db);
+  {
+    elsaa_status s_ = check_ws(pb, ELSAA_CALL_GATES_BWD, ws, ws_bytes);
+    if (s_ != ELSAA_OK) return s_;
+  }
+  elsaa::launch_gates_bwd(pb, Q, W, g_s, g_lr, dg_s, dg_lr, dQ, dW, db, ws, (hipStream_t)stream);
   return launched();
 }
 

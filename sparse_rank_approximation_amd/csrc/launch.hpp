@@ -198,6 +198,14 @@ bool launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
                 const float* g_lr, void* O, float* O_s, void* O_lr, float* lse, float* d_lr,
                 void* ws, hipStream_t st, bool dry);
 
+// Learnable gates of Eq. 4 from a projection of the query (gates.hip).
+size_t gates_bwd_ws_bytes(const Problem& pb);
+void launch_gates_fwd(const Problem& pb, const void* Q, const float* W, const float* b, float* gs,
+                      float* glr, hipStream_t st);
+void launch_gates_bwd(const Problem& pb, const void* Q, const float* W, const float* gs,
+                      const float* glr, const float* dgs, const float* dglr, void* dQ, float* dW,
+                      float* db, void* ws, hipStream_t st);
+
 // Per-token reductions over the sparse partial slots (merge.hip).
 void launch_merge(const Problem& pb, const void* Opart, const float* Lpart, float* O_s, float* lse,
                   hipStream_t st);

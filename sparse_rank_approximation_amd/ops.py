@@ -234,30 +234,78 @@ def backward(cfg: ElsaaConfig, q, k, v, do, O_s, O_lr, planes_lr, q_perm, k_perm
     return out
 
 
+def gates(cfg: ElsaaConfig, q, W, b):
+    """elsaa_gates_fwd: g_s, g_lr [B,H,N] fp32 = sigmoid(<W[h,k], Q_i> + b[h,k])."""
+    dev = q.device
+    _check_tensor("q", q, (cfg.B, cfg.H, cfg.N, cfg.d), cfg.dtype, dev)
+    _check_tensor("W", W, (cfg.H, 2, cfg.d), torch.float32, dev)
+    _check_tensor("b", b, (cfg.H, 2), torch.float32, dev)
+    gs = torch.empty(cfg.B, cfg.H, cfg.N, dtype=torch.float32, device=dev)
+    gl = torch.empty_like(gs)
+    p = cfg.params()
+    _lib.check(_lib.lib().elsaa_gates_fwd(ctypes.byref(p), _ptr(q), _ptr(W), _ptr(b), _ptr(gs),
+                                          _ptr(gl), _stream(dev)))
+    return gs, gl
+
+
+def gates_backward(cfg: ElsaaConfig, q, W, g_s, g_lr, dg_s, dg_lr, dq):
+    """elsaa_gates_bwd: adds the gate path's gradient to dq (in place) and returns
+    (dW [H,2,d], db [H,2])."""
+    dev = q.device
+    x = (cfg.B, cfg.H, cfg.N, cfg.d)
+    _check_tensor("q", q, x, cfg.dtype, dev)
+    _check_tensor("dq", dq, x, cfg.dtype, dev)
+    _check_tensor("W", W, (cfg.H, 2, cfg.d), torch.float32, dev)
+    for name, t in (("g_s", g_s), ("g_lr", g_lr), ("dg_s", dg_s), ("dg_lr", dg_lr)):
+        _check_tensor(name, t, (cfg.B, cfg.H, cfg.N), torch.float32, dev)
+    dW = torch.empty(cfg.H, 2, cfg.d, dtype=torch.float32, device=dev)
+    db = torch.empty(cfg.H, 2, dtype=torch.float32, device=dev)
+    ws, n = _workspace(cfg, _lib.CALL_GATES_BWD, dev)
+    p = cfg.params()
+    _lib.check(_lib.lib().elsaa_gates_bwd(ctypes.byref(p), _ptr(q), _ptr(W), _ptr(g_s), _ptr(g_lr),
+                                          _ptr(dg_s), _ptr(dg_lr), _ptr(dq), _ptr(dW), _ptr(db),
+                                          _ptr(ws), n, _stream(dev)))
+    return dW, db
+
+
 class ElsaaFunction(torch.autograd.Function):
     """O = ELSAA(Q, K, V; lambda, g_s, g_lr) with gradients for Q, K, V, lambda and
-    the gates; the hyperplanes are fixed inputs (no gradient)."""
+    the gates; the hyperplanes are fixed inputs (no gradient). With gate_w, gate_b
+    given, the gates are learned: g = sigmoid(<gate_w[h, k], Q_i> + gate_b[h, k])
+    (elsaa_gates_fwd), and gate_w, gate_b get gradients (g_s, g_lr must be None)."""
 
     @staticmethod
-    def forward(ctx, cfg, q, k, v, lam, g_s, g_lr, planes_s, planes_lr):
+    def forward(ctx, cfg, q, k, v, lam, g_s, g_lr, planes_s, planes_lr, gate_w=None, gate_b=None):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        learned = gate_w is not None
+        if learned:
+            if g_s is not None or g_lr is not None:
+                raise ValueError("give either gate tensors or a gate projection, not both")
+            g_s, g_lr = gates(cfg, q, gate_w.contiguous(), gate_b.contiguous())
         _, _, qp, kp = select(cfg, q, k, planes_s)
         A, z = lowrank_summary(cfg, k, v, planes_lr)
         out = forward(cfg, q, k, v, planes_lr, qp, kp, A, z, lam, g_s, g_lr)
         ctx.cfg = cfg
+        ctx.learned = learned
         ctx.save_for_backward(q, k, v, lam, g_s, g_lr, planes_lr, qp, kp, A, z, out["O_s"],
-                              out["O_lr"], out["lse"], out["d_lr"])
+                              out["O_lr"], out["lse"], out["d_lr"],
+                              gate_w.contiguous() if learned else None)
         return out["O"]
 
     @staticmethod
     def backward(ctx, dO):
-        (q, k, v, lam, g_s, g_lr, planes_lr, qp, kp, A, z, O_s, O_lr, lse, d_lr) = ctx.saved_tensors
+        (q, k, v, lam, g_s, g_lr, planes_lr, qp, kp, A, z, O_s, O_lr, lse, d_lr,
+         gate_w) = ctx.saved_tensors
+        want_dg = ctx.learned or ctx.needs_input_grad[5] or ctx.needs_input_grad[6]
         g = backward(ctx.cfg, q, k, v, dO.contiguous(), O_s, O_lr, planes_lr, qp, kp, A, z, lse,
-                     d_lr, lam, g_s, g_lr, want_dlam=ctx.needs_input_grad[4],
-                     want_dg=ctx.needs_input_grad[5] or ctx.needs_input_grad[6])
+                     d_lr, lam, g_s, g_lr, want_dlam=ctx.needs_input_grad[4], want_dg=want_dg)
+        dW = db = None
+        if ctx.learned:
+            dW, db = gates_backward(ctx.cfg, q, gate_w, g_s, g_lr, g["dg_s"], g["dg_lr"], g["dQ"])
+            return (None, g["dQ"], g["dK"], g["dV"], g["dlambda"], None, None, None, None, dW, db)
         return (None, g["dQ"], g["dK"], g["dV"], g["dlambda"],
                 g["dg_s"] if ctx.needs_input_grad[5] else None,
-                g["dg_lr"] if ctx.needs_input_grad[6] else None, None, None)
+                g["dg_lr"] if ctx.needs_input_grad[6] else None, None, None, None, None)
 
 
 def make_planes(cfg: ElsaaConfig, seed: int = 0, device="cuda"):
@@ -270,8 +318,11 @@ def make_planes(cfg: ElsaaConfig, seed: int = 0, device="cuda"):
 
 def elsaa_attention(q, k, v, *, causal: bool, block: int, lr_tables: int, lam=None, g_s=None,
                     g_lr=None, planes_s=None, planes_lr=None, seed: int = 0, chunk: int = 2048,
-                    hash_bits: int | None = None, tau: float = 1.0, eps: float = 1e-6):
-    """ELSAA attention of q, k, v [B, H, N, d] (fp32 or bf16 device tensors)."""
+                    hash_bits: int | None = None, tau: float = 1.0, eps: float = 1e-6,
+                    gate_w=None, gate_b=None):
+    """ELSAA attention of q, k, v [B, H, N, d] (fp32 or bf16 device tensors). Gates:
+    fixed tensors g_s, g_lr [B, H, N], or learned from the projection gate_w [H, 2, d],
+    gate_b [H, 2] of the query."""
     B, H, N, d = q.shape
     cfg = ElsaaConfig(B, H, N, d, q.dtype, causal, block, hash_bits, lr_tables, 4, chunk, tau, eps)
     if planes_s is None or planes_lr is None:
@@ -280,4 +331,4 @@ def elsaa_attention(q, k, v, *, causal: bool, block: int, lr_tables: int, lam=No
         planes_lr = pl if planes_lr is None else planes_lr
     if lam is None:
         lam = torch.ones(H, dtype=torch.float32, device=q.device)
-    return ElsaaFunction.apply(cfg, q, k, v, lam, g_s, g_lr, planes_s, planes_lr)
+    return ElsaaFunction.apply(cfg, q, k, v, lam, g_s, g_lr, planes_s, planes_lr, gate_w, gate_b)
