@@ -737,3 +737,54 @@ int ref_gates_bwd(const ref_params* p, const double* Q, const double* W, const d
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Exact per-query top-k selection on Q K^T (ties: lower key index).          */
+/* ------------------------------------------------------------------------- */
+
+typedef struct {
+  double s;
+  int32_t j;
+} scored_key;
+
+/* Descending score, then ascending key index. */
+static int by_score_then_index(const void* a, const void* b) {
+  const scored_key* x = (const scored_key*)a;
+  const scored_key* y = (const scored_key*)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  return (x->j > y->j) - (x->j < y->j);
+}
+
+static int by_index(const void* a, const void* b) {
+  const int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+int ref_topk(const ref_params* p, const double* Q, const double* K, int k, int32_t* idx) {
+  if (!p || p->G <= 0 || p->N <= 0 || p->d <= 0 || k <= 0 || !Q || !K || !idx) return RET_BAD;
+  const int N = p->N, d = p->d;
+#pragma omp parallel for schedule(dynamic)
+  for (int g = 0; g < p->G; ++g) {
+    scored_key* sk = (scored_key*)malloc(sizeof(scored_key) * N);
+    for (int i = 0; i < N; ++i) {
+      const double* q = Q + ((size_t)g * N + i) * d;
+      const int nc = p->causal ? i + 1 : N;
+      for (int j = 0; j < nc; ++j) {
+        const double* kr = K + ((size_t)g * N + j) * d;
+        double acc = 0.0;
+        for (int c = 0; c < d; ++c) acc = fma(q[c], kr[c], acc);
+        sk[j].s = acc;
+        sk[j].j = j;
+      }
+      qsort(sk, nc, sizeof(scored_key), by_score_then_index);
+      const int m = nc < k ? nc : k;
+      int32_t* out = idx + ((size_t)g * N + i) * k;
+      for (int t = 0; t < m; ++t) out[t] = sk[t].j;
+      qsort(out, m, sizeof(int32_t), by_index);
+      for (int t = m; t < k; ++t) out[t] = -1;
+    }
+    free(sk);
+  }
+  return 0;
+}

@@ -70,6 +70,16 @@ int ref_gates_fwd(const ref_params* p, const double* Q, const double* W, const d
 int ref_gates_bwd(const ref_params* p, const double* Q, const double* W, const double* b,
                   const double* dg_s, const double* dg_lr, double* dQ, double* dW, double* db);
 
+/* Exact per-query top-k key selection on Q K^T (the "learned top-k" kind of sparse
+ * selector the paper lists next to sortLSH in Section 3, here without learning):
+ * for query i, the candidate keys are every j (or j <= i when causal), the score
+ * of (i, j) is the fp64 fused-multiply-add chain acc = fma(Q_i[c], K_j[c], acc)
+ * over c = 0..d-1 from +0.0 (the positive scale of Q K^T / sqrt(d_h) does not
+ * change the order), and the selected set holds the min(k, #candidates) keys of
+ * largest score, ties broken by the lower key index. idx: int32 [G][N][k], each
+ * set in ascending key order, padded with -1. */
+int ref_topk(const ref_params* p, const double* Q, const double* K, int k, int32_t* idx);
+
 /* Exposed for the pins: the RACE soft bucket assignment of one row x[d]. */
 int ref_features(const ref_params* p, const float* planes_lr_head, const double* x,
                  double* phi);

@@ -186,6 +186,15 @@ def gates_bwd(p: RefParams, q, W, b, dg_s, dg_lr):
     return dq, dW, db
 
 
+def topk(p: RefParams, q, k, k_top: int):
+    """Exact per-query top-k keys on Q K^T: int32 [G, N, k_top], ascending, -1 padded."""
+    q, k = _f64(q), _f64(k)
+    G, N, _ = q.shape
+    idx = np.zeros((G, N, k_top), np.int32)
+    _check(lib().ref_topk(ctypes.byref(p.c(G)), _ptr(q), _ptr(k), int(k_top), _ptr(idx)), "topk")
+    return idx
+
+
 def features(p: RefParams, planes_lr_head, x):
     """RACE soft bucket assignment phi(x) for rows x [n, d] of one head."""
     x = _f64(x)

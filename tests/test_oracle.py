@@ -512,3 +512,48 @@ def test_gate_gradients_match_central_differences():
         b2[0, kk] -= h
         fd = (loss(W, b1) - loss(W, b2)) / (2 * h)
         assert abs(fd - db[0, kk]) <= 1e-6 * max(1.0, abs(fd))
+
+
+# ----------------------------------------------------------------------------- exact top-k selector
+
+def _int_qk(N, d, seed, lo=-3, hi=4):
+    rng = np.random.default_rng(seed)
+    return (rng.integers(lo, hi, (1, N, d)).astype(np.float64),
+            rng.integers(lo, hi, (1, N, d)).astype(np.float64))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("k_top", [1, 5, 16, 70])
+def test_topk_equals_brute_force_on_exact_integer_scores(causal, k_top):
+    """Small-integer rows make every fp64 score exact (and ties frequent): the
+    oracle equals a brute force over exact integer dot products ordered by
+    (score descending, key index ascending), as ascending sets padded with -1."""
+    N, d = 64, 8
+    q, k = _int_qk(N, d, 83 + k_top)
+    p = ref.RefParams(N=N, d=d, causal=causal, block=N, hash_bits=1, lr_tables=1)
+    got = ref.topk(p, q, k, k_top)[0]
+    qi, ki = q[0].astype(np.int64), k[0].astype(np.int64)
+    for i in range(N):
+        cand = range(i + 1) if causal else range(N)
+        order = sorted(cand, key=lambda j: (-int(qi[i] @ ki[j]), j))
+        want = sorted(order[:k_top])
+        want += [-1] * (k_top - len(want))
+        assert got[i].tolist() == want, i
+
+
+def test_topk_ties_take_the_lower_index_and_sets_are_causal():
+    """Duplicated keys score equally: the lower indices are taken; causal sets hold
+    only keys j <= i, min(k, i + 1) of them."""
+    N, d, k_top = 96, 16, 8
+    q, k = _int_qk(N, d, 89)
+    k[0, 40:80] = k[0, 10]  # 41 copies of key 10's row
+    q[0, :] = k[0, 10]      # every query prefers that row
+    p = ref.RefParams(N=N, d=d, causal=True, block=N, hash_bits=1, lr_tables=1)
+    got = ref.topk(p, q, k, k_top)[0]
+    for i in range(N):
+        sel = [j for j in got[i] if j >= 0]
+        assert len(sel) == min(k_top, i + 1) and all(j <= i for j in sel)
+        if i >= 47:  # 10, 40..46 are the 8 lowest copies
+            assert sel == [10] + list(range(40, 47)), (i, sel)
+    p.causal = False
+    assert ref.topk(p, q, k, N + 5)[0, 3].tolist() == list(range(N)) + [-1] * 5
