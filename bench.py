@@ -146,6 +146,42 @@ def cpu_baseline(w, seed, n_heads, threads):
                       f"{os.cpu_count()} CPUs); scaled by heads"}
 
 
+def bench_topk(args, w, cfg, d):
+    """elsaa_topk at the workload's shape with k = its block size. Its algorithmic
+    work is the score of every candidate pair, 2 d flops each on MFMA (the
+    contraction the selection needs); the exact rescoring and heap upkeep of the
+    keys near each query's threshold come on top."""
+    import torch
+    import sparse_rank_approximation_amd as S
+    from sparse_rank_approximation_amd import _lib
+    k_top = w.block
+    for _ in range(args.warmup):
+        S.topk(cfg, d["q"], d["k"], k_top)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        S.topk(cfg, d["q"], d["k"], k_top)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    BH, N = w.B * w.H, w.N
+    pairs = BH * (N * (N + 1) // 2 if w.causal else N * N)
+    flops = 2.0 * w.d * pairs
+    achieved = flops / (ms / 1e3) / 1e12
+    peak = PEAK_MFMA[w.dtype]
+    out = {"metric": "exact per-query top-k selection, queries/s", "value": round(BH * N / (ms / 1e3), 1),
+           "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+           "config": {"workload": w.name, "B": w.B, "H": w.H, "N": N, "d_h": w.d,
+                      "causal": w.causal, "k": k_top},
+           "roofline": {"bound": "mfma", "kernel": "topk", "achieved": round(achieved, 2),
+                        "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                        "avg_launch_us": round(ms * 1e3, 1), "traffic": None}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +190,9 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--topk", action="store_true",
+                    help="time elsaa_topk (exact per-query top-k keys, k = the workload's block) "
+                         "alone instead of the fwd+bwd step")
     ap.add_argument("--learned-gates", action="store_true",
                     help="gates of Eq. 4 from a learned projection of the query (elsaa_gates_fwd/"
                          "_bwd in every step) instead of unit gates")
@@ -203,6 +242,8 @@ def main():
         if args.learned_gates:
             S.gates_backward(cfg, d["q"], gate_w, gs, gl, g["dg_s"], g["dg_lr"], g["dQ"])
 
+    if args.topk:
+        return bench_topk(args, w, cfg, d)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

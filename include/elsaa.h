@@ -218,6 +218,21 @@ elsaa_status elsaa_bwd(const elsaa_params* p, const void* Q, const void* K, cons
                        void* dK, void* dV, float* dlambda, float* dg_s, float* dg_lr, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* Exact per-query top-k key selection on Q K^T, the top-k kind of sparse selector
+ * the paper lists beside sortLSH (Section 3), as an alternative to elsaa_select.
+ * For query i the candidate keys are every j (causal: j <= i); the score of (i, j)
+ * is the fp64 fused-multiply-add chain acc = fma(Q_i[c], K_j[c], acc), c = 0 ..
+ * d_h-1, from +0.0 (the positive score scale does not change the order); the set
+ * holds the min(k, #candidates) keys of largest score, ties to the lower index.
+ *   p   : as for the other calls; B, H, N, d_h, dtype and causal are used.
+ *   k   : 1 .. 256 keys per query (ELSAA_ERR_UNSUPPORTED above).
+ *   idx (out): int32 [B, H, N, k], each query's set in ascending key order, -1
+ *       past min(k, #candidates).
+ * The sets are exact: any correctly rounded fp64 implementation of the chain
+ * selects the same keys. No workspace. */
+elsaa_status elsaa_topk(const elsaa_params* p, const void* Q, const void* K, int32_t k,
+                        int32_t* idx, void* stream);
+
 /* Learnable gates of Eq. 4. The paper has g_sparse,i and g_lr,i learned with the
  * model (Section 7: shared by ELSAA and its Sort_Lsh_RACE ablation, and on NIAH
  * the gate learns to up-weight the low-rank branch; Section 8: gate schedules per

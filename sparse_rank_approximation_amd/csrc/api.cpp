@@ -296,6 +296,18 @@ elsaa_status elsaa_bwd(const elsaa_params* p, const void* Q, const void* K, cons
   return launched();
 }
 
+elsaa_status elsaa_topk(const elsaa_params* p, const void* Q, const void* K, int32_t k,
+                        int32_t* idx, void* stream) {
+  PROLOGUE(ELSAA_CALL_SELECT);
+  if (k < 1) return fail(ELSAA_ERR_INVALID_ARG, "k = %d must be >= 1", k);
+  if (!elsaa::launch_topk(pb, Q, K, k, idx, (hipStream_t)stream, true))
+    return fail(ELSAA_ERR_UNSUPPORTED, "k = %d: at most 256 keys per query are built", k);
+  if (empty) return ELSAA_OK;
+  NEED(Q); NEED(K); NEED(idx);
+  elsaa::launch_topk(pb, Q, K, k, idx, (hipStream_t)stream, false);
+  return launched();
+}
+
 elsaa_status elsaa_gates_fwd(const elsaa_params* p, const void* Q, const float* W,
                              const float* b, float* g_s, float* g_lr, void* stream) {
   PROLOGUE(ELSAA_CALL_GATES_BWD);

@@ -198,6 +198,11 @@ bool launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
                 const float* g_lr, void* O, float* O_s, void* O_lr, float* lse, float* d_lr,
                 void* ws, hipStream_t st, bool dry);
 
+// Exact per-query top-k selection (topk.hip); dry: report only whether a variant
+// is built for k.
+bool launch_topk(const Problem& pb, const void* Q, const void* K, int ktop, int32_t* out,
+                 hipStream_t st, bool dry);
+
 // Learnable gates of Eq. 4 from a projection of the query (gates.hip).
 size_t gates_bwd_ws_bytes(const Problem& pb);
 void launch_gates_fwd(const Problem& pb, const void* Q, const float* W, const float* b, float* gs,

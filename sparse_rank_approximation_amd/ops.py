@@ -155,6 +155,20 @@ def select_noalloc(cfg: ElsaaConfig, q, k, planes_s, out=None):
     return qc, kc, qp, kp
 
 
+def topk(cfg: ElsaaConfig, q, k, k_top: int):
+    """elsaa_topk: exact per-query top-k keys on Q K^T, int32 [B,H,N,k_top] ascending,
+    -1 padded (causal: keys j <= i)."""
+    dev = q.device
+    x = (cfg.B, cfg.H, cfg.N, cfg.d)
+    _check_tensor("q", q, x, cfg.dtype, dev)
+    _check_tensor("k", k, x, cfg.dtype, dev)
+    idx = torch.empty(cfg.B, cfg.H, cfg.N, k_top, dtype=torch.int32, device=dev)
+    p = cfg.params()
+    _lib.check(_lib.lib().elsaa_topk(ctypes.byref(p), _ptr(q), _ptr(k), int(k_top), _ptr(idx),
+                                     _stream(dev)))
+    return idx
+
+
 def lowrank_summary(cfg: ElsaaConfig, k, v, planes_lr):
     """elsaa_lowrank_summary: A [B,H,nA,d,r], z [B,H,nA,r] fp32."""
     dev = k.device
