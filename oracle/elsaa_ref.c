@@ -34,6 +34,7 @@ static int check_params(const ref_params* p) {
   if (!p || p->G <= 0 || p->N <= 0 || p->d <= 0) return RET_BAD;
   if (p->block <= 0 || p->N % p->block) return RET_BAD;
   if (p->hash_bits < 1 || p->hash_bits > 16) return RET_BAD;
+  if (p->hash_rounds < 0 || p->hash_rounds > 16) return RET_BAD;
   if (p->lr_tables < 1 || p->lr_bits < 0 || p->lr_bits > 8) return RET_BAD;
   if (p->causal) {
     if (ilog2_exact(p->N / p->block) < 0) return RET_BAD;
@@ -41,6 +42,9 @@ static int check_params(const ref_params* p) {
   }
   return 0;
 }
+
+/* sortLSH hash tables (rounds); 0 means one. */
+static int n_rounds(const ref_params* p) { return p->hash_rounds > 1 ? p->hash_rounds : 1; }
 
 /* Number of off-diagonal recursion levels of the causal sparse branch. */
 static int n_levels(const ref_params* p) {
@@ -126,16 +130,26 @@ static size_t perm_len(const ref_params* p) {
   return p->causal ? (size_t)n_levels(p) * (p->N / 2) : (size_t)p->N;
 }
 
+/* Every round's codes and orders of one head (round r uses its own hyperplanes). */
+static void select_rounds(const ref_params* p, const double* Q, const double* K,
+                          const float* planes, uint16_t* qc, uint16_t* kc, int32_t* qperm,
+                          int32_t* kperm) {
+  const size_t pl = perm_len(p), np = (size_t)p->hash_bits * p->d;
+  for (int r = 0; r < n_rounds(p); ++r)
+    select_head(p, Q, K, planes + r * np, qc + (size_t)r * p->N, kc + (size_t)r * p->N,
+                qperm + r * pl, kperm + r * pl);
+}
+
 int ref_select(const ref_params* p, const double* Q, const double* K,
                const float* planes_s, uint16_t* q_code, uint16_t* k_code,
                int32_t* q_perm, int32_t* k_perm) {
   if (check_params(p)) return RET_BAD;
-  const size_t nd = (size_t)p->N * p->d, pl = perm_len(p);
+  const size_t nd = (size_t)p->N * p->d, R = n_rounds(p), pl = perm_len(p);
 #pragma omp parallel for schedule(dynamic)
   for (int g = 0; g < p->G; ++g)
-    select_head(p, Q + g * nd, K + g * nd, planes_s + (size_t)g * p->hash_bits * p->d,
-                q_code + (size_t)g * p->N, k_code + (size_t)g * p->N,
-                q_perm + g * pl, k_perm + g * pl);
+    select_rounds(p, Q + g * nd, K + g * nd, planes_s + (size_t)g * R * p->hash_bits * p->d,
+                  q_code + (size_t)g * R * p->N, k_code + (size_t)g * R * p->N,
+                  q_perm + g * R * pl, k_perm + g * R * pl);
   return 0;
 }
 
@@ -249,6 +263,72 @@ static void sparse_head(const head_in* h, double* O_s, double* lse) {
   else
     sortlsh_blocks(h, h->qperm, h->kperm, h->p->N, Ob, lseb, emit_store, &acc);
   free(Ob); free(lseb);
+}
+
+/* Several hash rounds (Appendix C: L_s independent hash tables, the support
+ * Omega_LSH being the union of what each table selects). The union support of
+ * query i: its causal leaf, and for every round the key block paired with i's
+ * query block at every level where i is a future query (one level when not
+ * causal). Written as mark[j] = 1 for the keys j in it (each key once). invq:
+ * [rounds][levels][N], position of a token within its level's query order, or -1. */
+static void union_support(const ref_params* p, const int32_t* qperm, const int32_t* kperm,
+                          const int32_t* invq, int i, unsigned char* mark) {
+  const int N = p->N, s = p->block, L = n_levels(p), R = n_rounds(p);
+  const size_t pl = perm_len(p);
+  memset(mark, 0, N);
+  if (p->causal)
+    for (int j = (i / s) * s; j <= i; ++j) mark[j] = 1;
+  for (int r = 0; r < R; ++r)
+    for (int l = 0; l < L; ++l) {
+      const int t = invq[((size_t)r * L + l) * N + i];
+      if (t < 0) continue;
+      const int32_t* ks = kperm + r * pl + (size_t)l * (p->causal ? N / 2 : N) + (size_t)(t / s) * s;
+      for (int b = 0; b < s; ++b) mark[ks[b]] = 1;
+    }
+}
+
+static int32_t* query_positions(const ref_params* p, const int32_t* qperm) {
+  const int N = p->N, L = n_levels(p), R = n_rounds(p);
+  const size_t pl = perm_len(p), len = p->causal ? (size_t)N / 2 : (size_t)N;
+  int32_t* invq = (int32_t*)malloc(sizeof(int32_t) * (size_t)R * L * N);
+  for (size_t e = 0; e < (size_t)R * L * N; ++e) invq[e] = -1;
+  for (int r = 0; r < R; ++r)
+    for (int l = 0; l < L; ++l)
+      for (size_t t = 0; t < len; ++t)
+        invq[((size_t)r * L + l) * N + qperm[r * pl + (size_t)l * len + t]] = (int32_t)t;
+  return invq;
+}
+
+/* Sparse branch over the union support: one exact softmax per query. */
+static void sparse_union_head(const head_in* h, double* O_s, double* lse) {
+  const ref_params* p = h->p;
+  const int N = p->N, d = p->d;
+  int32_t* invq = query_positions(p, h->qperm);
+  unsigned char* mark = (unsigned char*)malloc(N);
+  double* e = (double*)malloc(sizeof(double) * N);
+  for (int i = 0; i < N; ++i) {
+    union_support(p, h->qperm, h->kperm, invq, i, mark);
+    double mx = -INFINITY;
+    for (int j = 0; j < N; ++j) {
+      if (!mark[j]) continue;
+      double sc = 0.0;
+      for (int c = 0; c < d; ++c) sc += h->Q[(size_t)i * d + c] * h->K[(size_t)j * d + c];
+      e[j] = sc * p->scale;
+      if (e[j] > mx) mx = e[j];
+    }
+    double den = 0.0;
+    for (int j = 0; j < N; ++j)
+      if (mark[j]) { e[j] = exp(e[j] - mx); den += e[j]; }
+    double* o = O_s + (size_t)i * d;
+    for (int c = 0; c < d; ++c) o[c] = 0.0;
+    for (int j = 0; j < N; ++j) {
+      if (!mark[j]) continue;
+      const double w = e[j] / den;
+      for (int c = 0; c < d; ++c) o[c] += w * h->V[(size_t)j * d + c];
+    }
+    lse[i] = mx + log(den);
+  }
+  free(invq); free(mark); free(e);
 }
 
 /* ------------------------------------------------------------------------- */
@@ -386,7 +466,7 @@ typedef struct {
 } head_fwd;
 
 static void head_fwd_alloc(const ref_params* p, head_fwd* f) {
-  const size_t N = p->N, d = p->d, r = feat_dim(p), pl = perm_len(p);
+  const size_t N = p->N, d = p->d, r = feat_dim(p), pl = perm_len(p) * n_rounds(p);
   f->O_s = (double*)malloc(sizeof(double) * N * d);
   f->lse = (double*)malloc(sizeof(double) * N);
   f->qf = (double*)malloc(sizeof(double) * N * r);
@@ -397,8 +477,8 @@ static void head_fwd_alloc(const ref_params* p, head_fwd* f) {
   f->m = (double*)malloc(sizeof(double) * N);
   f->qperm = (int32_t*)malloc(sizeof(int32_t) * pl);
   f->kperm = (int32_t*)malloc(sizeof(int32_t) * pl);
-  f->qc = (uint16_t*)malloc(sizeof(uint16_t) * N);
-  f->kc = (uint16_t*)malloc(sizeof(uint16_t) * N);
+  f->qc = (uint16_t*)malloc(sizeof(uint16_t) * N * n_rounds(p));
+  f->kc = (uint16_t*)malloc(sizeof(uint16_t) * N * n_rounds(p));
 }
 
 static void head_fwd_free(head_fwd* f) {
@@ -427,9 +507,12 @@ static void forward_head(const ref_params* p, const double* Q, const double* K,
                          const double* V, const float* Rs, const float* Rlr, double lam,
                          const double* gs, const double* glr, head_fwd* f, double* O) {
   const int N = p->N, d = p->d;
-  select_head(p, Q, K, Rs, f->qc, f->kc, f->qperm, f->kperm);
+  select_rounds(p, Q, K, Rs, f->qc, f->kc, f->qperm, f->kperm);
   head_in h = {p, Q, K, V, f->qperm, f->kperm};
-  sparse_head(&h, f->O_s, f->lse);
+  if (n_rounds(p) == 1)
+    sparse_head(&h, f->O_s, f->lse);
+  else
+    sparse_union_head(&h, f->O_s, f->lse);
   all_features(p, Rlr, Q, f->qf);
   all_features(p, Rlr, K, f->kf);
   lowrank_head(p, f->qf, f->kf, V, f->num, f->den);
@@ -450,7 +533,8 @@ int ref_fwd(const ref_params* p, const double* Q, const double* K, const double*
             double* O, double* O_s, double* O_lr, double* lse, double* d_lr) {
   if (check_params(p) || !lambda) return RET_BAD;
   const size_t N = p->N, nd = N * p->d;
-  const size_t ps = (size_t)p->hash_bits * p->d, plr = (size_t)p->lr_tables * p->lr_bits * p->d;
+  const size_t ps = (size_t)n_rounds(p) * p->hash_bits * p->d;
+  const size_t plr = (size_t)p->lr_tables * p->lr_bits * p->d;
 #pragma omp parallel for schedule(dynamic)
   for (int g = 0; g < p->G; ++g) {
     head_fwd f;
@@ -523,6 +607,38 @@ static void sparse_bwd_rec(const head_in* h, int a, int n, int l, const double* 
                         0, O_s, lse, dOs, dlse, dQ, dK, dV);
 }
 
+/* The same over the union support of several hash rounds, one query at a time. */
+static void sparse_union_bwd(const head_in* h, const double* O_s, const double* lse,
+                             const double* dOs, const double* dlse, double* dQ, double* dK,
+                             double* dV) {
+  const ref_params* p = h->p;
+  const int N = p->N, d = p->d;
+  const double sc = p->scale;
+  int32_t* invq = query_positions(p, h->qperm);
+  unsigned char* mark = (unsigned char*)malloc(N);
+  for (int i = 0; i < N; ++i) {
+    union_support(p, h->qperm, h->kperm, invq, i, mark);
+    double Di = 0.0;
+    for (int c = 0; c < d; ++c) Di += dOs[(size_t)i * d + c] * O_s[(size_t)i * d + c];
+    for (int j = 0; j < N; ++j) {
+      if (!mark[j]) continue;
+      double s = 0.0, dp = 0.0;
+      for (int c = 0; c < d; ++c) {
+        s += h->Q[(size_t)i * d + c] * h->K[(size_t)j * d + c];
+        dp += dOs[(size_t)i * d + c] * h->V[(size_t)j * d + c];
+      }
+      const double pij = exp(s * sc - lse[i]);
+      const double ds = pij * (dp - Di) + pij * dlse[i];
+      for (int c = 0; c < d; ++c) {
+        dV[(size_t)j * d + c] += pij * dOs[(size_t)i * d + c];
+        dQ[(size_t)i * d + c] += sc * ds * h->K[(size_t)j * d + c];
+        dK[(size_t)j * d + c] += sc * ds * h->Q[(size_t)i * d + c];
+      }
+    }
+  }
+  free(invq); free(mark);
+}
+
 /* Backward of phi = per-table softmax over hypercube vertices, then through the
  * projections u_lt = scale <R_lt, x>: adds d(loss)/dx to dx. */
 static void features_row_bwd(const ref_params* p, const float* R, const double* phi,
@@ -592,7 +708,9 @@ static void backward_head(const ref_params* p, const double* Q, const double* K,
   memset(dK, 0, sizeof(double) * (size_t)N * d);
   memset(dV, 0, sizeof(double) * (size_t)N * d);
   head_in h = {p, Q, K, V, f.qperm, f.kperm};
-  if (p->causal)
+  if (n_rounds(p) > 1)
+    sparse_union_bwd(&h, f.O_s, f.lse, dOs, dlse, dQ, dK, dV);
+  else if (p->causal)
     sparse_bwd_rec(&h, 0, N, 0, f.O_s, f.lse, dOs, dlse, dQ, dK, dV);
   else
     for (int b = 0; b < N / p->block; ++b)
@@ -669,7 +787,8 @@ int ref_bwd(const ref_params* p, const double* Q, const double* K, const double*
             double* dg_s, double* dg_lr) {
   if (check_params(p) || !lambda) return RET_BAD;
   const size_t N = p->N, nd = N * p->d;
-  const size_t ps = (size_t)p->hash_bits * p->d, plr = (size_t)p->lr_tables * p->lr_bits * p->d;
+  const size_t ps = (size_t)n_rounds(p) * p->hash_bits * p->d;
+  const size_t plr = (size_t)p->lr_tables * p->lr_bits * p->d;
 #pragma omp parallel for schedule(dynamic)
   for (int g = 0; g < p->G; ++g) {
     double dl = 0.0;

@@ -10,13 +10,16 @@
  * Every array holds G independent heads (the paper applies the operator to each
  * head independently, Section 3), contiguous, row-major:
  *   Q, K, V, dO, O, O_s, O_lr, dQ, dK, dV : double [G][N][d]
- *   planes_s  : float  [G][hash_bits][d]           (sortLSH hyperplanes)
+ *   planes_s  : float  [G][rounds][hash_bits][d]   (sortLSH hyperplanes; rounds =
+ *               hash_rounds, the L_s independent hash tables of Appendix C)
  *   planes_lr : float  [G][lr_tables][lr_bits][d]  (RACE hyperplanes)
  *   lambda    : double [G]
  *   g_s, g_lr : double [G][N] or NULL (NULL means every gate is 1)
- *   codes     : uint16 [G][N]
- *   perms     : int32  [G][levels][N/2] when causal (levels = log2(N/block)),
- *               int32  [G][1][N] when not
+ *   codes     : uint16 [G][rounds][N]
+ *   perms     : int32  [G][rounds][levels][N/2] when causal (levels =
+ *               log2(N/block)), int32 [G][rounds][1][N] when not
+ * With several rounds the sparse support of a query is the union of the rounds'
+ * supports (each pair counted once), Appendix C's Omega_LSH.
  *   A, z      : double [G][r][d], [G][r] (non-causal: sums over all keys);
  *               double [G][N/chunk][r][d], [G][N/chunk][r] (causal: sums over
  *               keys strictly before each chunk), with r = lr_tables << lr_bits.
@@ -35,6 +38,7 @@ typedef struct {
   int lr_bits;     /* RACE hyperplanes per table (gamma)         */
   int chunk;       /* causal RACE summary spacing C              */
   double tau, eps, scale;
+  int hash_rounds; /* sortLSH hash tables L_s (0 or 1: one)             */
 } ref_params;
 
 int ref_select(const ref_params* p, const double* Q, const double* K,

@@ -39,7 +39,8 @@ class _P(ctypes.Structure):
     _fields_ = [("G", ctypes.c_int), ("N", ctypes.c_int), ("d", ctypes.c_int),
                 ("causal", ctypes.c_int), ("block", ctypes.c_int), ("hash_bits", ctypes.c_int),
                 ("lr_tables", ctypes.c_int), ("lr_bits", ctypes.c_int), ("chunk", ctypes.c_int),
-                ("tau", ctypes.c_double), ("eps", ctypes.c_double), ("scale", ctypes.c_double)]
+                ("tau", ctypes.c_double), ("eps", ctypes.c_double), ("scale", ctypes.c_double),
+                ("hash_rounds", ctypes.c_int)]
 
 
 @dataclass
@@ -55,6 +56,7 @@ class RefParams:
     tau: float = 1.0
     eps: float = 1e-6
     scale: float | None = None
+    hash_rounds: int = 1
 
     @property
     def r(self) -> int:
@@ -74,7 +76,7 @@ class RefParams:
     def c(self, G: int) -> _P:
         sc = self.scale if self.scale is not None else 1.0 / math.sqrt(self.d)
         return _P(G, self.N, self.d, int(self.causal), self.block, self.hash_bits, self.lr_tables,
-                  self.lr_bits, self.chunk, self.tau, self.eps, sc)
+                  self.lr_bits, self.chunk, self.tau, self.eps, sc, self.hash_rounds)
 
 
 _lib = None
@@ -105,18 +107,24 @@ def _check(rc, what):
 
 
 def select(p: RefParams, q, k, planes_s):
+    """Codes and orders of every head. One round: codes [G, N], orders [G, levels, N/2]
+    (causal) or [G, 1, N]; several (planes_s [G, rounds, bits, d]): a round axis after G."""
     q, k, ps = _f64(q), _f64(k), _f32(planes_s)
     G, N = q.shape[0], p.N
+    R = max(1, p.hash_rounds)
     plen = p.levels * (N // 2) if p.causal else N
-    qc = np.zeros((G, N), np.uint16)
-    kc = np.zeros((G, N), np.uint16)
-    qp = np.zeros((G, plen), np.int32)
-    kp = np.zeros((G, plen), np.int32)
+    qc = np.zeros((G, R, N), np.uint16)
+    kc = np.zeros((G, R, N), np.uint16)
+    qp = np.zeros((G, R, plen), np.int32)
+    kp = np.zeros((G, R, plen), np.int32)
     pc = p.c(G)
     _check(lib().ref_select(ctypes.byref(pc), _ptr(q), _ptr(k), _ptr(ps), _ptr(qc), _ptr(kc),
                             _ptr(qp), _ptr(kp)), "select")
-    shape = (G, p.levels, N // 2) if p.causal else (G, 1, N)
-    return qc, kc, qp.reshape(shape), kp.reshape(shape)
+    shape = (G, R, p.levels, N // 2) if p.causal else (G, R, 1, N)
+    qp, kp = qp.reshape(shape), kp.reshape(shape)
+    if R == 1:
+        return qc[:, 0], kc[:, 0], qp[:, 0], kp[:, 0]
+    return qc, kc, qp, kp
 
 
 def lowrank_summary(p: RefParams, k, v, planes_lr):

@@ -557,3 +557,57 @@ def test_topk_ties_take_the_lower_index_and_sets_are_causal():
             assert sel == [10] + list(range(40, 47)), (i, sel)
     p.causal = False
     assert ref.topk(p, q, k, N + 5)[0, 3].tolist() == list(range(N)) + [-1] * 5
+
+
+# ----------------------------------------------------------------------------- several hash rounds
+
+def _round_planes(ps, R, seed):
+    """R rounds of sortLSH hyperplanes [1, R, bits, d]: round 0 the given ones."""
+    rng = np.random.default_rng(seed)
+    out = [ps[0]] + [rng.normal(size=ps[0].shape).astype(np.float32) for _ in range(R - 1)]
+    return np.stack(out)[None]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_repeated_round_equals_one_round(causal):
+    """Two rounds with the same hyperplanes select every pair twice; the union
+    counts it once, so the operator equals the one-round operator (forward and
+    backward)."""
+    w = small(causal, N=128, d=16, block=16, r=32)
+    p1 = ref.RefParams.from_workload(w)
+    p2 = ref.RefParams.from_workload(w, hash_rounds=2)
+    q, k, v, do, ps, pl = head(w, 97)
+    ps2 = np.stack([ps[0], ps[0]])[None]
+    o1 = ref.forward(p1, q[None], k[None], v[None], ps, pl, np.array([0.7]))
+    o2 = ref.forward(p2, q[None], k[None], v[None], ps2, pl, np.array([0.7]))
+    for n in ("O", "O_s", "lse"):
+        np.testing.assert_allclose(o2[n], o1[n], rtol=1e-12, atol=1e-12)
+    g1 = ref.backward(p1, q[None], k[None], v[None], do[None], ps, pl, np.array([0.7]))
+    g2 = ref.backward(p2, q[None], k[None], v[None], do[None], ps2, pl, np.array([0.7]))
+    for n in ("dQ", "dK", "dV", "dlambda"):
+        np.testing.assert_allclose(g2[n], g1[n], rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("R", [2, 3])
+def test_rounds_union_matches_dense_masked_softmax_and_autograd(causal, R):
+    """Several rounds: the sparse branch is the softmax over the union of the
+    rounds' supports (dense brute force with the OR of each round's mask), and the
+    backward equals autograd of the dense formulation over that mask."""
+    w = small(causal, N=128, d=16, block=16, r=32)
+    p = ref.RefParams.from_workload(w, hash_rounds=R)
+    q, k, v, do, ps, pl = head(w, 101 + R)
+    psR = _round_planes(ps, R, 7 + R)
+    _, _, qp, kp = ref.select(p, q[None], k[None], psR)
+    masks = [D.support_mask(128, 16, causal, qp[0, r], kp[0, r]) for r in range(R)]
+    M = np.logical_or.reduce(masks)
+    assert M.sum() > max(m.sum() for m in masks) and M.sum() <= sum(m.sum() for m in masks)
+    tq, tk, tv = (torch.from_numpy(x).clone().requires_grad_(True) for x in (q, k, v))
+    dn = D.dense_forward(tq, tk, tv, M, torch.from_numpy(pl[0]), 1.2, causal, 0.25)
+    o = ref.forward(p, q[None], k[None], v[None], psR, pl, np.array([1.2]))
+    for n in ("O", "O_s", "lse", "d_lr"):
+        np.testing.assert_allclose(o[n][0], dn[n].detach().numpy(), atol=1e-10, rtol=1e-9)
+    (dn["O"] * torch.from_numpy(do)).sum().backward()
+    g = ref.backward(p, q[None], k[None], v[None], do[None], psR, pl, np.array([1.2]))
+    for a, b in ((g["dQ"][0], tq.grad), (g["dK"][0], tk.grad), (g["dV"][0], tv.grad)):
+        np.testing.assert_allclose(a, b.numpy(), atol=1e-10, rtol=1e-9)
