@@ -88,8 +88,9 @@ typedef enum {
  *   B, H, N, d_h : batch, heads, tokens, head dimension; d_h in {32, 64, 128};
  *                  N a multiple of 32 up to 2^24; B * H == 0 is a valid empty
  *                  problem; B * H <= 65535, and B * H times the number of sparse
- *                  blocks per head (causal: log2(N/s) * N/(2s) + N/s; otherwise
- *                  N/s) below 2^31 (larger batches are split over calls).
+ *                  blocks per head (causal: R log2(N/s) N/(2s) + N/s; otherwise
+ *                  R N/s, R = hash_rounds) below 2^31 (larger batches are split
+ *                  over calls).
  *   dtype        : element type of Q, K, V, O, dO, dQ, dK, dV (elsaa_dtype).
  *   causal       : 0 = every query may see every key; 1 = key j only for j <= i.
  *   block        : sortLSH block size s in {16, 32, 64, 128, 256}; N % s == 0; when
@@ -107,9 +108,15 @@ typedef enum {
  *   tau          : temperature of the soft bucket assignment (> 0).
  *   eps          : the epsilon of Eq. 5 (>= 0).
  *   scale        : score scale, normally 1/sqrt(d_h) (Section 3) (> 0).
+ *   hash_rounds  : sortLSH hash tables R (Appendix C's L_s), 0 or 1 for one, at
+ *                  most 4. Each round hashes with its own hyperplanes and sorts
+ *                  independently; a query's sparse support is the union of the
+ *                  rounds' supports, each pair counted once (Appendix C's
+ *                  Omega_LSH). The per-query counts above then become upper bounds.
  * Derived: levels Lv = log2(N / s) when causal (off-diagonal recursion levels), 1
- * when not; the permutation length P = Lv * N / 2 when causal, N when not; the
- * number of summaries nA = N / C when causal, 1 when not.
+ * when not; the permutation length P = R * Lv * N / 2 when causal, R * N when not
+ * (the rounds' orders one after another); the number of summaries nA = N / C when
+ * causal, 1 when not.
  */
 typedef struct {
   int32_t B, H, N, d_h;
@@ -120,6 +127,7 @@ typedef struct {
   int32_t lr_tables, lr_bits;
   int32_t chunk;
   float tau, eps, scale;
+  int32_t hash_rounds;
 } elsaa_params;
 
 /* Bytes of workspace the given call needs for these parameters (written to
@@ -130,18 +138,19 @@ elsaa_status elsaa_workspace_size(const elsaa_params* p, int32_t call, size_t* b
 /* sortLSH selection (Section 3.2: queries and keys are hashed, sorted by hash and
  * grouped into equal-size blocks; query block b pairs with key block b).
  *   Q, K      : [B, H, N, d_h] dtype.
- *   planes_s  : fp32 [H, hash_bits, d_h], the hyperplanes of each head.
- *   q_code, k_code (out): uint16 [B, H, N]. Bit b of a token's code is set iff the
+ *   planes_s  : fp32 [H, R, hash_bits, d_h], the hyperplanes of each head and
+ *               round.
+ *   q_code, k_code (out): uint16 [B, H, R, N]. Bit b of a token's code is set iff the
  *               projection of its row x on hyperplane b is > 0, the projection being
  *               the fp64 fused-multiply-add chain acc = fma(x[j], R[b][j], acc) for
  *               j = 0..d_h-1 from acc = +0.0.
  *   q_perm, k_perm (out): int32 [B, H, P]. Tokens are ordered by the position of
  *               their code along the reflected Gray sequence, ties by ascending
- *               token index. Non-causal: one order of all N tokens. Causal: for
- *               level l in [0, Lv) and segment g of n = N >> l tokens starting at
- *               a = g n, entries [l N/2 + g n/2, l N/2 + (g+1) n/2) hold the sorted
- *               future half [a + n/2, a + n) (q_perm) and past half [a, a + n/2)
- *               (k_perm).
+ *               token index. Non-causal: round u's order of all N tokens at
+ *               [u N, (u+1) N). Causal: for round u, level l in [0, Lv) and segment
+ *               g of n = N >> l tokens starting at a = g n, the entries starting at
+ *               (u Lv + l) N/2 + g n/2, n/2 of them, hold the sorted future half
+ *               [a + n/2, a + n) (q_perm) and past half [a, a + n/2) (k_perm).
  *   ws        : device workspace of elsaa_workspace_size(p, ELSAA_CALL_SELECT) bytes
  *               (the hyperplanes widened to fp64).
  */

@@ -27,7 +27,7 @@ class Params(ctypes.Structure):
                 ("block", ctypes.c_int32), ("hash_bits", ctypes.c_int32),
                 ("lr_tables", ctypes.c_int32), ("lr_bits", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("tau", ctypes.c_float), ("eps", ctypes.c_float),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("hash_rounds", ctypes.c_int32)]
 
 
 class ElsaaError(RuntimeError):

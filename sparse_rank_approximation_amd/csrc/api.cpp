@@ -71,6 +71,10 @@ elsaa_status make_problem(const elsaa_params* p, Problem* pb, bool* empty) {
   if (p->hash_bits > elsaa::kMaxHashBits)
     return fail(ELSAA_ERR_UNSUPPORTED, "hash_bits = %d: at most %d are built", p->hash_bits,
                 elsaa::kMaxHashBits);
+  if (p->hash_rounds < 0) return fail(ELSAA_ERR_INVALID_ARG, "hash_rounds must be >= 0");
+  if (p->hash_rounds > elsaa::kMaxRounds)
+    return fail(ELSAA_ERR_UNSUPPORTED, "hash_rounds = %d: at most %d are built", p->hash_rounds,
+                elsaa::kMaxRounds);
   if (p->lr_tables < 1) return fail(ELSAA_ERR_INVALID_ARG, "lr_tables must be >= 1");
   if (p->lr_tables > elsaa::kMaxTables)
     return fail(ELSAA_ERR_UNSUPPORTED, "lr_tables = %d: at most %d are built", p->lr_tables,
@@ -93,7 +97,8 @@ elsaa_status make_problem(const elsaa_params* p, Problem* pb, bool* empty) {
                 (long)p->B * p->H);
   {
     const long nb = p->N / p->block;
-    const long items = p->causal ? (long)ilog2((int)nb) * (nb / 2) + nb : nb;
+    const long R = p->hash_rounds > 1 ? p->hash_rounds : 1;
+    const long items = p->causal ? R * ilog2((int)nb) * (nb / 2) + nb : R * nb;
     if (items * p->B * p->H > 0x7fffffffL)
       return fail(ELSAA_ERR_INVALID_ARG,
                   "B * H * %ld sparse blocks exceeds 2^31 - 1: split the heads over calls", items);
@@ -109,6 +114,7 @@ elsaa_status make_problem(const elsaa_params* p, Problem* pb, bool* empty) {
   pb->chunk = pb->causal ? p->chunk : p->N;
   pb->tau = p->tau; pb->eps = p->eps; pb->scale = p->scale;
   pb->levels = pb->causal ? ilog2(p->N / p->block) : 1;
+  pb->rounds = p->hash_rounds > 1 ? p->hash_rounds : 1;
   pb->nA = pb->causal ? p->N / pb->chunk : 1;
   pb->elem = pb->bf16 ? 2 : 4;
   if (lds_need(*pb) > elsaa::kLdsBytes)
@@ -194,7 +200,7 @@ elsaa_status elsaa_select(const elsaa_params* p, const void* Q, const void* K,
   PROLOGUE(ELSAA_CALL_SELECT);
   if (empty) return ELSAA_OK;
   NEED(Q); NEED(K); NEED(planes_s); NEED(q_code); NEED(k_code);
-  if (elsaa::perm_stride(pb.N, pb.levels, pb.causal) > 0) { NEED(q_perm); NEED(k_perm); }
+  if (elsaa::perm_stride(pb.N, pb.levels, pb.causal, pb.rounds) > 0) { NEED(q_perm); NEED(k_perm); }
   OPTIONAL(q_perm); OPTIONAL(k_perm);
   {
     elsaa_status s_ = check_ws(pb, ELSAA_CALL_SELECT, ws, ws_bytes);
@@ -211,7 +217,7 @@ elsaa_status elsaa_select_noalloc(const elsaa_params* p, const void* Q, const vo
   PROLOGUE(ELSAA_CALL_SELECT);
   if (empty) return ELSAA_OK;
   NEED(Q); NEED(K); NEED(planes_s); NEED(q_code); NEED(k_code);
-  if (elsaa::perm_stride(pb.N, pb.levels, pb.causal) > 0) { NEED(q_perm); NEED(k_perm); }
+  if (elsaa::perm_stride(pb.N, pb.levels, pb.causal, pb.rounds) > 0) { NEED(q_perm); NEED(k_perm); }
   OPTIONAL(q_perm); OPTIONAL(k_perm);
   const size_t n = elsaa::select_ws_bytes(pb), cap = elsaa::noalloc_scratch_bytes();
   if (n > cap)
@@ -252,7 +258,7 @@ elsaa_status elsaa_fwd(const elsaa_params* p, const void* Q, const void* K, cons
   PROLOGUE(ELSAA_CALL_FWD);
   if (empty) return ELSAA_OK;
   NEED(Q); NEED(K); NEED(V); NEED(planes_lr); NEED(A); NEED(z);
-  if (elsaa::perm_stride(pb.N, pb.levels, pb.causal) > 0) { NEED(q_perm); NEED(k_perm); }
+  if (elsaa::perm_stride(pb.N, pb.levels, pb.causal, pb.rounds) > 0) { NEED(q_perm); NEED(k_perm); }
   OPTIONAL(q_perm); OPTIONAL(k_perm);
   NEED(lambda); OPTIONAL(g_s); OPTIONAL(g_lr);
   NEED(O); NEED(O_s); NEED(O_lr); NEED(lse_s); NEED(d_lr);
@@ -278,7 +284,7 @@ elsaa_status elsaa_bwd(const elsaa_params* p, const void* Q, const void* K, cons
   PROLOGUE(ELSAA_CALL_BWD);
   if (empty) return ELSAA_OK;
   NEED(Q); NEED(K); NEED(V); NEED(dO); NEED(O_s); NEED(O_lr); NEED(planes_lr);
-  if (elsaa::perm_stride(pb.N, pb.levels, pb.causal) > 0) { NEED(q_perm); NEED(k_perm); }
+  if (elsaa::perm_stride(pb.N, pb.levels, pb.causal, pb.rounds) > 0) { NEED(q_perm); NEED(k_perm); }
   OPTIONAL(q_perm); OPTIONAL(k_perm);
   NEED(A); NEED(z); NEED(lse_s); NEED(d_lr); NEED(lambda); OPTIONAL(g_s); OPTIONAL(g_lr);
   NEED(dQ); NEED(dK); NEED(dV); OPTIONAL(dlambda); OPTIONAL(dg_s); OPTIONAL(dg_lr);

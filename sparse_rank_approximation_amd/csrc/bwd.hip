@@ -201,7 +201,7 @@ __global__ void __launch_bounds__(256) dlam_reduce_kernel(const float* __restric
 //     queries in lanes, so dS^T feeds dQ^T += K^T dS^T.
 // ROLE selects key waves (1), query waves (2) or both (3, one launch); with one
 // role per launch only the tiles that role reads are staged.
-template <typename T, int D, int SB, int ROLE>
+template <typename T, int D, int SB, int ROLE, bool MR = false>
 struct SbwdSmem {
   static constexpr int KT = SB < 32 ? 32 : SB;
   static constexpr int LD = tile_ld<T>(D);
@@ -213,6 +213,8 @@ struct SbwdSmem {
   T Os[HQ ? KT : 1][LD];  // c * dO
   float lse[KT], Dd[KT], cq[KT], sig[KT];
   int kidx[KT], qidx[KT];
+  // Several hash rounds: the rows' block indices in the earlier rounds' orders.
+  int qbe[MR ? kMaxRounds - 1 : 1][MR ? KT : 1], kbe[MR ? kMaxRounds - 1 : 1][MR ? KT : 1];
 };
 
 template <int SB>
@@ -247,45 +249,55 @@ __device__ __forceinline__ void row_frags(const T* x, bool valid, float sc,
   }
 }
 
-template <typename T, int D, int SB, int ROLE>
+template <typename T, int D, int SB, int ROLE, bool MR>
 __global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
     sparse_bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                       const T* __restrict__ dO, const float* __restrict__ lse,
                       const float* __restrict__ rc, const float* __restrict__ rD,
                       const float* __restrict__ rsig, const int32_t* __restrict__ qperm,
-                      const int32_t* __restrict__ kperm, int N,
-                      int causal, int levels, float scale, T* __restrict__ dQp,
+                      const int32_t* __restrict__ kperm, int N, int causal, int levels,
+                      int rounds, const int32_t* __restrict__ qbid,
+                      const int32_t* __restrict__ kbid, float scale, T* __restrict__ dQp,
                       T* __restrict__ dKp, T* __restrict__ dVp) {
   typedef MF<T> M;
-  typedef SbwdSmem<T, D, SB, ROLE> Sm;
+  typedef SbwdSmem<T, D, SB, ROLE, MR> Sm;
   constexpr int KT = Sm::KT, NW = KT / 32, LD = Sm::LD;
   constexpr int NT = sbwd_threads<SB>(ROLE);
   __shared__ Sm sm;
   const int bh = blockIdx.y, item = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int w = wave_id();  // wave index, uniform (scalar) so that role branches stay uniform
-  const size_t P = perm_stride(N, levels, causal);
-  const size_t slots = partial_slots(N, levels, causal);
+  const size_t P = perm_stride(N, levels, causal, rounds);
+  const size_t slots = partial_slots(N, levels, causal, rounds);
   const size_t rowbase = (size_t)bh * N;
 
+  // Orders (round, level): causal rounds x levels, order-major items then the
+  // leaves; otherwise one order per round.
+  const int nord = causal ? rounds * levels : rounds;
   const int per_level = causal ? (N / 2) / SB : 0;
-  const int nlev_items = causal ? levels * per_level : 0;
+  const int nlev_items = causal ? nord * per_level : 0;
   const int32_t* qsrc = nullptr;
   const int32_t* ksrc = nullptr;
-  int lev = -1, tok0 = 0;
+  int ord = -1, lev = 0, rnd = 0, tok0 = 0;
   bool leaf = false;
   if (causal && item < nlev_items) {
-    lev = item / per_level;
+    ord = item / per_level;
+    lev = ord % levels;
+    rnd = ord / levels;
     const int b = item % per_level;
-    qsrc = qperm + (size_t)bh * P + (size_t)lev * (N / 2) + (size_t)b * SB;
-    ksrc = kperm + (size_t)bh * P + (size_t)lev * (N / 2) + (size_t)b * SB;
+    qsrc = qperm + (size_t)bh * P + (size_t)ord * (N / 2) + (size_t)b * SB;
+    ksrc = kperm + (size_t)bh * P + (size_t)ord * (N / 2) + (size_t)b * SB;
   } else if (causal) {
     leaf = true;
     tok0 = (item - nlev_items) * SB;
   } else {
+    ord = rnd = item / (N / SB);
     qsrc = qperm + (size_t)bh * P + (size_t)item * SB;
     ksrc = kperm + (size_t)bh * P + (size_t)item * SB;
   }
+  // The query's own block (its causal leaf, or its first round's block) adds
+  // sigma_i Q_i to its dQ part.
+  const bool own = causal ? leaf : rnd == 0;
   for (int t = tid; t < KT; t += NT) {
     const int kj = t < SB ? (leaf ? tok0 + t : ksrc[t]) : -1;
     const int qi = t < SB ? (leaf ? tok0 + t : qsrc[t]) : -1;
@@ -295,8 +307,23 @@ __global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
     sm.Dd[t] = qi >= 0 ? rD[rowbase + qi] : 0.0f;
     sm.cq[t] = qi >= 0 ? rc[rowbase + qi] : 0.0f;
     sm.sig[t] = qi >= 0 ? rsig[rowbase + qi] : 0.0f;
+    if constexpr (MR) {
+      for (int r = 0; r < rnd; ++r) {
+        const size_t base = ((size_t)bh * nord + (causal ? r * levels + lev : r)) * N;
+        sm.qbe[r][t] = qi >= 0 ? qbid[base + qi] : -1;
+        sm.kbe[r][t] = kj >= 0 ? kbid[base + kj] : -2;
+      }
+    }
   }
   __syncthreads();
+  // A pair that shares a block in an earlier round is held there (several rounds).
+  auto dup = [&](int qr, int kr) __attribute__((always_inline)) {
+    bool d = false;
+    if constexpr (MR) {
+      for (int r = 0; r < rnd; ++r) d = d || sm.qbe[r][qr] == sm.kbe[r][kr];
+    }
+    return d;
+  };
   if constexpr (Sm::HK) {
     T* const dst[2] = {&sm.Ks[0][0], &sm.Vs[0][0]};
     const T* const src[2] = {K, V};
@@ -325,8 +352,9 @@ __global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
         row_frags<T, D>(K + (rowbase + (kvalid ? jk : 0)) * D, kvalid, 1.0f, kf, h);
       }
       const int qt0 = leaf ? w : 0;
-      const size_t ksl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_past(jk, N, lev)
-                                  : (size_t)jk;
+      const size_t ksl = !causal ? (size_t)rnd * N + jk
+                         : leaf  ? (size_t)jk
+                                 : (size_t)N + (size_t)ord * (N / 2) + compact_past(jk, N, lev);
       // Pass 0: dV^T = (c dO)^T P.   Pass 1: dK^T = Q^T dS.
 #pragma unroll 1
       for (int pass = 0; pass < 2; ++pass) {
@@ -369,7 +397,8 @@ __global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
             const int qr = 32 * qt + acc_row(v, h);
             // Masked pairs get exp(-inf) = 0 (no branch around the exponential);
             // every row of a block of 32 or more is valid.
-            const bool ok = kvalid & (SB >= 32 || sm.qidx[qr] >= 0) & !(leaf & (key > qr));
+            const bool ok = kvalid & (SB >= 32 || sm.qidx[qr] >= 0) & !(leaf & (key > qr)) &
+                            !dup(qr, key);
             const float p = fast_exp(ok ? s[v] * scale - sm.lse[qr] : -INFINITY);
             s[v] = pass == 0 ? p : p * (dp[v] - sm.Dd[qr]);
           }
@@ -442,7 +471,8 @@ __global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int kr = 32 * kt + acc_row(v, h);
-          const bool ok = qvalid & (SB >= 32 || sm.kidx[kr] >= 0) & !(leaf & (kr > query));
+          const bool ok = qvalid & (SB >= 32 || sm.kidx[kr] >= 0) & !(leaf & (kr > query)) &
+                          !dup(query, kr);
           const float p = fast_exp(ok ? s[v] * scale - lq : -INFINITY);
           s[v] = p * (dp[v] - dq);
         }
@@ -457,12 +487,13 @@ __global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
       }
       // (the query's own block, its leaf or its only block, adds the support-wide
       // sum back)
-      sig = sum_halves(sig) - (lev < 0 ? sm.sig[query] : 0.0f);
+      sig = sum_halves(sig) - (own ? sm.sig[query] : 0.0f);
       float qv[D / 32][4][4];
       qrow.unpack(qv);
       if (qvalid) {
-        const size_t sl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_future_b(iq, N, lev)
-                                   : (size_t)iq;
+        const size_t sl = !causal ? (size_t)rnd * N + iq
+                          : leaf  ? (size_t)iq
+                                  : (size_t)N + (size_t)ord * (N / 2) + compact_future_b(iq, N, lev);
         T* dst = dQp + ((size_t)bh * slots + sl) * D;  // (qvalid: the same for a query's two lanes)
         // The block's dQ part relative to the query: sum_j dS_ij (K_j - Q_i).
 #pragma unroll
@@ -490,7 +521,7 @@ __global__ void __launch_bounds__(sbwd_threads<SB>(ROLE))
 // P = exp(scale S - lse), dS = P (c dP_raw - D) (c = g_s m per query row),
 // dV^T += dO^T (c P) and dK^T += Q^T dS from registers, and dS^T goes to LDS.
 // After a barrier, wave w forms dQ^T = K^T dS^T for query tile w.
-template <int D, int SB>
+template <int D, int SB, bool MR = false>
 struct Sb2Smem {
   static constexpr int KT = SB < 32 ? 32 : SB;
   static constexpr int LD = tile_ld<__bf16>(D), LDK = tile_ld<__bf16>(KT);
@@ -506,9 +537,11 @@ struct Sb2Smem {
   __bf16 Os[KT][LD];    // dO (the row factor c is applied in registers)
   __bf16 Ks[KT][LD];
   __bf16 dST[KT][LDK];  // dS^T, [key][query]
+  // Several hash rounds: the rows' block indices in the earlier rounds' orders.
+  int qbe[MR ? kMaxRounds - 1 : 1][MR ? KT : 1], kbe[MR ? kMaxRounds - 1 : 1][MR ? KT : 1];
 };
 
-template <int D, int SB>
+template <int D, int SB, bool MR>
 __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
     sparse_bwd2_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                        const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
@@ -516,28 +549,32 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
                        const float* __restrict__ rD, const float* __restrict__ rsig,
                        const int32_t* __restrict__ qperm,
                        const int32_t* __restrict__ kperm, int N, int causal, int levels,
-                       float scale, int items, int total, __bf16* __restrict__ dQp,
-                       __bf16* __restrict__ dKp, __bf16* __restrict__ dVp) {
+                       int rounds, const int32_t* __restrict__ qbid,
+                       const int32_t* __restrict__ kbid, float scale, int items, int total,
+                       __bf16* __restrict__ dQp, __bf16* __restrict__ dKp,
+                       __bf16* __restrict__ dVp) {
   typedef __bf16 T;
   typedef MF<T> M;
-  typedef Sb2Smem<D, SB> Sm;
+  typedef Sb2Smem<D, SB, MR> Sm;
   constexpr int KT = Sm::KT, NW = KT / 32, NT = 64 * NW, LD = Sm::LD, LDK = Sm::LDK;
   constexpr int CH = D / 8, GIT = KT * CH / NT, KS = D / M::KSTEP;
   __shared__ Sm sm;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int w = wave_id();  // wave index, uniform (scalar) so that role branches stay uniform
   const int G = gridDim.x;
-  const size_t P = perm_stride(N, levels, causal);
-  const size_t slots = partial_slots(N, levels, causal);
+  const size_t P = perm_stride(N, levels, causal, rounds);
+  const size_t slots = partial_slots(N, levels, causal, rounds);
+  // Orders (round, level): causal rounds x levels, order-major items then the
+  // leaves; otherwise one order per round.
+  const int nord = causal ? rounds * levels : rounds;
   const int per_level = causal ? (N / 2) / SB : 0;
-  const int nlev = causal ? levels * per_level : 0;
+  const int nlev = causal ? nord * per_level : 0;
 
-  // Block g (in the XCD-aware order): head, level (-1 for a causal leaf or the
-  // non-causal level), rows. G is a multiple of 8, so a workgroup's blocks are
-  // all of its own XCD's share.
+  // Block g (in the XCD-aware order): head, order (-1 for a causal leaf), rows.
+  // G is a multiple of 8, so a workgroup's blocks are all of its own XCD's share.
   auto head_of = [&](int g) __attribute__((always_inline)) {
     int it;
-    return xcd_item(g, items, per_level, levels, it);
+    return xcd_item(g, items, per_level, nord, it);
   };
   // Rows of block g: row t's query and key tokens are (a, b) when alt < -1, else
   // both are alt (a causal leaf: the token itself; -1 past the block). The order
@@ -550,7 +587,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
   };
   auto rows_of = [&](int g, int t) __attribute__((always_inline)) {
     int it;
-    const int bh = xcd_item(g, items, per_level, levels, it);
+    const int bh = xcd_item(g, items, per_level, nord, it);
     const bool lf = causal && it >= nlev, past = t >= SB;
     const size_t off = (size_t)bh * P + (lf || past ? (size_t)0
                                          : causal ? (size_t)(it / per_level) * (N / 2) +
@@ -627,18 +664,39 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
       sm.cq[tid] = pvalid ? pc : 0.0f;
       sm.sig[tid] = pvalid ? psig : 0.0f;
     }
-    __syncthreads();
 
     int it;
-    const int bh = xcd_item(g, items, per_level, levels, it);
-    const int lev = causal ? (it < nlev ? it / per_level : -1) : -1;
+    const int bh = xcd_item(g, items, per_level, nord, it);
     const bool leaf = causal && it >= nlev;
+    // The block's order (-1: a leaf), its level (the segment geometry) and round.
+    const int ord = leaf ? -1 : causal ? it / per_level : it / (N / SB);
+    const int lev = causal && ord >= 0 ? ord % levels : 0;
+    const int rnd = ord < 0 ? 0 : causal ? ord / levels : ord;
+    // The query's own block (its causal leaf, or its first round's block) adds
+    // sigma_i Q_i to its dQ part.
+    const bool own = causal ? leaf : rnd == 0;
+    if constexpr (MR) {
+      // Several rounds: the rows' block indices in the earlier rounds' orders of
+      // the same level (a pair they share a block in is held there, not here).
+      if (rnd > 0 && tid < KT) {
+        const int rq = sm.qidx[tid], rk = sm.kidx[tid];
+        for (int r = 0; r < rnd; ++r) {
+          const size_t base = ((size_t)bh * nord + (causal ? r * levels + lev : r)) * N;
+          sm.qbe[r][tid] = rq >= 0 ? qbid[base + rq] : -1;
+          sm.kbe[r][tid] = rk >= 0 ? kbid[base + rk] : -2;
+        }
+      }
+    }
+    __syncthreads();
     // Phase 1: key wave w.
     const int key = 32 * w + col;
     floatx16 dv[D / 32], dk[D / 32];
     {
       const int jk = sm.kidx[key];
       const bool kvalid = jk >= 0;
+      int kbr[kMaxRounds - 1];
+#pragma unroll
+      for (int r = 0; r < kMaxRounds - 1; ++r) kbr[r] = MR && r < rnd ? sm.kbe[MR ? r : 0][key % KT] : -2;
       const float c2 = scale * kLog2e;  // P = 2^(c2 S - lse log2 e)
       typename M::frag kf[KS];
 #pragma unroll
@@ -674,7 +732,12 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
           for (int e = 0; e < 4; ++e) {
             const int v = 4 * gg + e;
             // Masked pairs get exp(-inf) = 0 (no branch around the exponential).
-            const bool ok = kvalid & !(leaf & (key > r0 + e));
+            bool ok = kvalid & !(leaf & (key > r0 + e));
+            if constexpr (MR) {
+#pragma unroll
+              for (int r = 0; r < kMaxRounds - 1; ++r)
+                ok = ok && !(r < rnd && sm.qbe[r][r0 + e] == kbr[r]);
+            }
             const float p = __builtin_amdgcn_exp2f(ok ? fmaf(s[v], c2, -L4[e]) : -INFINITY);
             dsv[e] = p * (C4[e] * dp[v] - D4[e]);
             s[v] = C4[e] * p;
@@ -759,7 +822,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
     }
     // (the query's own block, its leaf or its only block, adds the support-wide
     // sum back)
-    sig = sum_halves(sig) - (lev < 0 ? sm.sig[key] : 0.0f);
+    sig = sum_halves(sig) - (own ? sm.sig[key] : 0.0f);
     float qv[D / 32][4][4];
     qrow.unpack(qv);
     __syncthreads();  // Ks no longer read; dV, dK tiles complete
@@ -801,16 +864,17 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
           // Every row of a block of 32 or more is valid: the stores are then
           // issued on every path, which keeps the waits for the prefetches exact.
           if (SB >= 32 || jk[j] >= 0) {
-            const size_t sl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) +
-                                             compact_past(jk[j], N, lev)
-                                       : (size_t)jk[j];
+            const size_t sl = !causal ? (size_t)rnd * N + jk[j]
+                              : leaf  ? (size_t)jk[j]
+                                      : (size_t)N + (size_t)ord * (N / 2) + compact_past(jk[j], N, lev);
             a[j].store(dVp + (hb + sl) * D + c8[j]);
             b2[j].store(dKp + (hb + sl) * D + c8[j]);
           }
           if (SB >= 32 || iq[j] >= 0) {
-            const size_t sl = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) +
-                                             compact_future_b(iq[j], N, lev)
-                                       : (size_t)iq[j];
+            const size_t sl = !causal ? (size_t)rnd * N + iq[j]
+                              : leaf  ? (size_t)iq[j]
+                                      : (size_t)N + (size_t)ord * (N / 2) +
+                                            compact_future_b(iq[j], N, lev);
             c[j].store(dQp + (hb + sl) * D + c8[j]);
           }
         }
@@ -1347,13 +1411,13 @@ int rt_stride(const Problem& pb);
 
 // Workgroups of a persistent launch: as many as fit on the device at once.
 struct BwdLayout {
-  size_t rows, dlam, parts, gsum, gstate, rt, scratch, total;
+  size_t rows, dlam, parts, gsum, gstate, rt, scratch, bids, total;
   int nblk;
 };
 
 BwdLayout bwd_layout(const Problem& pb) {
   const size_t BH = (size_t)pb.B * pb.H, N = pb.N, D = pb.d;
-  const size_t slots = partial_slots(pb.N, pb.levels, pb.causal);
+  const size_t slots = partial_slots(pb.N, pb.levels, pb.causal, pb.rounds);
   const int rpb = 256 / (pb.d / 8);
   BwdLayout l;
   l.nblk = (pb.N + rpb - 1) / rpb;
@@ -1367,6 +1431,7 @@ BwdLayout bwd_layout(const Problem& pb) {
   l.rt = off; off += al(sizeof(float) * pb.H * D * rt_stride(pb));
   const int groups = padded_tables(pb.L) > 8 ? 2 : 1;
   l.scratch = off; off += groups > 1 ? al(sizeof(float) * 3 * BH * N * D) : 0;
+  l.bids = off; off += al(block_ids_bytes(pb));
   l.total = off;
   return l;
 }
@@ -1384,7 +1449,8 @@ size_t bwd_ws_bytes(const Problem& pb) { return bwd_layout(pb).total; }
 
 size_t bwd_lds_need(const Problem& pb) {
   const size_t e = pb.elem, d = pb.d, kt = pb.s < 32 ? 32 : pb.s;
-  const size_t sb = e * (2 * kt * (d + (pb.bf16 ? 24 : 8))) + 24 * kt;  // one-role launch
+  const size_t sb = e * (2 * kt * (d + (pb.bf16 ? 24 : 8))) + 24 * kt +  // one-role launch
+                    (pb.rounds > 1 ? 8 * (kMaxRounds - 1) * kt : 0);
   size_t lr = 0;
   with_T(pb.bf16, [&](auto tp) {
     using T = ELSAA_T(tp);
@@ -1429,7 +1495,7 @@ bool launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
   float* rdd = re + BH * N;
   float* rsig = rdd + BH * N;
   float* dlam_part = (float*)(base + lay.dlam);
-  const size_t slots = partial_slots(pb.N, pb.levels, pb.causal);
+  const size_t slots = partial_slots(pb.N, pb.levels, pb.causal, pb.rounds);
   char* parts = base + lay.parts;
   const size_t pbytes = BH * slots * pb.d * pb.elem;
   void* dQp = parts;
@@ -1446,7 +1512,11 @@ bool launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
   float* scrQ = scr;
   float* scrK = scr + BH * N * pb.d;
   float* scrV = scr + 2 * BH * N * pb.d;
-  const int items = pb.causal ? pb.levels * (pb.N / 2) / pb.s + pb.N / pb.s : pb.N / pb.s;
+  int32_t* qbid = (int32_t*)(base + lay.bids);
+  int32_t* kbid = qbid + block_ids_bytes(pb) / (2 * sizeof(int32_t));
+  const int nord = pb.causal ? pb.rounds * pb.levels : pb.rounds;
+  const int items = pb.causal ? nord * (pb.N / 2) / pb.s + pb.N / pb.s : nord * (pb.N / pb.s);
+  if (!dry && pb.rounds > 1) launch_block_ids(pb, qperm, kperm, qbid, kbid, st);
 
   with_T(pb.bf16, [&](auto tp) {
     using T = ELSAA_T(tp);
@@ -1467,42 +1537,47 @@ bool launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
       }
       auto run_sparse = [&](auto sc) {
         constexpr int SB = ELSAA_C(sc);
-        const dim3 grid(items, BH);
-        if constexpr (!(std::is_same_v<T, __bf16> && SB <= 128 &&
-                        sizeof(Sb2Smem<D, SB>) <= kLdsBytes) &&
-                      !(sizeof(SbwdSmem<T, D, SB, 3>) <= kLdsBytes && SB <= 128) &&
-                      !(sizeof(SbwdSmem<T, D, SB, 1>) <= kLdsBytes)) {
-          ok = false;
-        } else if (dry) {
-        } else if constexpr (std::is_same_v<T, __bf16> && SB <= 128 &&
-                             sizeof(Sb2Smem<D, SB>) <= kLdsBytes) {
-          constexpr int NT = 64 * (SB < 32 ? 1 : SB / 32);
-          const int total = items * (int)BH;
-          const int G = persistent_grid((const void*)sparse_bwd2_kernel<D, SB>, NT, total);
-          // The kernel reads an order entry for every row, leaves included; with no
+        auto go = [&](auto mc) {
+          constexpr bool MR = decltype(mc)::value;
+          const dim3 grid(items, BH);
+          // The kernels read an order entry for every row, leaves included; with no
           // level (causal, N = s) the orders are empty and may be null, and the
-          // entry it reads (and discards) is then the first row term.
+          // entry read (and discarded) is then the first row term.
           const int32_t* qp = qperm ? qperm : (const int32_t*)rc;
           const int32_t* kp = kperm ? kperm : (const int32_t*)rc;
-          ELSAA_LAUNCH("sparse_bwd", (sparse_bwd2_kernel<D, SB>), dim3(G), dim3(NT), 0, st,
-                       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, lse, rc, rD, rsig, qp, kp,
-                       pb.N, (int)pb.causal, pb.levels, pb.scale, items, total, (T*)dQp,
-                       (T*)dKp, (T*)dVp);
-        } else if constexpr (sizeof(SbwdSmem<T, D, SB, 3>) <= kLdsBytes && SB <= 128) {
-          ELSAA_LAUNCH("sparse_bwd", (sparse_bwd_kernel<T, D, SB, 3>), grid,
-                       dim3(sbwd_threads<SB>(3)), 0, st, (const T*)Q, (const T*)K, (const T*)V,
-                       (const T*)dO, lse, rc, rD, rsig, qperm, kperm, pb.N, (int)pb.causal, pb.levels,
-                       pb.scale, (T*)dQp, (T*)dKp, (T*)dVp);
-        } else if constexpr (sizeof(SbwdSmem<T, D, SB, 1>) <= kLdsBytes) {
-          ELSAA_LAUNCH("sparse_bwd", (sparse_bwd_kernel<T, D, SB, 1>), grid,
-                       dim3(sbwd_threads<SB>(1)), 0, st, (const T*)Q, (const T*)K, (const T*)V,
-                       (const T*)dO, lse, rc, rD, rsig, qperm, kperm, pb.N, (int)pb.causal, pb.levels,
-                       pb.scale, (T*)dQp, (T*)dKp, (T*)dVp);
-          ELSAA_LAUNCH("sparse_bwd_q", (sparse_bwd_kernel<T, D, SB, 2>), grid,
-                       dim3(sbwd_threads<SB>(2)), 0, st, (const T*)Q, (const T*)K, (const T*)V,
-                       (const T*)dO, lse, rc, rD, rsig, qperm, kperm, pb.N, (int)pb.causal, pb.levels,
-                       pb.scale, (T*)dQp, (T*)dKp, (T*)dVp);
-        }
+          if constexpr (!(std::is_same_v<T, __bf16> && SB <= 128 &&
+                          sizeof(Sb2Smem<D, SB, MR>) <= kLdsBytes) &&
+                        !(sizeof(SbwdSmem<T, D, SB, 3, MR>) <= kLdsBytes && SB <= 128) &&
+                        !(sizeof(SbwdSmem<T, D, SB, 1, MR>) <= kLdsBytes)) {
+            ok = false;
+          } else if (dry) {
+          } else if constexpr (std::is_same_v<T, __bf16> && SB <= 128 &&
+                               sizeof(Sb2Smem<D, SB, MR>) <= kLdsBytes) {
+            constexpr int NT = 64 * (SB < 32 ? 1 : SB / 32);
+            const int total = items * (int)BH;
+            const int G = persistent_grid((const void*)sparse_bwd2_kernel<D, SB, MR>, NT, total);
+            ELSAA_LAUNCH("sparse_bwd", (sparse_bwd2_kernel<D, SB, MR>), dim3(G), dim3(NT), 0, st,
+                         (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, lse, rc, rD, rsig, qp,
+                         kp, pb.N, (int)pb.causal, pb.levels, pb.rounds, qbid, kbid, pb.scale,
+                         items, total, (T*)dQp, (T*)dKp, (T*)dVp);
+          } else if constexpr (sizeof(SbwdSmem<T, D, SB, 3, MR>) <= kLdsBytes && SB <= 128) {
+            ELSAA_LAUNCH("sparse_bwd", (sparse_bwd_kernel<T, D, SB, 3, MR>), grid,
+                         dim3(sbwd_threads<SB>(3)), 0, st, (const T*)Q, (const T*)K, (const T*)V,
+                         (const T*)dO, lse, rc, rD, rsig, qp, kp, pb.N, (int)pb.causal, pb.levels,
+                         pb.rounds, qbid, kbid, pb.scale, (T*)dQp, (T*)dKp, (T*)dVp);
+          } else if constexpr (sizeof(SbwdSmem<T, D, SB, 1, MR>) <= kLdsBytes) {
+            ELSAA_LAUNCH("sparse_bwd", (sparse_bwd_kernel<T, D, SB, 1, MR>), grid,
+                         dim3(sbwd_threads<SB>(1)), 0, st, (const T*)Q, (const T*)K, (const T*)V,
+                         (const T*)dO, lse, rc, rD, rsig, qp, kp, pb.N, (int)pb.causal, pb.levels,
+                         pb.rounds, qbid, kbid, pb.scale, (T*)dQp, (T*)dKp, (T*)dVp);
+            ELSAA_LAUNCH("sparse_bwd_q", (sparse_bwd_kernel<T, D, SB, 2, MR>), grid,
+                         dim3(sbwd_threads<SB>(2)), 0, st, (const T*)Q, (const T*)K, (const T*)V,
+                         (const T*)dO, lse, rc, rD, rsig, qp, kp, pb.N, (int)pb.causal, pb.levels,
+                         pb.rounds, qbid, kbid, pb.scale, (T*)dQp, (T*)dKp, (T*)dVp);
+          }
+        };
+        if (pb.rounds > 1) go(std::true_type{});
+        else go(std::false_type{});
       };
       switch (pb.s) {
         case 16: run_sparse(std::integral_constant<int, 16>{}); break;

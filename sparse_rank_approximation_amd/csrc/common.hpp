@@ -495,24 +495,28 @@ struct DRow<float, NDT> {
 };
 
 // Partial-result slots of one token (see partial_slots): its own slot (the causal
-// leaf block, or the single non-causal block) and, causal, the slot of level l for
-// every level at which the token lies in a future half of a segment (QUERY) or in
-// a past half (!QUERY). next() hands them out in batches so that a batch of row
+// leaf block, or its first round's block) and then, causal, the slot of round r's
+// level l for every round and every level at which the token lies in a future
+// half of a segment (QUERY) or in a past half (!QUERY); non-causal, its block of
+// every further round. next() hands them out in batches so that a batch of row
 // loads can be in flight together.
 template <bool QUERY>
 struct SlotWalk {
-  int tok, N, levels, logN, l;
-  bool own;
-  __device__ __forceinline__ SlotWalk(int tok_, int N_, int levels_, bool causal)
-      : tok(tok_), N(N_), levels(causal ? levels_ : 0), logN(31 - __clz(N_)), l(0), own(true) {}
+  int tok, N, levels, total, logN, c;  // total: rounds x levels (causal), rounds - 1
+  bool own, causal;
+  __device__ __forceinline__ SlotWalk(int tok_, int N_, int levels_, bool causal_, int rounds = 1)
+      : tok(tok_), N(N_), levels(levels_),
+        total(causal_ ? rounds * levels_ : rounds - 1), logN(31 - __clz(N_)), c(0), own(true),
+        causal(causal_) {}
   __device__ __forceinline__ bool member(int lv) const {
     return (((tok >> (logN - 1 - lv)) & 1) != 0) == QUERY;
   }
   // (N is a power of two whenever there are levels: masks instead of divisions.)
-  __device__ __forceinline__ size_t slot(int lv) const {
+  __device__ __forceinline__ size_t slot(int cc, int lv) const {
+    if (!causal) return (size_t)(cc + 1) * N + tok;
     const int n = N >> lv;
-    const int c = ((tok & -n) >> 1) + (tok & (n - 1)) - (QUERY ? n >> 1 : 0);
-    return (size_t)N + (size_t)lv * (N / 2) + c;
+    const int s = ((tok & -n) >> 1) + (tok & (n - 1)) - (QUERY ? n >> 1 : 0);
+    return (size_t)N + (size_t)cc * (N / 2) + s;
   }
   // Fills sl[0 .. n) with the next n <= KB slots; returns n (0 when done).
   template <int KB>
@@ -523,9 +527,10 @@ struct SlotWalk {
       n = 1;
       own = false;
     }
-    for (; l < levels && n < KB; ++l) {
-      if (member(l)) {
-        const size_t x = slot(l);
+    for (; c < total && n < KB; ++c) {
+      const int lv = causal ? c % levels : 0;
+      if (!causal || member(lv)) {
+        const size_t x = slot(c, lv);
 #pragma unroll
         for (int j = 0; j < KB; ++j)
           if (j == n) sl[j] = x;

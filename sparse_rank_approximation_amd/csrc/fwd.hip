@@ -33,10 +33,11 @@ __device__ __forceinline__ int compact_future(int i, int N, int l) {
   return ((i & -n) >> 1) + (i & (n - 1)) - (n >> 1);
 }
 
-template <typename T, int D, int SB>
+template <typename T, int D, int SB, bool MR = false>
 constexpr size_t sparse_fwd_lds() {
   constexpr int KT = SB < 32 ? 32 : SB;
-  return sizeof(T) * 2 * (size_t)KT * tile_ld<T>(D) + sizeof(int) * 5 * KT;
+  return sizeof(T) * 2 * (size_t)KT * tile_ld<T>(D) +
+         sizeof(int) * (5 + (MR ? 2 * (kMaxRounds - 1) : 0)) * KT;
 }
 
 // Persistent workgroups take the selected blocks g, g + G, g + 2G, ... (G = grid
@@ -45,11 +46,14 @@ constexpr size_t sparse_fwd_lds() {
 // this block's rows and kept in LDS, so that a block's row gathers start at once.
 // bf16: two workgroups per CU (two waves per SIMD) is what the LDS allows; the
 // register budget is held to it.
-template <typename T, int D, int SB>
-__global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 ? 2 : 1)
+// MR: several hash rounds (the pair test against the earlier rounds' blocks and
+// its LDS are compiled only then).
+template <typename T, int D, int SB, bool MR>
+__global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 && !MR ? 2 : 1)
     sparse_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                       const int32_t* __restrict__ qperm, const int32_t* __restrict__ kperm, int N,
-                      int causal, int levels, float scale, int items, int total,
+                      int causal, int levels, int rounds, const int32_t* __restrict__ qbid,
+                      const int32_t* __restrict__ kbid, float scale, int items, int total,
                       T* __restrict__ Opart, float* __restrict__ Lpart) {
   typedef MF<T> M;
   constexpr int KT = SB < 32 ? 32 : SB;  // key rows held in LDS
@@ -59,13 +63,18 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 ?
   __shared__ T Vs[KT][LD];
   __shared__ int kix[2][KT], qix[2][KT];  // key / query token of each row, by block parity
   __shared__ int oslot[KT];               // output slot of each query row
+  // Block indices of the rows in the earlier rounds' orders (several rounds only).
+  __shared__ int qbe[MR ? kMaxRounds - 1 : 1][MR ? KT : 1], kbe[MR ? kMaxRounds - 1 : 1][MR ? KT : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int w = wave_id();  // wave index, uniform (scalar) so that role branches stay uniform
-  const size_t P = perm_stride(N, levels, causal);
-  const size_t slots = partial_slots(N, levels, causal);
+  const size_t P = perm_stride(N, levels, causal, rounds);
+  const size_t slots = partial_slots(N, levels, causal, rounds);
+  // Orders (round, level) of a head: causal, rounds x levels of N/2 entries each;
+  // otherwise one of N per round. Causal items are order-major, then the leaves.
+  const int nord = causal ? rounds * levels : rounds;
   const int per_level = causal ? (N / 2) / SB : 0;
-  const int nlev_items = causal ? levels * per_level : 0;
+  const int nlev_items = causal ? nord * per_level : 0;
   const int G = gridDim.x;
 
   // Order entries of row t of block g: both are read on every path (a leaf or a
@@ -76,7 +85,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 ?
   };
   auto row_idx = [&](int g, int t) __attribute__((always_inline)) {
     int it;
-    const int bh = xcd_item(g, items, per_level, levels, it);
+    const int bh = xcd_item(g, items, per_level, nord, it);
     const bool lf = causal && it >= nlev_items, past = t >= SB;
     const size_t off = (size_t)bh * P + (lf || past ? (size_t)0
                                          : causal ? (size_t)(it / per_level) * (N / 2) +
@@ -99,9 +108,12 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 ?
   const bool qvalid = qloc < SB;
   for (int par = 0; g < total; g += G, par ^= 1) {
     int item;
-    const int bh = xcd_item(g, items, per_level, levels, item);
+    const int bh = xcd_item(g, items, per_level, nord, item);
     const bool leaf = causal && item >= nlev_items;
-    const int lev = causal && !leaf ? item / per_level : -1;
+    // The block's order (-1: a leaf), its level (the segment geometry) and round.
+    const int ord = leaf ? -1 : causal ? item / per_level : item / (N / SB);
+    const int lev = causal && ord >= 0 ? ord % levels : 0;
+    const int rnd = ord < 0 ? 0 : causal ? ord / levels : ord;
     // The next block's order entries, then this block's query rows as MFMA
     // operands (queries past the block read row 0, unused) and its K and V rows
     // gathered into LDS (row-major, 16-byte row-contiguous copies; rows past the
@@ -110,6 +122,18 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 ?
     const int qi = qvalid ? qix[par][qloc] : 0;
     typename M::frag qf[D / M::KSTEP];
     prefetch_row_frags<T, D>(Q + ((size_t)bh * N + qi) * D, qf, h);
+    // Several rounds: the rows' block indices in the earlier rounds' orders of the
+    // same level (a pair they share a block in is held there, not here).
+    if constexpr (MR) {
+      if (rnd > 0 && tid < KT) {
+        const int rq = qix[par][tid], rk = kix[par][tid];
+        for (int r = 0; r < rnd; ++r) {
+          const size_t base = ((size_t)bh * nord + (causal ? r * levels + lev : r)) * N;
+          qbe[r][tid] = rq >= 0 ? qbid[base + rq] : -1;
+          kbe[r][tid] = rk >= 0 ? kbid[base + rk] : -2;
+        }
+      }
+    }
     {
       T* const dst[2] = {&Ks[0][0], &Vs[0][0]};
       const T* const src[2] = {K, V};
@@ -118,6 +142,9 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 ?
     }
     __syncthreads();
     put_idx(par ^ 1, nx);
+    int qbr[kMaxRounds - 1];
+#pragma unroll
+    for (int r = 0; r < kMaxRounds - 1; ++r) qbr[r] = MR && r < rnd ? qbe[MR ? r : 0][qloc % KT] : -1;
 
     floatx16 o[D / 32];
 #pragma unroll
@@ -138,7 +165,12 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 ?
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int kr = 32 * kt + acc_row(v, h);
-        const bool masked = kr >= SB || (leaf && kr > qloc);
+        bool masked = kr >= SB || (leaf && kr > qloc);
+        if constexpr (MR) {
+#pragma unroll
+          for (int r = 0; r < kMaxRounds - 1; ++r)
+            masked = masked || (r < rnd && qbr[r] == kbe[r][kr % KT]);
+        }
         sacc[v] = masked ? -INFINITY : sacc[v] * c2;
         mx = fmaxf(mx, sacc[v]);
       }
@@ -184,11 +216,14 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 ?
     // The normalized output tile goes to LDS as rows (one per query, over the key
     // tile once every wave is done with it) and leaves with row-contiguous 16-byte
     // stores to the queries' slots.
-    const size_t slot = lev >= 0 ? (size_t)N + (size_t)lev * (N / 2) + compact_future(qi, N, lev)
-                                 : (size_t)qi;
+    const size_t slot = !causal  ? (size_t)rnd * N + qi
+                        : leaf ? (size_t)qi
+                               : (size_t)N + (size_t)ord * (N / 2) + compact_future(qi, N, lev);
     __syncthreads();
     {
-      const float inv = 1.0f / lrun;
+      // (several rounds: every key of the block may already be held by an earlier
+      // round; the partial is then empty, weight 0)
+      const float inv = lrun > 0.0f ? 1.0f / lrun : 0.0f;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -200,7 +235,8 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 ?
         }
       if (h == 0) oslot[qloc] = qvalid ? (int)slot : -1;
     }
-    if (qvalid && h == 0) Lpart[(size_t)bh * slots + slot] = (mrun + __log2f(lrun)) * kLn2;
+    if (qvalid && h == 0)
+      Lpart[(size_t)bh * slots + slot] = lrun > 0.0f ? (mrun + __log2f(lrun)) * kLn2 : -INFINITY;
     __syncthreads();
     {
       // All of the thread's LDS reads are issued before its stores (one wait);
@@ -457,8 +493,9 @@ __global__ void __launch_bounds__(512)
 }
 
 size_t fwd_ws_bytes(const Problem& pb) {
-  const size_t slots = partial_slots(pb.N, pb.levels, pb.causal);
-  return (size_t)pb.B * pb.H * slots * ((size_t)pb.d * pb.elem + sizeof(float)) + 256;
+  const size_t slots = partial_slots(pb.N, pb.levels, pb.causal, pb.rounds);
+  return (size_t)pb.B * pb.H * slots * ((size_t)pb.d * pb.elem + sizeof(float)) + 512 +
+         block_ids_bytes(pb);
 }
 
 // The epilogue keeps the RACE hyperplanes in LDS unless that would cut its step
@@ -491,7 +528,8 @@ size_t fwd_lds_need(const Problem& pb) {
     });
   });
   const size_t kt = pb.s < 32 ? 32 : pb.s;
-  const size_t sparse = (size_t)pb.elem * 2 * kt * (pb.d + (pb.bf16 ? 24 : 8)) + 4 * 5 * kt;
+  const size_t sparse = (size_t)pb.elem * 2 * kt * (pb.d + (pb.bf16 ? 24 : 8)) +
+                        4 * (5 + (pb.rounds > 1 ? 2 * (kMaxRounds - 1) : 0)) * kt;
   return need > sparse ? need : sparse;
 }
 
@@ -502,31 +540,43 @@ bool launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
                 void* ws, hipStream_t st, bool dry) {
   bool ok = true;
   const int BH = pb.B * pb.H;
-  const size_t slots = partial_slots(pb.N, pb.levels, pb.causal);
+  const size_t slots = partial_slots(pb.N, pb.levels, pb.causal, pb.rounds);
   float* Lpart = (float*)ws;
-  void* Opart = (char*)ws + (((size_t)BH * slots * sizeof(float) + 255) & ~(size_t)255);
-  const int items = pb.causal ? pb.levels * (pb.N / 2) / pb.s + pb.N / pb.s : pb.N / pb.s;
+  const size_t lbytes = ((size_t)BH * slots * sizeof(float) + 255) & ~(size_t)255;
+  void* Opart = (char*)ws + lbytes;
+  const size_t obytes = ((size_t)BH * slots * pb.d * pb.elem + 255) & ~(size_t)255;
+  int32_t* qbid = (int32_t*)((char*)ws + lbytes + obytes);
+  int32_t* kbid = qbid + block_ids_bytes(pb) / (2 * sizeof(int32_t));
+  const int nord = pb.causal ? pb.rounds * pb.levels : pb.rounds;
+  const int items = pb.causal ? nord * (pb.N / 2) / pb.s + pb.N / pb.s : nord * (pb.N / pb.s);
+  if (!dry && pb.rounds > 1) launch_block_ids(pb, qperm, kperm, qbid, kbid, st);
   with_T(pb.bf16, [&](auto tp) {
     using T = ELSAA_T(tp);
     with_D(pb.d, [&](auto dc) {
       constexpr int D = ELSAA_C(dc);
       auto run = [&](auto sc) {
         constexpr int SB = ELSAA_C(sc);
-        if constexpr (sparse_fwd_lds<T, D, SB>() > kLdsBytes) {
-          ok = false;
-        } else if (!dry) {
-          constexpr int NT = 64 * (SB < 32 ? 1 : SB / 32);
-          const int total = items * BH;
-          const int G = persistent_grid((const void*)sparse_fwd_kernel<T, D, SB>, NT, total);
-          // The kernel reads an order entry for every row, leaves included; with no
-          // level (causal, N = s) the orders are empty and may be null, and the
-          // entry it reads (and discards) is then the first word of the workspace.
-          const int32_t* qp = qperm ? qperm : (const int32_t*)Lpart;
-          const int32_t* kp = kperm ? kperm : (const int32_t*)Lpart;
-          ELSAA_LAUNCH("sparse_fwd", (sparse_fwd_kernel<T, D, SB>), dim3(G), dim3(NT), 0, st,
-                       (const T*)Q, (const T*)K, (const T*)V, qp, kp, pb.N, (int)pb.causal,
-                       pb.levels, pb.scale, items, total, (T*)Opart, Lpart);
-        }
+        auto go = [&](auto mc) {
+          constexpr bool MR = decltype(mc)::value;
+          if constexpr (sparse_fwd_lds<T, D, SB, MR>() > kLdsBytes) {
+            ok = false;
+          } else if (!dry) {
+            constexpr int NT = 64 * (SB < 32 ? 1 : SB / 32);
+            const int total = items * BH;
+            const int G = persistent_grid((const void*)sparse_fwd_kernel<T, D, SB, MR>, NT, total);
+            // The kernel reads an order entry for every row, leaves included; with no
+            // level (causal, N = s) the orders are empty and may be null, and the
+            // entry it reads (and discards) is then the first word of the workspace.
+            const int32_t* qp = qperm ? qperm : (const int32_t*)Lpart;
+            const int32_t* kp = kperm ? kperm : (const int32_t*)Lpart;
+            ELSAA_LAUNCH("sparse_fwd", (sparse_fwd_kernel<T, D, SB, MR>), dim3(G), dim3(NT), 0, st,
+                         (const T*)Q, (const T*)K, (const T*)V, qp, kp, pb.N, (int)pb.causal,
+                         pb.levels, pb.rounds, qbid, kbid, pb.scale, items, total, (T*)Opart,
+                         Lpart);
+          }
+        };
+        if (pb.rounds > 1) go(std::true_type{});
+        else go(std::false_type{});
       };
       switch (pb.s) {
         case 16: run(std::integral_constant<int, 16>{}); break;

@@ -19,6 +19,7 @@ constexpr int kLrBits = 4;
 constexpr size_t kLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
 
 constexpr int kMaxLevels = 20;           // log2(N / s) for N <= 2^24, s >= 16
+constexpr int kMaxRounds = 4;            // sortLSH hash rounds (tables)
 
 // LDS of the kernels that walk a span of tokens in steps of STEP tokens: one
 // step's row-major channel tile (V, or the low-rank output gradient dnum), its
@@ -57,19 +58,22 @@ struct Problem {
   int chunk;      // causal RACE summary spacing (N when not causal)
   float tau, eps, scale;
   int levels;     // off-diagonal recursion levels (causal), 1 otherwise
+  int rounds;     // sortLSH hash rounds (the support is the union of theirs)
   int nA;         // summaries per head
   int elem;       // bytes per element of Q/K/V/...
 };
 
-// Entries of q_perm / k_perm per head.
-__host__ __device__ inline size_t perm_stride(int N, int levels, bool causal) {
-  return causal ? (size_t)levels * (N / 2) : (size_t)N;
+// Entries of q_perm / k_perm per head: for every round its orders (causal: one
+// per level, N/2 each; otherwise one of N), round-major.
+__host__ __device__ inline size_t perm_stride(int N, int levels, bool causal, int rounds = 1) {
+  return (size_t)rounds * (causal ? (size_t)levels * (N / 2) : (size_t)N);
 }
 
-// Slots of the sparse partial results of one head: [0, N) leaf blocks (causal)
-// or the single sorted level (non-causal), then level l at N + l N/2 (causal).
-__host__ __device__ inline size_t partial_slots(int N, int levels, bool causal) {
-  return causal ? (size_t)N + (size_t)levels * (N / 2) : (size_t)N;
+// Slots of the sparse partial results of one head. Causal: [0, N) the leaf
+// blocks, then round r's level l at N + (r levels + l) N/2. Otherwise round r's
+// block of each token at r N + token.
+__host__ __device__ inline size_t partial_slots(int N, int levels, bool causal, int rounds = 1) {
+  return causal ? (size_t)N + (size_t)rounds * levels * (N / 2) : (size_t)rounds * N;
 }
 
 // Sparse work items of one head: causal, `levels` off-diagonal levels of
@@ -165,6 +169,12 @@ void prof_suspend(bool on);
   } while (0)
 
 size_t select_ws_bytes(const Problem& pb);
+// Per-token block indices of every (round, level) order (select.hip), used by the
+// sparse kernels to count each pair once over several hash rounds; bytes of the
+// two arrays (0 with one round).
+size_t block_ids_bytes(const Problem& pb);
+void launch_block_ids(const Problem& pb, const int32_t* qperm, const int32_t* kperm, int32_t* qb,
+                      int32_t* kb, hipStream_t st);
 // The allocation-free selection's fixed scratch (select.hip): its size, and its
 // device address on the current device (looked up once per device).
 size_t noalloc_scratch_bytes();

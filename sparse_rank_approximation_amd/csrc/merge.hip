@@ -1,4 +1,5 @@
-// merge.hip -- per-token reductions over the sparse branch's partial slots, as
+// merge.hip -- per-token reductions over the sparse branch's partial slots (every
+// level and every hash round of a token), as
 // streaming kernels (each lane owns a 16-byte piece of a row, D / 8 lanes per row,
 // and every slot of a batch is loaded before any is used):
 //   merge_kernel    forward: the log-sum-exp merge of a query's partial block
@@ -18,15 +19,15 @@ constexpr int kMergeBatch = 8;  // slots in flight per lane
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
     merge_kernel(const T* __restrict__ Opart, const float* __restrict__ Lpart, int N, int levels,
-                 int causal, float* __restrict__ Os, float* __restrict__ lse) {
+                 int causal, int rounds, float* __restrict__ Os, float* __restrict__ lse) {
   constexpr int LPR = D / 8, RPB = 256 / LPR, MB = kMergeBatch;
   const int bh = blockIdx.y, tid = threadIdx.x;
   const int tok = blockIdx.x * RPB + tid / LPR, c8 = (tid % LPR) * 8;
   const bool valid = tok < N;
-  const size_t slots = partial_slots(N, levels, causal);
+  const size_t slots = partial_slots(N, levels, causal, rounds);
   const T* Op = Opart + (size_t)bh * slots * D + c8;
   const float* Lp = Lpart + (size_t)bh * slots;
-  SlotWalk<true> sw(valid ? tok : 0, N, levels, causal != 0);
+  SlotWalk<true> sw(valid ? tok : 0, N, levels, causal != 0, rounds);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float mrun = -INFINITY, lrun = 0.0f;
   for (;;) {
@@ -74,19 +75,19 @@ __global__ void __launch_bounds__(256)
 template <typename T, int D, bool QUERY, int NX>
 __global__ void __launch_bounds__(256)
     combine_kernel(const T* __restrict__ p0, const T* __restrict__ p1, T* __restrict__ o0,
-                   T* __restrict__ o1, int N, int levels, int causal) {
+                   T* __restrict__ o1, int N, int levels, int causal, int rounds) {
   constexpr int LPR = D / 8, RPB = 256 / LPR, MB = kMergeBatch;
   const int bh = blockIdx.y, tid = threadIdx.x;
   const int tok = blockIdx.x * RPB + tid / LPR, c8 = (tid % LPR) * 8;
   const bool valid = tok < N;
-  const size_t slots = partial_slots(N, levels, causal);
+  const size_t slots = partial_slots(N, levels, causal, rounds);
   const T* const part[2] = {p0 + (size_t)bh * slots * D + c8, p1 ? p1 + (size_t)bh * slots * D + c8 : nullptr};
   T* const out[2] = {o0, o1};
   const size_t row = ((size_t)bh * N + (valid ? tok : 0)) * D + c8;
   float acc[NX][8];
 #pragma unroll
   for (int x = 0; x < NX; ++x) load8(out[x] + row, acc[x]);
-  SlotWalk<QUERY> sw(valid ? tok : 0, N, levels, causal != 0);
+  SlotWalk<QUERY> sw(valid ? tok : 0, N, levels, causal != 0, rounds);
   for (;;) {
     size_t sl[MB];
     const int n = valid ? sw.template next<MB>(sl) : 0;
@@ -121,7 +122,7 @@ void launch_merge(const Problem& pb, const void* Opart, const float* Lpart, floa
       constexpr int D = ELSAA_C(dc);
       constexpr int RPB = 256 / (D / 8);
       ELSAA_LAUNCH("merge", (merge_kernel<T, D>), dim3((pb.N + RPB - 1) / RPB, BH), dim3(256), 0,
-                   st, (const T*)Opart, Lpart, pb.N, pb.levels, (int)pb.causal, O_s, lse);
+                   st, (const T*)Opart, Lpart, pb.N, pb.levels, (int)pb.causal, pb.rounds, O_s, lse);
     });
   });
 }
@@ -137,10 +138,10 @@ void launch_combine(const Problem& pb, const void* dQp, const void* dKp, const v
       const dim3 grid((pb.N + RPB - 1) / RPB, BH);
       ELSAA_LAUNCH("combine_q", (combine_kernel<T, D, true, 1>), grid, dim3(256), 0, st,
                    (const T*)dQp, (const T*)nullptr, (T*)dQ, (T*)nullptr, pb.N, pb.levels,
-                   (int)pb.causal);
+                   (int)pb.causal, pb.rounds);
       ELSAA_LAUNCH("combine_kv", (combine_kernel<T, D, false, 2>), grid, dim3(256), 0, st,
                    (const T*)dKp, (const T*)dVp, (T*)dK, (T*)dV, pb.N, pb.levels,
-                   (int)pb.causal);
+                   (int)pb.causal, pb.rounds);
     });
   });
 }

@@ -1,6 +1,7 @@
 // select.hip -- sortLSH selection: hash codes and sorted orders (ELSAA paper,
 // Section 3.2: queries and keys are hashed, sorted by hash and cut into
 // equal-size blocks; causally, per level of the past/future divide-and-conquer).
+#include <algorithm>
 #include <mutex>
 
 #include "common.hpp"
@@ -76,16 +77,20 @@ template <typename T, int D, int BITS>
 __global__ void __launch_bounds__(256) hash_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                    const double* __restrict__ planes,
                                                    uint16_t* __restrict__ qc,
-                                                   uint16_t* __restrict__ kc, int H, int N) {
+                                                   uint16_t* __restrict__ kc, int H, int N,
+                                                   int rounds) {
   constexpr int ROWS = 128, CH = D * (int)sizeof(T) / 16;
   constexpr int RW = D * (int)sizeof(T) / 4 + 4;  // row stride in dwords
   constexpr int IT = ROWS * CH / 256, B0 = (BITS + 1) / 2;
   __shared__ uint4 xs[ROWS * RW / 4];
   __shared__ unsigned hib[ROWS];
+  // blockIdx.z = 2 round + (0: queries, 1: keys); round r hashes with its own
+  // hyperplanes into its own codes.
   const int bh = blockIdx.y, h = bh % H, tid = threadIdx.x;
+  const int isk = blockIdx.z & 1, r = blockIdx.z >> 1;
   const int tok0 = blockIdx.x * ROWS;
-  const T* X = (blockIdx.z ? K : Q) + (size_t)bh * N * D;
-  const double* pl = planes + (size_t)h * BITS * D;
+  const T* X = (isk ? K : Q) + (size_t)bh * N * D;
+  const double* pl = planes + ((size_t)h * rounds + r) * BITS * D;
   {
     uint4 buf[IT];
 #pragma unroll
@@ -107,7 +112,8 @@ __global__ void __launch_bounds__(256) hash_kernel(const T* __restrict__ Q, cons
   const unsigned lo = tid < ROWS ? hash_bits<T, D, 0, B0>(xr, pl) : 0u;
   __syncthreads();
   const int t = tok0 + row;
-  if (tid < ROWS && t < N) (blockIdx.z ? kc : qc)[(size_t)bh * N + t] = (uint16_t)(lo | hib[row]);
+  if (tid < ROWS && t < N)
+    (isk ? kc : qc)[((size_t)bh * rounds + r) * N + t] = (uint16_t)(lo | hib[row]);
 }
 
 // Stable counting sort of one segment half by Gray rank (ties by token index).
@@ -124,7 +130,7 @@ __global__ void __launch_bounds__(256) sort_kernel(const uint16_t* __restrict__ 
                                                    const uint16_t* __restrict__ kc,
                                                    int32_t* __restrict__ qperm,
                                                    int32_t* __restrict__ kperm, int N, int causal,
-                                                   int levels, int bits) {
+                                                   int levels, int bits, int rounds) {
   extern __shared__ int smem[];
   const int nbins = 1 << bits;
   int* cnt = smem;                               // [kSortWaves][nbins]
@@ -133,7 +139,7 @@ __global__ void __launch_bounds__(256) sort_kernel(const uint16_t* __restrict__ 
   // the wave totals) with 16-byte loads all in flight, and both passes read them
   // there.
   uint16_t* cs = reinterpret_cast<uint16_t*>(part + 256);
-  const int bh = blockIdx.y, isk = blockIdx.z;
+  const int bh = blockIdx.y, isk = blockIdx.z & 1, rd = blockIdx.z >> 1;  // z = 2 round + isk
   int base, count;
   size_t out_off;
   if (causal) {
@@ -149,8 +155,9 @@ __global__ void __launch_bounds__(256) sort_kernel(const uint16_t* __restrict__ 
     count = N;
     out_off = 0;
   }
-  const uint16_t* code = (isk ? kc : qc) + (size_t)bh * N;
-  int32_t* out = (isk ? kperm : qperm) + (size_t)bh * perm_stride(N, levels, causal) + out_off;
+  const uint16_t* code = (isk ? kc : qc) + ((size_t)bh * rounds + rd) * N;
+  int32_t* out = (isk ? kperm : qperm) + (size_t)bh * perm_stride(N, levels, causal, rounds) +
+                 (size_t)rd * perm_stride(N, levels, causal) + out_off;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   for (int i = tid; i < kSortWaves * nbins; i += blockDim.x) cnt[i] = 0;
@@ -245,7 +252,48 @@ hipError_t noalloc_scratch(void** out) {
 }
 
 size_t select_ws_bytes(const Problem& pb) {
-  return (sizeof(double) * pb.H * pb.hash_bits * pb.d + 255) & ~(size_t)255;
+  return (sizeof(double) * pb.H * pb.rounds * pb.hash_bits * pb.d + 255) & ~(size_t)255;
+}
+
+// Block index of every token in every (round, level) order of a head, as a query
+// (qb) and as a key (kb): entry t of order c = r levels + l lies in block
+// (t mod half) / s of its segment's half (half = N >> (l + 1) causal, N when not);
+// entries of tokens absent from an order (the other half, causal) are not written
+// and not read. [B H][rounds levels][N]. The sparse kernels compare these to take
+// a pair that an earlier round already holds out of a later round's block.
+__global__ void __launch_bounds__(256)
+    block_ids_kernel(const int32_t* __restrict__ qperm, const int32_t* __restrict__ kperm, int N,
+                     int levels, int causal, int rounds, int s, int32_t* __restrict__ qb,
+                     int32_t* __restrict__ kb) {
+  const int bh = blockIdx.y;
+  const int len = causal ? N / 2 : N;
+  const int nord = causal ? rounds * levels : rounds;
+  const size_t P = perm_stride(N, levels, causal, rounds);
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < (size_t)nord * len;
+       e += (size_t)gridDim.x * 256) {
+    const int c = (int)(e / len), t = (int)(e % len);
+    const int half = causal ? (N >> ((c % levels) + 1)) : N;
+    const int b = (t % half) / s;
+    const size_t base = ((size_t)bh * nord + c) * N;
+    qb[base + qperm[(size_t)bh * P + e]] = b;
+    kb[base + kperm[(size_t)bh * P + e]] = b;
+  }
+}
+
+size_t block_ids_bytes(const Problem& pb) {
+  if (pb.rounds <= 1) return 0;
+  const size_t nord = pb.causal ? (size_t)pb.rounds * pb.levels : (size_t)pb.rounds;
+  return 2 * sizeof(int32_t) * (size_t)pb.B * pb.H * nord * pb.N;
+}
+
+void launch_block_ids(const Problem& pb, const int32_t* qperm, const int32_t* kperm, int32_t* qb,
+                      int32_t* kb, hipStream_t st) {
+  const size_t nord = pb.causal ? (size_t)pb.rounds * pb.levels : (size_t)pb.rounds;
+  const size_t n = nord * (pb.causal ? pb.N / 2 : pb.N);
+  if (n == 0 || pb.B * pb.H == 0) return;  // (no level: the leaves need no block index)
+  const int gx = (int)std::min<size_t>((n + 255) / 256, 1024);
+  ELSAA_LAUNCH("block_ids", block_ids_kernel, dim3(gx, pb.B * pb.H), dim3(256), 0, st, qperm,
+               kperm, pb.N, pb.levels, (int)pb.causal, pb.rounds, pb.s, qb, kb);
 }
 
 void launch_select(const Problem& pb, const void* Q, const void* K, const float* planes_s,
@@ -253,10 +301,10 @@ void launch_select(const Problem& pb, const void* Q, const void* K, const float*
                    hipStream_t st) {
   const int BH = pb.B * pb.H;
   double* pld = (double*)ws;
-  const int np = pb.H * pb.hash_bits * pb.d;
+  const int np = pb.H * pb.rounds * pb.hash_bits * pb.d;
   ELSAA_LAUNCH("planes_f64", planes_f64_kernel, dim3((np + 255) / 256), dim3(256), 0, st, planes_s,
                np, pld);
-  const dim3 hg((pb.N + 127) / 128, BH, 2);
+  const dim3 hg((pb.N + 127) / 128, BH, 2 * pb.rounds);
   with_T(pb.bf16, [&](auto tp) {
     using T = ELSAA_T(tp);
     with_D(pb.d, [&](auto dc) {
@@ -264,7 +312,7 @@ void launch_select(const Problem& pb, const void* Q, const void* K, const float*
       auto run = [&](auto bc) {
         constexpr int BITS = ELSAA_C(bc);
         ELSAA_LAUNCH("hash", (hash_kernel<T, D, BITS>), hg, dim3(256), 0, st, (const T*)Q,
-                     (const T*)K, (const double*)pld, qc, kc, pb.H, pb.N);
+                     (const T*)K, (const double*)pld, qc, kc, pb.H, pb.N, pb.rounds);
       };
       switch (pb.hash_bits) {
         case 1: run(std::integral_constant<int, 1>{}); break;
@@ -287,11 +335,13 @@ void launch_select(const Problem& pb, const void* Q, const void* K, const float*
   const size_t seg_codes = sizeof(uint16_t) * (size_t)(pb.causal ? pb.N / 2 : pb.N);
   if (nseg > 0) {
     if (lds + seg_codes <= 64 * 1024)
-      ELSAA_LAUNCH("sort", sort_kernel<true>, dim3(nseg, BH, 2), dim3(256), lds + seg_codes, st, qc,
-                   kc, qperm, kperm, pb.N, (int)pb.causal, pb.levels, pb.hash_bits);
+      ELSAA_LAUNCH("sort", sort_kernel<true>, dim3(nseg, BH, 2 * pb.rounds), dim3(256),
+                   lds + seg_codes, st, qc, kc, qperm, kperm, pb.N, (int)pb.causal, pb.levels,
+                   pb.hash_bits, pb.rounds);
     else
-      ELSAA_LAUNCH("sort", sort_kernel<false>, dim3(nseg, BH, 2), dim3(256), lds, st, qc, kc, qperm,
-                   kperm, pb.N, (int)pb.causal, pb.levels, pb.hash_bits);
+      ELSAA_LAUNCH("sort", sort_kernel<false>, dim3(nseg, BH, 2 * pb.rounds), dim3(256), lds, st,
+                   qc, kc, qperm, kperm, pb.N, (int)pb.causal, pb.levels, pb.hash_bits,
+                   pb.rounds);
   }
 }
 

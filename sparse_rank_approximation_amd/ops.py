@@ -32,6 +32,7 @@ class ElsaaConfig:
     tau: float = 1.0
     eps: float = 1e-6
     scale: float | None = None
+    hash_rounds: int = 1      # sortLSH hash tables (support = union over the rounds)
 
     @property
     def bits(self) -> int:
@@ -48,8 +49,26 @@ class ElsaaConfig:
         return int(round(math.log2(self.N // self.block))) if self.causal else 1
 
     @property
+    def rounds(self) -> int:
+        return max(1, self.hash_rounds)
+
+    @property
     def perm_len(self) -> int:
-        return self.levels * (self.N // 2) if self.causal else self.N
+        return self.rounds * (self.levels * (self.N // 2) if self.causal else self.N)
+
+    @property
+    def planes_s_shape(self) -> tuple:
+        """[H, bits, d] with one round, [H, R, bits, d] with several."""
+        if self.rounds == 1:
+            return (self.H, self.bits, self.d)
+        return (self.H, self.rounds, self.bits, self.d)
+
+    @property
+    def code_shape(self) -> tuple:
+        """[B, H, N] with one round, [B, H, R, N] with several."""
+        if self.rounds == 1:
+            return (self.B, self.H, self.N)
+        return (self.B, self.H, self.rounds, self.N)
 
     @property
     def n_summaries(self) -> int:
@@ -69,7 +88,7 @@ class ElsaaConfig:
         return _lib.Params(self.B, self.H, self.N, self.d,
                            _lib.BF16 if self.dtype == torch.bfloat16 else _lib.F32,
                            int(self.causal), self.block, self.bits, self.lr_tables, self.lr_bits,
-                           self.eff_chunk, self.tau, self.eps, sc)
+                           self.eff_chunk, self.tau, self.eps, sc, self.rounds)
 
 
 def _ptr(t):
@@ -109,13 +128,14 @@ def _workspace(cfg: ElsaaConfig, call: int, device) -> tuple[torch.Tensor | None
 
 
 def select(cfg: ElsaaConfig, q, k, planes_s):
-    """elsaa_select: codes [B,H,N] uint16 (as int16 storage) and perms [B,H,P] int32."""
+    """elsaa_select: codes [B,H,N] ([B,H,R,N] with R > 1 hash rounds) uint16 (as int16
+    storage) and perms [B,H,P] int32."""
     dev = q.device
     x = (cfg.B, cfg.H, cfg.N, cfg.d)
     _check_tensor("q", q, x, cfg.dtype, dev)
     _check_tensor("k", k, x, cfg.dtype, dev)
-    _check_tensor("planes_s", planes_s, (cfg.H, cfg.bits, cfg.d), torch.float32, dev)
-    qc = torch.empty(cfg.B, cfg.H, cfg.N, dtype=torch.int16, device=dev)
+    _check_tensor("planes_s", planes_s, cfg.planes_s_shape, torch.float32, dev)
+    qc = torch.empty(cfg.code_shape, dtype=torch.int16, device=dev)
     kc = torch.empty_like(qc)
     qp = torch.empty(cfg.B, cfg.H, cfg.perm_len, dtype=torch.int32, device=dev)
     kp = torch.empty_like(qp)
@@ -136,14 +156,14 @@ def select_noalloc(cfg: ElsaaConfig, q, k, planes_s, out=None):
     x = (cfg.B, cfg.H, cfg.N, cfg.d)
     _check_tensor("q", q, x, cfg.dtype, dev)
     _check_tensor("k", k, x, cfg.dtype, dev)
-    _check_tensor("planes_s", planes_s, (cfg.H, cfg.bits, cfg.d), torch.float32, dev)
+    _check_tensor("planes_s", planes_s, cfg.planes_s_shape, torch.float32, dev)
     if out is None:
-        qc = torch.empty(cfg.B, cfg.H, cfg.N, dtype=torch.int16, device=dev)
+        qc = torch.empty(cfg.code_shape, dtype=torch.int16, device=dev)
         qp = torch.empty(cfg.B, cfg.H, cfg.perm_len, dtype=torch.int32, device=dev)
         out = (qc, torch.empty_like(qc), qp, torch.empty_like(qp))
     qc, kc, qp, kp = out
-    for name, t, shp, dt in (("q_code", qc, (cfg.B, cfg.H, cfg.N), torch.int16),
-                             ("k_code", kc, (cfg.B, cfg.H, cfg.N), torch.int16),
+    for name, t, shp, dt in (("q_code", qc, cfg.code_shape, torch.int16),
+                             ("k_code", kc, cfg.code_shape, torch.int16),
                              ("q_perm", qp, (cfg.B, cfg.H, cfg.perm_len), torch.int32),
                              ("k_perm", kp, (cfg.B, cfg.H, cfg.perm_len), torch.int32)):
         _check_tensor(name, t, shp, dt, dev)
@@ -325,7 +345,7 @@ class ElsaaFunction(torch.autograd.Function):
 def make_planes(cfg: ElsaaConfig, seed: int = 0, device="cuda"):
     """iid N(0,1) sortLSH and RACE hyperplanes for every head (fixed, no gradient)."""
     g = torch.Generator().manual_seed(seed)
-    ps = torch.randn(cfg.H, cfg.bits, cfg.d, generator=g)
+    ps = torch.randn(*cfg.planes_s_shape, generator=g)
     pl = torch.randn(cfg.H, cfg.lr_tables, cfg.lr_bits, cfg.d, generator=g)
     return ps.to(device), pl.to(device)
 
@@ -333,12 +353,13 @@ def make_planes(cfg: ElsaaConfig, seed: int = 0, device="cuda"):
 def elsaa_attention(q, k, v, *, causal: bool, block: int, lr_tables: int, lam=None, g_s=None,
                     g_lr=None, planes_s=None, planes_lr=None, seed: int = 0, chunk: int = 2048,
                     hash_bits: int | None = None, tau: float = 1.0, eps: float = 1e-6,
-                    gate_w=None, gate_b=None):
+                    gate_w=None, gate_b=None, hash_rounds: int = 1):
     """ELSAA attention of q, k, v [B, H, N, d] (fp32 or bf16 device tensors). Gates:
     fixed tensors g_s, g_lr [B, H, N], or learned from the projection gate_w [H, 2, d],
     gate_b [H, 2] of the query."""
     B, H, N, d = q.shape
-    cfg = ElsaaConfig(B, H, N, d, q.dtype, causal, block, hash_bits, lr_tables, 4, chunk, tau, eps)
+    cfg = ElsaaConfig(B, H, N, d, q.dtype, causal, block, hash_bits, lr_tables, 4, chunk, tau, eps,
+                      hash_rounds=hash_rounds)
     if planes_s is None or planes_lr is None:
         ps, pl = make_planes(cfg, seed, q.device)
         planes_s = ps if planes_s is None else planes_s

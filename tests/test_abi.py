@@ -89,13 +89,36 @@ def test_valid_params_and_workspace_sizes():
     (dict(eps=-1.0), _lib.ERR_INVALID_ARG, "eps"),
     (dict(scale=float("nan")), _lib.ERR_INVALID_ARG, "scale"),
     (dict(dtype=torch.float32, d=128, block=256, N=1024), _lib.ERR_UNSUPPORTED, "LDS"),
+    (dict(hash_rounds=5), _lib.ERR_UNSUPPORTED, "hash_rounds"),
+    (dict(dtype=torch.bfloat16, d=128, block=256, N=1024, hash_rounds=2), _lib.ERR_UNSUPPORTED,
+     "LDS"),
     (dict(B=300, H=300), _lib.ERR_INVALID_ARG, "65535"),
+    (dict(B=1, H=100, N=1 << 24, block=16, hash_bits=12, hash_rounds=2), _lib.ERR_INVALID_ARG,
+     "2^31"),
     (dict(B=1, H=200, N=1 << 24, block=16, hash_bits=12), _lib.ERR_INVALID_ARG, "2^31"),
 ])
 def test_invalid_parameters(kw, status, needle):
     s, msg, _ = status_of(base(**kw))
     assert s == status, msg
     assert needle in msg
+
+
+def test_hash_rounds_sizes():
+    """Several hash rounds: the orders and the partial slots grow with the rounds;
+    0 and 1 both mean one round; a negative count is rejected."""
+    one, two = base(), base(hash_rounds=2)
+    assert two.perm_len == 2 * one.perm_len
+    for call in (_lib.CALL_SELECT, _lib.CALL_FWD, _lib.CALL_BWD):
+        s1, m1, n1 = status_of(one, call)
+        s2, m2, n2 = status_of(two, call)
+        assert s1 == _lib.OK and s2 == _lib.OK, (m1, m2)
+        assert n2 > n1, call
+    p = one.params()
+    p.hash_rounds = 0
+    assert status_of(p, _lib.CALL_FWD)[2] == status_of(one, _lib.CALL_FWD)[2]
+    p.hash_rounds = -1
+    s, msg, _ = status_of(p, _lib.CALL_FWD)
+    assert s == _lib.ERR_INVALID_ARG and "hash_rounds" in msg
 
 
 def test_bad_dtype_and_null_params():

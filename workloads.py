@@ -166,6 +166,16 @@ def gen_planes(w: Workload, seed: int) -> tuple[torch.Tensor, torch.Tensor]:
     return ps.contiguous(), plr.contiguous()
 
 
+def gen_planes_rounds(w: Workload, seed: int, rounds: int) -> torch.Tensor:
+    """sortLSH hyperplanes for several hash rounds, [H, rounds, hash_bits, d]:
+    round 0 is gen_planes' set, round u > 0 is drawn from its own generator."""
+    per = []
+    for h in range(w.H):
+        per.append(torch.stack([_randn(_gen(seed + 1 + 100 * u, h), w.hash_bits, w.d)
+                                for u in range(rounds)]))
+    return torch.stack(per).contiguous()
+
+
 def gen_gates(w: Workload, seed: int) -> tuple[torch.Tensor, torch.Tensor]:
     g = _gen(seed + 3, 0)
     gs = 0.5 + torch.rand(w.B, w.H, w.N, generator=g)
