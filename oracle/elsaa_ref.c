@@ -35,6 +35,7 @@ static int check_params(const ref_params* p) {
   if (p->block <= 0 || p->N % p->block) return RET_BAD;
   if (p->hash_bits < 1 || p->hash_bits > 16) return RET_BAD;
   if (p->hash_rounds < 0 || p->hash_rounds > 16) return RET_BAD;
+  if (p->extra_edges < 0) return RET_BAD;
   if (p->lr_tables < 1 || p->lr_bits < 0 || p->lr_bits > 8) return RET_BAD;
   if (p->causal) {
     if (ilog2_exact(p->N / p->block) < 0) return RET_BAD;
@@ -161,6 +162,7 @@ typedef struct {
   const ref_params* p;
   const double *Q, *K, *V;
   const int32_t *qperm, *kperm;
+  const int32_t* extra; /* [N][extra_edges] or NULL */
 } head_in;
 
 /* Exact softmax attention of the queries qs[0..nq) over the keys ks[0..nk),
@@ -266,13 +268,15 @@ static void sparse_head(const head_in* h, double* O_s, double* lse) {
 }
 
 /* Several hash rounds (Appendix C: L_s independent hash tables, the support
- * Omega_LSH being the union of what each table selects). The union support of
- * query i: its causal leaf, and for every round the key block paired with i's
- * query block at every level where i is a future query (one level when not
- * causal). Written as mark[j] = 1 for the keys j in it (each key once). invq:
+ * Omega_LSH being the union of what each table selects), and the listed extra
+ * edges (Appendix C's Omega_safe). The union support of query i: its causal leaf,
+ * for every round the key block paired with i's query block at every level where
+ * i is a future query (one level when not causal), and its valid listed keys.
+ * Written as mark[j] = 1 for the keys j in it (each key once). invq:
  * [rounds][levels][N], position of a token within its level's query order, or -1. */
 static void union_support(const ref_params* p, const int32_t* qperm, const int32_t* kperm,
-                          const int32_t* invq, int i, unsigned char* mark) {
+                          const int32_t* extra, const int32_t* invq, int i,
+                          unsigned char* mark) {
   const int N = p->N, s = p->block, L = n_levels(p), R = n_rounds(p);
   const size_t pl = perm_len(p);
   memset(mark, 0, N);
@@ -284,6 +288,11 @@ static void union_support(const ref_params* p, const int32_t* qperm, const int32
       if (t < 0) continue;
       const int32_t* ks = kperm + r * pl + (size_t)l * (p->causal ? N / 2 : N) + (size_t)(t / s) * s;
       for (int b = 0; b < s; ++b) mark[ks[b]] = 1;
+    }
+  if (extra)
+    for (int e = 0; e < p->extra_edges; ++e) {
+      const int32_t j = extra[(size_t)i * p->extra_edges + e];
+      if (j >= 0 && j < N && (!p->causal || j <= i)) mark[j] = 1;
     }
 }
 
@@ -307,7 +316,7 @@ static void sparse_union_head(const head_in* h, double* O_s, double* lse) {
   unsigned char* mark = (unsigned char*)malloc(N);
   double* e = (double*)malloc(sizeof(double) * N);
   for (int i = 0; i < N; ++i) {
-    union_support(p, h->qperm, h->kperm, invq, i, mark);
+    union_support(p, h->qperm, h->kperm, h->extra, invq, i, mark);
     double mx = -INFINITY;
     for (int j = 0; j < N; ++j) {
       if (!mark[j]) continue;
@@ -505,11 +514,12 @@ static void mass_ratio(double lse, double c, double* m, double* w) {
 /* One head forward. gs/glr may be NULL (gate 1). */
 static void forward_head(const ref_params* p, const double* Q, const double* K,
                          const double* V, const float* Rs, const float* Rlr, double lam,
-                         const double* gs, const double* glr, head_fwd* f, double* O) {
+                         const double* gs, const double* glr, const int32_t* extra, head_fwd* f,
+                         double* O) {
   const int N = p->N, d = p->d;
   select_rounds(p, Q, K, Rs, f->qc, f->kc, f->qperm, f->kperm);
-  head_in h = {p, Q, K, V, f->qperm, f->kperm};
-  if (n_rounds(p) == 1)
+  head_in h = {p, Q, K, V, f->qperm, f->kperm, extra};
+  if (n_rounds(p) == 1 && !extra)
     sparse_head(&h, f->O_s, f->lse);
   else
     sparse_union_head(&h, f->O_s, f->lse);
@@ -529,9 +539,11 @@ static void forward_head(const ref_params* p, const double* Q, const double* K,
 
 int ref_fwd(const ref_params* p, const double* Q, const double* K, const double* V,
             const float* planes_s, const float* planes_lr, const double* lambda,
-            const double* g_s, const double* g_lr,
+            const double* g_s, const double* g_lr, const int32_t* extra,
             double* O, double* O_s, double* O_lr, double* lse, double* d_lr) {
   if (check_params(p) || !lambda) return RET_BAD;
+  if (p->extra_edges == 0) extra = NULL;
+  const size_t ne = (size_t)p->N * p->extra_edges;
   const size_t N = p->N, nd = N * p->d;
   const size_t ps = (size_t)n_rounds(p) * p->hash_bits * p->d;
   const size_t plr = (size_t)p->lr_tables * p->lr_bits * p->d;
@@ -540,7 +552,8 @@ int ref_fwd(const ref_params* p, const double* Q, const double* K, const double*
     head_fwd f;
     head_fwd_alloc(p, &f);
     forward_head(p, Q + g * nd, K + g * nd, V + g * nd, planes_s + g * ps, planes_lr + g * plr,
-                 lambda[g], g_s ? g_s + g * N : NULL, g_lr ? g_lr + g * N : NULL, &f, O + g * nd);
+                 lambda[g], g_s ? g_s + g * N : NULL, g_lr ? g_lr + g * N : NULL,
+                 extra ? extra + g * ne : NULL, &f, O + g * nd);
     if (O_s) memcpy(O_s + g * nd, f.O_s, sizeof(double) * nd);
     if (O_lr) memcpy(O_lr + g * nd, f.O_lr, sizeof(double) * nd);
     if (lse) memcpy(lse + g * N, f.lse, sizeof(double) * N);
@@ -617,7 +630,7 @@ static void sparse_union_bwd(const head_in* h, const double* O_s, const double* 
   int32_t* invq = query_positions(p, h->qperm);
   unsigned char* mark = (unsigned char*)malloc(N);
   for (int i = 0; i < N; ++i) {
-    union_support(p, h->qperm, h->kperm, invq, i, mark);
+    union_support(p, h->qperm, h->kperm, h->extra, invq, i, mark);
     double Di = 0.0;
     for (int c = 0; c < d; ++c) Di += dOs[(size_t)i * d + c] * O_s[(size_t)i * d + c];
     for (int j = 0; j < N; ++j) {
@@ -662,13 +675,13 @@ static void features_row_bwd(const ref_params* p, const float* R, const double* 
 
 static void backward_head(const ref_params* p, const double* Q, const double* K, const double* V,
                           const double* dO, const float* Rs, const float* Rlr, double lam,
-                          const double* gs, const double* glr, double* dQ, double* dK, double* dV,
-                          double* dlam, double* dgs, double* dglr) {
+                          const double* gs, const double* glr, const int32_t* extra, double* dQ,
+                          double* dK, double* dV, double* dlam, double* dgs, double* dglr) {
   const int N = p->N, d = p->d, r = feat_dim(p);
   head_fwd f;
   head_fwd_alloc(p, &f);
   double* O = (double*)malloc(sizeof(double) * (size_t)N * d);
-  forward_head(p, Q, K, V, Rs, Rlr, lam, gs, glr, &f, O);
+  forward_head(p, Q, K, V, Rs, Rlr, lam, gs, glr, extra, &f, O);
 
   double* dOs = (double*)malloc(sizeof(double) * (size_t)N * d);
   double* dlse = (double*)malloc(sizeof(double) * N);
@@ -707,8 +720,8 @@ static void backward_head(const ref_params* p, const double* Q, const double* K,
   memset(dQ, 0, sizeof(double) * (size_t)N * d);
   memset(dK, 0, sizeof(double) * (size_t)N * d);
   memset(dV, 0, sizeof(double) * (size_t)N * d);
-  head_in h = {p, Q, K, V, f.qperm, f.kperm};
-  if (n_rounds(p) > 1)
+  head_in h = {p, Q, K, V, f.qperm, f.kperm, extra};
+  if (n_rounds(p) > 1 || extra)
     sparse_union_bwd(&h, f.O_s, f.lse, dOs, dlse, dQ, dK, dV);
   else if (p->causal)
     sparse_bwd_rec(&h, 0, N, 0, f.O_s, f.lse, dOs, dlse, dQ, dK, dV);
@@ -783,9 +796,11 @@ static void backward_head(const ref_params* p, const double* Q, const double* K,
 int ref_bwd(const ref_params* p, const double* Q, const double* K, const double* V,
             const double* dO, const float* planes_s, const float* planes_lr,
             const double* lambda, const double* g_s, const double* g_lr,
-            double* dQ, double* dK, double* dV, double* dlambda,
+            const int32_t* extra, double* dQ, double* dK, double* dV, double* dlambda,
             double* dg_s, double* dg_lr) {
   if (check_params(p) || !lambda) return RET_BAD;
+  if (p->extra_edges == 0) extra = NULL;
+  const size_t ne = (size_t)p->N * p->extra_edges;
   const size_t N = p->N, nd = N * p->d;
   const size_t ps = (size_t)n_rounds(p) * p->hash_bits * p->d;
   const size_t plr = (size_t)p->lr_tables * p->lr_bits * p->d;
@@ -794,7 +809,8 @@ int ref_bwd(const ref_params* p, const double* Q, const double* K, const double*
     double dl = 0.0;
     backward_head(p, Q + g * nd, K + g * nd, V + g * nd, dO + g * nd, planes_s + g * ps,
                   planes_lr + g * plr, lambda[g], g_s ? g_s + g * N : NULL,
-                  g_lr ? g_lr + g * N : NULL, dQ + g * nd, dK + g * nd, dV + g * nd, &dl,
+                  g_lr ? g_lr + g * N : NULL, extra ? extra + g * ne : NULL, dQ + g * nd,
+                  dK + g * nd, dV + g * nd, &dl,
                   dg_s ? dg_s + g * N : NULL, dg_lr ? dg_lr + g * N : NULL);
     if (dlambda) dlambda[g] = dl;
   }

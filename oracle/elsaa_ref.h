@@ -20,6 +20,13 @@
  *               log2(N/block)), int32 [G][rounds][1][N] when not
  * With several rounds the sparse support of a query is the union of the rounds'
  * supports (each pair counted once), Appendix C's Omega_LSH.
+ *   extra     : int32  [G][N][extra_edges] or NULL: further keys listed per query,
+ *               added to the sparse support (Appendix C's augmentation
+ *               Omega = Omega_LSH u Omega_safe with Omega_safe,ij ~ Bernoulli(p):
+ *               the random draw is the caller's, the edges come in as a list).
+ *               An entry j counts when 0 <= j < N (and j <= i when causal); the
+ *               support is a set, so a pair listed twice or already selected by
+ *               sortLSH is counted once.
  *   A, z      : double [G][r][d], [G][r] (non-causal: sums over all keys);
  *               double [G][N/chunk][r][d], [G][N/chunk][r] (causal: sums over
  *               keys strictly before each chunk), with r = lr_tables << lr_bits.
@@ -39,6 +46,7 @@ typedef struct {
   int chunk;       /* causal RACE summary spacing C              */
   double tau, eps, scale;
   int hash_rounds; /* sortLSH hash tables L_s (0 or 1: one)             */
+  int extra_edges; /* entries per query of the extra edge list (0: none) */
 } ref_params;
 
 int ref_select(const ref_params* p, const double* Q, const double* K,
@@ -50,13 +58,13 @@ int ref_lowrank_summary(const ref_params* p, const double* K, const double* V,
 
 int ref_fwd(const ref_params* p, const double* Q, const double* K, const double* V,
             const float* planes_s, const float* planes_lr, const double* lambda,
-            const double* g_s, const double* g_lr,
+            const double* g_s, const double* g_lr, const int32_t* extra,
             double* O, double* O_s, double* O_lr, double* lse, double* d_lr);
 
 int ref_bwd(const ref_params* p, const double* Q, const double* K, const double* V,
             const double* dO, const float* planes_s, const float* planes_lr,
             const double* lambda, const double* g_s, const double* g_lr,
-            double* dQ, double* dK, double* dV, double* dlambda,
+            const int32_t* extra, double* dQ, double* dK, double* dV, double* dlambda,
             double* dg_s, double* dg_lr);
 
 /* Learnable gates of Eq. 4. The paper names g_sparse,i and g_lr,i, has them

@@ -40,7 +40,7 @@ class _P(ctypes.Structure):
                 ("causal", ctypes.c_int), ("block", ctypes.c_int), ("hash_bits", ctypes.c_int),
                 ("lr_tables", ctypes.c_int), ("lr_bits", ctypes.c_int), ("chunk", ctypes.c_int),
                 ("tau", ctypes.c_double), ("eps", ctypes.c_double), ("scale", ctypes.c_double),
-                ("hash_rounds", ctypes.c_int)]
+                ("hash_rounds", ctypes.c_int), ("extra_edges", ctypes.c_int)]
 
 
 @dataclass
@@ -57,6 +57,7 @@ class RefParams:
     eps: float = 1e-6
     scale: float | None = None
     hash_rounds: int = 1
+    extra_edges: int = 0   # entries per query of the extra edge list (Omega_safe)
 
     @property
     def r(self) -> int:
@@ -76,7 +77,8 @@ class RefParams:
     def c(self, G: int) -> _P:
         sc = self.scale if self.scale is not None else 1.0 / math.sqrt(self.d)
         return _P(G, self.N, self.d, int(self.causal), self.block, self.hash_bits, self.lr_tables,
-                  self.lr_bits, self.chunk, self.tau, self.eps, sc, self.hash_rounds)
+                  self.lr_bits, self.chunk, self.tau, self.eps, sc, self.hash_rounds,
+                  self.extra_edges)
 
 
 _lib = None
@@ -141,21 +143,35 @@ def lowrank_summary(p: RefParams, k, v, planes_lr):
     return A, z
 
 
-def forward(p: RefParams, q, k, v, planes_s, planes_lr, lam, g_s=None, g_lr=None):
+def _extra(p: RefParams, extra, G):
+    if extra is None or p.extra_edges == 0:
+        return None
+    e = np.ascontiguousarray(np.asarray(extra, dtype=np.int32))
+    if e.shape != (G, p.N, p.extra_edges):
+        raise ValueError(f"extra has shape {e.shape}, expected {(G, p.N, p.extra_edges)}")
+    return e
+
+
+def forward(p: RefParams, q, k, v, planes_s, planes_lr, lam, g_s=None, g_lr=None, extra=None):
+    """extra: int32 [G, N, extra_edges] further keys per query (Omega_safe), or None."""
     q, k, v, ps, pl = _f64(q), _f64(k), _f64(v), _f32(planes_s), _f32(planes_lr)
     lam, g_s, g_lr = _f64(lam), _f64(g_s), _f64(g_lr)
+    ex = _extra(p, extra, q.shape[0])
     G, N, d = q.shape
     out = {n: np.zeros((G, N, d)) for n in ("O", "O_s", "O_lr")}
     out.update({n: np.zeros((G, N)) for n in ("lse", "d_lr")})
     pc = p.c(G)
     _check(lib().ref_fwd(ctypes.byref(pc), _ptr(q), _ptr(k), _ptr(v), _ptr(ps), _ptr(pl), _ptr(lam),
-                         _ptr(g_s), _ptr(g_lr), _ptr(out["O"]), _ptr(out["O_s"]), _ptr(out["O_lr"]),
+                         _ptr(g_s), _ptr(g_lr), _ptr(ex), _ptr(out["O"]), _ptr(out["O_s"]),
+                         _ptr(out["O_lr"]),
                          _ptr(out["lse"]), _ptr(out["d_lr"])), "fwd")
     return out
 
 
-def backward(p: RefParams, q, k, v, do, planes_s, planes_lr, lam, g_s=None, g_lr=None):
+def backward(p: RefParams, q, k, v, do, planes_s, planes_lr, lam, g_s=None, g_lr=None,
+             extra=None):
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    ex = _extra(p, extra, q.shape[0])
     ps, pl, lam, g_s, g_lr = _f32(planes_s), _f32(planes_lr), _f64(lam), _f64(g_s), _f64(g_lr)
     G, N, d = q.shape
     out = {n: np.zeros((G, N, d)) for n in ("dQ", "dK", "dV")}
@@ -164,7 +180,7 @@ def backward(p: RefParams, q, k, v, do, planes_s, planes_lr, lam, g_s=None, g_lr
     out["dg_lr"] = np.zeros((G, N))
     pc = p.c(G)
     _check(lib().ref_bwd(ctypes.byref(pc), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(ps), _ptr(pl),
-                         _ptr(lam), _ptr(g_s), _ptr(g_lr), _ptr(out["dQ"]), _ptr(out["dK"]),
+                         _ptr(lam), _ptr(g_s), _ptr(g_lr), _ptr(ex), _ptr(out["dQ"]), _ptr(out["dK"]),
                          _ptr(out["dV"]), _ptr(out["dlambda"]), _ptr(out["dg_s"]),
                          _ptr(out["dg_lr"])), "bwd")
     return out

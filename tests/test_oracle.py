@@ -611,3 +611,107 @@ def test_rounds_union_matches_dense_masked_softmax_and_autograd(causal, R):
     g = ref.backward(p, q[None], k[None], v[None], do[None], psR, pl, np.array([1.2]))
     for a, b in ((g["dQ"][0], tq.grad), (g["dK"][0], tk.grad), (g["dV"][0], tv.grad)):
         np.testing.assert_allclose(a, b.numpy(), atol=1e-10, rtol=1e-9)
+
+
+# ----------------------------------------------------------------------------- extra edges (Omega_safe)
+
+def _extra_list(N, E, causal, seed, qp=None, kp=None, s=None):
+    """[N, E] int32 extra keys per query with every kind of entry the definition
+    covers: random keys, -1 padding, out-of-range keys, a key listed twice, keys
+    after the query (ignored when causal) and a key sortLSH already selected."""
+    rng = np.random.default_rng(seed)
+    ex = rng.integers(0, N, size=(N, E)).astype(np.int32)
+    ex[:, 1] = -1
+    ex[::3, 2] = N + 5
+    ex[:, 3] = ex[:, 0]
+    ex[:, 4] = np.minimum(np.arange(N) + 3, N - 1)
+    ex[:, 5] = np.arange(N)  # the query itself: in its causal leaf
+    return ex
+
+
+def _extra_mask(N, causal, ex):
+    M = np.zeros((N, N), bool)
+    for i in range(N):
+        for j in ex[i]:
+            if 0 <= j < N and (not causal or j <= i):
+                M[i, j] = True
+    return M
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("R", [1, 2])
+def test_extra_edges_union_matches_dense_masked_softmax_and_autograd(causal, R):
+    """Extra edges (Appendix C's Omega = Omega_LSH u Omega_safe): the sparse branch
+    is the softmax over the union of the sortLSH support and the valid listed keys
+    (a set: duplicates and keys sortLSH already holds count once; -1, out-of-range
+    and, causal, later keys are ignored), checked against dense brute force over
+    that mask built here from the definition, and the backward against autograd."""
+    N, s, E = 128, 16, 7
+    w = small(causal, N=N, d=16, block=s, r=32)
+    p = ref.RefParams.from_workload(w, hash_rounds=R, extra_edges=E)
+    q, k, v, do, ps, pl = head(w, 211 + R + 2 * causal)
+    psR = _round_planes(ps, R, 17 + R) if R > 1 else ps
+    _, _, qp, kp = ref.select(p, q[None], k[None], psR)
+    lsh = [D.support_mask(N, s, causal, (qp[0, r] if R > 1 else qp[0]),
+                          (kp[0, r] if R > 1 else kp[0])) for r in range(R)]
+    ex = _extra_list(N, E, causal, 5 + R)
+    M0 = np.logical_or.reduce(lsh)
+    M = M0 | _extra_mask(N, causal, ex)
+    assert M.sum() > M0.sum()
+    tq, tk, tv = (torch.from_numpy(x).clone().requires_grad_(True) for x in (q, k, v))
+    dn = D.dense_forward(tq, tk, tv, M, torch.from_numpy(pl[0]), 0.8, causal, 0.25)
+    o = ref.forward(p, q[None], k[None], v[None], psR, pl, np.array([0.8]), extra=ex[None])
+    for n in ("O", "O_s", "lse", "d_lr"):
+        np.testing.assert_allclose(o[n][0], dn[n].detach().numpy(), atol=1e-10, rtol=1e-9)
+    (dn["O"] * torch.from_numpy(do)).sum().backward()
+    g = ref.backward(p, q[None], k[None], v[None], do[None], psR, pl, np.array([0.8]),
+                     extra=ex[None])
+    for a, b in ((g["dQ"][0], tq.grad), (g["dK"][0], tk.grad), (g["dV"][0], tv.grad)):
+        np.testing.assert_allclose(a, b.numpy(), atol=1e-10, rtol=1e-9)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_extra_edges_listing_every_key_is_exact_attention(causal):
+    """Listing every key for every query makes the support all keys (at or before
+    the query when causal), so the sparse branch is exact softmax attention,
+    whatever sortLSH selected."""
+    N, E = 64, 64
+    w = small(causal, N=N, d=16, block=16, r=32)
+    p = ref.RefParams.from_workload(w, extra_edges=E)
+    q, k, v, do, ps, pl = head(w, 223 + causal)
+    ex = np.tile(np.arange(N, dtype=np.int32), (N, 1))
+    o = ref.forward(p, q[None], k[None], v[None], ps, pl, np.array([1.0]), extra=ex[None])
+    S = (q @ k.T) * p.scale if p.scale else (q @ k.T) / math.sqrt(16)
+    if causal:
+        S = np.where(np.tril(np.ones((N, N), bool)), S, -np.inf)
+    lse = np.log(np.exp(S - S.max(1, keepdims=True)).sum(1)) + S.max(1)
+    Pm = np.exp(S - lse[:, None])
+    np.testing.assert_allclose(o["lse"][0], lse, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(o["O_s"][0], Pm @ v, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_extra_edges_already_selected_change_nothing(causal):
+    """Extra edges that sortLSH already selects (each query's own causal-leaf keys,
+    or the keys of its own block) leave the operator unchanged: the support is a
+    set."""
+    N, s, E = 128, 16, 4
+    w = small(causal, N=N, d=16, block=s, r=32)
+    p0 = ref.RefParams.from_workload(w)
+    p1 = ref.RefParams.from_workload(w, extra_edges=E)
+    q, k, v, do, ps, pl = head(w, 229 + causal)
+    _, _, qp, kp = ref.select(p0, q[None], k[None], ps)
+    M = D.support_mask(N, s, causal, qp[0], kp[0])
+    ex = np.full((N, E), -1, np.int32)
+    for i in range(N):
+        js = np.flatnonzero(M[i])[:E]
+        ex[i, :len(js)] = js
+    o0 = ref.forward(p0, q[None], k[None], v[None], ps, pl, np.array([0.6]))
+    o1 = ref.forward(p1, q[None], k[None], v[None], ps, pl, np.array([0.6]), extra=ex[None])
+    for n in ("O", "O_s", "lse"):
+        np.testing.assert_allclose(o1[n], o0[n], rtol=1e-12, atol=1e-13)
+    g0 = ref.backward(p0, q[None], k[None], v[None], do[None], ps, pl, np.array([0.6]))
+    g1 = ref.backward(p1, q[None], k[None], v[None], do[None], ps, pl, np.array([0.6]),
+                      extra=ex[None])
+    for n in ("dQ", "dK", "dV", "dlambda"):
+        np.testing.assert_allclose(g1[n], g0[n], rtol=1e-10, atol=1e-12)
