@@ -113,6 +113,8 @@ typedef enum {
  *                  independently; a query's sparse support is the union of the
  *                  rounds' supports, each pair counted once (Appendix C's
  *                  Omega_LSH). The per-query counts above then become upper bounds.
+ *   extra_edges  : E, 0..64, keys listed per query that join the sparse support
+ *                  (elsaa_fwd / elsaa_bwd's extra_idx); 0 for none.
  * Derived: levels Lv = log2(N / s) when causal (off-diagonal recursion levels), 1
  * when not; the permutation length P = R * Lv * N / 2 when causal, R * N when not
  * (the rounds' orders one after another); the number of summaries nA = N / C when
@@ -128,6 +130,7 @@ typedef struct {
   int32_t chunk;
   float tau, eps, scale;
   int32_t hash_rounds;
+  int32_t extra_edges;
 } elsaa_params;
 
 /* Bytes of workspace the given call needs for these parameters (written to
@@ -191,6 +194,14 @@ elsaa_status elsaa_lowrank_summary(const elsaa_params* p, const void* K, const v
 /* Forward: sparse branch over the selection, low-rank readout, Eq. 5 and Eq. 4.
  *   Q, K, V          : [B, H, N, d_h] dtype; planes_lr as above.
  *   q_perm, k_perm   : from elsaa_select; A, z: from elsaa_lowrank_summary.
+ *   extra_idx        : int32 [B, H, N, E] with E = extra_edges, or NULL when E = 0:
+ *                      keys listed per query that join its sparse support (Appendix
+ *                      C's augmentation Omega = Omega_LSH u Omega_safe, whose
+ *                      Bernoulli draw is the caller's; or any selector's picks,
+ *                      e.g. elsaa_topk's). An entry j counts when 0 <= j < N (and
+ *                      j <= i when causal); others (-1 padding) are ignored. The
+ *                      support is a set: a key listed twice, or already selected
+ *                      by sortLSH, counts once. elsaa_bwd takes the same list.
  *   lambda           : fp32 [H] (>= 0), the lambda of Eq. 5 per head.
  *   g_s, g_lr        : fp32 [B, H, N] gates g_sparse, g_lr of Eq. 4, or NULL for 1.
  *   O (out)          : [B, H, N, d_h] dtype, the fused output.
@@ -205,7 +216,8 @@ elsaa_status elsaa_lowrank_summary(const elsaa_params* p, const void* K, const v
  */
 elsaa_status elsaa_fwd(const elsaa_params* p, const void* Q, const void* K, const void* V,
                        const float* planes_lr, const int32_t* q_perm, const int32_t* k_perm,
-                       const float* A, const float* z, const float* lambda, const float* g_s,
+                       const int32_t* extra_idx, const float* A, const float* z,
+                       const float* lambda, const float* g_s,
                        const float* g_lr, void* O, float* O_s, void* O_lr, float* lse_s,
                        float* d_lr, void* ws, size_t ws_bytes, void* stream);
 
@@ -222,7 +234,8 @@ elsaa_status elsaa_fwd(const elsaa_params* p, const void* Q, const void* K, cons
 elsaa_status elsaa_bwd(const elsaa_params* p, const void* Q, const void* K, const void* V,
                        const void* dO, const float* O_s, const void* O_lr,
                        const float* planes_lr, const int32_t* q_perm, const int32_t* k_perm,
-                       const float* A, const float* z, const float* lse_s, const float* d_lr,
+                       const int32_t* extra_idx, const float* A, const float* z,
+                       const float* lse_s, const float* d_lr,
                        const float* lambda, const float* g_s, const float* g_lr, void* dQ,
                        void* dK, void* dV, float* dlambda, float* dg_s, float* dg_lr, void* ws,
                        size_t ws_bytes, void* stream);

@@ -27,7 +27,8 @@ class Params(ctypes.Structure):
                 ("block", ctypes.c_int32), ("hash_bits", ctypes.c_int32),
                 ("lr_tables", ctypes.c_int32), ("lr_bits", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("tau", ctypes.c_float), ("eps", ctypes.c_float),
-                ("scale", ctypes.c_float), ("hash_rounds", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("hash_rounds", ctypes.c_int32),
+                ("extra_edges", ctypes.c_int32)]
 
 
 class ElsaaError(RuntimeError):
@@ -54,8 +55,8 @@ def lib() -> ctypes.CDLL:
     L.elsaa_select.argtypes = [_PP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.elsaa_select_noalloc.argtypes = [_PP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.elsaa_lowrank_summary.argtypes = [_PP, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
-    L.elsaa_fwd.argtypes = [_PP] + [_vp] * 17 + [ctypes.c_size_t, _vp]
-    L.elsaa_bwd.argtypes = [_PP] + [_vp] * 23 + [ctypes.c_size_t, _vp]
+    L.elsaa_fwd.argtypes = [_PP] + [_vp] * 18 + [ctypes.c_size_t, _vp]
+    L.elsaa_bwd.argtypes = [_PP] + [_vp] * 24 + [ctypes.c_size_t, _vp]
     L.elsaa_gates_fwd.argtypes = [_PP] + [_vp] * 6
     L.elsaa_gates_bwd.argtypes = [_PP] + [_vp] * 10 + [ctypes.c_size_t, _vp]
     L.elsaa_topk.argtypes = [_PP, _vp, _vp, ctypes.c_int32, _vp, _vp]

@@ -75,6 +75,12 @@ elsaa_status make_problem(const elsaa_params* p, Problem* pb, bool* empty) {
   if (p->hash_rounds > elsaa::kMaxRounds)
     return fail(ELSAA_ERR_UNSUPPORTED, "hash_rounds = %d: at most %d are built", p->hash_rounds,
                 elsaa::kMaxRounds);
+  if (p->extra_edges < 0) return fail(ELSAA_ERR_INVALID_ARG, "extra_edges must be >= 0");
+  if (p->extra_edges > elsaa::kMaxExtra)
+    return fail(ELSAA_ERR_UNSUPPORTED, "extra_edges = %d: at most %d are built", p->extra_edges,
+                elsaa::kMaxExtra);
+  if ((long)p->N * p->extra_edges > 0x7fffffffL)
+    return fail(ELSAA_ERR_INVALID_ARG, "N * extra_edges exceeds 2^31 - 1");
   if (p->lr_tables < 1) return fail(ELSAA_ERR_INVALID_ARG, "lr_tables must be >= 1");
   if (p->lr_tables > elsaa::kMaxTables)
     return fail(ELSAA_ERR_UNSUPPORTED, "lr_tables = %d: at most %d are built", p->lr_tables,
@@ -115,6 +121,7 @@ elsaa_status make_problem(const elsaa_params* p, Problem* pb, bool* empty) {
   pb->tau = p->tau; pb->eps = p->eps; pb->scale = p->scale;
   pb->levels = pb->causal ? ilog2(p->N / p->block) : 1;
   pb->rounds = p->hash_rounds > 1 ? p->hash_rounds : 1;
+  pb->E = p->extra_edges;
   pb->nA = pb->causal ? p->N / pb->chunk : 1;
   pb->elem = pb->bf16 ? 2 : 4;
   if (lds_need(*pb) > elsaa::kLdsBytes)
@@ -252,33 +259,37 @@ elsaa_status elsaa_lowrank_summary(const elsaa_params* p, const void* K, const v
 
 elsaa_status elsaa_fwd(const elsaa_params* p, const void* Q, const void* K, const void* V,
                        const float* planes_lr, const int32_t* q_perm, const int32_t* k_perm,
-                       const float* A, const float* z, const float* lambda, const float* g_s,
-                       const float* g_lr, void* O, float* O_s, void* O_lr, float* lse_s,
-                       float* d_lr, void* ws, size_t ws_bytes, void* stream) {
+                       const int32_t* extra_idx, const float* A, const float* z,
+                       const float* lambda, const float* g_s, const float* g_lr, void* O,
+                       float* O_s, void* O_lr, float* lse_s, float* d_lr, void* ws,
+                       size_t ws_bytes, void* stream) {
   PROLOGUE(ELSAA_CALL_FWD);
   if (empty) return ELSAA_OK;
   NEED(Q); NEED(K); NEED(V); NEED(planes_lr); NEED(A); NEED(z);
   if (elsaa::perm_stride(pb.N, pb.levels, pb.causal, pb.rounds) > 0) { NEED(q_perm); NEED(k_perm); }
   OPTIONAL(q_perm); OPTIONAL(k_perm);
+  if (pb.E > 0) NEED(extra_idx);
+  OPTIONAL(extra_idx);
   NEED(lambda); OPTIONAL(g_s); OPTIONAL(g_lr);
   NEED(O); NEED(O_s); NEED(O_lr); NEED(lse_s); NEED(d_lr);
   {
     elsaa_status s_ = check_ws(pb, ELSAA_CALL_FWD, ws, ws_bytes);
     if (s_ != ELSAA_OK) return s_;
   }
-  if (!elsaa::launch_fwd(pb, Q, K, V, planes_lr, q_perm, k_perm, A, z, lambda, g_s, g_lr, O, O_s,
-                         O_lr, lse_s, d_lr, ws, (hipStream_t)stream, true))
+  if (!elsaa::launch_fwd(pb, Q, K, V, planes_lr, q_perm, k_perm, A, z, lambda, g_s, g_lr,
+                         extra_idx, O, O_s, O_lr, lse_s, d_lr, ws, (hipStream_t)stream, true))
     return fail(ELSAA_ERR_UNSUPPORTED, "no forward kernel variant is built for these sizes");
-  elsaa::launch_fwd(pb, Q, K, V, planes_lr, q_perm, k_perm, A, z, lambda, g_s, g_lr, O, O_s, O_lr,
-                    lse_s, d_lr, ws, (hipStream_t)stream, false);
+  elsaa::launch_fwd(pb, Q, K, V, planes_lr, q_perm, k_perm, A, z, lambda, g_s, g_lr, extra_idx, O,
+                    O_s, O_lr, lse_s, d_lr, ws, (hipStream_t)stream, false);
   return launched();
 }
 
 elsaa_status elsaa_bwd(const elsaa_params* p, const void* Q, const void* K, const void* V,
                        const void* dO, const float* O_s, const void* O_lr,
                        const float* planes_lr, const int32_t* q_perm, const int32_t* k_perm,
-                       const float* A, const float* z, const float* lse_s, const float* d_lr,
-                       const float* lambda, const float* g_s, const float* g_lr, void* dQ,
+                       const int32_t* extra_idx, const float* A, const float* z,
+                       const float* lse_s, const float* d_lr, const float* lambda,
+                       const float* g_s, const float* g_lr, void* dQ,
                        void* dK, void* dV, float* dlambda, float* dg_s, float* dg_lr, void* ws,
                        size_t ws_bytes, void* stream) {
   PROLOGUE(ELSAA_CALL_BWD);
@@ -286,6 +297,8 @@ elsaa_status elsaa_bwd(const elsaa_params* p, const void* Q, const void* K, cons
   NEED(Q); NEED(K); NEED(V); NEED(dO); NEED(O_s); NEED(O_lr); NEED(planes_lr);
   if (elsaa::perm_stride(pb.N, pb.levels, pb.causal, pb.rounds) > 0) { NEED(q_perm); NEED(k_perm); }
   OPTIONAL(q_perm); OPTIONAL(k_perm);
+  if (pb.E > 0) NEED(extra_idx);
+  OPTIONAL(extra_idx);
   NEED(A); NEED(z); NEED(lse_s); NEED(d_lr); NEED(lambda); OPTIONAL(g_s); OPTIONAL(g_lr);
   NEED(dQ); NEED(dK); NEED(dV); OPTIONAL(dlambda); OPTIONAL(dg_s); OPTIONAL(dg_lr);
   {
@@ -293,12 +306,12 @@ elsaa_status elsaa_bwd(const elsaa_params* p, const void* Q, const void* K, cons
     if (s_ != ELSAA_OK) return s_;
   }
   if (!elsaa::launch_bwd(pb, Q, K, V, dO, O_s, O_lr, planes_lr, q_perm, k_perm, A, z, lse_s, d_lr,
-                         lambda, g_s, g_lr, dQ, dK, dV, dlambda, dg_s, dg_lr, ws,
+                         lambda, g_s, g_lr, extra_idx, dQ, dK, dV, dlambda, dg_s, dg_lr, ws,
                          (hipStream_t)stream, true))
     return fail(ELSAA_ERR_UNSUPPORTED, "no backward kernel variant is built for these sizes");
   elsaa::launch_bwd(pb, Q, K, V, dO, O_s, O_lr, planes_lr, q_perm, k_perm, A, z, lse_s, d_lr,
-                    lambda, g_s, g_lr, dQ, dK, dV, dlambda, dg_s, dg_lr, ws, (hipStream_t)stream,
-                    false);
+                    lambda, g_s, g_lr, extra_idx, dQ, dK, dV, dlambda, dg_s, dg_lr, ws,
+                    (hipStream_t)stream, false);
   return launched();
 }
 

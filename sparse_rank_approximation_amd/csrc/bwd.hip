@@ -1411,7 +1411,7 @@ int rt_stride(const Problem& pb);
 
 // Workgroups of a persistent launch: as many as fit on the device at once.
 struct BwdLayout {
-  size_t rows, dlam, parts, gsum, gstate, rt, scratch, bids, total;
+  size_t rows, dlam, parts, gsum, gstate, rt, scratch, bids, extra, total;
   int nblk;
 };
 
@@ -1432,6 +1432,7 @@ BwdLayout bwd_layout(const Problem& pb) {
   const int groups = padded_tables(pb.L) > 8 ? 2 : 1;
   l.scratch = off; off += groups > 1 ? al(sizeof(float) * 3 * BH * N * D) : 0;
   l.bids = off; off += al(block_ids_bytes(pb));
+  l.extra = off; off += al(extra_layout(pb, true).total);
   l.total = off;
   return l;
 }
@@ -1483,8 +1484,8 @@ bool launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
                 const float* O_s, const void* O_lr, const float* planes_lr, const int32_t* qperm,
                 const int32_t* kperm, const float* A, const float* z, const float* lse,
                 const float* d_lr, const float* lambda, const float* g_s, const float* g_lr,
-                void* dQ, void* dK, void* dV, float* dlambda, float* dg_s, float* dg_lr, void* ws,
-                hipStream_t st, bool dry) {
+                const int32_t* extra, void* dQ, void* dK, void* dV, float* dlambda, float* dg_s,
+                float* dg_lr, void* ws, hipStream_t st, bool dry) {
   bool ok = true;
   const BwdLayout lay = bwd_layout(pb);
   char* base = (char*)ws;
@@ -1516,7 +1517,14 @@ bool launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
   int32_t* kbid = qbid + block_ids_bytes(pb) / (2 * sizeof(int32_t));
   const int nord = pb.causal ? pb.rounds * pb.levels : pb.rounds;
   const int items = pb.causal ? nord * (pb.N / 2) / pb.s + pb.N / pb.s : nord * (pb.N / pb.s);
-  if (!dry && pb.rounds > 1) launch_block_ids(pb, qperm, kperm, qbid, kbid, st);
+  if (!dry && (pb.rounds > 1 || pb.E > 0)) launch_block_ids(pb, qperm, kperm, qbid, kbid, st);
+  const ExtraLayout xl = extra_layout(pb, true);
+  char* xb = base + lay.extra;
+  int32_t* jq = (int32_t*)(xb + xl.jq);
+  const size_t xrow = BH * N * pb.d * pb.elem;
+  void* dQx = pb.E ? xb + xl.rows : nullptr;
+  void* dKx = pb.E ? xb + xl.rows + xrow : nullptr;
+  void* dVx = pb.E ? xb + xl.rows + 2 * xrow : nullptr;
 
   with_T(pb.bf16, [&](auto tp) {
     using T = ELSAA_T(tp);
@@ -1534,6 +1542,14 @@ bool launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
                              pb.B, pb.H, lay.nblk, dlambda);
         run_lr_sums(pb, Q, dO, re, rdd, planes_lr, S, Z, st);
         run_lr_scan(pb, S, Z, pb.causal ? 2 : 0, Gs, gzs, st);
+        if (pb.E > 0) {
+          int32_t* const sb[4] = {(int32_t*)(xb + xl.sort[0]), (int32_t*)(xb + xl.sort[1]),
+                                  (int32_t*)(xb + xl.sort[2]), (int32_t*)(xb + xl.sort[3])};
+          const int32_t *skey = nullptr, *sval = nullptr;
+          launch_extra_prep(pb, extra, qbid, kbid, jq, sb[0], sb[1], st);
+          launch_extra_sort(pb, sb, (int32_t*)(xb + xl.table), &skey, &sval, st);
+          launch_extra_bwd(pb, Q, K, V, dO, lse, rc, rD, jq, skey, sval, dQx, dKx, dVx, st);
+        }
       }
       auto run_sparse = [&](auto sc) {
         constexpr int SB = ELSAA_C(sc);
@@ -1626,7 +1642,7 @@ bool launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
         case 4: run_lr(std::integral_constant<int, 4>{}); break;
         default: run_lr(std::integral_constant<int, 8>{}); break;
       }
-      if (!dry) launch_combine(pb, dQp, dKp, dVp, dQ, dK, dV, st);
+      if (!dry) launch_combine(pb, dQp, dKp, dVp, dQx, dKx, dVx, dQ, dK, dV, st);
     });
   });
   return ok;

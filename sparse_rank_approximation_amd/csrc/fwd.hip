@@ -492,11 +492,26 @@ __global__ void __launch_bounds__(512)
   else walk(std::integral_constant<int, 1>{});
 }
 
-size_t fwd_ws_bytes(const Problem& pb) {
+// Workspace: the slots' log-sum-exps and outputs, the block indices (several
+// rounds or extra edges), the extra edges' region.
+struct FwdLayout {
+  size_t lpart, opart, bids, extra, total;
+};
+FwdLayout fwd_layout(const Problem& pb) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t BH = (size_t)pb.B * pb.H;
   const size_t slots = partial_slots(pb.N, pb.levels, pb.causal, pb.rounds);
-  return (size_t)pb.B * pb.H * slots * ((size_t)pb.d * pb.elem + sizeof(float)) + 512 +
-         block_ids_bytes(pb);
+  FwdLayout l;
+  size_t off = 0;
+  l.lpart = off; off += al(BH * slots * sizeof(float));
+  l.opart = off; off += al(BH * slots * pb.d * pb.elem);
+  l.bids = off; off += al(block_ids_bytes(pb));
+  l.extra = off; off += al(extra_layout(pb, false).total);
+  l.total = off;
+  return l;
 }
+
+size_t fwd_ws_bytes(const Problem& pb) { return fwd_layout(pb).total; }
 
 // The epilogue keeps the RACE hyperplanes in LDS unless that would cut its step
 // to 32 tokens where reading them from memory allows a longer one.
@@ -536,20 +551,27 @@ size_t fwd_lds_need(const Problem& pb) {
 bool launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
                 const float* planes_lr, const int32_t* qperm, const int32_t* kperm,
                 const float* A, const float* z, const float* lambda, const float* g_s,
-                const float* g_lr, void* O, float* O_s, void* O_lr, float* lse, float* d_lr,
-                void* ws, hipStream_t st, bool dry) {
+                const float* g_lr, const int32_t* extra, void* O, float* O_s, void* O_lr,
+                float* lse, float* d_lr, void* ws, hipStream_t st, bool dry) {
   bool ok = true;
   const int BH = pb.B * pb.H;
-  const size_t slots = partial_slots(pb.N, pb.levels, pb.causal, pb.rounds);
-  float* Lpart = (float*)ws;
-  const size_t lbytes = ((size_t)BH * slots * sizeof(float) + 255) & ~(size_t)255;
-  void* Opart = (char*)ws + lbytes;
-  const size_t obytes = ((size_t)BH * slots * pb.d * pb.elem + 255) & ~(size_t)255;
-  int32_t* qbid = (int32_t*)((char*)ws + lbytes + obytes);
+  const FwdLayout lay = fwd_layout(pb);
+  char* base = (char*)ws;
+  float* Lpart = (float*)(base + lay.lpart);
+  void* Opart = base + lay.opart;
+  int32_t* qbid = (int32_t*)(base + lay.bids);
   int32_t* kbid = qbid + block_ids_bytes(pb) / (2 * sizeof(int32_t));
+  const ExtraLayout xl = extra_layout(pb, false);
+  int32_t* jq = (int32_t*)(base + lay.extra + xl.jq);
+  void* Ox = pb.E ? base + lay.extra + xl.rows : nullptr;
+  float* Lx = pb.E ? (float*)(base + lay.extra + xl.lse) : nullptr;
   const int nord = pb.causal ? pb.rounds * pb.levels : pb.rounds;
   const int items = pb.causal ? nord * (pb.N / 2) / pb.s + pb.N / pb.s : nord * (pb.N / pb.s);
-  if (!dry && pb.rounds > 1) launch_block_ids(pb, qperm, kperm, qbid, kbid, st);
+  if (!dry && (pb.rounds > 1 || pb.E > 0)) launch_block_ids(pb, qperm, kperm, qbid, kbid, st);
+  if (!dry && pb.E > 0) {
+    launch_extra_prep(pb, extra, qbid, kbid, jq, nullptr, nullptr, st);
+    launch_extra_fwd(pb, Q, K, V, jq, Ox, Lx, st);
+  }
   with_T(pb.bf16, [&](auto tp) {
     using T = ELSAA_T(tp);
     with_D(pb.d, [&](auto dc) {
@@ -585,7 +607,7 @@ bool launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
         case 128: run(std::integral_constant<int, 128>{}); break;
         default: run(std::integral_constant<int, 256>{}); break;
       }
-      if (!dry) launch_merge(pb, Opart, Lpart, O_s, lse, st);
+      if (!dry) launch_merge(pb, Opart, Lpart, Ox, Lx, O_s, lse, st);
       with_LP(pb.L, [&](auto lc) {
         constexpr int LP = ELSAA_C(lc);
         constexpr bool PLDS = epilogue_planes_in_lds<T, D, LP>();

@@ -20,6 +20,7 @@ constexpr size_t kLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
 
 constexpr int kMaxLevels = 20;           // log2(N / s) for N <= 2^24, s >= 16
 constexpr int kMaxRounds = 4;            // sortLSH hash rounds (tables)
+constexpr int kMaxExtra = 64;            // extra edges listed per query
 
 // LDS of the kernels that walk a span of tokens in steps of STEP tokens: one
 // step's row-major channel tile (V, or the low-rank output gradient dnum), its
@@ -59,6 +60,7 @@ struct Problem {
   float tau, eps, scale;
   int levels;     // off-diagonal recursion levels (causal), 1 otherwise
   int rounds;     // sortLSH hash rounds (the support is the union of theirs)
+  int E;          // extra edges listed per query (0: none)
   int nA;         // summaries per head
   int elem;       // bytes per element of Q/K/V/...
 };
@@ -170,8 +172,9 @@ void prof_suspend(bool on);
 
 size_t select_ws_bytes(const Problem& pb);
 // Per-token block indices of every (round, level) order (select.hip), used by the
-// sparse kernels to count each pair once over several hash rounds; bytes of the
-// two arrays (0 with one round).
+// sparse kernels to count each pair once over several hash rounds, and to keep
+// extra edges sortLSH already selects out; bytes of the two arrays (0 with one
+// round and no extra edges).
 size_t block_ids_bytes(const Problem& pb);
 void launch_block_ids(const Problem& pb, const int32_t* qperm, const int32_t* kperm, int32_t* qb,
                       int32_t* kb, hipStream_t st);
@@ -205,8 +208,8 @@ size_t fwd_lds_need(const Problem& pb);
 bool launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
                 const float* planes_lr, const int32_t* qperm, const int32_t* kperm,
                 const float* A, const float* z, const float* lambda, const float* g_s,
-                const float* g_lr, void* O, float* O_s, void* O_lr, float* lse, float* d_lr,
-                void* ws, hipStream_t st, bool dry);
+                const float* g_lr, const int32_t* extra, void* O, float* O_s, void* O_lr,
+                float* lse, float* d_lr, void* ws, hipStream_t st, bool dry);
 
 // Exact per-query top-k selection (topk.hip); dry: report only whether a variant
 // is built for k.
@@ -221,11 +224,32 @@ void launch_gates_bwd(const Problem& pb, const void* Q, const float* W, const fl
                       const float* glr, const float* dgs, const float* dglr, void* dQ, float* dW,
                       float* db, void* ws, hipStream_t st);
 
-// Per-token reductions over the sparse partial slots (merge.hip).
-void launch_merge(const Problem& pb, const void* Opart, const float* Lpart, float* O_s, float* lse,
-                  hipStream_t st);
-void launch_combine(const Problem& pb, const void* dQp, const void* dKp, const void* dVp, void* dQ,
-                    void* dK, void* dV, hipStream_t st);
+// Extra edges listed per query (extra.hip). Workspace regions (byte offsets):
+// the kept keys per query, the partial rows (forward: output; backward: dQ, dK,
+// dV), the forward's log-sum-exps, and the backward's sort buffers and table.
+struct ExtraLayout {
+  size_t jq, rows, lse, sort[4], table, total;
+};
+ExtraLayout extra_layout(const Problem& pb, bool bwd);
+void launch_extra_prep(const Problem& pb, const int32_t* extra, const int32_t* qbid,
+                       const int32_t* kbid, int32_t* jq, int32_t* skey, int32_t* sval,
+                       hipStream_t st);
+void launch_extra_sort(const Problem& pb, int32_t* const (&buf)[4], int32_t* table,
+                       const int32_t** keys, const int32_t** vals, hipStream_t st);
+void launch_extra_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
+                      const int32_t* jq, void* Ox, float* Lx, hipStream_t st);
+void launch_extra_bwd(const Problem& pb, const void* Q, const void* K, const void* V,
+                      const void* dO, const float* lse, const float* rc, const float* rD,
+                      const int32_t* jq, const int32_t* skey, const int32_t* sval, void* dQx,
+                      void* dKx, void* dVx, hipStream_t st);
+
+// Per-token reductions over the sparse partial slots (merge.hip), with the extra
+// edges' partial rows (one per token, [B H][N]) when not null.
+void launch_merge(const Problem& pb, const void* Opart, const float* Lpart, const void* Ox,
+                  const float* Lx, float* O_s, float* lse, hipStream_t st);
+void launch_combine(const Problem& pb, const void* dQp, const void* dKp, const void* dVp,
+                    const void* dQx, const void* dKx, const void* dVx, void* dQ, void* dK,
+                    void* dV, hipStream_t st);
 
 size_t bwd_ws_bytes(const Problem& pb);
 size_t bwd_lds_need(const Problem& pb);
@@ -233,7 +257,7 @@ bool launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
                 const float* O_s, const void* O_lr, const float* planes_lr, const int32_t* qperm,
                 const int32_t* kperm, const float* A, const float* z, const float* lse,
                 const float* d_lr, const float* lambda, const float* g_s, const float* g_lr,
-                void* dQ, void* dK, void* dV, float* dlambda, float* dg_s, float* dg_lr, void* ws,
-                hipStream_t st, bool dry);
+                const int32_t* extra, void* dQ, void* dK, void* dV, float* dlambda, float* dg_s,
+                float* dg_lr, void* ws, hipStream_t st, bool dry);
 
 }  // namespace elsaa

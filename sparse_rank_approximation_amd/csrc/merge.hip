@@ -18,7 +18,8 @@ constexpr int kMergeBatch = 8;  // slots in flight per lane
 
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
-    merge_kernel(const T* __restrict__ Opart, const float* __restrict__ Lpart, int N, int levels,
+    merge_kernel(const T* __restrict__ Opart, const float* __restrict__ Lpart,
+                 const T* __restrict__ Ox, const float* __restrict__ Lx, int N, int levels,
                  int causal, int rounds, float* __restrict__ Os, float* __restrict__ lse) {
   constexpr int LPR = D / 8, RPB = 256 / LPR, MB = kMergeBatch;
   const int bh = blockIdx.y, tid = threadIdx.x;
@@ -63,6 +64,18 @@ __global__ void __launch_bounds__(256)
       mrun = mnew;
     }
   }
+  // The extra edges' partial (every token has a sortLSH partial, so mrun is
+  // finite here; an empty extra partial has weight 0).
+  if (Ox && valid) {
+    Vec8<T> raw;
+    raw.load(Ox + ((size_t)bh * N + tok) * D + c8);
+    const float lw = Lx[(size_t)bh * N + tok], mnew = fmaxf(mrun, lw);
+    const float a = fast_exp(mrun - mnew), wj = fast_exp(lw - mnew);
+    lrun = lrun * a + wj;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] * a + wj * raw.get(e);
+    mrun = mnew;
+  }
   if (valid) {
     const float inv = 1.0f / lrun;
 #pragma unroll
@@ -74,8 +87,9 @@ __global__ void __launch_bounds__(256)
 
 template <typename T, int D, bool QUERY, int NX>
 __global__ void __launch_bounds__(256)
-    combine_kernel(const T* __restrict__ p0, const T* __restrict__ p1, T* __restrict__ o0,
-                   T* __restrict__ o1, int N, int levels, int causal, int rounds) {
+    combine_kernel(const T* __restrict__ p0, const T* __restrict__ p1, const T* __restrict__ x0,
+                   const T* __restrict__ x1, T* __restrict__ o0, T* __restrict__ o1, int N,
+                   int levels, int causal, int rounds) {
   constexpr int LPR = D / 8, RPB = 256 / LPR, MB = kMergeBatch;
   const int bh = blockIdx.y, tid = threadIdx.x;
   const int tok = blockIdx.x * RPB + tid / LPR, c8 = (tid % LPR) * 8;
@@ -106,6 +120,16 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[x][e] += raw[x][j].get(e);
   }
+  if (x0 && valid) {  // the extra edges' part (one row per token)
+    const T* const xs[2] = {x0, x1};
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+      Vec8<T> raw;
+      raw.load(xs[x] + row);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[x][e] += raw.get(e);
+    }
+  }
   if (valid)
 #pragma unroll
     for (int x = 0; x < NX; ++x) store8(out[x] + row, acc[x]);
@@ -113,8 +137,8 @@ __global__ void __launch_bounds__(256)
 
 }  // namespace
 
-void launch_merge(const Problem& pb, const void* Opart, const float* Lpart, float* O_s, float* lse,
-                  hipStream_t st) {
+void launch_merge(const Problem& pb, const void* Opart, const float* Lpart, const void* Ox,
+                  const float* Lx, float* O_s, float* lse, hipStream_t st) {
   const int BH = pb.B * pb.H;
   with_T(pb.bf16, [&](auto tp) {
     using T = ELSAA_T(tp);
@@ -122,13 +146,15 @@ void launch_merge(const Problem& pb, const void* Opart, const float* Lpart, floa
       constexpr int D = ELSAA_C(dc);
       constexpr int RPB = 256 / (D / 8);
       ELSAA_LAUNCH("merge", (merge_kernel<T, D>), dim3((pb.N + RPB - 1) / RPB, BH), dim3(256), 0,
-                   st, (const T*)Opart, Lpart, pb.N, pb.levels, (int)pb.causal, pb.rounds, O_s, lse);
+                   st, (const T*)Opart, Lpart, (const T*)Ox, Lx, pb.N, pb.levels, (int)pb.causal,
+                   pb.rounds, O_s, lse);
     });
   });
 }
 
-void launch_combine(const Problem& pb, const void* dQp, const void* dKp, const void* dVp, void* dQ,
-                    void* dK, void* dV, hipStream_t st) {
+void launch_combine(const Problem& pb, const void* dQp, const void* dKp, const void* dVp,
+                    const void* dQx, const void* dKx, const void* dVx, void* dQ, void* dK,
+                    void* dV, hipStream_t st) {
   const int BH = pb.B * pb.H;
   with_T(pb.bf16, [&](auto tp) {
     using T = ELSAA_T(tp);
@@ -137,10 +163,12 @@ void launch_combine(const Problem& pb, const void* dQp, const void* dKp, const v
       constexpr int RPB = 256 / (D / 8);
       const dim3 grid((pb.N + RPB - 1) / RPB, BH);
       ELSAA_LAUNCH("combine_q", (combine_kernel<T, D, true, 1>), grid, dim3(256), 0, st,
-                   (const T*)dQp, (const T*)nullptr, (T*)dQ, (T*)nullptr, pb.N, pb.levels,
+                   (const T*)dQp, (const T*)nullptr, (const T*)dQx, (const T*)nullptr, (T*)dQ,
+                   (T*)nullptr, pb.N, pb.levels,
                    (int)pb.causal, pb.rounds);
       ELSAA_LAUNCH("combine_kv", (combine_kernel<T, D, false, 2>), grid, dim3(256), 0, st,
-                   (const T*)dKp, (const T*)dVp, (T*)dK, (T*)dV, pb.N, pb.levels,
+                   (const T*)dKp, (const T*)dVp, (const T*)dKx, (const T*)dVx, (T*)dK, (T*)dV,
+                   pb.N, pb.levels,
                    (int)pb.causal, pb.rounds);
     });
   });

@@ -281,7 +281,7 @@ __global__ void __launch_bounds__(256)
 }
 
 size_t block_ids_bytes(const Problem& pb) {
-  if (pb.rounds <= 1) return 0;
+  if (pb.rounds <= 1 && pb.E == 0) return 0;
   const size_t nord = pb.causal ? (size_t)pb.rounds * pb.levels : (size_t)pb.rounds;
   return 2 * sizeof(int32_t) * (size_t)pb.B * pb.H * nord * pb.N;
 }

@@ -33,6 +33,7 @@ class ElsaaConfig:
     eps: float = 1e-6
     scale: float | None = None
     hash_rounds: int = 1      # sortLSH hash tables (support = union over the rounds)
+    extra_edges: int = 0      # keys listed per query joining the sparse support
 
     @property
     def bits(self) -> int:
@@ -88,7 +89,7 @@ class ElsaaConfig:
         return _lib.Params(self.B, self.H, self.N, self.d,
                            _lib.BF16 if self.dtype == torch.bfloat16 else _lib.F32,
                            int(self.causal), self.block, self.bits, self.lr_tables, self.lr_bits,
-                           self.eff_chunk, self.tau, self.eps, sc, self.rounds)
+                           self.eff_chunk, self.tau, self.eps, sc, self.rounds, self.extra_edges)
 
 
 def _ptr(t):
@@ -208,8 +209,19 @@ def lowrank_summary(cfg: ElsaaConfig, k, v, planes_lr):
     return A, z
 
 
-def forward(cfg: ElsaaConfig, q, k, v, planes_lr, q_perm, k_perm, A, z, lam, g_s=None, g_lr=None):
-    """elsaa_fwd: returns dict(O, O_s (fp32), O_lr, lse, d_lr)."""
+def _extra_idx(cfg: ElsaaConfig, extra, dev):
+    if cfg.extra_edges == 0:
+        if extra is not None:
+            raise ValueError("extra edges given but cfg.extra_edges is 0")
+        return None
+    _check_tensor("extra", extra, (cfg.B, cfg.H, cfg.N, cfg.extra_edges), torch.int32, dev)
+    return extra
+
+
+def forward(cfg: ElsaaConfig, q, k, v, planes_lr, q_perm, k_perm, A, z, lam, g_s=None, g_lr=None,
+            extra=None):
+    """elsaa_fwd: returns dict(O, O_s (fp32), O_lr, lse, d_lr). extra: int32
+    [B,H,N,extra_edges] keys per query joining the sparse support (-1 padded)."""
     dev = q.device
     x = (cfg.B, cfg.H, cfg.N, cfg.d)
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -223,6 +235,7 @@ def forward(cfg: ElsaaConfig, q, k, v, planes_lr, q_perm, k_perm, A, z, lam, g_s
     _check_tensor("lam", lam, (cfg.H,), torch.float32, dev)
     _opt("g_s", g_s, (cfg.B, cfg.H, cfg.N), torch.float32, dev)
     _opt("g_lr", g_lr, (cfg.B, cfg.H, cfg.N), torch.float32, dev)
+    extra = _extra_idx(cfg, extra, dev)
     out = {n: torch.empty(x, dtype=cfg.dtype, device=dev) for n in ("O", "O_lr")}
     out["O_s"] = torch.empty(x, dtype=torch.float32, device=dev)
     out["lse"] = torch.empty(cfg.B, cfg.H, cfg.N, dtype=torch.float32, device=dev)
@@ -232,13 +245,14 @@ def forward(cfg: ElsaaConfig, q, k, v, planes_lr, q_perm, k_perm, A, z, lam, g_s
     _lib.check(_lib.lib().elsaa_fwd(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(planes_lr),
         _ptr(q_perm) if q_perm.numel() else None, _ptr(k_perm) if k_perm.numel() else None,
-        _ptr(A), _ptr(z), _ptr(lam), _ptr(g_s), _ptr(g_lr), _ptr(out["O"]), _ptr(out["O_s"]),
+        _ptr(extra), _ptr(A), _ptr(z), _ptr(lam), _ptr(g_s), _ptr(g_lr), _ptr(out["O"]),
+        _ptr(out["O_s"]),
         _ptr(out["O_lr"]), _ptr(out["lse"]), _ptr(out["d_lr"]), _ptr(ws), n, _stream(dev)))
     return out
 
 
 def backward(cfg: ElsaaConfig, q, k, v, do, O_s, O_lr, planes_lr, q_perm, k_perm, A, z, lse, d_lr,
-             lam, g_s=None, g_lr=None, want_dlam=True, want_dg=True):
+             lam, g_s=None, g_lr=None, want_dlam=True, want_dg=True, extra=None):
     """elsaa_bwd: returns dict(dQ, dK, dV, dlambda, dg_s, dg_lr)."""
     dev = q.device
     x = (cfg.B, cfg.H, cfg.N, cfg.d)
@@ -252,6 +266,7 @@ def backward(cfg: ElsaaConfig, q, k, v, do, O_s, O_lr, planes_lr, q_perm, k_perm
     _check_tensor("lam", lam, (cfg.H,), torch.float32, dev)
     _opt("g_s", g_s, (cfg.B, cfg.H, cfg.N), torch.float32, dev)
     _opt("g_lr", g_lr, (cfg.B, cfg.H, cfg.N), torch.float32, dev)
+    extra = _extra_idx(cfg, extra, dev)
     out = {n: torch.empty(x, dtype=cfg.dtype, device=dev) for n in ("dQ", "dK", "dV")}
     out["dlambda"] = torch.empty(cfg.H, dtype=torch.float32, device=dev) if want_dlam else None
     out["dg_s"] = torch.empty(cfg.B, cfg.H, cfg.N, dtype=torch.float32, device=dev) if want_dg else None
@@ -261,7 +276,8 @@ def backward(cfg: ElsaaConfig, q, k, v, do, O_s, O_lr, planes_lr, q_perm, k_perm
     _lib.check(_lib.lib().elsaa_bwd(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(O_s), _ptr(O_lr),
         _ptr(planes_lr), _ptr(q_perm) if q_perm.numel() else None,
-        _ptr(k_perm) if k_perm.numel() else None, _ptr(A), _ptr(z), _ptr(lse), _ptr(d_lr),
+        _ptr(k_perm) if k_perm.numel() else None, _ptr(extra), _ptr(A), _ptr(z), _ptr(lse),
+        _ptr(d_lr),
         _ptr(lam), _ptr(g_s), _ptr(g_lr), _ptr(out["dQ"]), _ptr(out["dK"]), _ptr(out["dV"]),
         _ptr(out["dlambda"]), _ptr(out["dg_s"]), _ptr(out["dg_lr"]), _ptr(ws), n,
         _stream(dev)))
@@ -306,10 +322,13 @@ class ElsaaFunction(torch.autograd.Function):
     """O = ELSAA(Q, K, V; lambda, g_s, g_lr) with gradients for Q, K, V, lambda and
     the gates; the hyperplanes are fixed inputs (no gradient). With gate_w, gate_b
     given, the gates are learned: g = sigmoid(<gate_w[h, k], Q_i> + gate_b[h, k])
-    (elsaa_gates_fwd), and gate_w, gate_b get gradients (g_s, g_lr must be None)."""
+    (elsaa_gates_fwd), and gate_w, gate_b get gradients (g_s, g_lr must be None).
+    extra: int32 [B, H, N, cfg.extra_edges] keys per query joining the sparse
+    support, or None."""
 
     @staticmethod
-    def forward(ctx, cfg, q, k, v, lam, g_s, g_lr, planes_s, planes_lr, gate_w=None, gate_b=None):
+    def forward(ctx, cfg, q, k, v, lam, g_s, g_lr, planes_s, planes_lr, gate_w=None, gate_b=None,
+                extra=None):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         learned = gate_w is not None
         if learned:
@@ -318,28 +337,30 @@ class ElsaaFunction(torch.autograd.Function):
             g_s, g_lr = gates(cfg, q, gate_w.contiguous(), gate_b.contiguous())
         _, _, qp, kp = select(cfg, q, k, planes_s)
         A, z = lowrank_summary(cfg, k, v, planes_lr)
-        out = forward(cfg, q, k, v, planes_lr, qp, kp, A, z, lam, g_s, g_lr)
+        out = forward(cfg, q, k, v, planes_lr, qp, kp, A, z, lam, g_s, g_lr, extra=extra)
         ctx.cfg = cfg
         ctx.learned = learned
         ctx.save_for_backward(q, k, v, lam, g_s, g_lr, planes_lr, qp, kp, A, z, out["O_s"],
                               out["O_lr"], out["lse"], out["d_lr"],
-                              gate_w.contiguous() if learned else None)
+                              gate_w.contiguous() if learned else None, extra)
         return out["O"]
 
     @staticmethod
     def backward(ctx, dO):
         (q, k, v, lam, g_s, g_lr, planes_lr, qp, kp, A, z, O_s, O_lr, lse, d_lr,
-         gate_w) = ctx.saved_tensors
+         gate_w, extra) = ctx.saved_tensors
         want_dg = ctx.learned or ctx.needs_input_grad[5] or ctx.needs_input_grad[6]
         g = backward(ctx.cfg, q, k, v, dO.contiguous(), O_s, O_lr, planes_lr, qp, kp, A, z, lse,
-                     d_lr, lam, g_s, g_lr, want_dlam=ctx.needs_input_grad[4], want_dg=want_dg)
+                     d_lr, lam, g_s, g_lr, want_dlam=ctx.needs_input_grad[4], want_dg=want_dg,
+                     extra=extra)
         dW = db = None
         if ctx.learned:
             dW, db = gates_backward(ctx.cfg, q, gate_w, g_s, g_lr, g["dg_s"], g["dg_lr"], g["dQ"])
-            return (None, g["dQ"], g["dK"], g["dV"], g["dlambda"], None, None, None, None, dW, db)
+            return (None, g["dQ"], g["dK"], g["dV"], g["dlambda"], None, None, None, None, dW, db,
+                    None)
         return (None, g["dQ"], g["dK"], g["dV"], g["dlambda"],
                 g["dg_s"] if ctx.needs_input_grad[5] else None,
-                g["dg_lr"] if ctx.needs_input_grad[6] else None, None, None, None, None)
+                g["dg_lr"] if ctx.needs_input_grad[6] else None, None, None, None, None, None)
 
 
 def make_planes(cfg: ElsaaConfig, seed: int = 0, device="cuda"):
@@ -353,17 +374,20 @@ def make_planes(cfg: ElsaaConfig, seed: int = 0, device="cuda"):
 def elsaa_attention(q, k, v, *, causal: bool, block: int, lr_tables: int, lam=None, g_s=None,
                     g_lr=None, planes_s=None, planes_lr=None, seed: int = 0, chunk: int = 2048,
                     hash_bits: int | None = None, tau: float = 1.0, eps: float = 1e-6,
-                    gate_w=None, gate_b=None, hash_rounds: int = 1):
+                    gate_w=None, gate_b=None, hash_rounds: int = 1, extra_idx=None):
     """ELSAA attention of q, k, v [B, H, N, d] (fp32 or bf16 device tensors). Gates:
     fixed tensors g_s, g_lr [B, H, N], or learned from the projection gate_w [H, 2, d],
-    gate_b [H, 2] of the query."""
+    gate_b [H, 2] of the query. extra_idx: int32 [B, H, N, E] keys per query that join
+    the sparse support (e.g. random edges, or topk()'s picks), -1 padded."""
     B, H, N, d = q.shape
     cfg = ElsaaConfig(B, H, N, d, q.dtype, causal, block, hash_bits, lr_tables, 4, chunk, tau, eps,
-                      hash_rounds=hash_rounds)
+                      hash_rounds=hash_rounds,
+                      extra_edges=0 if extra_idx is None else int(extra_idx.shape[-1]))
     if planes_s is None or planes_lr is None:
         ps, pl = make_planes(cfg, seed, q.device)
         planes_s = ps if planes_s is None else planes_s
         planes_lr = pl if planes_lr is None else planes_lr
     if lam is None:
         lam = torch.ones(H, dtype=torch.float32, device=q.device)
-    return ElsaaFunction.apply(cfg, q, k, v, lam, g_s, g_lr, planes_s, planes_lr, gate_w, gate_b)
+    return ElsaaFunction.apply(cfg, q, k, v, lam, g_s, g_lr, planes_s, planes_lr, gate_w, gate_b,
+                               extra_idx)

@@ -90,6 +90,7 @@ def test_valid_params_and_workspace_sizes():
     (dict(scale=float("nan")), _lib.ERR_INVALID_ARG, "scale"),
     (dict(dtype=torch.float32, d=128, block=256, N=1024), _lib.ERR_UNSUPPORTED, "LDS"),
     (dict(hash_rounds=5), _lib.ERR_UNSUPPORTED, "hash_rounds"),
+    (dict(extra_edges=65), _lib.ERR_UNSUPPORTED, "extra_edges"),
     (dict(dtype=torch.bfloat16, d=128, block=256, N=1024, hash_rounds=2), _lib.ERR_UNSUPPORTED,
      "LDS"),
     (dict(B=300, H=300), _lib.ERR_INVALID_ARG, "65535"),
@@ -138,12 +139,22 @@ def test_calls_reject_null_pointers_and_short_workspace_before_launching():
     s = L.elsaa_select(ctypes.byref(p), None, None, None, None, None, None, None, None, 0, None)
     assert s == _lib.ERR_INVALID_ARG and "NULL" in L.elsaa_last_error().decode()
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
-    args = [fake] * 16 + [None, 0, None]  # ws NULL with 0 bytes
+    args = [fake] * 17 + [None, 0, None]  # ws NULL with 0 bytes
     s = L.elsaa_fwd(ctypes.byref(p), *args)
     assert s == _lib.ERR_WORKSPACE, L.elsaa_last_error().decode()
-    args = [fake] * 5 + [None] * 11 + [None, 0, None]
+    args = [fake] * 5 + [None] * 12 + [None, 0, None]
     s = L.elsaa_fwd(ctypes.byref(p), *args)
     assert s == _lib.ERR_INVALID_ARG
+    # extra edges: the list is required when extra_edges > 0 (argument 7)
+    pe = base(extra_edges=8).params()
+    args = [fake] * 17 + [fake, 1 << 40, None]
+    args[6] = None
+    s = L.elsaa_fwd(ctypes.byref(pe), *args)
+    assert s == _lib.ERR_INVALID_ARG and "extra_idx" in L.elsaa_last_error().decode()
+    args = [fake] * 23 + [fake, 1 << 40, None]
+    args[9] = None
+    s = L.elsaa_bwd(ctypes.byref(pe), *args)
+    assert s == _lib.ERR_INVALID_ARG and "extra_idx" in L.elsaa_last_error().decode()
     s = L.elsaa_lowrank_summary(ctypes.byref(p), fake, fake, fake, fake, fake, None, 10, None)
     assert s == _lib.ERR_WORKSPACE
 
@@ -164,21 +175,21 @@ def test_misaligned_pointers_are_rejected_before_launching():
     ok = ctypes.c_void_p(0x1000)
     bad = ctypes.c_void_p(0x1008)
     # elsaa_fwd: Q misaligned
-    args = [bad] + [ok] * 15 + [ok, 1 << 40, None]
+    args = [bad] + [ok] * 16 + [ok, 1 << 40, None]
     s = L.elsaa_fwd(ctypes.byref(p), *args)
     assert s == _lib.ERR_INVALID_ARG and "aligned" in L.elsaa_last_error().decode()
-    # elsaa_fwd: optional gate g_s misaligned (argument 10)
-    args = [ok] * 16 + [ok, 1 << 40, None]
-    args[9] = bad
+    # elsaa_fwd: optional gate g_s misaligned (argument 11)
+    args = [ok] * 17 + [ok, 1 << 40, None]
+    args[10] = bad
     s = L.elsaa_fwd(ctypes.byref(p), *args)
     assert s == _lib.ERR_INVALID_ARG and "g_s" in L.elsaa_last_error().decode()
-    # elsaa_bwd: optional dg_lr misaligned (argument 22)
-    args = [ok] * 22 + [ok, 1 << 40, None]
-    args[21] = bad
+    # elsaa_bwd: optional dg_lr misaligned (argument 23)
+    args = [ok] * 23 + [ok, 1 << 40, None]
+    args[22] = bad
     s = L.elsaa_bwd(ctypes.byref(p), *args)
     assert s == _lib.ERR_INVALID_ARG and "dg_lr" in L.elsaa_last_error().decode()
     # the workspace too
-    args = [ok] * 16 + [bad, 1 << 40, None]
+    args = [ok] * 17 + [bad, 1 << 40, None]
     s = L.elsaa_fwd(ctypes.byref(p), *args)
     assert s == _lib.ERR_INVALID_ARG and "ws" in L.elsaa_last_error().decode()
     s = L.elsaa_select(ctypes.byref(p), ok, ok, ok, ok, bad, ok, ok, ok, 1 << 40, None)

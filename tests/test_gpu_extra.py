@@ -1,0 +1,178 @@
+"""GPU parity of extra edges listed per query (Appendix C's augmentation
+Omega = Omega_LSH u Omega_safe: the Bernoulli draw is the caller's and comes in
+as E keys per query) against the oracle.
+
+Each case runs select, the low-rank summary, the forward and the backward through
+the C ABI with the same list given to both sides, and compares every output and
+gradient within the usual bars (1e-4 fp32, 2e-2 bf16, max-relative; lse per
+element absolute, d_lr per element relative). The lists hold every kind of entry
+the definition covers: uniform random keys, -1 padding, keys listed twice, keys
+out of range, keys after the query (ignored when causal) and keys sortLSH already
+selects (counted once). Further cases: several hash rounds with extra edges, the
+top-k selector's picks as the list, keys that many queries list (long per-key
+lists for the backward's key-side sums), and a single causal block where every
+listed key is already held."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import ref
+from parity_util import (TOL, all_heads, cfg_of, elem_rel_err, head_arrays, lse_abs_err, rel_err,
+                         to_dev, wl)
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU containers
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+def _salt(ex: torch.Tensor, N: int) -> torch.Tensor:
+    """Out-of-range keys and keys after the query in a few entries."""
+    ex = ex.clone()
+    E = ex.shape[-1]
+    i = torch.arange(N, dtype=torch.int32)
+    if E > 2:
+        ex[..., ::2, 2] = N + 3
+    if E > 3:
+        ex[..., 3] = torch.minimum(i + 5, torch.tensor(N - 1, dtype=torch.int32))
+    return ex.contiguous()
+
+
+def _hubs(w, E):
+    """Every query lists keys 0 .. E-1 (causal: those at or before it count)."""
+    return torch.arange(E, dtype=torch.int32).expand(w.B, w.H, w.N, E).contiguous()
+
+
+# name: (workload, E, rounds, list kind)
+CASES = {
+    "causal_bf16_N1024_d128_s128_E16": (wl("c", 1, 2, 1024, 128, "bf16", True, 128, 128,
+                                           "clusters", chunk=512, n_clusters=16, sigma=0.5),
+                                        16, 1, "random"),
+    "causal_f32_N512_d64_s32_E8_R2": (wl("c", 1, 2, 512, 64, "f32", True, 32, 32, chunk=128),
+                                      8, 2, "random"),
+    "noncausal_bf16_N1024_d64_s64_E32": (wl("n", 2, 1, 1024, 64, "bf16", False, 64, 64,
+                                            "clusters_diffuse", n_clusters=16, sigma=0.5,
+                                            diffuse=0.2), 32, 1, "random"),
+    "noncausal_f32_N96_d32_s32_E5": (wl("r", 1, 1, 96, 32, "f32", False, 32, 16), 5, 1, "random"),
+    "causal_bf16_N512_d32_s16_E64": (wl("c", 1, 1, 512, 32, "bf16", True, 16, 32, chunk=128),
+                                     64, 1, "random"),
+    "causal_f32_N1024_d32_s32_hubs": (wl("h", 1, 1, 1024, 32, "f32", True, 32, 32, chunk=256),
+                                      8, 1, "hubs"),
+    "causal_f32_single_block_E4": (wl("d", 1, 1, 64, 32, "f32", True, 64, 32, chunk=64),
+                                   4, 1, "random"),
+    "causal_bf16_N512_d64_s64_topk16": (wl("t", 1, 2, 512, 64, "bf16", True, 64, 64, "clusters",
+                                           chunk=128, n_clusters=8, sigma=0.5), 16, 1, "topk"),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_extra_edges_parity(case):
+    import sparse_rank_approximation_amd as S
+    w, E, R, kind = CASES[case]
+    seed = 4300 + len(case)
+    print(f"[gpu extra] {case} {w} E={E} R={R} {kind}", flush=True)
+    inp = W.gen_inputs(w, seed)
+    if R > 1:
+        inp["planes_s"] = W.gen_planes_rounds(w, seed, R)
+    lam = W.gen_lambda(w, seed, random=True)
+    gs, glr = W.gen_gates(w, seed)
+    cfg = cfg_of(w, hash_rounds=R, extra_edges=E)
+    d = to_dev(inp)
+    if kind == "topk":
+        ex_d = S.topk(cfg, d["q"], d["k"], E)
+    else:
+        ex = _hubs(w, E) if kind == "hubs" else _salt(W.gen_extra_edges(w, seed, E), w.N)
+        ex_d = ex.cuda()
+    qc, kc, qp, kp = S.select(cfg, d["q"], d["k"], d["planes_s"])
+    A, z = S.lowrank_summary(cfg, d["k"], d["v"], d["planes_lr"])
+    lam_d = lam.to("cuda", torch.float32)
+    gs_d = gs.to("cuda", torch.float32).contiguous()
+    glr_d = glr.to("cuda", torch.float32).contiguous()
+    f = S.forward(cfg, d["q"], d["k"], d["v"], d["planes_lr"], qp, kp, A, z, lam_d, gs_d, glr_d,
+                  extra=ex_d)
+    g = S.backward(cfg, d["q"], d["k"], d["v"], d["do"], f["O_s"], f["O_lr"], d["planes_lr"], qp,
+                   kp, A, z, f["lse"], f["d_lr"], lam_d, gs_d, glr_d, extra=ex_d)
+    torch.cuda.synchronize()
+
+    heads = all_heads(w)
+    G = len(heads)
+    q, k, v, do, ps, pl = head_arrays(w, inp, heads)
+    p = ref.RefParams.from_workload(w, hash_rounds=R, extra_edges=E)
+    exh = ex_d.view(G, w.N, E).cpu().numpy()
+    lamh = np.array([float(lam[h]) for _, h in heads])
+    gsh = np.stack([gs[b, h].double().numpy() for b, h in heads])
+    glh = np.stack([glr[b, h].double().numpy() for b, h in heads])
+    o = ref.forward(p, q, k, v, ps, pl, lamh, gsh, glh, extra=exh)
+    rg = ref.backward(p, q, k, v, do, ps, pl, lamh, gsh, glh, extra=exh)
+
+    def cpu(t, shape):
+        return t.float().reshape(shape).cpu().numpy()
+
+    errs = {n: rel_err(cpu(f[n], o[n].shape), o[n]) for n in ("O", "O_s", "O_lr", "lse", "d_lr")}
+    errs["lse_elem_abs"] = lse_abs_err(cpu(f["lse"], o["lse"].shape), o["lse"])
+    errs["d_lr_elem_rel"] = elem_rel_err(cpu(f["d_lr"], o["d_lr"].shape), o["d_lr"])
+    for n in ("dQ", "dK", "dV", "dg_s", "dg_lr"):
+        errs[n] = rel_err(cpu(g[n], rg[n].shape), rg[n])
+    dl = np.zeros(w.H)
+    for (b, h), x in zip(heads, rg["dlambda"]):
+        dl[h] += x
+    errs["dlambda"] = rel_err(g["dlambda"].cpu().numpy(), dl)
+    print(f"[gpu extra] {case} errors {errs}", flush=True)
+    tol = TOL[w.dtype]
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, f"{case}: errors above {tol}: {bad}"
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_extra_edges_are_deterministic_and_held_edges_change_nothing(causal):
+    """Two backward calls on the same inputs give bitwise-equal gradients (the
+    key-side sums run in a fixed order); and a list holding only keys sortLSH
+    already selects (every query lists itself: causal, its own leaf; otherwise
+    the first key of its block in the sorted order) changes nothing beyond
+    rounding."""
+    import sparse_rank_approximation_amd as S
+    w = wl("c", 1, 2, 512, 64, "f32", causal, 64, 64, "clusters", chunk=128, n_clusters=8,
+           sigma=0.5)
+    seed = 4400 + int(causal)
+    print(f"[gpu extra] determinism causal={causal} {w}", flush=True)
+    inp = W.gen_inputs(w, seed)
+    lam = W.gen_lambda(w, seed, random=True).cuda()
+    d = to_dev(inp)
+    cfg0 = cfg_of(w)
+    cfg = cfg_of(w, extra_edges=8)
+    qc, kc, qp, kp = S.select(cfg, d["q"], d["k"], d["planes_s"])
+    A, z = S.lowrank_summary(cfg, d["k"], d["v"], d["planes_lr"])
+    ex = W.gen_extra_edges(w, seed, 8).cuda()
+
+    def run(c, e):
+        f = S.forward(c, d["q"], d["k"], d["v"], d["planes_lr"], qp, kp, A, z, lam, extra=e)
+        g = S.backward(c, d["q"], d["k"], d["v"], d["do"], f["O_s"], f["O_lr"], d["planes_lr"], qp,
+                       kp, A, z, f["lse"], f["d_lr"], lam, extra=e)
+        torch.cuda.synchronize()
+        return f, g
+
+    _, g1 = run(cfg, ex)
+    _, g2 = run(cfg, ex)
+    for n in ("dQ", "dK", "dV", "dlambda", "dg_s", "dg_lr"):
+        assert torch.equal(g1[n], g2[n]), n
+    # held edges only
+    if causal:
+        held = torch.arange(w.N, dtype=torch.int32)[:, None].expand(w.N, 8)
+        held = held.expand(w.B, w.H, w.N, 8).contiguous().cuda()
+    else:
+        first = torch.empty(w.B, w.H, w.N, dtype=torch.int32, device="cuda")
+        blk = kp.view(w.B, w.H, w.N // 64, 64)[..., :1].expand(w.B, w.H, w.N // 64, 64)
+        first.scatter_(2, qp.long(), blk.reshape(w.B, w.H, w.N).contiguous())
+        held = first[..., None].expand(w.B, w.H, w.N, 8).contiguous()
+    f0, g0 = run(cfg0, None)
+    fh, gh = run(cfg, held)
+    errs = {n: rel_err(fh[n].float().cpu().numpy(), f0[n].float().cpu().numpy())
+            for n in ("O", "O_s", "lse")}
+    for n in ("dQ", "dK", "dV", "dlambda"):
+        errs[n] = rel_err(gh[n].float().cpu().numpy(), g0[n].float().cpu().numpy())
+    print(f"[gpu extra] held-only causal={causal} differences {errs}", flush=True)
+    bad = {n: e for n, e in errs.items() if not e <= 1e-6}
+    assert not bad, bad

@@ -176,6 +176,23 @@ def gen_planes_rounds(w: Workload, seed: int, rounds: int) -> torch.Tensor:
     return torch.stack(per).contiguous()
 
 
+def gen_extra_edges(w: Workload, seed: int, E: int, pad: float = 0.25) -> torch.Tensor:
+    """Extra keys per query, int32 [B, H, N, E]: a stand-in for the Bernoulli draw
+    of Appendix C's Omega_safe. Each entry is a key drawn uniformly from the keys
+    the query may see (all N, or 0..i when causal), replaced by -1 padding with
+    probability `pad`; entry 1 repeats entry 0 (a key listed twice)."""
+    g = _gen(seed + 5, 0)
+    B, H, N = w.B, w.H, w.N
+    u = torch.rand(B, H, N, E, generator=g, dtype=torch.float64)
+    hi = (torch.arange(N, dtype=torch.float64) + 1.0)[None, None, :, None] if w.causal else float(N)
+    ex = torch.minimum(torch.floor(u * hi), torch.as_tensor(N - 1.0)).to(torch.int32)
+    drop = torch.rand(B, H, N, E, generator=g) < pad
+    ex = torch.where(drop, torch.full_like(ex, -1), ex)
+    if E > 1:
+        ex[..., 1] = ex[..., 0]
+    return ex.contiguous()
+
+
 def gen_gates(w: Workload, seed: int) -> tuple[torch.Tensor, torch.Tensor]:
     g = _gen(seed + 3, 0)
     gs = 0.5 + torch.rand(w.B, w.H, w.N, generator=g)
