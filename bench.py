@@ -31,21 +31,23 @@ PEAK_MFMA = {"bf16": 2500.0, "f32": 157.3}  # dense TFLOP/s
 PEAK_FP64_VECTOR = 78.6
 
 
-def selected_pairs(w) -> int:
-    """Query-key pairs of the sparse branch per head (the support sizes summed)."""
+def selected_pairs(w, rounds: int = 1) -> int:
+    """Query-key pairs of the sparse branch per head (the support sizes summed).
+    With several hash rounds, the pairs of every round's blocks (the kernels form
+    each round's blocks in full and mask the pairs an earlier round holds)."""
     if not w.causal:
-        return w.N * w.block
+        return rounds * w.N * w.block
     lv = int(round(math.log2(w.N // w.block)))
-    return lv * (w.N // 2) * w.block + w.N * (w.block + 1) // 2
+    return rounds * lv * (w.N // 2) * w.block + w.N * (w.block + 1) // 2
 
 
-def kernel_work(w) -> dict:
+def kernel_work(w, rounds: int = 1) -> dict:
     """Algorithmic work per launch of each kernel: (bound, amount, unit).
     Flops count the contractions the method needs (not masked-tile waste or
     recomputation); bytes count compulsory reads and writes of that kernel."""
     BH, N, d, r = w.B * w.H, w.N, w.d, w.r
     e = 2 if w.dtype == "bf16" else 4
-    pairs = selected_pairs(w) * BH
+    pairs = selected_pairs(w, rounds) * BH
     tok = BH * N
     return {
         "sparse_fwd": ("mfma", 4.0 * d * pairs, "TFLOP/s"),
@@ -61,7 +63,7 @@ def kernel_work(w) -> dict:
     }
 
 
-def step_work(w) -> tuple[float, float]:
+def step_work(w, rounds: int = 1) -> tuple[float, float]:
     """Algorithmic flops and bytes of one fwd+bwd step over the whole batch.
     Flops: 4 d per selected pair in the forward and 8 d in the backward; per token
     4 r (d + 1) + 4 d L gamma for the low-rank branch in the forward, twice that in
@@ -72,15 +74,15 @@ def step_work(w) -> tuple[float, float]:
     BH, N, d, r = w.B * w.H, w.N, w.d, w.r
     e = 2 if w.dtype == "bf16" else 4
     tok = BH * N
-    perm_len = w.levels * (N // 2) if w.causal else N
-    flops = 12.0 * d * selected_pairs(w) * BH
+    perm_len = rounds * (w.levels * (N // 2) if w.causal else N)
+    flops = 12.0 * d * selected_pairs(w, rounds) * BH
     flops += 3.0 * tok * (4.0 * r * (d + 1) + 4.0 * d * w.lr_tables * w.lr_bits)
     nbytes = tok * (12.0 * d * e + 16.0 + 4.0 + 3.0 * 8.0 * perm_len / N)
     return flops, nbytes
 
 
-def roofline(name, launches, total_ms, w, traffic_file):
-    work = kernel_work(w)
+def roofline(name, launches, total_ms, w, traffic_file, rounds: int = 1):
+    work = kernel_work(w, rounds)
     if name not in work:
         return None
     bound, amount, unit = work[name]
@@ -198,6 +200,10 @@ def main():
                          "_bwd in every step) instead of unit gates")
     ap.add_argument("--chunk", type=int, default=0,
                     help="causal RACE summary spacing (numerics-neutral); 0 keeps the workload's")
+    ap.add_argument("--hash-rounds", type=int, default=1,
+                    help="sortLSH hash rounds (the sparse support is the union of theirs)")
+    ap.add_argument("--extra-edges", type=int, default=0,
+                    help="random extra keys listed per query (Omega_safe) joining the support")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -224,7 +230,11 @@ def main():
     print(f"[bench] inputs for {w.name} ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr,
           flush=True)
     cfg = S.ElsaaConfig(w.B, w.H, w.N, w.d, w.torch_dtype, w.causal, w.block, w.hash_bits,
-                        w.lr_tables, w.lr_bits, w.chunk)
+                        w.lr_tables, w.lr_bits, w.chunk, hash_rounds=args.hash_rounds,
+                        extra_edges=args.extra_edges)
+    if args.hash_rounds > 1:
+        d["planes_s"] = W.gen_planes_rounds(w, seed, args.hash_rounds).to(dev)
+    extra = W.gen_extra_edges(w, seed, args.extra_edges).to(dev) if args.extra_edges else None
     lam = torch.ones(w.H, dtype=torch.float32, device=dev)
     gen = torch.Generator().manual_seed(seed + 5)
     gate_w = (0.2 * torch.randn(w.H, 2, w.d, generator=gen)).to(dev)
@@ -236,9 +246,10 @@ def main():
             gs, gl = S.gates(cfg, d["q"], gate_w, gate_b)
         _, _, qp, kp = S.select(cfg, d["q"], d["k"], d["planes_s"])
         A, z = S.lowrank_summary(cfg, d["k"], d["v"], d["planes_lr"])
-        o = S.forward(cfg, d["q"], d["k"], d["v"], d["planes_lr"], qp, kp, A, z, lam, gs, gl)
+        o = S.forward(cfg, d["q"], d["k"], d["v"], d["planes_lr"], qp, kp, A, z, lam, gs, gl,
+                      extra=extra)
         g = S.backward(cfg, d["q"], d["k"], d["v"], d["do"], o["O_s"], o["O_lr"], d["planes_lr"],
-                       qp, kp, A, z, o["lse"], o["d_lr"], lam, gs, gl)
+                       qp, kp, A, z, o["lse"], o["d_lr"], lam, gs, gl, extra=extra)
         if args.learned_gates:
             S.gates_backward(cfg, d["q"], gate_w, gs, gl, g["dg_s"], g["dg_lr"], g["dQ"])
 
@@ -273,10 +284,10 @@ def main():
                    "ms_per_step": round(t / psteps, 3)} for k, (n, t) in sorted(rep.items())}
     dom = max(rep, key=lambda k: rep[k][1])
     roof = roofline(dom, rep[dom][0], rep[dom][1], w,
-                    os.path.join(ROOT, "profiles", "traffic.json"))
+                    os.path.join(ROOT, "profiles", "traffic.json"), args.hash_rounds)
     if roof is None:
         roof = {"kernel": dom, "avg_launch_us": round(rep[dom][1] / rep[dom][0] * 1e3, 1)}
-    f_alg, b_alg = step_work(w)
+    f_alg, b_alg = step_work(w, args.hash_rounds)
     t_roof = max(f_alg / (PEAK_MFMA[w.dtype] * 1e12), b_alg / (PEAK_HBM_GBS * 1e9))
     roof["step_frac"] = round(t_roof / (ms / 1e3), 4)
     roof["step"] = {"flops": f_alg, "bytes": b_alg, "t_roof_us": round(t_roof * 1e6, 1),
@@ -285,7 +296,8 @@ def main():
     print("[bench] profiled; kernels: " + json.dumps(kernels), file=sys.stderr, flush=True)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    # (the oracle leg times the headline operator; the variants are GPU-only runs)
+    if not args.no_cpu_baseline and args.hash_rounds == 1 and args.extra_edges == 0:
         cpu = cpu_baseline(w, seed, min(args.cpu_heads, w.B * w.H), threads)
 
     out = {
@@ -296,6 +308,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d_h": w.d,
                    "causal": w.causal, "block": w.block, "r": w.r, "hash_bits": w.hash_bits,
                    "chunk": w.chunk, "gates": "learned" if args.learned_gates else "unit",
+                   "hash_rounds": args.hash_rounds, "extra_edges": args.extra_edges,
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "none"},
         "roofline": roof,
         "kernels": kernels,

@@ -538,7 +538,8 @@ struct Sb2Smem {
   __bf16 Ks[KT][LD];
   __bf16 dST[KT][LDK];  // dS^T, [key][query]
   // Several hash rounds: the rows' block indices in the earlier rounds' orders.
-  int qbe[MR ? kMaxRounds - 1 : 1][MR ? KT : 1], kbe[MR ? kMaxRounds - 1 : 1][MR ? KT : 1];
+  alignas(16) int qbe[MR ? kMaxRounds - 1 : 1][MR ? KT : 1];
+  int kbe[MR ? kMaxRounds - 1 : 1][MR ? KT : 1];
 };
 
 template <int D, int SB, bool MR>
@@ -601,8 +602,12 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
   typename M::frag pv[KS];
   float plse = 0.0f, pD = 0.0f, pc = 0.0f, psig = 0.0f;
   bool pvalid = false;
+  int pqb[kMaxRounds - 1], pkb[kMaxRounds - 1];  // (several rounds) block indices
   Rows prow{-1, -1, -1};
-  auto gather = [&](size_t rb) __attribute__((always_inline)) {
+  auto gather = [&](int gn) __attribute__((always_inline)) {
+    int itn;
+    const int bhn = xcd_item(gn, items, per_level, nord, itn);
+    const size_t rb = (size_t)bhn * N;
 #pragma unroll
     for (int i = 0; i < GIT; ++i) {
       const int piece = tid + NT * i, r = piece / CH, c8 = (piece % CH) * 8;
@@ -622,6 +627,25 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
       pc = rc[k];
       psig = rsig[k];
     }
+    if constexpr (MR) {
+      // The row's block indices in the earlier rounds' orders of the next block's
+      // level (used by threads tid < KT).
+      const bool lfn = causal && itn >= nlev;
+      const int ordn = lfn ? -1 : causal ? itn / per_level : itn / (N / SB);
+      const int levn = causal && ordn >= 0 ? ordn % levels : 0;
+      const int rndn = ordn < 0 ? 0 : causal ? ordn / levels : ordn;
+      const int qi = sm.qnext[tid % KT], kj = sm.knext[tid % KT];
+#pragma unroll
+      for (int r = 0; r < kMaxRounds - 1; ++r) {
+        pqb[r] = -1;
+        pkb[r] = -2;
+        if (r < rndn) {
+          const size_t base = ((size_t)bhn * nord + (causal ? r * levels + levn : r)) * N;
+          if (qi >= 0) pqb[r] = qbid[base + qi];
+          if (kj >= 0) pkb[r] = kbid[base + kj];
+        }
+      }
+    }
   };
 
   // V rows of the next block's keys of this wave, as MFMA operands (issued once
@@ -639,7 +663,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
     sm.knext[tid] = r0.alt < -1 ? r0.b : r0.alt;
   }
   __syncthreads();
-  gather((size_t)head_of(g) * N);
+  gather(g);
   // Past the last block, the prefetches repeat the last block (never used).
   prow = rows_of(min(g + G, total - 1), tid);
   gather_v((size_t)head_of(g) * N);
@@ -663,6 +687,13 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
       sm.Dd[tid] = pvalid ? pD : 0.0f;
       sm.cq[tid] = pvalid ? pc : 0.0f;
       sm.sig[tid] = pvalid ? psig : 0.0f;
+      if constexpr (MR) {
+#pragma unroll
+        for (int r = 0; r < kMaxRounds - 1; ++r) {
+          sm.qbe[r][tid] = pqb[r];
+          sm.kbe[r][tid] = pkb[r];
+        }
+      }
     }
 
     int it;
@@ -675,18 +706,9 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
     // The query's own block (its causal leaf, or its first round's block) adds
     // sigma_i Q_i to its dQ part.
     const bool own = causal ? leaf : rnd == 0;
-    if constexpr (MR) {
-      // Several rounds: the rows' block indices in the earlier rounds' orders of
-      // the same level (a pair they share a block in is held there, not here).
-      if (rnd > 0 && tid < KT) {
-        const int rq = sm.qidx[tid], rk = sm.kidx[tid];
-        for (int r = 0; r < rnd; ++r) {
-          const size_t base = ((size_t)bh * nord + (causal ? r * levels + lev : r)) * N;
-          sm.qbe[r][tid] = rq >= 0 ? qbid[base + rq] : -1;
-          sm.kbe[r][tid] = rk >= 0 ? kbid[base + rk] : -2;
-        }
-      }
-    }
+    // (several rounds: the rows' block indices in the earlier rounds' orders of the
+    // same level, staged above from the prefetch; a pair that shares a block there
+    // is held there, not here)
     __syncthreads();
     // Phase 1: key wave w.
     const int key = 32 * w + col;
@@ -694,16 +716,39 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
     {
       const int jk = sm.kidx[key];
       const bool kvalid = jk >= 0;
-      int kbr[kMaxRounds - 1];
+      // Several rounds: bit v of dup[qt] marks the pair (row v of query tile qt,
+      // this lane's key) as one an earlier round holds; formed for all tiles at
+      // once so that the LDS reads are in flight together, not in the softmax.
+      uint32_t dup[NW];
 #pragma unroll
-      for (int r = 0; r < kMaxRounds - 1; ++r) kbr[r] = MR && r < rnd ? sm.kbe[MR ? r : 0][key % KT] : -2;
+      for (int qt = 0; qt < NW; ++qt) dup[qt] = 0u;
+      if constexpr (MR) {
+        if (rnd > 0) {
+#pragma unroll
+          for (int r = 0; r < kMaxRounds - 1; ++r)
+            if (r < rnd) {
+              const int kb = sm.kbe[r][key % KT];
+#pragma unroll
+              for (int qt = 0; qt < NW; ++qt)
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg) {
+                  const int4 q4 =
+                      *reinterpret_cast<const int4*>(&sm.qbe[r][32 * qt + 8 * gg + 4 * h]);
+                  const int qe[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+                  for (int e = 0; e < 4; ++e)
+                    if (qe[e] == kb) dup[qt] |= 1u << (4 * gg + e);
+                }
+            }
+        }
+      }
       const float c2 = scale * kLog2e;  // P = 2^(c2 S - lse log2 e)
       typename M::frag kf[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kf[ks] = row_frag<T>(&sm.Ks[0][0], LD, 32 * w, 0, ks, lane);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) dv[dt] = dk[dt] = zero16();
-      auto qtile = [&](int qt) __attribute__((always_inline)) {
+      auto qtile = [&](int qt, uint32_t dq) __attribute__((always_inline)) {
         floatx16 s = zero16(), dp = zero16();
         // Fragments read KB k-steps at a time so that their LDS reads overlap.
         constexpr int KB = KS < 4 ? KS : 4;
@@ -733,11 +778,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
             const int v = 4 * gg + e;
             // Masked pairs get exp(-inf) = 0 (no branch around the exponential).
             bool ok = kvalid & !(leaf & (key > r0 + e));
-            if constexpr (MR) {
-#pragma unroll
-              for (int r = 0; r < kMaxRounds - 1; ++r)
-                ok = ok && !(r < rnd && sm.qbe[r][r0 + e] == kbr[r]);
-            }
+            if constexpr (MR) ok = ok && !((dq >> v) & 1u);
             const float p = __builtin_amdgcn_exp2f(ok ? fmaf(s[v], c2, -L4[e]) : -INFINITY);
             dsv[e] = p * (C4[e] * dp[v] - D4[e]);
             s[v] = C4[e] * p;
@@ -759,17 +800,18 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
       // Leaf blocks: query tiles from the diagonal on; otherwise all of them, the
       // loop unrolled so that one tile's products overlap the next tile's reads.
       if (leaf) {
-        for (int qt = w; qt < NW; ++qt) qtile(qt);
+        for (int qt = w; qt < NW; ++qt) qtile(qt, 0u);  // (a leaf is in every round)
       } else {
 #pragma unroll
-        for (int qt = 0; qt < NW; ++qt) qtile(qt);
+        for (int qt = 0; qt < NW; ++qt) qtile(qt, dup[qt]);
       }
     }
     // Loads for the next block (rows, issued now that phase 1 no longer needs the
     // registers; phase 2 and the stores cover their latency) and the one after
     // (indices).
-    const size_t nrb = (size_t)head_of(min(g + G, total - 1)) * N;
-    gather(nrb);
+    const int gn = min(g + G, total - 1);
+    const size_t nrb = (size_t)head_of(gn) * N;
+    gather(gn);
     prow = rows_of(min(g + 2 * G, total - 1), tid);
     gather_v(nrb);
     // The rows of phase 2's query tile (for the dQ parts relative to the query),

@@ -37,7 +37,7 @@ template <typename T, int D, int SB, bool MR = false>
 constexpr size_t sparse_fwd_lds() {
   constexpr int KT = SB < 32 ? 32 : SB;
   return sizeof(T) * 2 * (size_t)KT * tile_ld<T>(D) +
-         sizeof(int) * (5 + (MR ? 2 * (kMaxRounds - 1) : 0)) * KT;
+         sizeof(int) * (5 + (MR ? kMaxRounds - 1 : 0)) * KT;
 }
 
 // Persistent workgroups take the selected blocks g, g + G, g + 2G, ... (G = grid
@@ -47,9 +47,10 @@ constexpr size_t sparse_fwd_lds() {
 // bf16: two workgroups per CU (two waves per SIMD) is what the LDS allows; the
 // register budget is held to it.
 // MR: several hash rounds (the pair test against the earlier rounds' blocks and
-// its LDS are compiled only then).
+// its LDS are compiled only then; a lane keeps its query's block indices in
+// registers and only the keys' go to LDS, so that two workgroups still fit).
 template <typename T, int D, int SB, bool MR>
-__global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 && !MR ? 2 : 1)
+__global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 ? 2 : 1)
     sparse_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                       const int32_t* __restrict__ qperm, const int32_t* __restrict__ kperm, int N,
                       int causal, int levels, int rounds, const int32_t* __restrict__ qbid,
@@ -63,8 +64,8 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 &
   __shared__ T Vs[KT][LD];
   __shared__ int kix[2][KT], qix[2][KT];  // key / query token of each row, by block parity
   __shared__ int oslot[KT];               // output slot of each query row
-  // Block indices of the rows in the earlier rounds' orders (several rounds only).
-  __shared__ int qbe[MR ? kMaxRounds - 1 : 1][MR ? KT : 1], kbe[MR ? kMaxRounds - 1 : 1][MR ? KT : 1];
+  // Block indices of the key rows in the earlier rounds' orders (several rounds only).
+  __shared__ __align__(16) int kbe[MR ? kMaxRounds - 1 : 1][MR ? KT : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int w = wave_id();  // wave index, uniform (scalar) so that role branches stay uniform
@@ -123,16 +124,22 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 &
     typename M::frag qf[D / M::KSTEP];
     prefetch_row_frags<T, D>(Q + ((size_t)bh * N + qi) * D, qf, h);
     // Several rounds: the rows' block indices in the earlier rounds' orders of the
-    // same level (a pair they share a block in is held there, not here).
+    // same level (a pair they share a block in is held there, not here): this
+    // lane's query's to registers, the keys' to LDS. Their loads go out before
+    // the row gathers, and the keys' reach LDS after them, so that no wait for
+    // them holds up the gathers.
+    int qbr[kMaxRounds - 1], kbv[kMaxRounds - 1];
+#pragma unroll
+    for (int r = 0; r < kMaxRounds - 1; ++r) qbr[r] = kbv[r] = -2;
     if constexpr (MR) {
-      if (rnd > 0 && tid < KT) {
-        const int rq = qix[par][tid], rk = kix[par][tid];
-        for (int r = 0; r < rnd; ++r) {
+      const int rk = tid < KT ? kix[par][tid] : -1;
+#pragma unroll
+      for (int r = 0; r < kMaxRounds - 1; ++r)
+        if (r < rnd) {
           const size_t base = ((size_t)bh * nord + (causal ? r * levels + lev : r)) * N;
-          qbe[r][tid] = rq >= 0 ? qbid[base + rq] : -1;
-          kbe[r][tid] = rk >= 0 ? kbid[base + rk] : -2;
+          qbr[r] = qbid[base + qi];
+          if (rk >= 0) kbv[r] = kbid[base + rk];
         }
-      }
     }
     {
       T* const dst[2] = {&Ks[0][0], &Vs[0][0]};
@@ -140,11 +147,13 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 &
       const float* const sc[2] = {nullptr, nullptr};
       gather_rows<T, D, KT, NT, 2>(dst, LD, src, sc, kix[par], (size_t)bh * N, tid);
     }
+    if constexpr (MR) {
+      if (tid < KT)
+#pragma unroll
+        for (int r = 0; r < kMaxRounds - 1; ++r) kbe[r][tid] = kbv[r];
+    }
     __syncthreads();
     put_idx(par ^ 1, nx);
-    int qbr[kMaxRounds - 1];
-#pragma unroll
-    for (int r = 0; r < kMaxRounds - 1; ++r) qbr[r] = MR && r < rnd ? qbe[MR ? r : 0][qloc % KT] : -1;
 
     floatx16 o[D / 32];
 #pragma unroll
@@ -156,7 +165,30 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 &
     // first move no maximum).
     float mrun = -INFINITY, lrun = 0.0f;
     const float c2 = scale * kLog2e;
-    auto ktile = [&](int kt) __attribute__((always_inline)) {
+    // Several rounds: bit v of dup[kt] marks the pair (this lane's query, row v of
+    // key tile kt) as one an earlier round holds; formed for all tiles at once so
+    // that the LDS reads are in flight together, not in the softmax.
+    uint32_t dup[KT / 32];
+#pragma unroll
+    for (int kt = 0; kt < KT / 32; ++kt) dup[kt] = 0u;
+    if constexpr (MR) {
+      if (rnd > 0) {
+#pragma unroll
+        for (int r = 0; r < kMaxRounds - 1; ++r)
+          if (r < rnd)
+#pragma unroll
+            for (int kt = 0; kt < KT / 32; ++kt)
+#pragma unroll
+              for (int gg = 0; gg < 4; ++gg) {
+                const int4 kb = *reinterpret_cast<const int4*>(&kbe[r][32 * kt + 8 * gg + 4 * h]);
+                const int ke[4] = {kb.x, kb.y, kb.z, kb.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (ke[e] == qbr[r]) dup[kt] |= 1u << (4 * gg + e);
+              }
+      }
+    }
+    auto ktile = [&](int kt, uint32_t dk) __attribute__((always_inline)) {
       floatx16 sacc = zero16();
 #pragma unroll
       for (int ks = 0; ks < D / M::KSTEP; ++ks)
@@ -166,11 +198,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 &
       for (int v = 0; v < 16; ++v) {
         const int kr = 32 * kt + acc_row(v, h);
         bool masked = kr >= SB || (leaf && kr > qloc);
-        if constexpr (MR) {
-#pragma unroll
-          for (int r = 0; r < kMaxRounds - 1; ++r)
-            masked = masked || (r < rnd && qbr[r] == kbe[r][kr % KT]);
-        }
+        if constexpr (MR) masked = masked || ((dk >> v) & 1u);
         sacc[v] = masked ? -INFINITY : sacc[v] * c2;
         mx = fmaxf(mx, sacc[v]);
       }
@@ -207,10 +235,10 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 &
     // Causal leaf: key tiles up to the diagonal; otherwise all of them, unrolled so
     // that one tile's scores can be formed while the previous tile's softmax runs.
     if (leaf) {
-      for (int kt = 0; kt <= w; ++kt) ktile(kt);
+      for (int kt = 0; kt <= w; ++kt) ktile(kt, 0u);  // (a leaf is in every round)
     } else {
 #pragma unroll
-      for (int kt = 0; kt < KT / 32; ++kt) ktile(kt);
+      for (int kt = 0; kt < KT / 32; ++kt) ktile(kt, dup[kt]);
     }
 
     // The normalized output tile goes to LDS as rows (one per query, over the key
