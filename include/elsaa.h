@@ -81,7 +81,8 @@ typedef enum {
   ELSAA_CALL_SUMMARY = 1,
   ELSAA_CALL_FWD = 2,
   ELSAA_CALL_BWD = 3,
-  ELSAA_CALL_GATES_BWD = 4
+  ELSAA_CALL_GATES_BWD = 4,
+  ELSAA_CALL_CHECK = 5
 } elsaa_call;
 
 /* Problem description.
@@ -289,6 +290,30 @@ elsaa_status elsaa_profile_report(char* buf, size_t len, size_t* needed);
 
 /* Message for the last non-OK status returned on this host thread ("" if none). */
 const char* elsaa_last_error(void);
+
+/* Debug check of selection orders, for callers that build or modify q_perm /
+ * k_perm themselves (the sparse kernels index rows by them without bounds
+ * checks). For every order (round, and level when causal) of every head: each
+ * entry must be a token of the range its position stands for (non-causal: 0..N-1;
+ * causal level l: the future half [a + n/2, a + n) for q_perm, the past half
+ * [a, a + n/2) for k_perm, of its segment of n = N >> l tokens at a), and each
+ * range must hold each of its tokens exactly once.
+ *   bad (out) : int32 [B * H], the number of violations found in each head's
+ *               orders (entries out of range plus tokens missing or repeated);
+ *               0 for valid orders.
+ *   ws        : elsaa_workspace_size(p, ELSAA_CALL_CHECK) bytes.
+ * With the environment variable ELSAA_CHECK_ORDERS set to 1, elsaa_fwd and
+ * elsaa_bwd run this check first, wait for it, and return ELSAA_ERR_INVALID_ARG
+ * without launching their kernels if any head's orders are invalid (a debugging
+ * aid: it synchronizes the stream, so it does not suit graph capture).
+ * Likewise ELSAA_CHECK_FINITE=1 makes them count the NaN and infinite entries of
+ * Q, K, V (and dO) first and return ELSAA_ERR_INVALID_ARG, naming the tensor, if
+ * there are any. Without it such values propagate: a non-finite key or value
+ * reaches every query whose support or low-rank sums include it, a non-finite
+ * query only its own outputs. */
+elsaa_status elsaa_check_orders(const elsaa_params* p, const int32_t* q_perm,
+                                const int32_t* k_perm, int32_t* bad, void* ws, size_t ws_bytes,
+                                void* stream);
 
 #ifdef __cplusplus
 }

@@ -8,7 +8,9 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
+#include <vector>
 
 #include "elsaa.h"
 #include "launch.hpp"
@@ -160,6 +162,7 @@ size_t ws_bytes_for(const Problem& pb, int call) {
     case ELSAA_CALL_FWD: return elsaa::fwd_ws_bytes(pb);
     case ELSAA_CALL_BWD: return elsaa::bwd_ws_bytes(pb);
     case ELSAA_CALL_GATES_BWD: return elsaa::gates_bwd_ws_bytes(pb);
+    case ELSAA_CALL_CHECK: return elsaa::check_ws_bytes(pb);
     default: return 0;
   }
 }
@@ -179,6 +182,53 @@ elsaa_status launched() {
   return ELSAA_OK;
 }
 
+// Debug mode (ELSAA_CHECK_ORDERS=1): check the orders on the stream, wait, and
+// fail the call if any head's are invalid. The workspace of elsaa_fwd / elsaa_bwd
+// (at least the partial slots, B H N (d_h e + 4) bytes) holds the counts and the
+// per-token counters.
+elsaa_status debug_check_orders(const Problem& pb, const int32_t* qperm, const int32_t* kperm,
+                                void* ws, hipStream_t st) {
+  const char* e = getenv("ELSAA_CHECK_ORDERS");
+  if (!e || e[0] != '1' || elsaa::perm_stride(pb.N, pb.levels, pb.causal, pb.rounds) == 0)
+    return ELSAA_OK;
+  const size_t BH = (size_t)pb.B * pb.H;
+  int32_t* bad = (int32_t*)ws;
+  int32_t* mark = (int32_t*)((char*)ws + ((BH * sizeof(int32_t) + 255) & ~(size_t)255));
+  elsaa::launch_check_orders(pb, qperm, kperm, bad, mark, st);
+  std::vector<int32_t> h(BH);
+  hipError_t err = hipMemcpyAsync(h.data(), bad, BH * sizeof(int32_t), hipMemcpyDeviceToHost, st);
+  if (err == hipSuccess) err = hipStreamSynchronize(st);
+  if (err != hipSuccess)
+    return fail(ELSAA_ERR_HIP, "order check failed: %s", hipGetErrorString(err));
+  for (size_t bh = 0; bh < BH; ++bh)
+    if (h[bh] != 0)
+      return fail(ELSAA_ERR_INVALID_ARG,
+                  "q_perm / k_perm of head %zu (b %zu, h %zu) break the order layout: %d "
+                  "violations (ELSAA_CHECK_ORDERS)",
+                  bh, bh / pb.H, bh % pb.H, h[bh]);
+  return ELSAA_OK;
+}
+
+// Debug mode (ELSAA_CHECK_FINITE=1): count the NaN / infinite entries of the
+// input tensors on the stream, wait, and fail the call if there are any.
+elsaa_status debug_check_finite(const Problem& pb, const void* const* xs, const char* const* names,
+                                int nx, void* ws, hipStream_t st) {
+  const char* e = getenv("ELSAA_CHECK_FINITE");
+  if (!e || e[0] != '1') return ELSAA_OK;
+  int32_t* counts = (int32_t*)ws;
+  elsaa::launch_finite_count(pb, xs, nx, counts, st);
+  std::vector<int32_t> h(nx);
+  hipError_t err = hipMemcpyAsync(h.data(), counts, nx * sizeof(int32_t), hipMemcpyDeviceToHost, st);
+  if (err == hipSuccess) err = hipStreamSynchronize(st);
+  if (err != hipSuccess)
+    return fail(ELSAA_ERR_HIP, "finite check failed: %s", hipGetErrorString(err));
+  for (int i = 0; i < nx; ++i)
+    if (h[i] != 0)
+      return fail(ELSAA_ERR_INVALID_ARG, "%s holds %d NaN or infinite entries (ELSAA_CHECK_FINITE)",
+                  names[i], h[i]);
+  return ELSAA_OK;
+}
+
 #define PROLOGUE(call)                                   \
   Problem pb;                                            \
   bool empty;                                            \
@@ -193,7 +243,7 @@ extern "C" {
 
 elsaa_status elsaa_workspace_size(const elsaa_params* p, int32_t call, size_t* bytes) {
   if (!bytes) return fail(ELSAA_ERR_INVALID_ARG, "bytes is NULL");
-  if (call < ELSAA_CALL_SELECT || call > ELSAA_CALL_GATES_BWD)
+  if (call < ELSAA_CALL_SELECT || call > ELSAA_CALL_CHECK)
     return fail(ELSAA_ERR_INVALID_ARG, "unknown call %d", call);
   PROLOGUE(call);
   *bytes = empty ? 0 : ws_bytes_for(pb, call);
@@ -279,6 +329,14 @@ elsaa_status elsaa_fwd(const elsaa_params* p, const void* Q, const void* K, cons
   if (!elsaa::launch_fwd(pb, Q, K, V, planes_lr, q_perm, k_perm, A, z, lambda, g_s, g_lr,
                          extra_idx, O, O_s, O_lr, lse_s, d_lr, ws, (hipStream_t)stream, true))
     return fail(ELSAA_ERR_UNSUPPORTED, "no forward kernel variant is built for these sizes");
+  {
+    elsaa_status s_ = debug_check_orders(pb, q_perm, k_perm, ws, (hipStream_t)stream);
+    if (s_ != ELSAA_OK) return s_;
+    const void* xs[3] = {Q, K, V};
+    const char* names[3] = {"Q", "K", "V"};
+    s_ = debug_check_finite(pb, xs, names, 3, ws, (hipStream_t)stream);
+    if (s_ != ELSAA_OK) return s_;
+  }
   elsaa::launch_fwd(pb, Q, K, V, planes_lr, q_perm, k_perm, A, z, lambda, g_s, g_lr, extra_idx, O,
                     O_s, O_lr, lse_s, d_lr, ws, (hipStream_t)stream, false);
   return launched();
@@ -309,9 +367,33 @@ elsaa_status elsaa_bwd(const elsaa_params* p, const void* Q, const void* K, cons
                          lambda, g_s, g_lr, extra_idx, dQ, dK, dV, dlambda, dg_s, dg_lr, ws,
                          (hipStream_t)stream, true))
     return fail(ELSAA_ERR_UNSUPPORTED, "no backward kernel variant is built for these sizes");
+  {
+    elsaa_status s_ = debug_check_orders(pb, q_perm, k_perm, ws, (hipStream_t)stream);
+    if (s_ != ELSAA_OK) return s_;
+    const void* xs[4] = {Q, K, V, dO};
+    const char* names[4] = {"Q", "K", "V", "dO"};
+    s_ = debug_check_finite(pb, xs, names, 4, ws, (hipStream_t)stream);
+    if (s_ != ELSAA_OK) return s_;
+  }
   elsaa::launch_bwd(pb, Q, K, V, dO, O_s, O_lr, planes_lr, q_perm, k_perm, A, z, lse_s, d_lr,
                     lambda, g_s, g_lr, extra_idx, dQ, dK, dV, dlambda, dg_s, dg_lr, ws,
                     (hipStream_t)stream, false);
+  return launched();
+}
+
+elsaa_status elsaa_check_orders(const elsaa_params* p, const int32_t* q_perm,
+                                const int32_t* k_perm, int32_t* bad, void* ws, size_t ws_bytes,
+                                void* stream) {
+  PROLOGUE(ELSAA_CALL_CHECK);
+  if (empty) return ELSAA_OK;
+  if (elsaa::perm_stride(pb.N, pb.levels, pb.causal, pb.rounds) > 0) { NEED(q_perm); NEED(k_perm); }
+  OPTIONAL(q_perm); OPTIONAL(k_perm);
+  NEED(bad);
+  {
+    elsaa_status s_ = check_ws(pb, ELSAA_CALL_CHECK, ws, ws_bytes);
+    if (s_ != ELSAA_OK) return s_;
+  }
+  elsaa::launch_check_orders(pb, q_perm, k_perm, bad, (int32_t*)ws, (hipStream_t)stream);
   return launched();
 }
 

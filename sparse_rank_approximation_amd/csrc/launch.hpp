@@ -171,6 +171,14 @@ void prof_suspend(bool on);
   } while (0)
 
 size_t select_ws_bytes(const Problem& pb);
+// Debug check of the orders (check.hip): per head, the number of entries that
+// break the order layout, into bad[B H]; mark: B H N counters of workspace.
+size_t check_ws_bytes(const Problem& pb);
+void launch_check_orders(const Problem& pb, const int32_t* qperm, const int32_t* kperm,
+                         int32_t* bad, int32_t* mark, hipStream_t st);
+// The number of NaN and infinite entries of each of nx [B H N d] tensors.
+void launch_finite_count(const Problem& pb, const void* const* xs, int nx, int32_t* counts,
+                         hipStream_t st);
 // Per-token block indices of every (round, level) order (select.hip), used by the
 // sparse kernels to count each pair once over several hash rounds, and to keep
 // extra edges sortLSH already selects out; bytes of the two arrays (0 with one

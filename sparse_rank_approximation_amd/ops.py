@@ -176,6 +176,22 @@ def select_noalloc(cfg: ElsaaConfig, q, k, planes_s, out=None):
     return qc, kc, qp, kp
 
 
+def check_orders(cfg: ElsaaConfig, q_perm, k_perm):
+    """elsaa_check_orders: int32 [B, H], the number of entries of each head's orders
+    that break the order layout (0 for orders elsaa_select wrote)."""
+    dev = q_perm.device
+    _check_tensor("q_perm", q_perm, (cfg.B, cfg.H, cfg.perm_len), torch.int32, dev)
+    _check_tensor("k_perm", k_perm, (cfg.B, cfg.H, cfg.perm_len), torch.int32, dev)
+    bad = torch.empty(cfg.B, cfg.H, dtype=torch.int32, device=dev)
+    ws, n = _workspace(cfg, _lib.CALL_CHECK, dev)
+    p = cfg.params()
+    _lib.check(_lib.lib().elsaa_check_orders(ctypes.byref(p),
+                                             _ptr(q_perm) if q_perm.numel() else None,
+                                             _ptr(k_perm) if k_perm.numel() else None,
+                                             _ptr(bad), _ptr(ws), n, _stream(dev)))
+    return bad
+
+
 def topk(cfg: ElsaaConfig, q, k, k_top: int):
     """elsaa_topk: exact per-query top-k keys on Q K^T, int32 [B,H,N,k_top] ascending,
     -1 padded (causal: keys j <= i)."""

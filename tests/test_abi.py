@@ -61,7 +61,7 @@ def status_of(cfg_or_params, call=_lib.CALL_FWD):
 
 
 def test_valid_params_and_workspace_sizes():
-    for call in range(5):
+    for call in range(6):
         s, msg, n = status_of(base(), call)
         assert s == _lib.OK, msg
     # select: the hyperplanes widened to fp64, [H, hash_bits, d_h], 256-byte rounded
@@ -157,6 +157,19 @@ def test_calls_reject_null_pointers_and_short_workspace_before_launching():
     assert s == _lib.ERR_INVALID_ARG and "extra_idx" in L.elsaa_last_error().decode()
     s = L.elsaa_lowrank_summary(ctypes.byref(p), fake, fake, fake, fake, fake, None, 10, None)
     assert s == _lib.ERR_WORKSPACE
+
+
+def test_check_orders_validates_before_launching():
+    L = _lib.lib()
+    ok = ctypes.c_void_p(0x1000)
+    p = base().params()
+    s = L.elsaa_check_orders(ctypes.byref(p), ok, ok, None, ok, 1 << 40, None)
+    assert s == _lib.ERR_INVALID_ARG and "bad" in L.elsaa_last_error().decode()
+    s = L.elsaa_check_orders(ctypes.byref(p), ok, ok, ok, None, 0, None)
+    assert s == _lib.ERR_WORKSPACE
+    # the counters: one int32 per token of every head
+    n = status_of(base(), _lib.CALL_CHECK)[2]
+    assert n == (4 * p.B * p.H * p.N + 255) // 256 * 256
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
