@@ -151,8 +151,9 @@ def cpu_baseline(w, seed, n_heads, threads):
 def bench_topk(args, w, cfg, d):
     """elsaa_topk at the workload's shape with k = its block size. Its algorithmic
     work is the score of every candidate pair, 2 d flops each on MFMA (the
-    contraction the selection needs); the exact rescoring and heap upkeep of the
-    keys near each query's threshold come on top."""
+    contraction the selection needs); the selection forms those scores five times
+    (four radix passes and the listing pass) and rescores the listed keys in fp64
+    on top."""
     import torch
     import sparse_rank_approximation_amd as S
     from sparse_rank_approximation_amd import _lib
@@ -167,6 +168,14 @@ def bench_topk(args, w, cfg, d):
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+    # Per-kernel times from a second pass with the library's launch events on.
+    _lib.profile(True)
+    S.topk(cfg, d["q"], d["k"], k_top)
+    torch.cuda.synchronize()
+    _lib.profile(False)
+    rep = _lib.profile_report()
+    kernels = {k: {"launches": n, "avg_us": round(t / n * 1e3, 1)} for k, (n, t) in sorted(rep.items())}
+    print("[bench] profiled; kernels: " + json.dumps(kernels), file=sys.stderr, flush=True)
     BH, N = w.B * w.H, w.N
     pairs = BH * (N * (N + 1) // 2 if w.causal else N * N)
     flops = 2.0 * w.d * pairs
@@ -180,7 +189,8 @@ def bench_topk(args, w, cfg, d):
                       "causal": w.causal, "k": k_top},
            "roofline": {"bound": "mfma", "kernel": "topk", "achieved": round(achieved, 2),
                         "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                        "avg_launch_us": round(ms * 1e3, 1), "traffic": None}}
+                        "avg_launch_us": round(ms * 1e3, 1), "traffic": None},
+           "kernels": kernels}
     print(json.dumps(out), flush=True)
 
 

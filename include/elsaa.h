@@ -82,7 +82,8 @@ typedef enum {
   ELSAA_CALL_FWD = 2,
   ELSAA_CALL_BWD = 3,
   ELSAA_CALL_GATES_BWD = 4,
-  ELSAA_CALL_CHECK = 5
+  ELSAA_CALL_CHECK = 5,
+  ELSAA_CALL_TOPK = 6
 } elsaa_call;
 
 /* Problem description.
@@ -251,10 +252,15 @@ elsaa_status elsaa_bwd(const elsaa_params* p, const void* Q, const void* K, cons
  *   k   : 1 .. 256 keys per query (ELSAA_ERR_UNSUPPORTED above).
  *   idx (out): int32 [B, H, N, k], each query's set in ascending key order, -1
  *       past min(k, #candidates).
+ *   ws  : elsaa_workspace_size(p, ELSAA_CALL_TOPK) bytes (the same for any k <= 256:
+ *       per query a threshold, a bound, a count and a list of up to 320 keys with
+ *       their fp32 scores).
  * The sets are exact: any correctly rounded fp64 implementation of the chain
- * selects the same keys. No workspace. */
+ * selects the same keys. (fp32 scores on the matrix cores locate each query's
+ * k-th best to within their rounding bound; only the keys within twice that bound
+ * of it are rescored in fp64.) */
 elsaa_status elsaa_topk(const elsaa_params* p, const void* Q, const void* K, int32_t k,
-                        int32_t* idx, void* stream);
+                        int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /* Learnable gates of Eq. 4. The paper has g_sparse,i and g_lr,i learned with the
  * model (Section 7: shared by ELSAA and its Sort_Lsh_RACE ablation, and on NIAH

@@ -12,7 +12,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 STATUS_NAMES = {0: "ELSAA_OK", 1: "ELSAA_ERR_INVALID_ARG", 2: "ELSAA_ERR_UNSUPPORTED",
                 3: "ELSAA_ERR_WORKSPACE", 4: "ELSAA_ERR_HIP"}
 F32, BF16 = 0, 1
-CALL_SELECT, CALL_SUMMARY, CALL_FWD, CALL_BWD, CALL_GATES_BWD, CALL_CHECK = range(6)
+CALL_SELECT, CALL_SUMMARY, CALL_FWD, CALL_BWD, CALL_GATES_BWD, CALL_CHECK, CALL_TOPK = range(7)
 
 SYMBOLS = ("elsaa_workspace_size", "elsaa_select", "elsaa_select_noalloc",
            "elsaa_lowrank_summary", "elsaa_fwd", "elsaa_bwd", "elsaa_gates_fwd",
@@ -59,7 +59,7 @@ def lib() -> ctypes.CDLL:
     L.elsaa_bwd.argtypes = [_PP] + [_vp] * 24 + [ctypes.c_size_t, _vp]
     L.elsaa_gates_fwd.argtypes = [_PP] + [_vp] * 6
     L.elsaa_gates_bwd.argtypes = [_PP] + [_vp] * 10 + [ctypes.c_size_t, _vp]
-    L.elsaa_topk.argtypes = [_PP, _vp, _vp, ctypes.c_int32, _vp, _vp]
+    L.elsaa_topk.argtypes = [_PP, _vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_size_t, _vp]
     L.elsaa_check_orders.argtypes = [_PP] + [_vp] * 4 + [ctypes.c_size_t, _vp]
     L.elsaa_profile.argtypes = [ctypes.c_int32]
     L.elsaa_profile_report.argtypes = [ctypes.c_char_p, ctypes.c_size_t,

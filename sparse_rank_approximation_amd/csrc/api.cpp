@@ -163,6 +163,7 @@ size_t ws_bytes_for(const Problem& pb, int call) {
     case ELSAA_CALL_BWD: return elsaa::bwd_ws_bytes(pb);
     case ELSAA_CALL_GATES_BWD: return elsaa::gates_bwd_ws_bytes(pb);
     case ELSAA_CALL_CHECK: return elsaa::check_ws_bytes(pb);
+    case ELSAA_CALL_TOPK: return elsaa::topk_ws_bytes(pb);
     default: return 0;
   }
 }
@@ -243,7 +244,7 @@ extern "C" {
 
 elsaa_status elsaa_workspace_size(const elsaa_params* p, int32_t call, size_t* bytes) {
   if (!bytes) return fail(ELSAA_ERR_INVALID_ARG, "bytes is NULL");
-  if (call < ELSAA_CALL_SELECT || call > ELSAA_CALL_CHECK)
+  if (call < ELSAA_CALL_SELECT || call > ELSAA_CALL_TOPK)
     return fail(ELSAA_ERR_INVALID_ARG, "unknown call %d", call);
   PROLOGUE(call);
   *bytes = empty ? 0 : ws_bytes_for(pb, call);
@@ -398,14 +399,18 @@ elsaa_status elsaa_check_orders(const elsaa_params* p, const int32_t* q_perm,
 }
 
 elsaa_status elsaa_topk(const elsaa_params* p, const void* Q, const void* K, int32_t k,
-                        int32_t* idx, void* stream) {
-  PROLOGUE(ELSAA_CALL_SELECT);
+                        int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  PROLOGUE(ELSAA_CALL_TOPK);
   if (k < 1) return fail(ELSAA_ERR_INVALID_ARG, "k = %d must be >= 1", k);
-  if (!elsaa::launch_topk(pb, Q, K, k, idx, (hipStream_t)stream, true))
+  if (!elsaa::launch_topk(pb, Q, K, k, idx, nullptr, (hipStream_t)stream, true))
     return fail(ELSAA_ERR_UNSUPPORTED, "k = %d: at most 256 keys per query are built", k);
   if (empty) return ELSAA_OK;
   NEED(Q); NEED(K); NEED(idx);
-  elsaa::launch_topk(pb, Q, K, k, idx, (hipStream_t)stream, false);
+  {
+    elsaa_status s_ = check_ws(pb, ELSAA_CALL_TOPK, ws, ws_bytes);
+    if (s_ != ELSAA_OK) return s_;
+  }
+  elsaa::launch_topk(pb, Q, K, k, idx, ws, (hipStream_t)stream, false);
   return launched();
 }
 

@@ -221,8 +221,9 @@ bool launch_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
 
 // Exact per-query top-k selection (topk.hip); dry: report only whether a variant
 // is built for k.
+size_t topk_ws_bytes(const Problem& pb);
 bool launch_topk(const Problem& pb, const void* Q, const void* K, int ktop, int32_t* out,
-                 hipStream_t st, bool dry);
+                 void* ws, hipStream_t st, bool dry);
 
 // Learnable gates of Eq. 4 from a projection of the query (gates.hip).
 size_t gates_bwd_ws_bytes(const Problem& pb);

@@ -200,9 +200,10 @@ def topk(cfg: ElsaaConfig, q, k, k_top: int):
     _check_tensor("q", q, x, cfg.dtype, dev)
     _check_tensor("k", k, x, cfg.dtype, dev)
     idx = torch.empty(cfg.B, cfg.H, cfg.N, k_top, dtype=torch.int32, device=dev)
+    ws, n = _workspace(cfg, _lib.CALL_TOPK, dev)
     p = cfg.params()
     _lib.check(_lib.lib().elsaa_topk(ctypes.byref(p), _ptr(q), _ptr(k), int(k_top), _ptr(idx),
-                                     _stream(dev)))
+                                     _ptr(ws), n, _stream(dev)))
     return idx
 
 

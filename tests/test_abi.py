@@ -61,7 +61,7 @@ def status_of(cfg_or_params, call=_lib.CALL_FWD):
 
 
 def test_valid_params_and_workspace_sizes():
-    for call in range(6):
+    for call in range(7):
         s, msg, n = status_of(base(), call)
         assert s == _lib.OK, msg
     # select: the hyperplanes widened to fp64, [H, hash_bits, d_h], 256-byte rounded

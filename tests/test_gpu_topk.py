@@ -1,7 +1,9 @@
 """GPU parity of elsaa_topk (exact per-query top-k keys on Q K^T, ties to the
 lower key index) against the oracle, bit for bit: bf16 and fp32, causal and not,
 d_h 32 / 64 / 128, k from 16 to 256, clustered inputs with many near ties, exact
-duplicate keys, and k above the causal candidate count (padding)."""
+duplicate keys, and k above the causal candidate count (padding). A head whose
+keys are all one row ties every score: later queries then list more keys than
+their list holds, and their tiles are redone by the heap kernel."""
 from __future__ import annotations
 
 import numpy as np
@@ -26,6 +28,7 @@ CASES = {
                                             n_clusters=8, sigma=0.5), 128, True),
     "noncausal_bf16_N1024_d128_k256": (wl("t", 1, 1, 1024, 128, "bf16", False, 128, 16), 256, False),
     "causal_f32_N128_d64_k100_padded": (wl("t", 1, 1, 128, 64, "f32", True, 32, 16), 100, True),
+    "causal_bf16_N512_d64_k64_all_tied": (wl("t", 1, 2, 512, 64, "bf16", True, 64, 16), 64, "all"),
 }
 
 
@@ -35,7 +38,9 @@ def test_topk_parity(case):
     w, k_top, dup = CASES[case]
     print(f"[gpu topk] {case} {w} k={k_top}", flush=True)
     inp = W.gen_inputs(w, 6000 + len(case), with_do=False)
-    if dup:  # a run of exact copies of one key row in every head, and queries close to it
+    if dup == "all":  # every key of head 1 the same row: all scores of a query tie
+        inp["k"][:, 1] = inp["k"][:, 1, 7:8]
+    elif dup:  # a run of exact copies of one key row in every head, and queries close to it
         inp["k"][:, :, w.N // 4: w.N // 4 + w.N // 8] = inp["k"][:, :, 3:4]
         inp["q"][:, :, ::5] = inp["k"][:, :, 3:4]
     d = to_dev({n: inp[n] for n in ("q", "k")})
