@@ -81,7 +81,9 @@ def step_work(w, rounds: int = 1) -> tuple[float, float]:
     return flops, nbytes
 
 
-def roofline(name, launches, total_ms, w, traffic_file, rounds: int = 1):
+def roofline(name, launches, total_ms, w, traffic_file, rounds: int = 1, workload=None):
+    """workload: the name the committed traffic figures must carry to be used (None:
+    a variant run, which they never describe)."""
     work = kernel_work(w, rounds)
     if name not in work:
         return None
@@ -95,12 +97,13 @@ def roofline(name, launches, total_ms, w, traffic_file, rounds: int = 1):
         peak = PEAK_HBM_GBS
     return {"bound": bound, "kernel": name, "achieved": round(achieved, 2), "peak": peak,
             "unit": unit, "frac": round(achieved / peak, 4), "avg_launch_us": round(avg_s * 1e6, 1),
-            "traffic": traffic_bytes(name, traffic_file)}
+            "traffic": traffic_bytes(name, traffic_file, workload)}
 
 
-def traffic_bytes(name, path):
+def traffic_bytes(name, path, workload):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary, if it was taken with the library this run loads; else None."""
+    summary, if it was taken on this workload with the library this run loads;
+    else None."""
     from sparse_rank_approximation_amd.traffic import library_hash
     if not os.path.exists(path):
         return None
@@ -109,7 +112,7 @@ def traffic_bytes(name, path):
     except ValueError:
         return None
     lib = library_hash()
-    if lib is None or rec.get("library_hash") != lib:
+    if lib is None or rec.get("library_hash") != lib or rec.get("workload") != workload:
         return None
     k = rec.get("kernels", {}).get(name)
     return None if k is None else k.get("hbm_bytes_per_launch")
@@ -293,8 +296,10 @@ def main():
     kernels = {k: {"launches": n, "avg_us": round(t / n * 1e3, 1),
                    "ms_per_step": round(t / psteps, 3)} for k, (n, t) in sorted(rep.items())}
     dom = max(rep, key=lambda k: rep[k][1])
+    plain = args.hash_rounds == 1 and args.extra_edges == 0 and not args.learned_gates
     roof = roofline(dom, rep[dom][0], rep[dom][1], w,
-                    os.path.join(ROOT, "profiles", "traffic.json"), args.hash_rounds)
+                    os.path.join(ROOT, "profiles", "traffic.json"), args.hash_rounds,
+                    w.name if plain else None)
     if roof is None:
         roof = {"kernel": dom, "avg_launch_us": round(rep[dom][1] / rep[dom][0] * 1e3, 1)}
     f_alg, b_alg = step_work(w, args.hash_rounds)

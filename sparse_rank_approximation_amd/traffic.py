@@ -9,13 +9,15 @@ Two roles, one per step of the measurement:
         COPY_BYTES / counter converts the counters to bytes.
 
     python -m sparse_rank_approximation_amd.traffic summarize OUT.json \\
-        FETCH_BENCH.csv WRITE_BENCH.csv FETCH_COPY.csv WRITE_COPY.csv
+        FETCH_BENCH.csv WRITE_BENCH.csv FETCH_COPY.csv WRITE_COPY.csv [WORKLOAD]
         Reads the counter_collection CSVs of the four runs (the bench.py runs and
         the copy runs) and writes OUT.json: per kernel, the average FETCH_SIZE and
         WRITE_SIZE per dispatch, the calibration factors and the calibrated bytes
-        per launch, tagged with the hash of the built library they were taken
-        with (bench.py uses the figures only while that library is the one it
-        loads: a change to a kernel or to a launch changes it, a comment does not).
+        per launch, tagged with the workload they were taken on (default: the
+        B2 H32 N16384 d128 bf16 causal one that bench.py runs by default) and the
+        hash of the built library they were taken with (bench.py uses the figures
+        only for that workload and while that library is the one it loads: a
+        change to a kernel or to a launch changes it, a comment does not).
 """
 from __future__ import annotations
 
@@ -45,9 +47,13 @@ def short_name(name: str):
         return None
     if "combine_kernel" in name:
         return "combine_q" if "ELb1" in name else "combine_kv"
+    if "topk_stream_kernel" in name:  # (the radix passes, then the listing pass)
+        return "topk_collect" if "ELb1" in name else "topk_thresh"
     for k in ("sparse_bwd", "sparse_fwd", "lr_bwd_k", "lr_bwd_q", "fwd_epilogue", "lr_sums",
               "lr_scan", "hash_kernel", "sort_kernel", "merge_kernel", "bwd_rows", "dlam_reduce",
-              "planes_transpose", "planes_f64"):
+              "planes_transpose", "planes_f64", "block_ids", "extra_prep", "extra_fwd",
+              "extra_bwd_q", "extra_bwd_k", "radix_hist", "radix_scan", "radix_scatter",
+              "topk_finish", "topk_heap", "topk_zero", "gates_fwd", "gates_bwd", "gates_reduce"):
         if k in name:
             return k.replace("_kernel", "").replace("planes_transpose", "planes_t")
     return name.split("(")[0][-48:]
@@ -88,7 +94,10 @@ def run_copy() -> None:
     print(f"copied {COPY_BYTES} bytes", flush=True)
 
 
-def summarize(out, fb, wb, fc, wc) -> None:
+DEFAULT_WORKLOAD = "llama_long_context_B2_H32_N16384_d128_bf16_causal"
+
+
+def summarize(out, fb, wb, fc, wc, workload=DEFAULT_WORKLOAD) -> None:
     f_bench, w_bench = per_dispatch(fb), per_dispatch(wb)
     kf = COPY_BYTES / (copy_kib(fc) * 1024.0)
     kw = COPY_BYTES / (copy_kib(wc) * 1024.0)
@@ -98,7 +107,7 @@ def summarize(out, fb, wb, fc, wc) -> None:
         wk = w_bench.get(k, (0, 0.0))[1]
         kernels[k] = {"fetch_kib_per_launch": round(fk, 1), "write_kib_per_launch": round(wk, 1),
                       "hbm_bytes_per_launch": round(fk * 1024.0 * kf + wk * 1024.0 * kw)}
-    rec = {"library_hash": library_hash(), "copy_bytes": COPY_BYTES,
+    rec = {"library_hash": library_hash(), "workload": workload, "copy_bytes": COPY_BYTES,
            "fetch_factor": round(kf, 4), "write_factor": round(kw, 4), "kernels": kernels}
     json.dump(rec, open(out, "w"), indent=1)
     print(json.dumps(rec, indent=1))
@@ -107,7 +116,7 @@ def summarize(out, fb, wb, fc, wc) -> None:
 if __name__ == "__main__":
     if len(sys.argv) >= 2 and sys.argv[1] == "copy":
         run_copy()
-    elif len(sys.argv) == 7 and sys.argv[1] == "summarize":
+    elif len(sys.argv) in (7, 8) and sys.argv[1] == "summarize":
         summarize(*sys.argv[2:])
     else:
         print(__doc__)
