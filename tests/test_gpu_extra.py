@@ -176,3 +176,35 @@ def test_extra_edges_are_deterministic_and_held_edges_change_nothing(causal):
     print(f"[gpu extra] held-only causal={causal} differences {errs}", flush=True)
     bad = {n: e for n, e in errs.items() if not e <= 1e-6}
     assert not bad, bad
+
+
+def test_autograd_with_rounds_and_extra_edges_matches_calls():
+    """elsaa_attention (the autograd function) with two hash rounds and an extra-edge
+    list gives the same bits as the explicit select / summary / forward / backward
+    calls."""
+    import sparse_rank_approximation_amd as S
+    w = wl("a", 1, 2, 512, 64, "bf16", True, 64, 64, "clusters", chunk=128, n_clusters=8,
+           sigma=0.5)
+    print(f"[gpu extra] autograd with rounds and extra edges {w}", flush=True)
+    inp = W.gen_inputs(w, 4800)
+    inp["planes_s"] = W.gen_planes_rounds(w, 4800, 2)
+    d = to_dev(inp)
+    ex = W.gen_extra_edges(w, 4800, 8).cuda()
+    lam = torch.full((w.H,), 0.7, device="cuda")
+    q = d["q"].clone().requires_grad_(True)
+    k = d["k"].clone().requires_grad_(True)
+    v = d["v"].clone().requires_grad_(True)
+    out = S.elsaa_attention(q, k, v, causal=True, block=w.block, lr_tables=w.lr_tables, lam=lam,
+                            planes_s=d["planes_s"], planes_lr=d["planes_lr"], chunk=w.chunk,
+                            hash_rounds=2, extra_idx=ex)
+    (out * d["do"]).sum().backward()
+    cfg = cfg_of(w, hash_rounds=2, extra_edges=8)
+    _, _, qp, kp = S.select(cfg, d["q"], d["k"], d["planes_s"])
+    A, z = S.lowrank_summary(cfg, d["k"], d["v"], d["planes_lr"])
+    f = S.forward(cfg, d["q"], d["k"], d["v"], d["planes_lr"], qp, kp, A, z, lam, extra=ex)
+    g = S.backward(cfg, d["q"], d["k"], d["v"], d["do"], f["O_s"], f["O_lr"], d["planes_lr"], qp,
+                   kp, A, z, f["lse"], f["d_lr"], lam, extra=ex)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), f["O"])
+    for name, t in (("dQ", q), ("dK", k), ("dV", v)):
+        assert torch.equal(t.grad, g[name]), name

@@ -29,6 +29,9 @@ CASES = {
     "noncausal_bf16_N1024_d128_k256": (wl("t", 1, 1, 1024, 128, "bf16", False, 128, 16), 256, False),
     "causal_f32_N128_d64_k100_padded": (wl("t", 1, 1, 128, 64, "f32", True, 32, 16), 100, True),
     "causal_bf16_N512_d64_k64_all_tied": (wl("t", 1, 2, 512, 64, "bf16", True, 64, 16), 64, "all"),
+    # a partial 128-query workgroup and a partial 32-query tile; k = 1
+    "noncausal_f32_N96_d32_k8": (wl("t", 1, 1, 96, 32, "f32", False, 32, 16), 8, False),
+    "causal_bf16_N64_d128_k1": (wl("t", 1, 2, 64, 128, "bf16", True, 64, 16), 1, False),
 }
 
 
