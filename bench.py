@@ -60,6 +60,9 @@ def kernel_work(w, rounds: int = 1) -> dict:
         "bwd_rows": ("hbm", 3.0 * tok * d * e + 40.0 * tok, "GB/s"),
         "gates_fwd": ("hbm", tok * d * e + 8.0 * tok, "GB/s"),
         "gates_bwd": ("hbm", 3.0 * tok * d * e + 16.0 * tok, "GB/s"),
+        # the one-launch forward: reads Q, K, V; writes O, O_lr (dtype), O_s (fp32),
+        # lse, d_lr, two codes and two order entries per token-head
+        "fused_fwd": ("hbm", tok * (5.0 * d * e + 4.0 * d + 20.0), "GB/s"),
     }
 
 
@@ -217,6 +220,9 @@ def main():
                     help="sortLSH hash rounds (the sparse support is the union of theirs)")
     ap.add_argument("--extra-edges", type=int, default=0,
                     help="random extra keys listed per query (Omega_safe) joining the support")
+    ap.add_argument("--fused", action="store_true",
+                    help="the forward as one launch (elsaa_fwd_fused; non-causal workloads) "
+                         "instead of elsaa_select + elsaa_lowrank_summary + elsaa_fwd")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -257,10 +263,15 @@ def main():
         gs = gl = None
         if args.learned_gates:
             gs, gl = S.gates(cfg, d["q"], gate_w, gate_b)
-        _, _, qp, kp = S.select(cfg, d["q"], d["k"], d["planes_s"])
-        A, z = S.lowrank_summary(cfg, d["k"], d["v"], d["planes_lr"])
-        o = S.forward(cfg, d["q"], d["k"], d["v"], d["planes_lr"], qp, kp, A, z, lam, gs, gl,
-                      extra=extra)
+        if args.fused:
+            o = S.forward_fused(cfg, d["q"], d["k"], d["v"], d["planes_s"], d["planes_lr"], lam,
+                                gs, gl)
+            qp, kp, A, z = o["q_perm"], o["k_perm"], o["A"], o["z"]
+        else:
+            _, _, qp, kp = S.select(cfg, d["q"], d["k"], d["planes_s"])
+            A, z = S.lowrank_summary(cfg, d["k"], d["v"], d["planes_lr"])
+            o = S.forward(cfg, d["q"], d["k"], d["v"], d["planes_lr"], qp, kp, A, z, lam, gs, gl,
+                          extra=extra)
         g = S.backward(cfg, d["q"], d["k"], d["v"], d["do"], o["O_s"], o["O_lr"], d["planes_lr"],
                        qp, kp, A, z, o["lse"], o["d_lr"], lam, gs, gl, extra=extra)
         if args.learned_gates:
@@ -296,7 +307,8 @@ def main():
     kernels = {k: {"launches": n, "avg_us": round(t / n * 1e3, 1),
                    "ms_per_step": round(t / psteps, 3)} for k, (n, t) in sorted(rep.items())}
     dom = max(rep, key=lambda k: rep[k][1])
-    plain = args.hash_rounds == 1 and args.extra_edges == 0 and not args.learned_gates
+    plain = (args.hash_rounds == 1 and args.extra_edges == 0 and not args.learned_gates and
+             not args.fused)
     roof = roofline(dom, rep[dom][0], rep[dom][1], w,
                     os.path.join(ROOT, "profiles", "traffic.json"), args.hash_rounds,
                     w.name if plain else None)
@@ -324,6 +336,7 @@ def main():
                    "causal": w.causal, "block": w.block, "r": w.r, "hash_bits": w.hash_bits,
                    "chunk": w.chunk, "gates": "learned" if args.learned_gates else "unit",
                    "hash_rounds": args.hash_rounds, "extra_edges": args.extra_edges,
+                   "forward": "fused" if args.fused else "select+summary+fwd",
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "none"},
         "roofline": roof,
         "kernels": kernels,

@@ -242,6 +242,30 @@ elsaa_status elsaa_bwd(const elsaa_params* p, const void* Q, const void* K, cons
                        void* dK, void* dV, float* dlambda, float* dg_s, float* dg_lr, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* The whole non-causal forward in one launch (the paper's Section 8 names fused
+ * GPU kernels as the next step): sortLSH codes and orders, the RACE summary, the
+ * sparse block attention, the low-rank readout, Eq. 5 and Eq. 4, one workgroup per
+ * (batch, head), every query row read once for both branches. Its outputs are
+ * those of elsaa_select, elsaa_lowrank_summary and elsaa_fwd called in turn with
+ * the same arguments, and feed elsaa_bwd the same way:
+ *   Q, K, V, planes_s, planes_lr, lambda, g_s, g_lr : as for those calls.
+ *   q_code, k_code (out) : uint16 [B, H, N];  q_perm, k_perm (out) : int32 [B, H, N].
+ *   A, z (out)           : fp32 [B, H, 1, d_h, r], [B, H, 1, r].
+ *   O, O_s, O_lr, lse_s, d_lr (out) : as for elsaa_fwd.
+ * Taken for: causal = 0, hash_rounds <= 1, extra_edges = 0, hash_bits <= 10,
+ * block <= 128, N <= 65536, and the head's rows, statistics and orders within one
+ * workgroup's LDS (about 8 N bytes on top of the tiles); other parameters return
+ * ELSAA_ERR_UNSUPPORTED and the two-call path serves them. Needs no workspace.
+ * The summation order of A, z differs from elsaa_lowrank_summary's, so those (and
+ * what depends on them) agree with the two-call path to rounding, not bit for bit;
+ * codes and orders are the same bit for bit. */
+elsaa_status elsaa_fwd_fused(const elsaa_params* p, const void* Q, const void* K, const void* V,
+                             const float* planes_s, const float* planes_lr, const float* lambda,
+                             const float* g_s, const float* g_lr, uint16_t* q_code,
+                             uint16_t* k_code, int32_t* q_perm, int32_t* k_perm, float* A,
+                             float* z, void* O, float* O_s, void* O_lr, float* lse_s,
+                             float* d_lr, void* stream);
+
 /* Exact per-query top-k key selection on Q K^T, the top-k kind of sparse selector
  * the paper lists beside sortLSH (Section 3), as an alternative to elsaa_select.
  * For query i the candidate keys are every j (causal: j <= i); the score of (i, j)

@@ -15,7 +15,7 @@ F32, BF16 = 0, 1
 CALL_SELECT, CALL_SUMMARY, CALL_FWD, CALL_BWD, CALL_GATES_BWD, CALL_CHECK, CALL_TOPK = range(7)
 
 SYMBOLS = ("elsaa_workspace_size", "elsaa_select", "elsaa_select_noalloc",
-           "elsaa_lowrank_summary", "elsaa_fwd", "elsaa_bwd", "elsaa_gates_fwd",
+           "elsaa_lowrank_summary", "elsaa_fwd", "elsaa_bwd", "elsaa_fwd_fused", "elsaa_gates_fwd",
            "elsaa_gates_bwd", "elsaa_topk", "elsaa_check_orders", "elsaa_profile",
            "elsaa_profile_report", "elsaa_last_error")
 
@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
     L.elsaa_lowrank_summary.argtypes = [_PP, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.elsaa_fwd.argtypes = [_PP] + [_vp] * 18 + [ctypes.c_size_t, _vp]
     L.elsaa_bwd.argtypes = [_PP] + [_vp] * 24 + [ctypes.c_size_t, _vp]
+    L.elsaa_fwd_fused.argtypes = [_PP] + [_vp] * 20
     L.elsaa_gates_fwd.argtypes = [_PP] + [_vp] * 6
     L.elsaa_gates_bwd.argtypes = [_PP] + [_vp] * 10 + [ctypes.c_size_t, _vp]
     L.elsaa_topk.argtypes = [_PP, _vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_size_t, _vp]

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libelsaa.so")
 SOURCES = ["select.hip", "lowrank.hip", "fwd.hip", "bwd.hip", "merge.hip", "gates.hip", "topk.hip",
-           "extra.hip", "check.hip", "api.cpp", "prof.cpp"]
+           "extra.hip", "check.hip", "fused.hip", "api.cpp", "prof.cpp"]
 HEADERS = ["common.hpp", "launch.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

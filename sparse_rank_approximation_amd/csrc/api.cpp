@@ -343,6 +343,36 @@ elsaa_status elsaa_fwd(const elsaa_params* p, const void* Q, const void* K, cons
   return launched();
 }
 
+elsaa_status elsaa_fwd_fused(const elsaa_params* p, const void* Q, const void* K, const void* V,
+                             const float* planes_s, const float* planes_lr, const float* lambda,
+                             const float* g_s, const float* g_lr, uint16_t* q_code,
+                             uint16_t* k_code, int32_t* q_perm, int32_t* k_perm, float* A,
+                             float* z, void* O, float* O_s, void* O_lr, float* lse_s,
+                             float* d_lr, void* stream) {
+  PROLOGUE(ELSAA_CALL_FWD);
+  if (!elsaa::fused_fwd_supported(pb))
+    return fail(ELSAA_ERR_UNSUPPORTED,
+                "the fused forward takes non-causal problems with one hash round, no extra "
+                "edges, hash_bits <= 10, block <= 128, N <= 65536 and %zu bytes of LDS per "
+                "workgroup (these need %zu)",
+                (size_t)elsaa::kLdsBytes, elsaa::fused_fwd_lds(pb));
+  if (empty) return ELSAA_OK;
+  NEED(Q); NEED(K); NEED(V); NEED(planes_s); NEED(planes_lr); NEED(lambda);
+  OPTIONAL(g_s); OPTIONAL(g_lr);
+  NEED(q_code); NEED(k_code); NEED(q_perm); NEED(k_perm); NEED(A); NEED(z);
+  NEED(O); NEED(O_s); NEED(O_lr); NEED(lse_s); NEED(d_lr);
+  {
+    // (the debug count goes to the first words of O_s, which the kernel overwrites)
+    const void* xs[3] = {Q, K, V};
+    const char* names[3] = {"Q", "K", "V"};
+    elsaa_status s_ = debug_check_finite(pb, xs, names, 3, O_s, (hipStream_t)stream);
+    if (s_ != ELSAA_OK) return s_;
+  }
+  elsaa::launch_fused_fwd(pb, Q, K, V, planes_s, planes_lr, lambda, g_s, g_lr, q_code, k_code,
+                          q_perm, k_perm, A, z, O, O_s, O_lr, lse_s, d_lr, (hipStream_t)stream);
+  return launched();
+}
+
 elsaa_status elsaa_bwd(const elsaa_params* p, const void* Q, const void* K, const void* V,
                        const void* dO, const float* O_s, const void* O_lr,
                        const float* planes_lr, const int32_t* q_perm, const int32_t* k_perm,

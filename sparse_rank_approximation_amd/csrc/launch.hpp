@@ -260,6 +260,16 @@ void launch_combine(const Problem& pb, const void* dQp, const void* dKp, const v
                     const void* dQx, const void* dKx, const void* dVx, void* dQ, void* dK,
                     void* dV, hipStream_t st);
 
+// The non-causal forward in one launch (fused.hip): whether it takes these
+// parameters, its LDS per workgroup, and the launch.
+size_t fused_fwd_lds(const Problem& pb);
+bool fused_fwd_supported(const Problem& pb);
+void launch_fused_fwd(const Problem& pb, const void* Q, const void* K, const void* V,
+                      const float* planes_s, const float* planes_lr, const float* lambda,
+                      const float* g_s, const float* g_lr, uint16_t* qc, uint16_t* kc,
+                      int32_t* qperm, int32_t* kperm, float* A, float* z, void* O, float* O_s,
+                      void* O_lr, float* lse, float* d_lr, hipStream_t st);
+
 size_t bwd_ws_bytes(const Problem& pb);
 size_t bwd_lds_need(const Problem& pb);
 bool launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, const void* dO,

@@ -268,6 +268,41 @@ def forward(cfg: ElsaaConfig, q, k, v, planes_lr, q_perm, k_perm, A, z, lam, g_s
     return out
 
 
+def forward_fused(cfg: ElsaaConfig, q, k, v, planes_s, planes_lr, lam, g_s=None, g_lr=None):
+    """elsaa_fwd_fused: the non-causal forward in one launch. Returns dict(q_code, k_code,
+    q_perm, k_perm, A, z, O, O_s, O_lr, lse, d_lr), what select, lowrank_summary and
+    forward return together (and what backward takes)."""
+    dev = q.device
+    x = (cfg.B, cfg.H, cfg.N, cfg.d)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, x, cfg.dtype, dev)
+    _check_tensor("planes_s", planes_s, cfg.planes_s_shape, torch.float32, dev)
+    _check_tensor("planes_lr", planes_lr, (cfg.H, cfg.lr_tables, cfg.lr_bits, cfg.d),
+                  torch.float32, dev)
+    _check_tensor("lam", lam, (cfg.H,), torch.float32, dev)
+    _opt("g_s", g_s, (cfg.B, cfg.H, cfg.N), torch.float32, dev)
+    _opt("g_lr", g_lr, (cfg.B, cfg.H, cfg.N), torch.float32, dev)
+    out = {"q_code": torch.empty(cfg.code_shape, dtype=torch.int16, device=dev)}
+    out["k_code"] = torch.empty_like(out["q_code"])
+    out["q_perm"] = torch.empty(cfg.B, cfg.H, cfg.perm_len, dtype=torch.int32, device=dev)
+    out["k_perm"] = torch.empty_like(out["q_perm"])
+    out["A"] = torch.empty(cfg.B, cfg.H, cfg.n_summaries, cfg.d, cfg.r, dtype=torch.float32,
+                           device=dev)
+    out["z"] = torch.empty(cfg.B, cfg.H, cfg.n_summaries, cfg.r, dtype=torch.float32, device=dev)
+    for n in ("O", "O_lr"):
+        out[n] = torch.empty(x, dtype=cfg.dtype, device=dev)
+    out["O_s"] = torch.empty(x, dtype=torch.float32, device=dev)
+    out["lse"] = torch.empty(cfg.B, cfg.H, cfg.N, dtype=torch.float32, device=dev)
+    out["d_lr"] = torch.empty_like(out["lse"])
+    p = cfg.params()
+    _lib.check(_lib.lib().elsaa_fwd_fused(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(planes_s), _ptr(planes_lr), _ptr(lam),
+        _ptr(g_s), _ptr(g_lr), _ptr(out["q_code"]), _ptr(out["k_code"]), _ptr(out["q_perm"]),
+        _ptr(out["k_perm"]), _ptr(out["A"]), _ptr(out["z"]), _ptr(out["O"]), _ptr(out["O_s"]),
+        _ptr(out["O_lr"]), _ptr(out["lse"]), _ptr(out["d_lr"]), _stream(dev)))
+    return out
+
+
 def backward(cfg: ElsaaConfig, q, k, v, do, O_s, O_lr, planes_lr, q_perm, k_perm, A, z, lse, d_lr,
              lam, g_s=None, g_lr=None, want_dlam=True, want_dg=True, extra=None):
     """elsaa_bwd: returns dict(dQ, dK, dV, dlambda, dg_s, dg_lr)."""
@@ -352,9 +387,19 @@ class ElsaaFunction(torch.autograd.Function):
             if g_s is not None or g_lr is not None:
                 raise ValueError("give either gate tensors or a gate projection, not both")
             g_s, g_lr = gates(cfg, q, gate_w.contiguous(), gate_b.contiguous())
-        _, _, qp, kp = select(cfg, q, k, planes_s)
-        A, z = lowrank_summary(cfg, k, v, planes_lr)
-        out = forward(cfg, q, k, v, planes_lr, qp, kp, A, z, lam, g_s, g_lr, extra=extra)
+        out = None
+        if not cfg.causal and cfg.rounds == 1 and extra is None:
+            # the one-launch forward where it takes the sizes
+            try:
+                out = forward_fused(cfg, q, k, v, planes_s, planes_lr, lam, g_s, g_lr)
+                qp, kp, A, z = out["q_perm"], out["k_perm"], out["A"], out["z"]
+            except _lib.ElsaaError as e:
+                if e.status != _lib.ERR_UNSUPPORTED:
+                    raise
+        if out is None:
+            _, _, qp, kp = select(cfg, q, k, planes_s)
+            A, z = lowrank_summary(cfg, k, v, planes_lr)
+            out = forward(cfg, q, k, v, planes_lr, qp, kp, A, z, lam, g_s, g_lr, extra=extra)
         ctx.cfg = cfg
         ctx.learned = learned
         ctx.save_for_backward(q, k, v, lam, g_s, g_lr, planes_lr, qp, kp, A, z, out["O_s"],

@@ -221,3 +221,36 @@ def test_noalloc_select_rejects_sizes_beyond_its_scratch():
     p = base().params()
     s = L.elsaa_select_noalloc(ctypes.byref(p), None, ok, ok, ok, ok, ok, ok, None)
     assert s == _lib.ERR_INVALID_ARG and "NULL" in L.elsaa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(causal=True), "non-causal"),
+    (dict(causal=False, hash_rounds=2), "one hash round"),
+    (dict(causal=False, extra_edges=4), "extra"),
+    (dict(causal=False, N=1 << 16, block=16, hash_bits=12), "hash_bits"),
+    (dict(causal=False, N=1 << 16, d=128, lr_tables=8), "LDS"),
+])
+def test_fused_forward_rejects_what_it_does_not_take(kw, needle):
+    """elsaa_fwd_fused takes non-causal, single-round problems without extra edges
+    whose head fits one workgroup's LDS; anything else is ELSAA_ERR_UNSUPPORTED,
+    decided before any pointer is looked at or anything launched."""
+    L = _lib.lib()
+    p = base(**kw).params()
+    s = L.elsaa_fwd_fused(ctypes.byref(p), *([None] * 20))
+    assert s == _lib.ERR_UNSUPPORTED, L.elsaa_last_error().decode()
+    assert needle in L.elsaa_last_error().decode()
+
+
+def test_fused_forward_validates_pointers_before_launching():
+    L = _lib.lib()
+    ok = ctypes.c_void_p(0x1000)
+    bad = ctypes.c_void_p(0x1008)
+    p = base(causal=False, N=1024, block=32, lr_tables=2).params()
+    args = [ok] * 19 + [None]
+    args[8] = None  # q_code
+    s = L.elsaa_fwd_fused(ctypes.byref(p), *args)
+    assert s == _lib.ERR_INVALID_ARG and "q_code" in L.elsaa_last_error().decode()
+    args = [ok] * 19 + [None]
+    args[6] = bad  # g_s (optional) misaligned
+    s = L.elsaa_fwd_fused(ctypes.byref(p), *args)
+    assert s == _lib.ERR_INVALID_ARG and "g_s" in L.elsaa_last_error().decode()

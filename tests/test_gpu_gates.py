@@ -31,15 +31,22 @@ def gate_params(w, seed):
     return 0.2 * torch.randn(w.H, 2, w.d, generator=g), 0.5 * torch.randn(w.H, 2, generator=g)
 
 
-def run_gpu(w, inp, Wg, bg, lam):
+def run_gpu(w, inp, Wg, bg, lam, fused=False):
+    """The gated operator by explicit calls; fused: the forward as elsaa_fwd_fused
+    (what the autograd function runs for a non-causal single-round problem)."""
     import sparse_rank_approximation_amd as S
     cfg = cfg_of(w)
     d = to_dev(inp)
     Wd, bd, lamd = Wg.cuda(), bg.cuda(), lam.cuda()
     gs, gl = S.gates(cfg, d["q"], Wd, bd)
-    _, _, qp, kp = S.select(cfg, d["q"], d["k"], d["planes_s"])
-    A, z = S.lowrank_summary(cfg, d["k"], d["v"], d["planes_lr"])
-    o = S.forward(cfg, d["q"], d["k"], d["v"], d["planes_lr"], qp, kp, A, z, lamd, gs, gl)
+    if fused:
+        o = S.forward_fused(cfg, d["q"], d["k"], d["v"], d["planes_s"], d["planes_lr"], lamd, gs,
+                            gl)
+        qp, kp, A, z = o["q_perm"], o["k_perm"], o["A"], o["z"]
+    else:
+        _, _, qp, kp = S.select(cfg, d["q"], d["k"], d["planes_s"])
+        A, z = S.lowrank_summary(cfg, d["k"], d["v"], d["planes_lr"])
+        o = S.forward(cfg, d["q"], d["k"], d["v"], d["planes_lr"], qp, kp, A, z, lamd, gs, gl)
     g = S.backward(cfg, d["q"], d["k"], d["v"], d["do"], o["O_s"], o["O_lr"], d["planes_lr"], qp,
                    kp, A, z, o["lse"], o["d_lr"], lamd, gs, gl)
     dW, db = S.gates_backward(cfg, d["q"], Wd, gs, gl, g["dg_s"], g["dg_lr"], g["dQ"])
@@ -110,7 +117,8 @@ def test_autograd_with_learned_gates_matches_calls():
                             lam=lam.cuda(), planes_s=d["planes_s"], planes_lr=d["planes_lr"],
                             chunk=w.chunk, gate_w=gw, gate_b=gb)
     (out * d["do"]).sum().backward()
-    got = run_gpu(w, inp, Wg, bg, lam)
+    assert not w.causal  # the autograd function takes the one-launch forward here
+    got = run_gpu(w, inp, Wg, bg, lam, fused=True)
     assert torch.equal(out.detach(), got["O"])
     for name, t in (("dQ", q), ("dK", k), ("dV", v)):
         assert torch.equal(t.grad, got[name]), name
