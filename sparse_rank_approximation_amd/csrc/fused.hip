@@ -47,10 +47,10 @@ struct FusedSmem {
       T Ks[128][LD];  // K and V rows of the blocks of one round
       T Vs[128][LD];
     } blk;
-    double planes[kFusedBits][D];   // sortLSH hyperplanes, widened to fp64
     int bins[2][1 << kFusedBits];   // counting sort, one array per side
   } u;
   T SF[RP][LD];            // the statistics as the readout's operand, [feature][channel]
+  PlanesLds<T, D, LP> PL;  // the RACE hyperplanes as MFMA operands
   alignas(16) float zr[RP];
 };
 
@@ -59,6 +59,50 @@ struct FusedSmem {
 template <typename T, int D, int LP>
 constexpr size_t fused_static_lds() {
   return sizeof(FusedSmem<T, D, LP>);
+}
+
+// Code of one row (its NP 16-byte pieces in registers) against `bits` hyperplanes
+// ps ([bits][D] fp32; the same for every lane, so read with scalar loads and
+// widened exactly to fp64 where used): bit b is the sign of the fp64 chain
+// acc = fma(x[j], (double)ps[b][j], acc), j = 0 .. D-1, from +0.0. Two bits at a
+// time, so that two independent chains are in flight.
+template <typename T, int D>
+__device__ __forceinline__ unsigned hash_row(const uint4 (&cur)[D * (int)sizeof(T) / 16],
+                                             const float* ps, int bits) {
+  constexpr int NP = D * (int)sizeof(T) / 16, EPP = 16 / (int)sizeof(T);
+  unsigned cd = 0;
+  for (int b = 0; b < bits; b += 2) {
+    const float* p0 = ps + b * D;
+    const float* p1 = ps + (b + 1 < bits ? b + 1 : b) * D;
+    double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+    for (int c = 0; c < NP; ++c) {
+      const uint4 v = cur[c];
+      float xv[EPP];
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xv[2 * e] = __uint_as_float(w4[e] << 16);
+          xv[2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+        }
+      } else {
+        xv[0] = __uint_as_float(v.x);
+        xv[1] = __uint_as_float(v.y);
+        xv[2] = __uint_as_float(v.z);
+        xv[3] = __uint_as_float(v.w);
+      }
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) {
+        const double xd = (double)xv[e];
+        a0 = __builtin_fma(xd, (double)p0[c * EPP + e], a0);
+        a1 = __builtin_fma(xd, (double)p1[c * EPP + e], a1);
+      }
+    }
+    if (a0 > 0.0) cd |= 1u << b;
+    if (b + 1 < bits && a1 > 0.0) cd |= 1u << (b + 1);
+  }
+  return cd;
 }
 
 template <typename T, int D, int LP>
@@ -93,14 +137,17 @@ __global__ void __launch_bounds__(256)
   const T* Kh = K + rb * D;
   const T* Vh = V + rb * D;
   const float* pl = planes_lr + (size_t)head * L * 4 * D;
+  stage_planes<T, D, LP, 256>(pl, L, sm.PL, tid);  // (read after the first barrier)
+  const T* PH = &sm.PL.p[0][0][0];
+  const T* PLo = &sm.PL.p[PlanesLds<T, D, LP>::NPART - 1][0][0];
+  constexpr int LDP = PlanesLds<T, D, LP>::LDP;
 
   // ---- 1. codes ----------------------------------------------------------------
   {
+    // The hyperplanes are the same for every lane: read with scalar loads (fp32,
+    // widened exactly to fp64 where used), not from LDS, whose bandwidth a
+    // per-operation broadcast of them would take.
     const float* ps = planes_s + (size_t)head * bits * D;
-    for (int i = tid; i < bits * D; i += 256) sm.u.planes[i / D][i % D] = (double)ps[i];
-  }
-  __syncthreads();
-  {
     // Each thread hashes rows tid, tid + 256, ...; the next row's pieces are loaded
     // while the current row's chains run.
     constexpr int NP = D * (int)sizeof(T) / 16, EPP = 16 / (int)sizeof(T);
@@ -120,40 +167,7 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
         for (int c = 0; c < NP; ++c) nxt[c] = x[c];
       }
-      double acc[kFusedBits];
-#pragma unroll
-      for (int b = 0; b < kFusedBits; ++b) acc[b] = 0.0;
-#pragma unroll
-      for (int c = 0; c < NP; ++c) {
-        const uint4 v = cur[c];
-        float xv[EPP];
-        if constexpr (sizeof(T) == 2) {
-          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            xv[2 * e] = __uint_as_float(w4[e] << 16);
-            xv[2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
-          }
-        } else {
-          xv[0] = __uint_as_float(v.x);
-          xv[1] = __uint_as_float(v.y);
-          xv[2] = __uint_as_float(v.z);
-          xv[3] = __uint_as_float(v.w);
-        }
-#pragma unroll
-        for (int e = 0; e < EPP; ++e) {
-          const double xd = (double)xv[e];
-#pragma unroll
-          for (int b = 0; b < kFusedBits; ++b)
-            if (b < bits) acc[b] = __builtin_fma(xd, sm.u.planes[b][c * EPP + e], acc[b]);
-        }
-        // (one piece at a time: the hyperplane reads of later pieces stay behind)
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      unsigned cd = 0;
-#pragma unroll
-      for (int b = 0; b < kFusedBits; ++b)
-        if (b < bits && acc[b] > 0.0) cd |= 1u << b;
+      const unsigned cd = hash_row<T, D>(cur, ps, bits);
       const int isk = row >= N, t = isk ? row - N : row;
       code[isk][t] = (uint16_t)cd;
       (isk ? kc : qc)[rb + t] = (uint16_t)cd;
@@ -239,7 +253,7 @@ __global__ void __launch_bounds__(256)
   };
   load_step(0);
   for (int s0 = 0; s0 < N; s0 += kFusedStep) {
-    Feat::template compute_to_row<0, NJP>(kx, pl, L, scale, tau, lane, s0 + 32 * w + col < N,
+    Feat::template compute_to_row<0, NJP>(kx, PH, PLo, LDP, L, scale, tau, lane, s0 + 32 * w + col < N,
                                           &sm.u.sum.FS[32 * w + col][0]);
 #pragma unroll
     for (int i = 0; i < VIT; ++i) {
@@ -293,7 +307,18 @@ __global__ void __launch_bounds__(256)
       }
     }
   };
-  if constexpr (KV_AHEAD) load_round(0);
+  // This lane's query of round b0 (its block b0 + w / WPB, row 32 (w % WPB) + col).
+  const int cb = w / WPB, qloc = 32 * (w % WPB) + col;
+  auto query_of = [&](int b0) __attribute__((always_inline)) {
+    const int b = b0 + cb;
+    return b < nb && qloc < sb ? (int)ord[0][b * sb + qloc] : 0;
+  };
+  // With D <= 64 the next round's query rows are in flight during this round too.
+  typename M::frag qf[D / M::KSTEP], qn[D / M::KSTEP];
+  if constexpr (KV_AHEAD) {
+    load_round(0);
+    prefetch_row_frags<T, D>(Qh + (size_t)query_of(0) * D, qn, h);
+  }
   for (int b0 = 0; b0 < nb; b0 += CB) {
     if constexpr (!KV_AHEAD) load_round(b0);
 #pragma unroll
@@ -302,15 +327,21 @@ __global__ void __launch_bounds__(256)
       kb[i].store(&sm.u.blk.Ks[row][c8]);
       vb[i].store(&sm.u.blk.Vs[row][c8]);
     }
-    const int cb = w / WPB, b = b0 + cb;
-    const int qloc = 32 * (w % WPB) + col;  // this lane's query row of its block
+    const int b = b0 + cb;
     const bool qvalid = b < nb && qloc < sb;
-    const int qi = qvalid ? ord[0][b * sb + qloc] : 0;
-    typename M::frag qf[D / M::KSTEP];
-    prefetch_row_frags<T, D>(Qh + (size_t)qi * D, qf, h);
+    const int qi = query_of(b0);
+    if constexpr (KV_AHEAD) {
+#pragma unroll
+      for (int ks = 0; ks < D / M::KSTEP; ++ks) qf[ks] = qn[ks];
+    } else {
+      prefetch_row_frags<T, D>(Qh + (size_t)qi * D, qf, h);
+    }
     __syncthreads();
     if constexpr (KV_AHEAD)
-      if (b0 + CB < nb) load_round(b0 + CB);
+      if (b0 + CB < nb) {
+        load_round(b0 + CB);
+        prefetch_row_frags<T, D>(Qh + (size_t)query_of(b0 + CB) * D, qn, h);
+      }
     if (b < nb) {
       const T* Kb = &sm.u.blk.Ks[cb * KT][0];
       const T* Vb = &sm.u.blk.Vs[cb * KT][0];
@@ -357,7 +388,7 @@ __global__ void __launch_bounds__(256)
       }
       // Low-rank branch from the same query rows: num^T = S^T phi(Q)^T, den = phi(Q) . z.
       Feat Fq;
-      Fq.compute(qf, pl, L, scale, tau, lane);
+      Fq.compute(qf, PH, PLo, LDP, L, scale, tau, lane);
       float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int jp = 0; jp < NJP; ++jp)
