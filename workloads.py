@@ -65,7 +65,7 @@ WORKLOADS = {
                 64, 64, "clusters", dict(n_clusters=64, sigma=0.3), chunk=512),
     3: Workload("llama_long_context_B2_H32_N16384_d128_bf16_causal", 2, 32, 16384, 128, "bf16",
                 True, 128, 128, "clusters_diffuse",
-                dict(n_clusters=256, sigma=0.5, diffuse=0.2)),
+                dict(n_clusters=256, sigma=0.5, diffuse=0.2), chunk=4096),
     4: Workload("very_long_context_B1_H8_N65536_d128_bf16_causal", 1, 8, 65536, 128, "bf16", True,
                 256, 256, "ar1_clusters", dict(n_clusters=1024, rho=0.9, jitter=0.1)),
     5: Workload("vit_batch_B64_H12_N1024_d64_bf16", 64, 12, 1024, 64, "bf16", False, 32, 32,
