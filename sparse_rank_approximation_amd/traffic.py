@@ -53,7 +53,8 @@ def short_name(name: str):
               "lr_scan", "hash_kernel", "sort_kernel", "merge_kernel", "bwd_rows", "dlam_reduce",
               "planes_transpose", "planes_f64", "block_ids", "extra_prep", "extra_fwd",
               "extra_bwd_q", "extra_bwd_k", "radix_hist", "radix_scan", "radix_scatter",
-              "topk_finish", "topk_heap", "topk_zero", "gates_fwd", "gates_bwd", "gates_reduce"):
+              "topk_finish", "topk_heap", "topk_zero", "gates_fwd", "gates_bwd", "gates_reduce",
+              "fused_fwd"):
         if k in name:
             return k.replace("_kernel", "").replace("planes_transpose", "planes_t")
     return name.split("(")[0][-48:]
