@@ -909,15 +909,15 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
             const size_t sl = !causal ? (size_t)rnd * N + jk[j]
                               : leaf  ? (size_t)jk[j]
                                       : (size_t)N + (size_t)ord * (N / 2) + compact_past(jk[j], N, lev);
-            a[j].store(dVp + (hb + sl) * D + c8[j]);
-            b2[j].store(dKp + (hb + sl) * D + c8[j]);
+            a[j].store_nt(dVp + (hb + sl) * D + c8[j]);
+            b2[j].store_nt(dKp + (hb + sl) * D + c8[j]);
           }
           if (SB >= 32 || iq[j] >= 0) {
             const size_t sl = !causal ? (size_t)rnd * N + iq[j]
                               : leaf  ? (size_t)iq[j]
                                       : (size_t)N + (size_t)ord * (N / 2) +
                                             compact_future_b(iq[j], N, lev);
-            c[j].store(dQp + (hb + sl) * D + c8[j]);
+            c[j].store_nt(dQp + (hb + sl) * D + c8[j]);
           }
         }
       }

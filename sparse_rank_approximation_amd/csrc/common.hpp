@@ -297,6 +297,11 @@ struct Vec8<__bf16> {
     for (int e = 0; e < 8; ++e) v[e] = (__bf16)((float)v[e] * c);
   }
   __device__ __forceinline__ void store(__bf16* p) const { *reinterpret_cast<bf16x8*>(p) = v; }
+  // A store of data no kernel reads soon (partial slots, read back by a later
+  // pass): marked non-temporal so that it does not displace reused rows in L2.
+  __device__ __forceinline__ void store_nt(__bf16* p) const {
+    __builtin_nontemporal_store(v, reinterpret_cast<bf16x8*>(p));
+  }
   __device__ __forceinline__ float get(int e) const { return (float)v[e]; }
 };
 template <>
@@ -317,6 +322,10 @@ struct Vec8<float> {
   __device__ __forceinline__ void store(float* p) const {
     *reinterpret_cast<floatx4*>(p) = a;
     *reinterpret_cast<floatx4*>(p + 4) = b;
+  }
+  __device__ __forceinline__ void store_nt(float* p) const {
+    __builtin_nontemporal_store(a, reinterpret_cast<floatx4*>(p));
+    __builtin_nontemporal_store(b, reinterpret_cast<floatx4*>(p + 4));
   }
   __device__ __forceinline__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
 };

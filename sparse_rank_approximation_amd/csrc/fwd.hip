@@ -283,7 +283,7 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), sizeof(T) == 2 ?
       for (int i = 0; i < PIT; ++i) {
         const int piece = tid + NT * i, c8 = (piece % CH) * 8;
         if ((SB >= 32 && (KT * CH) % NT == 0) || os[i] >= 0)
-          x[i].store(Opart + ((size_t)bh * slots + os[i]) * D + c8);
+          x[i].store_nt(Opart + ((size_t)bh * slots + os[i]) * D + c8);
       }
     }
     __syncthreads();  // Ks and oslot free for the next block

@@ -4,7 +4,8 @@ the same as elsaa_select's), A and z, the outputs and the saved statistics withi
 1e-4 (fp32) / 2e-2 (bf16) max-relative error; the backward taken from its saved
 tensors against the oracle's backward; run-to-run determinism; and the full-size
 vision workload (B64 H12 N1024 d64) in the launch configuration bench.py times, on
-sampled heads."""
+sampled heads; and codes of rows on or near their hyperplanes (the products cannot
+decide those bits, the fp64 chain does) bit for bit."""
 from __future__ import annotations
 
 import numpy as np
@@ -162,3 +163,44 @@ def test_fused_full_size_vision_workload():
     print(f"[gpu fused full] config {cid}: errors {errs}", flush=True)
     bad = {n: e for n, e in errs.items() if not e <= TOL[w.dtype]}
     assert not bad, f"errors above {TOL[w.dtype]}: {bad}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fused_codes_on_and_near_hyperplanes(dtype):
+    """Rows whose projections are exactly zero or within a few ulps of it,
+    subnormal rows, a hyperplane of zeros and a hyperplane holding a value below
+    2^-100: every code and order equal to the oracle's and to elsaa_select's."""
+    import sparse_rank_approximation_amd as S
+    w = wl("f", 1, 2, 512, 64, dtype, False, 32, 32)  # 4 hyperplanes per head
+    inp = W.gen_inputs(w, 5150)
+    q, k, ps = inp["q"].clone(), inp["k"].clone(), inp["planes_s"].clone()
+    # Head 0: hyperplanes 0 and 3 pair each even coordinate with its negation, so
+    # rows with x[2i] = x[2i + 1] lie exactly on them (every chain step cancels).
+    for b in (0, 3):
+        ps[0, b, 1::2] = -ps[0, b, 0::2]
+    for x in (q, k):
+        x[0, 0, 0:200, 1::2] = x[0, 0, 0:200, 0::2]
+        # one pair off by an ulp: a projection a few ulps from zero
+        x[0, 0, 100:200, 7] = x[0, 0, 100:200, 6] * (1 + 2.0 ** -7)
+        # subnormal rows (products the unit flushes)
+        x[0, 0, 300:310] = torch.where(x[0, 0, 300:310] > 0, 3e-39, -3e-39).to(x.dtype)
+    # Head 1: a hyperplane of zeros and one holding a value below 2^-100.
+    ps[1, 1] = 0.0
+    ps[1, 2, 5] = 1e-35
+    inp.update(q=q.contiguous(), k=k.contiguous(), planes_s=ps.contiguous())
+    lam = torch.ones(w.H)
+    cfg, d, f, _ = fused_forward(w, inp, lam)
+    qc, kc, qp, kp = S.select(cfg, d["q"], d["k"], d["planes_s"])
+    torch.cuda.synchronize()
+    heads = all_heads(w)
+    hq, hk, _, _, hps, _ = head_arrays(w, inp, heads)
+    rqc, rkc, rqp, rkp = ref.select(ref.RefParams.from_workload(w), hq, hk, hps)
+    G = len(heads)
+    np.testing.assert_array_equal(f["q_code"].view(G, -1).cpu().numpy().astype(np.uint16), rqc)
+    np.testing.assert_array_equal(f["k_code"].view(G, -1).cpu().numpy().astype(np.uint16), rkc)
+    np.testing.assert_array_equal(f["q_perm"].view(G, -1).cpu().numpy(), rqp.reshape(G, -1))
+    np.testing.assert_array_equal(f["k_perm"].view(G, -1).cpu().numpy(), rkp.reshape(G, -1))
+    for n, t in (("q_code", qc), ("k_code", kc), ("q_perm", qp), ("k_perm", kp)):
+        assert torch.equal(f[n], t), n
+    # the planted rows did land on the hyperplanes: bit 0 clear on head 0's paired rows
+    assert not (rqc[0, 0:100] & 1).any() and not (rqc[1] & (1 << 1)).any()
