@@ -926,6 +926,310 @@ __global__ void __launch_bounds__(64 * (SB < 32 ? 1 : SB / 32), D <= 64 ? 2 : 1)
 }
 
 // ---------------------------------------------------------------------------
+// Sparse backward with 16-key tiles: the same blocks, LDS tiles and slot stores
+// as sparse_bwd2_kernel (bf16, s = 128, one hash round), computed by 8 waves on
+// the 16x16x32 bf16 MFMA. Wave w takes keys 16w .. 16w + 15 in the key phase and
+// queries 16w .. 16w + 15 in the dQ phase, so that its dV, dK accumulators (16
+// keys x D channels each) and operands fit two waves per SIMD.
+//
+// 16x16x32 operand layout (lane = 16 g + s): A[m][k] is held by lane (m = s) at
+// k = 8 g + e; B[k][n] by lane (n = s) at k = 8 g + e; D[m][n] by lane (n = s) at
+// m = 4 g + e, e < 4.
+__device__ __forceinline__ floatx4 mma16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// Operand whose lanes run over 16 columns (n0 + s) of a row-major LDS matrix X and
+// whose K elements are X's rows kb1 .. kb1 + 3 (e < 4) and kb2 .. kb2 + 3 (e >= 4),
+// read with two ds_read_b64_tr_b16 (each 16-lane group may pass its own rows).
+__device__ __forceinline__ bf16x8 tr16(const __bf16* X, int ld, int kb1, int kb2, int n0, int lane) {
+  const int s = lane & 15;
+  typedef __attribute__((address_space(3))) bf16x4_tr* lds_ptr;
+  const int nb = n0 + 4 * (s & 3);
+  const bf16x4_tr a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_ptr)(X + (size_t)(kb1 + (s >> 2)) * ld + nb));
+  const bf16x4_tr b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_ptr)(X + (size_t)(kb2 + (s >> 2)) * ld + nb));
+  bf16x8 f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { f[e] = a[e]; f[4 + e] = b[e]; }
+  return f;
+}
+__device__ __forceinline__ floatx4 zero4() {
+  floatx4 z;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) z[e] = 0.0f;
+  return z;
+}
+
+template <int D>
+__global__ void __launch_bounds__(512)
+    sparse_bwd3_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                       const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                       const float* __restrict__ lse, const float* __restrict__ rc,
+                       const float* __restrict__ rD, const float* __restrict__ rsig,
+                       const int32_t* __restrict__ qperm, const int32_t* __restrict__ kperm,
+                       int N, int causal, int levels, float scale, int items, int total,
+                       __bf16* __restrict__ dQp, __bf16* __restrict__ dKp,
+                       __bf16* __restrict__ dVp) {
+  typedef __bf16 T;
+  constexpr int SB = 128;
+  typedef Sb2Smem<D, SB, false> Sm;
+  constexpr int KT = SB, NT = 512, LD = Sm::LD, LDK = Sm::LDK;
+  constexpr int CH = D / 8, GIT = KT * CH / NT, KS = D / 32, CT = D / 16;
+  __shared__ Sm sm;
+  const int tid = threadIdx.x, lane = tid & 63, s = lane & 15, g4 = lane >> 4;
+  const int w = wave_id();
+  const int G = gridDim.x;
+  const size_t P = perm_stride(N, levels, causal);
+  const size_t slots = partial_slots(N, levels, causal);
+  const int nord = causal ? levels : 1;
+  const int per_level = causal ? (N / 2) / SB : 0;
+  const int nlev = causal ? nord * per_level : 0;
+
+  auto head_of = [&](int gg) __attribute__((always_inline)) {
+    int it;
+    return xcd_item(gg, items, per_level, nord, it);
+  };
+  // Rows of block gg (as in sparse_bwd2_kernel): query and key tokens (a, b) when
+  // alt < -1, else both are alt (a causal leaf's token); threads t >= SB read the
+  // head's first entry and discard it.
+  struct Rows {
+    int a, b, alt;
+  };
+  auto rows_of = [&](int gg, int t) __attribute__((always_inline)) {
+    int it;
+    const int bh = xcd_item(gg, items, per_level, nord, it);
+    const bool lf = causal && it >= nlev, past = t >= SB;
+    const size_t off = (size_t)bh * P + (lf || past ? (size_t)0
+                                         : causal ? (size_t)(it / per_level) * (N / 2) +
+                                                        (size_t)(it % per_level) * SB + t
+                                                  : (size_t)it * SB + t);
+    return Rows{qperm[off], kperm[off], past ? -1 : lf ? (it - nlev) * SB + t : -2};
+  };
+
+  Vec8<T> pq[GIT], po[GIT], pk[GIT];
+  bf16x8 pv[KS];
+  float plse = 0.0f, pD = 0.0f, pc = 0.0f, psig = 0.0f;
+  bool pvalid = false;
+  Rows prow{-1, -1, -1};
+  auto gather = [&](int gn) __attribute__((always_inline)) {
+    const size_t rb = (size_t)head_of(gn) * N;
+#pragma unroll
+    for (int i = 0; i < GIT; ++i) {
+      const int piece = tid + NT * i, r = piece / CH, c8 = (piece % CH) * 8;
+      const int qi = sm.qnext[r], kj = sm.knext[r];
+      pq[i].load(Q + (rb + qi) * D + c8);
+      po[i].load(dO + (rb + qi) * D + c8);
+      pk[i].load(K + (rb + kj) * D + c8);
+    }
+    const int qi = sm.qnext[tid % KT];
+    const size_t k = rb + qi;
+    pvalid = qi >= 0;
+    plse = lse[k];
+    pD = rD[k];
+    pc = rc[k];
+    psig = rsig[k];
+  };
+  // V rows of this wave's 16 keys of the next block, as B operands (lane (key s,
+  // group g) holds channels 32 ks + 8 g .. + 7).
+  auto gather_v = [&](size_t rb) __attribute__((always_inline)) {
+    const int kv = sm.knext[16 * w + s];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      pv[ks] = *reinterpret_cast<const bf16x8*>(V + (rb + kv) * D + 32 * ks + 8 * g4);
+  };
+
+  int g = blockIdx.x;
+  if (g >= total) return;
+  if (tid < KT) {
+    const Rows r0 = rows_of(g, tid);
+    sm.qnext[tid] = r0.alt < -1 ? r0.a : r0.alt;
+    sm.knext[tid] = r0.alt < -1 ? r0.b : r0.alt;
+  }
+  __syncthreads();
+  gather(g);
+  prow = rows_of(min(g + G, total - 1), tid);
+  gather_v((size_t)head_of(g) * N);
+
+  for (; g < total; g += G) {
+    __syncthreads();  // the previous block is done with LDS
+#pragma unroll
+    for (int i = 0; i < GIT; ++i) {
+      const int piece = tid + NT * i, r = piece / CH, c8 = (piece % CH) * 8;
+      pq[i].store(&sm.Qs[r][c8]);
+      po[i].store(&sm.Os[r][c8]);
+      pk[i].store(&sm.Ks[r][c8]);
+    }
+    if (tid < KT) {
+      sm.qidx[tid] = sm.qnext[tid];
+      sm.kidx[tid] = sm.knext[tid];
+      sm.qnext[tid] = prow.alt < -1 ? prow.a : prow.alt;
+      sm.knext[tid] = prow.alt < -1 ? prow.b : prow.alt;
+      sm.lse[tid] = pvalid ? plse * kLog2e : INFINITY;
+      sm.Dd[tid] = pvalid ? pD : 0.0f;
+      sm.cq[tid] = pvalid ? pc : 0.0f;
+      sm.sig[tid] = pvalid ? psig : 0.0f;
+    }
+    int it;
+    const int bh = xcd_item(g, items, per_level, nord, it);
+    const bool leaf = causal && it >= nlev;
+    const int ord = leaf ? -1 : causal ? it / per_level : 0;
+    const int lev = causal && ord >= 0 ? ord : 0;
+    const bool own = causal ? leaf : true;
+    __syncthreads();
+
+    // Key phase: wave w, keys 16 w + s. S (queries x keys) and dP tiles of 16
+    // queries; dV^T, dK^T (channels x keys) accumulate over the block's queries.
+    const int key = 16 * w + s;
+    floatx4 dv[CT], dk[CT];
+    {
+      const bool kvalid = sm.kidx[key] >= 0;
+      const float c2 = scale * kLog2e;
+      bf16x8 kf[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[ks] = *reinterpret_cast<const bf16x8*>(&sm.Ks[key][32 * ks + 8 * g4]);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) dv[ct] = dk[ct] = zero4();
+      auto qtile = [&](int qt) __attribute__((always_inline)) {
+        floatx4 sa[2], da[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          sa[t] = zero4();
+          da[t] = zero4();
+          const int q = 32 * qt + 16 * t + s;
+          bf16x8 qa[KS], oa[KS];
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            qa[ks] = *reinterpret_cast<const bf16x8*>(&sm.Qs[q][32 * ks + 8 * g4]);
+            oa[ks] = *reinterpret_cast<const bf16x8*>(&sm.Os[q][32 * ks + 8 * g4]);
+          }
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            sa[t] = mma16(qa[ks], kf[ks], sa[t]);
+            da[t] = mma16(oa[ks], pv[ks], da[t]);
+          }
+        }
+        bf16x8 pf, sf;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int r0 = 32 * qt + 16 * t + 4 * g4;
+          const floatx4 L4 = *reinterpret_cast<const floatx4*>(&sm.lse[r0]);
+          const floatx4 D4 = *reinterpret_cast<const floatx4*>(&sm.Dd[r0]);
+          const floatx4 C4 = *reinterpret_cast<const floatx4*>(&sm.cq[r0]);
+          float dsv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool ok = kvalid & !(leaf & (key > r0 + e));
+            const float p = __builtin_amdgcn_exp2f(ok ? fmaf(sa[t][e], c2, -L4[e]) : -INFINITY);
+            dsv[e] = p * (C4[e] * da[t][e] - D4[e]);
+            pf[4 * t + e] = (__bf16)(C4[e] * p);
+            sf[4 * t + e] = (__bf16)dsv[e];
+          }
+          store4(&sm.dST[key][r0], dsv);
+        }
+        // K order of pf / sf: queries 32 qt + 4 g + e (e < 4), 32 qt + 16 + 4 g + e - 4.
+        const int kb1 = 32 * qt + 4 * g4, kb2 = kb1 + 16;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          dv[ct] = mma16(tr16(&sm.Os[0][0], LD, kb1, kb2, 16 * ct, lane), pf, dv[ct]);
+          dk[ct] = mma16(tr16(&sm.Qs[0][0], LD, kb1, kb2, 16 * ct, lane), sf, dk[ct]);
+        }
+      };
+      if (leaf) {
+        for (int qt = w >> 1; qt < 4; ++qt) qtile(qt);
+      } else {
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) qtile(qt);
+      }
+    }
+    // Loads for the next block and the indices of the one after.
+    const int gn = min(g + G, total - 1);
+    const size_t nrb = (size_t)head_of(gn) * N;
+    gather(gn);
+    prow = rows_of(min(g + 2 * G, total - 1), tid);
+    gather_v(nrb);
+    // This wave's dQ-phase queries (16 w + s): their channels 16 ct + 4 g .. + 3,
+    // read before Qs is reused.
+    bf16x4 qv[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+      qv[ct] = *reinterpret_cast<const bf16x4*>(&sm.Qs[16 * w + s][16 * ct + 4 * g4]);
+    __syncthreads();  // dS^T complete; Qs and Os no longer read
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      float xv[4], xk[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xv[e] = dv[ct][e];
+        xk[e] = dk[ct][e] * scale;
+      }
+      store4(&sm.Qs[key][16 * ct + 4 * g4], xv);
+      store4(&sm.Os[key][16 * ct + 4 * g4], xk);
+    }
+    // dQ phase: dQ^T (channels x queries 16 w + s) = K^T dS^T over the block's keys
+    // (leaf blocks: keys up to the wave's last query).
+    floatx4 dq[CT];
+    float sig = 0.0f;
+    {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) dq[ct] = zero4();
+      const int nks = leaf ? (w >> 1) + 1 : KT / 32;
+      for (int ks = 0; ks < nks; ++ks) {
+        const int kb = 32 * ks + 8 * g4;
+        const bf16x8 bq = tr16(&sm.dST[0][0], LDK, kb, kb + 4, 16 * w, lane);
+        sig = frag_sum<T>(bq, sig);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          dq[ct] = mma16(tr16(&sm.Ks[0][0], LD, kb, kb + 4, 16 * ct, lane), bq, dq[ct]);
+      }
+    }
+    sig += __shfl_xor(sig, 16);
+    sig += __shfl_xor(sig, 32);
+    sig -= own ? sm.sig[16 * w + s] : 0.0f;
+    __syncthreads();  // Ks no longer read; dV, dK tiles complete
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      float xq[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xq[e] = (dq[ct][e] - sig * (float)qv[ct][e]) * scale;
+      store4(&sm.Ks[16 * w + s][16 * ct + 4 * g4], xq);
+    }
+    __syncthreads();
+    {
+      const size_t hb = (size_t)bh * slots;
+      constexpr int PB = GIT % 2 == 0 ? 2 : 1;
+#pragma unroll
+      for (int i0 = 0; i0 < GIT; i0 += PB) {
+        Vec8<T> a[PB], b2[PB], c[PB];
+        int jk[PB], iq[PB], rr[PB], c8[PB];
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+          const int piece = tid + NT * (i0 + j);
+          rr[j] = piece / CH;
+          c8[j] = (piece % CH) * 8;
+          jk[j] = sm.kidx[rr[j]];
+          iq[j] = sm.qidx[rr[j]];
+          a[j].load(&sm.Qs[rr[j]][c8[j]]);
+          b2[j].load(&sm.Os[rr[j]][c8[j]]);
+          c[j].load(&sm.Ks[rr[j]][c8[j]]);
+        }
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+          const size_t slk = !causal ? (size_t)jk[j]
+                             : leaf  ? (size_t)jk[j]
+                                     : (size_t)N + (size_t)ord * (N / 2) + compact_past(jk[j], N, lev);
+          a[j].store_nt(dVp + (hb + slk) * D + c8[j]);
+          b2[j].store_nt(dKp + (hb + slk) * D + c8[j]);
+          const size_t slq = !causal ? (size_t)iq[j]
+                             : leaf  ? (size_t)iq[j]
+                                     : (size_t)N + (size_t)ord * (N / 2) + compact_future_b(iq[j], N, lev);
+          c[j].store_nt(dQp + (hb + slq) * D + c8[j]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Low-rank branch, query side: one head and span per workgroup, walked forwards in
 // steps of STEP tokens by 8 waves. Each query tile of the step is shared by a
 // wave of half 0 (waves 0..3, tiles in order) and one of half 1 (waves 4..7, tiles
@@ -1609,6 +1913,14 @@ bool launch_bwd(const Problem& pb, const void* Q, const void* K, const void* V, 
                         !(sizeof(SbwdSmem<T, D, SB, 1, MR>) <= kLdsBytes)) {
             ok = false;
           } else if (dry) {
+          } else if constexpr (std::is_same_v<T, __bf16> && SB == 128 && !MR &&
+                               (D == 64 || D == 128)) {
+            const int total = items * (int)BH;
+            const int G = persistent_grid((const void*)sparse_bwd3_kernel<D>, 512, total);
+            ELSAA_LAUNCH("sparse_bwd", (sparse_bwd3_kernel<D>), dim3(G), dim3(512), 0, st,
+                         (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, (const __bf16*)dO,
+                         lse, rc, rD, rsig, qp, kp, pb.N, (int)pb.causal, pb.levels, pb.scale,
+                         items, total, (__bf16*)dQp, (__bf16*)dKp, (__bf16*)dVp);
           } else if constexpr (std::is_same_v<T, __bf16> && SB <= 128 &&
                                sizeof(Sb2Smem<D, SB, MR>) <= kLdsBytes) {
             constexpr int NT = 64 * (SB < 32 ? 1 : SB / 32);
