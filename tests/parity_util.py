@@ -85,6 +85,14 @@ CASES = {
     # bf16 causal with planted clusters, d 128, s 128, r 128, two summaries per head
     "causal_bf16_N1024_d128_s128": (wl("c", 1, 2, 1024, 128, "bf16", True, 128, 128,
                                        "clusters", chunk=512, n_clusters=16, sigma=0.5), True, True),
+    # bf16 causal, d 64, s 128: the backward's 16-key-tile kernel at d 64 over the
+    # off-diagonal levels as well as the leaves
+    "causal_bf16_N1024_d64_s128": (wl("c", 1, 2, 1024, 64, "bf16", True, 128, 64,
+                                      "clusters", chunk=256, n_clusters=16, sigma=0.5), True, True),
+    # bf16 non-causal, d 128, s 128, three blocks per head and three heads (a block
+    # count that is no multiple of the eight XCDs)
+    "noncausal_bf16_N384_d128_s128": (wl("n", 1, 3, 384, 128, "bf16", False, 128, 64,
+                                         "clusters", n_clusters=8, sigma=0.5), True, True),
     # bf16 non-causal vision-like field, d 64, s 32, r 32
     "vit_bf16_N1024_d64_s32": (wl("v", 2, 2, 1024, 64, "bf16", False, 32, 32, "smooth_field",
                                   grid=32, blur=2.0, noise=0.3), False, False),
