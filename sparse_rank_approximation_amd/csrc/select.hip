@@ -220,6 +220,84 @@ __global__ void __launch_bounds__(256) sort_kernel(const uint16_t* __restrict__ 
   }
 }
 
+// The same sort for the causal levels whose segment halves hold at most
+// kSmallHalf tokens: one wave per segment half, four to a workgroup, with no
+// barrier across waves (segment id = first_id + 4 blockIdx.x + wave; ids past the
+// last segment leave their wave idle). Counts per bin, their exclusive scan and the
+// ballot placement are those of sort_kernel for a single wave.
+constexpr int kSmallHalf = 512;
+
+__global__ void __launch_bounds__(256) sort_small_kernel(const uint16_t* __restrict__ qc,
+                                                         const uint16_t* __restrict__ kc,
+                                                         int32_t* __restrict__ qperm,
+                                                         int32_t* __restrict__ kperm, int N,
+                                                         int levels, int bits, int rounds,
+                                                         int first_id, int nseg) {
+  extern __shared__ int smem[];
+  const int nbins = 1 << bits;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  int* cnt = smem + w * nbins;  // this wave's bins
+  const int id = first_id + 4 * blockIdx.x + w;
+  if (id >= nseg) return;  // (whole waves: nothing below synchronizes across waves)
+  const int bh = blockIdx.y, isk = blockIdx.z & 1, rd = blockIdx.z >> 1;
+  const int l = 31 - __clz(id + 1);
+  const int g = id + 1 - (1 << l);
+  const int n = N >> l, half = n >> 1;
+  const int base = g * n + (isk ? 0 : half), count = half;
+  const uint16_t* code = (isk ? kc : qc) + ((size_t)bh * rounds + rd) * N + base;
+  int32_t* out = (isk ? kperm : qperm) + (size_t)bh * perm_stride(N, levels, true, rounds) +
+                 (size_t)rd * perm_stride(N, levels, true) + (size_t)l * (N / 2) + (size_t)g * half;
+  for (int i = lane; i < nbins; i += 64) cnt[i] = 0;
+  __builtin_amdgcn_wave_barrier();
+  unsigned keys[kSmallHalf / 64];
+#pragma unroll
+  for (int j = 0; j < kSmallHalf / 64; ++j) {
+    const int t = 64 * j + lane;
+    keys[j] = t < count ? gray_rank(code[t]) : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < kSmallHalf / 64; ++j)
+    if (64 * j + lane < count) atomicAdd(&cnt[keys[j]], 1);
+  __builtin_amdgcn_wave_barrier();
+  // Exclusive scan of the bins: lane takes a run of per consecutive bins.
+  const int per = (nbins + 63) / 64;
+  int sum = 0;
+  for (int e = lane * per; e < min(nbins, (lane + 1) * per); ++e) sum += cnt[e];
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  int run = incl - sum;
+  __builtin_amdgcn_wave_barrier();
+  for (int e = lane * per; e < min(nbins, (lane + 1) * per); ++e) {
+    const int v = cnt[e];
+    cnt[e] = run;
+    run += v;
+  }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int j = 0; j < kSmallHalf / 64; ++j) {
+    const int t = 64 * j + lane;
+    if (64 * j >= count) break;
+    const bool valid = t < count;
+    const unsigned key = keys[j];
+    unsigned long long eq = __ballot(valid);
+    for (int b = 0; b < bits; ++b) {
+      const unsigned long long m = __ballot(valid && ((key >> b) & 1u));
+      eq &= ((key >> b) & 1u) ? m : ~m;
+    }
+    if (valid) {
+      const unsigned long long below = (lane == 0) ? 0ull : (eq & ((1ull << lane) - 1ull));
+      out[cnt[key] + __popcll(below)] = base + t;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (eq >> lane) == 1ull) cnt[key] += __popcll(eq);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 // Scratch of the allocation-free selection (elsaa_select_noalloc): the fp64
 // hyperplanes go to this fixed array instead of a caller's workspace. Every GPU
 // the library runs on holds its own copy until the process ends; calls on one
@@ -331,18 +409,31 @@ void launch_select(const Problem& pb, const void* Q, const void* K, const float*
     });
   });
   const int nseg = pb.causal ? (1 << pb.levels) - 1 : 1;
+  // Causal levels l whose halves N >> (l + 1) hold at most kSmallHalf tokens go to
+  // the one-wave-per-segment kernel (segment ids from 2^l_small - 1 on).
+  int nbig = nseg;
+  if (pb.causal)
+    for (int l = 0; l < pb.levels; ++l)
+      if ((pb.N >> (l + 1)) <= kSmallHalf) {
+        nbig = (1 << l) - 1;
+        break;
+      }
   const size_t lds = sizeof(int) * ((size_t)kSortWaves * (1 << pb.hash_bits) + 256);
   const size_t seg_codes = sizeof(uint16_t) * (size_t)(pb.causal ? pb.N / 2 : pb.N);
-  if (nseg > 0) {
+  if (nbig > 0) {
     if (lds + seg_codes <= 64 * 1024)
-      ELSAA_LAUNCH("sort", sort_kernel<true>, dim3(nseg, BH, 2 * pb.rounds), dim3(256),
+      ELSAA_LAUNCH("sort", sort_kernel<true>, dim3(nbig, BH, 2 * pb.rounds), dim3(256),
                    lds + seg_codes, st, qc, kc, qperm, kperm, pb.N, (int)pb.causal, pb.levels,
                    pb.hash_bits, pb.rounds);
     else
-      ELSAA_LAUNCH("sort", sort_kernel<false>, dim3(nseg, BH, 2 * pb.rounds), dim3(256), lds, st,
+      ELSAA_LAUNCH("sort", sort_kernel<false>, dim3(nbig, BH, 2 * pb.rounds), dim3(256), lds, st,
                    qc, kc, qperm, kperm, pb.N, (int)pb.causal, pb.levels, pb.hash_bits,
                    pb.rounds);
   }
+  if (nseg > nbig)
+    ELSAA_LAUNCH("sort_small", sort_small_kernel, dim3((nseg - nbig + 3) / 4, BH, 2 * pb.rounds),
+                 dim3(256), sizeof(int) * 4 * ((size_t)1 << pb.hash_bits), st, qc, kc, qperm,
+                 kperm, pb.N, pb.levels, pb.hash_bits, pb.rounds, nbig, nseg);
 }
 
 }  // namespace elsaa
