@@ -50,7 +50,7 @@ def short_name(name: str):
     if "topk_stream_kernel" in name:  # (the radix passes, then the listing pass)
         return "topk_collect" if "ELb1" in name else "topk_thresh"
     for k in ("sparse_bwd", "sparse_fwd", "lr_bwd_k", "lr_bwd_q", "fwd_epilogue", "lr_sums",
-              "lr_scan", "hash_kernel", "sort_kernel", "merge_kernel", "bwd_rows", "dlam_reduce",
+              "lr_scan", "hash_kernel", "sort_small_kernel", "sort_kernel", "merge_kernel", "bwd_rows", "dlam_reduce",
               "planes_transpose", "planes_f64", "block_ids", "extra_prep", "extra_fwd",
               "extra_bwd_q", "extra_bwd_k", "radix_hist", "radix_scan", "radix_scatter",
               "topk_finish", "topk_heap", "topk_zero", "gates_fwd", "gates_bwd", "gates_reduce",
