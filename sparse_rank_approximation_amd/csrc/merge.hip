@@ -14,14 +14,18 @@ namespace elsaa {
 
 namespace {
 
-constexpr int kMergeBatch = 8;  // slots in flight per lane
+// Slots in flight per lane (MB): measured per kernel at the headline workload
+// (merge 4, dQ combine 2, dK/dV combine 4; 8 cost each of them 8-12 %, 16 nearly
+// doubled them: more rows in flight per lane hold more registers, and fewer
+// workgroups stay resident).
+constexpr int kMergeBatch = 4, kCombineQBatch = 2, kCombineKVBatch = 4;
 
-template <typename T, int D>
+template <typename T, int D, int MB>
 __global__ void __launch_bounds__(256)
     merge_kernel(const T* __restrict__ Opart, const float* __restrict__ Lpart,
                  const T* __restrict__ Ox, const float* __restrict__ Lx, int N, int levels,
                  int causal, int rounds, float* __restrict__ Os, float* __restrict__ lse) {
-  constexpr int LPR = D / 8, RPB = 256 / LPR, MB = kMergeBatch;
+  constexpr int LPR = D / 8, RPB = 256 / LPR;
   const int bh = blockIdx.y, tid = threadIdx.x;
   const int tok = blockIdx.x * RPB + tid / LPR, c8 = (tid % LPR) * 8;
   const bool valid = tok < N;
@@ -85,12 +89,12 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-template <typename T, int D, bool QUERY, int NX>
+template <typename T, int D, bool QUERY, int NX, int MB>
 __global__ void __launch_bounds__(256)
     combine_kernel(const T* __restrict__ p0, const T* __restrict__ p1, const T* __restrict__ x0,
                    const T* __restrict__ x1, T* __restrict__ o0, T* __restrict__ o1, int N,
                    int levels, int causal, int rounds) {
-  constexpr int LPR = D / 8, RPB = 256 / LPR, MB = kMergeBatch;
+  constexpr int LPR = D / 8, RPB = 256 / LPR;
   const int bh = blockIdx.y, tid = threadIdx.x;
   const int tok = blockIdx.x * RPB + tid / LPR, c8 = (tid % LPR) * 8;
   const bool valid = tok < N;
@@ -145,7 +149,7 @@ void launch_merge(const Problem& pb, const void* Opart, const float* Lpart, cons
     with_D(pb.d, [&](auto dc) {
       constexpr int D = ELSAA_C(dc);
       constexpr int RPB = 256 / (D / 8);
-      ELSAA_LAUNCH("merge", (merge_kernel<T, D>), dim3((pb.N + RPB - 1) / RPB, BH), dim3(256), 0,
+      ELSAA_LAUNCH("merge", (merge_kernel<T, D, kMergeBatch>), dim3((pb.N + RPB - 1) / RPB, BH), dim3(256), 0,
                    st, (const T*)Opart, Lpart, (const T*)Ox, Lx, pb.N, pb.levels, (int)pb.causal,
                    pb.rounds, O_s, lse);
     });
@@ -162,11 +166,11 @@ void launch_combine(const Problem& pb, const void* dQp, const void* dKp, const v
       constexpr int D = ELSAA_C(dc);
       constexpr int RPB = 256 / (D / 8);
       const dim3 grid((pb.N + RPB - 1) / RPB, BH);
-      ELSAA_LAUNCH("combine_q", (combine_kernel<T, D, true, 1>), grid, dim3(256), 0, st,
+      ELSAA_LAUNCH("combine_q", (combine_kernel<T, D, true, 1, kCombineQBatch>), grid, dim3(256), 0, st,
                    (const T*)dQp, (const T*)nullptr, (const T*)dQx, (const T*)nullptr, (T*)dQ,
                    (T*)nullptr, pb.N, pb.levels,
                    (int)pb.causal, pb.rounds);
-      ELSAA_LAUNCH("combine_kv", (combine_kernel<T, D, false, 2>), grid, dim3(256), 0, st,
+      ELSAA_LAUNCH("combine_kv", (combine_kernel<T, D, false, 2, kCombineKVBatch>), grid, dim3(256), 0, st,
                    (const T*)dKp, (const T*)dVp, (const T*)dKx, (const T*)dVx, (T*)dK, (T*)dV,
                    pb.N, pb.levels,
                    (int)pb.causal, pb.rounds);
