@@ -26,6 +26,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import sys
 
 COPY_BYTES = 1 << 30  # 1 GiB read + 1 GiB written: well past the last-level cache
@@ -49,6 +50,16 @@ def short_name(name: str):
         return "combine_q" if "ELb1" in name else "combine_kv"
     if "topk_stream_kernel" in name:  # (the radix passes, then the listing pass)
         return "topk_collect" if "ELb1" in name else "topk_thresh"
+    # sparse_bwd_kernel<T, D, SB, ROLE, MR>: role 2 is the separate dQ launch
+    m = re.search(r"sparse_bwd_kernelI(?:DF16b|f)Li\d+ELi\d+ELi(\d)E", name)
+    if m or "sparse_bwd_kernel<" in name:
+        role = m.group(1) if m else name.split("sparse_bwd_kernel<")[1].split(",")[3].strip()
+        return "sparse_bwd_q" if role == "2" else "sparse_bwd"
+    for k, launch in (("topk_heap_kernel", "topk_redo"), ("order_fill_kernel", "check_fill"),
+                      ("order_mark_kernel", "check_mark"), ("order_verify_kernel", "check_verify"),
+                      ("finite_count_kernel", "check_finite")):
+        if k in name:
+            return launch
     for k in ("sparse_bwd", "sparse_fwd", "lr_bwd_k", "lr_bwd_q", "fwd_epilogue", "lr_sums",
               "lr_scan", "hash_kernel", "sort_small_kernel", "sort_kernel", "merge_kernel", "bwd_rows", "dlam_reduce",
               "planes_transpose", "planes_f64", "block_ids", "extra_prep", "extra_fwd",

@@ -42,6 +42,34 @@ def test_short_names():
     assert traffic.short_name("elsaa::planes_transpose_kernel(float const*, int, int, int, float*)") == "planes_t"
 
 
+def test_every_launch_name_maps_back():
+    """Every ELSAA_LAUNCH name in the sources is what short_name gives for its
+    kernel, so a counter summary is keyed by the names bench.py reports."""
+    import glob
+    import os
+    import re
+    csrc = os.path.join(os.path.dirname(traffic.__file__), "csrc")
+    text = "".join(open(f).read() for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) +
+                                                 glob.glob(os.path.join(csrc, "*.cpp"))))
+    pairs = set(re.findall(r'ELSAA_LAUNCH\("([a-z_0-9]+)",\s*\(?([A-Za-z_0-9]+)', text))
+    assert len(pairs) > 30
+    names = {}
+    for launch, kern in pairs:
+        names.setdefault(kern, set()).add(launch)
+    for kern, launches in names.items():
+        if len(launches) == 1:  # (kernels launched under several names: below)
+            assert traffic.short_name(f"elsaa::{kern}(int)") == next(iter(launches)), kern
+    assert {k for k, v in names.items() if len(v) > 1} == {
+        "combine_kernel", "topk_stream_kernel", "sparse_bwd_kernel"}
+    assert traffic.short_name(COMBINE_Q) == "combine_q"
+    assert traffic.short_name(COMBINE_KV) == "combine_kv"
+    role = "_ZN5elsaa17sparse_bwd_kernelIDF16bLi128ELi256ELi{}ELb0EEEvPKT_S3_S3_S3_PKfS5_S5_S5_PKiS7_iiiiS7_S7_fPS1_S8_S8_"
+    assert traffic.short_name(role.format(1)) == "sparse_bwd"
+    assert traffic.short_name(role.format(3)) == "sparse_bwd"
+    assert traffic.short_name(role.format(2)) == "sparse_bwd_q"
+    assert traffic.short_name("void elsaa::sparse_bwd_kernel<float, 64, 32, 2, false>(float const*)") == "sparse_bwd_q"
+
+
 def test_summarize_calibrates_and_averages(tmp_path):
     kib = traffic.COPY_BYTES / 1024.0
     # Calibration runs: the copy reads half of what it moves as FETCH_SIZE and all of
