@@ -27,9 +27,11 @@
 //   lr_sums + lr_scan    (lowrank.hip) G = sum_i phi(Q_i) dnum_i^T, g = sum_i
 //                        phi(Q_i) dd_lr,i per chunk, combined as the exclusive suffix
 //                        over chunks (causal) or the total;
-//   sparse_bwd2_kernel   per selected block (bf16, blocks of at most 128; else
-//   / sparse_bwd_kernel  sparse_bwd_kernel, in one launch or a key launch and a
-//                        query launch): dQ, dK, dV partials per level slot;
+//   sparse_bwd3_kernel   per selected block: dQ, dK, dV partials per level slot
+//   / sparse_bwd2_kernel (bf16 blocks of 128 with one hash round: sparse_bwd3 on
+//   / sparse_bwd_kernel  16-key tiles, 8 waves; other bf16 blocks of at most 128:
+//                        sparse_bwd2; else sparse_bwd_kernel, in one launch or a
+//                        key launch and a query launch);
 //   lr_bwd_q_kernel      query side of the low-rank branch, walking each chunk
 //                        forwards with the running key statistics A, z:
 //                        dphi(Q_i) = sum_{j<=i} (<dnum_i, V_j> + dd_lr,i) phi(K_j),
